@@ -1,0 +1,671 @@
+/*
+ * Plain CPU oracle for NVFP4 fake-quantized attention (Attn-QAT).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or constant with the
+ * HIP library.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [QAD]  "nvfp4_qad.py" (FastVideo fastvideo/layers/quantization source page):
+ *         module docstring (per-16 E4M3 block scales under a unit or static
+ *         global scale), FP4_RANGE = 448*6, weight_global_sf (nan_to_num and
+ *         the 1e-12 clamp), NVFP4QADLinearMethod.input_global_sf.
+ *  [META] "vsqa-preview-1.3b metadata.json": attention.precision ("fine":
+ *         NVFP4 fake-quant with BF16 matmul, quant_p, quant_v, quantize_coarse
+ *         false), attention.selection (effective_topk formula, sparsity 0.9),
+ *         attention.cube_shape [4,4,8]; the dense parent's precision record
+ *         (group_size 16, qk/pv_format NVFP4 E2M1, scale dtype FP8 E4M3FN,
+ *         backward "consistent STE with auxiliary output").
+ *  [API]  "attn_qat_train" API reference page: attn_qat_train (BHLD layout,
+ *         default sm_scale 1/sqrt(D), use_high_prec_o, fake_quant_p_bwd,
+ *         use_qat_qkv_backward, unit global scales).
+ *
+ * Readings where the pages are silent are listed in the design notes; the
+ * ones that shape arithmetic here are: the running max is refreshed once per
+ * 128-key chunk (the chunk length is a parameter), the softmax denominator
+ * sums unquantized P, the quotient |x|/S and amax/6 are fp32 IEEE divisions,
+ * E4M3 saturates at 448 and keeps subnormals, E2M1 saturates at 6, ties go to
+ * the even code, and a zero block scale gives signed zeros.
+ *
+ * Precision: the codec runs in fp32 (the precision both sides take the
+ * rounding decisions in); dot products, softmax sums and gradients run in
+ * fp64.  Build with -ffp-contract=off so no FMA contraction changes fp32
+ * results.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* bf16 <-> fp32                                                            */
+/* ------------------------------------------------------------------------ */
+
+static float bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round-to-nearest-even fp32 -> bf16 (inputs here are always finite). */
+static uint16_t f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+static uint16_t f64_to_bf16(double d)
+{
+    /* Exact RNE of a double to bf16: find the two neighbouring bf16 values
+       by truncating toward zero, then compare distances in double. */
+    if (d == 0.0) return signbit(d) ? 0x8000 : 0x0000;
+    float f = (float)d; /* nearest fp32 */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint16_t lo = (uint16_t)(u >> 16);           /* truncated magnitude */
+    uint16_t hi = (uint16_t)(lo + 1);            /* next magnitude away from 0 */
+    double vlo = bf16_to_f32(lo), vhi = bf16_to_f32(hi);
+    double dlo = fabs(d - vlo), dhi = fabs(d - vhi);
+    if (dlo < dhi) return lo;
+    if (dhi < dlo) return hi;
+    return (lo & 1u) ? hi : lo;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Codec: value tables and nearest-value search.                            */
+/* ------------------------------------------------------------------------ */
+
+/* FP8 E4M3FN ([META] qk_scale_dtype "FP8 E4M3FN"): bias 7, 3 mantissa bits,
+   no infinities, code 0x7F is NaN, largest finite value 448 ([QAD] FP4_RANGE
+   = 448 * 6).  Codes 0..126 are the non-negative finite values in
+   increasing order. */
+static float e4m3_table[127];
+/* E2M1 magnitudes ([META] qk_format "NVFP4 E2M1"): codes 0..7. */
+static const float e2m1_table[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+static void init_tables(void)
+{
+    static int done = 0;
+    if (done) return;
+    for (int code = 0; code < 127; ++code) {
+        int e = code >> 3, m = code & 7;
+        e4m3_table[code] = (e == 0) ? ldexpf((float)m, -9)
+                                    : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    }
+    done = 1;
+}
+
+/* Nearest entry of an increasing table to v >= 0; on an exact tie the even
+   code wins; values above the last entry saturate to it. */
+static int nearest_code(const float *table, int n, float v)
+{
+    if (v >= table[n - 1]) return n - 1;
+    int best = 0;
+    double bestd = fabs((double)v - (double)table[0]);
+    for (int c = 1; c < n; ++c) {
+        double d = fabs((double)v - (double)table[c]);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+float oracle_e4m3(float v) { init_tables(); return e4m3_table[nearest_code(e4m3_table, 127, v)]; }
+float oracle_e2m1(float v) { return e2m1_table[nearest_code(e2m1_table, 8, v)]; }
+int oracle_e2m1_code(float v) { return nearest_code(e2m1_table, 8, v); }
+
+/* Block scale actually used to dequantize, for a block with abs-max `amax`
+   under global scale g: s = E4M3(fp32(fp32(amax / 6) * g)), S = fp32(s / g). */
+float oracle_block_scale(float amax, float g)
+{
+    init_tables();
+    volatile float a6 = amax / 6.0f;
+    volatile float sg = a6 * g;
+    float s = oracle_e4m3(sg);
+    volatile float S = s / g;
+    return S;
+}
+
+/* One fake-quantized element given its block scale S: E2M1 of fp32(|x|/S),
+   times S, sign restored. */
+static float fq_elem(float x, float S)
+{
+    if (S == 0.0f) return copysignf(0.0f, x);
+    volatile float r = fabsf(x) / S;
+    float q = oracle_e2m1(r);
+    volatile float y = q * S;
+    return copysignf(y, x);
+}
+
+/* Fake-quantize one block of n (<= 16) fp32 values in place. */
+static void fq_block_f32(float *x, int n, float g)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i)
+        if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+    float S = oracle_block_scale(amax, g);
+    for (int i = 0; i < n; ++i) x[i] = fq_elem(x[i], S);
+}
+
+/* Standalone fake-quant of a bf16 tensor viewed as [outer, axis, inner],
+   blocks of 16 consecutive positions along `axis` (the last block may be
+   shorter), global scale g (1.0 = unit).  Output is bf16 RNE of the fp32
+   dequantized value.  [QAD] module docstring; [META] group_size 16. */
+void oracle_fq_bf16(const uint16_t *x, uint16_t *y, int64_t outer, int64_t axis, int64_t inner,
+                    float g)
+{
+    init_tables();
+    float buf[16];
+    for (int64_t o = 0; o < outer; ++o)
+        for (int64_t a0 = 0; a0 < axis; a0 += 16) {
+            int n = (int)((axis - a0) < 16 ? (axis - a0) : 16);
+            for (int64_t in = 0; in < inner; ++in) {
+                for (int i = 0; i < n; ++i)
+                    buf[i] = bf16_to_f32(x[(o * axis + a0 + i) * inner + in]);
+                fq_block_f32(buf, n, g);
+                for (int i = 0; i < n; ++i)
+                    y[(o * axis + a0 + i) * inner + in] = f32_to_bf16(buf[i]);
+            }
+        }
+}
+
+/* Static global scale [QAD] weight_global_sf / input_global_sf:
+   g = 448*6 / max(nan_to_num(amax|x|), 1e-12), in fp32. */
+float oracle_static_scale_bf16(const uint16_t *x, int64_t n)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = fabsf(bf16_to_f32(x[i]));
+        if (isnan(v)) v = 0.0f;
+        if (v > amax) amax = v;
+    }
+    if (amax < 1e-12f) amax = 1e-12f;
+    volatile float g = (448.0f * 6.0f) / amax;
+    return g;
+}
+
+/* Fake-quant of fp32 values in blocks of 16 along a contiguous vector (used by
+   the tests to exercise the codec on fp32 inputs such as softmax
+   probabilities). */
+void oracle_fq_f32_rows(const float *x, float *y, int64_t rows, int64_t len, float g)
+{
+    init_tables();
+    float buf[16];
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t a0 = 0; a0 < len; a0 += 16) {
+            int n = (int)((len - a0) < 16 ? (len - a0) : 16);
+            for (int i = 0; i < n; ++i) buf[i] = x[r * len + a0 + i];
+            fq_block_f32(buf, n, g);
+            for (int i = 0; i < n; ++i) y[r * len + a0 + i] = buf[i];
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention.  Tensors are [B, H, L, D] bf16 (row-major); D is the head size. */
+/* ------------------------------------------------------------------------ */
+
+enum { QF_Q = 1, QF_K = 2, QF_V = 4, QF_P = 8 };
+
+/* Per-head operands after fake quantization: Q and K along D, V along the
+   key axis ([META] quant_v, qk_format/pv_format; [API] unit global scales
+   use_global_sf_qkv = use_global_sf_p = False). */
+typedef struct {
+    float *qh; /* [Lq, D] */
+    float *kh; /* [Lk, D] */
+    float *vh; /* [Lk, D] */
+} head_ops;
+
+static void load_head(const uint16_t *src, float *dst, int64_t L, int D)
+{
+    for (int64_t i = 0; i < L * D; ++i) dst[i] = bf16_to_f32(src[i]);
+}
+
+static void quant_rows_D(float *x, int64_t L, int D)
+{
+    for (int64_t i = 0; i < L; ++i)
+        for (int d0 = 0; d0 < D; d0 += 16) fq_block_f32(x + i * D + d0, D - d0 < 16 ? D - d0 : 16, 1.0f);
+}
+
+static void quant_cols_L(float *x, int64_t L, int D)
+{
+    float buf[16];
+    for (int d = 0; d < D; ++d)
+        for (int64_t j0 = 0; j0 < L; j0 += 16) {
+            int n = (int)((L - j0) < 16 ? (L - j0) : 16);
+            for (int i = 0; i < n; ++i) buf[i] = x[(j0 + i) * D + d];
+            fq_block_f32(buf, n, 1.0f);
+            for (int i = 0; i < n; ++i) x[(j0 + i) * D + d] = buf[i];
+        }
+}
+
+static void make_head_ops(head_ops *h, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          int64_t Lq, int64_t Lk, int D, unsigned flags)
+{
+    h->qh = (float *)malloc(sizeof(float) * Lq * D);
+    h->kh = (float *)malloc(sizeof(float) * Lk * D);
+    h->vh = (float *)malloc(sizeof(float) * Lk * D);
+    load_head(q, h->qh, Lq, D);
+    load_head(k, h->kh, Lk, D);
+    load_head(v, h->vh, Lk, D);
+    if (flags & QF_Q) quant_rows_D(h->qh, Lq, D);
+    if (flags & QF_K) quant_rows_D(h->kh, Lk, D);
+    if (flags & QF_V) quant_cols_L(h->vh, Lk, D);
+}
+
+static void free_head_ops(head_ops *h)
+{
+    free(h->qh);
+    free(h->kh);
+    free(h->vh);
+}
+
+/* S_ij = fp32(scale * <q_i, k_j>), dot product in fp64. */
+static float logit(const head_ops *h, int64_t i, int64_t j, int D, double scale)
+{
+    const float *a = h->qh + i * D, *b = h->kh + j * D;
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s += (double)a[d] * (double)b[d];
+    return (float)(scale * s);
+}
+
+/* Online-softmax forward for one query row (the fine stage of both the dense
+   and the cube-sparse method).  The keys are visited as a list of chunks; in
+   each chunk the running max is refreshed first, then P = exp(S - m) is
+   formed, fake-quantized over 16-key blocks (keys aligned to the chunk start;
+   masked or absent keys count as 0), and folded into the accumulators.
+   keys[c*chunk + t] is the key index of position t of chunk c, or -1 when
+   the position is masked/absent.
+   Outputs: o (quantized-P output), o_hp (auxiliary high-precision output,
+   unquantized P; [API] use_high_prec_o), lse = m + ln l, and the running
+   max after every chunk (cmax[c], -inf for a chunk that had no live key). */
+static void row_forward(const head_ops *h, int64_t i, const int64_t *keys, int64_t nchunks, int chunk,
+                        int D, double scale, unsigned flags, double *o, double *o_hp, double *lse,
+                        double *cmax)
+{
+    float *S = (float *)malloc(sizeof(float) * chunk);
+    float *P = (float *)malloc(sizeof(float) * chunk);
+    float *Pq = (float *)malloc(sizeof(float) * chunk);
+    double *acc = (double *)calloc(D, sizeof(double));
+    double *acc_hp = (double *)calloc(D, sizeof(double));
+    float m = -INFINITY;
+    double l = 0.0;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t *kc = keys + c * chunk;
+        int live = 0;
+        float cm = -INFINITY;
+        for (int t = 0; t < chunk; ++t) {
+            if (kc[t] < 0) continue;
+            S[t] = logit(h, i, kc[t], D, scale);
+            if (S[t] > cm) cm = S[t];
+            live = 1;
+        }
+        if (!live) {
+            if (cmax) cmax[c] = -INFINITY;
+            continue;
+        }
+        float m_new = m > cm ? m : cm;
+        for (int t = 0; t < chunk; ++t)
+            P[t] = (kc[t] < 0) ? 0.0f : (float)exp((double)S[t] - (double)m_new);
+        memcpy(Pq, P, sizeof(float) * chunk);
+        if (flags & QF_P)
+            for (int t0 = 0; t0 < chunk; t0 += 16) fq_block_f32(Pq + t0, chunk - t0 < 16 ? chunk - t0 : 16, 1.0f);
+        double alpha = (m == -INFINITY) ? 0.0 : exp((double)m - (double)m_new);
+        double psum = 0.0;
+        for (int t = 0; t < chunk; ++t) psum += (double)P[t];
+        l = alpha * l + psum;
+        for (int d = 0; d < D; ++d) {
+            double a = 0.0, ahp = 0.0;
+            for (int t = 0; t < chunk; ++t) {
+                if (kc[t] < 0) continue;
+                double vv = (double)h->vh[kc[t] * D + d];
+                a += (double)Pq[t] * vv;
+                ahp += (double)P[t] * vv;
+            }
+            acc[d] = alpha * acc[d] + a;
+            acc_hp[d] = alpha * acc_hp[d] + ahp;
+        }
+        if (cmax) cmax[c] = m_new;
+        m = m_new;
+    }
+    for (int d = 0; d < D; ++d) {
+        if (o) o[d] = acc[d] / l;
+        if (o_hp) o_hp[d] = acc_hp[d] / l;
+    }
+    if (lse) *lse = (double)m + log(l);
+    free(S);
+    free(P);
+    free(Pq);
+    free(acc);
+    free(acc_hp);
+}
+
+/* Dense key schedule: chunk c holds keys [c*chunk, c*chunk+chunk) clipped to
+   Lk; with causal masking, keys after the query row are masked (top-left
+   alignment, Lq == Lk). */
+static int64_t *dense_keys(int64_t Lk, int chunk, int64_t i, int causal, int64_t *nchunks)
+{
+    int64_t C = (Lk + chunk - 1) / chunk;
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * C * chunk);
+    for (int64_t p = 0; p < C * chunk; ++p) {
+        int64_t j = p;
+        keys[p] = (j >= Lk || (causal && j > i)) ? -1 : j;
+    }
+    *nchunks = C;
+    return keys;
+}
+
+/* Forward for the requested query rows of every (b, h).
+   Outputs (any may be NULL), indexed [bh][r] for row rows[r]:
+     o, o_hp : [B*H, nrows, D] fp64
+     lse     : [B*H, nrows]
+     cmax    : [B*H, nrows, ceil(Lk/chunk)]                               */
+int oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int H, int64_t Lq,
+                    int64_t Lk, int D, double scale, int causal, unsigned flags, int chunk,
+                    const int64_t *rows, int64_t nrows, double *o, double *o_hp, double *lse,
+                    double *cmax)
+{
+    init_tables();
+    if (causal && Lq != Lk) return -1;
+    int64_t C = (Lk + chunk - 1) / chunk;
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        head_ops hd;
+        make_head_ops(&hd, q + bh * Lq * D, k + bh * Lk * D, v + bh * Lk * D, Lq, Lk, D, flags);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t nc;
+            int64_t *keys = dense_keys(Lk, chunk, rows[r], causal, &nc);
+            int64_t idx = bh * nrows + r;
+            row_forward(&hd, rows[r], keys, nc, chunk, D, scale, flags, o ? o + idx * D : NULL,
+                        o_hp ? o_hp + idx * D : NULL, lse ? lse + idx : NULL,
+                        cmax ? cmax + idx * C : NULL);
+            free(keys);
+        }
+        free_head_ops(&hd);
+    }
+    return 0;
+}
+
+/* Straight-through backward ([META] backward "consistent STE with auxiliary
+   output"; [API] use_qat_qkv_backward, fake_quant_p_bwd, use_high_prec_o).
+   Fake-quant nodes pass gradients unchanged and the running maxima are
+   constants, so with A = exp(S - LSE) (unquantized probabilities) and
+   Ahat = fq(exp(S - m_c)) * exp(m_c - LSE) (the probabilities the forward
+   multiplied V with):
+     D_i   = <dO_i, Ohp_i>
+     dV_j  = sum_i Ahat_ij dO_i
+     dP_ij = <dO_i, Vhat_j>
+     dS_ij = A_ij (dP_ij - D_i)
+     dQ_i  = scale sum_j dS_ij Khat_j,   dK_j = scale sum_i dS_ij Qhat_i. */
+
+typedef struct {
+    const head_ops *hd;
+    const uint16_t *dO; /* [Lq, D] bf16 of this head */
+    int64_t Lk, C;
+    int D, chunk, causal;
+    unsigned flags;
+    double scale;
+} bwd_head;
+
+/* The 16-key block that holds key j (blocks start at multiples of 16 from
+   the start of j's chunk): first key and length. */
+static void key_block(const bwd_head *x, int64_t j, int64_t *b0, int *nb)
+{
+    int64_t c0 = (j / x->chunk) * x->chunk;
+    int64_t s = c0 + ((j - c0) / 16) * 16;
+    int64_t e = s + 16;
+    if (e > c0 + x->chunk) e = c0 + x->chunk;
+    if (e > x->Lk) e = x->Lk;
+    *b0 = s;
+    *nb = (int)(e - s);
+}
+
+/* For row i with forward statistics (lse, cmax[C]) and key block [b0, b0+nb):
+   A[t] = exp(S - lse), Ahat[t] = fq(exp(S - m_c))[t] * exp(m_c - lse),
+   for the block's keys (masked keys give 0). */
+static void block_weights(const bwd_head *x, int64_t i, int64_t b0, int nb, double lse, const double *cmax,
+                          double *A, double *Ahat)
+{
+    float P[16];
+    double mc = cmax[b0 / x->chunk];
+    float S[16];
+    for (int t = 0; t < nb; ++t) {
+        int live = !(x->causal && b0 + t > i);
+        S[t] = live ? logit(x->hd, i, b0 + t, x->D, x->scale) : -INFINITY;
+        P[t] = live ? (float)exp((double)S[t] - mc) : 0.0f;
+    }
+    if (x->flags & QF_P) fq_block_f32(P, nb, 1.0f);
+    for (int t = 0; t < nb; ++t) {
+        int live = !(x->causal && b0 + t > i);
+        A[t] = live ? exp((double)S[t] - lse) : 0.0;
+        Ahat[t] = (double)P[t] * exp(mc - lse);
+    }
+}
+
+static double dot_do_v(const bwd_head *x, int64_t i, int64_t j)
+{
+    double s = 0.0;
+    for (int d = 0; d < x->D; ++d)
+        s += (double)bf16_to_f32(x->dO[i * x->D + d]) * (double)x->hd->vh[j * x->D + d];
+    return s;
+}
+
+/* Forward statistics of row i: lse, running max per chunk, and
+   D_i = <dO_i, Ohp_i>. */
+static void row_stats(const bwd_head *x, int64_t i, double *lse, double *cmax, double *Di)
+{
+    int64_t nc;
+    int64_t *keys = dense_keys(x->Lk, x->chunk, i, x->causal, &nc);
+    double *ohp = (double *)malloc(sizeof(double) * x->D);
+    row_forward(x->hd, i, keys, nc, x->chunk, x->D, x->scale, x->flags, NULL, ohp, lse, cmax);
+    double s = 0.0;
+    for (int d = 0; d < x->D; ++d) s += (double)bf16_to_f32(x->dO[i * x->D + d]) * ohp[d];
+    *Di = s;
+    free(ohp);
+    free(keys);
+}
+
+/* Computes dQ for query rows qrows and dK, dV for key rows krows, per (b,h).
+   Outputs fp64: dq [B*H, nq, D], dk/dv [B*H, nk, D]. */
+int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout, int B,
+                    int H, int64_t Lq, int64_t Lk, int D, double scale, int causal, unsigned flags,
+                    int chunk, const int64_t *qrows, int64_t nq, const int64_t *krows, int64_t nk,
+                    double *dq, double *dk, double *dv)
+{
+    init_tables();
+    if (causal && Lq != Lk) return -1;
+    int64_t C = (Lk + chunk - 1) / chunk;
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        head_ops hd;
+        make_head_ops(&hd, q + bh * Lq * D, k + bh * Lk * D, v + bh * Lk * D, Lq, Lk, D, flags);
+        bwd_head x = {&hd, dout + bh * Lq * D, Lk, C, D, chunk, causal, flags, scale};
+
+        if (dq && nq > 0) {
+#pragma omp parallel for schedule(dynamic, 1)
+            for (int64_t a = 0; a < nq; ++a) {
+                int64_t i = qrows[a];
+                double lse, Di, A[16], Ah[16];
+                double *cmax = (double *)malloc(sizeof(double) * C);
+                row_stats(&x, i, &lse, cmax, &Di);
+                double *out = dq + (bh * nq + a) * D;
+                for (int d = 0; d < D; ++d) out[d] = 0.0;
+                for (int64_t b0 = 0; b0 < Lk;) {
+                    int64_t s;
+                    int nb;
+                    key_block(&x, b0, &s, &nb);
+                    block_weights(&x, i, s, nb, lse, cmax, A, Ah);
+                    for (int t = 0; t < nb; ++t) {
+                        int64_t j = s + t;
+                        if (causal && j > i) continue;
+                        double dS = A[t] * (dot_do_v(&x, i, j) - Di);
+                        for (int d = 0; d < D; ++d) out[d] += scale * dS * (double)hd.kh[j * D + d];
+                    }
+                    b0 = s + nb;
+                }
+                free(cmax);
+            }
+        }
+
+        if (nk > 0 && (dk || dv)) {
+            /* Key gradients need every row's statistics. */
+            double *lse = (double *)malloc(sizeof(double) * Lq);
+            double *cmax = (double *)malloc(sizeof(double) * Lq * C);
+            double *Dv = (double *)malloc(sizeof(double) * Lq);
+#pragma omp parallel for schedule(dynamic, 16)
+            for (int64_t i = 0; i < Lq; ++i) row_stats(&x, i, lse + i, cmax + i * C, Dv + i);
+#pragma omp parallel for schedule(dynamic, 1)
+            for (int64_t a = 0; a < nk; ++a) {
+                int64_t j = krows[a];
+                int64_t s;
+                int nb;
+                key_block(&x, j, &s, &nb);
+                double *ok = dk ? dk + (bh * nk + a) * D : NULL;
+                double *ov = dv ? dv + (bh * nk + a) * D : NULL;
+                for (int d = 0; d < D; ++d) {
+                    if (ok) ok[d] = 0.0;
+                    if (ov) ov[d] = 0.0;
+                }
+                double A[16], Ah[16];
+                for (int64_t i = 0; i < Lq; ++i) {
+                    if (causal && j > i) continue;
+                    block_weights(&x, i, s, nb, lse[i], cmax + i * C, A, Ah);
+                    double dS = A[j - s] * (dot_do_v(&x, i, j) - Dv[i]);
+                    for (int d = 0; d < D; ++d) {
+                        if (ok) ok[d] += scale * dS * (double)hd.qh[i * D + d];
+                        if (ov) ov[d] += Ah[j - s] * (double)bf16_to_f32(x.dO[i * D + d]);
+                    }
+                }
+            }
+            free(lse);
+            free(cmax);
+            free(Dv);
+        }
+        free_head_ops(&hd);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Cube-sparse (VSA) forward.  [META] attention: kind "vsa", cube_shape
+   [4,4,8], precision.coarse "BF16", quantize_coarse false, quantize_fine
+   true, selection.effective_topk = max(1, min(ceil((1-sparsity)*n), n)).  */
+/* ------------------------------------------------------------------------ */
+
+int oracle_vsa_topk(double sparsity, int n)
+{
+    double t = ceil((1.0 - sparsity) * (double)n);
+    int k = (int)t;
+    if (k > n) k = n;
+    if (k < 1) k = 1;
+    return k;
+}
+
+/* Mean over each cube of `ct` consecutive tokens (tokens are cube-major),
+   computed in fp64 and rounded to bf16. out: [ncubes, D] bf16. */
+static void pool_cubes(const uint16_t *x, int64_t ncubes, int ct, int D, uint16_t *out)
+{
+    for (int64_t c = 0; c < ncubes; ++c)
+        for (int d = 0; d < D; ++d) {
+            double s = 0.0;
+            for (int t = 0; t < ct; ++t) s += (double)bf16_to_f32(x[(c * ct + t) * D + d]);
+            out[c * D + d] = f64_to_bf16(s / (double)ct);
+        }
+}
+
+/* Outputs per (b,h):
+     qpool, kpool, vpool : [B*H, n, D] bf16 (may be NULL)
+     score   : [B*H, n, n] fp64 coarse logits scale * <Qc, Kc> (may be NULL)
+     sel     : [B*H, n, topk] int32, selected cubes in ascending order
+     o_fine  : [B*H, nrows, D] fp64 for the query rows `rows`
+     o_coarse: [B*H, nrows, D] fp64 softmax(score) @ Vc of the row's cube
+   The fine stage reuses the dense forward with the selected cubes' keys in
+   ascending cube order, one chunk per cube. */
+int oracle_vsa_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int H, int64_t L, int D,
+                   int cube_tokens, double sparsity, double scale, unsigned flags, const int64_t *rows,
+                   int64_t nrows, uint16_t *qpool, uint16_t *kpool, uint16_t *vpool, double *score,
+                   int32_t *sel, double *o_fine, double *o_coarse)
+{
+    init_tables();
+    if (L % cube_tokens) return -1;
+    int64_t n = L / cube_tokens;
+    int topk = oracle_vsa_topk(sparsity, (int)n);
+    uint16_t *qp = (uint16_t *)malloc(2 * n * D), *kp = (uint16_t *)malloc(2 * n * D),
+             *vp = (uint16_t *)malloc(2 * n * D);
+    double *sc = (double *)malloc(sizeof(double) * n * n);
+    int32_t *sl = (int32_t *)malloc(sizeof(int32_t) * n * topk);
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const uint16_t *qh = q + bh * L * D, *kh = k + bh * L * D, *vh = v + bh * L * D;
+        pool_cubes(qh, n, cube_tokens, D, qp);
+        pool_cubes(kh, n, cube_tokens, D, kp);
+        pool_cubes(vh, n, cube_tokens, D, vp);
+        for (int64_t a = 0; a < n; ++a)
+            for (int64_t b = 0; b < n; ++b) {
+                double s = 0.0;
+                for (int d = 0; d < D; ++d) s += (double)bf16_to_f32(qp[a * D + d]) * (double)bf16_to_f32(kp[b * D + d]);
+                sc[a * n + b] = scale * s;
+            }
+        /* Top-k by coarse score, ties to the lower cube index; then the
+           selected cubes are listed in ascending order. */
+        for (int64_t a = 0; a < n; ++a) {
+            char *taken = (char *)calloc(n, 1);
+            for (int t = 0; t < topk; ++t) {
+                int64_t best = -1;
+                for (int64_t b = 0; b < n; ++b)
+                    if (!taken[b] && (best < 0 || sc[a * n + b] > sc[a * n + best])) best = b;
+                taken[best] = 1;
+            }
+            int t = 0;
+            for (int64_t b = 0; b < n; ++b)
+                if (taken[b]) sl[a * topk + t++] = (int32_t)b;
+            free(taken);
+        }
+        if (qpool) memcpy(qpool + bh * n * D, qp, 2 * n * D);
+        if (kpool) memcpy(kpool + bh * n * D, kp, 2 * n * D);
+        if (vpool) memcpy(vpool + bh * n * D, vp, 2 * n * D);
+        if (score) memcpy(score + bh * n * n, sc, sizeof(double) * n * n);
+        if (sel) memcpy(sel + bh * n * topk, sl, sizeof(int32_t) * n * topk);
+
+        head_ops hd;
+        make_head_ops(&hd, qh, kh, vh, L, L, D, flags);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t i = rows[r];
+            int64_t a = i / cube_tokens;
+            int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * topk * cube_tokens);
+            for (int t = 0; t < topk; ++t)
+                for (int u = 0; u < cube_tokens; ++u)
+                    keys[t * cube_tokens + u] = (int64_t)sl[a * topk + t] * cube_tokens + u;
+            if (o_fine)
+                row_forward(&hd, i, keys, topk, cube_tokens, D, scale, flags, o_fine + (bh * nrows + r) * D,
+                            NULL, NULL, NULL);
+            if (o_coarse) {
+                double mx = -INFINITY, l = 0.0;
+                for (int64_t b = 0; b < n; ++b)
+                    if (sc[a * n + b] > mx) mx = sc[a * n + b];
+                double *out = o_coarse + (bh * nrows + r) * D;
+                for (int d = 0; d < D; ++d) out[d] = 0.0;
+                for (int64_t b = 0; b < n; ++b) {
+                    double p = exp(sc[a * n + b] - mx);
+                    l += p;
+                    for (int d = 0; d < D; ++d) out[d] += p * (double)bf16_to_f32(vp[b * D + d]);
+                }
+                for (int d = 0; d < D; ++d) out[d] /= l;
+            }
+            free(keys);
+        }
+        free_head_ops(&hd);
+    }
+    free(qp);
+    free(kp);
+    free(vp);
+    free(sc);
+    free(sl);
+    return topk;
+}
