@@ -1,0 +1,182 @@
+/*
+ * attnqat.h - C ABI of the MI355X (gfx950) NVFP4 fake-quantized attention library.
+ *
+ * The operations follow these web pages (cited by title and section):
+ *   [API]  "attn_qat_train" API reference page (fastvideo.attention.backends.attn_qat_train):
+ *          attn_qat_train(q_BLHD, k_BLHD, v_BLHD, is_causal, sm_scale), its fixed kernel flags
+ *          (use_qat_qkv_backward, fake_quant_p_bwd, use_high_prec_o, unit global scales),
+ *          AttnQatTrainBackend.get_supported_head_sizes() == [128], AttnQatTrainImpl (dropout
+ *          refused), AttentionImpl(num_heads, head_size, softmax_scale, causal, num_kv_heads).
+ *   [DOC]  "Attn-QAT Training" guide: "Prerequisites" (fail instead of falling back to dense
+ *          attention), "Architecture-specific Triton routing" (query and key/value lengths may
+ *          differ; key and value lengths must match).
+ *   [QAD]  "nvfp4_qad.py" source page: module docstring (per-16 E4M3 block scales under a unit or
+ *          static global scale), FP4_RANGE = 448*6, weight_global_sf / input_global_sf.
+ *   [META] "vsqa-preview-1.3b metadata.json": attention.precision (NVFP4 fake-quant with BF16
+ *          matmul; quant_p, quant_v; coarse BF16, quantize_coarse false), attention.selection
+ *          (effective_topk formula), attention.cube_shape [4,4,8]; the dense parent's precision
+ *          record (group_size 16, E2M1 values, FP8 E4M3FN scales, backward "consistent STE with
+ *          auxiliary output").
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE memory owned by the caller.  The library never allocates or
+ *     frees memory and keeps no pointer after the call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).  No call
+ *     synchronises the host; results are ready when the stream reaches them.
+ *   - bf16 tensors are IEEE bfloat16 bit patterns; fp32 tensors are IEEE binary32.
+ *   - Attention tensors are 4-D with a contiguous head dimension D = 128.  Their layout is given
+ *     by element strides {b, h, l} (batch, head, token), so both the pages' public [B, L, H, D]
+ *     layout and the kernel-side [B, H, L, D] layout are accepted without copies.
+ *   - Return value: AQ_OK (0) on success, a negative code on failure.  On failure nothing has
+ *     been enqueued and aq_last_error() returns a message (thread-local, valid until the next
+ *     call on the same thread).  Argument checks run on the host before any launch.
+ *   - Calls that overlap on one stream are ordered by the stream; the library holds no state
+ *     between calls, so calls on different streams are independent when their buffers are.
+ */
+#ifndef ATTNQAT_H
+#define ATTNQAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    AQ_OK = 0,
+    AQ_EINVAL = -1,  /* malformed argument: null pointer, size, stride, scale, flag, workspace */
+    AQ_ENOTSUP = -2, /* well-formed but outside what the kernels implement */
+    AQ_EHIP = -3     /* a HIP launch failed */
+};
+
+/* Which operands are fake-quantized ([API] is_qat with unit global scales; [META] quant_p,
+   quant_v).  AQ_QUANT_ALL is the pages' configuration. */
+enum {
+    AQ_QUANT_Q = 1, /* Q in 16-element blocks along D */
+    AQ_QUANT_K = 2, /* K in 16-element blocks along D */
+    AQ_QUANT_V = 4, /* V in 16-element blocks along the key axis */
+    AQ_QUANT_P = 8, /* softmax probabilities in 16-key blocks along the key axis */
+    AQ_QUANT_ALL = 15
+};
+
+/* Element strides of a 4-D attention tensor, indexed (batch, head, token, d) with d contiguous. */
+typedef struct {
+    int64_t b, h, l;
+} aq_strides;
+
+/* Message describing the most recent failure on this thread ("" if none). */
+const char *aq_last_error(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * fq_nvfp4 - standalone NVFP4 fake quantization ([QAD] module docstring; [META] group_size 16,
+ * E2M1 values, FP8 E4M3FN block scales).
+ *
+ * x, y   : bf16 tensors viewed as [outer, axis_len, inner], row-major and contiguous; y may equal
+ *          x (in place).  Blocks are 16 consecutive positions along `axis`; the last block of an
+ *          axis whose length is not a multiple of 16 is shorter.
+ * global_scale : NULL for the unit global scale g = 1 (the attention setting), or a DEVICE
+ *          pointer to one fp32 g (for instance from fq_nvfp4_static_scale).
+ * Per block with abs-max a: s = E4M3(fp32(fp32(a/6)*g)) (round to nearest, ties to even,
+ * saturating at 448, subnormals kept), S = fp32(s/g); each element becomes
+ * bf16(sign(x) * E2M1(fp32(|x|/S)) * S), E2M1 rounding to nearest with ties to the even code and
+ * saturating at 6; a block whose S is 0 becomes signed zeros.
+ * Errors: AQ_EINVAL for null x/y or non-positive sizes.
+ * ------------------------------------------------------------------------------------------- */
+int fq_nvfp4(const void *x, void *y, int64_t outer, int64_t axis_len, int64_t inner,
+             const float *global_scale, void *stream);
+
+/* Static global scale ([QAD] weight_global_sf and input_global_sf):
+ * *g_out = fp32(448*6 / max(a, 1e-12)) with a = max |x| over the n bf16 elements of x (NaN read
+ * as 0).  g_out is a DEVICE pointer to one fp32.  Errors: AQ_EINVAL for null pointers or n <= 0. */
+int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * attn_qat_fwd - fake-quantized attention forward ([API] attn_qat_train; [META] "NVFP4
+ * fake-quant with BF16 matmul").
+ *
+ * q [B, H, lq, 128], k and v [B, H, lk, 128], o [B, H, lq, 128]: bf16, layout by strides.
+ * Q-hat, K-hat along D and V-hat along keys are fake-quantized per quant_flags.  The keys are
+ * visited in chunks of 128 ([0,128), [128,256), ...); in chunk c the running row maximum m_c of
+ * the logits softmax_scale * <q-hat, k-hat> is refreshed first, then P = exp(logit - m_c) is
+ * formed, fake-quantized in 16-key blocks (AQ_QUANT_P) and multiplied with V-hat on BF16 MFMA;
+ * the denominator sums the unquantized P.  o = acc / l rounded to bf16.
+ * softmax_scale : finite and > 0 ([API] default 1/sqrt(D) is applied by the caller).
+ * causal        : top-left causal mask; requires lq == lk.
+ * Optional training outputs (any may be NULL; all three are needed by attn_qat_bwd):
+ *   lse_log2       [B, H, lq] fp32 contiguous: log2 of the softmax denominator in base-2 logit
+ *                  units, i.e. log2(e) * (m + ln l) with m the final row maximum.
+ *   chunk_max_log2 [B, H, ceil(lk/128), lq] fp32 contiguous: log2(e) * m_c after each chunk
+ *                  (entries of chunks a causal row never reaches are left unwritten).
+ *   o_hp           [B, H, lq, 128] fp32 contiguous: the auxiliary high-precision output with
+ *                  unquantized P ([API] use_high_prec_o).
+ * workspace : DEVICE scratch of at least attn_qat_workspace_size(0, ...) bytes, 256-byte aligned.
+ * Errors: AQ_EINVAL (null q/k/v/o/workspace, head_size != 128 [API]
+ * get_supported_head_sizes, sizes <= 0, non-finite or non-positive softmax_scale, flags outside
+ * AQ_QUANT_ALL, strides that are not positive, workspace too small); AQ_ENOTSUP
+ * (num_kv_heads != num_heads, causal with lq != lk).
+ * ------------------------------------------------------------------------------------------- */
+int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch, int num_heads,
+                 int num_kv_heads, int head_size, int64_t lq, int64_t lk, aq_strides sq,
+                 aq_strides sk, aq_strides sv, aq_strides so, float softmax_scale, int causal,
+                 unsigned quant_flags, float *lse_log2, float *chunk_max_log2, float *o_hp,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * attn_qat_bwd - straight-through backward ([META] backward "consistent STE with auxiliary
+ * output"; [API] use_qat_qkv_backward, fake_quant_p_bwd, use_high_prec_o).
+ *
+ * Fake-quant nodes pass gradients unchanged and the chunk maxima are constants.  With
+ * A = exp(logit - lse) and A-hat = fq(exp(logit - m_c)) * exp(m_c - lse) (bit-for-bit the P-hat
+ * the forward used): D_i = <dO_i, o_hp_i>, dV = A-hat^T dO, dP = dO V-hat^T,
+ * dS = A * (dP - D), dQ = scale dS K-hat, dK = scale dS^T Q-hat.
+ * Inputs q, k, v, d_o (bf16, strided as in the forward) and o_hp, lse_log2, chunk_max_log2
+ * exactly as written by attn_qat_fwd with the same arguments; outputs dq, dk, dv bf16 with
+ * their own strides.  workspace: at least attn_qat_workspace_size(1, ...) bytes.
+ * Errors: as attn_qat_fwd, plus AQ_EINVAL for any null gradient or statistics pointer.
+ * ------------------------------------------------------------------------------------------- */
+int attn_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp, const void *d_o,
+                 const float *lse_log2, const float *chunk_max_log2, void *dq, void *dk, void *dv,
+                 int batch, int num_heads, int num_kv_heads, int head_size, int64_t lq,
+                 int64_t lk, aq_strides sq, aq_strides sk, aq_strides sv, aq_strides sdo,
+                 aq_strides sdq, aq_strides sdk, aq_strides sdv, float softmax_scale, int causal,
+                 unsigned quant_flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * vsa_qat_fwd - cube-sparse fake-quant attention forward ([META] attention kind "vsa",
+ * cube_shape [4,4,8], coarse "BF16" not quantized, fine "NVFP4 fake-quant with BF16 matmul",
+ * selection effective_topk = max(1, min(ceil((1-sparsity)*n), n))).
+ *
+ * Tokens are cube-major: the grid grid_t x grid_h x grid_w is cut into cubes of
+ * cube_t x cube_h x cube_w tokens and each cube's tokens are contiguous along l (cube index
+ * raster order over the cube grid).  n = number of cubes.
+ *   1. Qc, Kc (and Vc when o_coarse is requested) = per-cube means in fp32, rounded to bf16.
+ *   2. coarse logits softmax_scale * <Qc, Kc>; each query cube keeps the topk highest-scoring
+ *      key cubes (ties to the lower cube index), listed in ascending cube order.
+ *   3. fine stage: the dense forward restricted to the selected cubes' keys, visited in that
+ *      ascending order with one 128-key chunk per cube.
+ * o_fine [B, H, L, 128] bf16 (strides so); o_coarse (NULL allowed) receives
+ * softmax(coarse logits) @ Vc broadcast to every token of the query cube, bf16, strides so;
+ * sel (NULL allowed) receives the [B, H, n, topk] int32 selection.
+ * workspace: at least attn_qat_workspace_size(2, ...) bytes with lk = L.
+ * Errors: AQ_EINVAL (as the forward, plus grid sizes not divisible by the cube, L !=
+ * grid_t*grid_h*grid_w, sparsity outside [0,1]); AQ_ENOTSUP (cube of other than 128 tokens).
+ * ------------------------------------------------------------------------------------------- */
+int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void *o_coarse,
+                int32_t *sel, int batch, int num_heads, int head_size, int64_t seq_len,
+                int grid_t, int grid_h, int grid_w, int cube_t, int cube_h, int cube_w,
+                double sparsity, aq_strides sq, aq_strides sk, aq_strides sv, aq_strides so,
+                float softmax_scale, unsigned quant_flags, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Number of cubes kept per query cube: max(1, min(ceil((1 - sparsity) * n), n)). */
+int vsa_topk(double sparsity, int n_cubes);
+
+/* Workspace bytes needed by op 0 = attn_qat_fwd, 1 = attn_qat_bwd, 2 = vsa_qat_fwd (lk = L). */
+size_t attn_qat_workspace_size(int op, int batch, int num_heads, int64_t lq, int64_t lk);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNQAT_H */

@@ -145,6 +145,13 @@ static float fq_elem(float x, float S)
     return copysignf(y, x);
 }
 
+/* Exported for element-level checks: one value with a given block scale. */
+float oracle_fq_value(float x, float S)
+{
+    init_tables();
+    return fq_elem(x, S);
+}
+
 /* Fake-quantize one block of n (<= 16) fp32 values in place. */
 static void fq_block_f32(float *x, int n, float g)
 {
@@ -163,10 +170,11 @@ void oracle_fq_bf16(const uint16_t *x, uint16_t *y, int64_t outer, int64_t axis,
                     float g)
 {
     init_tables();
-    float buf[16];
+#pragma omp parallel for schedule(static)
     for (int64_t o = 0; o < outer; ++o)
         for (int64_t a0 = 0; a0 < axis; a0 += 16) {
             int n = (int)((axis - a0) < 16 ? (axis - a0) : 16);
+            float buf[16];
             for (int64_t in = 0; in < inner; ++in) {
                 for (int i = 0; i < n; ++i)
                     buf[i] = bf16_to_f32(x[(o * axis + a0 + i) * inner + in]);

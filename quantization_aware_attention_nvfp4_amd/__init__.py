@@ -1,0 +1,18 @@
+"""MI355X (gfx950) NVFP4 fake-quantized attention (Attn-QAT).
+
+The computation lives in ``libattnqat.so`` (hand-written HIP kernels behind the
+C ABI of ``include/attnqat.h``); this package is a thin torch binding over it.
+Importing the package loads the library and fails with ImportError when it is
+missing: there is no fallback path.
+"""
+from ._lib import load as _load
+
+_load()
+
+from .ops import (AQ_QUANT_ALL, AQ_QUANT_K, AQ_QUANT_P, AQ_QUANT_Q, AQ_QUANT_V,  # noqa: E402
+                  AttnQatTrainImpl, attn_qat_bwd, attn_qat_fwd, attn_qat_train, fq_nvfp4,
+                  static_global_scale, vsa_qat_fwd, vsa_topk)
+
+__all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "fq_nvfp4",
+           "static_global_scale", "attn_qat_fwd", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
+           "vsa_qat_fwd", "vsa_topk"]

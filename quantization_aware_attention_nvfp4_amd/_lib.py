@@ -1,0 +1,89 @@
+"""ctypes loader for libattnqat.so (the C ABI declared in include/attnqat.h).
+
+The library is required: there is no fallback.  Like the pages' ATTN_QAT_TRAIN
+backend ("Attn-QAT Training" guide, "Prerequisites": it fails instead of falling
+back to dense attention when its kernel cannot be loaded), a missing or broken
+library raises ImportError carrying the original error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattnqat.so")
+
+AQ_OK, AQ_EINVAL, AQ_ENOTSUP, AQ_EHIP = 0, -1, -2, -3
+AQ_QUANT_Q, AQ_QUANT_K, AQ_QUANT_V, AQ_QUANT_P = 1, 2, 4, 8
+AQ_QUANT_ALL = 15
+
+EXPORTED = ("aq_last_error", "fq_nvfp4", "fq_nvfp4_static_scale", "attn_qat_fwd", "attn_qat_bwd",
+            "vsa_qat_fwd", "vsa_topk", "attn_qat_workspace_size")
+
+
+class aq_strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("l", ctypes.c_int64)]
+
+
+_lib = None
+_load_error = None
+
+
+def _declare(lib):
+    P, i32, i64, f32, f64, u32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                      ctypes.c_double, ctypes.c_uint, ctypes.c_size_t)
+    S = aq_strides
+    lib.aq_last_error.argtypes = []
+    lib.aq_last_error.restype = ctypes.c_char_p
+    lib.fq_nvfp4.argtypes = [P, P, i64, i64, i64, P, P]
+    lib.fq_nvfp4.restype = i32
+    lib.fq_nvfp4_static_scale.argtypes = [P, i64, P, P]
+    lib.fq_nvfp4_static_scale.restype = i32
+    lib.attn_qat_fwd.argtypes = [P, P, P, P, i32, i32, i32, i32, i64, i64, S, S, S, S, f32, i32, u32,
+                                 P, P, P, P, sz, P]
+    lib.attn_qat_fwd.restype = i32
+    lib.attn_qat_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i64, i64, S, S, S,
+                                 S, S, S, S, f32, i32, u32, P, sz, P]
+    lib.attn_qat_bwd.restype = i32
+    lib.vsa_qat_fwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i64, i32, i32, i32, i32, i32, i32,
+                                f64, S, S, S, S, f32, u32, P, sz, P]
+    lib.vsa_qat_fwd.restype = i32
+    lib.vsa_topk.argtypes = [f64, i32]
+    lib.vsa_topk.restype = i32
+    lib.attn_qat_workspace_size.argtypes = [i32, i32, i32, i64, i64]
+    lib.attn_qat_workspace_size.restype = sz
+
+
+def load():
+    """Load the shared library once; raise ImportError if it is missing or broken."""
+    global _lib, _load_error
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libattnqat.so not found at {LIB_PATH}; build it with "
+                          "quantization_aware_attention_nvfp4_amd.build.build() "
+                          "(there is no fallback implementation)")
+    try:
+        lib = ctypes.CDLL(LIB_PATH)
+        _declare(lib)
+    except OSError as e:  # pragma: no cover - depends on the machine
+        _load_error = e
+        raise ImportError(f"libattnqat.so could not be loaded: {e}") from e
+    _lib = lib
+    return lib
+
+
+class AttnQatError(RuntimeError):
+    pass
+
+
+def check(rc: int, what: str) -> None:
+    """Map a C return code onto a Python exception."""
+    if rc == AQ_OK:
+        return
+    msg = load().aq_last_error().decode(errors="replace")
+    if rc == AQ_EINVAL:
+        raise ValueError(f"{what}: {msg}")
+    if rc == AQ_ENOTSUP:
+        raise NotImplementedError(f"{what}: {msg}")
+    raise AttnQatError(f"{what}: {msg} (code {rc})")

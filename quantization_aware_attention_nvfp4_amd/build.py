@@ -1,0 +1,67 @@
+"""Builds libattnqat.so (the C-ABI of include/attnqat.h) for gfx950 with hipcc.
+
+Every HIP source is compiled ahead of time, in-tree, into
+``quantization_aware_attention_nvfp4_amd/libattnqat.so``; nothing is compiled at
+run time.  Flags:
+  * ``--offload-arch=gfx950``: MI355X only;
+  * ``-ffp-contract=off``: fp32 arithmetic is exactly what the source writes
+    (fused multiply-adds only where the code calls ``__builtin_fmaf``);
+  * ``-Xclang -target-feature -Xclang -packed-fp32-ops``: no packed fp32 VALU
+    instructions are generated.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libattnqat.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", INCLUDE, "-I", CSRC]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "abi.cpp")]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    cmd = [HIPCC] + COMMON + lang + ["-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

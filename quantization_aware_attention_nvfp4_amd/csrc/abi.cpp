@@ -1,0 +1,198 @@
+// abi.cpp - the extern "C" surface declared in include/attnqat.h: argument validation, error
+// reporting and dispatch to the gfx950 launchers.  Every check runs on the host before anything
+// is enqueued, so a rejected call leaves the stream untouched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "attnqat.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return AQ_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(AQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+aq::Strides cvt(aq_strides s) { return aq::Strides{s.b, s.h, s.l}; }
+
+bool strides_ok(aq_strides s) { return s.b > 0 && s.h > 0 && s.l > 0; }
+
+// Checks shared by the attention entry points ("attn_qat_train" page: head sizes [128],
+// AttentionImpl(num_heads, head_size, softmax_scale, causal, num_kv_heads)).
+int check_attention(int batch, int num_heads, int num_kv_heads, int head_size, int64_t lq,
+                    int64_t lk, float softmax_scale, int causal, unsigned quant_flags) {
+  if (head_size != aq::kHeadDimHost)
+    return fail(AQ_EINVAL, "head_size %d is not supported (supported: 128)", head_size);
+  if (batch <= 0 || num_heads <= 0 || lq <= 0 || lk <= 0)
+    return fail(AQ_EINVAL, "sizes must be positive (batch %d, heads %d, lq %lld, lk %lld)", batch,
+                num_heads, (long long)lq, (long long)lk);
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
+    return fail(AQ_EINVAL, "softmax_scale must be finite and > 0 (got %g)", (double)softmax_scale);
+  if (quant_flags & ~(unsigned)AQ_QUANT_ALL)
+    return fail(AQ_EINVAL, "quant_flags 0x%x has bits outside AQ_QUANT_ALL", quant_flags);
+  if (num_kv_heads != num_heads)
+    return fail(AQ_ENOTSUP, "num_kv_heads (%d) must equal num_heads (%d)", num_kv_heads, num_heads);
+  if (causal && lq != lk)
+    return fail(AQ_ENOTSUP, "causal attention needs lq == lk (got %lld, %lld)", (long long)lq,
+                (long long)lk);
+  return AQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *aq_last_error(void) { return g_err; }
+
+int fq_nvfp4(const void *x, void *y, int64_t outer, int64_t axis_len, int64_t inner,
+             const float *global_scale, void *stream) {
+  if (!x || !y) return fail(AQ_EINVAL, "fq_nvfp4: null tensor pointer");
+  if (outer <= 0 || axis_len <= 0 || inner <= 0)
+    return fail(AQ_EINVAL, "fq_nvfp4: sizes must be positive (%lld, %lld, %lld)", (long long)outer,
+                (long long)axis_len, (long long)inner);
+  return hip_status(aq::launch_fq(x, y, outer, axis_len, inner, global_scale, (hipStream_t)stream),
+                    "fq_nvfp4 launch");
+}
+
+int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream) {
+  if (!x || !g_out) return fail(AQ_EINVAL, "fq_nvfp4_static_scale: null pointer");
+  if (n <= 0) return fail(AQ_EINVAL, "fq_nvfp4_static_scale: n must be positive");
+  return hip_status(aq::launch_static_scale(x, n, g_out, (hipStream_t)stream),
+                    "fq_nvfp4_static_scale launch");
+}
+
+int vsa_topk(double sparsity, int n_cubes) {
+  if (n_cubes <= 0 || !(sparsity >= 0.0 && sparsity <= 1.0)) return 0;
+  const double t = ceil((1.0 - sparsity) * (double)n_cubes);
+  int k = (int)t;
+  if (k > n_cubes) k = n_cubes;
+  if (k < 1) k = 1;
+  return k;
+}
+
+size_t attn_qat_workspace_size(int op, int batch, int num_heads, int64_t lq, int64_t lk) {
+  if (batch <= 0 || num_heads <= 0 || lq <= 0 || lk <= 0 || op < 0 || op > 2) return 0;
+  return aq::workspace_bytes(op, batch, num_heads, lq, lk);
+}
+
+int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch, int num_heads,
+                 int num_kv_heads, int head_size, int64_t lq, int64_t lk, aq_strides sq,
+                 aq_strides sk, aq_strides sv, aq_strides so, float softmax_scale, int causal,
+                 unsigned quant_flags, float *lse_log2, float *chunk_max_log2, float *o_hp,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o) return fail(AQ_EINVAL, "attn_qat_fwd: null tensor pointer");
+  int rc = check_attention(batch, num_heads, num_kv_heads, head_size, lq, lk, softmax_scale, causal,
+                           quant_flags);
+  if (rc) return rc;
+  if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so))
+    return fail(AQ_EINVAL, "attn_qat_fwd: strides must be positive with d contiguous");
+  const size_t need = aq::workspace_bytes(0, batch, num_heads, lq, lk);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
+    return fail(AQ_EINVAL, "attn_qat_fwd: workspace must be 256-byte aligned and hold %zu bytes",
+                need);
+  aq::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.batch = batch; a.heads = num_heads; a.lq = lq; a.lk = lk;
+  a.sq = cvt(sq); a.sk = cvt(sk); a.sv = cvt(sv); a.so = cvt(so);
+  a.scale = softmax_scale; a.causal = causal != 0; a.flags = quant_flags;
+  a.lse = lse_log2; a.cmax = chunk_max_log2; a.o_hp = o_hp;
+  a.workspace = workspace;
+  return hip_status(aq::launch_attn_fwd(a, (hipStream_t)stream), "attn_qat_fwd launch");
+}
+
+int attn_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp, const void *d_o,
+                 const float *lse_log2, const float *chunk_max_log2, void *dq, void *dk, void *dv,
+                 int batch, int num_heads, int num_kv_heads, int head_size, int64_t lq,
+                 int64_t lk, aq_strides sq, aq_strides sk, aq_strides sv, aq_strides sdo,
+                 aq_strides sdq, aq_strides sdk, aq_strides sdv, float softmax_scale, int causal,
+                 unsigned quant_flags, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !d_o || !dq || !dk || !dv)
+    return fail(AQ_EINVAL, "attn_qat_bwd: null tensor pointer");
+  if (!o_hp || !lse_log2 || !chunk_max_log2)
+    return fail(AQ_EINVAL, "attn_qat_bwd: o_hp, lse_log2 and chunk_max_log2 are required");
+  int rc = check_attention(batch, num_heads, num_kv_heads, head_size, lq, lk, softmax_scale, causal,
+                           quant_flags);
+  if (rc) return rc;
+  if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(sdo) ||
+      !strides_ok(sdq) || !strides_ok(sdk) || !strides_ok(sdv))
+    return fail(AQ_EINVAL, "attn_qat_bwd: strides must be positive with d contiguous");
+  const size_t need = aq::workspace_bytes(1, batch, num_heads, lq, lk);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
+    return fail(AQ_EINVAL, "attn_qat_bwd: workspace must be 256-byte aligned and hold %zu bytes",
+                need);
+  aq::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.batch = batch; a.heads = num_heads; a.lq = lq; a.lk = lk;
+  a.sq = cvt(sq); a.sk = cvt(sk); a.sv = cvt(sv);
+  a.scale = softmax_scale; a.causal = causal != 0; a.flags = quant_flags;
+  a.lse = const_cast<float *>(lse_log2); a.cmax = const_cast<float *>(chunk_max_log2);
+  a.o_hp = const_cast<float *>(o_hp);
+  a.workspace = workspace;
+  aq::BwdArgs b{};
+  b.d_o = d_o; b.dq = dq; b.dk = dk; b.dv = dv;
+  b.sdo = cvt(sdo); b.sdq = cvt(sdq); b.sdk = cvt(sdk); b.sdv = cvt(sdv);
+  return hip_status(aq::launch_attn_bwd(a, b, (hipStream_t)stream), "attn_qat_bwd launch");
+}
+
+int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void *o_coarse,
+                int32_t *sel, int batch, int num_heads, int head_size, int64_t seq_len,
+                int grid_t, int grid_h, int grid_w, int cube_t, int cube_h, int cube_w,
+                double sparsity, aq_strides sq, aq_strides sk, aq_strides sv, aq_strides so,
+                float softmax_scale, unsigned quant_flags, void *workspace, size_t workspace_bytes,
+                void *stream) {
+  if (!q || !k || !v || !o_fine) return fail(AQ_EINVAL, "vsa_qat_fwd: null tensor pointer");
+  int rc = check_attention(batch, num_heads, num_heads, head_size, seq_len, seq_len, softmax_scale,
+                           0, quant_flags);
+  if (rc) return rc;
+  if (grid_t <= 0 || grid_h <= 0 || grid_w <= 0 || cube_t <= 0 || cube_h <= 0 || cube_w <= 0)
+    return fail(AQ_EINVAL, "vsa_qat_fwd: grid and cube sizes must be positive");
+  if (grid_t % cube_t || grid_h % cube_h || grid_w % cube_w)
+    return fail(AQ_EINVAL, "vsa_qat_fwd: grid %dx%dx%d is not divisible by cube %dx%dx%d", grid_t,
+                grid_h, grid_w, cube_t, cube_h, cube_w);
+  if ((int64_t)grid_t * grid_h * grid_w != seq_len)
+    return fail(AQ_EINVAL, "vsa_qat_fwd: seq_len %lld != grid_t*grid_h*grid_w", (long long)seq_len);
+  if (!(sparsity >= 0.0 && sparsity <= 1.0))
+    return fail(AQ_EINVAL, "vsa_qat_fwd: sparsity must lie in [0, 1] (got %g)", sparsity);
+  if (cube_t * cube_h * cube_w != aq::kChunkHost)
+    return fail(AQ_ENOTSUP, "vsa_qat_fwd: cubes of %d tokens are not supported (only 128)",
+                cube_t * cube_h * cube_w);
+  if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so))
+    return fail(AQ_EINVAL, "vsa_qat_fwd: strides must be positive with d contiguous");
+  const size_t need = aq::workspace_bytes(2, batch, num_heads, seq_len, seq_len);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
+    return fail(AQ_EINVAL, "vsa_qat_fwd: workspace must be 256-byte aligned and hold %zu bytes",
+                need);
+  aq::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o_fine;
+  a.batch = batch; a.heads = num_heads; a.lq = seq_len; a.lk = seq_len;
+  a.sq = cvt(sq); a.sk = cvt(sk); a.sv = cvt(sv); a.so = cvt(so);
+  a.scale = softmax_scale; a.causal = false; a.flags = quant_flags;
+  a.workspace = workspace;
+  aq::VsaArgs s{};
+  s.o_coarse = o_coarse; s.sel = sel;
+  s.n_cubes = (int)(seq_len / aq::kChunkHost);
+  s.topk = vsa_topk(sparsity, s.n_cubes);
+  return hip_status(aq::launch_vsa_fwd(a, s, (hipStream_t)stream), "vsa_qat_fwd launch");
+}
+
+}  // extern "C"

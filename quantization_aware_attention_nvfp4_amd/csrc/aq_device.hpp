@@ -1,0 +1,126 @@
+// aq_device.hpp - device helpers shared by the gfx950 kernels: bf16 packing, the NVFP4 codec
+// and MFMA operand types.
+//
+// Format ("vsqa-preview-1.3b metadata.json", dense precision record: group_size 16, qk/pv_format
+// NVFP4 E2M1, qk/pv_scale_dtype FP8 E4M3FN; "nvfp4_qad.py" module docstring: per-16 E4M3 block
+// scales under a unit or static global scale, FP4_RANGE = 448*6).
+//
+// Every function here is __host__ __device__ so the arithmetic can be checked exhaustively on the
+// CPU; the CPU and gfx950 both round fp32 add/mul/fma/div to nearest-even, so results agree bit
+// for bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aq {
+
+constexpr int kHeadDim = 128;  // the only supported head size ("attn_qat_train" page,
+                               // get_supported_head_sizes)
+constexpr int kBlock = 16;     // fake-quant block length
+constexpr int kChunk = 128;    // keys per online-softmax chunk
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__host__ __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// bf16 bits <-> fp32.  The round-to-nearest-even conversion is only used where the kernels need
+// it outside the packed hardware conversion.
+__host__ __device__ __forceinline__ float bf16lo(uint32_t w) { return u2f(w << 16); }
+__host__ __device__ __forceinline__ float bf16hi(uint32_t w) { return u2f(w & 0xFFFF0000u); }
+__host__ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = f2u(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+// Two fp32 values whose bf16 rounding is exact (every fake-quantized value is): truncate.
+__host__ __device__ __forceinline__ uint32_t pack_exact_bf16(float lo, float hi) {
+  return (f2u(lo) >> 16) | (f2u(hi) & 0xFFFF0000u);
+}
+
+// Round v >= 0 (finite) to the nearest FP8 E4M3FN value: 3 mantissa bits, smallest normal
+// exponent -6 (subnormals are multiples of 2^-9), ties to even, saturating at 448.
+// Adding c = 2^(max(e, -6) + 20), e the exponent of v, leaves exactly the bits of v above
+// 2^(max(e,-6)-3) after the fp32 round-to-nearest-even; subtracting c restores the value.
+__host__ __device__ __forceinline__ float round_e4m3(float v) {
+  uint32_t e = f2u(v) & 0x7F800000u;
+  e = e > 0x3C800000u ? e : 0x3C800000u;  // 2^-6
+  const float c = u2f(e + (20u << 23));
+  const float r = (v + c) - c;
+  return r < 448.0f ? r : 448.0f;
+}
+
+// Round r >= 0 to the nearest E2M1 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6}: one mantissa bit,
+// smallest normal exponent 0 (step 0.5 below 2), ties to the even code, saturating at 6.
+// Same construction with c = 2^(max(e, 0) + 22): the grid step is 0.5 on [0,2), 1 on [2,4) and 2
+// on [4,8); the even multiple of the step is the even code.
+__host__ __device__ __forceinline__ float round_e2m1(float r) {
+  uint32_t e = f2u(r) & 0x7F800000u;
+  e = e > 0x3F800000u ? e : 0x3F800000u;  // 2^0
+  const float c = u2f(e + (22u << 23));
+  const float y = (r + c) - c;
+  return y < 6.0f ? y : 6.0f;
+}
+
+// fp32(a / 6) without a division: q0 = a * RN(1/6), one Markstein correction.  Equal to the
+// IEEE quotient for every fp32 a >= 2^-120; below that both round to the E4M3 scale 0 (checked
+// exhaustively on the host).
+__host__ __device__ __forceinline__ float div6(float a) {
+  const float inv6 = 0.16666667163372039794921875f;  // RN(1/6)
+  const float q0 = a * inv6;
+  const float rem = __builtin_fmaf(-q0, 6.0f, a);
+  return __builtin_fmaf(rem, inv6, q0);
+}
+
+// fp32(x / S) for an E4M3 value S > 0 given inv = fp32(1 / S): one Markstein correction.
+// Equal to the IEEE quotient for every such S and every non-negative fp32 x whose quotient is
+// below 2^64 (checked exhaustively on the host over the 8 significands of S).
+__host__ __device__ __forceinline__ float div_e4m3(float x, float S, float inv) {
+  const float q0 = x * inv;
+  const float rem = __builtin_fmaf(-q0, S, x);
+  return __builtin_fmaf(rem, inv, q0);
+}
+
+// One Newton step that turns any approximation y0 within 2 ulps of 1/S into fp32(1/S) for every
+// positive E4M3 value S (checked on the host for all 126 values and all such y0).
+__host__ __device__ __forceinline__ float newton_recip(float S, float y0) {
+  const float e = __builtin_fmaf(-S, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
+}
+
+// fp32(1/S) for an E4M3 value S > 0: hardware reciprocal (about 1 ulp) plus the Newton step.
+__device__ __forceinline__ float recip_e4m3(float S) { return newton_recip(S, __builtin_amdgcn_rcpf(S)); }
+
+// Unit-global-scale block scale: S = E4M3(fp32(amax / 6)).
+__host__ __device__ __forceinline__ float block_scale_unit(float amax) { return round_e4m3(div6(amax)); }
+
+// Fake-quantize one value with block scale S (> 0) and inv = 1/S under the unit global scale:
+// sign(x) * E2M1(|x| / S) * S.  The product has at most 6 significant bits, so it is exact.
+__host__ __device__ __forceinline__ float fq_unit(float x, float S, float inv) {
+  const float ax = __builtin_fabsf(x);
+  const float q = round_e2m1(div_e4m3(ax, S, inv));
+  return u2f(f2u(q * S) | (f2u(x) & 0x80000000u));
+}
+
+// Same under a general global scale: S = s/g is not an E4M3 value, so the quotient is an IEEE
+// division.  Returns the fp32 dequantized value (the caller rounds to bf16).
+__host__ __device__ __forceinline__ float fq_general(float x, float S) {
+  const float ax = __builtin_fabsf(x);
+  const float q = round_e2m1(ax / S);
+  return u2f(f2u(q * S) | (f2u(x) & 0x80000000u));
+}
+
+// Cross-lane exchanges inside a 64-wide wavefront.
+// Value of lane (l ^ 1): DPP quad permutation [1, 0, 3, 2].
+__device__ __forceinline__ float xor1(float v) {
+  return u2f(__builtin_amdgcn_mov_dpp((int)f2u(v), 0xB1, 0xF, 0xF, true));
+}
+// Value of lane (l ^ 32): swap the two 32-lane halves.
+__device__ __forceinline__ float xor32(float v) {
+  return u2f(__builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false)[0]);
+}
+
+}  // namespace aq

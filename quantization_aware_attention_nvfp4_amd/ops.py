@@ -1,0 +1,271 @@
+"""Thin torch binding over libattnqat.so.
+
+PyTorch is used only to own device memory and to name the current HIP stream;
+every step of the computation runs in the library's gfx950 kernels.  These
+functions only validate tensor properties, compute strides and allocate the
+outputs and the workspace.
+
+Names follow the pages:
+  * ``attn_qat_train(q_BLHD, k_BLHD, v_BLHD, is_causal=False, sm_scale=None)``
+    and ``AttnQatTrainImpl`` mirror the "attn_qat_train" API reference page
+    (attn_qat_train, AttnQatTrainImpl, AttnQatTrainBackend);
+  * ``fq_nvfp4`` / ``static_global_scale`` follow "nvfp4_qad.py" (module
+    docstring, weight_global_sf, input_global_sf);
+  * ``vsa_qat_fwd`` follows the attention record of "vsqa-preview-1.3b
+    metadata.json" (cube_shape, selection.effective_topk).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (AQ_QUANT_ALL, AQ_QUANT_K, AQ_QUANT_P, AQ_QUANT_Q, AQ_QUANT_V, aq_strides, check,
+                   load)
+
+HEAD_SIZE = 128
+CHUNK = 128
+
+
+def _stream_ptr(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require_bf16_cuda(name: str, t: torch.Tensor):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+
+
+def _strides_blhd(t: torch.Tensor) -> aq_strides:
+    """Strides of a [B, L, H, D] tensor as (b, h, l) with D contiguous."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("attention tensors must be 4-D [B, L, H, D] with a contiguous last dim")
+    return aq_strides(t.stride(0), t.stride(2), t.stride(1))
+
+
+def _workspace(op: int, B: int, H: int, lq: int, lk: int, device) -> torch.Tensor:
+    nbytes = load().attn_qat_workspace_size(op, B, H, lq, lk)
+    return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+
+
+def _aligned_ptr(ws: torch.Tensor) -> int:
+    p = ws.data_ptr()
+    return (p + 255) & ~255
+
+
+# ----------------------------------------------------------------------------------------------
+# Standalone fake quantization
+# ----------------------------------------------------------------------------------------------
+
+def static_global_scale(x: torch.Tensor) -> torch.Tensor:
+    """g = 448*6 / max(amax|x|, 1e-12) as a 1-element fp32 device tensor."""
+    _require_bf16_cuda("x", x)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    g = torch.empty(1, dtype=torch.float32, device=x.device)
+    check(load().fq_nvfp4_static_scale(x.data_ptr(), x.numel(), g.data_ptr(), _stream_ptr(x)),
+          "fq_nvfp4_static_scale")
+    return g
+
+
+def fq_nvfp4(x: torch.Tensor, axis: int = -1, global_scale=None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """NVFP4 fake quantization of a contiguous bf16 tensor in 16-element blocks
+    along ``axis``.  ``global_scale``: None (unit), "static" (computed from x),
+    or a 1-element fp32 device tensor."""
+    _require_bf16_cuda("x", x)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    axis = axis % x.dim()
+    outer = math.prod(x.shape[:axis])
+    inner = math.prod(x.shape[axis + 1:])
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must match x")
+    g = None
+    if isinstance(global_scale, str):
+        if global_scale != "static":
+            raise ValueError("global_scale must be None, 'static' or a tensor")
+        global_scale = static_global_scale(x)
+    if global_scale is not None:
+        if global_scale.dtype != torch.float32 or global_scale.numel() != 1 or not global_scale.is_cuda:
+            raise ValueError("global_scale must be a 1-element fp32 device tensor")
+        g = global_scale.data_ptr()
+    check(load().fq_nvfp4(x.data_ptr(), out.data_ptr(), outer, x.shape[axis], inner, g, _stream_ptr(x)),
+          "fq_nvfp4")
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Dense attention
+# ----------------------------------------------------------------------------------------------
+
+def _check_qkv(q, k, v):
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _require_bf16_cuda(n, t)
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be [B, L, H, D]")
+    B, Lq, H, D = q.shape
+    if k.shape[0] != B or v.shape[0] != B:
+        raise ValueError("batch sizes differ")
+    if k.shape[1] != v.shape[1]:
+        raise ValueError("key and value must have the same sequence length")
+    if k.shape[2] != v.shape[2] or k.shape[3] != D or v.shape[3] != D:
+        raise ValueError("k and v must be [B, Lk, Hkv, D] with q's D")
+    return B, Lq, k.shape[1], H, k.shape[2], D
+
+
+def attn_qat_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                 sm_scale: Optional[float] = None, quant_flags: int = AQ_QUANT_ALL,
+                 training: bool = False):
+    """Fake-quant attention forward on [B, L, H, D] bf16 tensors.
+
+    Returns o [B, Lq, H, D] bf16; with ``training`` also a dict holding the
+    auxiliary outputs the backward needs: lse_log2 [B, H, Lq], chunk_max_log2
+    [B, H, ceil(Lk/128), Lq] and o_hp [B, H, Lq, D] (fp32)."""
+    B, Lq, Lk, H, Hkv, D = _check_qkv(q, k, v)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)  # the pages' default (attn_qat_train)
+    o = torch.empty(B, Lq, H, D, dtype=torch.bfloat16, device=q.device)
+    lse = cmax = ohp = None
+    if training:
+        C = (Lk + CHUNK - 1) // CHUNK
+        lse = torch.empty(B, H, Lq, dtype=torch.float32, device=q.device)
+        cmax = torch.empty(B, H, C, Lq, dtype=torch.float32, device=q.device)
+        ohp = torch.empty(B, H, Lq, D, dtype=torch.float32, device=q.device)
+    ws = _workspace(0, B, H, Lq, Lk, q.device) if D == HEAD_SIZE and Hkv == H else torch.empty(
+        256, dtype=torch.uint8, device=q.device)
+    p = lambda t: None if t is None else t.data_ptr()
+    check(load().attn_qat_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, Hkv, D, Lq,
+                              Lk, _strides_blhd(q), _strides_blhd(k), _strides_blhd(v), _strides_blhd(o),
+                              float(sm_scale), int(bool(causal)), int(quant_flags), p(lse), p(cmax),
+                              p(ohp), _aligned_ptr(ws), ws.numel() - 256, _stream_ptr(q)),
+          "attn_qat_fwd")
+    if training:
+        return o, {"lse_log2": lse, "chunk_max_log2": cmax, "o_hp": ohp}
+    return o
+
+
+def attn_qat_bwd(q, k, v, aux, d_o, causal: bool = False, sm_scale: Optional[float] = None,
+                 quant_flags: int = AQ_QUANT_ALL):
+    """Straight-through backward.  ``aux`` is the dict returned by
+    ``attn_qat_fwd(..., training=True)``.  Returns dq, dk, dv [B, L, H, D] bf16."""
+    B, Lq, Lk, H, Hkv, D = _check_qkv(q, k, v)
+    _require_bf16_cuda("d_o", d_o)
+    if d_o.shape != q.shape:
+        raise ValueError("d_o must have q's shape")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    ws = _workspace(1, B, H, Lq, Lk, q.device) if D == HEAD_SIZE and Hkv == H else torch.empty(
+        256, dtype=torch.uint8, device=q.device)
+    for n in ("lse_log2", "chunk_max_log2", "o_hp"):
+        t = aux[n]
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"aux[{n}] must be a contiguous fp32 device tensor")
+    check(load().attn_qat_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), aux["o_hp"].data_ptr(),
+                              d_o.data_ptr(), aux["lse_log2"].data_ptr(), aux["chunk_max_log2"].data_ptr(),
+                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, D, Lq, Lk,
+                              _strides_blhd(q), _strides_blhd(k), _strides_blhd(v), _strides_blhd(d_o),
+                              _strides_blhd(dq), _strides_blhd(dk), _strides_blhd(dv), float(sm_scale),
+                              int(bool(causal)), int(quant_flags), _aligned_ptr(ws), ws.numel() - 256,
+                              _stream_ptr(q)),
+          "attn_qat_bwd")
+    return dq, dk, dv
+
+
+class _AttnQatTrain(torch.autograd.Function):
+    """Forward = fake-quant attention; backward = the consistent straight-through
+    estimator of the library (fake-quant Jacobians are the identity)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, is_causal, sm_scale):
+        o, aux = attn_qat_fwd(q, k, v, causal=is_causal, sm_scale=sm_scale, training=True)
+        ctx.save_for_backward(q, k, v, aux["lse_log2"], aux["chunk_max_log2"], aux["o_hp"])
+        ctx.is_causal, ctx.sm_scale = is_causal, sm_scale
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k, v, lse, cmax, ohp = ctx.saved_tensors
+        aux = {"lse_log2": lse, "chunk_max_log2": cmax, "o_hp": ohp}
+        dq, dk, dv = attn_qat_bwd(q, k, v, aux, d_o.contiguous(), causal=ctx.is_causal,
+                                  sm_scale=ctx.sm_scale)
+        return dq, dk, dv, None, None
+
+
+def attn_qat_train(q_BLHD: torch.Tensor, k_BLHD: torch.Tensor, v_BLHD: torch.Tensor,
+                   is_causal: bool = False, sm_scale: Optional[float] = None) -> torch.Tensor:
+    """Fake-quant attention with the straight-through backward, [B, L, H, D] in and out
+    ("attn_qat_train" page: attn_qat_train; the kernel reads the strided BLHD tensors
+    directly, so no permuted copies are made)."""
+    return _AttnQatTrain.apply(q_BLHD, k_BLHD, v_BLHD, bool(is_causal), sm_scale)
+
+
+class AttnQatTrainImpl:
+    """Mirror of the pages' AttnQatTrainImpl: refuses dropout, forwards to attn_qat_train."""
+
+    def __init__(self, num_heads: int, head_size: int, causal: bool, softmax_scale: float,
+                 num_kv_heads: Optional[int] = None, prefix: str = "", **extra_impl_args) -> None:
+        if head_size != HEAD_SIZE:
+            raise ValueError(f"head_size {head_size} is not supported (supported: [128])")
+        self.num_heads = num_heads
+        self.num_kv_heads = num_heads if num_kv_heads is None else num_kv_heads
+        self.causal = causal
+        self.softmax_scale = softmax_scale
+        dropout_p = extra_impl_args.get("dropout_p", 0.0)
+        if dropout_p > 0:
+            raise NotImplementedError(f"attn_qat_train does not support dropout (got dropout_p={dropout_p})")
+
+    def forward(self, query, key, value, attn_metadata=None):
+        return attn_qat_train(query, key, value, is_causal=self.causal, sm_scale=self.softmax_scale)
+
+
+# ----------------------------------------------------------------------------------------------
+# Cube-sparse attention
+# ----------------------------------------------------------------------------------------------
+
+def vsa_topk(sparsity: float, n_cubes: int) -> int:
+    return load().vsa_topk(float(sparsity), int(n_cubes))
+
+
+def vsa_qat_fwd(q, k, v, grid=(16, 28, 56), cube=(4, 4, 8), sparsity: float = 0.9,
+                sm_scale: Optional[float] = None, quant_flags: int = AQ_QUANT_ALL,
+                coarse: bool = False, return_sel: bool = False):
+    """Cube-sparse fake-quant forward on cube-major [B, L, H, D] bf16 tensors.
+    Returns o_fine (and o_coarse, sel when requested)."""
+    B, L, Lk, H, Hkv, D = _check_qkv(q, k, v)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    n = L // max(1, cube[0] * cube[1] * cube[2])
+    topk = vsa_topk(sparsity, n) if n > 0 else 0
+    o = torch.empty(B, L, H, D, dtype=torch.bfloat16, device=q.device)
+    oc = torch.empty_like(o) if coarse else None
+    sel = torch.empty(B, H, n, max(topk, 1), dtype=torch.int32, device=q.device) if return_sel else None
+    ws = _workspace(2, B, H, L, L, q.device) if D == HEAD_SIZE and L > 0 else torch.empty(
+        256, dtype=torch.uint8, device=q.device)
+    p = lambda t: None if t is None else t.data_ptr()
+    check(load().vsa_qat_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), p(oc), p(sel), B, H, D,
+                             L, grid[0], grid[1], grid[2], cube[0], cube[1], cube[2], float(sparsity),
+                             _strides_blhd(q), _strides_blhd(k), _strides_blhd(v), _strides_blhd(o),
+                             float(sm_scale), int(quant_flags), _aligned_ptr(ws), ws.numel() - 256,
+                             _stream_ptr(q)),
+          "vsa_qat_fwd")
+    out = [o]
+    if coarse:
+        out.append(oc)
+    if return_sel:
+        out.append(sel)
+    return out[0] if len(out) == 1 else tuple(out)
+
+
+__all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "fq_nvfp4",
+           "static_global_scale", "attn_qat_fwd", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
+           "vsa_qat_fwd", "vsa_topk"]

@@ -1,0 +1,131 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol that
+include/attnqat.h declares, and rejects malformed arguments on the host before
+any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnqat.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from quantization_aware_attention_nvfp4_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from quantization_aware_attention_nvfp4_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fq_nvfp4", "fq_nvfp4_static_scale", "attn_qat_fwd", "attn_qat_bwd", "vsa_qat_fwd",
+              "vsa_topk", "attn_qat_workspace_size", "aq_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from quantization_aware_attention_nvfp4_amd import _lib
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_lib.EXPORTED) == set(declared_functions())
+
+
+def S(b=1, h=1, l=1):
+    from quantization_aware_attention_nvfp4_amd._lib import aq_strides
+    return aq_strides(b, h, l)
+
+
+def fwd(lib, **kw):
+    a = dict(q=8, k=8, v=8, o=8, B=1, H=2, Hkv=2, D=128, lq=64, lk=64, scale=0.088, causal=0, flags=15,
+             ws=256, ws_bytes=1 << 40)
+    a.update(kw)
+    s = S(64 * 256, 128, 256)
+    return lib.attn_qat_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["Hkv"], a["D"], a["lq"], a["lk"],
+                            s, s, s, s, a["scale"], a["causal"], a["flags"], None, None, None, a["ws"],
+                            a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=64), -1, "head_size"),
+    (dict(q=None), -1, "null"),
+    (dict(lq=0), -1, "positive"),
+    (dict(scale=float("nan")), -1, "softmax_scale"),
+    (dict(scale=-1.0), -1, "softmax_scale"),
+    (dict(flags=16), -1, "quant_flags"),
+    (dict(Hkv=1), -2, "num_kv_heads"),
+    (dict(causal=1, lk=32), -2, "causal"),
+    (dict(ws_bytes=100), -1, "workspace"),
+    (dict(ws=257), -1, "workspace"),
+])
+def test_forward_rejects_bad_arguments(lib, kw, code, msg):
+    assert fwd(lib, **kw) == code
+    assert msg in lib.aq_last_error().decode()
+
+
+def test_backward_requires_statistics(lib):
+    s = S(64 * 256, 128, 256)
+    rc = lib.attn_qat_bwd(8, 8, 8, None, 8, None, None, 8, 8, 8, 1, 2, 2, 128, 64, 64, s, s, s, s, s, s, s,
+                          0.088, 0, 15, 256, 1 << 40, None)
+    assert rc == -1 and "required" in lib.aq_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(grid=(16, 28, 56), cube=(4, 4, 8), L=25087), -1, "seq_len"),
+    (dict(grid=(16, 28, 55), cube=(4, 4, 8), L=16 * 28 * 55), -1, "divisible"),
+    (dict(grid=(16, 28, 56), cube=(4, 4, 4), L=25088), -2, "128"),
+    (dict(grid=(16, 28, 56), cube=(4, 4, 8), L=25088, sparsity=1.5), -1, "sparsity"),
+])
+def test_vsa_rejects_bad_arguments(lib, kw, code, msg):
+    s = S(25088 * 1536, 128, 1536)
+    g, c = kw["grid"], kw["cube"]
+    rc = lib.vsa_qat_fwd(8, 8, 8, 8, None, None, 1, 12, 128, kw["L"], g[0], g[1], g[2], c[0], c[1], c[2],
+                         kw.get("sparsity", 0.9), s, s, s, s, 0.088, 15, 256, 1 << 40, None)
+    assert rc == code
+    assert msg in lib.aq_last_error().decode()
+
+
+def test_fq_rejects_bad_arguments(lib):
+    assert lib.fq_nvfp4(None, 8, 1, 16, 1, None, None) == -1
+    assert lib.fq_nvfp4(8, 8, 1, 0, 1, None, None) == -1
+    assert lib.fq_nvfp4_static_scale(8, 0, 8, None) == -1
+
+
+def test_topk_and_workspace(lib):
+    assert lib.vsa_topk(0.9, 196) == 20
+    assert lib.vsa_topk(0.0, 196) == 196
+    assert lib.vsa_topk(1.0, 196) == 1
+    assert lib.vsa_topk(2.0, 196) == 0
+    # K-hat and V-hat for 12 heads x 25088 keys: 2 x 77.07 MB
+    assert lib.attn_qat_workspace_size(0, 1, 12, 25088, 25088) == 2 * 12 * 25088 * 128 * 2
+    assert lib.attn_qat_workspace_size(0, 0, 12, 25088, 25088) == 0
+
+
+def test_python_binding_validates_before_the_library(lib):
+    import torch
+    from quantization_aware_attention_nvfp4_amd import ops
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ops.fq_nvfp4(x)  # a CPU tensor is refused
+    with pytest.raises(NotImplementedError):
+        ops.AttnQatTrainImpl(12, 128, False, 0.088, dropout_p=0.1)
+    with pytest.raises(ValueError):
+        ops.AttnQatTrainImpl(12, 64, False, 0.088)
+
+
+def test_missing_library_raises_import_error(tmp_path, monkeypatch):
+    from quantization_aware_attention_nvfp4_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libattnqat.so"))
+    with pytest.raises(ImportError):
+        _lib.load()
