@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 fake-quant attention hot path on one MI355X.
+
+One step runs every stage of the hot path once, on synthetic inputs already
+resident in HBM (Wan2.1-T2V-1.3B attention shape at 448x896, 61 frames:
+B=1, H=12, L=16*28*56=25088, D=128):
+  1. fq_nvfp4, unit global scale, on a bf16 [301056, 128] tensor (25088 tokens x
+     12 heads x D=128; 4 rotating input/output pairs, 616 MB, so the 256 MB
+     Infinity Cache cannot serve it);
+  2. attn_qat_fwd in training mode (Q, K, V and P fake-quantized; lse, chunk
+     maxima and the high-precision auxiliary output written);
+  3. attn_qat_bwd, the straight-through backward;
+  4. vsa_qat_fwd, the cube-sparse forward (196 cubes of 4x4x8, top-20).
+
+value = algorithmic attention FLOP per step / ms_per_step, where the dense
+forward counts 4*B*H*L^2*D, the backward 2.5x that (10*B*H*L^2*D), and the
+cube-sparse forward 4*B*H*n*k*128^2*D for its fine stage plus 4*B*H*n^2*D for
+its coarse stage; fq contributes time but no FLOP.  Per-kernel durations come
+from HIP events the library records around each of its launches on the launch
+stream while kernel timing is on (aq_kernel_timing).
+
+Prints one JSON line.  Only one GPU is supported: --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn_qat fwd+bwd TFLOP/s @H=12,L=25088,D=128 (%BF16 MFMA peak); fq GB/s"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+B, H, D = 1, 12, 128
+GRID = (16, 28, 56)
+L = GRID[0] * GRID[1] * GRID[2]
+CUBE = (4, 4, 8)
+SPARSITY = 0.9
+
+
+def flops():
+    fwd = 4.0 * B * H * L * L * D
+    n = L // (CUBE[0] * CUBE[1] * CUBE[2])
+    k = max(1, min(math.ceil((1 - SPARSITY) * n), n))
+    vsa = 4.0 * B * H * n * k * 128 * 128 * D + 4.0 * B * H * n * n * D
+    return {"fwd": fwd, "bwd": 2.5 * fwd, "vsa": vsa, "topk": k, "cubes": n}
+
+
+def cpu_baseline(q, k, v, do, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload: forward and dQ rows of
+    head 0, in the metric's unit."""
+    import numpy as np
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_threads(cores)
+    oracle.build()
+    from synth import to_bhld_bits
+    qb, kb, vb, db = (to_bhld_bits(t[:, :, :1]) for t in (q, k, v, do))
+    scale = 1.0 / math.sqrt(D)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.attn_fwd(qb, kb, vb, scale, rows=rows)
+        oracle.attn_bwd(qb, kb, vb, db, scale, qrows=rows, krows=np.zeros(0, np.int64))
+        return time.perf_counter() - t0
+
+    probe = np.arange(0, L, L // 16)[:16]
+    run(probe)  # first call: library load and thread start-up
+    t_probe = run(probe)
+    R = int(min(L, max(16, 16 * seconds / max(t_probe, 1e-3))))
+    rows = np.linspace(0, L - 1, R).astype(np.int64)
+    t = run(rows)
+    # per query row: forward 4*L*D (logits, P@V); dQ row 6*L*D (logits, dP, dQ)
+    fl = R * (4.0 + 6.0) * L * D
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle forward + dQ backward for {R} query rows of head 0 at L={L}, D={D} "
+                      f"(fp64 C, OpenMP), {t:.1f} s; per row 4*L*D + 6*L*D FLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); sharding the "
+              "heads of a call over several GPUs is not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantization_aware_attention_nvfp4_amd as m
+    import synth
+    from quantization_aware_attention_nvfp4_amd import _lib
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    fl = flops()
+
+    x = synth.fq_tensor()
+    xs = [x.to(dev) for _ in range(4)]
+    ys = [torch.empty_like(xs[0]) for _ in range(4)]
+    q, k, v = synth.wan_448x896x61()
+    do = synth.normal_bf16((B, L, H, D), 2003)
+    qv, kv, vv = synth.vsa_inputs()
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    qvd, kvd, vvd = (t.to(dev) for t in (qv, kv, vv))
+
+    phases = ("fq", "fwd", "bwd", "vsa")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        m.fq_nvfp4(xs[i % 4], out=ys[i % 4])
+        if ev is not None:
+            ev[1].record()
+        o, aux = m.attn_qat_fwd(qd, kd, vd, training=True)
+        if ev is not None:
+            ev[2].record()
+        m.attn_qat_bwd(qd, kd, vd, aux, dod)
+        if ev is not None:
+            ev[3].record()
+        m.vsa_qat_fwd(qvd, kvd, vvd, grid=GRID, cube=CUBE, sparsity=SPARSITY)
+        if ev is not None:
+            ev[4].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    _lib.kernel_times(reset=True)
+    _lib.kernel_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    _lib.kernel_timing(False)
+    kt = _lib.kernel_times(reset=True)
+
+    ms_step = wall * 1e3 / args.steps
+    phase_ms = {p: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, p in enumerate(phases)}
+    total_flop = fl["fwd"] + fl["bwd"] + fl["vsa"]
+    value = total_flop / (ms_step * 1e-3) / 1e12
+
+    # Per-kernel averages and their algorithmic work per launch.
+    fq_bytes = 2.0 * 2 * xs[0].numel()
+    alg = {  # kernel name -> (work per launch, unit)
+        "attn_fwd_train": (fl["fwd"], "flop"),
+        "bwd_dkdv": (0.8 * fl["bwd"], "flop"),  # S, dP, dV, dK: 4 of the 5 backward products
+        "bwd_dq": (0.2 * fl["bwd"], "flop"),    # dQ (its S and dP recomputation counts as overhead)
+        "fq_contig_unit": (fq_bytes, "byte"),
+    }
+    kernels = {}
+    for name, (cnt, ms) in kt.items():
+        avg = ms / max(cnt, 1)
+        entry = {"launches_per_step": cnt / args.steps, "avg_ms": round(avg, 5)}
+        if name in alg:
+            w, unit = alg[name]
+            if unit == "flop":
+                entry["TFLOP/s"] = round(w / (avg * 1e-3) / 1e12, 1)
+                entry["frac_bf16_peak"] = round(w / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+            else:
+                entry["GB/s"] = round(w / (avg * 1e-3) / 1e9, 1)
+                entry["frac_hbm_peak"] = round(w / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        kernels[name] = entry
+    dominant = max((n for n in kt if n in alg and alg[n][1] == "flop"), key=lambda n: kt[n][1])
+    dom_avg = kt[dominant][1] / kt[dominant][0]
+    achieved = alg[dominant][0] / (dom_avg * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    fq_avg = kt["fq_contig_unit"][1] / kt["fq_contig_unit"][0]
+    fq = {"kernel": "fq_contig_unit", "bytes_per_launch": fq_bytes, "avg_us": round(fq_avg * 1e3, 2),
+          "GB/s": round(fq_bytes / (fq_avg * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+          "frac": round(fq_bytes / (fq_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    attn_ms = phase_ms["fwd"] + phase_ms["bwd"]
+    attn = {"fwd_bwd_ms": round(attn_ms, 4),
+            "fwd_bwd_TFLOP/s": round((fl["fwd"] + fl["bwd"]) / (attn_ms * 1e-3) / 1e12, 1),
+            "frac_bf16_peak": round((fl["fwd"] + fl["bwd"]) / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "fwd_TFLOP/s": round(fl["fwd"] / (phase_ms["fwd"] * 1e-3) / 1e12, 1),
+            "bwd_TFLOP/s": round(fl["bwd"] / (phase_ms["bwd"] * 1e-3) / 1e12, 1),
+            "vsa_TFLOP/s": round(fl["vsa"] / (phase_ms["vsa"] * 1e-3) / 1e12, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(q, k, v, do, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Wan2.1-T2V-1.3B attention at 448x896, 61 frames: fq + fwd + bwd + VSA",
+                   "B": B, "H": H, "L": L, "D": D, "causal": False, "quant": "Q,K,V,P NVFP4 unit scale",
+                   "vsa_cubes": fl["cubes"], "vsa_topk": fl["topk"], "fq_shape": list(xs[0].shape)},
+        "roofline": roofline, "cpu_baseline": cpu, "attention": attn, "fq": fq,
+        "phases_ms": {p: round(t, 4) for p, t in phase_ms.items()}, "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

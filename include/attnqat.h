@@ -175,6 +175,18 @@ int vsa_topk(double sparsity, int n_cubes);
 /* Workspace bytes needed by op 0 = attn_qat_fwd, 1 = attn_qat_bwd, 2 = vsa_qat_fwd (lk = L). */
 size_t attn_qat_workspace_size(int op, int batch, int num_heads, int64_t lq, int64_t lk);
 
+/* ---------------------------------------------------------------------------------------------
+ * Kernel timing (profiling aid, not part of the method).
+ * aq_kernel_timing(1) makes every later kernel launch of the library, on any stream, record a
+ * HIP event before and after the kernel on that stream; aq_kernel_timing(0) stops it.
+ * aq_kernel_times() waits for the recorded events and writes one line per kernel name,
+ * "<name> <launches> <total milliseconds>\n", accumulated since the last reset, into buf (at
+ * most len bytes, NUL-terminated); reset != 0 clears the totals afterwards.  Returns the length
+ * of the full report, or AQ_EHIP if an event could not be read.
+ * ------------------------------------------------------------------------------------------- */
+int aq_kernel_timing(int enable);
+int aq_kernel_times(char *buf, size_t len, int reset);
+
 #ifdef __cplusplus
 }
 #endif

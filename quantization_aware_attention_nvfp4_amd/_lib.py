@@ -18,7 +18,7 @@ AQ_QUANT_Q, AQ_QUANT_K, AQ_QUANT_V, AQ_QUANT_P = 1, 2, 4, 8
 AQ_QUANT_ALL = 15
 
 EXPORTED = ("aq_last_error", "fq_nvfp4", "fq_nvfp4_static_scale", "attn_qat_fwd", "attn_qat_bwd",
-            "vsa_qat_fwd", "vsa_topk", "attn_qat_workspace_size")
+            "vsa_qat_fwd", "vsa_topk", "attn_qat_workspace_size", "aq_kernel_timing", "aq_kernel_times")
 
 
 class aq_strides(ctypes.Structure):
@@ -52,6 +52,10 @@ def _declare(lib):
     lib.vsa_topk.restype = i32
     lib.attn_qat_workspace_size.argtypes = [i32, i32, i32, i64, i64]
     lib.attn_qat_workspace_size.restype = sz
+    lib.aq_kernel_timing.argtypes = [i32]
+    lib.aq_kernel_timing.restype = i32
+    lib.aq_kernel_times.argtypes = [ctypes.c_char_p, sz, i32]
+    lib.aq_kernel_times.restype = i32
 
 
 def load():
@@ -87,3 +91,21 @@ def check(rc: int, what: str) -> None:
     if rc == AQ_ENOTSUP:
         raise NotImplementedError(f"{what}: {msg}")
     raise AttnQatError(f"{what}: {msg} (code {rc})")
+
+
+def kernel_timing(enable: bool) -> None:
+    """Bracket every library kernel launch with HIP events (see aq_kernel_timing)."""
+    load().aq_kernel_timing(1 if enable else 0)
+
+
+def kernel_times(reset: bool = True) -> dict:
+    """{kernel name: (launches, total ms)} accumulated while timing was enabled."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    rc = load().aq_kernel_times(buf, len(buf), 1 if reset else 0)
+    if rc < 0:
+        raise AttnQatError("aq_kernel_times failed")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, count, ms = line.split()
+        out[name] = (int(count), float(ms))
+    return out

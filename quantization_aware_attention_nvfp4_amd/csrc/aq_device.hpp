@@ -76,8 +76,9 @@ __host__ __device__ __forceinline__ float div6(float a) {
 }
 
 // fp32(x / S) for an E4M3 value S > 0 given inv = fp32(1 / S): one Markstein correction.
-// Equal to the IEEE quotient for every such S and every non-negative fp32 x whose quotient is
-// below 2^64 (checked exhaustively on the host over the 8 significands of S).
+// Equal to the IEEE quotient for every such S and every fp32 x with |x/S| in [2^-5, 2^7)
+// (checked exhaustively on the host over the 8 significands of S; the sequence is odd in x and
+// invariant under power-of-two scaling).  Smaller quotients round to 0 either way.
 __host__ __device__ __forceinline__ float div_e4m3(float x, float S, float inv) {
   const float q0 = x * inv;
   const float rem = __builtin_fmaf(-q0, S, x);
@@ -118,9 +119,47 @@ __host__ __device__ __forceinline__ float fq_general(float x, float S) {
 __device__ __forceinline__ float xor1(float v) {
   return u2f(__builtin_amdgcn_mov_dpp((int)f2u(v), 0xB1, 0xF, 0xF, true));
 }
-// Value of lane (l ^ 32): swap the two 32-lane halves.
-__device__ __forceinline__ float xor32(float v) {
-  return u2f(__builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false)[0]);
+// Combine a value with the one in lane (l ^ 32).  v_permlane32_swap exchanges the upper half
+// of its first operand with the lower half of its second; with both operands equal to v its two
+// results hold (v_l, v_{l^32}) in some order in every lane, so a symmetric combination of the two
+// gives both lanes of a pair the same bits.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  return fmaxf(u2f(p[0]), u2f(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  return u2f(p[0]) + u2f(p[1]);
+}
+
+// Two values rounded to the nearest E2M1 value (ties to the even code, saturating at +-6, sign
+// kept) by the gfx950 packed FP4 conversion with a unit scale, and converted back.  Equal to
+// round_e2m1 with the sign restored (an in-bounds sweep of 11.3M fp32 inputs, every midpoint and
+// its neighbours included, and the bit-exact fake-quant tests check this on the GPU).
+__device__ __forceinline__ void e2m1_pair(float &a, float &b) {
+  const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
+  a = r[0];
+  b = r[1];
+}
+
+// Fake-quantize two non-negative values of one block (unit global scale, scale S and inv = 1/S,
+// inv = 0 for a zero block): E2M1(x / S) * S.
+__device__ __forceinline__ void fq_pos_pair(float &a, float &b, float S, float inv) {
+  float ra = div_e4m3(a, S, inv), rb = div_e4m3(b, S, inv);
+  e2m1_pair(ra, rb);
+  a = ra * S;
+  b = rb * S;
+}
+
+// Same for signed values: the magnitude is quantized and the sign bit of x is put back, so -0
+// stays -0.
+__device__ __forceinline__ void fq_unit_pair(float &a, float &b, float S, float inv) {
+  const uint32_t sa = f2u(a) & 0x80000000u, sb = f2u(b) & 0x80000000u;
+  float ra = __builtin_fabsf(a), rb = __builtin_fabsf(b);
+  fq_pos_pair(ra, rb, S, inv);
+  a = u2f(f2u(ra) | sa);
+  b = u2f(f2u(rb) | sb);
 }
 
 }  // namespace aq

@@ -1,0 +1,72 @@
+// attn_common.hpp - lane mappings and LDS addressing shared by the attention kernels.
+//
+// v_mfma_f32_32x32x16_bf16: lane l supplies row l%32 of A and column l%32 of B, each with the 8
+// k-slots 8*(l/32) .. 8*(l/32)+7; accumulator element (row i, column j) sits in lane
+// j + 32*((i/4)%2), register 4*(i/8) + i%4 (checked on the GPU).
+#pragma once
+
+#include "aq_device.hpp"
+
+namespace aq {
+
+// A key (or query) tile is fed as A rows in the order row i -> local index
+// 16*((i/4)%2) + 4*(i/8) + i%4, so that accumulator register r of lane half h holds local index
+// 16*h + r: each lane then owns 16 consecutive local indices of one column.
+__device__ __forceinline__ int perm_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+// Byte offset of 16-byte column j of row r in a 256-byte-row LDS tile, XOR-swizzled so that the
+// 8 lanes that read the same column of 8 rows together hit 8 different bank groups.
+// kq_off serves A-operand reads in perm_row order (rows {0..3, 16..19} + 4k together), row_off
+// reads of 8 consecutive rows.
+__device__ __forceinline__ int kq_off(int r, int j) { return r * 256 + ((j ^ ((r & 3) | ((r >> 2) & 4))) << 4); }
+__device__ __forceinline__ int row_off(int r, int j) { return r * 256 + ((j ^ (r & 7)) << 4); }
+
+// One-hot B operand of a 32x32x16 MFMA that moves A's k-slot values into column j: lane (column
+// j = l%32, half h) holds 1 in slot jj where j == 16h + 8*step + jj.
+__device__ __forceinline__ bf16x8 onehot_b(int lane, int step) {
+  const int j = lane & 31, h = lane >> 5;
+  bf16x8 b;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) b[jj] = (__bf16)((j == 16 * h + 8 * step + jj) ? 1.0f : 0.0f);
+  return b;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Eight fp32 values -> bf16x8 with round-to-nearest-even.
+__device__ __forceinline__ bf16x8 pack8_rne(const float *f) {
+  u32x4 w;
+  w.x = f32_to_bf16_rne(f[0]) | (f32_to_bf16_rne(f[1]) << 16);
+  w.y = f32_to_bf16_rne(f[2]) | (f32_to_bf16_rne(f[3]) << 16);
+  w.z = f32_to_bf16_rne(f[4]) | (f32_to_bf16_rne(f[5]) << 16);
+  w.w = f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16);
+  return as_bf16x8(w);
+}
+// Eight fp32 values that are exact in bf16 -> bf16x8.
+__device__ __forceinline__ bf16x8 pack8_exact(const float *f) {
+  return as_bf16x8(u32x4{pack_exact_bf16(f[0], f[1]), pack_exact_bf16(f[2], f[3]), pack_exact_bf16(f[4], f[5]),
+                         pack_exact_bf16(f[6], f[7])});
+}
+
+// Number of leading registers, out of the 16 consecutive keys key0 .. key0+15 a lane holds, whose
+// key is at most `last` (the largest key the lane's query may see; -1 for none).
+__device__ __forceinline__ int valid_prefix(int64_t key0, int64_t last) {
+  const int64_t rel = last - key0;
+  return rel < 0 ? 0 : (rel >= 15 ? 16 : (int)rel + 1);
+}
+
+// Set registers at and past `nvalid` to -inf (selects with constant indices, no branches).
+__device__ __forceinline__ void mask_tail(f32x16 &s, int nvalid) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = r < nvalid ? s[r] : -__builtin_inff();
+}
+
+// XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a contiguous range of work ids so
+// workgroups that share a head's operands share that XCD's L2.  Returns -1 for the padding
+// workgroups of the last partial range.
+__device__ __forceinline__ int64_t xcd_work_id(int64_t bid, int64_t per_xcd, int64_t nwork) {
+  const int64_t vid = (bid & 7) * per_xcd + (bid >> 3);
+  return vid < nwork ? vid : -1;
+}
+
+}  // namespace aq

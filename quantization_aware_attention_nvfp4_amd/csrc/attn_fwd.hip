@@ -7,10 +7,9 @@
 // matmuls run on BF16 MFMA with fp32 accumulation inside an online softmax whose running maximum
 // is refreshed once per 128-key chunk.
 //
-// Kernels:
-//   kq_prepass  K-hat  -> workspace kq [B*H, C*128, 128] bf16 (row-major, zero padded keys)
-//   vt_prepass  V-hat  -> workspace vt [B*H, C, 128 d, 128 keys] bf16 (each chunk d-major)
-//   attn_fwd    one workgroup per (head, tile of 32*WAVES queries); each wave owns 32 queries.
+// K-hat (rows) and V-hat (d-major chunk tiles) are fake-quantized once per call into the workspace
+// by the tile prepass (prepass.hip); the forward kernel runs one workgroup per (head, tile of
+// 32*WAVES queries) and each wave owns 32 queries.
 //
 // Wave data layout (v_mfma_f32_32x32x16_bf16; accumulator element (row i, column j) sits in lane
 // j + 32*((i/4)%2), register 4*(i/8) + i%4):
@@ -25,93 +24,14 @@
 //   permlane32 swap, the denominator is combined once at the end.
 // LDS: one K-hat chunk (32 KiB) and one V-hat^T chunk (32 KiB), 16-byte columns XOR-swizzled by
 // row so the A-operand reads of 8 lanes hit 8 different bank groups.
-#include "aq_device.hpp"
+#include "attn_common.hpp"
 #include "launch.hpp"
+#include "timing.hpp"
 
 namespace aq {
 namespace {
 
 constexpr int kD = kHeadDim;
-
-// ------------------------------------------------------------------------------------------
-// Prepass kernels
-// ------------------------------------------------------------------------------------------
-
-// K-hat: one lane per 8 d-values of a key row; lanes 2i, 2i+1 hold one 16-element block.
-__global__ __launch_bounds__(256) void kq_prepass(const uint16_t *__restrict__ k, Strides sk,
-                                                  u32x4 *__restrict__ kq, int heads, int64_t lk,
-                                                  int64_t lk_pad, int64_t total16, bool quant) {
-  for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total16;
-       id += (int64_t)gridDim.x * 256) {
-    const int part = (int)(id & 15);             // which 8-value group of the row
-    const int64_t row = (id >> 4) % lk_pad;      // key
-    const int64_t bh = (id >> 4) / lk_pad;
-    const int64_t b = bh / heads, h = bh % heads;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < lk) v = *(const u32x4 *)(k + b * sk.b + h * sk.h + row * sk.l + part * 8);
-    if (quant) {
-      float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
-                    bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
-      float am = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
-      am = fmaxf(am, xor1(am));
-      const float S = block_scale_unit(am);
-      const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
-      v.x = pack_exact_bf16(fq_unit(f[0], S, inv), fq_unit(f[1], S, inv));
-      v.y = pack_exact_bf16(fq_unit(f[2], S, inv), fq_unit(f[3], S, inv));
-      v.z = pack_exact_bf16(fq_unit(f[4], S, inv), fq_unit(f[5], S, inv));
-      v.w = pack_exact_bf16(fq_unit(f[6], S, inv), fq_unit(f[7], S, inv));
-    }
-    kq[id] = v;
-  }
-}
-
-// V-hat, transposed per chunk: one workgroup per (head, 128-key chunk).  The chunk is staged in
-// LDS as [key][d]; lane (d, half) quantizes the four 16-key blocks of column d in its half of the
-// chunk and writes them as 32 contiguous bytes of row d of the transposed tile.
-__global__ __launch_bounds__(256) void vt_prepass(const uint16_t *__restrict__ v, Strides sv,
-                                                  uint16_t *__restrict__ vt, int heads, int64_t lk,
-                                                  int64_t nchunks, bool quant) {
-  __shared__ uint16_t tile[kChunk][kD];
-  const int64_t bh = blockIdx.x / nchunks;
-  const int64_t c = blockIdx.x % nchunks;
-  const int64_t b = bh / heads, h = bh % heads;
-  const uint16_t *src = v + b * sv.b + h * sv.h;
-  for (int i = threadIdx.x; i < kChunk * kD / 8; i += 256) {
-    const int row = i / (kD / 8), part = i % (kD / 8);
-    const int64_t key = c * kChunk + row;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < lk) x = *(const u32x4 *)(src + key * sv.l + part * 8);
-    *(u32x4 *)&tile[row][part * 8] = x;
-  }
-  __syncthreads();
-  const int d = threadIdx.x & (kD - 1);
-  const int half = threadIdx.x >> 7;
-  uint16_t *dst = vt + ((bh * nchunks + c) * kD + d) * kChunk;
-  for (int blk = 0; blk < 4; ++blk) {
-    const int k0 = half * 64 + blk * 16;
-    float f[16];
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      f[i] = bf16lo(tile[k0 + i][d]);
-      am = fmaxf(am, __builtin_fabsf(f[i]));
-    }
-    uint32_t w[8];
-    if (quant) {
-      const float S = block_scale_unit(am);
-      const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = pack_exact_bf16(fq_unit(f[2 * i], S, inv), fq_unit(f[2 * i + 1], S, inv));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = pack_exact_bf16(f[2 * i], f[2 * i + 1]);
-    }
-    *(u32x4 *)(dst + k0) = u32x4{w[0], w[1], w[2], w[3]};
-    *(u32x4 *)(dst + k0 + 8) = u32x4{w[4], w[5], w[6], w[7]};
-  }
-}
 
 // ------------------------------------------------------------------------------------------
 // Forward kernel
@@ -139,13 +59,6 @@ struct FwdParams {
   bool causal, quant_q, quant_p;
 };
 
-// Swizzled byte offset of 16-byte column j of row r in a 256-byte-row LDS tile.
-__device__ __forceinline__ int kq_off(int r, int j) { return r * 256 + ((j ^ ((r & 3) | ((r >> 2) & 4))) << 4); }
-__device__ __forceinline__ int vt_off(int r, int j) { return r * 256 + ((j ^ (r & 7)) << 4); }
-
-// Accumulator register r of lane half h holds row 8*(r/4) + 4*h + r%4 of a 32x32 tile.
-__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-
 template <int WAVES, bool TRAIN>
 __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
   constexpr int BM = 32 * WAVES;
@@ -155,9 +68,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
 
   // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a contiguous range of
   // (head, query-tile) ids so the workgroups sharing a head's K/V share that XCD's L2.
-  const int64_t bid = blockIdx.x;
-  const int64_t vid = (bid & 7) * p.per_xcd + (bid >> 3);
-  if (vid >= p.nblocks) return;
+  const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
+  if (vid < 0) return;
   const int64_t bh = vid / p.qtiles;
   const int qt = (int)(vid % p.qtiles);
   const int64_t bb = bh / p.heads, hh = bh % p.heads;
@@ -184,13 +96,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
         float am = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
-        am = fmaxf(am, xor32(am));
+        am = pair_max(am);
         const float S = block_scale_unit(am);
         const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
-        v.x = pack_exact_bf16(fq_unit(f[0], S, inv), fq_unit(f[1], S, inv));
-        v.y = pack_exact_bf16(fq_unit(f[2], S, inv), fq_unit(f[3], S, inv));
-        v.z = pack_exact_bf16(fq_unit(f[4], S, inv), fq_unit(f[5], S, inv));
-        v.w = pack_exact_bf16(fq_unit(f[6], S, inv), fq_unit(f[7], S, inv));
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);
+        v = u32x4{pack_exact_bf16(f[0], f[1]), pack_exact_bf16(f[2], f[3]), pack_exact_bf16(f[4], f[5]),
+                  pack_exact_bf16(f[6], f[7])};
       }
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
@@ -207,8 +119,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
   float l_run = 0.0f;
   constexpr bool train = TRAIN;
 
-  // The K row this lane feeds as A-operand row i = n: key(i) within a 32-key sub-tile.
-  const int krow = 16 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
+  // The K row this lane feeds as A-operand row n of each 32-key sub-tile.
+  const int krow = perm_row(n);
   const int64_t q_last = (int64_t)qt * BM + BM - 1;  // last query of the workgroup's tile
   int64_t n_iter = p.nchunks;
   if (p.causal) {
@@ -235,7 +147,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
         const int id = i * WAVES * 64 + tid;
         const int r = id >> 4, j = id & 15;
         *(u32x4 *)(lds_k + kq_off(r, j)) = kv[i];
-        *(u32x4 *)(lds_v + vt_off(r, j)) = vv[i];
+        *(u32x4 *)(lds_v + row_off(r, j)) = vv[i];
       }
     }
     __syncthreads();
@@ -258,13 +170,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
     const bool tail = (chunk + 1) * kChunk > p.lk;
     const bool diag = p.causal && (chunk + 1) * kChunk - 1 > (int64_t)qt * BM + wave * 32;
     if (tail || diag) {
+      const int64_t last = p.causal ? (qrow < p.lk - 1 ? qrow : p.lk - 1) : p.lk - 1;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t key = key0 + 32 * kt + r;
-          if (key >= p.lk || (p.causal && key > qrow)) s[kt][r] = -__builtin_inff();
-        }
+      for (int kt = 0; kt < 4; ++kt) mask_tail(s[kt], valid_prefix(key0 + 32 * kt, last));
     }
 
     // ---- running max (refreshed once per chunk) -----------------------------------------
@@ -273,7 +181,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) cm = fmaxf(cm, s[kt][r]);
-    cm = fmaxf(cm, xor32(cm));
+    cm = pair_max(cm);
     const float m_new = fmaxf(m_run, cm * p.c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
 
@@ -303,7 +211,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
         const float S = block_scale_unit(am);
         const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) P[r] = fq_unit(P[r], S, inv);
+        for (int r = 0; r < 16; r += 2) fq_pos_pair(P[r], P[r + 1], S, inv);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           uint32_t w[4];
@@ -337,14 +245,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds_v + vt_off(32 * dt + n, 4 * kt + 2 * hf + j)));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds_v + row_off(32 * dt + n, 4 * kt + 2 * hf + j)));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pq[kt][j], acc[dt], 0, 0, 0);
           if (train) acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ph[kt][j], acc_hp[dt], 0, 0, 0);
         }
   }
 
   // ---- epilogue --------------------------------------------------------------------------
-  const float l = l_run + xor32(l_run);
+  const float l = pair_sum(l_run);
   const float inv_l = 1.0f / l;
   if (!qvalid) return;
   uint16_t *op = p.o + bb * p.so.b + hh * p.so.h + qrow * p.so.l;
@@ -366,23 +274,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
 }
 
 }  // namespace
-
-hipError_t launch_kv_prepass(const AttnArgs &a, hipStream_t stream) {
-  const Workspace w = workspace_layout(0, a.batch, a.heads, a.lq, a.lk);
-  const int64_t C = (a.lk + kChunk - 1) / kChunk;
-  const int64_t bh = (int64_t)a.batch * a.heads;
-  uint8_t *ws = (uint8_t *)a.workspace;
-  const int64_t total16 = bh * C * kChunk * (kD / 8);
-  int64_t grid = (total16 + 255) / 256;
-  if (grid > 16384) grid = 16384;
-  hipLaunchKernelGGL(kq_prepass, dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const uint16_t *)a.k, a.sk, (u32x4 *)(ws + w.kq), a.heads, a.lk, C * kChunk,
-                     total16, (a.flags & 2u) != 0);
-  hipLaunchKernelGGL(vt_prepass, dim3((unsigned)(bh * C)), dim3(256), 0, stream,
-                     (const uint16_t *)a.v, a.sv, (uint16_t *)(ws + w.vt), a.heads, a.lk, C,
-                     (a.flags & 4u) != 0);
-  return hipGetLastError();
-}
 
 hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t nsel, hipStream_t stream) {
   constexpr int WAVES = 4;
@@ -412,12 +303,23 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   p.quant_q = (a.flags & 1u) != 0;
   p.quant_p = (a.flags & 8u) != 0;
   if (a.o_hp)
-    hipLaunchKernelGGL((attn_fwd_kernel<WAVES, true>), dim3((unsigned)(p.per_xcd * 8)), dim3(WAVES * 64), 0,
+    AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<WAVES, true>), dim3((unsigned)(p.per_xcd * 8)), dim3(WAVES * 64), 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<WAVES, false>), dim3((unsigned)(p.per_xcd * 8)), dim3(WAVES * 64), 0,
+    AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<WAVES, false>), dim3((unsigned)(p.per_xcd * 8)), dim3(WAVES * 64), 0,
                        stream, p);
   return hipGetLastError();
+}
+
+// K-hat rows and V-hat tiles for keys [0, lk) of every head into the forward workspace.
+hipError_t launch_kv_prepass(const AttnArgs &a, hipStream_t stream) {
+  const Workspace w = workspace_layout(0, a.batch, a.heads, a.lq, a.lk);
+  uint8_t *ws = (uint8_t *)a.workspace;
+  hipError_t e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, (a.flags & 2u) ? kQuantD : kQuantNone,
+                                     ws + w.kq, nullptr, stream);
+  if (e != hipSuccess) return e;
+  return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, (a.flags & 4u) ? kQuantRows : kQuantNone,
+                             nullptr, ws + w.vt, stream);
 }
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {

@@ -8,6 +8,7 @@
 // covers 1 KiB of consecutive memory.
 #include "aq_device.hpp"
 #include "launch.hpp"
+#include "timing.hpp"
 
 namespace aq {
 namespace {
@@ -28,7 +29,10 @@ __device__ __forceinline__ u32x4 fq8(u32x4 v, float g) {
     const float S = block_scale_unit(am);
     const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pack_exact_bf16(fq_unit(f[2 * i], S, inv), fq_unit(f[2 * i + 1], S, inv));
+    for (int i = 0; i < 4; ++i) {
+      fq_unit_pair(f[2 * i], f[2 * i + 1], S, inv);
+      w[i] = pack_exact_bf16(f[2 * i], f[2 * i + 1]);
+    }
   } else {
     const float s = round_e4m3((am / 6.0f) * g);
     const float S = s / g;
@@ -98,8 +102,10 @@ __global__ __launch_bounds__(kThreads) void fq_general_kernel(const uint16_t *__
       const float S = block_scale_unit(am);
       const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
 #pragma unroll
+      for (int i = 0; i < kBlock; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);
+#pragma unroll
       for (int i = 0; i < kBlock; ++i)
-        if (i < n) y[base + i * inner] = (uint16_t)(f2u(fq_unit(f[i], S, inv)) >> 16);
+        if (i < n) y[base + i * inner] = (uint16_t)(f2u(f[i]) >> 16);
     } else {
       const float s = round_e4m3((am / 6.0f) * g);
       const float S = s / g;
@@ -155,29 +161,29 @@ hipError_t launch_fq(const void *x, void *y, int64_t outer, int64_t axis, int64_
     const int64_t n8 = outer * axis / 8;
     const int grid = grid_for(n8, kUnroll * 4);
     if (g == nullptr)
-      hipLaunchKernelGGL(fq_contig_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
+      AQ_LAUNCH("fq_contig_unit", fq_contig_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
                          (const u32x4 *)x, (u32x4 *)y, n8, g);
     else
-      hipLaunchKernelGGL(fq_contig_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
+      AQ_LAUNCH("fq_contig_static", fq_contig_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
                          (const u32x4 *)x, (u32x4 *)y, n8, g);
   } else {
     const int64_t cols = outer * ((axis + kBlock - 1) / kBlock) * inner;
     const int grid = grid_for(cols, 1);
     if (g == nullptr)
-      hipLaunchKernelGGL(fq_general_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
+      AQ_LAUNCH("fq_general_unit", fq_general_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
                          (const uint16_t *)x, (uint16_t *)y, outer, axis, inner, g);
     else
-      hipLaunchKernelGGL(fq_general_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
+      AQ_LAUNCH("fq_general_static", fq_general_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
                          (const uint16_t *)x, (uint16_t *)y, outer, axis, inner, g);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_static_scale(const void *x, int64_t n, float *g_out, hipStream_t stream) {
-  hipLaunchKernelGGL(static_scale_init, dim3(1), dim3(1), 0, stream, g_out);
-  hipLaunchKernelGGL(static_scale_reduce, dim3(grid_for(n / 8 + 1, 16)), dim3(kThreads), 0, stream,
+  AQ_LAUNCH("static_scale_init", static_scale_init, dim3(1), dim3(1), 0, stream, g_out);
+  AQ_LAUNCH("static_scale_reduce", static_scale_reduce, dim3(grid_for(n / 8 + 1, 16)), dim3(kThreads), 0, stream,
                      (const uint16_t *)x, n, g_out);
-  hipLaunchKernelGGL(static_scale_final, dim3(1), dim3(1), 0, stream, g_out);
+  AQ_LAUNCH("static_scale_final", static_scale_final, dim3(1), dim3(1), 0, stream, g_out);
   return hipGetLastError();
 }
 

@@ -43,40 +43,47 @@ struct VsaArgs {
   int n_cubes, topk;
 };
 
-// Workspace regions, each 256-byte aligned, in this order:
-//   kq    [B*H, C*128, 128] bf16   K-hat, keys padded with zeros to a multiple of 128
-//   vt    [B*H, C, 128 d, 128 keys] bf16   V-hat, each 128-key chunk stored d-major
-//   (op 1) dvec [B*H, lq] fp32      D_i = <dO_i, o_hp_i>
-//   (op 1) dqacc [B*H, lq, 128] fp32  dQ accumulator
-//   (op 2) pool  [3, B*H, n, 128] bf16 cube means of Q, K, V
-//   (op 2) selw  [B*H, n, n] int32   selection when the caller passes none
+// Workspace regions, each 256-byte aligned.  Row tensors are [B*H, C*128, 128] bf16 with rows
+// padded by zeros to a multiple of 128; tile tensors are [B*H, C, 128 d, 128 rows] bf16 (each
+// 128-row chunk stored d-major).
+//   op 0 (forward):  kq (K-hat rows), vt (V-hat tiles)
+//   op 1 (backward): kq, vq (V-hat rows), kt (K-hat tiles), qq (Q-hat rows), qt (Q-hat tiles),
+//                    dot (dO tiles), dvec [B*H, lq] fp32 (D_i = <dO_i, o_hp_i>)
+//   op 2 (cube-sparse forward): kq, vt, pool [3, B*H, n, 128] bf16 (cube means of Q, K, V),
+//                    selw [B*H, n, n] int32 (selection when the caller passes none)
 struct Workspace {
-  size_t kq, vt, dvec, dqacc, pool, selw, total;
+  size_t kq, vt, vq, kt, qq, qt, dot, dvec, pool, selw, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline Workspace workspace_layout(int op, int batch, int heads, int64_t lq, int64_t lk) {
   const size_t bh = (size_t)batch * heads;
-  const size_t C = (size_t)((lk + kChunkHost - 1) / kChunkHost);
+  const size_t Ck = (size_t)((lk + kChunkHost - 1) / kChunkHost);
+  const size_t Cq = (size_t)((lq + kChunkHost - 1) / kChunkHost);
+  const size_t kbytes = bh * Ck * kChunkHost * kHeadDimHost * 2;
+  const size_t qbytes = bh * Cq * kChunkHost * kHeadDimHost * 2;
   Workspace w{};
   size_t off = 0;
-  w.kq = off;
-  off = align256(off + bh * C * kChunkHost * kHeadDimHost * 2);
-  w.vt = off;
-  off = align256(off + bh * C * kChunkHost * kHeadDimHost * 2);
+  auto take = [&off](size_t n) {
+    const size_t at = off;
+    off = align256(off + n);
+    return at;
+  };
+  w.kq = take(kbytes);
+  if (op == 0 || op == 2) w.vt = take(kbytes);
   if (op == 1) {
-    w.dvec = off;
-    off = align256(off + bh * (size_t)lq * 4);
-    w.dqacc = off;
-    off = align256(off + bh * (size_t)lq * kHeadDimHost * 4);
+    w.vq = take(kbytes);
+    w.kt = take(kbytes);
+    w.qq = take(qbytes);
+    w.qt = take(qbytes);
+    w.dot = take(qbytes);
+    w.dvec = take(bh * (size_t)lq * 4);
   }
   if (op == 2) {
     const size_t n = (size_t)(lk / kChunkHost);
-    w.pool = off;
-    off = align256(off + 3 * bh * n * kHeadDimHost * 2);
-    w.selw = off;
-    off = align256(off + bh * n * n * 4);
+    w.pool = take(3 * bh * n * kHeadDimHost * 2);
+    w.selw = take(bh * n * n * 4);
   }
   w.total = off;
   return w;
@@ -92,9 +99,19 @@ hipError_t launch_fq(const void *x, void *y, int64_t outer, int64_t axis, int64_
 // *g_out = 2688 / max(max|x|, 1e-12).
 hipError_t launch_static_scale(const void *x, int64_t n, float *g_out, hipStream_t stream);
 
-// K-hat / V-hat into the workspace (kq, vt regions) for keys [0, lk) of every head.
-hipError_t launch_kv_prepass(const AttnArgs &a, hipStream_t stream);
+// One 128-row chunk of a strided [B, L, H, 128] bf16 tensor per workgroup: optional fake
+// quantization (kQuantNone, kQuantD along d per row, kQuantRows along rows per column), then a
+// row-major copy and/or a d-major tile copy into the workspace.
+enum TileQuant { kQuantNone = 0, kQuantD = 1, kQuantRows = 2 };
+hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
+                               TileQuant quant, void *rows_out, void *tiles_out,
+                               hipStream_t stream);
 
+// K-hat rows and V-hat tiles of every head into the forward workspace layout.
+hipError_t launch_kv_prepass(const AttnArgs &a, hipStream_t stream);
+// Forward kernel only (operands already in the workspace); sel: cube-sparse chunk lists
+// [B*H, lq/128, nsel] or null for dense attention.
+hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t nsel, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stream);
 hipError_t launch_vsa_fwd(const AttnArgs &a, const VsaArgs &s, hipStream_t stream);

@@ -1,0 +1,122 @@
+// prepass.hip - fake quantization of whole attention operands into the workspace, once per call.
+//
+// Q-hat and K-hat are fake-quantized along D, V-hat along the key axis, in 16-element blocks with
+// E4M3 scales and E2M1 values under the unit global scale ("vsqa-preview-1.3b metadata.json":
+// dense precision record, group_size 16, qk/pv_format NVFP4 E2M1, use_global_sf_qkv false).
+// Quantizing each operand once here keeps the codec out of the attention kernels' inner loops,
+// where it would be repeated by every query tile of a head.
+//
+// One workgroup handles one 128-row chunk of one head: the chunk is staged in LDS as
+// [row][d] (rows past L read as zero), quantized in place, then written as
+//   rows_out  [B*H, C*128, 128]       row-major (the MFMA operand rows of the attention kernels)
+//   tiles_out [B*H, C, 128 d, 128 rows] d-major (operands whose contraction runs over rows).
+#include "aq_device.hpp"
+#include "launch.hpp"
+#include "timing.hpp"
+
+namespace aq {
+namespace {
+
+constexpr int kD = kHeadDim;
+
+__global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__ src, Strides s,
+                                                    int heads, int64_t L, int64_t C, int quant,
+                                                    u32x4 *__restrict__ rows_out,
+                                                    uint16_t *__restrict__ tiles_out) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kChunk][kD];
+  const int64_t bh = blockIdx.x / C;
+  const int64_t c = blockIdx.x % C;
+  const int64_t b = bh / heads, h = bh % heads;
+  const uint16_t *base = src + b * s.b + h * s.h;
+  const int tid = threadIdx.x;
+
+  for (int i = tid; i < kChunk * kD / 8; i += 256) {
+    const int row = i >> 4, part = i & 15;
+    const int64_t r = c * kChunk + row;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (r < L) x = *(const u32x4 *)(base + r * s.l + part * 8);
+    *(u32x4 *)&tile[row][part * 8] = x;
+  }
+  __syncthreads();
+
+  if (quant == kQuantD) {
+    // lane: row tid/2, d in [64*(tid&1), +64): four 16-element blocks
+    const int row = tid >> 1, d0 = (tid & 1) * 64;
+    for (int blk = 0; blk < 4; ++blk) {
+      u32x4 *p = (u32x4 *)&tile[row][d0 + 16 * blk];
+      float f[16];
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const u32x4 v = p[i];
+        f[8 * i + 0] = bf16lo(v.x); f[8 * i + 1] = bf16hi(v.x);
+        f[8 * i + 2] = bf16lo(v.y); f[8 * i + 3] = bf16hi(v.y);
+        f[8 * i + 4] = bf16lo(v.z); f[8 * i + 5] = bf16hi(v.z);
+        f[8 * i + 6] = bf16lo(v.w); f[8 * i + 7] = bf16hi(v.w);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
+      const float S = block_scale_unit(am);
+      const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        p[i] = u32x4{pack_exact_bf16(f[8 * i], f[8 * i + 1]), pack_exact_bf16(f[8 * i + 2], f[8 * i + 3]),
+                     pack_exact_bf16(f[8 * i + 4], f[8 * i + 5]), pack_exact_bf16(f[8 * i + 6], f[8 * i + 7])};
+    }
+    __syncthreads();
+  } else if (quant == kQuantRows) {
+    // lane: column d = tid%128, rows [64*(tid/128), +64): four 16-row blocks
+    const int d = tid & (kD - 1), r0 = (tid >> 7) * 64;
+    for (int blk = 0; blk < 4; ++blk) {
+      float f[16];
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        f[i] = bf16lo(tile[r0 + 16 * blk + i][d]);
+        am = fmaxf(am, __builtin_fabsf(f[i]));
+      }
+      const float S = block_scale_unit(am);
+      const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tile[r0 + 16 * blk + i][d] = (uint16_t)(f2u(f[i]) >> 16);
+    }
+    __syncthreads();
+  }
+
+  if (rows_out) {
+    u32x4 *dst = rows_out + (bh * C + c) * (kChunk * kD / 8);
+    for (int i = tid; i < kChunk * kD / 8; i += 256) dst[i] = *(const u32x4 *)&tile[i >> 4][(i & 15) * 8];
+  }
+  if (tiles_out) {
+    // lane: d = tid/2, rows [64*(tid&1), +64)
+    const int d = tid >> 1, r0 = (tid & 1) * 64;
+    uint16_t *dst = tiles_out + ((bh * C + c) * kD + d) * kChunk + r0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)tile[r0 + 8 * i + 2 * j][d] | ((uint32_t)tile[r0 + 8 * i + 2 * j + 1][d] << 16);
+      *(u32x4 *)(dst + 8 * i) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
+                               TileQuant quant, void *rows_out, void *tiles_out,
+                               hipStream_t stream) {
+  const int64_t C = (L + kChunk - 1) / kChunk;
+  const int64_t blocks = (int64_t)batch * heads * C;
+  AQ_LAUNCH("tile_prepass", tile_prepass, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uint16_t *)src, s, heads, L, C, (int)quant, (u32x4 *)rows_out,
+                     (uint16_t *)tiles_out);
+  return hipGetLastError();
+}
+
+}  // namespace aq

@@ -96,3 +96,27 @@ def test_in_place_and_deterministic(lib):
     torch.cuda.synchronize()
     assert np.array_equal(y1, y2)
     assert np.array_equal(bits(xg), y1)
+
+
+def test_every_e2m1_decision_boundary(lib):
+    # For every positive E4M3 scale S: blocks whose amax is 6S (so the block scale is S) holding
+    # each midpoint t*S of the E2M1 grid, its bf16 neighbours, and their negations.
+    codes = np.arange(1, 127)
+    e, mnt = codes >> 3, codes & 7
+    scales = np.where(e == 0, np.ldexp(mnt.astype(np.float64), -9), np.ldexp(1 + mnt / 8.0, e - 7))
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    rows = []
+    for S in scales:
+        t = torch.tensor(mids * S, dtype=torch.float32).to(torch.bfloat16)
+        tb = t.view(torch.int16).numpy().view(np.uint16)
+        vals = np.concatenate([tb, tb - 1, tb + 1])
+        vals = np.concatenate([vals, vals | 0x8000]).astype(np.uint16)  # 42 values
+        amax = torch.tensor([6 * S], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        for i in range(0, 42, 14):
+            blk = np.zeros(16, np.uint16)
+            blk[0] = amax[0]
+            blk[1:15] = vals[i:i + 14]
+            rows.append(blk)
+    blocks = np.stack(rows)
+    x = torch.from_numpy(blocks.view(np.int16)).view(torch.bfloat16)
+    assert np.array_equal(gpu_fq(lib, x), oracle.fq_bf16(blocks))

@@ -1,0 +1,88 @@
+"""GPU parity of the cube-sparse forward (vsa_qat_fwd) against the oracle.
+
+Selection is an integer decision taken on fp32 coarse logits by the kernel and on
+fp64 by the oracle, from cube means that may differ by one bf16 ulp; where the two
+selections differ, the differing cubes must be a near tie at the top-k boundary,
+and the fine output is compared on the query cubes whose selections agree.  The
+fine and coarse outputs use the stated attention tolerance (tests/parity.py)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.parity import assert_close, bf16_values, bhld_bits
+
+pytestmark = pytest.mark.gpu
+SCALE = 1.0 / math.sqrt(128)
+
+
+@pytest.fixture(scope="module")
+def m():
+    import quantization_aware_attention_nvfp4_amd as m
+    return m
+
+
+def run(m, q, k, v, grid, sparsity):
+    o, oc, sel = m.vsa_qat_fwd(q.cuda(), k.cuda(), v.cuda(), grid=grid, cube=(4, 4, 8), sparsity=sparsity,
+                               coarse=True, return_sel=True)
+    torch.cuda.synchronize()
+    return o, oc, sel.cpu().numpy()
+
+
+def check_selection(sel_gpu, r, rel_tol=2e-3):
+    """Selections must agree except at near ties; returns a mask of agreeing query cubes."""
+    sel_ref, score = r["sel"], r["score"]
+    agree = np.all(np.sort(sel_gpu, -1) == sel_ref, axis=-1)
+    B, H, n, k = sel_ref.shape
+    spread = np.abs(score).max()
+    for b, h, a in zip(*np.nonzero(~agree)):
+        s = score[b, h, a]
+        kth = np.sort(s)[::-1][k - 1]
+        extra = set(sel_gpu[b, h, a]) ^ set(sel_ref[b, h, a])
+        for c in extra:
+            assert abs(s[c] - kth) <= rel_tol * spread, (b, h, a, c, s[c], kth)
+    assert agree.mean() >= 0.97
+    return agree
+
+
+def test_small_grid(m):
+    grid = (4, 8, 32)  # 8 cubes of 128 tokens
+    q, k, v = synth.qkv_headscaled(1, 1024, 2, 128, seed=91, scaled=False)
+    o, oc, sel = run(m, q, k, v, grid, 0.6)
+    rows = np.arange(0, 1024, 3)
+    r = oracle.vsa_fwd(bhld_bits(q), bhld_bits(k), bhld_bits(v), SCALE, sparsity=0.6, rows=rows)
+    assert r["topk"] == 4 and sel.shape[-1] == 4
+    agree = check_selection(sel, r)
+    ok = agree[:, :, rows // 128]  # [B, H, R]
+    got = bf16_values(o.permute(0, 2, 1, 3)[:, :, torch.as_tensor(rows)])
+    assert_close(got[ok], r["o_fine"][ok], "vsa fine")
+    gotc = bf16_values(oc.permute(0, 2, 1, 3)[:, :, torch.as_tensor(rows)])
+    assert_close(gotc, r["o_coarse"], "vsa coarse")
+
+
+def test_sparsity_zero_equals_dense(m):
+    grid = (4, 8, 16)  # 4 cubes
+    q, k, v = synth.qkv_headscaled(1, 512, 3, 128, seed=92, scaled=False)
+    o, oc, sel = run(m, q, k, v, grid, 0.0)
+    assert np.array_equal(sel, np.broadcast_to(np.arange(4), sel.shape))
+    dense = m.attn_qat_fwd(q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu().view(torch.int16), dense.cpu().view(torch.int16))
+
+
+def test_wan_vsa_workload(m):
+    q, k, v = synth.vsa_inputs()
+    o, oc, sel = run(m, q, k, v, (16, 28, 56), 0.9)
+    L = q.shape[1]
+    rows = synth.sample_rows(L, 64, seed=9).numpy()
+    r = oracle.vsa_fwd(bhld_bits(q), bhld_bits(k), bhld_bits(v), SCALE, sparsity=0.9, rows=rows)
+    assert r["topk"] == 20 and sel.shape == (1, 12, 196, 20)
+    agree = check_selection(sel, r)
+    ok = agree[:, :, rows // 128]
+    got = bf16_values(o.permute(0, 2, 1, 3)[:, :, torch.as_tensor(rows)])
+    assert_close(got[ok], r["o_fine"][ok], "Wan VSA fine")
+    gotc = bf16_values(oc.permute(0, 2, 1, 3)[:, :, torch.as_tensor(rows)])
+    assert_close(gotc, r["o_coarse"], "Wan VSA coarse")
