@@ -192,6 +192,8 @@ int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void 
   s.o_coarse = o_coarse; s.sel = sel;
   s.n_cubes = (int)(seq_len / aq::kChunkHost);
   s.topk = vsa_topk(sparsity, s.n_cubes);
+  if (s.topk > 1024)
+    return fail(AQ_ENOTSUP, "vsa_qat_fwd: at most 1024 selected cubes per query cube (got %d)", s.topk);
   return hip_status(aq::launch_vsa_fwd(a, s, (hipStream_t)stream), "vsa_qat_fwd launch");
 }
 

@@ -48,6 +48,32 @@ __device__ __forceinline__ bf16x8 pack8_exact(const float *f) {
                          pack_exact_bf16(f[6], f[7])});
 }
 
+// Asynchronous 16-byte global -> LDS copy: lane l of the wave writes LDS bytes
+// [lds_base + 16*l, +16) (checked on the GPU); lds_base must be the same in every lane.
+__device__ __forceinline__ void load_lds16(const void *gsrc, uint8_t *lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+// Stage a 32 KiB tile ([128 rows][256 bytes] in global memory) into LDS with the XOR swizzle
+// `sw` applied, using 8 asynchronous 16-byte copies per lane of a 256-lane workgroup.  LDS
+// instruction i of wave w covers rows 16i + 4w .. +3, physical column = lane%16; the lane fetches
+// the logical column that the swizzle maps there.
+template <int (*SW)(int)>
+__device__ __forceinline__ void stage_tile_async(const uint8_t *gtile, uint8_t *lds_tile, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 16 * i + 4 * wave + (lane >> 4);
+    const int pc = lane & 15;
+    const int j = pc ^ SW(r);
+    load_lds16(gtile + r * 256 + j * 16, lds_tile + (i * 256 + 64 * wave) * 16);
+  }
+}
+__device__ __forceinline__ int sw_kq(int r) { return (r & 3) | ((r >> 2) & 4); }
+__device__ __forceinline__ int sw_row(int r) { return r & 7; }
+
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+#define AQ_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
+
 // Number of leading registers, out of the 16 consecutive keys key0 .. key0+15 a lane holds, whose
 // key is at most `last` (the largest key the lane's query may see; -1 for none).
 __device__ __forceinline__ int valid_prefix(int64_t key0, int64_t last) {

@@ -32,6 +32,7 @@ namespace aq {
 namespace {
 
 constexpr int kD = kHeadDim;
+constexpr int kMaxSel = 1024;  // longest cube-sparse chunk list (checked by the launcher)
 
 // ------------------------------------------------------------------------------------------
 // Forward kernel
@@ -60,14 +61,14 @@ struct FwdParams {
 };
 
 template <int WAVES, bool TRAIN>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
+  static_assert(WAVES == 4, "LDS staging assumes 256 lanes");
   constexpr int BM = 32 * WAVES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunk * 256];
-  uint8_t *lds_k = lds;
-  uint8_t *lds_v = lds + kChunk * 256;
+  // Separate objects, so the compiler can tell reads of one tile from copies into the other.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kChunk * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kChunk * 256];
+  __shared__ int32_t lds_sel[kMaxSel];
 
-  // XCD-aware tile order: workgroup i runs on XCD i % 8; give each XCD a contiguous range of
-  // (head, query-tile) ids so the workgroups sharing a head's K/V share that XCD's L2.
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
   if (vid < 0) return;
   const int64_t bh = vid / p.qtiles;
@@ -81,6 +82,26 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
   const int hf = lane >> 5;  // lane half
   const int64_t qrow = (int64_t)qt * BM + wave * 32 + n;
   const bool qvalid = qrow < p.lq;
+
+  int64_t n_iter = p.nchunks;
+  if (p.causal) {
+    const int64_t q_last = (int64_t)qt * BM + BM - 1;
+    n_iter = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
+  }
+  // Cube-sparse: this query cube's chunk list, read once into LDS.
+  if (p.sel) {
+    const int32_t *src = p.sel + (bh * (p.lq / kChunk) + (int64_t)qt * BM / kChunk) * p.nchunks;
+    for (int i = tid; i < p.nchunks; i += WAVES * 64) lds_sel[i] = src[i];
+    __syncthreads();
+  }
+  auto chunk_of = [&](int64_t it) -> int64_t { return p.sel ? (int64_t)lds_sel[it] : it; };
+  auto ktile = [&](int64_t c) { return (const uint8_t *)(p.kq + (bh * p.kchunks + c) * (kChunk * kD / 8)); };
+  auto vtile = [&](int64_t c) { return (const uint8_t *)(p.vt + (bh * p.kchunks + c) * (kChunk * kD / 8)); };
+
+  // Start the first chunk's copies before the Q work so they overlap it.
+  int64_t chunk = chunk_of(0);
+  stage_tile_async<sw_kq>(ktile(chunk), lds_k, wave, lane);
+  stage_tile_async<sw_row>(vtile(chunk), lds_v, wave, lane);
 
   // ---- Q-hat fragment: B operand of S^T, d = 16t + 8hf + (0..7) -------------------------
   bf16x8 qf[8];
@@ -109,48 +130,22 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
   }
 
   f32x16 acc[4];
-  f32x16 acc_hp[4];
+  f32x16 acc_hp[TRAIN ? 4 : 1];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    acc[dt] = f32x16{};
-    acc_hp[dt] = f32x16{};
-  }
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+#pragma unroll
+  for (int dt = 0; dt < (TRAIN ? 4 : 1); ++dt) acc_hp[dt] = f32x16{};
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
-  constexpr bool train = TRAIN;
 
   // The K row this lane feeds as A-operand row n of each 32-key sub-tile.
   const int krow = perm_row(n);
-  const int64_t q_last = (int64_t)qt * BM + BM - 1;  // last query of the workgroup's tile
-  int64_t n_iter = p.nchunks;
-  if (p.causal) {
-    const int64_t last_needed = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk;
-    n_iter = last_needed + 1;
-  }
 
   for (int64_t it = 0; it < n_iter; ++it) {
-    const int64_t chunk = p.sel ? (int64_t)p.sel[(bh * (p.lq / kChunk) + (int64_t)qt * BM / kChunk) * p.nchunks + it] : it;
-    // ---- stage K-hat and V-hat^T chunk into LDS ----------------------------------------
-    __syncthreads();
-    {
-      const u32x4 *ksrc = p.kq + (bh * p.kchunks + chunk) * (kChunk * kD / 8);
-      const u32x4 *vsrc = p.vt + (bh * p.kchunks + chunk) * (kChunk * kD / 8);
-      constexpr int kPer = kChunk * kD / 8 / (WAVES * 64);
-      u32x4 kv[kPer], vv[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        kv[i] = ksrc[i * WAVES * 64 + tid];
-        vv[i] = vsrc[i * WAVES * 64 + tid];
-      }
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int id = i * WAVES * 64 + tid;
-        const int r = id >> 4, j = id & 15;
-        *(u32x4 *)(lds_k + kq_off(r, j)) = kv[i];
-        *(u32x4 *)(lds_v + row_off(r, j)) = vv[i];
-      }
-    }
-    __syncthreads();
+    // K-hat(chunk) has landed once this wave's V copies (issued after it) are the only ones
+    // outstanding; the barrier makes every wave's copies visible.
+    AQ_WAIT_VMCNT(8);
+    __builtin_amdgcn_s_barrier();
 
     // ---- S^T = K-hat Q-hat^T for the 128 keys of the chunk ------------------------------
     f32x16 s[4];
@@ -159,11 +154,17 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
       s[kt] = f32x16{};
       const int r = 32 * kt + krow;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds_k + kq_off(r, 2 * t + hf)));
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kt], 0, 0, 0);
+      for (int t0 = 0; t0 < 8; t0 += 4) {
+        bf16x8 a[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a[t] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds_k + kq_off(r, 2 * (t0 + t) + hf)));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qf[t0 + t], s[kt], 0, 0, 0);
       }
     }
+    const int64_t next = it + 1 < n_iter ? chunk_of(it + 1) : -1;
+    __builtin_amdgcn_s_barrier();  // every wave is done reading K-hat(chunk)
+    if (next >= 0) stage_tile_async<sw_kq>(ktile(next), lds_k, wave, lane);
 
     // ---- masks: keys past lk (last chunk) and causal -------------------------------------
     const int64_t key0 = chunk * kChunk + 16 * hf;  // key of register 0 in sub-tile 0
@@ -184,9 +185,23 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
     cm = pair_max(cm);
     const float m_new = fmaxf(m_run, cm * p.c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
+    if (p.cmax && hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
+    m_run = m_new;
+    // The rescale is skipped when no row of the wave moved its maximum (alpha == 1 exactly).
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+      if (TRAIN) {
+#pragma unroll
+        for (int dt = 0; dt < (TRAIN ? 4 : 1); ++dt) acc_hp[dt] *= alpha;
+      }
+    }
 
-    // ---- P, its sum, and P-hat in bf16 B-operands -----------------------------------------
-    bf16x8 pq[4][2], ph[4][2];
+    // V-hat(chunk): wait for this wave's V copies (K(next) may still be in flight).
+    if (next >= 0) AQ_WAIT_VMCNT(8); else AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+
+    // ---- per 32-key sub-tile: P, its sum, P-hat, and O^T += V-hat^T P-hat^T ---------------
     float psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -198,57 +213,41 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
         psum += P[r];
         am = fmaxf(am, P[r]);
       }
-      if (train) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint32_t w[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16_rne(P[8 * j + 2 * i]) | (f32_to_bf16_rne(P[8 * j + 2 * i + 1]) << 16);
-          ph[kt][j] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-        }
+      bf16x8 ph[2];
+      if (TRAIN) {
+        ph[0] = pack8_rne(P);
+        ph[1] = pack8_rne(P + 8);
       }
+      bf16x8 pq[2];
       if (p.quant_p) {
         const float S = block_scale_unit(am);
         const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
 #pragma unroll
         for (int r = 0; r < 16; r += 2) fq_pos_pair(P[r], P[r + 1], S, inv);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint32_t w[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = pack_exact_bf16(P[8 * j + 2 * i], P[8 * j + 2 * i + 1]);
-          pq[kt][j] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-        }
+        pq[0] = pack8_exact(P);
+        pq[1] = pack8_exact(P + 8);
       } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint32_t w[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16_rne(P[8 * j + 2 * i]) | (f32_to_bf16_rne(P[8 * j + 2 * i + 1]) << 16);
-          pq[kt][j] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-        }
+        pq[0] = pack8_rne(P);
+        pq[1] = pack8_rne(P + 8);
       }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (p.cmax && hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
-
-    // ---- O^T = alpha O^T + V-hat^T P-hat^T ------------------------------------------------
+      bf16x8 a[2][4];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      acc[dt] *= alpha;
-      if (train) acc_hp[dt] *= alpha;
-    }
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int dt = 0; dt < 4; ++dt)
+          a[j][dt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds_v + row_off(32 * dt + n, 4 * kt + 2 * hf + j)));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds_v + row_off(32 * dt + n, 4 * kt + 2 * hf + j)));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pq[kt][j], acc[dt], 0, 0, 0);
-          if (train) acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ph[kt][j], acc_hp[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][dt], pq[j], acc[dt], 0, 0, 0);
+          if (TRAIN) acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][dt], ph[j], acc_hp[dt], 0, 0, 0);
         }
+    }
+    l_run = l_run * alpha + psum;
+    __builtin_amdgcn_s_barrier();  // every wave is done reading V-hat(chunk)
+    if (next >= 0) stage_tile_async<sw_row>(vtile(next), lds_v, wave, lane);
+    chunk = next;
   }
 
   // ---- epilogue --------------------------------------------------------------------------
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
       const uint32_t w0 = f32_to_bf16_rne(acc[dt][4 * a + 0] * inv_l) | (f32_to_bf16_rne(acc[dt][4 * a + 1] * inv_l) << 16);
       const uint32_t w1 = f32_to_bf16_rne(acc[dt][4 * a + 2] * inv_l) | (f32_to_bf16_rne(acc[dt][4 * a + 3] * inv_l) << 16);
       *(uint2 *)(op + d0) = make_uint2(w0, w1);
-      if (train) {
+      if (TRAIN) {
         float *hp = p.o_hp + (bh * p.lq + qrow) * kD + d0;
         *(f32x4 *)hp = f32x4{acc_hp[dt][4 * a] * inv_l, acc_hp[dt][4 * a + 1] * inv_l,
                              acc_hp[dt][4 * a + 2] * inv_l, acc_hp[dt][4 * a + 3] * inv_l};
@@ -277,6 +276,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(FwdParams p) {
 
 hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t nsel, hipStream_t stream) {
   constexpr int WAVES = 4;
+  if (sel && (nsel > kMaxSel || nsel < 1)) return hipErrorInvalidValue;
   const Workspace w = workspace_layout(0, a.batch, a.heads, a.lq, a.lk);
   uint8_t *ws = (uint8_t *)a.workspace;
   FwdParams p{};
