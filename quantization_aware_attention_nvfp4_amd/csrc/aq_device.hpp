@@ -143,10 +143,47 @@ __device__ __forceinline__ void e2m1_pair(float &a, float &b) {
   b = r[1];
 }
 
+// Eight quotients rounded to E2M1 in one code register (byte i holds pair i), then converted
+// back; same rounding as e2m1_pair.
+__device__ __forceinline__ void e2m1_oct(float *r) {
+  uint32_t code = 0u;
+  code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[0], r[1], 1.0f, 0);
+  code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[2], r[3], 1.0f, 1);
+  code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[4], r[5], 1.0f, 2);
+  code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[6], r[7], 1.0f, 3);
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 1);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 2);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 3);
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+}
+
+// Softmax-probability fake quantization of 8 values of one block (see fq_prob_pair).
+__device__ __forceinline__ void fq_prob_oct(float *x, float S, float inv) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = x[i] * inv;
+  e2m1_oct(r);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = r[i] * S;
+}
+
 // Fake-quantize two non-negative values of one block (unit global scale, scale S and inv = 1/S,
 // inv = 0 for a zero block): E2M1(x / S) * S.
 __device__ __forceinline__ void fq_pos_pair(float &a, float &b, float S, float inv) {
   float ra = div_e4m3(a, S, inv), rb = div_e4m3(b, S, inv);
+  e2m1_pair(ra, rb);
+  a = ra * S;
+  b = rb * S;
+}
+
+// Softmax-probability variant: the quotient is the fp32 product x * fl(1/S) rather than the
+// correctly rounded x / S (they differ by at most one ulp, so only inputs within an ulp of an
+// E2M1 midpoint can round the other way - the same size as the error of the hardware exp2 that
+// produced x).  Used for P, whose forward and backward share this exact function.
+__device__ __forceinline__ void fq_prob_pair(float &a, float &b, float S, float inv) {
+  float ra = a * inv, rb = b * inv;
   e2m1_pair(ra, rb);
   a = ra * S;
   b = rb * S;

@@ -74,7 +74,7 @@ struct BwdParams {
 // 64-key halves.  LDS: K-hat rows, V-hat rows (A operands of S^T and dP^T, perm_row order) and the
 // K-hat tile (A operand of dQ^T), 96 KiB.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t *lds_k = lds, *lds_v = lds + 32768, *lds_kt = lds + 65536;
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nwork);
@@ -112,22 +112,32 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     const int64_t q_last = qc * kChunk + kChunk - 1;
     n_iter = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
   }
-  for (int64_t ch = 0; ch < n_iter; ++ch) {
-    __syncthreads();
-    {
-      const u32x4 *ks = p.kq + (bh * p.Ck + ch) * (kChunk * kD / 8);
-      const u32x4 *vs = p.vq + (bh * p.Ck + ch) * (kChunk * kD / 8);
-      const u32x4 *ts = p.kt + (bh * p.Ck + ch) * (kChunk * kD / 8);
+  // The next chunk's three tiles stream into registers while the current one is computed.
+  u32x4 stg[24];
+  auto load_chunk = [&](int64_t ch) {
+    const u32x4 *ks = p.kq + (bh * p.Ck + ch) * (kChunk * kD / 8);
+    const u32x4 *vs = p.vq + (bh * p.Ck + ch) * (kChunk * kD / 8);
+    const u32x4 *ts = p.kt + (bh * p.Ck + ch) * (kChunk * kD / 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int id = i * 256 + tid, r = id >> 4, j = id & 15;
-        const u32x4 a = ks[id], b = vs[id], c = ts[id];
-        *(u32x4 *)(lds_k + kq_off(r, j)) = a;
-        *(u32x4 *)(lds_v + kq_off(r, j)) = b;
-        *(u32x4 *)(lds_kt + row_off(r, j)) = c;
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int id = i * 256 + tid;
+      stg[i] = ks[id];
+      stg[8 + i] = vs[id];
+      stg[16 + i] = ts[id];
+    }
+  };
+  load_chunk(0);
+  for (int64_t ch = 0; ch < n_iter; ++ch) {
+    __syncthreads();  // every wave is done reading the previous chunk
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int id = i * 256 + tid, r = id >> 4, j = id & 15;
+      *(u32x4 *)(lds_k + kq_off(r, j)) = stg[i];
+      *(u32x4 *)(lds_v + kq_off(r, j)) = stg[8 + i];
+      *(u32x4 *)(lds_kt + row_off(r, j)) = stg[16 + i];
     }
     __syncthreads();
+    if (ch + 1 < n_iter) load_chunk(ch + 1);
     const bool tail = (ch + 1) * kChunk > p.lk;
     const bool diag = p.causal && (ch + 1) * kChunk - 1 > qc * kChunk + wave * 32;
 #pragma unroll
@@ -155,8 +165,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
           const float A = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -lse2));
           ds[rr] = A * (dp[rr] - Di);
         }
-        dsb[k2][0] = pack8_rne(ds);
-        dsb[k2][1] = pack8_rne(ds + 8);
+        dsb[k2][0] = pack8_cvt(ds);
+        dsb[k2][1] = pack8_cvt(ds + 8);
       }
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
@@ -177,9 +187,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int d0 = 32 * dt + 8 * a + 4 * hf;
-      const uint32_t w0 = f32_to_bf16_rne(acc[dt][4 * a] * p.scale) | (f32_to_bf16_rne(acc[dt][4 * a + 1] * p.scale) << 16);
-      const uint32_t w1 = f32_to_bf16_rne(acc[dt][4 * a + 2] * p.scale) | (f32_to_bf16_rne(acc[dt][4 * a + 3] * p.scale) << 16);
-      *(uint2 *)(op + d0) = make_uint2(w0, w1);
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      *(bf16x4 *)(op + d0) = bf16x4{(__bf16)(acc[dt][4 * a] * p.scale), (__bf16)(acc[dt][4 * a + 1] * p.scale),
+                                    (__bf16)(acc[dt][4 * a + 2] * p.scale), (__bf16)(acc[dt][4 * a + 3] * p.scale)};
     }
 }
 
@@ -194,7 +204,66 @@ constexpr int kQT = 64;  // queries per tile
 // columns XOR-swizzled by d so the 8 lanes reading 8 consecutive rows hit different banks.
 __device__ __forceinline__ int qt_off(int d, int g) { return d * 128 + ((((g >> 1) ^ (d & 7)) << 4) | ((g & 1) << 3)); }
 
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+// Per-lane statistics of one 64-query tile (two 32-query blocks).
+struct TileStats {
+  float mc[2], lse[2], dv[2];
+};
+
+__device__ __forceinline__ void load_stats(const BwdParams &p, int64_t bh, int64_t kc, int64_t qb, int n,
+                                           TileStats &st) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t qrow = qb * kQT + 32 * nt + n;
+    const bool ok = qrow < p.lq;
+    st.mc[nt] = ok ? p.cmax[(bh * p.Ck + kc) * p.lq + qrow] : 0.0f;
+    st.lse[nt] = ok ? p.lse[bh * p.lq + qrow] : 0.0f;
+    st.dv[nt] = ok ? p.dvec[bh * p.lq + qrow] : 0.0f;
+  }
+}
+
+// One 64-query tile in registers, 16 x 16 bytes per lane: Q-hat rows, dO rows (64 rows x 256 B
+// each), then the Q-hat and dO tiles (128 d-rows x 128 B each).
+__device__ __forceinline__ void load_tile(const BwdParams &p, int64_t bh, int64_t bb, int64_t hh, int64_t qb,
+                                          int tid, u32x4 *stg) {
+  const u32x4 *qs = p.qq + (bh * p.Cq * kChunk + qb * kQT) * (kD / 8);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = i * 256 + tid, r = id >> 4, j = id & 15;
+    const int64_t qrow = qb * kQT + r;
+    stg[i] = qs[id];
+    stg[4 + i] = u32x4{0u, 0u, 0u, 0u};
+    if (qrow < p.lq) stg[4 + i] = *(const u32x4 *)(p.d_o + bb * p.sdo.b + hh * p.sdo.h + qrow * p.sdo.l + 8 * j);
+  }
+  const int64_t tc = (qb * kQT) / kChunk, toff = (qb * kQT) % kChunk;
+  const uint8_t *qts = (const uint8_t *)(p.qt + (bh * p.Cq + tc) * (kChunk * kD / 8));
+  const uint8_t *ots = (const uint8_t *)(p.dot + (bh * p.Cq + tc) * (kChunk * kD / 8));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = i * 256 + tid, d = id >> 3, j = id & 7;
+    const int64_t src = (int64_t)d * 256 + toff * 2 + j * 16;
+    stg[8 + i] = *(const u32x4 *)(qts + src);
+    stg[12 + i] = *(const u32x4 *)(ots + src);
+  }
+}
+
+__device__ __forceinline__ void store_tile(uint8_t *lds_q, uint8_t *lds_o, uint8_t *lds_qt, uint8_t *lds_ot, int tid,
+                                           const u32x4 *stg) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = i * 256 + tid, r = id >> 4, j = id & 15;
+    *(u32x4 *)(lds_q + row_off(r, j)) = stg[i];
+    *(u32x4 *)(lds_o + row_off(r, j)) = stg[4 + i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = i * 256 + tid, d = id >> 3, j = id & 7;
+    const int dst = d * 128 + ((j ^ (d & 7)) << 4);
+    *(u32x4 *)(lds_qt + dst) = stg[8 + i];
+    *(u32x4 *)(lds_ot + dst) = stg[12 + i];
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t *lds_q = lds, *lds_o = lds + 16384, *lds_qt = lds + 32768, *lds_ot = lds + 49152;
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nwork);
@@ -203,6 +272,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int64_t kc = vid % p.Ck;
   const int64_t bb = bh / p.heads, hh = bh % p.heads;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, hf = lane >> 5;
+  const int64_t nqt = (p.lq + kQT - 1) / kQT;
+  const int64_t qt0 = p.causal ? (kc * kChunk) / kQT : 0;
+
+  // Prefetch the first tile and its statistics before the per-wave set-up.
+  TileStats st;
+  u32x4 stg[16];
+  load_stats(p, bh, kc, qt0, n, st);
+  load_tile(p, bh, bb, hh, qt0, tid, stg);
 
   // This wave's 32 keys as A rows (perm_row order), K-hat for S^T and V-hat for dP^T.
   bf16x8 kf[8], vf[8];
@@ -223,37 +300,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   }
   const int64_t key_base = kc * kChunk + wave * 32 + 16 * hf;  // key of register 0 (S^T layout)
   const bool tail = (kc + 1) * kChunk > p.lk;
-  const int64_t nqt = (p.lq + kQT - 1) / kQT;
-  const int64_t qt0 = p.causal ? (kc * kChunk) / kQT : 0;
 
   for (int64_t qb = qt0; qb < nqt; ++qb) {
+    __syncthreads();  // every wave is done reading the previous tile
+    store_tile(lds_q, lds_o, lds_qt, lds_ot, tid, stg);
+    const TileStats cur = st;
     __syncthreads();
-    {
-      // rows: 64 x 16 chunks of 16 bytes each for Q-hat and dO
-      const u32x4 *qs = p.qq + (bh * p.Cq * kChunk + qb * kQT) * (kD / 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int id = i * 256 + tid, r = id >> 4, j = id & 15;
-        const int64_t qrow = qb * kQT + r;
-        u32x4 o = {0u, 0u, 0u, 0u};
-        if (qrow < p.lq) o = *(const u32x4 *)(p.d_o + bb * p.sdo.b + hh * p.sdo.h + qrow * p.sdo.l + 8 * j);
-        *(u32x4 *)(lds_q + row_off(r, j)) = qs[id];
-        *(u32x4 *)(lds_o + row_off(r, j)) = o;
-      }
-      // tiles: 128 d-rows x 64 queries (half of a 128-query chunk tile)
-      const int64_t tc = (qb * kQT) / kChunk, toff = (qb * kQT) % kChunk;
-      const uint8_t *qts = (const uint8_t *)(p.qt + (bh * p.Cq + tc) * (kChunk * kD / 8));
-      const uint8_t *ots = (const uint8_t *)(p.dot + (bh * p.Cq + tc) * (kChunk * kD / 8));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int id = i * 256 + tid, d = id >> 3, j = id & 7;  // 8 chunks of 16 bytes per d-row
-        const int64_t src = (int64_t)d * 256 + toff * 2 + j * 16;
-        const int dst = d * 128 + ((j ^ (d & 7)) << 4);
-        *(u32x4 *)(lds_qt + dst) = *(const u32x4 *)(qts + src);
-        *(u32x4 *)(lds_ot + dst) = *(const u32x4 *)(ots + src);
-      }
+    if (qb + 1 < nqt) {  // the next tile streams in while this one is computed
+      load_stats(p, bh, kc, qb + 1, n, st);
+      load_tile(p, bh, bb, hh, qb + 1, tid, stg);
     }
-    __syncthreads();
 
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -261,47 +317,50 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       const bool qvalid = qrow < p.lq;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bf16x8 bq = as_bf16x8(*(const u32x4 *)(lds_q + row_off(32 * nt + n, 2 * t + hf)));
-        const bf16x8 bo = as_bf16x8(*(const u32x4 *)(lds_o + row_off(32 * nt + n, 2 * t + hf)));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], bq, s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], bo, dp, 0, 0, 0);
+      for (int t0 = 0; t0 < 8; t0 += 4) {
+        bf16x8 bq[4], bo[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          bq[t] = as_bf16x8(*(const u32x4 *)(lds_q + row_off(32 * nt + n, 2 * (t0 + t) + hf)));
+          bo[t] = as_bf16x8(*(const u32x4 *)(lds_o + row_off(32 * nt + n, 2 * (t0 + t) + hf)));
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t0 + t], bq[t], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t0 + t], bo[t], dp, 0, 0, 0);
+        }
       }
-      const float mc = qvalid ? p.cmax[(bh * p.Ck + kc) * p.lq + qrow] : 0.0f;
-      const float lse2 = qvalid ? p.lse[bh * p.lq + qrow] : 0.0f;
-      const float Di = qvalid ? p.dvec[bh * p.lq + qrow] : 0.0f;
+      const float mc = cur.mc[nt], lse2 = cur.lse[nt], Di = cur.dv[nt];
       if (tail || !qvalid || (p.causal && key_base + 15 > qrow)) {
         const int64_t last = !qvalid ? -1 : (p.causal && qrow < p.lk - 1 ? qrow : p.lk - 1);
         mask_tail(s, valid_prefix(key_base, last));
       }
       // P exactly as the forward formed it, its fake quantization, and the weights.
-      float P[16], Ah[16], ds[16];
-      float am = 0.0f;
+      float Ah[16], ds[16];
+      float bm = s[0];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        P[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -mc));
-        am = fmaxf(am, P[rr]);
-      }
+      for (int rr = 1; rr < 16; ++rr) bm = fmaxf(bm, s[rr]);
       const float w = __builtin_amdgcn_exp2f(mc - lse2);
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        Ah[rr] = P[rr];
-        ds[rr] = (P[rr] * w) * (dp[rr] - Di);
+        Ah[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -mc));
+        ds[rr] = (Ah[rr] * w) * (dp[rr] - Di);
       }
       if (p.quant_p) {
+        const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(bm, p.c, -mc));  // as the forward
         const float S = block_scale_unit(am);
         const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
-#pragma unroll
-        for (int rr = 0; rr < 16; rr += 2) fq_pos_pair(Ah[rr], Ah[rr + 1], S, inv);
+        fq_prob_oct(Ah, S, inv);
+        fq_prob_oct(Ah + 8, S, inv);
       }
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) Ah[rr] *= w;
       // Move A-hat and dS to one key per lane: D[query][key] = sum_k X[query][k] onehot[k][key].
       f32x16 ta = f32x16{}, ts = f32x16{};
-      ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_rne(Ah), one0, ta, 0, 0, 0);
-      ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_rne(Ah + 8), one1, ta, 0, 0, 0);
-      ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_rne(ds), one0, ts, 0, 0, 0);
-      ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_rne(ds + 8), one1, ts, 0, 0, 0);
+      ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(Ah), one0, ta, 0, 0, 0);
+      ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(Ah + 8), one1, ta, 0, 0, 0);
+      ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds), one0, ts, 0, 0, 0);
+      ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds + 8), one1, ts, 0, 0, 0);
       // ta/ts register r of lane (key j, half h) holds query 8*(r/4) + 4*h + r%4 of this 32-query
       // block; k-slot (h, jj) of step s2 is register 8*s2 + jj, i.e. queries 16*s2 + 4h + {0..3}
       // and 16*s2 + 8 + 4h + {0..3}.
@@ -315,6 +374,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         }
         const bf16x8 ba = pack8_exact(fa), bs = pack8_exact(fs);
         const int g0 = (32 * nt + 16 * s2 + 4 * hf) >> 2;  // 4-query group index
+        bf16x8 ao[4], aq[4];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int d = 32 * dt + n;
@@ -322,10 +382,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
           const uint2 o1 = *(const uint2 *)(lds_ot + qt_off(d, g0 + 2));
           const uint2 q0 = *(const uint2 *)(lds_qt + qt_off(d, g0));
           const uint2 q1 = *(const uint2 *)(lds_qt + qt_off(d, g0 + 2));
-          const bf16x8 ao = as_bf16x8(u32x4{o0.x, o0.y, o1.x, o1.y});
-          const bf16x8 aq = as_bf16x8(u32x4{q0.x, q0.y, q1.x, q1.y});
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, ba, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bs, dk[dt], 0, 0, 0);
+          ao[dt] = as_bf16x8(u32x4{o0.x, o0.y, o1.x, o1.y});
+          aq[dt] = as_bf16x8(u32x4{q0.x, q0.y, q1.x, q1.y});
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[dt], ba, dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[dt], bs, dk[dt], 0, 0, 0);
         }
       }
     }
@@ -336,16 +399,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   if (key >= p.lk) return;
   uint16_t *kp = p.dk + bb * p.sdk.b + hh * p.sdk.h + key * p.sdk.l;
   uint16_t *vp = p.dv + bb * p.sdv.b + hh * p.sdv.h + key * p.sdv.l;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int d0 = 32 * dt + 8 * a + 4 * hf;
-      *(uint2 *)(kp + d0) = make_uint2(
-          f32_to_bf16_rne(dk[dt][4 * a] * p.scale) | (f32_to_bf16_rne(dk[dt][4 * a + 1] * p.scale) << 16),
-          f32_to_bf16_rne(dk[dt][4 * a + 2] * p.scale) | (f32_to_bf16_rne(dk[dt][4 * a + 3] * p.scale) << 16));
-      *(uint2 *)(vp + d0) = make_uint2(f32_to_bf16_rne(dv[dt][4 * a]) | (f32_to_bf16_rne(dv[dt][4 * a + 1]) << 16),
-                                       f32_to_bf16_rne(dv[dt][4 * a + 2]) | (f32_to_bf16_rne(dv[dt][4 * a + 3]) << 16));
+      *(bf16x4 *)(kp + d0) = bf16x4{(__bf16)(dk[dt][4 * a] * p.scale), (__bf16)(dk[dt][4 * a + 1] * p.scale),
+                                    (__bf16)(dk[dt][4 * a + 2] * p.scale), (__bf16)(dk[dt][4 * a + 3] * p.scale)};
+      *(bf16x4 *)(vp + d0) = bf16x4{(__bf16)dv[dt][4 * a], (__bf16)dv[dt][4 * a + 1], (__bf16)dv[dt][4 * a + 2],
+                                    (__bf16)dv[dt][4 * a + 3]};
     }
 }
 

@@ -42,11 +42,16 @@ __device__ __forceinline__ bf16x8 pack8_rne(const float *f) {
   w.w = f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16);
   return as_bf16x8(w);
 }
-// Eight fp32 values that are exact in bf16 -> bf16x8.
-__device__ __forceinline__ bf16x8 pack8_exact(const float *f) {
-  return as_bf16x8(u32x4{pack_exact_bf16(f[0], f[1]), pack_exact_bf16(f[2], f[3]), pack_exact_bf16(f[4], f[5]),
-                         pack_exact_bf16(f[6], f[7])});
+// Eight fp32 values -> bf16x8 through the hardware packed conversion (v_cvt_pk_bf16_f32,
+// round to nearest even; exact for values that are already bf16).
+__device__ __forceinline__ bf16x8 pack8_cvt(const float *f) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)f[i];
+  return r;
 }
+// Eight fp32 values that are exact in bf16 -> bf16x8.
+__device__ __forceinline__ bf16x8 pack8_exact(const float *f) { return pack8_cvt(f); }
 
 // Asynchronous 16-byte global -> LDS copy: lane l of the wave writes LDS bytes
 // [lds_base + 16*l, +16) (checked on the GPU); lds_base must be the same in every lane.

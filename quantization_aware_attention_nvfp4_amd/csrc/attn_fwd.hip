@@ -177,11 +177,17 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
     }
 
     // ---- running max (refreshed once per chunk) -----------------------------------------
-    float cm = -__builtin_inff();
+    // Block maxima of the logits first: each lane's 16 registers of a sub-tile are one P block,
+    // and exp2 is monotone, so the block's P amax is exp2 of its logit max.
+    float bmax[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt) {
+      float mx = s[kt][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) cm = fmaxf(cm, s[kt][r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      bmax[kt] = mx;
+    }
+    float cm = fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3]));
     cm = pair_max(cm);
     const float m_new = fmaxf(m_run, cm * p.c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
@@ -206,30 +212,26 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       float P[16];
-      float am = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         P[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], p.c, -m_new));
         psum += P[r];
-        am = fmaxf(am, P[r]);
       }
       bf16x8 ph[2];
       if (TRAIN) {
-        ph[0] = pack8_rne(P);
-        ph[1] = pack8_rne(P + 8);
+        ph[0] = pack8_cvt(P);
+        ph[1] = pack8_cvt(P + 8);
       }
-      bf16x8 pq[2];
       if (p.quant_p) {
+        const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(bmax[kt], p.c, -m_new));
         const float S = block_scale_unit(am);
         const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) fq_pos_pair(P[r], P[r + 1], S, inv);
-        pq[0] = pack8_exact(P);
-        pq[1] = pack8_exact(P + 8);
-      } else {
-        pq[0] = pack8_rne(P);
-        pq[1] = pack8_rne(P + 8);
+        fq_prob_oct(P, S, inv);
+        fq_prob_oct(P + 8, S, inv);
       }
+      bf16x8 pq[2];
+      pq[0] = pack8_cvt(P);
+      pq[1] = pack8_cvt(P + 8);
       bf16x8 a[2][4];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -260,9 +262,10 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int d0 = 32 * dt + 8 * a + 4 * hf;
-      const uint32_t w0 = f32_to_bf16_rne(acc[dt][4 * a + 0] * inv_l) | (f32_to_bf16_rne(acc[dt][4 * a + 1] * inv_l) << 16);
-      const uint32_t w1 = f32_to_bf16_rne(acc[dt][4 * a + 2] * inv_l) | (f32_to_bf16_rne(acc[dt][4 * a + 3] * inv_l) << 16);
-      *(uint2 *)(op + d0) = make_uint2(w0, w1);
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 w = {(__bf16)(acc[dt][4 * a + 0] * inv_l), (__bf16)(acc[dt][4 * a + 1] * inv_l),
+                        (__bf16)(acc[dt][4 * a + 2] * inv_l), (__bf16)(acc[dt][4 * a + 3] * inv_l)};
+      *(bf16x4 *)(op + d0) = w;
       if (TRAIN) {
         float *hp = p.o_hp + (bh * p.lq + qrow) * kD + d0;
         *(f32x4 *)hp = f32x4{acc_hp[dt][4 * a] * inv_l, acc_hp[dt][4 * a + 1] * inv_l,
