@@ -195,14 +195,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------------------------
 // dK, dV: workgroup = (head, 128-key chunk), 4 waves x 32 keys, loop over 64-query tiles.
-// LDS per tile: Q-hat rows and dO rows [64][256 B] (B operands of S^T and dP^T), Q-hat^T and
-// dO^T [128 d][128 B] (A operands of dK^T and dV^T), 64 KiB.
+// LDS: per tile Q-hat rows and dO rows [64][256 B] (B operands of S^T and dP^T), Q-hat^T and
+// dO^T [128 d][128 B] (A operands of dK^T and dV^T), 64 KiB; plus the chunk's K-hat and V-hat
+// rows (A operands of S^T and dP^T), 64 KiB.
 // ---------------------------------------------------------------------------------------------
 constexpr int kQT = 64;  // queries per tile
 
-// Byte offset of the 8-byte group g (4 queries) of row d in a [128 d][64 q] tile; 16-byte
-// columns XOR-swizzled by d so the 8 lanes reading 8 consecutive rows hit different banks.
-__device__ __forceinline__ int qt_off(int d, int g) { return d * 128 + ((((g >> 1) ^ (d & 7)) << 4) | ((g & 1) << 3)); }
+// Byte offset of the 8-byte group g (4 queries) of row d in a [128 d][64 q] tile.  The 8-byte
+// slots of each 128-byte row are XOR-swizzled by d/2, so the 32 lanes reading the same group of
+// 32 consecutive rows (two rows per 256-byte bank window) use 32 distinct slots.
+__device__ __forceinline__ int qt_swz(int d) { return (d >> 1) & 15; }
+__device__ __forceinline__ int qt_off(int d, int g) { return d * 128 + ((g ^ qt_swz(d)) << 3); }
 
 // Per-lane statistics of one 64-query tile (two 32-query blocks).
 struct TileStats {
@@ -256,16 +259,20 @@ __device__ __forceinline__ void store_tile(uint8_t *lds_q, uint8_t *lds_o, uint8
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int id = i * 256 + tid, d = id >> 3, j = id & 7;
-    const int dst = d * 128 + ((j ^ (d & 7)) << 4);
-    *(u32x4 *)(lds_qt + dst) = stg[8 + i];
-    *(u32x4 *)(lds_ot + dst) = stg[12 + i];
+    // 16-byte chunk j holds 8-byte groups 2j, 2j+1; under the swizzle they land in chunk
+    // j ^ (f/2), with the two halves exchanged when f is odd.
+    const int id = i * 256 + tid, d = id >> 3, j = id & 7, f = qt_swz(d);
+    const int dst = d * 128 + ((j ^ (f >> 1)) << 4);
+    const u32x4 a = stg[8 + i], b = stg[12 + i];
+    *(u32x4 *)(lds_qt + dst) = (f & 1) ? u32x4{a.z, a.w, a.x, a.y} : a;
+    *(u32x4 *)(lds_ot + dst) = (f & 1) ? u32x4{b.z, b.w, b.x, b.y} : b;
   }
 }
 
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t *lds_q = lds, *lds_o = lds + 16384, *lds_qt = lds + 32768, *lds_ot = lds + 49152;
+  uint8_t *lds_k = lds + 65536, *lds_v = lds + 98304;  // this chunk's K-hat and V-hat rows
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nwork);
   if (vid < 0) return;
   const int64_t bh = vid / p.Ck;
@@ -281,16 +288,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   load_stats(p, bh, kc, qt0, n, st);
   load_tile(p, bh, bb, hh, qt0, tid, stg);
 
-  // This wave's 32 keys as A rows (perm_row order), K-hat for S^T and V-hat for dP^T.
-  bf16x8 kf[8], vf[8];
+  // This chunk's K-hat and V-hat rows (A operands of S^T and dP^T, read in perm_row order).
   {
-    const int64_t row = bh * p.Ck * kChunk + kc * kChunk + wave * 32 + perm_row(n);
+    const u32x4 *ks = p.kq + (bh * p.Ck + kc) * (kChunk * kD / 8);
+    const u32x4 *vs = p.vq + (bh * p.Ck + kc) * (kChunk * kD / 8);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      kf[t] = as_bf16x8(p.kq[row * (kD / 8) + 2 * t + hf]);
-      vf[t] = as_bf16x8(p.vq[row * (kD / 8) + 2 * t + hf]);
+    for (int i = 0; i < 8; ++i) {
+      const int id = i * 256 + tid, r = id >> 4, j = id & 15;
+      *(u32x4 *)(lds_k + kq_off(r, j)) = ks[id];
+      *(u32x4 *)(lds_v + kq_off(r, j)) = vs[id];
     }
   }
+  const int krow = wave * 32 + perm_row(n);
   const bf16x8 one0 = onehot_b(lane, 0), one1 = onehot_b(lane, 1);
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -317,18 +326,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       const bool qvalid = qrow < p.lq;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int t0 = 0; t0 < 8; t0 += 4) {
-        bf16x8 bq[4], bo[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          bq[t] = as_bf16x8(*(const u32x4 *)(lds_q + row_off(32 * nt + n, 2 * (t0 + t) + hf)));
-          bo[t] = as_bf16x8(*(const u32x4 *)(lds_o + row_off(32 * nt + n, 2 * (t0 + t) + hf)));
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t0 + t], bq[t], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t0 + t], bo[t], dp, 0, 0, 0);
-        }
+      for (int t = 0; t < 8; ++t) {
+        const bf16x8 ak = as_bf16x8(*(const u32x4 *)(lds_k + kq_off(krow, 2 * t + hf)));
+        const bf16x8 bq = as_bf16x8(*(const u32x4 *)(lds_q + row_off(32 * nt + n, 2 * t + hf)));
+        const bf16x8 av = as_bf16x8(*(const u32x4 *)(lds_v + kq_off(krow, 2 * t + hf)));
+        const bf16x8 bo = as_bf16x8(*(const u32x4 *)(lds_o + row_off(32 * nt + n, 2 * t + hf)));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bo, dp, 0, 0, 0);
       }
       const float mc = cur.mc[nt], lse2 = cur.lse[nt], Di = cur.dv[nt];
       if (tail || !qvalid || (p.causal && key_base + 15 > qrow)) {
@@ -374,7 +378,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         }
         const bf16x8 ba = pack8_exact(fa), bs = pack8_exact(fs);
         const int g0 = (32 * nt + 16 * s2 + 4 * hf) >> 2;  // 4-query group index
-        bf16x8 ao[4], aq[4];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int d = 32 * dt + n;
@@ -382,13 +385,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           const uint2 o1 = *(const uint2 *)(lds_ot + qt_off(d, g0 + 2));
           const uint2 q0 = *(const uint2 *)(lds_qt + qt_off(d, g0));
           const uint2 q1 = *(const uint2 *)(lds_qt + qt_off(d, g0 + 2));
-          ao[dt] = as_bf16x8(u32x4{o0.x, o0.y, o1.x, o1.y});
-          aq[dt] = as_bf16x8(u32x4{q0.x, q0.y, q1.x, q1.y});
-        }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[dt], ba, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[dt], bs, dk[dt], 0, 0, 0);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{o0.x, o0.y, o1.x, o1.y}), ba, dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{q0.x, q0.y, q1.x, q1.y}), bs, dk[dt], 0, 0, 0);
         }
       }
     }
@@ -464,7 +462,7 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
   // Dynamic LDS above 64 KiB must be allowed per kernel.
   if ((e = hipFuncSetAttribute((const void *)bwd_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 98304)))
     return e;
-  if ((e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 65536)))
+  if ((e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 131072)))
     return e;
   p.nwork = bh * p.Cq;
   p.per_xcd = (p.nwork + 7) / 8;
@@ -473,7 +471,7 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
 
   p.nwork = bh * p.Ck;
   p.per_xcd = (p.nwork + 7) / 8;
-  AQ_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(256), 65536, stream, p);
+  AQ_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(256), 131072, stream, p);
   return hipGetLastError();
 }
 

@@ -14,12 +14,14 @@ namespace aq {
 // 16*h + r: each lane then owns 16 consecutive local indices of one column.
 __device__ __forceinline__ int perm_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
-// Byte offset of 16-byte column j of row r in a 256-byte-row LDS tile, XOR-swizzled so that the
-// 8 lanes that read the same column of 8 rows together hit 8 different bank groups.
-// kq_off serves A-operand reads in perm_row order (rows {0..3, 16..19} + 4k together), row_off
-// reads of 8 consecutive rows.
-__device__ __forceinline__ int kq_off(int r, int j) { return r * 256 + ((j ^ ((r & 3) | ((r >> 2) & 4))) << 4); }
-__device__ __forceinline__ int row_off(int r, int j) { return r * 256 + ((j ^ (r & 7)) << 4); }
+// XOR swizzles of the 16-byte columns of a 256-byte-row LDS tile, so that 16 lanes reading the
+// same logical column of 16 different rows hit 16 different 16-byte bank groups.
+// sw_kq serves A-operand reads in perm_row order (lanes 0..15 read rows {0..3, 16..19, 4..7,
+// 20..23} + 8k), sw_row reads of consecutive rows.
+__device__ __forceinline__ int sw_kq(int r) { return (r & 3) | ((r >> 2) & 4) | ((r & 4) << 1); }
+__device__ __forceinline__ int sw_row(int r) { return r & 15; }
+__device__ __forceinline__ int kq_off(int r, int j) { return r * 256 + ((j ^ sw_kq(r)) << 4); }
+__device__ __forceinline__ int row_off(int r, int j) { return r * 256 + ((j ^ sw_row(r)) << 4); }
 
 // One-hot B operand of a 32x32x16 MFMA that moves A's k-slot values into column j: lane (column
 // j = l%32, half h) holds 1 in slot jj where j == 16h + 8*step + jj.
@@ -55,8 +57,14 @@ __device__ __forceinline__ bf16x8 pack8_exact(const float *f) { return pack8_cvt
 
 // Asynchronous 16-byte global -> LDS copy: lane l of the wave writes LDS bytes
 // [lds_base + 16*l, +16) (checked on the GPU); lds_base must be the same in every lane.
+// Written as inline assembly (M0 = LDS base, then global_load_lds_dwordx4) so the compiler does
+// not treat every later LDS read as dependent on the copy and drain all copies before it; the
+// callers order copies and reads themselves with AQ_WAIT_VMCNT and s_barrier.  The compiler's
+// own vmcnt waits stay correct: vector memory operations complete in order, so extra copies in
+// flight can only make it wait longer, never shorter.
 __device__ __forceinline__ void load_lds16(const void *gsrc, uint8_t *lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(gsrc) : "memory", "m0");
 }
 
 // Stage a 32 KiB tile ([128 rows][256 bytes] in global memory) into LDS with the XOR swizzle
@@ -73,8 +81,6 @@ __device__ __forceinline__ void stage_tile_async(const uint8_t *gtile, uint8_t *
     load_lds16(gtile + r * 256 + j * 16, lds_tile + (i * 256 + 64 * wave) * 16);
   }
 }
-__device__ __forceinline__ int sw_kq(int r) { return (r & 3) | ((r >> 2) & 4); }
-__device__ __forceinline__ int sw_row(int r) { return r & 7; }
 
 // Wait until at most N of this wave's vector-memory operations are outstanding.
 #define AQ_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
