@@ -96,6 +96,8 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  * fake-quant with BF16 matmul").
  *
  * q [B, H, lq, 128], k and v [B, H, lk, 128], o [B, H, lq, 128]: bf16, layout by strides.
+ * Every bf16 tensor of the attention entry points starts 16-byte aligned and has strides that
+ * are multiples of 8 elements and below 2^24 (rows move in 16-byte pieces); lq, lk <= 2^30.
  * Q-hat, K-hat along D and V-hat along keys are fake-quantized per quant_flags.  The keys are
  * visited in chunks of 128 ([0,128), [128,256), ...); in chunk c the running row maximum m_c of
  * the logits softmax_scale * <q-hat, k-hat> is refreshed first, then P = exp(logit - m_c) is
@@ -113,8 +115,8 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  * workspace : DEVICE scratch of at least attn_qat_workspace_size(0, ...) bytes, 256-byte aligned.
  * Errors: AQ_EINVAL (null q/k/v/o/workspace, head_size != 128 [API]
  * get_supported_head_sizes, sizes <= 0, non-finite or non-positive softmax_scale, flags outside
- * AQ_QUANT_ALL, strides that are not positive, workspace too small); AQ_ENOTSUP
- * (num_kv_heads != num_heads, causal with lq != lk).
+ * AQ_QUANT_ALL, strides that are not positive, misaligned tensors or strides, workspace too
+ * small); AQ_ENOTSUP (num_kv_heads != num_heads, causal with lq != lk, lengths above 2^30).
  * ------------------------------------------------------------------------------------------- */
 int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch, int num_heads,
                  int num_kv_heads, int head_size, int64_t lq, int64_t lk, aq_strides sq,

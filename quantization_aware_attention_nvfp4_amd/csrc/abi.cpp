@@ -37,6 +37,15 @@ aq::Strides cvt(aq_strides s) { return aq::Strides{s.b, s.h, s.l}; }
 
 bool strides_ok(aq_strides s) { return s.b > 0 && s.h > 0 && s.l > 0; }
 
+// The attention kernels move rows in 16-byte pieces and keep per-lane row offsets in 32 bits:
+// bf16 tensors must start 16-byte aligned, with strides that are multiples of 8 elements and
+// below 2^24 elements.
+bool tensor_ok(const void *p, aq_strides s) {
+  const int64_t lim = (int64_t)1 << 24;
+  return ((uintptr_t)p & 15) == 0 && s.b % 8 == 0 && s.h % 8 == 0 && s.l % 8 == 0 && s.b < lim * 64 &&
+         s.h < lim * 64 && s.l < lim;
+}
+
 // Checks shared by the attention entry points ("attn_qat_train" page: head sizes [128],
 // AttentionImpl(num_heads, head_size, softmax_scale, causal, num_kv_heads)).
 int check_attention(int batch, int num_heads, int num_kv_heads, int head_size, int64_t lq,
@@ -54,6 +63,9 @@ int check_attention(int batch, int num_heads, int num_kv_heads, int head_size, i
     return fail(AQ_ENOTSUP, "num_kv_heads (%d) must equal num_heads (%d)", num_kv_heads, num_heads);
   if (causal && lq != lk)
     return fail(AQ_ENOTSUP, "causal attention needs lq == lk (got %lld, %lld)", (long long)lq,
+                (long long)lk);
+  if (lq > ((int64_t)1 << 30) || lk > ((int64_t)1 << 30))
+    return fail(AQ_ENOTSUP, "sequence lengths above 2^30 are not supported (lq %lld, lk %lld)", (long long)lq,
                 (long long)lk);
   return AQ_OK;
 }
@@ -106,6 +118,9 @@ int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch
   if (rc) return rc;
   if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so))
     return fail(AQ_EINVAL, "attn_qat_fwd: strides must be positive with d contiguous");
+  if (!tensor_ok(q, sq) || !tensor_ok(k, sk) || !tensor_ok(v, sv) || !tensor_ok(o, so))
+    return fail(AQ_EINVAL, "attn_qat_fwd: tensors must be 16-byte aligned with strides that are multiples of 8 "
+                           "elements and below 2^24");
   const size_t need = aq::workspace_bytes(0, batch, num_heads, lq, lk);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
     return fail(AQ_EINVAL, "attn_qat_fwd: workspace must be 256-byte aligned and hold %zu bytes",
@@ -136,6 +151,10 @@ int attn_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp,
   if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(sdo) ||
       !strides_ok(sdq) || !strides_ok(sdk) || !strides_ok(sdv))
     return fail(AQ_EINVAL, "attn_qat_bwd: strides must be positive with d contiguous");
+  if (!tensor_ok(q, sq) || !tensor_ok(k, sk) || !tensor_ok(v, sv) || !tensor_ok(d_o, sdo) || !tensor_ok(dq, sdq) ||
+      !tensor_ok(dk, sdk) || !tensor_ok(dv, sdv))
+    return fail(AQ_EINVAL, "attn_qat_bwd: tensors must be 16-byte aligned with strides that are multiples of 8 "
+                           "elements and below 2^24");
   const size_t need = aq::workspace_bytes(1, batch, num_heads, lq, lk);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
     return fail(AQ_EINVAL, "attn_qat_bwd: workspace must be 256-byte aligned and hold %zu bytes",
@@ -178,6 +197,10 @@ int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void 
                 cube_t * cube_h * cube_w);
   if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so))
     return fail(AQ_EINVAL, "vsa_qat_fwd: strides must be positive with d contiguous");
+  if (!tensor_ok(q, sq) || !tensor_ok(k, sk) || !tensor_ok(v, sv) || !tensor_ok(o_fine, so) ||
+      (o_coarse && !tensor_ok(o_coarse, so)))
+    return fail(AQ_EINVAL, "vsa_qat_fwd: tensors must be 16-byte aligned with strides that are multiples of 8 "
+                           "elements and below 2^24");
   const size_t need = aq::workspace_bytes(2, batch, num_heads, seq_len, seq_len);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
     return fail(AQ_EINVAL, "vsa_qat_fwd: workspace must be 256-byte aligned and hold %zu bytes",

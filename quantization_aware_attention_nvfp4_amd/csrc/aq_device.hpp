@@ -169,6 +169,17 @@ __device__ __forceinline__ void fq_prob_oct(float *x, float S, float inv) {
   for (int i = 0; i < 8; ++i) x[i] = r[i] * S;
 }
 
+// The same quantization with another dequantization factor: x = E2M1(x * inv) * sdq (the backward
+// folds the probability normalisation into sdq = S * exp2(m_c - lse)).
+__device__ __forceinline__ void fq_prob_oct_dq(float *x, float inv, float sdq) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = x[i] * inv;
+  e2m1_oct(r);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = r[i] * sdq;
+}
+
 // Fake-quantize two non-negative values of one block (unit global scale, scale S and inv = 1/S,
 // inv = 0 for a zero block): E2M1(x / S) * S.
 __device__ __forceinline__ void fq_pos_pair(float &a, float &b, float S, float inv) {

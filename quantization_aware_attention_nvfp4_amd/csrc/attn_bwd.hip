@@ -50,8 +50,6 @@ __global__ __launch_bounds__(256) void dvec_kernel(const uint16_t *__restrict__ 
 
 struct BwdParams {
   const u32x4 *qq;    // Q-hat rows   [BH, Cq*128, 128]
-  const u32x4 *qt;    // Q-hat tiles  [BH, Cq, 128, 128]
-  const u32x4 *dot;   // dO tiles     [BH, Cq, 128, 128]
   const u32x4 *kq;    // K-hat rows   [BH, Ck*128, 128]
   const u32x4 *kt;    // K-hat tiles  [BH, Ck, 128, 128]
   const u32x4 *vq;    // V-hat rows   [BH, Ck*128, 128]
@@ -194,219 +192,267 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: workgroup = (head, 128-key chunk), 4 waves x 32 keys, loop over 64-query tiles.
-// LDS: per tile Q-hat rows and dO rows [64][256 B] (B operands of S^T and dP^T), Q-hat^T and
-// dO^T [128 d][128 B] (A operands of dK^T and dV^T), 64 KiB; plus the chunk's K-hat and V-hat
-// rows (A operands of S^T and dP^T), 64 KiB.
+// dK, dV: workgroup = (head, 128-key chunk), 8 waves, loop over 64-query tiles.  Wave w owns keys
+// 32*(w%4) .. +31 of the chunk and queries 32*(w/4) .. +31 of every tile; the two waves that share
+// keys add their partial dK/dV through LDS at the end.  Two waves per SIMD, so one wave's
+// exponentials and fake quantization overlap the other's MFMAs.
+//
+// LDS (bytes):
+//   [0, 32K)         K-hat rows of the chunk (A operand of S^T, perm_row order, sw_kq swizzle)
+//   [32K, 64K)       V-hat rows of the chunk (A operand of dP^T)
+//   [64K, 128K)      two tile buffers, each Q-hat rows [64][256 B] then dO rows [64][256 B]
+//                    (B operands of S^T and dP^T; read transposed as the A operands of dK^T and
+//                    dV^T), sw_qr swizzle
+//   [128K, 128K+1.5K) two statistic buffers, each chunk max, lse and D of the tile's 64 queries
+// Tile qb+1 is copied asynchronously into the other buffer while tile qb is computed; one barrier
+// per tile.
 // ---------------------------------------------------------------------------------------------
 constexpr int kQT = 64;  // queries per tile
+constexpr int kDkdvThreads = 512;
+constexpr int kLdsR = 65536, kLdsStat = 131072;
+constexpr int kLdsOneHot = kLdsStat + 2 * 768;  // two one-hot B operands, 16 bytes per lane
+constexpr int kDkdvLds = kLdsOneHot + 2048;
 
-// Byte offset of the 8-byte group g (4 queries) of row d in a [128 d][64 q] tile.  The 8-byte
-// slots of each 128-byte row are XOR-swizzled by d/2, so the 32 lanes reading the same group of
-// 32 consecutive rows (two rows per 256-byte bank window) use 32 distinct slots.
-__device__ __forceinline__ int qt_swz(int d) { return (d >> 1) & 15; }
-__device__ __forceinline__ int qt_off(int d, int g) { return d * 128 + ((g ^ qt_swz(d)) << 3); }
+// Lane layout of the S^T B operand: lane n takes query pi(n) of its wave's 32 (bits 2 and 3 of n
+// exchanged).  After the one-hot transposition the 8 k-slots of each lane half are then 8
+// consecutive queries, so the matching A operand is one transposed LDS read pair.
+__device__ __forceinline__ int pi_q(int n) { return (n & 19) | ((n & 4) << 1) | ((n & 8) >> 1); }
 
-// Per-lane statistics of one 64-query tile (two 32-query blocks).
-struct TileStats {
-  float mc[2], lse[2], dv[2];
+// Per-lane constants of the dK/dV kernel.  Byte offsets whose swizzled 16-byte column depends on
+// a loop index t carry the lane's XOR term in bits 5..7, so column pair t is `off ^ (32 * t)`.
+struct DkdvLane {
+  int k_off;     // K-hat/V-hat A-operand row kg*32 + perm_row(n), column hf
+  int r_off;     // Q-hat/dO B-operand row qloc, column hf
+  int tr_off;    // transposed reads, query group a = 0; bits 6..7 hold e (d tile dt enters as ^ 64*dt)
+  int qloc;      // tile-local query of this lane's S^T column
+  uint32_t q_voff[2], o_voff[2];  // copy offsets of this lane's two Q-hat and dO rows of a tile
+  int o_row[2];  // those rows, tile-local
+  int key_base;  // head-local key of register 0
 };
 
-__device__ __forceinline__ void load_stats(const BwdParams &p, int64_t bh, int64_t kc, int64_t qb, int n,
-                                           TileStats &st) {
+// Copies of tile qb into buffer `buf`: Q-hat rows from the workspace, dO rows from the caller's
+// tensor (rows past lq repeat row lq-1; every product they feed is masked), and the three
+// per-query statistics (entries past lq repeat entry lq-1).  Per lane: 4 copies of 16 bytes, plus
+// one 4-byte copy in waves 0..2.
+__device__ __forceinline__ void dkdv_stage_tile(const BwdParams &p, const DkdvLane &ln, int64_t bh, int64_t bb,
+                                                int64_t hh, int64_t kc, int64_t qb, uint8_t *lds, int buf, int wave,
+                                                int lane) {
+  uint8_t *rq = lds + kLdsR + buf * 32768, *ro = rq + 16384;
+  const u32x4 *qsrc = p.qq + (bh * p.Cq * kChunk + qb * kQT) * (kD / 8);
+  const uint16_t *osrc = p.d_o + bb * p.sdo.b + hh * p.sdo.h + qb * kQT * p.sdo.l;
+  const int64_t rem = p.lq - 1 - qb * kQT;  // last valid tile-local row
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int64_t qrow = qb * kQT + 32 * nt + n;
-    const bool ok = qrow < p.lq;
-    st.mc[nt] = ok ? p.cmax[(bh * p.Ck + kc) * p.lq + qrow] : 0.0f;
-    st.lse[nt] = ok ? p.lse[bh * p.lq + qrow] : 0.0f;
-    st.dv[nt] = ok ? p.dvec[bh * p.lq + qrow] : 0.0f;
+  for (int i = 0; i < 2; ++i) {
+    load_lds16_s(qsrc, ln.q_voff[i], rq + (i * 8 + wave) * 1024);
+    uint32_t ov = ln.o_voff[i];
+    if (rem < kQT - 1 && ln.o_row[i] > rem)  // tail tile: repeat the last valid row
+      ov = (uint32_t)(rem * p.sdo.l * 2) + (ln.o_voff[i] - (uint32_t)(ln.o_row[i] * p.sdo.l * 2));
+    load_lds16_s(osrc, ov, ro + (i * 8 + wave) * 1024);
+  }
+  if (wave < 3) {
+    const float *src = (wave == 0 ? p.cmax + (bh * p.Ck + kc) * p.lq : (wave == 1 ? p.lse : p.dvec) + bh * p.lq) + qb * kQT;
+    const int q = lane < rem ? lane : (int)(rem < 0 ? 0 : rem);
+    load_lds4_s(src, (uint32_t)q * 4u, lds + kLdsStat + buf * 768 + wave * 256);
   }
 }
 
-// One 64-query tile in registers, 16 x 16 bytes per lane: Q-hat rows, dO rows (64 rows x 256 B
-// each), then the Q-hat and dO tiles (128 d-rows x 128 B each).
-__device__ __forceinline__ void load_tile(const BwdParams &p, int64_t bh, int64_t bb, int64_t hh, int64_t qb,
-                                          int tid, u32x4 *stg) {
-  const u32x4 *qs = p.qq + (bh * p.Cq * kChunk + qb * kQT) * (kD / 8);
+// One 64-query tile for one wave (BUF: which tile buffer holds it).
+template <int BUF>
+__device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, DkdvLane ln, int64_t qb, bool tail,
+                                          f32x16 *dk, f32x16 *dv) {
+  // LDS byte addresses; lds0 is 256-byte aligned, so the swizzle XORs act on the offsets alone.
+  uint32_t ka = lds0 + ln.k_off, ra = lds0 + kLdsR + ln.r_off, ta0 = lds0 + kLdsR + ln.tr_off;
+  AQ_OPAQUE(ka);
+  AQ_OPAQUE(ra);
+  AQ_OPAQUE(ta0);
+  constexpr uint32_t kQ = BUF * 32768, kO = BUF * 32768 + 16384;  // buffer offsets from kLdsR
+
+  f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = i * 256 + tid, r = id >> 4, j = id & 15;
-    const int64_t qrow = qb * kQT + r;
-    stg[i] = qs[id];
-    stg[4 + i] = u32x4{0u, 0u, 0u, 0u};
-    if (qrow < p.lq) stg[4 + i] = *(const u32x4 *)(p.d_o + bb * p.sdo.b + hh * p.sdo.h + qrow * p.sdo.l + 8 * j);
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t kt_ = ka ^ (32 * t), rt = ra ^ (32 * t);
+    const bf16x8 ak = as_bf16x8(lds_read16(kt_));
+    const bf16x8 bq = as_bf16x8(lds_read16(rt + kQ));
+    const bf16x8 av = as_bf16x8(lds_read16(kt_ + 32768));
+    const bf16x8 bo = as_bf16x8(lds_read16(rt + kO));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, s, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bo, dp, 0, 0, 0);
   }
-  const int64_t tc = (qb * kQT) / kChunk, toff = (qb * kQT) % kChunk;
-  const uint8_t *qts = (const uint8_t *)(p.qt + (bh * p.Cq + tc) * (kChunk * kD / 8));
-  const uint8_t *ots = (const uint8_t *)(p.dot + (bh * p.Cq + tc) * (kChunk * kD / 8));
+  const uint32_t sta = lds0 + kLdsStat + BUF * 768 + 4 * ln.qloc;
+  const float mc = lds_read_f32(sta), lse2 = lds_read_f32(sta + 256), Di = lds_read_f32(sta + 512);
+  const int qrow = (int)(qb * kQT) + ln.qloc;
+  const int lq = (int)p.lq;
+  if (tail || qrow >= lq || (p.causal && ln.key_base + 15 > qrow)) {
+    const int last = qrow >= lq ? -1 : (p.causal && qrow < (int)p.lk - 1 ? qrow : (int)p.lk - 1);
+    mask_tail(s, valid_prefix(ln.key_base, last));
+  }
+  // A = exp2(y - m_c) exp2(m_c - lse2); dS = A (dP - D); A-hat = fq(exp2(y - m_c)) exp2(m_c - lse2).
+  float bm = s[0];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = i * 256 + tid, d = id >> 3, j = id & 7;
-    const int64_t src = (int64_t)d * 256 + toff * 2 + j * 16;
-    stg[8 + i] = *(const u32x4 *)(qts + src);
-    stg[12 + i] = *(const u32x4 *)(ots + src);
+  for (int rr = 1; rr < 16; ++rr) bm = fmaxf(bm, s[rr]);
+  const float w = __builtin_amdgcn_exp2f(mc - lse2);
+  const float wD = w * Di;
+  float ah[16], ds[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    ah[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -mc));
+    ds[rr] = ah[rr] * __builtin_fmaf(w, dp[rr], -wD);
+  }
+  if (p.quant_p) {
+    const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(bm, p.c, -mc));  // as the forward
+    const float S = block_scale_unit(am);
+    const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+    fq_prob_oct_dq(ah, inv, S * w);
+    fq_prob_oct_dq(ah + 8, inv, S * w);
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) ah[rr] *= w;
+  }
+  // Move A-hat and dS to one key per lane: D[query][key] = sum_k X[query][k] onehot[k][key].
+  const uint32_t oh = lds0 + kLdsOneHot + 16 * (threadIdx.x & 63);
+  const bf16x8 one0 = as_bf16x8(lds_read16(oh)), one1 = as_bf16x8(lds_read16(oh + 1024));
+  f32x16 ta = f32x16{}, ts = f32x16{};
+  ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ah), one0, ta, 0, 0, 0);
+  ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ah + 8), one1, ta, 0, 0, 0);
+  ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds), one0, ts, 0, 0, 0);
+  ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds + 8), one1, ts, 0, 0, 0);
+  // ta/ts register 8*s2 + kk of lane (key j, half h) holds query 16*s2 + 8*h + kk of the wave's 32.
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    float fa[8], fs[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      fa[kk] = ta[8 * s2 + kk];
+      fs[kk] = ts[8 * s2 + kk];
+    }
+    const bf16x8 ba = pack8_exact(fa), bs = pack8_exact(fs);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      // query groups a = 0, 1: rows +0 / +4 (1024 bytes) with column-pair bit 4 flipped
+      const uint32_t a0 = ta0 ^ (dt << 6), a1 = ta0 ^ ((dt << 6) | 16);
+      const uint32_t s2o = s2 * 4096;
+      const uint2 o0 = ds_read_tr16_at(a0 + kO + s2o), o1 = ds_read_tr16_at(a1 + kO + s2o + 1024);
+      const uint2 q0 = ds_read_tr16_at(a0 + kQ + s2o), q1 = ds_read_tr16_at(a1 + kQ + s2o + 1024);
+      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{o0.x, o0.y, o1.x, o1.y}), ba, dv[dt], 0, 0, 0);
+      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{q0.x, q0.y, q1.x, q1.y}), bs, dk[dt], 0, 0, 0);
+    }
   }
 }
 
-__device__ __forceinline__ void store_tile(uint8_t *lds_q, uint8_t *lds_o, uint8_t *lds_qt, uint8_t *lds_ot, int tid,
-                                           const u32x4 *stg) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = i * 256 + tid, r = id >> 4, j = id & 15;
-    *(u32x4 *)(lds_q + row_off(r, j)) = stg[i];
-    *(u32x4 *)(lds_o + row_off(r, j)) = stg[4 + i];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // 16-byte chunk j holds 8-byte groups 2j, 2j+1; under the swizzle they land in chunk
-    // j ^ (f/2), with the two halves exchanged when f is odd.
-    const int id = i * 256 + tid, d = id >> 3, j = id & 7, f = qt_swz(d);
-    const int dst = d * 128 + ((j ^ (f >> 1)) << 4);
-    const u32x4 a = stg[8 + i], b = stg[12 + i];
-    *(u32x4 *)(lds_qt + dst) = (f & 1) ? u32x4{a.z, a.w, a.x, a.y} : a;
-    *(u32x4 *)(lds_ot + dst) = (f & 1) ? u32x4{b.z, b.w, b.x, b.y} : b;
-  }
-}
-
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t *lds_q = lds, *lds_o = lds + 16384, *lds_qt = lds + 32768, *lds_ot = lds + 49152;
-  uint8_t *lds_k = lds + 65536, *lds_v = lds + 98304;  // this chunk's K-hat and V-hat rows
+__global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kDkdvLds];
+  const uint32_t lds0 = lds_addr(lds);
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nwork);
   if (vid < 0) return;
   const int64_t bh = vid / p.Ck;
   const int64_t kc = vid % p.Ck;
   const int64_t bb = bh / p.heads, hh = bh % p.heads;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, hf = lane >> 5;
+  const int kg = wave & 3, qh = wave >> 2;
   const int64_t nqt = (p.lq + kQT - 1) / kQT;
   const int64_t qt0 = p.causal ? (kc * kChunk) / kQT : 0;
 
-  // Prefetch the first tile and its statistics before the per-wave set-up.
-  TileStats st;
-  u32x4 stg[16];
-  load_stats(p, bh, kc, qt0, n, st);
-  load_tile(p, bh, bb, hh, qt0, tid, stg);
+  DkdvLane ln;
+  {
+    const int krow = kg * 32 + perm_row(n), swk = sw_kq(krow);
+    ln.k_off = krow * 256 + 16 * ((hf ^ swk) & 1) + 32 * (swk >> 1);
+    ln.qloc = 32 * qh + pi_q(n);
+    const int swq = sw_qr(ln.qloc);
+    ln.r_off = ln.qloc * 256 + 16 * ((hf ^ swq) & 1) + 32 * (swq >> 1);
+    // Transposed read (ds_read_b64_tr_b16): in each 16-lane group, lane 4e+j supplies 4 elements
+    // of row (base + e) and lane i receives element i%4 from lanes 4e + i/4, e = 0..3.  Lane
+    // (group g = (lane/16)%2, h = lane/32, e = (lane/4)%4, j = lane%4) reads tile row
+    // 32*qh + 16*s2 + 8*h + 4*a + e, d columns 32*dt + 16*g + 4*j .. +3.  That row's swizzle is
+    // 4*e + 2*h + a, so the 16-byte column is 4*(dt^e) + ((2*g + j/2) ^ (2*h + a)).
+    const int e = (lane >> 2) & 3, j = lane & 3, g = (lane >> 4) & 1;
+    const int lo = (2 * g + (j >> 1)) ^ (2 * hf);
+    ln.tr_off = (32 * qh + 8 * hf + e) * 256 + 64 * e + 16 * lo + 8 * (j & 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = (i * 8 + wave) * 4 + (lane >> 4);
+      const int jc = (lane & 15) ^ sw_qr(r);
+      ln.o_row[i] = r;
+      ln.q_voff[i] = (uint32_t)(r * 256 + jc * 16);
+      ln.o_voff[i] = (uint32_t)(r * p.sdo.l * 2 + jc * 16);
+    }
+  }
+  ln.key_base = (int)(kc * kChunk) + kg * 32 + 16 * hf;
 
-  // This chunk's K-hat and V-hat rows (A operands of S^T and dP^T, read in perm_row order).
+  // This chunk's K-hat and V-hat rows, the one-hot operands, then the first tile.
   {
     const u32x4 *ks = p.kq + (bh * p.Ck + kc) * (kChunk * kD / 8);
     const u32x4 *vs = p.vq + (bh * p.Ck + kc) * (kChunk * kD / 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int id = i * 256 + tid, r = id >> 4, j = id & 15;
-      *(u32x4 *)(lds_k + kq_off(r, j)) = ks[id];
-      *(u32x4 *)(lds_v + kq_off(r, j)) = vs[id];
+    for (int i = 0; i < 4; ++i) {
+      const int r = (i * 8 + wave) * 4 + (lane >> 4);
+      const uint32_t off = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
+      load_lds16_s(ks, off, lds + (i * 8 + wave) * 1024);
+      load_lds16_s(vs, off, lds + 32768 + (i * 8 + wave) * 1024);
+    }
+    if (wave == 0) {
+      *(bf16x8 *)(lds + kLdsOneHot + lane * 16) = onehot_b(lane, 0);
+      *(bf16x8 *)(lds + kLdsOneHot + 1024 + lane * 16) = onehot_b(lane, 1);
     }
   }
-  const int krow = wave * 32 + perm_row(n);
-  const bf16x8 one0 = onehot_b(lane, 0), one1 = onehot_b(lane, 1);
+  if (qt0 < nqt) dkdv_stage_tile(p, ln, bh, bb, hh, kc, qt0, lds, 0, wave, lane);
+
+  const bool tail = (kc + 1) * kChunk > p.lk;
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
-  const int64_t key_base = kc * kChunk + wave * 32 + 16 * hf;  // key of register 0 (S^T layout)
-  const bool tail = (kc + 1) * kChunk > p.lk;
 
-  for (int64_t qb = qt0; qb < nqt; ++qb) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile(lds_q, lds_o, lds_qt, lds_ot, tid, stg);
-    const TileStats cur = st;
+  // Tiles in pairs (buffer 0, then buffer 1), then an odd last tile in buffer 0.
+  int64_t qb = qt0;
+  for (; qb + 1 < nqt; qb += 2) {
+    AQ_WAIT_VMCNT(0);  // this wave's copies of tile qb
+    __syncthreads();   // everyone's copies landed; buffer 1 is free
+    dkdv_stage_tile(p, ln, bh, bb, hh, kc, qb + 1, lds, 1, wave, lane);
+    dkdv_tile<0>(p, lds0, ln, qb, tail, dk, dv);
+    AQ_WAIT_VMCNT(0);
+    __syncthreads();  // buffer 0 is free
+    if (qb + 2 < nqt) dkdv_stage_tile(p, ln, bh, bb, hh, kc, qb + 2, lds, 0, wave, lane);
+    dkdv_tile<1>(p, lds0, ln, qb + 1, tail, dk, dv);
+  }
+  if (qb < nqt) {
+    AQ_WAIT_VMCNT(0);
     __syncthreads();
-    if (qb + 1 < nqt) {  // the next tile streams in while this one is computed
-      load_stats(p, bh, kc, qb + 1, n, st);
-      load_tile(p, bh, bb, hh, qb + 1, tid, stg);
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t qrow = qb * kQT + 32 * nt + n;
-      const bool qvalid = qrow < p.lq;
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bf16x8 ak = as_bf16x8(*(const u32x4 *)(lds_k + kq_off(krow, 2 * t + hf)));
-        const bf16x8 bq = as_bf16x8(*(const u32x4 *)(lds_q + row_off(32 * nt + n, 2 * t + hf)));
-        const bf16x8 av = as_bf16x8(*(const u32x4 *)(lds_v + kq_off(krow, 2 * t + hf)));
-        const bf16x8 bo = as_bf16x8(*(const u32x4 *)(lds_o + row_off(32 * nt + n, 2 * t + hf)));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bo, dp, 0, 0, 0);
-      }
-      const float mc = cur.mc[nt], lse2 = cur.lse[nt], Di = cur.dv[nt];
-      if (tail || !qvalid || (p.causal && key_base + 15 > qrow)) {
-        const int64_t last = !qvalid ? -1 : (p.causal && qrow < p.lk - 1 ? qrow : p.lk - 1);
-        mask_tail(s, valid_prefix(key_base, last));
-      }
-      // P exactly as the forward formed it, its fake quantization, and the weights.
-      float Ah[16], ds[16];
-      float bm = s[0];
-#pragma unroll
-      for (int rr = 1; rr < 16; ++rr) bm = fmaxf(bm, s[rr]);
-      const float w = __builtin_amdgcn_exp2f(mc - lse2);
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        Ah[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -mc));
-        ds[rr] = (Ah[rr] * w) * (dp[rr] - Di);
-      }
-      if (p.quant_p) {
-        const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(bm, p.c, -mc));  // as the forward
-        const float S = block_scale_unit(am);
-        const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
-        fq_prob_oct(Ah, S, inv);
-        fq_prob_oct(Ah + 8, S, inv);
-      }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) Ah[rr] *= w;
-      // Move A-hat and dS to one key per lane: D[query][key] = sum_k X[query][k] onehot[k][key].
-      f32x16 ta = f32x16{}, ts = f32x16{};
-      ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(Ah), one0, ta, 0, 0, 0);
-      ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(Ah + 8), one1, ta, 0, 0, 0);
-      ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds), one0, ts, 0, 0, 0);
-      ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds + 8), one1, ts, 0, 0, 0);
-      // ta/ts register r of lane (key j, half h) holds query 8*(r/4) + 4*h + r%4 of this 32-query
-      // block; k-slot (h, jj) of step s2 is register 8*s2 + jj, i.e. queries 16*s2 + 4h + {0..3}
-      // and 16*s2 + 8 + 4h + {0..3}.
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        float fa[8], fs[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          fa[jj] = ta[8 * s2 + jj];
-          fs[jj] = ts[8 * s2 + jj];
-        }
-        const bf16x8 ba = pack8_exact(fa), bs = pack8_exact(fs);
-        const int g0 = (32 * nt + 16 * s2 + 4 * hf) >> 2;  // 4-query group index
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = 32 * dt + n;
-          const uint2 o0 = *(const uint2 *)(lds_ot + qt_off(d, g0));
-          const uint2 o1 = *(const uint2 *)(lds_ot + qt_off(d, g0 + 2));
-          const uint2 q0 = *(const uint2 *)(lds_qt + qt_off(d, g0));
-          const uint2 q1 = *(const uint2 *)(lds_qt + qt_off(d, g0 + 2));
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{o0.x, o0.y, o1.x, o1.y}), ba, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{q0.x, q0.y, q1.x, q1.y}), bs, dk[dt], 0, 0, 0);
-        }
-      }
-    }
+    dkdv_tile<0>(p, lds0, ln, qb, tail, dk, dv);
   }
 
-  // dK^T / dV^T: lane holds key j = n of the wave's 32 (natural order), rows d.
-  const int64_t key = kc * kChunk + wave * 32 + n;
+  // The two waves of a key group add their partial sums: wave qh = 0 finishes dK, qh = 1 dV.
+  // Partner partials go through LDS as [key group][tensor][dt][register/4][lane] float4.
+  AQ_WAIT_VMCNT(0);  // no copy may still be landing in the LDS reused below
+  __syncthreads();
+  {
+    f32x16 *give = qh == 0 ? dv : dk;
+    float *dst = (float *)(lds + (kg * 2 + (qh == 0 ? 1 : 0)) * 16384);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *(f32x4 *)(dst + ((dt * 4 + a) * 64 + lane) * 4) =
+            f32x4{give[dt][4 * a], give[dt][4 * a + 1], give[dt][4 * a + 2], give[dt][4 * a + 3]};
+  }
+  __syncthreads();
+  const int64_t key = kc * kChunk + kg * 32 + n;
+  f32x16 *mine = qh == 0 ? dk : dv;
+  const float *src = (const float *)(lds + (kg * 2 + (qh == 0 ? 0 : 1)) * 16384);
+  const float mul = qh == 0 ? p.scale : 1.0f;
   if (key >= p.lk) return;
-  uint16_t *kp = p.dk + bb * p.sdk.b + hh * p.sdk.h + key * p.sdk.l;
-  uint16_t *vp = p.dv + bb * p.sdv.b + hh * p.sdv.h + key * p.sdv.l;
+  uint16_t *out = qh == 0 ? p.dk + bb * p.sdk.b + hh * p.sdk.h + key * p.sdk.l
+                          : p.dv + bb * p.sdv.b + hh * p.sdv.h + key * p.sdv.l;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
+      const f32x4 o = *(const f32x4 *)(src + ((dt * 4 + a) * 64 + lane) * 4);
       const int d0 = 32 * dt + 8 * a + 4 * hf;
-      *(bf16x4 *)(kp + d0) = bf16x4{(__bf16)(dk[dt][4 * a] * p.scale), (__bf16)(dk[dt][4 * a + 1] * p.scale),
-                                    (__bf16)(dk[dt][4 * a + 2] * p.scale), (__bf16)(dk[dt][4 * a + 3] * p.scale)};
-      *(bf16x4 *)(vp + d0) = bf16x4{(__bf16)dv[dt][4 * a], (__bf16)dv[dt][4 * a + 1], (__bf16)dv[dt][4 * a + 2],
-                                    (__bf16)dv[dt][4 * a + 3]};
+      *(bf16x4 *)(out + d0) = bf16x4{(__bf16)((mine[dt][4 * a] + o[0]) * mul), (__bf16)((mine[dt][4 * a + 1] + o[1]) * mul),
+                                     (__bf16)((mine[dt][4 * a + 2] + o[2]) * mul), (__bf16)((mine[dt][4 * a + 3] + o[3]) * mul)};
     }
 }
 
@@ -419,10 +465,9 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
   const TileQuant qd_k = (a.flags & 2u) ? kQuantD : kQuantNone;
   const TileQuant qr_v = (a.flags & 4u) ? kQuantRows : kQuantNone;
   hipError_t e;
-  if ((e = launch_tile_prepass(a.q, a.sq, a.batch, a.heads, a.lq, qd_q, ws + w.qq, ws + w.qt, stream))) return e;
+  if ((e = launch_tile_prepass(a.q, a.sq, a.batch, a.heads, a.lq, qd_q, ws + w.qq, nullptr, stream))) return e;
   if ((e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, qd_k, ws + w.kq, ws + w.kt, stream))) return e;
   if ((e = launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qr_v, ws + w.vq, nullptr, stream))) return e;
-  if ((e = launch_tile_prepass(b.d_o, b.sdo, a.batch, a.heads, a.lq, kQuantNone, nullptr, ws + w.dot, stream))) return e;
 
   const int64_t bh = (int64_t)a.batch * a.heads;
   const int64_t rows = bh * a.lq;
@@ -433,8 +478,6 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
 
   BwdParams p{};
   p.qq = (const u32x4 *)(ws + w.qq);
-  p.qt = (const u32x4 *)(ws + w.qt);
-  p.dot = (const u32x4 *)(ws + w.dot);
   p.kq = (const u32x4 *)(ws + w.kq);
   p.kt = (const u32x4 *)(ws + w.kt);
   p.vq = (const u32x4 *)(ws + w.vq);
@@ -462,8 +505,6 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
   // Dynamic LDS above 64 KiB must be allowed per kernel.
   if ((e = hipFuncSetAttribute((const void *)bwd_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 98304)))
     return e;
-  if ((e = hipFuncSetAttribute((const void *)bwd_dkdv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 131072)))
-    return e;
   p.nwork = bh * p.Cq;
   p.per_xcd = (p.nwork + 7) / 8;
   AQ_LAUNCH("bwd_dq", bwd_dq_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(256), 98304, stream, p);
@@ -471,7 +512,7 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
 
   p.nwork = bh * p.Ck;
   p.per_xcd = (p.nwork + 7) / 8;
-  AQ_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(256), 131072, stream, p);
+  AQ_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(kDkdvThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -22,6 +22,11 @@ __device__ __forceinline__ int sw_kq(int r) { return (r & 3) | ((r >> 2) & 4) | 
 __device__ __forceinline__ int sw_row(int r) { return r & 15; }
 __device__ __forceinline__ int kq_off(int r, int j) { return r * 256 + ((j ^ sw_kq(r)) << 4); }
 __device__ __forceinline__ int row_off(int r, int j) { return r * 256 + ((j ^ sw_row(r)) << 4); }
+// sw_qr serves both reads of the backward's query tiles: 16 lanes reading one column of 16
+// consecutive rows (all 16 values of the 4 bits), and transposed reads in which 4 consecutive rows
+// (r%4 = 0..3) each supply 32 contiguous bytes (r%4 picks the 64-byte quarter of the row).
+__device__ __forceinline__ int sw_qr(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int qr_off(int r, int j) { return r * 256 + ((j ^ sw_qr(r)) << 4); }
 
 // One-hot B operand of a 32x32x16 MFMA that moves A's k-slot values into column j: lane (column
 // j = l%32, half h) holds 1 in slot jj where j == 16h + 8*step + jj.
@@ -67,6 +72,56 @@ __device__ __forceinline__ void load_lds16(const void *gsrc, uint8_t *lds_base) 
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(gsrc) : "memory", "m0");
 }
 
+// A wave-uniform pointer moved to scalar registers.
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Same copy from a wave-uniform base plus a 32-bit per-lane byte offset (the saddr form: the
+// per-lane address costs one VGPR instead of two).
+__device__ __forceinline__ void load_lds16_s(const void *sbase, uint32_t voff, uint8_t *lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff), "s"(uniform_ptr(sbase))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void load_lds4_s(const void *sbase, uint32_t voff, uint8_t *lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0v), "v"(voff), "s"(uniform_ptr(sbase))
+               : "memory", "m0");
+}
+
+// Asynchronous 4-byte global -> LDS copy: lane l writes LDS bytes [lds_base + 4*l, +4).
+__device__ __forceinline__ void load_lds4(const void *gsrc, uint8_t *lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(gsrc) : "memory", "m0");
+}
+
+// LDS reads at an integer LDS byte address (a constant added to the address folds into the
+// instruction's offset field).
+typedef const u32x4 __attribute__((address_space(3))) *lds_u32x4_ptr;
+typedef const float __attribute__((address_space(3))) *lds_f32_ptr;
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) { return *(lds_u32x4_ptr)(uintptr_t)addr; }
+__device__ __forceinline__ float lds_read_f32(uint32_t addr) { return *(lds_f32_ptr)(uintptr_t)addr; }
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16, gfx950).  Each lane supplies the address of 4
+// consecutive 16-bit elements; within every group of 16 lanes, lane i receives element i%4 of the
+// four lanes 4e + i/4, e = 0..3, in that order (checked on the GPU).  So if lane 4e+j points at
+// columns c0+4j .. c0+4j+3 of row r0+e, lane i gets column c0+i of rows r0 .. r0+3.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ds_read_tr16(const uint8_t *lds_addr) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)lds_addr);
+  return __builtin_bit_cast(uint2, r);
+}
+__device__ __forceinline__ uint2 ds_read_tr16_at(uint32_t addr) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(uintptr_t)addr);
+  return __builtin_bit_cast(uint2, r);
+}
+
 // Stage a 32 KiB tile ([128 rows][256 bytes] in global memory) into LDS with the XOR swizzle
 // `sw` applied, using 8 asynchronous 16-byte copies per lane of a 256-lane workgroup.  LDS
 // instruction i of wave w covers rows 16i + 4w .. +3, physical column = lane%16; the lane fetches
@@ -82,6 +137,10 @@ __device__ __forceinline__ void stage_tile_async(const uint8_t *gtile, uint8_t *
   }
 }
 
+// Makes v opaque to the optimiser at this point, so values derived from it after this point are
+// recomputed there instead of being hoisted out of the enclosing loop (and held in registers).
+#define AQ_OPAQUE(v) asm volatile("" : "+v"(v))
+
 // Wait until at most N of this wave's vector-memory operations are outstanding.
 #define AQ_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
 
@@ -90,6 +149,11 @@ __device__ __forceinline__ void stage_tile_async(const uint8_t *gtile, uint8_t *
 __device__ __forceinline__ int valid_prefix(int64_t key0, int64_t last) {
   const int64_t rel = last - key0;
   return rel < 0 ? 0 : (rel >= 15 ? 16 : (int)rel + 1);
+}
+
+__device__ __forceinline__ int valid_prefix(int key0, int last) {
+  const int rel = last - key0;
+  return rel < 0 ? 0 : (rel >= 15 ? 16 : rel + 1);
 }
 
 // Set registers at and past `nvalid` to -inf (selects with constant indices, no branches).

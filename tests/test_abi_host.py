@@ -47,10 +47,10 @@ def S(b=1, h=1, l=1):
 
 
 def fwd(lib, **kw):
-    a = dict(q=8, k=8, v=8, o=8, B=1, H=2, Hkv=2, D=128, lq=64, lk=64, scale=0.088, causal=0, flags=15,
+    a = dict(q=16, k=16, v=16, o=16, B=1, H=2, Hkv=2, D=128, lq=64, lk=64, scale=0.088, causal=0, flags=15,
              ws=256, ws_bytes=1 << 40)
     a.update(kw)
-    s = S(64 * 256, 128, 256)
+    s = a.get("s", S(64 * 256, 128, 256))
     return lib.attn_qat_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["Hkv"], a["D"], a["lq"], a["lk"],
                             s, s, s, s, a["scale"], a["causal"], a["flags"], None, None, None, a["ws"],
                             a["ws_bytes"], None)
@@ -67,15 +67,19 @@ def fwd(lib, **kw):
     (dict(causal=1, lk=32), -2, "causal"),
     (dict(ws_bytes=100), -1, "workspace"),
     (dict(ws=257), -1, "workspace"),
+    (dict(q=8), -1, "16-byte aligned"),
+    (dict(s=None), -1, "16-byte aligned"),
 ])
 def test_forward_rejects_bad_arguments(lib, kw, code, msg):
+    if "s" in kw:
+        kw = dict(kw, s=S(64 * 256, 128, 132))  # row stride not a multiple of 8 elements
     assert fwd(lib, **kw) == code
     assert msg in lib.aq_last_error().decode()
 
 
 def test_backward_requires_statistics(lib):
     s = S(64 * 256, 128, 256)
-    rc = lib.attn_qat_bwd(8, 8, 8, None, 8, None, None, 8, 8, 8, 1, 2, 2, 128, 64, 64, s, s, s, s, s, s, s,
+    rc = lib.attn_qat_bwd(16, 16, 16, None, 16, None, None, 16, 16, 16, 1, 2, 2, 128, 64, 64, s, s, s, s, s, s, s,
                           0.088, 0, 15, 256, 1 << 40, None)
     assert rc == -1 and "required" in lib.aq_last_error().decode()
 
@@ -89,7 +93,7 @@ def test_backward_requires_statistics(lib):
 def test_vsa_rejects_bad_arguments(lib, kw, code, msg):
     s = S(25088 * 1536, 128, 1536)
     g, c = kw["grid"], kw["cube"]
-    rc = lib.vsa_qat_fwd(8, 8, 8, 8, None, None, 1, 12, 128, kw["L"], g[0], g[1], g[2], c[0], c[1], c[2],
+    rc = lib.vsa_qat_fwd(16, 16, 16, 16, None, None, 1, 12, 128, kw["L"], g[0], g[1], g[2], c[0], c[1], c[2],
                          kw.get("sparsity", 0.9), s, s, s, s, 0.088, 15, 256, 1 << 40, None)
     assert rc == code
     assert msg in lib.aq_last_error().decode()
