@@ -51,7 +51,6 @@ __global__ __launch_bounds__(256) void dvec_kernel(const uint16_t *__restrict__ 
 struct BwdParams {
   const u32x4 *qq;    // Q-hat rows   [BH, Cq*128, 128]
   const u32x4 *kq;    // K-hat rows   [BH, Ck*128, 128]
-  const u32x4 *kt;    // K-hat tiles  [BH, Ck, 128, 128]
   const u32x4 *vq;    // V-hat rows   [BH, Ck*128, 128]
   const uint16_t *d_o;
   Strides sdo;
@@ -68,26 +67,65 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------------------------------------
-// dQ: workgroup = (head, 128 queries), 4 waves x 32 queries; loop over 128-key chunks in two
-// 64-key halves.  LDS: K-hat rows, V-hat rows (A operands of S^T and dP^T, perm_row order) and the
-// K-hat tile (A operand of dQ^T), 96 KiB.
+// dQ: workgroup = (head, 128 queries), 8 waves, loop over 128-key chunks.  Wave w owns queries
+// 32*(w%4) .. +31 (their Q-hat and dO in registers, the B operands of S^T and dP^T) and keys
+// 64*(w/4) .. +63 of every chunk; the two waves that share queries add their partial dQ through
+// LDS at the end.  Two waves per SIMD.
+//
+// LDS: two chunk buffers of 64 KiB, each K-hat rows [128][256 B] then V-hat rows (A operands of
+// S^T and dP^T, sw_kd swizzle).  The A operand of dQ^T (K-hat^T: 8 consecutive keys of one d per
+// lane half) comes from the same K-hat rows through transposed reads.  Chunk c+1 is copied
+// asynchronously while chunk c is computed; one barrier per chunk.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t *lds_k = lds, *lds_v = lds + 32768, *lds_kt = lds + 65536;
+constexpr int kDqThreads = 512;
+constexpr int kDqLds = 2 * 65536;
+
+// Swizzle of the dQ kernel's K-hat/V-hat rows.  A-operand reads in perm_row order: 16 lanes read
+// rows {0..3, 16..19, 4..7, 20..23} (+8 for the next 16), told apart by bits 0, 1, 2 and 4 of the
+// row.  Transposed reads: 4 consecutive rows (bits 0, 1) each supply 32 contiguous bytes, so bits
+// 0 and 1 must pick the 64-byte quarter (the two high bits of the 16-byte column).
+__device__ __forceinline__ int sw_kd(int r) { return ((r >> 2) & 1) | ((r >> 3) & 2) | ((r & 3) << 2); }
+
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kDqLds];
+  const uint32_t lds0 = lds_addr(lds);
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nwork);
   if (vid < 0) return;
   const int64_t bh = vid / p.Cq;
   const int64_t qc = vid % p.Cq;
   const int64_t bb = bh / p.heads, hh = bh % p.heads;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, hf = lane >> 5;
-  const int64_t qrow = qc * kChunk + wave * 32 + n;
+  const int qg = wave & 3, kh = wave >> 2;
+  const int qrow = (int)(qc * kChunk) + qg * 32 + n;
   const bool qvalid = qrow < p.lq;
+
+  int64_t n_iter = p.Ck;
+  if (p.causal) {
+    const int64_t q_last = qc * kChunk + kChunk - 1;
+    n_iter = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
+  }
+  // Chunk copies: per lane 4 K-hat and 4 V-hat pieces of 16 bytes.
+  uint32_t c_voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (i * 8 + wave) * 4 + (lane >> 4);
+    c_voff[i] = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kd(r)) << 4));
+  }
+  auto stage_chunk = [&](int64_t ch, int buf) {
+    const u32x4 *ks = p.kq + (bh * p.Ck + ch) * (kChunk * kD / 8);
+    const u32x4 *vs = p.vq + (bh * p.Ck + ch) * (kChunk * kD / 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      load_lds16_s(ks, c_voff[i], lds + buf * 65536 + (i * 8 + wave) * 1024);
+      load_lds16_s(vs, c_voff[i], lds + buf * 65536 + 32768 + (i * 8 + wave) * 1024);
+    }
+  };
+  stage_chunk(0, 0);
 
   bf16x8 qf[8], of[8];
   {
-    const u32x4 *qsrc = p.qq + (bh * p.Cq * kChunk + qc * kChunk + wave * 32 + n) * (kD / 8);
-    const uint16_t *osrc = p.d_o + bb * p.sdo.b + hh * p.sdo.h + (qvalid ? qrow : 0) * p.sdo.l;
+    const u32x4 *qsrc = p.qq + (bh * p.Cq * kChunk + qc * kChunk + qg * 32 + n) * (kD / 8);
+    const uint16_t *osrc = p.d_o + bb * p.sdo.b + hh * p.sdo.h + (int64_t)(qvalid ? qrow : 0) * p.sdo.l;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       qf[t] = as_bf16x8(qsrc[2 * t + hf]);
@@ -99,95 +137,96 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const float lse2 = qvalid ? p.lse[bh * p.lq + qrow] : 0.0f;
   const float Di = qvalid ? p.dvec[bh * p.lq + qrow] : 0.0f;
   // largest key this query sees (-1: an out-of-range query row sees none)
-  const int64_t last = !qvalid ? -1 : (p.causal && qrow < p.lk - 1 ? qrow : p.lk - 1);
+  const int last = !qvalid ? -1 : (p.causal && qrow < p.lk - 1 ? qrow : (int)p.lk - 1);
+
+  // S^T / dP^T A operand: row 64*kh + 32*k2 + perm_row(n), 16-byte column 2t + hf (XOR term of the
+  // swizzle in bits 5..7, so column pair t is `^ 32*t`; k2 adds 8 KiB, V-hat 32 KiB).
+  int a_off;
+  {
+    const int r = 64 * kh + perm_row(n), sw = sw_kd(r);
+    a_off = r * 256 + 16 * ((hf ^ sw) & 1) + 32 * (sw >> 1);
+  }
+  // Transposed reads (see ds_read_tr16): lane (group g = (lane/16)%2, h = lane/32, e = (lane/4)%4,
+  // j = lane%4) reads key row 64*kh + 32*k2 + 16*h + 8*jj + 4*a + e, d columns 32*dt + 16*g + 4*j
+  // .. +3, for dQ^T k-slot group jj (8 keys) and half a.  The row's swizzle is 4*e + 2*h + a, so the
+  // 16-byte column is 4*(dt^e) + ((2*g + j/2) ^ (2*h + a)).
+  int t_off;
+  {
+    const int e = (lane >> 2) & 3, j = lane & 3, g = (lane >> 4) & 1;
+    const int lo = (2 * g + (j >> 1)) ^ (2 * hf);
+    t_off = (64 * kh + 16 * hf + e) * 256 + 64 * e + 16 * lo + 8 * (j & 1);
+  }
+
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-  const int krow = perm_row(n);
 
-  int64_t n_iter = p.Ck;
-  if (p.causal) {
-    const int64_t q_last = qc * kChunk + kChunk - 1;
-    n_iter = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
-  }
-  // The next chunk's three tiles stream into registers while the current one is computed.
-  u32x4 stg[24];
-  auto load_chunk = [&](int64_t ch) {
-    const u32x4 *ks = p.kq + (bh * p.Ck + ch) * (kChunk * kD / 8);
-    const u32x4 *vs = p.vq + (bh * p.Ck + ch) * (kChunk * kD / 8);
-    const u32x4 *ts = p.kt + (bh * p.Ck + ch) * (kChunk * kD / 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int id = i * 256 + tid;
-      stg[i] = ks[id];
-      stg[8 + i] = vs[id];
-      stg[16 + i] = ts[id];
-    }
-  };
-  load_chunk(0);
   for (int64_t ch = 0; ch < n_iter; ++ch) {
-    __syncthreads();  // every wave is done reading the previous chunk
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int id = i * 256 + tid, r = id >> 4, j = id & 15;
-      *(u32x4 *)(lds_k + kq_off(r, j)) = stg[i];
-      *(u32x4 *)(lds_v + kq_off(r, j)) = stg[8 + i];
-      *(u32x4 *)(lds_kt + row_off(r, j)) = stg[16 + i];
-    }
-    __syncthreads();
-    if (ch + 1 < n_iter) load_chunk(ch + 1);
+    const int buf = (int)(ch & 1);
+    AQ_WAIT_VMCNT(0);  // this wave's copies of chunk ch
+    __syncthreads();   // everyone's copies landed; the other buffer is free
+    if (ch + 1 < n_iter) stage_chunk(ch + 1, buf ^ 1);
+    uint32_t ka = lds0 + buf * 65536 + a_off, ta = lds0 + buf * 65536 + t_off;
+    AQ_OPAQUE(ka);
+    AQ_OPAQUE(ta);
     const bool tail = (ch + 1) * kChunk > p.lk;
-    const bool diag = p.causal && (ch + 1) * kChunk - 1 > qc * kChunk + wave * 32;
+    const bool diag = p.causal && (ch + 1) * kChunk - 1 > qc * kChunk + qg * 32;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      bf16x8 dsb[2][2];
+    for (int k2 = 0; k2 < 2; ++k2) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int kt = 2 * kh + k2;
-        const int r = 32 * kt + krow;
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 ak = as_bf16x8(*(const u32x4 *)(lds_k + kq_off(r, 2 * t + hf)));
-          const bf16x8 av = as_bf16x8(*(const u32x4 *)(lds_v + kq_off(r, 2 * t + hf)));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[t], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[t], dp, 0, 0, 0);
-        }
-        if (tail || diag || !qvalid) {
-          const int64_t key0 = ch * kChunk + 32 * kt + 16 * hf;
-          mask_tail(s, valid_prefix(key0, last));
-        }
-        float ds[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float A = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -lse2));
-          ds[rr] = A * (dp[rr] - Di);
-        }
-        dsb[k2][0] = pack8_cvt(ds);
-        dsb[k2][1] = pack8_cvt(ds + 8);
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t at = (ka ^ (32 * t)) + k2 * 8192;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at)), qf[t], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at + 32768)), of[t], dp, 0, 0, 0);
       }
+      if (tail || diag || !qvalid) {
+        const int key0 = (int)(ch * kChunk) + 64 * kh + 32 * k2 + 16 * hf;
+        mask_tail(s, valid_prefix(key0, last));
+      }
+      float ds[16];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+      for (int rr = 0; rr < 16; ++rr) {
+        const float A = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -lse2));
+        ds[rr] = A * (dp[rr] - Di);
+      }
+      const bf16x8 d0 = pack8_cvt(ds), d1 = pack8_cvt(ds + 8);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const int kt = 2 * kh + k2;
-            const bf16x8 a = as_bf16x8(*(const u32x4 *)(lds_kt + row_off(32 * dt + n, 4 * kt + 2 * hf + j)));
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[k2][j], acc[dt], 0, 0, 0);
-          }
+      for (int dt = 0; dt < 4; ++dt) {
+        // k-slot group jj = 0 (keys 16h + 0..7, register pack d0) and jj = 1 (keys 16h + 8..15)
+        const uint32_t b0 = (ta ^ (dt << 6)) + k2 * 8192, b1 = (ta ^ ((dt << 6) | 16)) + k2 * 8192;
+        const uint2 x0 = ds_read_tr16_at(b0), x1 = ds_read_tr16_at(b1 + 1024);
+        const uint2 y0 = ds_read_tr16_at(b0 + 2048), y1 = ds_read_tr16_at(b1 + 3072);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{x0.x, x0.y, x1.x, x1.y}), d0, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{y0.x, y0.y, y1.x, y1.y}), d1, acc[dt], 0, 0, 0);
+      }
     }
   }
-  if (!qvalid) return;
-  uint16_t *op = p.dq + bb * p.sdq.b + hh * p.sdq.h + qrow * p.sdq.l;
+
+  // The two waves of a query group add their partial sums; wave kh = 0 stores.
+  AQ_WAIT_VMCNT(0);
+  __syncthreads();
+  float *xch = (float *)(lds + qg * 16384);
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *(f32x4 *)(xch + ((dt * 4 + a) * 64 + lane) * 4) =
+            f32x4{acc[dt][4 * a], acc[dt][4 * a + 1], acc[dt][4 * a + 2], acc[dt][4 * a + 3]};
+  }
+  __syncthreads();
+  if (kh == 1 || !qvalid) return;
+  uint16_t *op = p.dq + bb * p.sdq.b + hh * p.sdq.h + (int64_t)qrow * p.sdq.l;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
+      const f32x4 o = *(const f32x4 *)(xch + ((dt * 4 + a) * 64 + lane) * 4);
       const int d0 = 32 * dt + 8 * a + 4 * hf;
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      *(bf16x4 *)(op + d0) = bf16x4{(__bf16)(acc[dt][4 * a] * p.scale), (__bf16)(acc[dt][4 * a + 1] * p.scale),
-                                    (__bf16)(acc[dt][4 * a + 2] * p.scale), (__bf16)(acc[dt][4 * a + 3] * p.scale)};
+      *(bf16x4 *)(op + d0) = bf16x4{(__bf16)((acc[dt][4 * a] + o[0]) * p.scale), (__bf16)((acc[dt][4 * a + 1] + o[1]) * p.scale),
+                                    (__bf16)((acc[dt][4 * a + 2] + o[2]) * p.scale), (__bf16)((acc[dt][4 * a + 3] + o[3]) * p.scale)};
     }
 }
 
@@ -466,7 +505,7 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
   const TileQuant qr_v = (a.flags & 4u) ? kQuantRows : kQuantNone;
   hipError_t e;
   if ((e = launch_tile_prepass(a.q, a.sq, a.batch, a.heads, a.lq, qd_q, ws + w.qq, nullptr, stream))) return e;
-  if ((e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, qd_k, ws + w.kq, ws + w.kt, stream))) return e;
+  if ((e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, qd_k, ws + w.kq, nullptr, stream))) return e;
   if ((e = launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qr_v, ws + w.vq, nullptr, stream))) return e;
 
   const int64_t bh = (int64_t)a.batch * a.heads;
@@ -479,7 +518,6 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
   BwdParams p{};
   p.qq = (const u32x4 *)(ws + w.qq);
   p.kq = (const u32x4 *)(ws + w.kq);
-  p.kt = (const u32x4 *)(ws + w.kt);
   p.vq = (const u32x4 *)(ws + w.vq);
   p.d_o = (const uint16_t *)b.d_o;
   p.sdo = b.sdo;
@@ -503,11 +541,9 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
   p.quant_p = (a.flags & 8u) != 0;
 
   // Dynamic LDS above 64 KiB must be allowed per kernel.
-  if ((e = hipFuncSetAttribute((const void *)bwd_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 98304)))
-    return e;
   p.nwork = bh * p.Cq;
   p.per_xcd = (p.nwork + 7) / 8;
-  AQ_LAUNCH("bwd_dq", bwd_dq_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(256), 98304, stream, p);
+  AQ_LAUNCH("bwd_dq", bwd_dq_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(kDqThreads), 0, stream, p);
   if ((e = hipGetLastError())) return e;
 
   p.nwork = bh * p.Ck;

@@ -47,12 +47,11 @@ struct VsaArgs {
 // padded by zeros to a multiple of 128; tile tensors are [B*H, C, 128 d, 128 rows] bf16 (each
 // 128-row chunk stored d-major).
 //   op 0 (forward):  kq (K-hat rows), vt (V-hat tiles)
-//   op 1 (backward): kq, vq (V-hat rows), kt (K-hat tiles), qq (Q-hat rows),
-//                    dvec [B*H, lq] fp32 (D_i = <dO_i, o_hp_i>)
+//   op 1 (backward): kq, vq (V-hat rows), qq (Q-hat rows), dvec [B*H, lq] fp32 (D_i = <dO_i, o_hp_i>)
 //   op 2 (cube-sparse forward): kq, vt, pool [3, B*H, n, 128] bf16 (cube means of Q, K, V),
 //                    selw [B*H, n, n] int32 (selection when the caller passes none)
 struct Workspace {
-  size_t kq, vt, vq, kt, qq, dvec, pool, selw, total;
+  size_t kq, vt, vq, qq, dvec, pool, selw, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -74,7 +73,6 @@ inline Workspace workspace_layout(int op, int batch, int heads, int64_t lq, int6
   if (op == 0 || op == 2) w.vt = take(kbytes);
   if (op == 1) {
     w.vq = take(kbytes);
-    w.kt = take(kbytes);
     w.qq = take(qbytes);
     w.dvec = take(bh * (size_t)lq * 4);
   }
