@@ -72,10 +72,14 @@ def cpu_baseline(q, k, v, do, seconds: float):
         oracle.attn_bwd(qb, kb, vb, db, scale, qrows=rows, krows=np.zeros(0, np.int64))
         return time.perf_counter() - t0
 
-    probe = np.arange(0, L, L // 16)[:16]
-    run(probe)  # first call: library load and thread start-up
-    t_probe = run(probe)
-    R = int(min(L, max(16, 16 * seconds / max(t_probe, 1e-3))))
+    # Each call has a fixed part (quantizing the head's K and V) and a per-row part; size the
+    # sample from both so the timed call takes about `seconds`.
+    run(np.arange(0, L, L // 16)[:16])  # first call: library load and thread start-up
+    t16 = run(np.linspace(0, L - 1, 16).astype(np.int64))
+    t64 = run(np.linspace(0, L - 1, 64).astype(np.int64))
+    per_row = max((t64 - t16) / 48, 1e-5)
+    fixed = max(t16 - 16 * per_row, 0.0)
+    R = int(min(L, max(16, (seconds - fixed) / per_row)))
     rows = np.linspace(0, L - 1, R).astype(np.int64)
     t = run(rows)
     # per query row: forward 4*L*D (logits, P@V); dQ row 6*L*D (logits, dP, dQ)
@@ -85,18 +89,85 @@ def cpu_baseline(q, k, v, do, seconds: float):
                       f"(fp64 C, OpenMP), {t:.1f} s; per row 4*L*D + 6*L*D FLOP"}
 
 
+# Sources each timed kernel is built from: the HBM traffic recorded under profiles/ for a kernel is
+# reported only while the sha256 of these files matches the one recorded with the counters.
+KERNEL_SOURCES = {
+    "bwd_dkdv": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
+    "bwd_dq": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
+    "attn_fwd_train": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
+    "fq_contig_unit": ("fq.hip", "aq_device.hpp"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_qat_step_wan448x896x61_hbm_traffic.md")
+
+
+def kernel_source_hash(name):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, "quantization_aware_attention_nvfp4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch of kernel `name` from the counter summary (rows
+    `| name | sha | fetch KiB | write KiB | bytes |`), or None when absent or when the kernel's
+    sources changed since the counters were taken."""
+    if name not in KERNEL_SOURCES or not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = kernel_source_hash(name)
+    for line in open(TRAFFIC_FILE):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 5 and cells[0] == name and cells[1] == want:
+            try:
+                return float(cells[4])
+            except ValueError:
+                return None
+    return None
+
+
+def pmc_probe():
+    """One pass of every stage (no timing) plus a plain 1 GiB device copy, for counter runs: the
+    copy's FETCH_SIZE / WRITE_SIZE readings calibrate the counters' unit."""
+    import torch
+
+    import quantization_aware_attention_nvfp4_amd as m
+    import synth
+    dev = torch.device("cuda", 0)
+    x = synth.fq_tensor().to(dev)
+    y = torch.empty_like(x)
+    q, k, v = (t.to(dev) for t in synth.wan_448x896x61())
+    do = synth.normal_bf16((B, L, H, D), 2003).to(dev)
+    qv, kv, vv = (t.to(dev) for t in synth.vsa_inputs())
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    m.fq_nvfp4(x, out=y)
+    o, aux = m.attn_qat_fwd(q, k, v, training=True)
+    m.attn_qat_bwd(q, k, v, aux, do)
+    m.vsa_qat_fwd(qv, kv, vv, grid=GRID, cube=CUBE, sparsity=SPARSITY)
+    torch.cuda.synchronize()
+    print("pmc probe done: copy bytes", 2 * src.numel(), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true", help="one untimed pass of each stage plus a 1 GiB copy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); sharding the "
               "heads of a call over several GPUs is not built.", file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_probe:
+        pmc_probe()
+        return
 
     import torch
 
@@ -180,12 +251,16 @@ def main():
     dominant = max((n for n in kt if n in alg and alg[n][1] == "flop"), key=lambda n: kt[n][1])
     dom_avg = kt[dominant][1] / kt[dominant][0]
     achieved = alg[dominant][0] / (dom_avg * 1e-3) / 1e12
+    traffic = recorded_traffic(dominant)
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if traffic is None else int(traffic),
+                "traffic_unit": "HBM bytes per launch (TCC FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
     fq_avg = kt["fq_contig_unit"][1] / kt["fq_contig_unit"][0]
     fq = {"kernel": "fq_contig_unit", "bytes_per_launch": fq_bytes, "avg_us": round(fq_avg * 1e3, 2),
           "GB/s": round(fq_bytes / (fq_avg * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-          "frac": round(fq_bytes / (fq_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+          "frac": round(fq_bytes / (fq_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+          "traffic": None if recorded_traffic("fq_contig_unit") is None else int(recorded_traffic("fq_contig_unit"))}
     attn_ms = phase_ms["fwd"] + phase_ms["bwd"]
     attn = {"fwd_bwd_ms": round(attn_ms, 4),
             "fwd_bwd_TFLOP/s": round((fl["fwd"] + fl["bwd"]) / (attn_ms * 1e-3) / 1e12, 1),
