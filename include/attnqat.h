@@ -105,7 +105,7 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  * the denominator sums the unquantized P.  o = acc / l rounded to bf16.
  * softmax_scale : finite and > 0 ([API] default 1/sqrt(D) is applied by the caller).
  * causal        : top-left causal mask; requires lq == lk.
- * Optional training outputs (any may be NULL; all three are needed by attn_qat_bwd):
+ * Optional training outputs (all three or none; attn_qat_bwd needs all three):
  *   lse_log2       [B, H, lq] fp32 contiguous: log2 of the softmax denominator in base-2 logit
  *                  units, i.e. log2(e) * (m + ln l) with m the final row maximum.
  *   chunk_max_log2 [B, H, ceil(lk/128), lq] fp32 contiguous: log2(e) * m_c after each chunk
@@ -116,7 +116,8 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  * Errors: AQ_EINVAL (null q/k/v/o/workspace, head_size != 128 [API]
  * get_supported_head_sizes, sizes <= 0, non-finite or non-positive softmax_scale, flags outside
  * AQ_QUANT_ALL, strides that are not positive, misaligned tensors or strides, workspace too
- * small); AQ_ENOTSUP (num_kv_heads != num_heads, causal with lq != lk, lengths above 2^30).
+ * small, only some of the training outputs); AQ_ENOTSUP (num_kv_heads != num_heads, causal with
+ * lq != lk, lengths above 2^30).
  * ------------------------------------------------------------------------------------------- */
 int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch, int num_heads,
                  int num_kv_heads, int head_size, int64_t lq, int64_t lk, aq_strides sq,

@@ -121,6 +121,9 @@ int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch
   if (!tensor_ok(q, sq) || !tensor_ok(k, sk) || !tensor_ok(v, sv) || !tensor_ok(o, so))
     return fail(AQ_EINVAL, "attn_qat_fwd: tensors must be 16-byte aligned with strides that are multiples of 8 "
                            "elements and below 2^24");
+  if ((lse_log2 || chunk_max_log2 || o_hp) && !(lse_log2 && chunk_max_log2 && o_hp))
+    return fail(AQ_EINVAL, "attn_qat_fwd: the training outputs lse_log2, chunk_max_log2 and o_hp come together "
+                           "(all three or none)");
   const size_t need = aq::workspace_bytes(0, batch, num_heads, lq, lk);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
     return fail(AQ_EINVAL, "attn_qat_fwd: workspace must be 256-byte aligned and hold %zu bytes",

@@ -143,58 +143,62 @@ __device__ __forceinline__ void e2m1_pair(float &a, float &b) {
   b = r[1];
 }
 
-// Eight quotients rounded to E2M1 in one code register (byte i holds pair i), then converted
-// back; same rounding as e2m1_pair.
-__device__ __forceinline__ void e2m1_oct(float *r) {
+// ---- Softmax-probability fake quantization in the attention kernels -----------------------
+// A P block (16 keys of one query) has P = exp2(y - m) with y = c * logit.  Its scale is
+// S = E4M3(amax / 6) with amax = exp2(c * logit_max - m), logit_max the block's largest logit
+// (exp2 is monotone).
+// The E2M1 argument P / S is taken in one exponential, r = exp2(y - mb) with mb = m + log2(Sd),
+// Sd = S, or 1 for a block whose scale is 0 (then every P <= 6 * 2^-10 < 0.25 and every code is
+// 0).  The unquantized P of the block is Sd * r.  Forward and backward both use this exact
+// sequence, so they agree on every code.
+struct ProbBlock {
+  float S;   // the block scale (0 for a zero block)
+  float Sd;  // S, or 1 when S == 0
+  float mb;  // m + log2(Sd)
+};
+__device__ __forceinline__ ProbBlock prob_block(float logit_max, float c, float m) {
+  const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(logit_max, c, -m));
+  const float S = block_scale_unit(am);
+  const float Sd = S == 0.0f ? 1.0f : S;
+  return ProbBlock{S, Sd, m + __builtin_amdgcn_logf(Sd)};
+}
+
+// Eight values rounded to E2M1 codes in one register (byte i holds pair i; ties to the even
+// code, saturating at 6), by the gfx950 packed FP4 conversion with a unit scale.
+__device__ __forceinline__ uint32_t e2m1_codes8(const float *r) {
   uint32_t code = 0u;
   code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[0], r[1], 1.0f, 0);
   code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[2], r[3], 1.0f, 1);
   code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[4], r[5], 1.0f, 2);
   code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[6], r[7], 1.0f, 3);
+  return code;
+}
+// The eight coded values times f, as fp32.
+__device__ __forceinline__ void e2m1_decode8(uint32_t code, float f, float *x) {
   const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
   const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 1);
   const auto c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 2);
   const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 3);
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  x[0] = a[0] * f; x[1] = a[1] * f; x[2] = b[0] * f; x[3] = b[1] * f;
+  x[4] = c[0] * f; x[5] = c[1] * f; x[6] = d[0] * f; x[7] = d[1] * f;
 }
-
-// Softmax-probability fake quantization of 8 values of one block (see fq_prob_pair).
-__device__ __forceinline__ void fq_prob_oct(float *x, float S, float inv) {
-  float r[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = x[i] * inv;
-  e2m1_oct(r);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = r[i] * S;
-}
-
-// The same quantization with another dequantization factor: x = E2M1(x * inv) * sdq (the backward
-// folds the probability normalisation into sdq = S * exp2(m_c - lse)).
-__device__ __forceinline__ void fq_prob_oct_dq(float *x, float inv, float sdq) {
-  float r[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = x[i] * inv;
-  e2m1_oct(r);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = r[i] * sdq;
+// The eight coded values times S as fp16 (exact: an E2M1 value times an E4M3 scale has at most 6
+// significant bits and lies in [2^-10, 6 * 448]), packed two per register.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 e2m1_decode8_f16(uint32_t code, float S) {
+  const _Float16 h = (_Float16)S;
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0) * h;
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 1) * h;
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 2) * h;
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 3) * h;
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
 }
 
 // Fake-quantize two non-negative values of one block (unit global scale, scale S and inv = 1/S,
 // inv = 0 for a zero block): E2M1(x / S) * S.
 __device__ __forceinline__ void fq_pos_pair(float &a, float &b, float S, float inv) {
   float ra = div_e4m3(a, S, inv), rb = div_e4m3(b, S, inv);
-  e2m1_pair(ra, rb);
-  a = ra * S;
-  b = rb * S;
-}
-
-// Softmax-probability variant: the quotient is the fp32 product x * fl(1/S) rather than the
-// correctly rounded x / S (they differ by at most one ulp, so only inputs within an ulp of an
-// E2M1 midpoint can round the other way - the same size as the error of the hardware exp2 that
-// produced x).  Used for P, whose forward and backward share this exact function.
-__device__ __forceinline__ void fq_prob_pair(float &a, float &b, float S, float inv) {
-  float ra = a * inv, rb = b * inv;
   e2m1_pair(ra, rb);
   a = ra * S;
   b = rb * S;

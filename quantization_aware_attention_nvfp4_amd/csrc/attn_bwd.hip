@@ -325,27 +325,32 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
     const int last = qrow >= lq ? -1 : (p.causal && qrow < (int)p.lk - 1 ? qrow : (int)p.lk - 1);
     mask_tail(s, valid_prefix(ln.key_base, last));
   }
-  // A = exp2(y - m_c) exp2(m_c - lse2); dS = A (dP - D); A-hat = fq(exp2(y - m_c)) exp2(m_c - lse2).
+  // A = exp2(y - m_c) exp2(m_c - lse2); dS = A (dP - D); A-hat = fq(exp2(y - m_c)) exp2(m_c - lse2),
+  // with the P block's codes formed exactly as the forward formed them (prob_block).
   float bm = s[0];
 #pragma unroll
   for (int rr = 1; rr < 16; ++rr) bm = fmaxf(bm, s[rr]);
   const float w = __builtin_amdgcn_exp2f(mc - lse2);
-  const float wD = w * Di;
   float ah[16], ds[16];
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    ah[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -mc));
-    ds[rr] = ah[rr] * __builtin_fmaf(w, dp[rr], -wD);
-  }
   if (p.quant_p) {
-    const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(bm, p.c, -mc));  // as the forward
-    const float S = block_scale_unit(am);
-    const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
-    fq_prob_oct_dq(ah, inv, S * w);
-    fq_prob_oct_dq(ah + 8, inv, S * w);
-  } else {
+    const ProbBlock pb = prob_block(bm, p.c, mc);
+    const float sw = pb.Sd * w, swD = sw * Di;  // A = r * Sd * w
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) ah[rr] *= w;
+    for (int rr = 0; rr < 16; ++rr) {
+      ah[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -pb.mb));  // P / Sd
+      ds[rr] = ah[rr] * __builtin_fmaf(sw, dp[rr], -swD);
+    }
+    const uint32_t c0 = e2m1_codes8(ah), c1 = e2m1_codes8(ah + 8);
+    e2m1_decode8(c0, pb.S * w, ah);
+    e2m1_decode8(c1, pb.S * w, ah + 8);
+  } else {
+    const float wD = w * Di;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      ah[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -mc));
+      ds[rr] = ah[rr] * __builtin_fmaf(w, dp[rr], -wD);
+      ah[rr] *= w;
+    }
   }
   // Move A-hat and dS to one key per lane: D[query][key] = sum_k X[query][k] onehot[k][key].
   const uint32_t oh = lds0 + kLdsOneHot + 16 * (threadIdx.x & 63);

@@ -57,16 +57,46 @@ struct FwdParams {
   int64_t nblocks;   // heads*batch*qtiles
   int64_t per_xcd;   // ceil(nblocks / 8)
   float c;           // softmax_scale * log2(e)
-  bool causal, quant_q, quant_p;
+  bool causal, quant_q;
 };
 
-template <int WAVES, bool TRAIN>
-__global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
-  static_assert(WAVES == 4, "LDS staging assumes 256 lanes");
+// Copy offsets of this lane's 16-byte pieces of a staged [128][256 B] tile: LDS instruction i of
+// wave w covers rows 16i + 4w .. +3 (physical column lane%16); the lane fetches the logical
+// column the swizzle maps there.  Row 16i + 4w + lane/16 of the source starts 4096*i bytes past
+// the tile base, which the wave-uniform base absorbs, so one 32-bit offset serves every i whose
+// swizzle term is the same (sw_kq depends on i%2, sw_row not at all).
+struct StageOffsets {
+  uint32_t k_even, k_odd, v;
+};
+__device__ __forceinline__ StageOffsets stage_offsets(int wave, int lane) {
+  const int r = 4 * wave + (lane >> 4), pc = lane & 15;
+  return StageOffsets{(uint32_t)(r * 256 + ((pc ^ sw_kq(r)) << 4)),
+                      (uint32_t)(r * 256 + ((pc ^ sw_kq(r + 16)) << 4)),
+                      (uint32_t)(r * 256 + ((pc ^ sw_row(r)) << 4))};
+}
+__device__ __forceinline__ void stage_k(const uint8_t *gtile, uint8_t *lds, const StageOffsets &so, int wave) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load_lds16_s(gtile + 4096 * i, (i & 1) ? so.k_odd : so.k_even, lds + 4096 * i + 1024 * wave);
+}
+__device__ __forceinline__ void stage_v(const uint8_t *gtile, uint8_t *lds, const StageOffsets &so, int wave) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load_lds16_s(gtile + 4096 * i, so.v, lds + 4096 * i + 1024 * wave);
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// TRAIN: also write lse, chunk maxima and O^hp.  QP: P is fake-quantized.  F16: P-hat and V-hat
+// (both fake-quantized, hence exact in fp16) multiply on the fp16 MFMA, whose products are the
+// same as the bf16 ones for these values.
+template <bool TRAIN, bool QP, bool F16>
+__global__ __launch_bounds__(256, TRAIN ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
+  static_assert(!F16 || QP, "the fp16 product needs a quantized P");
+  constexpr int WAVES = 4;
   constexpr int BM = 32 * WAVES;
+  constexpr bool HP = TRAIN && QP;  // O^hp needs its own product only when P is quantized
   // Separate objects, so the compiler can tell reads of one tile from copies into the other.
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kChunk * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kChunk * 256];
+  __shared__ __attribute__((aligned(256))) uint8_t lds_k[kChunk * 256];
+  __shared__ __attribute__((aligned(256))) uint8_t lds_v[kChunk * 256];
   __shared__ int32_t lds_sel[kMaxSel];
 
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
@@ -76,7 +106,7 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
   const int64_t bb = bh / p.heads, hh = bh % p.heads;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
   const int lane = tid & 63;
   const int n = lane & 31;   // the lane's query within the wave
   const int hf = lane >> 5;  // lane half
@@ -94,14 +124,17 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
     for (int i = tid; i < p.nchunks; i += WAVES * 64) lds_sel[i] = src[i];
     __syncthreads();
   }
-  auto chunk_of = [&](int64_t it) -> int64_t { return p.sel ? (int64_t)lds_sel[it] : it; };
+  auto chunk_of = [&](int64_t it) -> int64_t {
+    return p.sel ? (int64_t)__builtin_amdgcn_readfirstlane(lds_sel[it]) : it;  // uniform: a scalar
+  };
   auto ktile = [&](int64_t c) { return (const uint8_t *)(p.kq + (bh * p.kchunks + c) * (kChunk * kD / 8)); };
   auto vtile = [&](int64_t c) { return (const uint8_t *)(p.vt + (bh * p.kchunks + c) * (kChunk * kD / 8)); };
 
   // Start the first chunk's copies before the Q work so they overlap it.
+  const StageOffsets so = stage_offsets(wave, lane);
   int64_t chunk = chunk_of(0);
-  stage_tile_async<sw_kq>(ktile(chunk), lds_k, wave, lane);
-  stage_tile_async<sw_row>(vtile(chunk), lds_v, wave, lane);
+  stage_k(ktile(chunk), lds_k, so, wave);
+  stage_v(vtile(chunk), lds_v, so, wave);
 
   // ---- Q-hat fragment: B operand of S^T, d = 16t + 8hf + (0..7) -------------------------
   bf16x8 qf[8];
@@ -130,41 +163,52 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
   }
 
   f32x16 acc[4];
-  f32x16 acc_hp[TRAIN ? 4 : 1];
+  f32x16 acc_hp[HP ? 4 : 1];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 #pragma unroll
-  for (int dt = 0; dt < (TRAIN ? 4 : 1); ++dt) acc_hp[dt] = f32x16{};
+  for (int dt = 0; dt < (HP ? 4 : 1); ++dt) acc_hp[dt] = f32x16{};
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
 
-  // The K row this lane feeds as A-operand row n of each 32-key sub-tile.
-  const int krow = perm_row(n);
+  // LDS byte addresses of this lane's A-operand reads.  The arrays are 256-byte aligned and a
+  // column's XOR swizzle only touches bits 4..7 of the offset, so the loop-dependent part of a
+  // column index enters as one XOR.  K-hat row krow, column 2t + hf: `^ 32*t`.  V-hat^T row
+  // d = 32*dt + n, column 4*kt + 2*hf + j: sw_row(d) = n & 15 for every dt, so the physical
+  // column (4*kt + j) ^ (2*hf ^ sw) is `^ 16*(4*kt + j)`.
+  uint32_t ka, va;
+  {
+    const int krow = perm_row(n), swk = sw_kq(krow);
+    ka = lds_addr(lds_k) + krow * 256 + 16 * (hf ^ swk);
+    const int swv = n & 15;
+    va = lds_addr(lds_v) + n * 256 + 16 * ((2 * hf) ^ swv);
+  }
 
   for (int64_t it = 0; it < n_iter; ++it) {
     // K-hat(chunk) has landed once this wave's V copies (issued after it) are the only ones
     // outstanding; the barrier makes every wave's copies visible.
     AQ_WAIT_VMCNT(8);
     __builtin_amdgcn_s_barrier();
+    AQ_OPAQUE(ka);
+    AQ_OPAQUE(va);
 
     // ---- S^T = K-hat Q-hat^T for the 128 keys of the chunk ------------------------------
     f32x16 s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       s[kt] = f32x16{};
-      const int r = 32 * kt + krow;
 #pragma unroll
       for (int t0 = 0; t0 < 8; t0 += 4) {
         bf16x8 a[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) a[t] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds_k + kq_off(r, 2 * (t0 + t) + hf)));
+        for (int t = 0; t < 4; ++t) a[t] = as_bf16x8(lds_read16((ka ^ (32 * (t0 + t))) + 8192 * kt));
 #pragma unroll
         for (int t = 0; t < 4; ++t) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qf[t0 + t], s[kt], 0, 0, 0);
       }
     }
     const int64_t next = it + 1 < n_iter ? chunk_of(it + 1) : -1;
     __builtin_amdgcn_s_barrier();  // every wave is done reading K-hat(chunk)
-    if (next >= 0) stage_tile_async<sw_kq>(ktile(next), lds_k, wave, lane);
+    if (next >= 0) stage_k(ktile(next), lds_k, so, wave);
 
     // ---- masks: keys past lk (last chunk) and causal -------------------------------------
     const int64_t key0 = chunk * kChunk + 16 * hf;  // key of register 0 in sub-tile 0
@@ -177,8 +221,7 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
     }
 
     // ---- running max (refreshed once per chunk) -----------------------------------------
-    // Block maxima of the logits first: each lane's 16 registers of a sub-tile are one P block,
-    // and exp2 is monotone, so the block's P amax is exp2 of its logit max.
+    // Block maxima of the logits first: each lane's 16 registers of a sub-tile are one P block.
     float bmax[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -191,15 +234,15 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
     cm = pair_max(cm);
     const float m_new = fmaxf(m_run, cm * p.c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
-    if (p.cmax && hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
+    if (TRAIN && hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
     m_run = m_new;
     // The rescale is skipped when no row of the wave moved its maximum (alpha == 1 exactly).
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
-      if (TRAIN) {
+      if (HP) {
 #pragma unroll
-        for (int dt = 0; dt < (TRAIN ? 4 : 1); ++dt) acc_hp[dt] *= alpha;
+        for (int dt = 0; dt < (HP ? 4 : 1); ++dt) acc_hp[dt] *= alpha;
       }
     }
 
@@ -211,44 +254,78 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
     float psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      float P[16];
+      u32x4 pq[2], ph[2];
+      if (QP) {
+        const ProbBlock pb = prob_block(bmax[kt], p.c, m_new);
+        float r[16], rsum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        P[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], p.c, -m_new));
-        psum += P[r];
+        for (int i = 0; i < 16; ++i) {
+          r[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], p.c, -pb.mb));
+          rsum += r[i];
+        }
+        psum = __builtin_fmaf(pb.Sd, rsum, psum);
+        const uint32_t c0 = e2m1_codes8(r), c1 = e2m1_codes8(r + 8);
+        if (F16) {
+          pq[0] = e2m1_decode8_f16(c0, pb.S);
+          pq[1] = e2m1_decode8_f16(c1, pb.S);
+        } else {
+          float x[8];
+          e2m1_decode8(c0, pb.S, x);
+          pq[0] = __builtin_bit_cast(u32x4, pack8_cvt(x));
+          e2m1_decode8(c1, pb.S, x);
+          pq[1] = __builtin_bit_cast(u32x4, pack8_cvt(x));
+        }
+        if (HP) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) r[i] *= pb.Sd;  // the unquantized P
+          if (F16) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              f16x8 h;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) h[i] = (_Float16)r[8 * j + i];
+              ph[j] = __builtin_bit_cast(u32x4, h);
+            }
+          } else {
+            ph[0] = __builtin_bit_cast(u32x4, pack8_cvt(r));
+            ph[1] = __builtin_bit_cast(u32x4, pack8_cvt(r + 8));
+          }
+        }
+      } else {
+        float P[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          P[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], p.c, -m_new));
+          psum += P[i];
+        }
+        pq[0] = __builtin_bit_cast(u32x4, pack8_cvt(P));
+        pq[1] = __builtin_bit_cast(u32x4, pack8_cvt(P + 8));
       }
-      bf16x8 ph[2];
-      if (TRAIN) {
-        ph[0] = pack8_cvt(P);
-        ph[1] = pack8_cvt(P + 8);
-      }
-      if (p.quant_p) {
-        const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(bmax[kt], p.c, -m_new));
-        const float S = block_scale_unit(am);
-        const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
-        fq_prob_oct(P, S, inv);
-        fq_prob_oct(P + 8, S, inv);
-      }
-      bf16x8 pq[2];
-      pq[0] = pack8_cvt(P);
-      pq[1] = pack8_cvt(P + 8);
-      bf16x8 a[2][4];
+      u32x4 a[2][4];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          a[j][dt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds_v + row_off(32 * dt + n, 4 * kt + 2 * hf + j)));
+        for (int dt = 0; dt < 4; ++dt) a[j][dt] = lds_read16((va ^ (16 * (4 * kt + j))) + 8192 * dt);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][dt], pq[j], acc[dt], 0, 0, 0);
-          if (TRAIN) acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][dt], ph[j], acc_hp[dt], 0, 0, 0);
+          if (F16) {
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[j][dt]),
+                                                             __builtin_bit_cast(f16x8, pq[j]), acc[dt], 0, 0, 0);
+            if (HP)
+              acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[j][dt]),
+                                                                  __builtin_bit_cast(f16x8, ph[j]), acc_hp[dt], 0, 0, 0);
+          } else {
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[j][dt]), as_bf16x8(pq[j]), acc[dt], 0, 0, 0);
+            if (HP)
+              acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[j][dt]), as_bf16x8(ph[j]), acc_hp[dt], 0, 0, 0);
+          }
         }
     }
     l_run = l_run * alpha + psum;
     __builtin_amdgcn_s_barrier();  // every wave is done reading V-hat(chunk)
-    if (next >= 0) stage_tile_async<sw_row>(vtile(next), lds_v, wave, lane);
+    if (next >= 0) stage_v(vtile(next), lds_v, so, wave);
     chunk = next;
   }
 
@@ -267,15 +344,18 @@ __global__ __launch_bounds__(WAVES * 64, TRAIN ? 1 : 2) void attn_fwd_kernel(Fwd
                         (__bf16)(acc[dt][4 * a + 2] * inv_l), (__bf16)(acc[dt][4 * a + 3] * inv_l)};
       *(bf16x4 *)(op + d0) = w;
       if (TRAIN) {
+        const f32x16 &h = HP ? acc_hp[HP ? dt : 0] : acc[dt];
         float *hp = p.o_hp + (bh * p.lq + qrow) * kD + d0;
-        *(f32x4 *)hp = f32x4{acc_hp[dt][4 * a] * inv_l, acc_hp[dt][4 * a + 1] * inv_l,
-                             acc_hp[dt][4 * a + 2] * inv_l, acc_hp[dt][4 * a + 3] * inv_l};
+        *(f32x4 *)hp = f32x4{h[4 * a] * inv_l, h[4 * a + 1] * inv_l, h[4 * a + 2] * inv_l, h[4 * a + 3] * inv_l};
       }
     }
-  if (p.lse && hf == 0) p.lse[bh * p.lq + qrow] = m_run + __builtin_amdgcn_logf(l);
+  if (TRAIN && hf == 0) p.lse[bh * p.lq + qrow] = m_run + __builtin_amdgcn_logf(l);
 }
 
 }  // namespace
+
+// fp16 P-hat V-hat product: both operands fake-quantized.
+static bool use_f16(unsigned flags) { return (flags & 4u) && (flags & 8u); }
 
 hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t nsel, hipStream_t stream) {
   constexpr int WAVES = 4;
@@ -304,13 +384,20 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   p.c = (float)((double)a.scale * 1.4426950408889634);
   p.causal = a.causal;
   p.quant_q = (a.flags & 1u) != 0;
-  p.quant_p = (a.flags & 8u) != 0;
-  if (a.o_hp)
-    AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<WAVES, true>), dim3((unsigned)(p.per_xcd * 8)), dim3(WAVES * 64), 0,
-                       stream, p);
-  else
-    AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<WAVES, false>), dim3((unsigned)(p.per_xcd * 8)), dim3(WAVES * 64), 0,
-                       stream, p);
+  const bool qp = (a.flags & 8u) != 0, f16 = use_f16(a.flags);
+  // Training outputs come as a set (lse, chunk maxima, O^hp).
+  const bool train = a.o_hp && a.lse && a.cmax;
+  if (!train && (a.o_hp || a.lse || a.cmax)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.per_xcd * 8)), block(WAVES * 64);
+  if (train) {
+    if (f16) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, true>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, false, false>), grid, block, 0, stream, p);
+  } else {
+    if (f16) AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, true, true>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, true, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, false, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -321,8 +408,8 @@ hipError_t launch_kv_prepass(const AttnArgs &a, hipStream_t stream) {
   hipError_t e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, (a.flags & 2u) ? kQuantD : kQuantNone,
                                      ws + w.kq, nullptr, stream);
   if (e != hipSuccess) return e;
-  return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, (a.flags & 4u) ? kQuantRows : kQuantNone,
-                             nullptr, ws + w.vt, stream);
+  const TileQuant qv = use_f16(a.flags) ? kQuantRowsF16 : ((a.flags & 4u) ? kQuantRows : kQuantNone);
+  return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qv, nullptr, ws + w.vt, stream);
 }
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {

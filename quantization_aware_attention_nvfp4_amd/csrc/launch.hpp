@@ -96,9 +96,10 @@ hipError_t launch_fq(const void *x, void *y, int64_t outer, int64_t axis, int64_
 hipError_t launch_static_scale(const void *x, int64_t n, float *g_out, hipStream_t stream);
 
 // One 128-row chunk of a strided [B, L, H, 128] bf16 tensor per workgroup: optional fake
-// quantization (kQuantNone, kQuantD along d per row, kQuantRows along rows per column), then a
+// quantization (kQuantNone, kQuantD along d per row, kQuantRows along rows per column; kQuantRowsF16
+// the same with fp16 output values), then a
 // row-major copy and/or a d-major tile copy into the workspace.
-enum TileQuant { kQuantNone = 0, kQuantD = 1, kQuantRows = 2 };
+enum TileQuant { kQuantNone = 0, kQuantD = 1, kQuantRows = 2, kQuantRowsF16 = 3 };
 hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
                                TileQuant quant, void *rows_out, void *tiles_out,
                                hipStream_t stream);

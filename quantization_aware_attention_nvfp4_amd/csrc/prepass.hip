@@ -6,6 +6,9 @@
 // Quantizing each operand once here keeps the codec out of the attention kernels' inner loops,
 // where it would be repeated by every query tile of a head.
 //
+// kQuantRowsF16 writes the V-hat values as fp16 instead of bf16 (exact, see below) for the
+// forward's fp16 P-hat V-hat product.
+//
 // One workgroup handles one 128-row chunk of one head: the chunk is staged in LDS as
 // [row][d] (rows past L read as zero), quantized in place, then written as
 //   rows_out  [B*H, C*128, 128]       row-major (the MFMA operand rows of the attention kernels)
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
                      pack_exact_bf16(f[8 * i + 4], f[8 * i + 5]), pack_exact_bf16(f[8 * i + 6], f[8 * i + 7])};
     }
     __syncthreads();
-  } else if (quant == kQuantRows) {
+  } else if (quant == kQuantRows || quant == kQuantRowsF16) {
     // lane: column d = tid%128, rows [64*(tid/128), +64): four 16-row blocks
     const int d = tid & (kD - 1), r0 = (tid >> 7) * 64;
     for (int blk = 0; blk < 4; ++blk) {
@@ -81,8 +84,15 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
       const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
 #pragma unroll
       for (int i = 0; i < 16; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);
+      // kQuantRowsF16: the value as fp16 bits.  Every unit-scale NVFP4 value (|x| <= 6 * 448,
+      // nonzero |x| >= 2^-10, at most 6 significant bits) is exact in fp16.
+      if (quant == kQuantRowsF16) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tile[r0 + 16 * blk + i][d] = (uint16_t)(f2u(f[i]) >> 16);
+        for (int i = 0; i < 16; ++i) tile[r0 + 16 * blk + i][d] = __builtin_bit_cast(uint16_t, (_Float16)f[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tile[r0 + 16 * blk + i][d] = (uint16_t)(f2u(f[i]) >> 16);
+      }
     }
     __syncthreads();
   }

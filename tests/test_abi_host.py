@@ -77,6 +77,13 @@ def test_forward_rejects_bad_arguments(lib, kw, code, msg):
     assert msg in lib.aq_last_error().decode()
 
 
+def test_forward_training_outputs_come_together(lib):
+    s = S(64 * 256, 128, 256)
+    rc = lib.attn_qat_fwd(16, 16, 16, 16, 1, 2, 2, 128, 64, 64, s, s, s, s, 0.088, 0, 15, 256, None, None, 256,
+                          1 << 40, None)
+    assert rc == -1 and "together" in lib.aq_last_error().decode()
+
+
 def test_backward_requires_statistics(lib):
     s = S(64 * 256, 128, 256)
     rc = lib.attn_qat_bwd(16, 16, 16, None, 16, None, None, 16, 16, 16, 1, 2, 2, 128, 64, 64, s, s, s, s, s, s, s,
