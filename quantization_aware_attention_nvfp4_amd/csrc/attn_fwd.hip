@@ -60,27 +60,32 @@ struct FwdParams {
   bool causal, quant_q;
 };
 
-// Copy offsets of this lane's 16-byte pieces of a staged [128][256 B] tile: LDS instruction i of
-// wave w covers rows 16i + 4w .. +3 (physical column lane%16); the lane fetches the logical
-// column the swizzle maps there.  Row 16i + 4w + lane/16 of the source starts 4096*i bytes past
-// the tile base, which the wave-uniform base absorbs, so one 32-bit offset serves every i whose
-// swizzle term is the same (sw_kq depends on i%2, sw_row not at all).
+// Copy offsets of this lane's 16-byte pieces of a staged [128][256 B] tile by a workgroup of
+// WAVES waves: LDS instruction i of wave w covers rows 4*WAVES*i + 4w .. +3 (physical column
+// lane%16); the lane fetches the logical column the swizzle maps there.  Row 4*WAVES*i + 4w +
+// lane/16 of the source starts 1024*WAVES*i bytes past the tile base, which the wave-uniform base
+// absorbs, so one 32-bit offset serves every i whose swizzle term is the same (sw_kq depends on
+// row bit 4, i.e. on i%2 for 4 waves and not on i for 8; sw_row on neither).
 struct StageOffsets {
   uint32_t k_even, k_odd, v;
 };
+template <int WAVES>
 __device__ __forceinline__ StageOffsets stage_offsets(int wave, int lane) {
   const int r = 4 * wave + (lane >> 4), pc = lane & 15;
   return StageOffsets{(uint32_t)(r * 256 + ((pc ^ sw_kq(r)) << 4)),
-                      (uint32_t)(r * 256 + ((pc ^ sw_kq(r + 16)) << 4)),
+                      (uint32_t)(r * 256 + ((pc ^ sw_kq(r + 4 * WAVES)) << 4)),
                       (uint32_t)(r * 256 + ((pc ^ sw_row(r)) << 4))};
 }
+template <int WAVES>
 __device__ __forceinline__ void stage_k(const uint8_t *gtile, uint8_t *lds, const StageOffsets &so, int wave) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) load_lds16_s(gtile + 4096 * i, (i & 1) ? so.k_odd : so.k_even, lds + 4096 * i + 1024 * wave);
+  for (int i = 0; i < 32 / WAVES; ++i)
+    load_lds16_s(gtile + 1024 * WAVES * i, (i & 1) ? so.k_odd : so.k_even, lds + 1024 * WAVES * i + 1024 * wave);
 }
+template <int WAVES>
 __device__ __forceinline__ void stage_v(const uint8_t *gtile, uint8_t *lds, const StageOffsets &so, int wave) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) load_lds16_s(gtile + 4096 * i, so.v, lds + 4096 * i + 1024 * wave);
+  for (int i = 0; i < 32 / WAVES; ++i) load_lds16_s(gtile + 1024 * WAVES * i, so.v, lds + 1024 * WAVES * i + 1024 * wave);
 }
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -88,15 +93,22 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // TRAIN: also write lse, chunk maxima and O^hp.  QP: P is fake-quantized.  F16: P-hat and V-hat
 // (both fake-quantized, hence exact in fp16) multiply on the fp16 MFMA, whose products are the
 // same as the bf16 ones for these values.
+//
+// Inference: 4 waves (128 queries) per workgroup, two workgroups per CU.  With the O^hp product
+// the two accumulators leave no room for the Q-hat operand in registers at two waves per SIMD,
+// so that variant runs 8 waves (256 queries) per workgroup, one per CU, with each wave's Q-hat
+// rows in LDS (8 KiB per wave) and re-read once per chunk.
 template <bool TRAIN, bool QP, bool F16>
-__global__ __launch_bounds__(256, TRAIN ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__((TRAIN && QP) ? 512 : 256, (TRAIN && QP) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   static_assert(!F16 || QP, "the fp16 product needs a quantized P");
-  constexpr int WAVES = 4;
-  constexpr int BM = 32 * WAVES;
   constexpr bool HP = TRAIN && QP;  // O^hp needs its own product only when P is quantized
+  constexpr bool QL = HP;           // Q-hat operand from LDS
+  constexpr int WAVES = QL ? 8 : 4;
+  constexpr int BM = 32 * WAVES;
   // Separate objects, so the compiler can tell reads of one tile from copies into the other.
   __shared__ __attribute__((aligned(256))) uint8_t lds_k[kChunk * 256];
   __shared__ __attribute__((aligned(256))) uint8_t lds_v[kChunk * 256];
+  __shared__ __attribute__((aligned(256))) uint8_t lds_q[QL ? WAVES * 32 * 256 : 256];
   __shared__ int32_t lds_sel[kMaxSel];
 
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
@@ -131,10 +143,10 @@ __global__ __launch_bounds__(256, TRAIN ? 1 : 2) void attn_fwd_kernel(FwdParams 
   auto vtile = [&](int64_t c) { return (const uint8_t *)(p.vt + (bh * p.kchunks + c) * (kChunk * kD / 8)); };
 
   // Start the first chunk's copies before the Q work so they overlap it.
-  const StageOffsets so = stage_offsets(wave, lane);
+  const StageOffsets so = stage_offsets<WAVES>(wave, lane);
   int64_t chunk = chunk_of(0);
-  stage_k(ktile(chunk), lds_k, so, wave);
-  stage_v(vtile(chunk), lds_v, so, wave);
+  stage_k<WAVES>(ktile(chunk), lds_k, so, wave);
+  stage_v<WAVES>(vtile(chunk), lds_v, so, wave);
 
   // ---- Q-hat fragment: B operand of S^T, d = 16t + 8hf + (0..7) -------------------------
   bf16x8 qf[8];
@@ -160,6 +172,16 @@ __global__ __launch_bounds__(256, TRAIN ? 1 : 2) void attn_fwd_kernel(FwdParams 
       }
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
+  }
+  // QL: the wave's 32 Q-hat rows go to its own LDS region (row n = the lane's query, columns
+  // swizzled by sw_row), read back as the S^T B operand once per chunk.
+  uint32_t qa = 0;
+  if (QL) {
+    const int sw = n & 15;
+    uint8_t *qrow_lds = lds_q + wave * 8192 + n * 256;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) *(bf16x8 *)(qrow_lds + (((2 * t + hf) ^ sw) << 4)) = qf[t];
+    qa = lds_addr(lds_q) + wave * 8192 + n * 256 + 16 * (hf ^ sw);
   }
 
   f32x16 acc[4];
@@ -187,28 +209,42 @@ __global__ __launch_bounds__(256, TRAIN ? 1 : 2) void attn_fwd_kernel(FwdParams 
   for (int64_t it = 0; it < n_iter; ++it) {
     // K-hat(chunk) has landed once this wave's V copies (issued after it) are the only ones
     // outstanding; the barrier makes every wave's copies visible.
-    AQ_WAIT_VMCNT(8);
+    if constexpr (WAVES == 4) AQ_WAIT_VMCNT(8); else AQ_WAIT_VMCNT(4);
     __builtin_amdgcn_s_barrier();
     AQ_OPAQUE(ka);
     AQ_OPAQUE(va);
 
     // ---- S^T = K-hat Q-hat^T for the 128 keys of the chunk ------------------------------
     f32x16 s[4];
+    if constexpr (QL) {
+      // Q-hat column pair t is read once and feeds the four sub-tiles' chains.
+      AQ_OPAQUE(qa);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = f32x16{};
+      for (int kt = 0; kt < 4; ++kt) s[kt] = f32x16{};
 #pragma unroll
-      for (int t0 = 0; t0 < 8; t0 += 4) {
-        bf16x8 a[4];
+      for (int t = 0; t < 8; ++t) {
+        const bf16x8 b = as_bf16x8(lds_read16(qa ^ (32 * t)));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) a[t] = as_bf16x8(lds_read16((ka ^ (32 * (t0 + t))) + 8192 * kt));
+        for (int kt = 0; kt < 4; ++kt)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16((ka ^ (32 * t)) + 8192 * kt)), b, s[kt], 0, 0, 0);
+      }
+    } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qf[t0 + t], s[kt], 0, 0, 0);
+      for (int kt = 0; kt < 4; ++kt) {
+        s[kt] = f32x16{};
+#pragma unroll
+        for (int t0 = 0; t0 < 8; t0 += 4) {
+          bf16x8 a[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) a[t] = as_bf16x8(lds_read16((ka ^ (32 * (t0 + t))) + 8192 * kt));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qf[t0 + t], s[kt], 0, 0, 0);
+        }
       }
     }
     const int64_t next = it + 1 < n_iter ? chunk_of(it + 1) : -1;
     __builtin_amdgcn_s_barrier();  // every wave is done reading K-hat(chunk)
-    if (next >= 0) stage_k(ktile(next), lds_k, so, wave);
+    if (next >= 0) stage_k<WAVES>(ktile(next), lds_k, so, wave);
 
     // ---- masks: keys past lk (last chunk) and causal -------------------------------------
     const int64_t key0 = chunk * kChunk + 16 * hf;  // key of register 0 in sub-tile 0
@@ -247,7 +283,9 @@ __global__ __launch_bounds__(256, TRAIN ? 1 : 2) void attn_fwd_kernel(FwdParams 
     }
 
     // V-hat(chunk): wait for this wave's V copies (K(next) may still be in flight).
-    if (next >= 0) AQ_WAIT_VMCNT(8); else AQ_WAIT_VMCNT(0);
+    if (next < 0) AQ_WAIT_VMCNT(0);
+    else if constexpr (WAVES == 4) AQ_WAIT_VMCNT(8);
+    else AQ_WAIT_VMCNT(4);
     __builtin_amdgcn_s_barrier();
 
     // ---- per 32-key sub-tile: P, its sum, P-hat, and O^T += V-hat^T P-hat^T ---------------
@@ -325,7 +363,7 @@ __global__ __launch_bounds__(256, TRAIN ? 1 : 2) void attn_fwd_kernel(FwdParams 
     }
     l_run = l_run * alpha + psum;
     __builtin_amdgcn_s_barrier();  // every wave is done reading V-hat(chunk)
-    if (next >= 0) stage_v(vtile(next), lds_v, so, wave);
+    if (next >= 0) stage_v<WAVES>(vtile(next), lds_v, so, wave);
     chunk = next;
   }
 
@@ -378,17 +416,19 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   p.lk = a.lk;
   p.kchunks = (a.lk + kChunk - 1) / kChunk;
   p.nchunks = sel ? nsel : p.kchunks;
-  p.qtiles = (int)((a.lq + 32 * WAVES - 1) / (32 * WAVES));
+  const bool qp = (a.flags & 8u) != 0, f16 = use_f16(a.flags);
+  // Training outputs come as a set (lse, chunk maxima, O^hp).
+  const bool train = a.o_hp && a.lse && a.cmax;
+  if (!train && (a.o_hp || a.lse || a.cmax)) return hipErrorInvalidValue;
+  const int waves = (train && qp) ? 8 : WAVES;  // see attn_fwd_kernel
+  if (sel && waves != WAVES) return hipErrorInvalidValue;  // chunk lists are per 128 queries
+  p.qtiles = (int)((a.lq + 32 * waves - 1) / (32 * waves));
   p.nblocks = (int64_t)a.batch * a.heads * p.qtiles;
   p.per_xcd = (p.nblocks + 7) / 8;
   p.c = (float)((double)a.scale * 1.4426950408889634);
   p.causal = a.causal;
   p.quant_q = (a.flags & 1u) != 0;
-  const bool qp = (a.flags & 8u) != 0, f16 = use_f16(a.flags);
-  // Training outputs come as a set (lse, chunk maxima, O^hp).
-  const bool train = a.o_hp && a.lse && a.cmax;
-  if (!train && (a.o_hp || a.lse || a.cmax)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(p.per_xcd * 8)), block(WAVES * 64);
+  const dim3 grid((unsigned)(p.per_xcd * 8)), block(waves * 64);
   if (train) {
     if (f16) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, true>), grid, block, 0, stream, p);
     else if (qp) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, false>), grid, block, 0, stream, p);
