@@ -76,8 +76,8 @@ def cpu_baseline(q, k, v, do, seconds: float):
     # sample from both so the timed call takes about `seconds`.
     run(np.arange(0, L, L // 16)[:16])  # first call: library load and thread start-up
     t16 = run(np.linspace(0, L - 1, 16).astype(np.int64))
-    t64 = run(np.linspace(0, L - 1, 64).astype(np.int64))
-    per_row = max((t64 - t16) / 48, 1e-5)
+    t256 = run(np.linspace(0, L - 1, 256).astype(np.int64))  # enough rows to keep every core busy
+    per_row = max((t256 - t16) / 240, 1e-5)
     fixed = max(t16 - 16 * per_row, 0.0)
     R = int(min(L, max(16, (seconds - fixed) / per_row)))
     rows = np.linspace(0, L - 1, R).astype(np.int64)
