@@ -164,7 +164,7 @@ __device__ __forceinline__ ProbBlock prob_block(float logit_max, float c, float 
 }
 
 // Eight values rounded to E2M1 codes in one register (byte i holds pair i; ties to the even
-// code, saturating at 6), by the gfx950 packed FP4 conversion with a unit scale.
+// code, saturating at +-6, sign kept), by the gfx950 packed FP4 conversion with a unit scale.
 __device__ __forceinline__ uint32_t e2m1_codes8(const float *r) {
   uint32_t code = 0u;
   code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[0], r[1], 1.0f, 0);
