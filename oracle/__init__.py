@@ -83,6 +83,9 @@ def _load():
             lib.oracle_vsa_fwd.argtypes = [P, P, P, i32, i32, i64, i32, i32, f64, f64, u32, P, i64, P, P, P,
                                            P, P, P, P]
             lib.oracle_vsa_fwd.restype = i32
+            lib.oracle_vsa_bwd.argtypes = [P, P, P, P, i32, i32, i64, i32, i32, f64, f64, u32, P, i64, P, i64,
+                                           P, P, P, P]
+            lib.oracle_vsa_bwd.restype = i32
             _lib = lib
     return _lib
 
@@ -235,6 +238,30 @@ def vsa_fwd(q, k, v, scale, cube_tokens=128, sparsity=0.9, flags=QUANT_ALL, rows
         raise ValueError("oracle_vsa_fwd rejected the arguments")
     return {"qpool": qp, "kpool": kp, "vpool": vp, "score": score, "sel": sel, "o_fine": of,
             "o_coarse": oc, "topk": topk, "rows": rows}
+
+
+def vsa_bwd(q, k, v, do, scale, cube_tokens=128, sparsity=0.9, flags=QUANT_ALL, qrows=None, krows=None):
+    """Straight-through backward of the cube-sparse fine stage: dQ at query
+    rows ``qrows``, dK/dV at key rows ``krows`` (fp64 [B, H, R, D]), and the
+    selection it used (int32 [B, H, n, topk], ascending)."""
+    q, k, v, do = _u16(q), _u16(k), _u16(v), _u16(do)
+    B, H, L, D = q.shape
+    n = L // cube_tokens
+    topk = vsa_topk(sparsity, n)
+    qrows = (np.arange(L, dtype=np.int64) if qrows is None
+             else np.ascontiguousarray(qrows, dtype=np.int64))
+    krows = (np.arange(L, dtype=np.int64) if krows is None
+             else np.ascontiguousarray(krows, dtype=np.int64))
+    dq = np.empty((B, H, qrows.size, D))
+    dk = np.empty((B, H, krows.size, D))
+    dv = np.empty((B, H, krows.size, D))
+    sel = np.empty((B, H, n, topk), np.int32)
+    rc = _load().oracle_vsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), B, H, L, D, cube_tokens, float(sparsity),
+                                float(scale), int(flags), _ptr(qrows), qrows.size, _ptr(krows), krows.size,
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(sel))
+    if rc < 0:
+        raise ValueError("oracle_vsa_bwd rejected the arguments")
+    return {"dq": dq, "dk": dk, "dv": dv, "sel": sel, "topk": topk, "qrows": qrows, "krows": krows}
 
 
 # ----------------------------------------------------------------------------

@@ -435,14 +435,14 @@ static void key_block(const bwd_head *x, int64_t j, int64_t *b0, int *nb)
     *nb = (int)(e - s);
 }
 
-/* For row i with forward statistics (lse, cmax[C]) and key block [b0, b0+nb):
+/* For row i with forward statistics (lse, and m_c the running max after the
+   chunk that holds the block) and key block [b0, b0+nb):
    A[t] = exp(S - lse), Ahat[t] = fq(exp(S - m_c))[t] * exp(m_c - lse),
    for the block's keys (masked keys give 0). */
-static void block_weights(const bwd_head *x, int64_t i, int64_t b0, int nb, double lse, const double *cmax,
-                          double *A, double *Ahat)
+static void block_weights_mc(const bwd_head *x, int64_t i, int64_t b0, int nb, double lse, double mc,
+                             double *A, double *Ahat)
 {
     float P[16];
-    double mc = cmax[b0 / x->chunk];
     float S[16];
     for (int t = 0; t < nb; ++t) {
         int live = !(x->causal && b0 + t > i);
@@ -455,6 +455,13 @@ static void block_weights(const bwd_head *x, int64_t i, int64_t b0, int nb, doub
         A[t] = live ? exp((double)S[t] - lse) : 0.0;
         Ahat[t] = (double)P[t] * exp(mc - lse);
     }
+}
+
+/* Dense schedule: the block's chunk is the one its keys fall in. */
+static void block_weights(const bwd_head *x, int64_t i, int64_t b0, int nb, double lse, const double *cmax,
+                          double *A, double *Ahat)
+{
+    block_weights_mc(x, i, b0, nb, lse, cmax[b0 / x->chunk], A, Ahat);
 }
 
 static double dot_do_v(const bwd_head *x, int64_t i, int64_t j)
@@ -587,6 +594,45 @@ static void pool_cubes(const uint16_t *x, int64_t ncubes, int ct, int D, uint16_
         }
 }
 
+/* The selection of one head: cube means of Q and K (fp64, rounded to bf16),
+   coarse logits scale * <Qc, Kc>, and for every query cube the topk highest
+   scoring key cubes (ties to the lower cube index) listed in ascending order.
+   qp, kp: [n, D] bf16; sc: [n, n]; sl: [n, topk]. */
+static void vsa_select_head(const uint16_t *qh, const uint16_t *kh, int64_t n, int ct, int D, double scale,
+                            int topk, uint16_t *qp, uint16_t *kp, double *sc, int32_t *sl)
+{
+    pool_cubes(qh, n, ct, D, qp);
+    pool_cubes(kh, n, ct, D, kp);
+    for (int64_t a = 0; a < n; ++a)
+        for (int64_t b = 0; b < n; ++b) {
+            double s = 0.0;
+            for (int d = 0; d < D; ++d) s += (double)bf16_to_f32(qp[a * D + d]) * (double)bf16_to_f32(kp[b * D + d]);
+            sc[a * n + b] = scale * s;
+        }
+    for (int64_t a = 0; a < n; ++a) {
+        char *taken = (char *)calloc(n, 1);
+        for (int t = 0; t < topk; ++t) {
+            int64_t best = -1;
+            for (int64_t b = 0; b < n; ++b)
+                if (!taken[b] && (best < 0 || sc[a * n + b] > sc[a * n + best])) best = b;
+            taken[best] = 1;
+        }
+        int t = 0;
+        for (int64_t b = 0; b < n; ++b)
+            if (taken[b]) sl[a * topk + t++] = (int32_t)b;
+        free(taken);
+    }
+}
+
+/* Key list of a query cube: its selected cubes' tokens, one chunk per cube. */
+static int64_t *vsa_keys(const int32_t *sl_row, int topk, int ct)
+{
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * topk * ct);
+    for (int t = 0; t < topk; ++t)
+        for (int u = 0; u < ct; ++u) keys[t * ct + u] = (int64_t)sl_row[t] * ct + u;
+    return keys;
+}
+
 /* Outputs per (b,h):
      qpool, kpool, vpool : [B*H, n, D] bf16 (may be NULL)
      score   : [B*H, n, n] fp64 coarse logits scale * <Qc, Kc> (may be NULL)
@@ -610,30 +656,8 @@ int oracle_vsa_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int 
     int32_t *sl = (int32_t *)malloc(sizeof(int32_t) * n * topk);
     for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
         const uint16_t *qh = q + bh * L * D, *kh = k + bh * L * D, *vh = v + bh * L * D;
-        pool_cubes(qh, n, cube_tokens, D, qp);
-        pool_cubes(kh, n, cube_tokens, D, kp);
+        vsa_select_head(qh, kh, n, cube_tokens, D, scale, topk, qp, kp, sc, sl);
         pool_cubes(vh, n, cube_tokens, D, vp);
-        for (int64_t a = 0; a < n; ++a)
-            for (int64_t b = 0; b < n; ++b) {
-                double s = 0.0;
-                for (int d = 0; d < D; ++d) s += (double)bf16_to_f32(qp[a * D + d]) * (double)bf16_to_f32(kp[b * D + d]);
-                sc[a * n + b] = scale * s;
-            }
-        /* Top-k by coarse score, ties to the lower cube index; then the
-           selected cubes are listed in ascending order. */
-        for (int64_t a = 0; a < n; ++a) {
-            char *taken = (char *)calloc(n, 1);
-            for (int t = 0; t < topk; ++t) {
-                int64_t best = -1;
-                for (int64_t b = 0; b < n; ++b)
-                    if (!taken[b] && (best < 0 || sc[a * n + b] > sc[a * n + best])) best = b;
-                taken[best] = 1;
-            }
-            int t = 0;
-            for (int64_t b = 0; b < n; ++b)
-                if (taken[b]) sl[a * topk + t++] = (int32_t)b;
-            free(taken);
-        }
         if (qpool) memcpy(qpool + bh * n * D, qp, 2 * n * D);
         if (kpool) memcpy(kpool + bh * n * D, kp, 2 * n * D);
         if (vpool) memcpy(vpool + bh * n * D, vp, 2 * n * D);
@@ -646,10 +670,7 @@ int oracle_vsa_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int 
         for (int64_t r = 0; r < nrows; ++r) {
             int64_t i = rows[r];
             int64_t a = i / cube_tokens;
-            int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * topk * cube_tokens);
-            for (int t = 0; t < topk; ++t)
-                for (int u = 0; u < cube_tokens; ++u)
-                    keys[t * cube_tokens + u] = (int64_t)sl[a * topk + t] * cube_tokens + u;
+            int64_t *keys = vsa_keys(sl + a * topk, topk, cube_tokens);
             if (o_fine)
                 row_forward(&hd, i, keys, topk, cube_tokens, D, scale, flags, o_fine + (bh * nrows + r) * D,
                             NULL, NULL, NULL);
@@ -673,6 +694,122 @@ int oracle_vsa_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int 
     free(qp);
     free(kp);
     free(vp);
+    free(sc);
+    free(sl);
+    return topk;
+}
+
+/* Straight-through backward of the fine stage (the same formulas as
+   oracle_attn_bwd) with each query cube attending to its selected cubes only,
+   visited in ascending order with one chunk per cube.  The running max of row
+   i after its t-th selected cube is the chunk max of every key block of that
+   cube.  Computes dQ for query rows qrows and dK, dV for key rows krows, per
+   (b,h); outputs fp64 [B*H, nq, D] and [B*H, nk, D]; sel [B*H, n, topk] (may
+   be NULL).  Returns topk, or -1 when L is not a whole number of cubes. */
+int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout, int B, int H,
+                   int64_t L, int D, int cube_tokens, double sparsity, double scale, unsigned flags,
+                   const int64_t *qrows, int64_t nq, const int64_t *krows, int64_t nk, double *dq, double *dk,
+                   double *dv, int32_t *sel)
+{
+    init_tables();
+    if (L % cube_tokens) return -1;
+    const int64_t n = L / cube_tokens;
+    const int ct = cube_tokens;
+    const int topk = oracle_vsa_topk(sparsity, (int)n);
+    uint16_t *qp = (uint16_t *)malloc(2 * n * D), *kp = (uint16_t *)malloc(2 * n * D);
+    double *sc = (double *)malloc(sizeof(double) * n * n);
+    int32_t *sl = (int32_t *)malloc(sizeof(int32_t) * n * topk);
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const uint16_t *qh = q + bh * L * D, *kh = k + bh * L * D, *vh = v + bh * L * D;
+        vsa_select_head(qh, kh, n, ct, D, scale, topk, qp, kp, sc, sl);
+        if (sel) memcpy(sel + bh * n * topk, sl, sizeof(int32_t) * n * topk);
+        head_ops hd;
+        make_head_ops(&hd, qh, kh, vh, L, L, D, flags);
+        bwd_head x = {&hd, dout + bh * L * D, L, n, D, ct, 0, flags, scale};
+
+        /* Row statistics (lse, running max after each selected cube, D_i). */
+        double *lse = (double *)malloc(sizeof(double) * L);
+        double *cmax = (double *)malloc(sizeof(double) * L * topk);
+        double *Dv = (double *)malloc(sizeof(double) * L);
+        char *need = (char *)calloc(L, 1);
+        for (int64_t a = 0; a < nq; ++a) need[qrows[a]] = 1;
+        if (nk > 0 && (dk || dv))
+            for (int64_t i = 0; i < L; ++i) need[i] = 1;
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t i = 0; i < L; ++i) {
+            if (!need[i]) continue;
+            int64_t *keys = vsa_keys(sl + (i / ct) * topk, topk, ct);
+            double *ohp = (double *)malloc(sizeof(double) * D);
+            row_forward(&hd, i, keys, topk, ct, D, scale, flags, NULL, ohp, lse + i, cmax + i * topk);
+            double s = 0.0;
+            for (int d = 0; d < D; ++d) s += (double)bf16_to_f32(x.dO[i * D + d]) * ohp[d];
+            Dv[i] = s;
+            free(ohp);
+            free(keys);
+        }
+
+        if (dq && nq > 0) {
+#pragma omp parallel for schedule(dynamic, 1)
+            for (int64_t a = 0; a < nq; ++a) {
+                int64_t i = qrows[a];
+                const int32_t *row_sel = sl + (i / ct) * topk;
+                double *out = dq + (bh * nq + a) * D;
+                double A[16], Ah[16];
+                for (int d = 0; d < D; ++d) out[d] = 0.0;
+                for (int t = 0; t < topk; ++t)
+                    for (int64_t b0 = (int64_t)row_sel[t] * ct; b0 < (int64_t)(row_sel[t] + 1) * ct; b0 += 16) {
+                        int64_t s;
+                        int nb;
+                        key_block(&x, b0, &s, &nb);
+                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + t], A, Ah);
+                        for (int u = 0; u < nb; ++u) {
+                            int64_t j = s + u;
+                            double dS = A[u] * (dot_do_v(&x, i, j) - Dv[i]);
+                            for (int d = 0; d < D; ++d) out[d] += scale * dS * (double)hd.kh[j * D + d];
+                        }
+                    }
+            }
+        }
+
+        if (nk > 0 && (dk || dv)) {
+#pragma omp parallel for schedule(dynamic, 1)
+            for (int64_t a = 0; a < nk; ++a) {
+                int64_t j = krows[a];
+                int64_t s;
+                int nb;
+                key_block(&x, j, &s, &nb);
+                double *ok = dk ? dk + (bh * nk + a) * D : NULL;
+                double *ov = dv ? dv + (bh * nk + a) * D : NULL;
+                for (int d = 0; d < D; ++d) {
+                    if (ok) ok[d] = 0.0;
+                    if (ov) ov[d] = 0.0;
+                }
+                double A[16], Ah[16];
+                const int64_t b = j / ct;
+                for (int64_t qc = 0; qc < n; ++qc) {
+                    int t = -1;
+                    for (int u = 0; u < topk; ++u)
+                        if (sl[qc * topk + u] == b) t = u;
+                    if (t < 0) continue;  /* this query cube did not select j's cube */
+                    for (int64_t i = qc * ct; i < (qc + 1) * ct; ++i) {
+                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + t], A, Ah);
+                        double dS = A[j - s] * (dot_do_v(&x, i, j) - Dv[i]);
+                        for (int d = 0; d < D; ++d) {
+                            if (ok) ok[d] += scale * dS * (double)hd.qh[i * D + d];
+                            if (ov) ov[d] += Ah[j - s] * (double)bf16_to_f32(x.dO[i * D + d]);
+                        }
+                    }
+                }
+            }
+        }
+        free(lse);
+        free(cmax);
+        free(Dv);
+        free(need);
+        free_head_ops(&hd);
+    }
+    free(qp);
+    free(kp);
     free(sc);
     free(sl);
     return topk;

@@ -14,7 +14,10 @@ Each check ties the oracle to something other than itself:
   * O is linear in V, and <dO, O> = sum_j <dV_j, V-hat_j> ties dV to the forward;
   * cube-sparse attention at sparsity 0 equals dense attention with 128-key
     chunks; the top-k count follows its printed formula; the selection equals
-    torch.topk on the coarse scores; the coarse output equals torch softmax.
+    torch.topk on the coarse scores; the coarse output equals torch softmax;
+  * the cube-sparse backward equals the dense backward at sparsity 0, PyTorch
+    float64 autograd of block-masked attention without quantization (and for
+    dQ/dK on the fake-quantized operands), and pairs dV with the fine output.
 """
 import math
 
@@ -247,3 +250,71 @@ def test_vsa_selection_pool_and_coarse_against_torch():
             # V-hat blocks of 16 keys stay inside a cube, so gathering cubes
             # before quantizing V changes nothing
             assert np.array_equal(r["o_fine"][0, bh, t], sub["o"][0, 0, 0])
+
+
+# ---- cube-sparse backward ----------------------------------------------------
+
+def block_mask(sel, L, cube):
+    """Boolean [B, H, L, L] mask: query i may see key j when j's cube is among
+    the cubes selected for i's cube."""
+    B, H, n, _ = sel.shape
+    m = torch.zeros(B, H, n, n, dtype=torch.bool)
+    for b in range(B):
+        for h in range(H):
+            for a in range(n):
+                m[b, h, a, torch.as_tensor(sel[b, h, a], dtype=torch.long)] = True
+    return m.repeat_interleave(cube, 2).repeat_interleave(cube, 3)
+
+
+def test_vsa_bwd_sparsity_zero_is_dense_bwd():
+    L, cube = 512, 128
+    q, k, v, do = (rand_bits((1, 2, L, D), s) for s in (50, 51, 52, 53))
+    sp = oracle.vsa_bwd(q, k, v, do, SCALE, cube_tokens=cube, sparsity=0.0)
+    de = oracle.attn_bwd(q, k, v, do, SCALE)
+    assert sp["topk"] == 4
+    for name in ("dq", "dk", "dv"):
+        assert np.array_equal(sp[name], de[name]), name
+
+
+def test_vsa_bwd_without_quantization_is_masked_autograd():
+    L, cube = 1024, 128
+    q, k, v, do = (rand_bits((1, 2, L, D), s) for s in (54, 55, 56, 57))
+    r = oracle.vsa_bwd(q, k, v, do, SCALE, cube_tokens=cube, sparsity=0.6, flags=0)
+    assert r["topk"] == 4
+    # the selection is the forward's
+    assert np.array_equal(r["sel"], oracle.vsa_fwd(q, k, v, SCALE, cube_tokens=cube, sparsity=0.6,
+                                                   rows=np.array([0]))["sel"])
+    mask = block_mask(r["sel"], L, cube)
+    Q, K, V = (f64(t).requires_grad_() for t in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=SCALE)
+    out.backward(f64(do))
+    for name, t in (("dq", Q), ("dk", K), ("dv", V)):
+        assert np.allclose(r[name], t.grad.numpy(), rtol=0, atol=5e-6), name
+
+
+def test_vsa_bwd_ste_dq_dk_equal_masked_autograd_on_quantized_operands():
+    L, cube = 1024, 128
+    q, k, v, do = (rand_bits((1, 1, L, D), s) for s in (58, 59, 60, 61))
+    r = oracle.vsa_bwd(q, k, v, do, SCALE, cube_tokens=cube, sparsity=0.6)
+    mask = block_mask(r["sel"], L, cube)
+    Q = f64(fq_bits(q, -1)).requires_grad_()
+    K = f64(fq_bits(k, -1)).requires_grad_()
+    V = f64(fq_bits(v, 2))
+    torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=SCALE).backward(f64(do))
+    assert np.allclose(r["dq"], Q.grad.numpy(), rtol=0, atol=5e-6)
+    assert np.allclose(r["dk"], K.grad.numpy(), rtol=0, atol=5e-6)
+
+
+def test_vsa_bwd_dv_pairs_with_the_fine_output_and_rows_sample():
+    L, cube = 1024, 128
+    q, k, v, do = (rand_bits((1, 2, L, D), s) for s in (62, 63, 64, 65))
+    f = oracle.vsa_fwd(q, k, v, SCALE, cube_tokens=cube, sparsity=0.6)
+    b = oracle.vsa_bwd(q, k, v, do, SCALE, cube_tokens=cube, sparsity=0.6)
+    vh = oracle.bf16_bits_to_f32(fq_bits(v, 2)).astype(np.float64)
+    lhs = np.einsum("bhid,bhid->bh", oracle.bf16_bits_to_f32(do).astype(np.float64), f["o_fine"])
+    rhs = np.einsum("bhjd,bhjd->bh", b["dv"], vh)
+    assert np.allclose(lhs, rhs, rtol=1e-10)
+    qr, kr = np.array([0, 300, 1023]), np.array([5, 127, 128, 640])
+    part = oracle.vsa_bwd(q, k, v, do, SCALE, cube_tokens=cube, sparsity=0.6, qrows=qr, krows=kr)
+    for name, rows in (("dq", qr), ("dk", kr), ("dv", kr)):
+        assert np.array_equal(part[name], b[name][:, :, rows]), name
