@@ -161,21 +161,51 @@ int attn_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp,
  * o_fine [B, H, L, 128] bf16 (strides so); o_coarse (NULL allowed) receives
  * softmax(coarse logits) @ Vc broadcast to every token of the query cube, bf16, strides so;
  * sel (NULL allowed) receives the [B, H, n, topk] int32 selection.
+ * Optional training outputs of the fine stage (all three or none; vsa_qat_bwd needs them and
+ * sel): lse_log2 [B, H, L], chunk_max_log2 [B, H, topk, L] (the running maximum after each
+ * selected cube, in list order) and o_hp [B, H, L, 128], fp32 contiguous, defined as for
+ * attn_qat_fwd.
  * workspace: at least attn_qat_workspace_size(2, ...) bytes with lk = L.
  * Errors: AQ_EINVAL (as the forward, plus grid sizes not divisible by the cube, L !=
- * grid_t*grid_h*grid_w, sparsity outside [0,1]); AQ_ENOTSUP (cube of other than 128 tokens).
+ * grid_t*grid_h*grid_w, sparsity outside [0,1], only some of the training outputs);
+ * AQ_ENOTSUP (cube of other than 128 tokens).
  * ------------------------------------------------------------------------------------------- */
 int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void *o_coarse,
                 int32_t *sel, int batch, int num_heads, int head_size, int64_t seq_len,
                 int grid_t, int grid_h, int grid_w, int cube_t, int cube_h, int cube_w,
                 double sparsity, aq_strides sq, aq_strides sk, aq_strides sv, aq_strides so,
+                float softmax_scale, unsigned quant_flags, float *lse_log2, float *chunk_max_log2,
+                float *o_hp, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * vsa_qat_bwd - straight-through backward of the cube-sparse fine stage ([META] attention kind
+ * "vsa" with quantize_fine, backward "consistent STE with auxiliary output"; needed to train the
+ * sparse model).
+ *
+ * The dense backward's formulas (attn_qat_bwd) with every query cube attending only to its
+ * selected cubes: dQ of a query sums over its cube's selected keys; dK and dV of a key sum over
+ * the queries of every cube that selected the key's cube, with the chunk maximum of the
+ * selection slot that cube used.  The coarse stage (o_coarse) is not differentiated here.
+ * Inputs q, k, v, d_o (bf16 [B, L, H, 128] by strides), sel, lse_log2, chunk_max_log2 and o_hp
+ * exactly as written by vsa_qat_fwd with the same arguments (sel: ascending, distinct);
+ * outputs dq, dk, dv bf16 with their own strides.
+ * workspace: at least attn_qat_workspace_size(3, ...) bytes with lq = lk = L.
+ * Errors: as vsa_qat_fwd, plus AQ_EINVAL for a null gradient, statistics or sel pointer and
+ * AQ_ENOTSUP for more than 4096 cubes.
+ * ------------------------------------------------------------------------------------------- */
+int vsa_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp, const void *d_o,
+                const float *lse_log2, const float *chunk_max_log2, const int32_t *sel, void *dq, void *dk,
+                void *dv, int batch, int num_heads, int head_size, int64_t seq_len, int grid_t, int grid_h,
+                int grid_w, int cube_t, int cube_h, int cube_w, double sparsity, aq_strides sq, aq_strides sk,
+                aq_strides sv, aq_strides sdo, aq_strides sdq, aq_strides sdk, aq_strides sdv,
                 float softmax_scale, unsigned quant_flags, void *workspace, size_t workspace_bytes,
                 void *stream);
 
 /* Number of cubes kept per query cube: max(1, min(ceil((1 - sparsity) * n), n)). */
 int vsa_topk(double sparsity, int n_cubes);
 
-/* Workspace bytes needed by op 0 = attn_qat_fwd, 1 = attn_qat_bwd, 2 = vsa_qat_fwd (lk = L). */
+/* Workspace bytes needed by op 0 = attn_qat_fwd, 1 = attn_qat_bwd, 2 = vsa_qat_fwd and
+ * 3 = vsa_qat_bwd (lq = lk = L); 0 for invalid arguments. */
 size_t attn_qat_workspace_size(int op, int batch, int num_heads, int64_t lq, int64_t lk);
 
 /* ---------------------------------------------------------------------------------------------

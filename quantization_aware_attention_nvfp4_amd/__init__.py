@@ -11,8 +11,8 @@ _load()
 
 from .ops import (AQ_QUANT_ALL, AQ_QUANT_K, AQ_QUANT_P, AQ_QUANT_Q, AQ_QUANT_V,  # noqa: E402
                   AttnQatTrainImpl, attn_qat_bwd, attn_qat_fwd, attn_qat_train, fq_nvfp4,
-                  static_global_scale, vsa_qat_fwd, vsa_topk)
+                  static_global_scale, vsa_qat_bwd, vsa_qat_fwd, vsa_qat_train, vsa_topk)
 
 __all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "fq_nvfp4",
            "static_global_scale", "attn_qat_fwd", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
-           "vsa_qat_fwd", "vsa_topk"]
+           "vsa_qat_fwd", "vsa_qat_bwd", "vsa_qat_train", "vsa_topk"]

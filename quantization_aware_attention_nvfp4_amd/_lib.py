@@ -18,7 +18,8 @@ AQ_QUANT_Q, AQ_QUANT_K, AQ_QUANT_V, AQ_QUANT_P = 1, 2, 4, 8
 AQ_QUANT_ALL = 15
 
 EXPORTED = ("aq_last_error", "fq_nvfp4", "fq_nvfp4_static_scale", "attn_qat_fwd", "attn_qat_bwd",
-            "vsa_qat_fwd", "vsa_topk", "attn_qat_workspace_size", "aq_kernel_timing", "aq_kernel_times")
+            "vsa_qat_fwd", "vsa_qat_bwd", "vsa_topk", "attn_qat_workspace_size", "aq_kernel_timing",
+            "aq_kernel_times")
 
 
 class aq_strides(ctypes.Structure):
@@ -46,8 +47,11 @@ def _declare(lib):
                                  S, S, S, S, f32, i32, u32, P, sz, P]
     lib.attn_qat_bwd.restype = i32
     lib.vsa_qat_fwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i64, i32, i32, i32, i32, i32, i32,
-                                f64, S, S, S, S, f32, u32, P, sz, P]
+                                f64, S, S, S, S, f32, u32, P, P, P, P, sz, P]
     lib.vsa_qat_fwd.restype = i32
+    lib.vsa_qat_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, i32, i32, i64, i32, i32, i32, i32, i32,
+                                i32, f64, S, S, S, S, S, S, S, f32, u32, P, sz, P]
+    lib.vsa_qat_bwd.restype = i32
     lib.vsa_topk.argtypes = [f64, i32]
     lib.vsa_topk.restype = i32
     lib.attn_qat_workspace_size.argtypes = [i32, i32, i32, i64, i64]
@@ -73,6 +77,10 @@ def load():
     except OSError as e:  # pragma: no cover - depends on the machine
         _load_error = e
         raise ImportError(f"libattnqat.so could not be loaded: {e}") from e
+    except AttributeError as e:  # a library built from older sources lacks a symbol
+        _load_error = e
+        raise ImportError(f"libattnqat.so is out of date ({e}); rebuild it with "
+                          "quantization_aware_attention_nvfp4_amd/build.py") from e
     _lib = lib
     return lib
 

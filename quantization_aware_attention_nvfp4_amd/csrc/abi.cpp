@@ -103,7 +103,7 @@ int vsa_topk(double sparsity, int n_cubes) {
 }
 
 size_t attn_qat_workspace_size(int op, int batch, int num_heads, int64_t lq, int64_t lk) {
-  if (batch <= 0 || num_heads <= 0 || lq <= 0 || lk <= 0 || op < 0 || op > 2) return 0;
+  if (batch <= 0 || num_heads <= 0 || lq <= 0 || lk <= 0 || op < 0 || op > 3) return 0;
   return aq::workspace_bytes(op, batch, num_heads, lq, lk);
 }
 
@@ -176,28 +176,40 @@ int attn_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp,
   return hip_status(aq::launch_attn_bwd(a, b, (hipStream_t)stream), "attn_qat_bwd launch");
 }
 
-int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void *o_coarse,
-                int32_t *sel, int batch, int num_heads, int head_size, int64_t seq_len,
-                int grid_t, int grid_h, int grid_w, int cube_t, int cube_h, int cube_w,
-                double sparsity, aq_strides sq, aq_strides sk, aq_strides sv, aq_strides so,
-                float softmax_scale, unsigned quant_flags, void *workspace, size_t workspace_bytes,
-                void *stream) {
-  if (!q || !k || !v || !o_fine) return fail(AQ_EINVAL, "vsa_qat_fwd: null tensor pointer");
+// Shape checks shared by the cube-sparse entry points.
+static int check_vsa(const char *fn, int batch, int num_heads, int head_size, int64_t seq_len, int grid_t,
+              int grid_h, int grid_w, int cube_t, int cube_h, int cube_w, double sparsity, float softmax_scale,
+              unsigned quant_flags) {
   int rc = check_attention(batch, num_heads, num_heads, head_size, seq_len, seq_len, softmax_scale,
                            0, quant_flags);
   if (rc) return rc;
   if (grid_t <= 0 || grid_h <= 0 || grid_w <= 0 || cube_t <= 0 || cube_h <= 0 || cube_w <= 0)
-    return fail(AQ_EINVAL, "vsa_qat_fwd: grid and cube sizes must be positive");
+    return fail(AQ_EINVAL, "%s: grid and cube sizes must be positive", fn);
   if (grid_t % cube_t || grid_h % cube_h || grid_w % cube_w)
-    return fail(AQ_EINVAL, "vsa_qat_fwd: grid %dx%dx%d is not divisible by cube %dx%dx%d", grid_t,
-                grid_h, grid_w, cube_t, cube_h, cube_w);
+    return fail(AQ_EINVAL, "%s: grid %dx%dx%d is not divisible by cube %dx%dx%d", fn, grid_t, grid_h, grid_w,
+                cube_t, cube_h, cube_w);
   if ((int64_t)grid_t * grid_h * grid_w != seq_len)
-    return fail(AQ_EINVAL, "vsa_qat_fwd: seq_len %lld != grid_t*grid_h*grid_w", (long long)seq_len);
+    return fail(AQ_EINVAL, "%s: seq_len %lld != grid_t*grid_h*grid_w", fn, (long long)seq_len);
   if (!(sparsity >= 0.0 && sparsity <= 1.0))
-    return fail(AQ_EINVAL, "vsa_qat_fwd: sparsity must lie in [0, 1] (got %g)", sparsity);
+    return fail(AQ_EINVAL, "%s: sparsity must lie in [0, 1] (got %g)", fn, sparsity);
   if (cube_t * cube_h * cube_w != aq::kChunkHost)
-    return fail(AQ_ENOTSUP, "vsa_qat_fwd: cubes of %d tokens are not supported (only 128)",
-                cube_t * cube_h * cube_w);
+    return fail(AQ_ENOTSUP, "%s: cubes of %d tokens are not supported (only 128)", fn, cube_t * cube_h * cube_w);
+  return AQ_OK;
+}
+
+int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void *o_coarse,
+                int32_t *sel, int batch, int num_heads, int head_size, int64_t seq_len,
+                int grid_t, int grid_h, int grid_w, int cube_t, int cube_h, int cube_w,
+                double sparsity, aq_strides sq, aq_strides sk, aq_strides sv, aq_strides so,
+                float softmax_scale, unsigned quant_flags, float *lse_log2, float *chunk_max_log2,
+                float *o_hp, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o_fine) return fail(AQ_EINVAL, "vsa_qat_fwd: null tensor pointer");
+  int rc = check_vsa("vsa_qat_fwd", batch, num_heads, head_size, seq_len, grid_t, grid_h, grid_w, cube_t, cube_h,
+                     cube_w, sparsity, softmax_scale, quant_flags);
+  if (rc) return rc;
+  if ((lse_log2 || chunk_max_log2 || o_hp) && !(lse_log2 && chunk_max_log2 && o_hp))
+    return fail(AQ_EINVAL, "vsa_qat_fwd: the training outputs lse_log2, chunk_max_log2 and o_hp come together "
+                           "(all three or none)");
   if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so))
     return fail(AQ_EINVAL, "vsa_qat_fwd: strides must be positive with d contiguous");
   if (!tensor_ok(q, sq) || !tensor_ok(k, sk) || !tensor_ok(v, sv) || !tensor_ok(o_fine, so) ||
@@ -213,6 +225,7 @@ int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void 
   a.batch = batch; a.heads = num_heads; a.lq = seq_len; a.lk = seq_len;
   a.sq = cvt(sq); a.sk = cvt(sk); a.sv = cvt(sv); a.so = cvt(so);
   a.scale = softmax_scale; a.causal = false; a.flags = quant_flags;
+  a.lse = lse_log2; a.cmax = chunk_max_log2; a.o_hp = o_hp;
   a.workspace = workspace;
   aq::VsaArgs s{};
   s.o_coarse = o_coarse; s.sel = sel;
@@ -221,6 +234,47 @@ int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void 
   if (s.topk > 1024)
     return fail(AQ_ENOTSUP, "vsa_qat_fwd: at most 1024 selected cubes per query cube (got %d)", s.topk);
   return hip_status(aq::launch_vsa_fwd(a, s, (hipStream_t)stream), "vsa_qat_fwd launch");
+}
+
+int vsa_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp, const void *d_o,
+                const float *lse_log2, const float *chunk_max_log2, const int32_t *sel, void *dq, void *dk,
+                void *dv, int batch, int num_heads, int head_size, int64_t seq_len, int grid_t, int grid_h,
+                int grid_w, int cube_t, int cube_h, int cube_w, double sparsity, aq_strides sq, aq_strides sk,
+                aq_strides sv, aq_strides sdo, aq_strides sdq, aq_strides sdk, aq_strides sdv,
+                float softmax_scale, unsigned quant_flags, void *workspace, size_t workspace_bytes,
+                void *stream) {
+  if (!q || !k || !v || !d_o || !dq || !dk || !dv) return fail(AQ_EINVAL, "vsa_qat_bwd: null tensor pointer");
+  if (!o_hp || !lse_log2 || !chunk_max_log2 || !sel)
+    return fail(AQ_EINVAL, "vsa_qat_bwd: o_hp, lse_log2, chunk_max_log2 and sel are required");
+  int rc = check_vsa("vsa_qat_bwd", batch, num_heads, head_size, seq_len, grid_t, grid_h, grid_w, cube_t, cube_h,
+                     cube_w, sparsity, softmax_scale, quant_flags);
+  if (rc) return rc;
+  if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(sdo) || !strides_ok(sdq) ||
+      !strides_ok(sdk) || !strides_ok(sdv))
+    return fail(AQ_EINVAL, "vsa_qat_bwd: strides must be positive with d contiguous");
+  if (!tensor_ok(q, sq) || !tensor_ok(k, sk) || !tensor_ok(v, sv) || !tensor_ok(d_o, sdo) || !tensor_ok(dq, sdq) ||
+      !tensor_ok(dk, sdk) || !tensor_ok(dv, sdv))
+    return fail(AQ_EINVAL, "vsa_qat_bwd: tensors must be 16-byte aligned with strides that are multiples of 8 "
+                           "elements and below 2^24");
+  const int n = (int)(seq_len / aq::kChunkHost);
+  if (n > aq::kMaxCubesHost)
+    return fail(AQ_ENOTSUP, "vsa_qat_bwd: at most %d cubes (got %d)", aq::kMaxCubesHost, n);
+  const size_t need = aq::workspace_bytes(3, batch, num_heads, seq_len, seq_len);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
+    return fail(AQ_EINVAL, "vsa_qat_bwd: workspace must be 256-byte aligned and hold %zu bytes", need);
+  aq::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.batch = batch; a.heads = num_heads; a.lq = seq_len; a.lk = seq_len;
+  a.sq = cvt(sq); a.sk = cvt(sk); a.sv = cvt(sv);
+  a.scale = softmax_scale; a.causal = false; a.flags = quant_flags;
+  a.lse = const_cast<float *>(lse_log2); a.cmax = const_cast<float *>(chunk_max_log2);
+  a.o_hp = const_cast<float *>(o_hp);
+  a.workspace = workspace;
+  aq::BwdArgs b{};
+  b.d_o = d_o; b.dq = dq; b.dk = dk; b.dv = dv;
+  b.sdo = cvt(sdo); b.sdq = cvt(sdq); b.sdk = cvt(sdk); b.sdv = cvt(sdv);
+  return hip_status(aq::launch_vsa_bwd(a, b, sel, n, vsa_topk(sparsity, n), (hipStream_t)stream),
+                    "vsa_qat_bwd launch");
 }
 
 }  // extern "C"

@@ -64,6 +64,12 @@ struct BwdParams {
   int64_t nwork, per_xcd;
   float c, scale;
   bool causal, quant_p;
+  // Cube-sparse fine stage (null for dense): sel [BH, n, nsel] selected key cubes of every query
+  // cube, ascending; slot_t [BH, n key cubes, n query cubes] position of the key cube in that
+  // query cube's list, or -1.  Chunk maxima are then [BH, nsel, lq], one per selected cube.
+  const int32_t *sel;
+  const int16_t *slot_t;
+  int64_t nsel;
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -99,11 +105,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int qrow = (int)(qc * kChunk) + qg * 32 + n;
   const bool qvalid = qrow < p.lq;
 
-  int64_t n_iter = p.Ck;
+  int64_t n_iter = p.sel ? p.nsel : p.Ck;
   if (p.causal) {
     const int64_t q_last = qc * kChunk + kChunk - 1;
     n_iter = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
   }
+  // Key chunk of iteration `it`: the it-th selected cube, or chunk `it` (a uniform scalar).
+  const int32_t *sel_row = p.sel ? p.sel + (bh * p.Cq + qc) * p.nsel : nullptr;
+  auto chunk_at = [&](int64_t it) -> int64_t { return sel_row ? (int64_t)sel_row[it] : it; };
   // Chunk copies: per lane 4 K-hat and 4 V-hat pieces of 16 bytes.
   uint32_t c_voff[4];
 #pragma unroll
@@ -120,7 +129,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
       load_lds16_s(vs, c_voff[i], lds + buf * 65536 + 32768 + (i * 8 + wave) * 1024);
     }
   };
-  stage_chunk(0, 0);
+  stage_chunk(chunk_at(0), 0);
 
   bf16x8 qf[8], of[8];
   {
@@ -161,11 +170,12 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-  for (int64_t ch = 0; ch < n_iter; ++ch) {
-    const int buf = (int)(ch & 1);
+  for (int64_t it = 0; it < n_iter; ++it) {
+    const int buf = (int)(it & 1);
+    const int64_t ch = chunk_at(it);
     AQ_WAIT_VMCNT(0);  // this wave's copies of chunk ch
     __syncthreads();   // everyone's copies landed; the other buffer is free
-    if (ch + 1 < n_iter) stage_chunk(ch + 1, buf ^ 1);
+    if (it + 1 < n_iter) stage_chunk(chunk_at(it + 1), buf ^ 1);
     uint32_t ka = lds0 + buf * 65536 + a_off, ta = lds0 + buf * 65536 + t_off;
     AQ_OPAQUE(ka);
     AQ_OPAQUE(ta);
@@ -250,7 +260,9 @@ constexpr int kQT = 64;  // queries per tile
 constexpr int kDkdvThreads = 512;
 constexpr int kLdsR = 65536, kLdsStat = 131072;
 constexpr int kLdsOneHot = kLdsStat + 2 * 768;  // two one-hot B operands, 16 bytes per lane
-constexpr int kDkdvLds = kLdsOneHot + 2048;
+constexpr int kMaxCubes = 4096;                   // cube-sparse: longest query-cube list
+constexpr int kLdsList = kLdsOneHot + 2048;       // that list (+ its length), int32
+constexpr int kDkdvLds = kLdsList + 4 * (kMaxCubes + 1);
 
 // Lane layout of the S^T B operand: lane n takes query pi(n) of its wave's 32 (bits 2 and 3 of n
 // exchanged).  After the one-hot transposition the 8 k-slots of each lane half are then 8
@@ -271,11 +283,12 @@ struct DkdvLane {
 
 // Copies of tile qb into buffer `buf`: Q-hat rows from the workspace, dO rows from the caller's
 // tensor (rows past lq repeat row lq-1; every product they feed is masked), and the three
-// per-query statistics (entries past lq repeat entry lq-1).  Per lane: 4 copies of 16 bytes, plus
+// per-query statistics (entries past lq repeat entry lq-1); cm_row is the chunk-max row of the
+// key chunk for these queries.  Per lane: 4 copies of 16 bytes, plus
 // one 4-byte copy in waves 0..2.
 __device__ __forceinline__ void dkdv_stage_tile(const BwdParams &p, const DkdvLane &ln, int64_t bh, int64_t bb,
-                                                int64_t hh, int64_t kc, int64_t qb, uint8_t *lds, int buf, int wave,
-                                                int lane) {
+                                                int64_t hh, int64_t cm_row, int64_t qb, uint8_t *lds, int buf,
+                                                int wave, int lane) {
   uint8_t *rq = lds + kLdsR + buf * 32768, *ro = rq + 16384;
   const u32x4 *qsrc = p.qq + (bh * p.Cq * kChunk + qb * kQT) * (kD / 8);
   const uint16_t *osrc = p.d_o + bb * p.sdo.b + hh * p.sdo.h + qb * kQT * p.sdo.l;
@@ -289,7 +302,7 @@ __device__ __forceinline__ void dkdv_stage_tile(const BwdParams &p, const DkdvLa
     load_lds16_s(osrc, ov, ro + (i * 8 + wave) * 1024);
   }
   if (wave < 3) {
-    const float *src = (wave == 0 ? p.cmax + (bh * p.Ck + kc) * p.lq : (wave == 1 ? p.lse : p.dvec) + bh * p.lq) + qb * kQT;
+    const float *src = (wave == 0 ? p.cmax + cm_row * p.lq : (wave == 1 ? p.lse : p.dvec) + bh * p.lq) + qb * kQT;
     const int q = lane < rem ? lane : (int)(rem < 0 ? 0 : rem);
     load_lds4_s(src, (uint32_t)q * 4u, lds + kLdsStat + buf * 768 + wave * 256);
   }
@@ -396,6 +409,33 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
   const int64_t nqt = (p.lq + kQT - 1) / kQT;
   const int64_t qt0 = p.causal ? (kc * kChunk) / kQT : 0;
 
+  // Cube-sparse: the query cubes that selected this key cube, ascending, with the key cube's
+  // position in each one's list (packed qc | slot << 16), compacted by wave 0.
+  int32_t *lds_list = (int32_t *)(lds + kLdsList);
+  int64_t ntiles = nqt - qt0;
+  if (p.sel) {
+    if (wave == 0) {
+      const int16_t *col = p.slot_t + (bh * p.Ck + kc) * p.Cq;
+      int cnt = 0;
+      for (int64_t base = 0; base < p.Cq; base += 64) {
+        const int64_t qcube = base + lane;
+        const int sl = qcube < p.Cq ? (int)col[qcube] : -1;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(sl >= 0);
+        const int pos = cnt + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+        if (sl >= 0) lds_list[pos] = (int32_t)qcube | (sl << 16);
+        cnt += (int)__builtin_popcountll(m);
+      }
+      if (lane == 0) lds_list[kMaxCubes] = cnt;
+    }
+    __syncthreads();
+    ntiles = 2 * (int64_t)lds_list[kMaxCubes];
+  }
+  // Tile t: query tile and chunk-max row.
+  auto tile_qb = [&](int64_t t) -> int64_t { return p.sel ? 2 * (int64_t)(lds_list[t >> 1] & 0xffff) + (t & 1) : qt0 + t; };
+  auto tile_cm = [&](int64_t t) -> int64_t {
+    return p.sel ? bh * p.nsel + (lds_list[t >> 1] >> 16) : bh * p.Ck + kc;
+  };
+
   DkdvLane ln;
   {
     const int krow = kg * 32 + perm_row(n), swk = sw_kq(krow);
@@ -438,7 +478,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
       *(bf16x8 *)(lds + kLdsOneHot + 1024 + lane * 16) = onehot_b(lane, 1);
     }
   }
-  if (qt0 < nqt) dkdv_stage_tile(p, ln, bh, bb, hh, kc, qt0, lds, 0, wave, lane);
+  if (ntiles > 0) dkdv_stage_tile(p, ln, bh, bb, hh, tile_cm(0), tile_qb(0), lds, 0, wave, lane);
 
   const bool tail = (kc + 1) * kChunk > p.lk;
   f32x16 dk[4], dv[4];
@@ -449,21 +489,21 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
   }
 
   // Tiles in pairs (buffer 0, then buffer 1), then an odd last tile in buffer 0.
-  int64_t qb = qt0;
-  for (; qb + 1 < nqt; qb += 2) {
-    AQ_WAIT_VMCNT(0);  // this wave's copies of tile qb
+  int64_t t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    AQ_WAIT_VMCNT(0);  // this wave's copies of tile t
     __syncthreads();   // everyone's copies landed; buffer 1 is free
-    dkdv_stage_tile(p, ln, bh, bb, hh, kc, qb + 1, lds, 1, wave, lane);
-    dkdv_tile<0>(p, lds0, ln, qb, tail, dk, dv);
+    dkdv_stage_tile(p, ln, bh, bb, hh, tile_cm(t + 1), tile_qb(t + 1), lds, 1, wave, lane);
+    dkdv_tile<0>(p, lds0, ln, tile_qb(t), tail, dk, dv);
     AQ_WAIT_VMCNT(0);
     __syncthreads();  // buffer 0 is free
-    if (qb + 2 < nqt) dkdv_stage_tile(p, ln, bh, bb, hh, kc, qb + 2, lds, 0, wave, lane);
-    dkdv_tile<1>(p, lds0, ln, qb + 1, tail, dk, dv);
+    if (t + 2 < ntiles) dkdv_stage_tile(p, ln, bh, bb, hh, tile_cm(t + 2), tile_qb(t + 2), lds, 0, wave, lane);
+    dkdv_tile<1>(p, lds0, ln, tile_qb(t + 1), tail, dk, dv);
   }
-  if (qb < nqt) {
+  if (t < ntiles) {
     AQ_WAIT_VMCNT(0);
     __syncthreads();
-    dkdv_tile<0>(p, lds0, ln, qb, tail, dk, dv);
+    dkdv_tile<0>(p, lds0, ln, tile_qb(t), tail, dk, dv);
   }
 
   // The two waves of a key group add their partial sums: wave qh = 0 finishes dK, qh = 1 dV.
@@ -502,8 +542,25 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
 
 }  // namespace
 
-hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stream) {
-  const Workspace w = workspace_layout(1, a.batch, a.heads, a.lq, a.lk);
+namespace {
+
+// slot_t[bh][kc][qc] = position of key cube kc in query cube qc's selection, or -1: one lane per
+// entry, a linear search of the (short) selection row.
+__global__ __launch_bounds__(256) void vsa_slot_kernel(const int32_t *__restrict__ sel, int16_t *__restrict__ slot_t,
+                                                       int64_t n, int64_t nsel, int64_t total) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int64_t qc = gid % n, kc = (gid / n) % n, bh = gid / (n * n);
+  const int32_t *row = sel + (bh * n + qc) * nsel;
+  int s = -1;
+  for (int64_t t = 0; t < nsel; ++t)
+    if (row[t] == (int32_t)kc) s = (int)t;
+  slot_t[gid] = (int16_t)s;
+}
+
+// Shared by the dense and the cube-sparse backward: operand prepasses, D, dQ, dK/dV.
+hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspace &w, const int32_t *sel,
+                             const int16_t *slot_t, int64_t nsel, hipStream_t stream) {
   uint8_t *ws = (uint8_t *)a.workspace;
   const TileQuant qd_q = (a.flags & 1u) ? kQuantD : kQuantNone;
   const TileQuant qd_k = (a.flags & 2u) ? kQuantD : kQuantNone;
@@ -544,8 +601,10 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
   p.scale = a.scale;
   p.causal = a.causal;
   p.quant_p = (a.flags & 8u) != 0;
+  p.sel = sel;
+  p.slot_t = slot_t;
+  p.nsel = nsel;
 
-  // Dynamic LDS above 64 KiB must be allowed per kernel.
   p.nwork = bh * p.Cq;
   p.per_xcd = (p.nwork + 7) / 8;
   AQ_LAUNCH("bwd_dq", bwd_dq_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(kDqThreads), 0, stream, p);
@@ -555,6 +614,25 @@ hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stre
   p.per_xcd = (p.nwork + 7) / 8;
   AQ_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(kDkdvThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stream) {
+  return launch_bwd_common(a, b, workspace_layout(1, a.batch, a.heads, a.lq, a.lk), nullptr, nullptr, 0, stream);
+}
+
+hipError_t launch_vsa_bwd(const AttnArgs &a, const BwdArgs &b, const int32_t *sel, int n_cubes, int topk,
+                          hipStream_t stream) {
+  if (n_cubes > kMaxCubes || a.lq != a.lk || a.lk != (int64_t)n_cubes * kChunk) return hipErrorInvalidValue;
+  const Workspace w = workspace_layout(3, a.batch, a.heads, a.lq, a.lk);
+  int16_t *slot = (int16_t *)((uint8_t *)a.workspace + w.slot);
+  const int64_t total = (int64_t)a.batch * a.heads * n_cubes * n_cubes;
+  AQ_LAUNCH("vsa_slot", vsa_slot_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, sel, slot,
+                     (int64_t)n_cubes, (int64_t)topk, total);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_bwd_common(a, b, w, sel, slot, topk, stream);
 }
 
 }  // namespace aq

@@ -98,11 +98,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // the two accumulators leave no room for the Q-hat operand in registers at two waves per SIMD,
 // so that variant runs 8 waves (256 queries) per workgroup, one per CU, with each wave's Q-hat
 // rows in LDS (8 KiB per wave) and re-read once per chunk.
-template <bool TRAIN, bool QP, bool F16>
-__global__ __launch_bounds__((TRAIN && QP) ? 512 : 256, (TRAIN && QP) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
+//
+// QL selects the 8-wave layout.  The cube-sparse training forward keeps 4 waves (its chunk lists
+// are per 128 queries) and then runs one wave per SIMD.
+template <bool TRAIN, bool QP, bool F16, bool QL>
+__global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   static_assert(!F16 || QP, "the fp16 product needs a quantized P");
   constexpr bool HP = TRAIN && QP;  // O^hp needs its own product only when P is quantized
-  constexpr bool QL = HP;           // Q-hat operand from LDS
   constexpr int WAVES = QL ? 8 : 4;
   constexpr int BM = 32 * WAVES;
   // Separate objects, so the compiler can tell reads of one tile from copies into the other.
@@ -420,8 +422,8 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   // Training outputs come as a set (lse, chunk maxima, O^hp).
   const bool train = a.o_hp && a.lse && a.cmax;
   if (!train && (a.o_hp || a.lse || a.cmax)) return hipErrorInvalidValue;
-  const int waves = (train && qp) ? 8 : WAVES;  // see attn_fwd_kernel
-  if (sel && waves != WAVES) return hipErrorInvalidValue;  // chunk lists are per 128 queries
+  const bool ql = train && qp && !sel;  // see attn_fwd_kernel
+  const int waves = ql ? 8 : WAVES;
   p.qtiles = (int)((a.lq + 32 * waves - 1) / (32 * waves));
   p.nblocks = (int64_t)a.batch * a.heads * p.qtiles;
   p.per_xcd = (p.nblocks + 7) / 8;
@@ -429,14 +431,17 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   p.causal = a.causal;
   p.quant_q = (a.flags & 1u) != 0;
   const dim3 grid((unsigned)(p.per_xcd * 8)), block(waves * 64);
-  if (train) {
-    if (f16) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, true>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, false, false>), grid, block, 0, stream, p);
+  if (ql) {
+    if (f16) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, true, true>), grid, block, 0, stream, p);
+    else AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, false, true>), grid, block, 0, stream, p);
+  } else if (train) {
+    if (f16) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, true, false>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, false, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, false, false, false>), grid, block, 0, stream, p);
   } else {
-    if (f16) AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, true, true>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, true, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, false, false>), grid, block, 0, stream, p);
+    if (f16) AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, true, true, false>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, true, false, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, false, false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

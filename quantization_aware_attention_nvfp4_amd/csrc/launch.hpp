@@ -10,6 +10,7 @@ namespace aq {
 
 constexpr int kHeadDimHost = 128;
 constexpr int kChunkHost = 128;
+constexpr int kMaxCubesHost = 4096;  // cube-sparse backward: longest per-key-cube list
 
 struct Strides {
   int64_t b, h, l;
@@ -50,8 +51,10 @@ struct VsaArgs {
 //   op 1 (backward): kq, vq (V-hat rows), qq (Q-hat rows), dvec [B*H, lq] fp32 (D_i = <dO_i, o_hp_i>)
 //   op 2 (cube-sparse forward): kq, vt, pool [3, B*H, n, 128] bf16 (cube means of Q, K, V),
 //                    selw [B*H, n, n] int32 (selection when the caller passes none)
+//   op 3 (cube-sparse backward): the op 1 regions, plus slot [B*H, n, n] int16 (position of every
+//                    key cube in every query cube's selection, or -1)
 struct Workspace {
-  size_t kq, vt, vq, qq, dvec, pool, selw, total;
+  size_t kq, vt, vq, qq, dvec, pool, selw, slot, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -71,10 +74,14 @@ inline Workspace workspace_layout(int op, int batch, int heads, int64_t lq, int6
   };
   w.kq = take(kbytes);
   if (op == 0 || op == 2) w.vt = take(kbytes);
-  if (op == 1) {
+  if (op == 1 || op == 3) {
     w.vq = take(kbytes);
     w.qq = take(qbytes);
     w.dvec = take(bh * (size_t)lq * 4);
+  }
+  if (op == 3) {
+    const size_t n = (size_t)(lk / kChunkHost);
+    w.slot = take(bh * n * n * 2);
   }
   if (op == 2) {
     const size_t n = (size_t)(lk / kChunkHost);
@@ -112,5 +119,9 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stream);
 hipError_t launch_vsa_fwd(const AttnArgs &a, const VsaArgs &s, hipStream_t stream);
+// Straight-through backward of the cube-sparse fine stage; sel [B*H, n, topk] is the forward's
+// selection (ascending, distinct), a.cmax holds [B*H, topk, lq] chunk maxima.
+hipError_t launch_vsa_bwd(const AttnArgs &a, const BwdArgs &b, const int32_t *sel, int n_cubes, int topk,
+                          hipStream_t stream);
 
 }  // namespace aq

@@ -238,9 +238,12 @@ def vsa_topk(sparsity: float, n_cubes: int) -> int:
 
 def vsa_qat_fwd(q, k, v, grid=(16, 28, 56), cube=(4, 4, 8), sparsity: float = 0.9,
                 sm_scale: Optional[float] = None, quant_flags: int = AQ_QUANT_ALL,
-                coarse: bool = False, return_sel: bool = False):
+                coarse: bool = False, return_sel: bool = False, training: bool = False):
     """Cube-sparse fake-quant forward on cube-major [B, L, H, D] bf16 tensors.
-    Returns o_fine (and o_coarse, sel when requested)."""
+    Returns o_fine (and o_coarse, sel when requested).  With ``training`` the
+    return value is (o_fine, aux), aux holding the selection and the fine
+    stage's statistics for ``vsa_qat_bwd`` (sel, lse_log2, chunk_max_log2,
+    o_hp), and o_coarse when requested."""
     B, L, Lk, H, Hkv, D = _check_qkv(q, k, v)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
@@ -248,16 +251,27 @@ def vsa_qat_fwd(q, k, v, grid=(16, 28, 56), cube=(4, 4, 8), sparsity: float = 0.
     topk = vsa_topk(sparsity, n) if n > 0 else 0
     o = torch.empty(B, L, H, D, dtype=torch.bfloat16, device=q.device)
     oc = torch.empty_like(o) if coarse else None
-    sel = torch.empty(B, H, n, max(topk, 1), dtype=torch.int32, device=q.device) if return_sel else None
+    want_sel = return_sel or training
+    sel = torch.empty(B, H, n, max(topk, 1), dtype=torch.int32, device=q.device) if want_sel else None
+    lse = cmax = ohp = None
+    if training:
+        lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device)
+        cmax = torch.empty(B, H, max(topk, 1), L, dtype=torch.float32, device=q.device)
+        ohp = torch.empty(B, H, L, D, dtype=torch.float32, device=q.device)
     ws = _workspace(2, B, H, L, L, q.device) if D == HEAD_SIZE and L > 0 else torch.empty(
         256, dtype=torch.uint8, device=q.device)
     p = lambda t: None if t is None else t.data_ptr()
     check(load().vsa_qat_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), p(oc), p(sel), B, H, D,
                              L, grid[0], grid[1], grid[2], cube[0], cube[1], cube[2], float(sparsity),
                              _strides_blhd(q), _strides_blhd(k), _strides_blhd(v), _strides_blhd(o),
-                             float(sm_scale), int(quant_flags), _aligned_ptr(ws), ws.numel() - 256,
-                             _stream_ptr(q)),
+                             float(sm_scale), int(quant_flags), p(lse), p(cmax), p(ohp), _aligned_ptr(ws),
+                             ws.numel() - 256, _stream_ptr(q)),
           "vsa_qat_fwd")
+    if training:
+        aux = {"sel": sel, "lse_log2": lse, "chunk_max_log2": cmax, "o_hp": ohp}
+        if coarse:
+            aux["o_coarse"] = oc
+        return o, aux
     out = [o]
     if coarse:
         out.append(oc)
@@ -266,6 +280,67 @@ def vsa_qat_fwd(q, k, v, grid=(16, 28, 56), cube=(4, 4, 8), sparsity: float = 0.
     return out[0] if len(out) == 1 else tuple(out)
 
 
+def vsa_qat_bwd(q, k, v, aux, d_o, grid=(16, 28, 56), cube=(4, 4, 8), sparsity: float = 0.9,
+                sm_scale: Optional[float] = None, quant_flags: int = AQ_QUANT_ALL):
+    """Straight-through backward of the cube-sparse fine stage.  ``aux`` is the
+    dict returned by ``vsa_qat_fwd(..., training=True)`` with the same
+    arguments.  Returns dq, dk, dv [B, L, H, D] bf16."""
+    B, L, Lk, H, Hkv, D = _check_qkv(q, k, v)
+    _require_bf16_cuda("d_o", d_o)
+    if d_o.shape != q.shape:
+        raise ValueError("d_o must have q's shape")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    for name in ("lse_log2", "chunk_max_log2", "o_hp"):
+        t = aux[name]
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"aux[{name}] must be a contiguous fp32 device tensor")
+    sel = aux["sel"]
+    if sel.dtype != torch.int32 or not sel.is_contiguous() or not sel.is_cuda:
+        raise ValueError("aux['sel'] must be a contiguous int32 device tensor")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    ws = _workspace(3, B, H, L, L, q.device) if D == HEAD_SIZE and L > 0 else torch.empty(
+        256, dtype=torch.uint8, device=q.device)
+    check(load().vsa_qat_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), aux["o_hp"].data_ptr(), d_o.data_ptr(),
+                             aux["lse_log2"].data_ptr(), aux["chunk_max_log2"].data_ptr(), sel.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, D, L, grid[0], grid[1], grid[2],
+                             cube[0], cube[1], cube[2], float(sparsity), _strides_blhd(q), _strides_blhd(k),
+                             _strides_blhd(v), _strides_blhd(d_o), _strides_blhd(dq), _strides_blhd(dk),
+                             _strides_blhd(dv), float(sm_scale), int(quant_flags), _aligned_ptr(ws),
+                             ws.numel() - 256, _stream_ptr(q)),
+          "vsa_qat_bwd")
+    return dq, dk, dv
+
+
+class _VsaQatTrain(torch.autograd.Function):
+    """Forward = the cube-sparse fine stage; backward = its straight-through
+    estimator (vsa_qat_bwd)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, grid, cube, sparsity, sm_scale):
+        o, aux = vsa_qat_fwd(q, k, v, grid=grid, cube=cube, sparsity=sparsity, sm_scale=sm_scale, training=True)
+        ctx.save_for_backward(q, k, v, aux["sel"], aux["lse_log2"], aux["chunk_max_log2"], aux["o_hp"])
+        ctx.args = (grid, cube, sparsity, sm_scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k, v, sel, lse, cmax, ohp = ctx.saved_tensors
+        grid, cube, sparsity, sm_scale = ctx.args
+        aux = {"sel": sel, "lse_log2": lse, "chunk_max_log2": cmax, "o_hp": ohp}
+        dq, dk, dv = vsa_qat_bwd(q, k, v, aux, d_o.contiguous(), grid=grid, cube=cube, sparsity=sparsity,
+                                 sm_scale=sm_scale)
+        return dq, dk, dv, None, None, None, None
+
+
+def vsa_qat_train(q_BLHD: torch.Tensor, k_BLHD: torch.Tensor, v_BLHD: torch.Tensor, grid=(16, 28, 56),
+                  cube=(4, 4, 8), sparsity: float = 0.9, sm_scale: Optional[float] = None) -> torch.Tensor:
+    """Cube-sparse fine stage with the straight-through backward, cube-major [B, L, H, D] in and out."""
+    return _VsaQatTrain.apply(q_BLHD, k_BLHD, v_BLHD, tuple(grid), tuple(cube), float(sparsity), sm_scale)
+
+
 __all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "fq_nvfp4",
            "static_global_scale", "attn_qat_fwd", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
-           "vsa_qat_fwd", "vsa_topk"]
+           "vsa_qat_fwd", "vsa_qat_bwd", "vsa_qat_train", "vsa_topk"]

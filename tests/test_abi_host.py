@@ -13,10 +13,10 @@ HEADER = os.path.join(ROOT, "include", "attnqat.h")
 
 @pytest.fixture(scope="module")
 def lib():
+    if not os.path.exists(os.path.join(ROOT, "quantization_aware_attention_nvfp4_amd", "libattnqat.so")):
+        import __graft_entry__
+        __graft_entry__._libbuild().build()
     from quantization_aware_attention_nvfp4_amd import _lib
-    if not os.path.exists(_lib.LIB_PATH):
-        from quantization_aware_attention_nvfp4_amd import build
-        build.build()
     return _lib.load()
 
 
@@ -101,9 +101,24 @@ def test_vsa_rejects_bad_arguments(lib, kw, code, msg):
     s = S(25088 * 1536, 128, 1536)
     g, c = kw["grid"], kw["cube"]
     rc = lib.vsa_qat_fwd(16, 16, 16, 16, None, None, 1, 12, 128, kw["L"], g[0], g[1], g[2], c[0], c[1], c[2],
-                         kw.get("sparsity", 0.9), s, s, s, s, 0.088, 15, 256, 1 << 40, None)
+                         kw.get("sparsity", 0.9), s, s, s, s, 0.088, 15, None, None, None, 256, 1 << 40, None)
     assert rc == code
     assert msg in lib.aq_last_error().decode()
+    # the backward makes the same shape checks
+    rc = lib.vsa_qat_bwd(16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1, 12, 128, kw["L"], g[0], g[1], g[2], c[0],
+                         c[1], c[2], kw.get("sparsity", 0.9), s, s, s, s, s, s, s, 0.088, 15, 256, 1 << 40, None)
+    assert rc == code
+    assert msg in lib.aq_last_error().decode()
+
+
+def test_vsa_training_outputs_and_backward_inputs(lib):
+    s = S(25088 * 1536, 128, 1536)
+    rc = lib.vsa_qat_fwd(16, 16, 16, 16, None, None, 1, 12, 128, 25088, 16, 28, 56, 4, 4, 8, 0.9, s, s, s, s,
+                         0.088, 15, 16, None, None, 256, 1 << 40, None)
+    assert rc == -1 and "together" in lib.aq_last_error().decode()
+    rc = lib.vsa_qat_bwd(16, 16, 16, 16, 16, 16, 16, None, 16, 16, 16, 1, 12, 128, 25088, 16, 28, 56, 4, 4, 8, 0.9,
+                         s, s, s, s, s, s, s, 0.088, 15, 256, 1 << 40, None)
+    assert rc == -1 and "required" in lib.aq_last_error().decode()
 
 
 def test_fq_rejects_bad_arguments(lib):
