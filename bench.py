@@ -10,12 +10,16 @@ B=1, H=12, L=16*28*56=25088, D=128):
   2. attn_qat_fwd in training mode (Q, K, V and P fake-quantized; lse, chunk
      maxima and the high-precision auxiliary output written);
   3. attn_qat_bwd, the straight-through backward;
-  4. vsa_qat_fwd, the cube-sparse forward (196 cubes of 4x4x8, top-20).
+  4. vsa_qat_fwd in training mode, the cube-sparse forward (196 cubes of 4x4x8,
+     top-20; its fine stage's lse, chunk maxima and auxiliary output written);
+  5. vsa_qat_bwd, the straight-through backward of the cube-sparse fine stage.
 
 value = algorithmic attention FLOP per step / ms_per_step, where the dense
-forward counts 4*B*H*L^2*D, the backward 2.5x that (10*B*H*L^2*D), and the
+forward counts 4*B*H*L^2*D, the backward 2.5x that (10*B*H*L^2*D), the
 cube-sparse forward 4*B*H*n*k*128^2*D for its fine stage plus 4*B*H*n^2*D for
-its coarse stage; fq contributes time but no FLOP.  Per-kernel durations come
+its coarse stage, and its backward 2.5x the fine stage; fq contributes time but
+no FLOP.  After the step loop, the cube-sparse inference forward and fq on its
+own (back-to-back launches) are timed for the "attention" and "fq" objects.  Per-kernel durations come
 from HIP events the library records around each of its launches on the launch
 stream while kernel timing is on (aq_kernel_timing).
 
@@ -49,8 +53,9 @@ def flops():
     fwd = 4.0 * B * H * L * L * D
     n = L // (CUBE[0] * CUBE[1] * CUBE[2])
     k = max(1, min(math.ceil((1 - SPARSITY) * n), n))
-    vsa = 4.0 * B * H * n * k * 128 * 128 * D + 4.0 * B * H * n * n * D
-    return {"fwd": fwd, "bwd": 2.5 * fwd, "vsa": vsa, "topk": k, "cubes": n}
+    fine = 4.0 * B * H * n * k * 128 * 128 * D
+    return {"fwd": fwd, "bwd": 2.5 * fwd, "vsa_fine": fine, "vsa": fine + 4.0 * B * H * n * n * D,
+            "vsa_bwd": 2.5 * fine, "topk": k, "cubes": n}
 
 
 def cpu_baseline(q, k, v, do, seconds: float):
@@ -96,6 +101,9 @@ KERNEL_SOURCES = {
     "bwd_dq": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "attn_fwd_train": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "fq_contig_unit": ("fq.hip", "aq_device.hpp"),
+    "vsa_fwd_train": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
+    "vsa_bwd_dkdv": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
+    "vsa_bwd_dq": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_qat_step_wan448x896x61_hbm_traffic.md")
 
@@ -139,6 +147,7 @@ def pmc_probe():
     q, k, v = (t.to(dev) for t in synth.wan_448x896x61())
     do = synth.normal_bf16((B, L, H, D), 2003).to(dev)
     qv, kv, vv = (t.to(dev) for t in synth.vsa_inputs())
+    dov = synth.normal_bf16((B, L, H, D), 2005).to(dev)
     src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -146,7 +155,8 @@ def pmc_probe():
     m.fq_nvfp4(x, out=y)
     o, aux = m.attn_qat_fwd(q, k, v, training=True)
     m.attn_qat_bwd(q, k, v, aux, do)
-    m.vsa_qat_fwd(qv, kv, vv, grid=GRID, cube=CUBE, sparsity=SPARSITY)
+    ov, auxv = m.vsa_qat_fwd(qv, kv, vv, grid=GRID, cube=CUBE, sparsity=SPARSITY, training=True)
+    m.vsa_qat_bwd(qv, kv, vv, auxv, dov, grid=GRID, cube=CUBE, sparsity=SPARSITY)
     torch.cuda.synchronize()
     print("pmc probe done: copy bytes", 2 * src.numel(), flush=True)
 
@@ -185,10 +195,12 @@ def main():
     q, k, v = synth.wan_448x896x61()
     do = synth.normal_bf16((B, L, H, D), 2003)
     qv, kv, vv = synth.vsa_inputs()
+    dov = synth.normal_bf16((B, L, H, D), 2005)
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
-    qvd, kvd, vvd = (t.to(dev) for t in (qv, kv, vv))
+    qvd, kvd, vvd, dovd = (t.to(dev) for t in (qv, kv, vv, dov))
 
-    phases = ("fq", "fwd", "bwd", "vsa")
+    phases = ("fq", "fwd", "bwd", "vsa_fwd", "vsa_bwd")
+    vsa_args = dict(grid=GRID, cube=CUBE, sparsity=SPARSITY)
 
     def step(i, ev=None):
         if ev is not None:
@@ -202,15 +214,18 @@ def main():
         m.attn_qat_bwd(qd, kd, vd, aux, dod)
         if ev is not None:
             ev[3].record()
-        m.vsa_qat_fwd(qvd, kvd, vvd, grid=GRID, cube=CUBE, sparsity=SPARSITY)
+        ov, auxv = m.vsa_qat_fwd(qvd, kvd, vvd, training=True, **vsa_args)
         if ev is not None:
             ev[4].record()
+        m.vsa_qat_bwd(qvd, kvd, vvd, auxv, dovd, **vsa_args)
+        if ev is not None:
+            ev[5].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
     _lib.kernel_times(reset=True)
     _lib.kernel_timing(True)
     torch.cuda.synchronize()
@@ -222,9 +237,30 @@ def main():
     _lib.kernel_timing(False)
     kt = _lib.kernel_times(reset=True)
 
+    # The cube-sparse inference forward (no training outputs), outside the step.
+    vev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for i in range(5):
+        vev[i].record()
+        m.vsa_qat_fwd(qvd, kvd, vvd, **vsa_args)
+    vev[5].record()
+    torch.cuda.synchronize()
+    vsa_inf_ms = sum(vev[i].elapsed_time(vev[i + 1]) for i in range(1, 5)) / 4
+
+    # fq on its own: 40 back-to-back launches over the 4 rotating pairs between one pair of events
+    # (a per-launch event pair adds about a microsecond to a 26 us kernel).
+    fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for i in range(4):
+        m.fq_nvfp4(xs[i], out=ys[i])
+    fev[0].record()
+    for i in range(40):
+        m.fq_nvfp4(xs[i % 4], out=ys[i % 4])
+    fev[1].record()
+    torch.cuda.synchronize()
+    fq_alone_ms = fev[0].elapsed_time(fev[1]) / 40
+
     ms_step = wall * 1e3 / args.steps
     phase_ms = {p: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, p in enumerate(phases)}
-    total_flop = fl["fwd"] + fl["bwd"] + fl["vsa"]
+    total_flop = fl["fwd"] + fl["bwd"] + fl["vsa"] + fl["vsa_bwd"]
     value = total_flop / (ms_step * 1e-3) / 1e12
 
     # Per-kernel averages and their algorithmic work per launch.
@@ -234,6 +270,9 @@ def main():
         "bwd_dkdv": (0.8 * fl["bwd"], "flop"),  # S, dP, dV, dK: 4 of the 5 backward products
         "bwd_dq": (0.2 * fl["bwd"], "flop"),    # dQ (its S and dP recomputation counts as overhead)
         "fq_contig_unit": (fq_bytes, "byte"),
+        "vsa_fwd_train": (fl["vsa_fine"], "flop"),
+        "vsa_bwd_dkdv": (0.8 * fl["vsa_bwd"], "flop"),
+        "vsa_bwd_dq": (0.2 * fl["vsa_bwd"], "flop"),
     }
     kernels = {}
     for name, (cnt, ms) in kt.items():
@@ -256,18 +295,24 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": None if traffic is None else int(traffic),
                 "traffic_unit": "HBM bytes per launch (TCC FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
-    fq_avg = kt["fq_contig_unit"][1] / kt["fq_contig_unit"][0]
-    fq = {"kernel": "fq_contig_unit", "bytes_per_launch": fq_bytes, "avg_us": round(fq_avg * 1e3, 2),
-          "GB/s": round(fq_bytes / (fq_avg * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-          "frac": round(fq_bytes / (fq_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-          "traffic": None if recorded_traffic("fq_contig_unit") is None else int(recorded_traffic("fq_contig_unit"))}
+    fq_step_ms = kt["fq_contig_unit"][1] / kt["fq_contig_unit"][0]
+    fq_gbs = fq_bytes / (fq_alone_ms * 1e-3) / 1e9
+    fq_traffic = recorded_traffic("fq_contig_unit")
+    fq = {"kernel": "fq_contig_unit", "bytes_per_launch": fq_bytes, "avg_us": round(fq_alone_ms * 1e3, 2),
+          "GB/s": round(fq_gbs, 1), "peak": PEAK_HBM_GBS, "frac": round(fq_gbs / PEAK_HBM_GBS, 4),
+          "timing": "40 back-to-back launches over 4 rotating 154 MB pairs, one event pair",
+          "in_step_avg_us": round(fq_step_ms * 1e3, 2),
+          "traffic": None if fq_traffic is None else int(fq_traffic)}
     attn_ms = phase_ms["fwd"] + phase_ms["bwd"]
     attn = {"fwd_bwd_ms": round(attn_ms, 4),
             "fwd_bwd_TFLOP/s": round((fl["fwd"] + fl["bwd"]) / (attn_ms * 1e-3) / 1e12, 1),
             "frac_bf16_peak": round((fl["fwd"] + fl["bwd"]) / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "fwd_TFLOP/s": round(fl["fwd"] / (phase_ms["fwd"] * 1e-3) / 1e12, 1),
             "bwd_TFLOP/s": round(fl["bwd"] / (phase_ms["bwd"] * 1e-3) / 1e12, 1),
-            "vsa_TFLOP/s": round(fl["vsa"] / (phase_ms["vsa"] * 1e-3) / 1e12, 1)}
+            "vsa_fwd_train_TFLOP/s": round(fl["vsa"] / (phase_ms["vsa_fwd"] * 1e-3) / 1e12, 1),
+            "vsa_bwd_TFLOP/s": round(fl["vsa_bwd"] / (phase_ms["vsa_bwd"] * 1e-3) / 1e12, 1),
+            "vsa_inference_fwd_ms": round(vsa_inf_ms, 4),
+            "vsa_inference_fwd_TFLOP/s": round(fl["vsa"] / (vsa_inf_ms * 1e-3) / 1e12, 1)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -277,7 +322,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "Wan2.1-T2V-1.3B attention at 448x896, 61 frames: fq + fwd + bwd + VSA",
+        "config": {"workload": "Wan2.1-T2V-1.3B attention at 448x896, 61 frames: fq + fwd + bwd + VSA fwd + VSA bwd",
                    "B": B, "H": H, "L": L, "D": D, "causal": False, "quant": "Q,K,V,P NVFP4 unit scale",
                    "vsa_cubes": fl["cubes"], "vsa_topk": fl["topk"], "fq_shape": list(xs[0].shape)},
         "roofline": roofline, "cpu_baseline": cpu, "attention": attn, "fq": fq,

@@ -92,6 +92,7 @@ constexpr int kDqLds = 2 * 65536;
 // 0 and 1 must pick the 64-byte quarter (the two high bits of the 16-byte column).
 __device__ __forceinline__ int sw_kd(int r) { return ((r >> 2) & 1) | ((r >> 3) & 2) | ((r & 3) << 2); }
 
+template <bool SPARSE>
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) uint8_t lds[kDqLds];
   const uint32_t lds0 = lds_addr(lds);
@@ -105,14 +106,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int qrow = (int)(qc * kChunk) + qg * 32 + n;
   const bool qvalid = qrow < p.lq;
 
-  int64_t n_iter = p.sel ? p.nsel : p.Ck;
+  int64_t n_iter = SPARSE ? p.nsel : p.Ck;
   if (p.causal) {
     const int64_t q_last = qc * kChunk + kChunk - 1;
     n_iter = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
   }
   // Key chunk of iteration `it`: the it-th selected cube, or chunk `it` (a uniform scalar).
-  const int32_t *sel_row = p.sel ? p.sel + (bh * p.Cq + qc) * p.nsel : nullptr;
-  auto chunk_at = [&](int64_t it) -> int64_t { return sel_row ? (int64_t)sel_row[it] : it; };
+  const int32_t *sel_row = SPARSE ? p.sel + (bh * p.Cq + qc) * p.nsel : nullptr;
+  auto chunk_at = [&](int64_t it) -> int64_t { return SPARSE ? (int64_t)sel_row[it] : it; };
   // Chunk copies: per lane 4 K-hat and 4 V-hat pieces of 16 bytes.
   uint32_t c_voff[4];
 #pragma unroll
@@ -396,6 +397,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
   }
 }
 
+template <bool SPARSE>
 __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) uint8_t lds[kDkdvLds];
   const uint32_t lds0 = lds_addr(lds);
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
   // position in each one's list (packed qc | slot << 16), compacted by wave 0.
   int32_t *lds_list = (int32_t *)(lds + kLdsList);
   int64_t ntiles = nqt - qt0;
-  if (p.sel) {
+  if constexpr (SPARSE) {
     if (wave == 0) {
       const int16_t *col = p.slot_t + (bh * p.Ck + kc) * p.Cq;
       int cnt = 0;
@@ -431,9 +433,11 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
     ntiles = 2 * (int64_t)lds_list[kMaxCubes];
   }
   // Tile t: query tile and chunk-max row.
-  auto tile_qb = [&](int64_t t) -> int64_t { return p.sel ? 2 * (int64_t)(lds_list[t >> 1] & 0xffff) + (t & 1) : qt0 + t; };
+  auto tile_qb = [&](int64_t t) -> int64_t {
+    return SPARSE ? 2 * (int64_t)(lds_list[t >> 1] & 0xffff) + (t & 1) : qt0 + t;
+  };
   auto tile_cm = [&](int64_t t) -> int64_t {
-    return p.sel ? bh * p.nsel + (lds_list[t >> 1] >> 16) : bh * p.Ck + kc;
+    return SPARSE ? bh * p.nsel + (lds_list[t >> 1] >> 16) : bh * p.Ck + kc;
   };
 
   DkdvLane ln;
@@ -607,12 +611,16 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
 
   p.nwork = bh * p.Cq;
   p.per_xcd = (p.nwork + 7) / 8;
-  AQ_LAUNCH("bwd_dq", bwd_dq_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(kDqThreads), 0, stream, p);
+  const dim3 dq_grid((unsigned)(p.per_xcd * 8));
+  if (sel) AQ_LAUNCH("vsa_bwd_dq", bwd_dq_kernel<true>, dq_grid, dim3(kDqThreads), 0, stream, p);
+  else AQ_LAUNCH("bwd_dq", bwd_dq_kernel<false>, dq_grid, dim3(kDqThreads), 0, stream, p);
   if ((e = hipGetLastError())) return e;
 
   p.nwork = bh * p.Ck;
   p.per_xcd = (p.nwork + 7) / 8;
-  AQ_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3((unsigned)(p.per_xcd * 8)), dim3(kDkdvThreads), 0, stream, p);
+  const dim3 dkdv_grid((unsigned)(p.per_xcd * 8));
+  if (sel) AQ_LAUNCH("vsa_bwd_dkdv", bwd_dkdv_kernel<true>, dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
+  else AQ_LAUNCH("bwd_dkdv", bwd_dkdv_kernel<false>, dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
   return hipGetLastError();
 }
 

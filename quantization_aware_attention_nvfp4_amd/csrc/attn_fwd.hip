@@ -431,17 +431,18 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   p.causal = a.causal;
   p.quant_q = (a.flags & 1u) != 0;
   const dim3 grid((unsigned)(p.per_xcd * 8)), block(waves * 64);
+  const char *nm_train = sel ? "vsa_fwd_train" : "attn_fwd_train", *nm = sel ? "vsa_fwd" : "attn_fwd";
   if (ql) {
-    if (f16) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, true, true>), grid, block, 0, stream, p);
-    else AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, false, true>), grid, block, 0, stream, p);
+    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, true>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true>), grid, block, 0, stream, p);
   } else if (train) {
-    if (f16) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, true, false>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, true, false, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH("attn_fwd_train", (attn_fwd_kernel<true, false, false, false>), grid, block, 0, stream, p);
+    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, false>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, false, false, false>), grid, block, 0, stream, p);
   } else {
-    if (f16) AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, true, true, false>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, true, false, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH("attn_fwd", (attn_fwd_kernel<false, false, false, false>), grid, block, 0, stream, p);
+    if (f16) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, true, false>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm, (attn_fwd_kernel<false, false, false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
