@@ -18,8 +18,9 @@ value = algorithmic attention FLOP per step / ms_per_step, where the dense
 forward counts 4*B*H*L^2*D, the backward 2.5x that (10*B*H*L^2*D), the
 cube-sparse forward 4*B*H*n*k*128^2*D for its fine stage plus 4*B*H*n^2*D for
 its coarse stage, and its backward 2.5x the fine stage; fq contributes time but
-no FLOP.  After the step loop, the cube-sparse inference forward and fq on its
-own (back-to-back launches) are timed for the "attention" and "fq" objects.  Per-kernel durations come
+no FLOP.  After the step loop, the dense and cube-sparse inference forwards and
+fq on its own (back-to-back launches) are timed for the "attention" and "fq"
+objects.  Per-kernel durations come
 from HIP events the library records around each of its launches on the launch
 stream while kernel timing is on (aq_kernel_timing).
 
@@ -100,6 +101,7 @@ KERNEL_SOURCES = {
     "bwd_dkdv": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "bwd_dq": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "attn_fwd_train": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
+    "attn_fwd": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "fq_contig_unit": ("fq.hip", "aq_device.hpp"),
     "vsa_fwd_train": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "vsa_bwd_dkdv": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
@@ -153,6 +155,7 @@ def pmc_probe():
     torch.cuda.synchronize()
     dst.copy_(src)
     m.fq_nvfp4(x, out=y)
+    m.attn_qat_fwd(q, k, v)
     o, aux = m.attn_qat_fwd(q, k, v, training=True)
     m.attn_qat_bwd(q, k, v, aux, do)
     ov, auxv = m.vsa_qat_fwd(qv, kv, vv, grid=GRID, cube=CUBE, sparsity=SPARSITY, training=True)
@@ -246,6 +249,16 @@ def main():
     torch.cuda.synchronize()
     vsa_inf_ms = sum(vev[i].elapsed_time(vev[i + 1]) for i in range(1, 5)) / 4
 
+    # The dense inference forward (the forward-only workload's kernel), outside the step.
+    iev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    m.attn_qat_fwd(qd, kd, vd)
+    iev[0].record()
+    for _ in range(5):
+        m.attn_qat_fwd(qd, kd, vd)
+    iev[1].record()
+    torch.cuda.synchronize()
+    fwd_inf_ms = iev[0].elapsed_time(iev[1]) / 5
+
     # fq on its own: 40 back-to-back launches over the 4 rotating pairs between one pair of events
     # (a per-launch event pair adds about a microsecond to a 26 us kernel).
     fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -311,6 +324,9 @@ def main():
             "bwd_TFLOP/s": round(fl["bwd"] / (phase_ms["bwd"] * 1e-3) / 1e12, 1),
             "vsa_fwd_train_TFLOP/s": round(fl["vsa"] / (phase_ms["vsa_fwd"] * 1e-3) / 1e12, 1),
             "vsa_bwd_TFLOP/s": round(fl["vsa_bwd"] / (phase_ms["vsa_bwd"] * 1e-3) / 1e12, 1),
+            "inference_fwd_ms": round(fwd_inf_ms, 4),
+            "inference_fwd_TFLOP/s": round(fl["fwd"] / (fwd_inf_ms * 1e-3) / 1e12, 1),
+            "inference_fwd_frac_bf16_peak": round(fl["fwd"] / (fwd_inf_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "vsa_inference_fwd_ms": round(vsa_inf_ms, 4),
             "vsa_inference_fwd_TFLOP/s": round(fl["vsa"] / (vsa_inf_ms * 1e-3) / 1e12, 1)}
 

@@ -86,6 +86,12 @@ __device__ __forceinline__ void load_lds16_s(const void *sbase, uint32_t voff, u
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff), "s"(uniform_ptr(sbase))
                : "memory", "m0");
 }
+// Same, with the LDS destination given as a wave-uniform LDS byte address (kept in a scalar
+// register, so no vector register carries it across a loop).
+__device__ __forceinline__ void load_lds16_sa(const void *sbase, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(voff), "s"(uniform_ptr(sbase))
+               : "memory", "m0");
+}
 __device__ __forceinline__ void load_lds4_s(const void *sbase, uint32_t voff, uint8_t *lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0v), "v"(voff), "s"(uniform_ptr(sbase))

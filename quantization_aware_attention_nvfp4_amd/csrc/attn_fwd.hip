@@ -87,14 +87,109 @@ __device__ __forceinline__ void stage_v(const uint8_t *gtile, uint8_t *lds, cons
 #pragma unroll
   for (int i = 0; i < 32 / WAVES; ++i) load_lds16_s(gtile + 1024 * WAVES * i, so.v, lds + 1024 * WAVES * i + 1024 * wave);
 }
+// The same copies with the LDS tile given as an LDS byte address.
+template <int WAVES>
+__device__ __forceinline__ void stage_k_at(const uint8_t *gtile, uint32_t lds, const StageOffsets &so, int wave) {
+#pragma unroll
+  for (int i = 0; i < 32 / WAVES; ++i)
+    load_lds16_sa(gtile + 1024 * WAVES * i, (i & 1) ? so.k_odd : so.k_even, lds + 1024 * WAVES * i + 1024 * wave);
+}
+template <int WAVES>
+__device__ __forceinline__ void stage_v_at(const uint8_t *gtile, uint32_t lds, const StageOffsets &so, int wave) {
+#pragma unroll
+  for (int i = 0; i < 32 / WAVES; ++i) load_lds16_sa(gtile + 1024 * WAVES * i, so.v, lds + 1024 * WAVES * i + 1024 * wave);
+}
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Q-hat fragment of the lane's query (zero past lq): the S^T B operand, d = 16t + 8hf + (0..7);
+// the two lane halves hold the two 8-element halves of each 16-element block along D.
+__device__ __forceinline__ void load_q_frags(const FwdParams &p, int64_t bb, int64_t hh, int64_t qrow, bool qvalid,
+                                             int hf, bf16x8 (&qf)[8]) {
+  const uint16_t *qp = p.q + bb * p.sq.b + hh * p.sq.h + (qvalid ? qrow : 0) * p.sq.l;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (qvalid) v = *(const u32x4 *)(qp + 16 * t + 8 * hf);
+    if (p.quant_q) {
+      float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                    bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
+      am = pair_max(am);
+      const float S = block_scale_unit(am);
+      const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);
+      v = u32x4{pack_exact_bf16(f[0], f[1]), pack_exact_bf16(f[2], f[3]), pack_exact_bf16(f[4], f[5]),
+                pack_exact_bf16(f[6], f[7])};
+    }
+    qf[t] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// P of one 32-key sub-tile, whose 16 logits in the lane's registers are one P block, as the two
+// P-hat V-hat B operands (keys 0-7 and 8-15 of the block); psum gains the block's unquantized sum.
+// HP: also the unquantized P as operands (ph), for O^hp.
+template <bool QP, bool F16, bool HP>
+__device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, float m_new, float &psum, u32x4 (&pq)[2],
+                                       u32x4 (&ph)[2]) {
+  if (QP) {
+    const ProbBlock pb = prob_block(bmax, c, m_new);
+    float r[16], rsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      r[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -pb.mb));
+      rsum += r[i];
+    }
+    psum = __builtin_fmaf(pb.Sd, rsum, psum);
+    const uint32_t c0 = e2m1_codes8(r), c1 = e2m1_codes8(r + 8);
+    if (F16) {
+      pq[0] = e2m1_decode8_f16(c0, pb.S);
+      pq[1] = e2m1_decode8_f16(c1, pb.S);
+    } else {
+      float x[8];
+      e2m1_decode8(c0, pb.S, x);
+      pq[0] = __builtin_bit_cast(u32x4, pack8_cvt(x));
+      e2m1_decode8(c1, pb.S, x);
+      pq[1] = __builtin_bit_cast(u32x4, pack8_cvt(x));
+    }
+    if (HP) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r[i] *= pb.Sd;  // the unquantized P
+      if (F16) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          f16x8 h;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) h[i] = (_Float16)r[8 * j + i];
+          ph[j] = __builtin_bit_cast(u32x4, h);
+        }
+      } else {
+        ph[0] = __builtin_bit_cast(u32x4, pack8_cvt(r));
+        ph[1] = __builtin_bit_cast(u32x4, pack8_cvt(r + 8));
+      }
+    }
+  } else {
+    float P[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      P[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m_new));
+      psum += P[i];
+    }
+    pq[0] = __builtin_bit_cast(u32x4, pack8_cvt(P));
+    pq[1] = __builtin_bit_cast(u32x4, pack8_cvt(P + 8));
+  }
+}
 
 // TRAIN: also write lse, chunk maxima and O^hp.  QP: P is fake-quantized.  F16: P-hat and V-hat
 // (both fake-quantized, hence exact in fp16) multiply on the fp16 MFMA, whose products are the
 // same as the bf16 ones for these values.
 //
-// Inference: 4 waves (128 queries) per workgroup, two workgroups per CU.  With the O^hp product
+// This kernel serves training and the cube-sparse calls; dense inference runs the pipelined
+// kernel below.  Inference: 4 waves (128 queries) per workgroup, two workgroups per CU.  With the
+// O^hp product
 // the two accumulators leave no room for the Q-hat operand in registers at two waves per SIMD,
 // so that variant runs 8 waves (256 queries) per workgroup, one per CU, with each wave's Q-hat
 // rows in LDS (8 KiB per wave) and re-read once per chunk.
@@ -150,31 +245,8 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
   stage_k<WAVES>(ktile(chunk), lds_k, so, wave);
   stage_v<WAVES>(vtile(chunk), lds_v, so, wave);
 
-  // ---- Q-hat fragment: B operand of S^T, d = 16t + 8hf + (0..7) -------------------------
   bf16x8 qf[8];
-  {
-    const uint16_t *qp = p.q + bb * p.sq.b + hh * p.sq.h + (qvalid ? qrow : 0) * p.sq.l;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qvalid) v = *(const u32x4 *)(qp + 16 * t + 8 * hf);
-      if (p.quant_q) {
-        float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
-                      bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
-        float am = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
-        am = pair_max(am);
-        const float S = block_scale_unit(am);
-        const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);
-        v = u32x4{pack_exact_bf16(f[0], f[1]), pack_exact_bf16(f[2], f[3]), pack_exact_bf16(f[4], f[5]),
-                  pack_exact_bf16(f[6], f[7])};
-      }
-      qf[t] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+  load_q_frags(p, bb, hh, qrow, qvalid, hf, qf);
   // QL: the wave's 32 Q-hat rows go to its own LDS region (row n = the lane's query, columns
   // swizzled by sw_row), read back as the S^T B operand once per chunk.
   uint32_t qa = 0;
@@ -295,52 +367,7 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       u32x4 pq[2], ph[2];
-      if (QP) {
-        const ProbBlock pb = prob_block(bmax[kt], p.c, m_new);
-        float r[16], rsum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          r[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], p.c, -pb.mb));
-          rsum += r[i];
-        }
-        psum = __builtin_fmaf(pb.Sd, rsum, psum);
-        const uint32_t c0 = e2m1_codes8(r), c1 = e2m1_codes8(r + 8);
-        if (F16) {
-          pq[0] = e2m1_decode8_f16(c0, pb.S);
-          pq[1] = e2m1_decode8_f16(c1, pb.S);
-        } else {
-          float x[8];
-          e2m1_decode8(c0, pb.S, x);
-          pq[0] = __builtin_bit_cast(u32x4, pack8_cvt(x));
-          e2m1_decode8(c1, pb.S, x);
-          pq[1] = __builtin_bit_cast(u32x4, pack8_cvt(x));
-        }
-        if (HP) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) r[i] *= pb.Sd;  // the unquantized P
-          if (F16) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              f16x8 h;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) h[i] = (_Float16)r[8 * j + i];
-              ph[j] = __builtin_bit_cast(u32x4, h);
-            }
-          } else {
-            ph[0] = __builtin_bit_cast(u32x4, pack8_cvt(r));
-            ph[1] = __builtin_bit_cast(u32x4, pack8_cvt(r + 8));
-          }
-        }
-      } else {
-        float P[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          P[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], p.c, -m_new));
-          psum += P[i];
-        }
-        pq[0] = __builtin_bit_cast(u32x4, pack8_cvt(P));
-        pq[1] = __builtin_bit_cast(u32x4, pack8_cvt(P + 8));
-      }
+      form_p<QP, F16, HP>(s[kt], bmax[kt], p.c, m_new, psum, pq, ph);
       u32x4 a[2][4];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -392,6 +419,228 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
   if (TRAIN && hf == 0) p.lse[bh * p.lq + qrow] = m_run + __builtin_amdgcn_logf(l);
 }
 
+// ------------------------------------------------------------------------------------------
+// Pipelined inference forward (dense)
+// ------------------------------------------------------------------------------------------
+//
+// 4 waves (128 queries) per workgroup, two workgroups per CU (one wave of each per SIMD).  The
+// logits of chunk it+1 are computed during chunk it: step kt of iteration it forms P-hat(it, kt+1)
+// on the vector ALUs while the matrix cores run S(it+1, kt) = K-hat(it+1, kt) Q-hat^T into the
+// registers that sub-tile kt of chunk it has just released, and O^T += V-hat(it, kt)^T
+// P-hat(it, kt)^T.  The two workgroups of a CU drift out of phase, so one's softmax at the top of
+// a chunk runs beside the other's matrix work.
+//
+// LDS (64 KiB per workgroup): one K-hat chunk as four 8 KiB sub-tiles of 32 rows (256 B rows,
+// sw_kq swizzle) and one V-hat^T chunk as four 8 KiB sub-tiles [128 d][32 keys] (64 B rows,
+// 16-byte columns swizzled by sw_v64, so each sub-tile is contiguous).  After step kt every wave
+// has finished with sub-tile kt of both chunks, and one barrier later K-hat(it+2, kt) and
+// V-hat(it+1, kt) start copying into them: a full iteration ahead of their use, with one barrier
+// per step.  Measured on the 448x896x61 workload it runs ~9% fewer cycles than the
+// unpipelined kernel; the clock under this load (about 1.8-2.0 GHz) keeps the time gain small.
+constexpr int kPipeWaves = 4;
+constexpr uint32_t kPipeK = 0, kPipeV = 32768;  // LDS byte offsets
+
+// A ds_read_b128 serves 16 lanes per cycle from 64 banks (256 bytes): the 16 rows d..d+15 of a
+// read must then cover the 16 distinct 16-byte slots of 256 bytes, 4 * (d & 3) + column, so rows
+// that share d & 3 get different columns.
+__device__ __forceinline__ int sw_v64(int d) { return (d >> 2) & 3; }
+constexpr int kPipeAhead = 3, kPipeValu = 5;  // LDS reads issued ahead; VALU per MFMA in a step
+
+template <bool QP, bool F16>
+__global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) {
+  constexpr int WAVES = kPipeWaves;
+  constexpr int BM = 32 * WAVES;
+  constexpr int kCopies = 8 / WAVES;  // 1 KiB copies per wave and sub-tile
+  __shared__ __attribute__((aligned(256))) uint8_t lds[65536];
+
+  const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
+  if (vid < 0) return;
+  const int64_t bh = vid / p.qtiles;
+  const int qt = (int)(vid % p.qtiles);
+  const int64_t bb = bh / p.heads, hh = bh % p.heads;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const int64_t qrow = (int64_t)qt * BM + wave * 32 + n;
+  const bool qvalid = qrow < p.lq;
+
+  // Chunk counts and key indices in 32 bits (lengths are below 2^30): 64-bit compares of two
+  // uniform values would take a vector register.
+  const int lk = (int)p.lk;
+  int n_iter = (int)p.nchunks;
+  if (p.causal) {
+    const int q_last = qt * BM + BM - 1;
+    n_iter = (q_last < lk - 1 ? q_last : lk - 1) / kChunk + 1;
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.kchunks * (kChunk * kD / 8));
+  const uint8_t *vbase = (const uint8_t *)(p.vt + bh * p.kchunks * (kChunk * kD / 8));
+  // Copy of sub-tile kt of chunk c: this wave's 1 KiB of each.  K: rows 32kt + 4w + lane/16,
+  // physical column lane%16 (sw_kq does not depend on row bits 5-6).  V: rows d = 16w + lane/4,
+  // physical column lane%4, logical keys 32kt + 8*(column ^ sw_v64(d)).
+  uint32_t k_off[kCopies], v_off[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int ci = kCopies * wave + i, r = 4 * ci + (lane >> 4), d = 16 * ci + (lane >> 2);
+    k_off[i] = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
+    v_off[i] = (uint32_t)(d * 256 + (((lane & 3) ^ sw_v64(d)) << 4));
+  }
+  auto copy_k = [&](int c, int kt) {
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i)
+      load_lds16_sa(kbase + (int64_t)c * 32768 + kt * 8192, k_off[i],
+                    lds0 + kPipeK + kt * 8192 + 1024 * (kCopies * wave + i));
+  };
+  auto copy_v = [&](int c, int kt) {
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i)
+      load_lds16_sa(vbase + (int64_t)c * 32768 + kt * 64, v_off[i], lds0 + kPipeV + kt * 8192 + 1024 * (kCopies * wave + i));
+  };
+
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    copy_k(0, kt);
+    copy_v(0, kt);
+  }
+  bf16x8 qf[8];
+  load_q_frags(p, bb, hh, qrow, qvalid, hf, qf);
+
+  uint32_t ka, va;
+  {
+    const int krow = perm_row(n), swk = sw_kq(krow);
+    ka = lds0 + kPipeK + krow * 256 + 16 * (hf ^ swk);
+    va = lds0 + kPipeV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
+  }
+  // S^T of one 32-key sub-tile from the K-hat chunk in LDS, into st (old contents dropped).
+  auto logits = [&](int kt, f32x16 &st) {
+    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(ka + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int t = 1; t < 8; ++t)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16((ka ^ (32 * t)) + 8192 * kt)), qf[t], st, 0,
+                                                   0, 0);
+  };
+
+  f32x16 s[4];
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+  float m_run = -__builtin_inff();
+  float l_run = 0.0f;
+
+  // Prologue: S(0), then K-hat(1) into the K buffer.
+  AQ_WAIT_VMCNT(0);
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) logits(kt, s[kt]);
+  __builtin_amdgcn_s_barrier();
+  if (n_iter > 1) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) copy_k(1, kt);
+  }
+  AQ_WAIT_VMCNT(0);
+  __builtin_amdgcn_s_barrier();
+
+  for (int it = 0; it < n_iter; ++it) {
+    // ---- masks: keys past lk (last chunk) and causal -------------------------------------
+    const bool tail = (it + 1) * kChunk > lk;
+    const bool diag = p.causal && (it + 1) * kChunk - 1 > qt * BM + wave * 32;
+    if (tail || diag) {
+      const int key0 = it * kChunk + 16 * hf, lk1 = lk - 1, q = (int)qrow;
+      const int last = p.causal ? (q < lk1 ? q : lk1) : lk1;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) mask_tail(s[kt], valid_prefix(key0 + 32 * kt, last));
+    }
+
+    // ---- running max (refreshed once per chunk) -----------------------------------------
+    float bmax[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      float mx = s[kt][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      bmax[kt] = mx;
+    }
+    float cm = fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3]));
+    cm = pair_max(cm);
+    const float m_new = fmaxf(m_run, cm * p.c);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+    }
+
+    // ---- steps: P-hat(it, kt+1) beside S(it+1, kt) and O^T += V-hat^T P-hat^T(it, kt) -------
+    // The last iteration also computes logits, from a stale K buffer, and drops them: a branch
+    // would split the block the scheduler interleaves.
+    const bool near_end = it + 2 >= n_iter;  // some copies are not issued: wait for all
+    float psum = 0.0f;
+    u32x4 pq[2][2], ph[2][2];
+    form_p<QP, F16, false>(s[0], bmax[0], p.c, m_new, psum, pq[0], ph[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      logits(kt, s[kt]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const u32x4 a = lds_read16((va ^ (16 * j)) + 8192 * kt + 2048 * dt);
+          if (F16)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                             __builtin_bit_cast(f16x8, pq[kt & 1][j]), acc[dt], 0, 0, 0);
+          else
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pq[kt & 1][j]), acc[dt], 0, 0, 0);
+        }
+      if (kt < 3) {
+        form_p<QP, F16, false>(s[kt + 1], bmax[kt + 1], p.c, m_new, psum, pq[(kt + 1) & 1], ph[(kt + 1) & 1]);
+        // Pinned here: otherwise the compiler sinks this work into the next step, beside its use.
+        AQ_OPAQUE(pq[(kt + 1) & 1][0]);
+        AQ_OPAQUE(pq[(kt + 1) & 1][1]);
+        AQ_OPAQUE(psum);
+      }
+      // Issue order: the A/B operands of three MFMAs ahead, then per MFMA the reads that keep
+      // that distance and a share of the P work.
+      __builtin_amdgcn_sched_group_barrier(0x100, kPipeAhead, 0);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (g < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (kt < 3) __builtin_amdgcn_sched_group_barrier(0x002, kPipeValu, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Sub-tile kt + 1 of both buffers has landed (this wave's copies: all but the last two
+      // steps' pairs), every wave is done with sub-tile kt, and its next contents start copying.
+      if (near_end) AQ_WAIT_VMCNT(0);
+      else if constexpr (kCopies == 1) AQ_WAIT_VMCNT(4);
+      else AQ_WAIT_VMCNT(8);
+      __builtin_amdgcn_s_barrier();
+      if (it + 2 < n_iter) copy_k(it + 2, kt);
+      if (it + 1 < n_iter) copy_v(it + 1, kt);
+    }
+    l_run = l_run * alpha + psum;
+  }
+
+  // ---- epilogue --------------------------------------------------------------------------
+  const float l = pair_sum(l_run);
+  const float inv_l = 1.0f / l;
+  if (!qvalid) return;
+  uint16_t *op = p.o + bb * p.so.b + hh * p.so.h + qrow * p.so.l;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * dt + 8 * a + 4 * hf;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 w = {(__bf16)(acc[dt][4 * a + 0] * inv_l), (__bf16)(acc[dt][4 * a + 1] * inv_l),
+                        (__bf16)(acc[dt][4 * a + 2] * inv_l), (__bf16)(acc[dt][4 * a + 3] * inv_l)};
+      *(bf16x4 *)(op + d0) = w;
+    }
+}
+
 }  // namespace
 
 // fp16 P-hat V-hat product: both operands fake-quantized.
@@ -423,7 +672,8 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   const bool train = a.o_hp && a.lse && a.cmax;
   if (!train && (a.o_hp || a.lse || a.cmax)) return hipErrorInvalidValue;
   const bool ql = train && qp && !sel;  // see attn_fwd_kernel
-  const int waves = ql ? 8 : WAVES;
+  const bool pipe = !train && !sel;     // attn_fwd_pipe_kernel
+  const int waves = ql ? 8 : pipe ? kPipeWaves : WAVES;
   p.qtiles = (int)((a.lq + 32 * waves - 1) / (32 * waves));
   p.nblocks = (int64_t)a.batch * a.heads * p.qtiles;
   p.per_xcd = (p.nblocks + 7) / 8;
@@ -439,6 +689,10 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
     if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, false>), grid, block, 0, stream, p);
     else if (qp) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false>), grid, block, 0, stream, p);
     else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, false, false, false>), grid, block, 0, stream, p);
+  } else if (pipe) {
+    if (f16) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, true>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<false, false>), grid, block, 0, stream, p);
   } else {
     if (f16) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, true, false>), grid, block, 0, stream, p);
     else if (qp) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false>), grid, block, 0, stream, p);
