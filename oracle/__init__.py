@@ -35,6 +35,10 @@ _lib = None
 
 QUANT_Q, QUANT_K, QUANT_V, QUANT_P = 1, 2, 4, 8
 QUANT_ALL = 15
+# Variants (readings in nvfp4_oracle.c): statistics relative to the final row
+# maximum, static per-tensor global scales for Q/K/V, the static global scale
+# of P, and smooth-K.
+FINAL_MAX, GSF_QKV, GSF_P, SMOOTH_K = 16, 32, 64, 128
 
 
 def build(force: bool = False) -> str:
@@ -175,6 +179,8 @@ def attn_fwd(q, k, v, scale, causal=False, flags=QUANT_ALL, chunk=128, rows=None
     Lk = k.shape[2]
     rows = np.arange(Lq, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     R = rows.size
+    if flags & FINAL_MAX:
+        chunk = (Lk + 15) // 16 * 16
     C = (Lk + chunk - 1) // chunk
     o = np.empty((B, H, R, D))
     ohp = np.empty((B, H, R, D))

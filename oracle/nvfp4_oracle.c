@@ -221,51 +221,129 @@ void oracle_fq_f32_rows(const float *x, float *y, int64_t rows, int64_t len, flo
 /* ------------------------------------------------------------------------ */
 
 enum { QF_Q = 1, QF_K = 2, QF_V = 4, QF_P = 8 };
+/* Variants named by the [API] flag list and the [META] precision records
+   (use_global_sf_qkv, use_global_sf_p, smooth_k; "sm100_exact_m" and the
+   reference-order statistics of the "Attn-QAT Training" guide); their
+   arithmetic is the reading given with each use below. */
+enum { QF_FINAL_MAX = 16, QF_GSF_QKV = 32, QF_GSF_P = 64, QF_SMOOTH_K = 128 };
 
 /* Per-head operands after fake quantization: Q and K along D, V along the
-   key axis ([META] quant_v, qk_format/pv_format; [API] unit global scales
-   use_global_sf_qkv = use_global_sf_p = False). */
+   key axis ([META] quant_v, qk_format/pv_format).  They are the operands of a
+   BF16 matmul ([META] "NVFP4 fake-quant with BF16 matmul"), so each value is
+   rounded to bf16 after dequantization; under the unit global scale this
+   changes nothing (an E2M1 value times an E4M3 scale is exact in bf16). */
 typedef struct {
     float *qh; /* [Lq, D] */
     float *kh; /* [Lk, D] */
     float *vh; /* [Lk, D] */
+    float gp;  /* global scale of P's blocks */
 } head_ops;
+
+/* Global scales of one call: unit, or static per tensor (QF_GSF_QKV: the
+   [QAD] input_global_sf formula 448*6/amax over the whole tensor, taken on
+   the values that are quantized, i.e. after smoothing), and for P
+   (QF_GSF_P: 448*6 / 1, P's largest value being exp(0) = 1). */
+typedef struct {
+    float gq, gk, gv, gp;
+} call_scales;
 
 static void load_head(const uint16_t *src, float *dst, int64_t L, int D)
 {
     for (int64_t i = 0; i < L * D; ++i) dst[i] = bf16_to_f32(src[i]);
 }
 
-static void quant_rows_D(float *x, int64_t L, int D)
+static void quant_rows_D(float *x, int64_t L, int D, float g)
 {
     for (int64_t i = 0; i < L; ++i)
-        for (int d0 = 0; d0 < D; d0 += 16) fq_block_f32(x + i * D + d0, D - d0 < 16 ? D - d0 : 16, 1.0f);
+        for (int d0 = 0; d0 < D; d0 += 16) fq_block_f32(x + i * D + d0, D - d0 < 16 ? D - d0 : 16, g);
 }
 
-static void quant_cols_L(float *x, int64_t L, int D)
+static void quant_cols_L(float *x, int64_t L, int D, float g)
 {
     float buf[16];
     for (int d = 0; d < D; ++d)
         for (int64_t j0 = 0; j0 < L; j0 += 16) {
             int n = (int)((L - j0) < 16 ? (L - j0) : 16);
             for (int i = 0; i < n; ++i) buf[i] = x[(j0 + i) * D + d];
-            fq_block_f32(buf, n, 1.0f);
+            fq_block_f32(buf, n, g);
             for (int i = 0; i < n; ++i) x[(j0 + i) * D + d] = buf[i];
         }
 }
 
+static void round_bf16(float *x, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) x[i] = bf16_to_f32(f32_to_bf16(x[i]));
+}
+
+/* Smooth-K (flag smooth_k): the keys' mean over the sequence, per channel,
+   is subtracted before quantization.  Reading: the mean is the fp64 sum over
+   the L keys divided by L, rounded to fp32; the smoothed key is
+   fp32(k - mean).  Every logit of a query row moves by the same amount, so
+   the softmax is unchanged. */
+static void smooth_rows(float *x, int64_t L, int D)
+{
+    for (int d = 0; d < D; ++d) {
+        double s = 0.0;
+        for (int64_t j = 0; j < L; ++j) s += (double)x[j * D + d];
+        float mean = (float)(s / (double)L);
+        for (int64_t j = 0; j < L; ++j) {
+            volatile float t = x[j * D + d] - mean;
+            x[j * D + d] = t;
+        }
+    }
+}
+
+/* 448*6 / max(amax, 1e-12) over all B*H heads of a [B*H, L, D] tensor, on
+   the values that are quantized (smoothed first when `smooth`). */
+static float tensor_scale(const uint16_t *x, int64_t BH, int64_t L, int D, int smooth)
+{
+    float amax = 0.0f;
+    float *buf = (float *)malloc(sizeof(float) * L * D);
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        load_head(x + bh * L * D, buf, L, D);
+        if (smooth) smooth_rows(buf, L, D);
+        for (int64_t i = 0; i < L * D; ++i) {
+            float a = fabsf(buf[i]);
+            if (isnan(a)) a = 0.0f;
+            if (a > amax) amax = a;
+        }
+    }
+    free(buf);
+    if (amax < 1e-12f) amax = 1e-12f;
+    volatile float g = (448.0f * 6.0f) / amax;
+    return g;
+}
+
+static call_scales make_scales(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t BH, int64_t Lq,
+                               int64_t Lk, int D, unsigned flags)
+{
+    call_scales c = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (flags & QF_GSF_QKV) {
+        c.gq = tensor_scale(q, BH, Lq, D, 0);
+        c.gk = tensor_scale(k, BH, Lk, D, (flags & QF_SMOOTH_K) != 0);
+        c.gv = tensor_scale(v, BH, Lk, D, 0);
+    }
+    if (flags & QF_GSF_P) c.gp = 448.0f * 6.0f;
+    return c;
+}
+
 static void make_head_ops(head_ops *h, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                          int64_t Lq, int64_t Lk, int D, unsigned flags)
+                          int64_t Lq, int64_t Lk, int D, unsigned flags, const call_scales *cs)
 {
     h->qh = (float *)malloc(sizeof(float) * Lq * D);
     h->kh = (float *)malloc(sizeof(float) * Lk * D);
     h->vh = (float *)malloc(sizeof(float) * Lk * D);
+    h->gp = cs->gp;
     load_head(q, h->qh, Lq, D);
     load_head(k, h->kh, Lk, D);
     load_head(v, h->vh, Lk, D);
-    if (flags & QF_Q) quant_rows_D(h->qh, Lq, D);
-    if (flags & QF_K) quant_rows_D(h->kh, Lk, D);
-    if (flags & QF_V) quant_cols_L(h->vh, Lk, D);
+    if (flags & QF_SMOOTH_K) smooth_rows(h->kh, Lk, D);
+    if (flags & QF_Q) quant_rows_D(h->qh, Lq, D, cs->gq);
+    if (flags & QF_K) quant_rows_D(h->kh, Lk, D, cs->gk);
+    if (flags & QF_V) quant_cols_L(h->vh, Lk, D, cs->gv);
+    round_bf16(h->qh, Lq * D);
+    round_bf16(h->kh, Lk * D);
+    round_bf16(h->vh, Lk * D);
 }
 
 static void free_head_ops(head_ops *h)
@@ -323,8 +401,10 @@ static void row_forward(const head_ops *h, int64_t i, const int64_t *keys, int64
         for (int t = 0; t < chunk; ++t)
             P[t] = (kc[t] < 0) ? 0.0f : (float)exp((double)S[t] - (double)m_new);
         memcpy(Pq, P, sizeof(float) * chunk);
-        if (flags & QF_P)
-            for (int t0 = 0; t0 < chunk; t0 += 16) fq_block_f32(Pq + t0, chunk - t0 < 16 ? chunk - t0 : 16, 1.0f);
+        if (flags & QF_P) {
+            for (int t0 = 0; t0 < chunk; t0 += 16) fq_block_f32(Pq + t0, chunk - t0 < 16 ? chunk - t0 : 16, h->gp);
+            round_bf16(Pq, chunk); /* the P-hat V-hat matmul operand */
+        }
         double alpha = (m == -INFINITY) ? 0.0 : exp((double)m - (double)m_new);
         double psum = 0.0;
         for (int t = 0; t < chunk; ++t) psum += (double)P[t];
@@ -382,10 +462,12 @@ int oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int
 {
     init_tables();
     if (causal && Lq != Lk) return -1;
+    if (flags & QF_FINAL_MAX) chunk = (int)((Lk + 15) / 16 * 16);
     int64_t C = (Lk + chunk - 1) / chunk;
+    const call_scales cs = make_scales(q, k, v, (int64_t)B * H, Lq, Lk, D, flags);
     for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
         head_ops hd;
-        make_head_ops(&hd, q + bh * Lq * D, k + bh * Lk * D, v + bh * Lk * D, Lq, Lk, D, flags);
+        make_head_ops(&hd, q + bh * Lq * D, k + bh * Lk * D, v + bh * Lk * D, Lq, Lk, D, flags, &cs);
 #pragma omp parallel for schedule(dynamic, 1)
         for (int64_t r = 0; r < nrows; ++r) {
             int64_t nc;
@@ -449,7 +531,10 @@ static void block_weights_mc(const bwd_head *x, int64_t i, int64_t b0, int nb, d
         S[t] = live ? logit(x->hd, i, b0 + t, x->D, x->scale) : -INFINITY;
         P[t] = live ? (float)exp((double)S[t] - mc) : 0.0f;
     }
-    if (x->flags & QF_P) fq_block_f32(P, nb, 1.0f);
+    if (x->flags & QF_P) {
+        fq_block_f32(P, nb, x->hd->gp);
+        round_bf16(P, nb);
+    }
     for (int t = 0; t < nb; ++t) {
         int live = !(x->causal && b0 + t > i);
         A[t] = live ? exp((double)S[t] - lse) : 0.0;
@@ -496,10 +581,12 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
 {
     init_tables();
     if (causal && Lq != Lk) return -1;
+    if (flags & QF_FINAL_MAX) chunk = (int)((Lk + 15) / 16 * 16);
     int64_t C = (Lk + chunk - 1) / chunk;
+    const call_scales cs = make_scales(q, k, v, (int64_t)B * H, Lq, Lk, D, flags);
     for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
         head_ops hd;
-        make_head_ops(&hd, q + bh * Lq * D, k + bh * Lk * D, v + bh * Lk * D, Lq, Lk, D, flags);
+        make_head_ops(&hd, q + bh * Lq * D, k + bh * Lk * D, v + bh * Lk * D, Lq, Lk, D, flags, &cs);
         bwd_head x = {&hd, dout + bh * Lq * D, Lk, C, D, chunk, causal, flags, scale};
 
         if (dq && nq > 0) {
@@ -654,6 +741,10 @@ int oracle_vsa_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int 
              *vp = (uint16_t *)malloc(2 * n * D);
     double *sc = (double *)malloc(sizeof(double) * n * n);
     int32_t *sl = (int32_t *)malloc(sizeof(int32_t) * n * topk);
+    /* Reference-order statistics over the selected keys: one chunk. */
+    const int64_t nchunk = (flags & QF_FINAL_MAX) ? 1 : topk;
+    const int chunk = (flags & QF_FINAL_MAX) ? topk * cube_tokens : cube_tokens;
+    const call_scales cs = make_scales(q, k, v, (int64_t)B * H, L, L, D, flags);
     for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
         const uint16_t *qh = q + bh * L * D, *kh = k + bh * L * D, *vh = v + bh * L * D;
         vsa_select_head(qh, kh, n, cube_tokens, D, scale, topk, qp, kp, sc, sl);
@@ -665,14 +756,14 @@ int oracle_vsa_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int 
         if (sel) memcpy(sel + bh * n * topk, sl, sizeof(int32_t) * n * topk);
 
         head_ops hd;
-        make_head_ops(&hd, qh, kh, vh, L, L, D, flags);
+        make_head_ops(&hd, qh, kh, vh, L, L, D, flags, &cs);
 #pragma omp parallel for schedule(dynamic, 1)
         for (int64_t r = 0; r < nrows; ++r) {
             int64_t i = rows[r];
             int64_t a = i / cube_tokens;
             int64_t *keys = vsa_keys(sl + a * topk, topk, cube_tokens);
             if (o_fine)
-                row_forward(&hd, i, keys, topk, cube_tokens, D, scale, flags, o_fine + (bh * nrows + r) * D,
+                row_forward(&hd, i, keys, nchunk, chunk, D, scale, flags, o_fine + (bh * nrows + r) * D,
                             NULL, NULL, NULL);
             if (o_coarse) {
                 double mx = -INFINITY, l = 0.0;
@@ -719,12 +810,17 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
     uint16_t *qp = (uint16_t *)malloc(2 * n * D), *kp = (uint16_t *)malloc(2 * n * D);
     double *sc = (double *)malloc(sizeof(double) * n * n);
     int32_t *sl = (int32_t *)malloc(sizeof(int32_t) * n * topk);
+    /* Reference-order statistics over the selected keys: one chunk, whose
+       maximum every block of every selected cube uses. */
+    const int fm = (flags & QF_FINAL_MAX) != 0;
+    const int64_t nchunk = fm ? 1 : topk;
+    const call_scales cs = make_scales(q, k, v, (int64_t)B * H, L, L, D, flags);
     for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
         const uint16_t *qh = q + bh * L * D, *kh = k + bh * L * D, *vh = v + bh * L * D;
         vsa_select_head(qh, kh, n, ct, D, scale, topk, qp, kp, sc, sl);
         if (sel) memcpy(sel + bh * n * topk, sl, sizeof(int32_t) * n * topk);
         head_ops hd;
-        make_head_ops(&hd, qh, kh, vh, L, L, D, flags);
+        make_head_ops(&hd, qh, kh, vh, L, L, D, flags, &cs);
         bwd_head x = {&hd, dout + bh * L * D, L, n, D, ct, 0, flags, scale};
 
         /* Row statistics (lse, running max after each selected cube, D_i). */
@@ -740,7 +836,8 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
             if (!need[i]) continue;
             int64_t *keys = vsa_keys(sl + (i / ct) * topk, topk, ct);
             double *ohp = (double *)malloc(sizeof(double) * D);
-            row_forward(&hd, i, keys, topk, ct, D, scale, flags, NULL, ohp, lse + i, cmax + i * topk);
+            row_forward(&hd, i, keys, nchunk, fm ? topk * ct : ct, D, scale, flags, NULL, ohp, lse + i,
+                        cmax + i * topk);
             double s = 0.0;
             for (int d = 0; d < D; ++d) s += (double)bf16_to_f32(x.dO[i * D + d]) * ohp[d];
             Dv[i] = s;
@@ -761,7 +858,7 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
                         int64_t s;
                         int nb;
                         key_block(&x, b0, &s, &nb);
-                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + t], A, Ah);
+                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + (fm ? 0 : t)], A, Ah);
                         for (int u = 0; u < nb; ++u) {
                             int64_t j = s + u;
                             double dS = A[u] * (dot_do_v(&x, i, j) - Dv[i]);
@@ -792,7 +889,7 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
                         if (sl[qc * topk + u] == b) t = u;
                     if (t < 0) continue;  /* this query cube did not select j's cube */
                     for (int64_t i = qc * ct; i < (qc + 1) * ct; ++i) {
-                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + t], A, Ah);
+                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + (fm ? 0 : t)], A, Ah);
                         double dS = A[j - s] * (dot_do_v(&x, i, j) - Dv[i]);
                         for (int d = 0; d < D; ++d) {
                             if (ok) ok[d] += scale * dS * (double)hd.qh[i * D + d];

@@ -1,0 +1,228 @@
+"""Pins for the oracle's attention variants (CPU only).
+
+The variants are the flags the "attn_qat_train" API page lists and the
+"vsqa-preview-1.3b metadata.json" precision records carry (use_global_sf_qkv,
+use_global_sf_p, smooth_k), plus the reference-order softmax statistics the
+"Attn-QAT Training" guide's environment table names.  Each check ties the
+variant to something other than the oracle's own variant code:
+  * final max: the output equals the closed form over the whole row (one
+    maximum, 16-key blocks from key 0, the pinned fp32 codec); lse equals the
+    default reading's; the recorded maximum is the row maximum; dQ/dK equal
+    float64 autograd on the quantized operands; dV pairs with the output; at
+    sparsity 0 the cube-sparse variant equals the dense one;
+  * static Q/K/V scales: attention equals the default attention on operands
+    quantized beforehand by the pinned standalone fake quantization with the
+    pinned static scale of each tensor;
+  * static P scale: the output equals the unrolled closed form with P's blocks
+    quantized by the pinned codec under g = 448*6;
+  * smooth-K: without quantization the output is softmax attention on the
+    smoothed keys, which matches attention on the original keys up to the
+    keys' bf16 rounding (the softmax ignores a per-row shift); with
+    quantization it equals attention on keys smoothed and quantized by the
+    pinned fp32 codec.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+D = 128
+SCALE = 1.0 / math.sqrt(D)
+ALL = oracle.QUANT_ALL
+
+
+def rand_bits(shape, seed, mult=1.0, shift=0.0):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(*shape, generator=g) * mult + shift).to(torch.bfloat16)
+    return x.view(torch.int16).numpy().view(np.uint16)
+
+
+def f32(u16):
+    return oracle.bf16_bits_to_f32(u16)
+
+
+def f64(u16):
+    return torch.from_numpy(f32(u16).astype(np.float64))
+
+
+def bits_of(x32):
+    return oracle.f32_to_bf16_bits(np.asarray(x32, np.float32))
+
+
+def sdpa64(q, k, v, scale, causal=False):
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale, is_causal=causal)
+
+
+def closed_form(S, vh, gp=1.0, chunk=None):
+    """Per row: the unrolled online recurrence over `chunk`-key chunks (one
+    chunk = the whole row when None), fp32 probabilities relative to each
+    chunk's running max (libm exp), P-hat from the pinned codec under global
+    scale gp rounded to bf16, the denominator summing unquantized P."""
+    Lq, Lk = S.shape
+    chunk = chunk or (Lk + 15) // 16 * 16
+    C = (Lk + chunk - 1) // chunk
+    out = np.zeros((Lq, vh.shape[1]))
+    for i in range(Lq):
+        mc = [S[i, : min(Lk, chunk * (c + 1))].max() for c in range(C)]
+        lsum, acc = 0.0, np.zeros(vh.shape[1])
+        for c in range(C):
+            seg = S[i, chunk * c: min(Lk, chunk * (c + 1))]
+            P = np.array([math.exp(float(t) - float(mc[c])) for t in seg]).astype(np.float32)
+            Pp = np.zeros((len(P) + 15) // 16 * 16, np.float32)
+            Pp[: len(P)] = P
+            Pq = f32(bits_of(oracle.fq_f32_rows(Pp[None], g=gp)[0][: len(P)]))
+            w = math.exp(float(mc[c]) - float(mc[-1]))
+            lsum += w * P.astype(np.float64).sum()
+            acc += w * (Pq.astype(np.float64) @ vh[chunk * c: chunk * c + len(P)])
+        out[i] = acc / lsum
+    return out
+
+
+def quantized_ops(q, k, v):
+    qh = f32(oracle.fq_bf16(q, -1))[0, 0].astype(np.float64)
+    kh = f32(oracle.fq_bf16(k, -1))[0, 0].astype(np.float64)
+    vh = f32(oracle.fq_bf16(v, 2))[0, 0].astype(np.float64)
+    return qh, kh, vh
+
+
+# ---------------------------------------------------------------- final max
+
+def test_final_max_equals_whole_row_closed_form():
+    Lq, Lk = 20, 300
+    q, k, v = rand_bits((1, 1, Lq, D), 101), rand_bits((1, 1, Lk, D), 102, 2.0), rand_bits((1, 1, Lk, D), 103)
+    r = oracle.attn_fwd(q, k, v, SCALE, flags=ALL | oracle.FINAL_MAX)
+    qh, kh, vh = quantized_ops(q, k, v)
+    S = (SCALE * (qh @ kh.T)).astype(np.float32)
+    assert np.allclose(r["o"][0, 0], closed_form(S, vh), rtol=1e-9, atol=1e-12)
+    # one recorded maximum: the row maximum; lse does not depend on the reading
+    # beyond the fp32 rounding of P relative to a different maximum
+    assert r["cmax"].shape[-1] == 1
+    assert np.array_equal(r["cmax"][0, 0, :, 0], S.max(-1).astype(np.float64))
+    d = oracle.attn_fwd(q, k, v, SCALE, flags=ALL)
+    assert np.allclose(r["lse"], d["lse"], rtol=0, atol=1e-6)
+    # the readings differ (P is not scale-equivariant)
+    assert not np.array_equal(r["o"], d["o"])
+
+
+def test_final_max_backward_identities():
+    Lq, Lk = 60, 270
+    q, do = rand_bits((1, 2, Lq, D), 104), rand_bits((1, 2, Lq, D), 107)
+    k, v = rand_bits((1, 2, Lk, D), 105, 2.0), rand_bits((1, 2, Lk, D), 106)
+    fl = ALL | oracle.FINAL_MAX
+    b = oracle.attn_bwd(q, k, v, do, SCALE, flags=fl)
+    Q = f64(oracle.fq_bf16(q, -1)).requires_grad_()
+    K = f64(oracle.fq_bf16(k, -1)).requires_grad_()
+    sdpa64(Q, K, f64(oracle.fq_bf16(v, 2)), SCALE).backward(f64(do))
+    assert np.allclose(b["dq"], Q.grad.numpy(), rtol=0, atol=5e-6)
+    assert np.allclose(b["dk"], K.grad.numpy(), rtol=0, atol=5e-6)
+    f = oracle.attn_fwd(q, k, v, SCALE, flags=fl)
+    vh = f32(oracle.fq_bf16(v, 2)).astype(np.float64)
+    lhs = np.einsum("bhid,bhid->bh", f32(do).astype(np.float64), f["o"])
+    rhs = np.einsum("bhjd,bhjd->bh", b["dv"], vh)
+    assert np.allclose(lhs, rhs, rtol=1e-10)
+
+
+def test_final_max_causal_matches_closed_form():
+    L = 150
+    q, k, v = (rand_bits((1, 1, L, D), s) for s in (108, 109, 110))
+    r = oracle.attn_fwd(q, k, v, SCALE, causal=True, flags=ALL | oracle.FINAL_MAX, rows=np.arange(0, L, 7))
+    qh, kh, vh = quantized_ops(q, k, v)
+    S = (SCALE * (qh @ kh.T)).astype(np.float32)
+    for n, i in enumerate(range(0, L, 7)):
+        want = closed_form(S[i: i + 1, : i + 1], vh[: i + 1])
+        assert np.allclose(r["o"][0, 0, n], want[0], rtol=1e-9, atol=1e-12)
+
+
+def test_vsa_final_max_sparsity_zero_is_dense_final_max():
+    L = 512
+    q, k, v = (rand_bits((1, 2, L, D), s) for s in (111, 112, 113))
+    fl = ALL | oracle.FINAL_MAX
+    s = oracle.vsa_fwd(q, k, v, SCALE, sparsity=0.0, flags=fl)
+    d = oracle.attn_fwd(q, k, v, SCALE, flags=fl)
+    assert np.array_equal(s["o_fine"], d["o"])
+    do = rand_bits((1, 2, L, D), 114)
+    sb = oracle.vsa_bwd(q, k, v, do, SCALE, sparsity=0.0, flags=fl)
+    db = oracle.attn_bwd(q, k, v, do, SCALE, flags=fl)
+    for name in ("dq", "dk", "dv"):
+        assert np.allclose(sb[name], db[name], rtol=0, atol=1e-12), name
+
+
+# ---------------------------------------------------------- static scales
+
+@pytest.mark.parametrize("smooth", [False, True])
+def test_static_qkv_scales_compose_the_standalone_fake_quant(smooth):
+    Lq, Lk = 40, 200
+    q = rand_bits((1, 2, Lq, D), 115, 3.0)
+    k = rand_bits((1, 2, Lk, D), 116, 0.5, 0.7)
+    v = rand_bits((1, 2, Lk, D), 117, 2.0)
+    fl = ALL | oracle.GSF_QKV | (oracle.SMOOTH_K if smooth else 0)
+    r = oracle.attn_fwd(q, k, v, SCALE, flags=fl)
+    if smooth:
+        ks = smoothed_f32(k)
+        amax = np.abs(ks).max()
+        gk = np.float32(np.float32(2688.0) / np.float32(max(amax, 1e-12)))
+        kq = bits_of(oracle.fq_f32_rows(ks, g=float(gk)))
+    else:
+        kq = oracle.fq_bf16(k, -1, g=oracle.static_scale_bf16(k))
+    qq = oracle.fq_bf16(q, -1, g=oracle.static_scale_bf16(q))
+    vq = oracle.fq_bf16(v, 2, g=oracle.static_scale_bf16(v))
+    ref = oracle.attn_fwd(qq, kq, vq, SCALE, flags=oracle.QUANT_P)
+    assert np.array_equal(r["o"], ref["o"])
+    assert np.array_equal(r["lse"], ref["lse"])
+    b = oracle.attn_bwd(q, k, v, rand_bits((1, 2, Lq, D), 118), SCALE, flags=fl)
+    bref = oracle.attn_bwd(qq, kq, vq, rand_bits((1, 2, Lq, D), 118), SCALE, flags=oracle.QUANT_P)
+    for name in ("dq", "dk", "dv"):
+        assert np.array_equal(b[name], bref[name]), name
+
+
+def test_static_p_scale_equals_closed_form():
+    Lq, Lk = 16, 300
+    q, k, v = rand_bits((1, 1, Lq, D), 119), rand_bits((1, 1, Lk, D), 120, 2.0), rand_bits((1, 1, Lk, D), 121)
+    r = oracle.attn_fwd(q, k, v, SCALE, flags=ALL | oracle.GSF_P)
+    qh, kh, vh = quantized_ops(q, k, v)
+    S = (SCALE * (qh @ kh.T)).astype(np.float32)
+    assert np.allclose(r["o"][0, 0], closed_form(S, vh, gp=2688.0, chunk=128), rtol=1e-9, atol=1e-12)
+    # the P scale changes the result (P-hat is not bf16-exact under it)
+    assert not np.array_equal(r["o"], oracle.attn_fwd(q, k, v, SCALE, flags=ALL)["o"])
+
+
+# ----------------------------------------------------------------- smooth K
+
+def smoothed_f32(k_bits):
+    """fp32(k - mean) with the mean per (b, h, channel): fp64 sum / L, rounded to fp32."""
+    kf = f32(k_bits)
+    mean = (kf.astype(np.float64).sum(axis=2, keepdims=True) / kf.shape[2]).astype(np.float32)
+    return (kf - mean).astype(np.float32)
+
+
+def test_smooth_k_without_quantization_is_softmax_on_smoothed_keys():
+    Lq, Lk = 50, 230
+    q = rand_bits((1, 2, Lq, D), 122)
+    k = rand_bits((1, 2, Lk, D), 123, 1.0, 1.5)  # keys with a large common offset
+    v = rand_bits((1, 2, Lk, D), 124)
+    r = oracle.attn_fwd(q, k, v, SCALE, flags=oracle.SMOOTH_K)
+    ks = torch.from_numpy(f32(bits_of(smoothed_f32(k))).astype(np.float64))
+    want = sdpa64(f64(q), ks, f64(v), SCALE).numpy()
+    assert np.allclose(r["o"], want, rtol=0, atol=1e-6)  # the oracle's S and P are fp32
+    # the softmax ignores the per-row shift: close to attention on the original keys
+    orig = sdpa64(f64(q), f64(k), f64(v), SCALE).numpy()
+    assert np.abs(r["o"] - orig).max() < 2e-2 * np.abs(orig).max()
+
+
+def test_smooth_k_with_quantization_composes_the_fp32_codec():
+    Lq, Lk = 30, 200
+    q = rand_bits((1, 1, Lq, D), 125)
+    k = rand_bits((1, 1, Lk, D), 126, 1.0, -2.0)
+    v = rand_bits((1, 1, Lk, D), 127)
+    r = oracle.attn_fwd(q, k, v, SCALE, flags=ALL | oracle.SMOOTH_K)
+    kq = bits_of(oracle.fq_f32_rows(smoothed_f32(k)))
+    ref = oracle.attn_fwd(q, kq, v, SCALE, flags=ALL & ~oracle.QUANT_K)
+    assert np.array_equal(r["o"], ref["o"])
+    do = rand_bits((1, 1, Lq, D), 128)
+    b = oracle.attn_bwd(q, k, v, do, SCALE, flags=ALL | oracle.SMOOTH_K)
+    bref = oracle.attn_bwd(q, kq, v, do, SCALE, flags=ALL & ~oracle.QUANT_K)
+    for name in ("dq", "dk", "dv"):
+        assert np.array_equal(b[name], bref[name]), name
