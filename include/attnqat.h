@@ -60,6 +60,31 @@ enum {
     AQ_QUANT_ALL = 15
 };
 
+/* Variants, OR-ed into the same flags word.  [API] lists the kernel flags use_global_sf_qkv,
+   use_global_sf_p and smooth_k (all off in attn_qat_train) and [META]'s precision records carry the
+   same names; [DOC]'s environment table names reference-order softmax statistics
+   (FASTVIDEO_ATTN_QAT_FWD_EXACT_M).  None is defined on the pages; the readings implemented:
+     AQ_FINAL_MAX  every P relative to its row's final maximum over all keys (the selected keys for
+                   vsa_qat_fwd) instead of the running maximum of 128-key chunks; the forward
+                   first runs a row-maximum pass (+50% QK^T work).  The training outputs then hold
+                   that maximum in every chunk-maximum row, which the backward uses unchanged.
+     AQ_GSF_QKV    static global scale per tensor for Q, K, V: g = 448*6 / max(amax, 1e-12) over
+                   the whole tensor (["nvfp4_qad.py"] input_global_sf), computed on the device
+                   for every call; the dequantized values are rounded to bf16.
+     AQ_GSF_P      static global scale of P's blocks, g = 448*6 (P's largest value is 1).
+     AQ_SMOOTH_K   the keys' per-channel mean over the sequence (fp64 sum / L, rounded to fp32)
+                   subtracted before quantization; the softmax of a row ignores the shift and the
+                   gradient passes to K unchanged.
+   Under AQ_GSF_QKV or AQ_GSF_P the P-hat V-hat product runs in bf16 (the values are no longer
+   exact in fp16). */
+enum {
+    AQ_FINAL_MAX = 16,
+    AQ_GSF_QKV = 32,
+    AQ_GSF_P = 64,
+    AQ_SMOOTH_K = 128,
+    AQ_FLAGS_ALL = 255
+};
+
 /* Element strides of a 4-D attention tensor, indexed (batch, head, token, d) with d contiguous. */
 typedef struct {
     int64_t b, h, l;
@@ -98,7 +123,8 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  * q [B, H, lq, 128], k and v [B, H, lk, 128], o [B, H, lq, 128]: bf16, layout by strides.
  * Every bf16 tensor of the attention entry points starts 16-byte aligned and has strides that
  * are multiples of 8 elements and below 2^24 (rows move in 16-byte pieces); lq, lk <= 2^30.
- * Q-hat, K-hat along D and V-hat along keys are fake-quantized per quant_flags.  The keys are
+ * Q-hat, K-hat along D and V-hat along keys are fake-quantized per quant_flags (quantizers and
+ * the AQ_FINAL_MAX / AQ_GSF_QKV / AQ_GSF_P / AQ_SMOOTH_K variants above).  The keys are
  * visited in chunks of 128 ([0,128), [128,256), ...); in chunk c the running row maximum m_c of
  * the logits softmax_scale * <q-hat, k-hat> is refreshed first, then P = exp(logit - m_c) is
  * formed, fake-quantized in 16-key blocks (AQ_QUANT_P) and multiplied with V-hat on BF16 MFMA;
@@ -115,7 +141,7 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  * workspace : DEVICE scratch of at least attn_qat_workspace_size(0, ...) bytes, 256-byte aligned.
  * Errors: AQ_EINVAL (null q/k/v/o/workspace, head_size != 128 [API]
  * get_supported_head_sizes, sizes <= 0, non-finite or non-positive softmax_scale, flags outside
- * AQ_QUANT_ALL, strides that are not positive, misaligned tensors or strides, workspace too
+ * AQ_FLAGS_ALL, strides that are not positive, misaligned tensors or strides, workspace too
  * small, only some of the training outputs); AQ_ENOTSUP (num_kv_heads != num_heads, causal with
  * lq != lk, lengths above 2^30).
  * ------------------------------------------------------------------------------------------- */
@@ -134,7 +160,8 @@ int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch
  * the forward used): D_i = <dO_i, o_hp_i>, dV = A-hat^T dO, dP = dO V-hat^T,
  * dS = A * (dP - D), dQ = scale dS K-hat, dK = scale dS^T Q-hat.
  * Inputs q, k, v, d_o (bf16, strided as in the forward) and o_hp, lse_log2, chunk_max_log2
- * exactly as written by attn_qat_fwd with the same arguments; outputs dq, dk, dv bf16 with
+ * exactly as written by attn_qat_fwd with the same arguments, quant_flags included (the
+ * variants' scales and key means are recomputed from the same tensors); outputs dq, dk, dv bf16 with
  * their own strides.  workspace: at least attn_qat_workspace_size(1, ...) bytes.
  * Errors: as attn_qat_fwd, plus AQ_EINVAL for any null gradient or statistics pointer.
  * ------------------------------------------------------------------------------------------- */

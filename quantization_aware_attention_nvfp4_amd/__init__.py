@@ -9,10 +9,12 @@ from ._lib import load as _load
 
 _load()
 
-from .ops import (AQ_QUANT_ALL, AQ_QUANT_K, AQ_QUANT_P, AQ_QUANT_Q, AQ_QUANT_V,  # noqa: E402
+from .ops import (AQ_FINAL_MAX, AQ_FLAGS_ALL, AQ_GSF_P, AQ_GSF_QKV, AQ_QUANT_ALL, AQ_QUANT_K,  # noqa: E402
+                  AQ_QUANT_P, AQ_QUANT_Q, AQ_QUANT_V, AQ_SMOOTH_K,
                   AttnQatTrainImpl, attn_qat_bwd, attn_qat_fwd, attn_qat_train, fq_nvfp4,
                   static_global_scale, vsa_qat_bwd, vsa_qat_fwd, vsa_qat_train, vsa_topk)
 
-__all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "fq_nvfp4",
+__all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "AQ_FINAL_MAX", "AQ_GSF_QKV",
+           "AQ_GSF_P", "AQ_SMOOTH_K", "AQ_FLAGS_ALL", "fq_nvfp4",
            "static_global_scale", "attn_qat_fwd", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
            "vsa_qat_fwd", "vsa_qat_bwd", "vsa_qat_train", "vsa_topk"]

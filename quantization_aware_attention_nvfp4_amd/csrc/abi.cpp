@@ -57,8 +57,8 @@ int check_attention(int batch, int num_heads, int num_kv_heads, int head_size, i
                 num_heads, (long long)lq, (long long)lk);
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
     return fail(AQ_EINVAL, "softmax_scale must be finite and > 0 (got %g)", (double)softmax_scale);
-  if (quant_flags & ~(unsigned)AQ_QUANT_ALL)
-    return fail(AQ_EINVAL, "quant_flags 0x%x has bits outside AQ_QUANT_ALL", quant_flags);
+  if (quant_flags & ~(unsigned)AQ_FLAGS_ALL)
+    return fail(AQ_EINVAL, "quant_flags 0x%x has bits outside AQ_FLAGS_ALL", quant_flags);
   if (num_kv_heads != num_heads)
     return fail(AQ_ENOTSUP, "num_kv_heads (%d) must equal num_heads (%d)", num_kv_heads, num_heads);
   if (causal && lq != lk)

@@ -162,6 +162,17 @@ __device__ __forceinline__ ProbBlock prob_block(float logit_max, float c, float 
   const float Sd = S == 0.0f ? 1.0f : S;
   return ProbBlock{S, Sd, m + __builtin_amdgcn_logf(Sd)};
 }
+// The same under the static global scale g of P's blocks: s = E4M3(fp32(fp32(amax / 6) * g)),
+// S = fp32(s / g).  S is then not an E4M3 value, so the dequantized P-hat is rounded to bf16 as
+// the matmul operand.
+__device__ __forceinline__ ProbBlock prob_block_static(float logit_max, float c, float m, float g) {
+  const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(logit_max, c, -m));
+  const float S = round_e4m3((am / 6.0f) * g) / g;
+  const float Sd = S == 0.0f ? 1.0f : S;
+  return ProbBlock{S, Sd, m + __builtin_amdgcn_logf(Sd)};
+}
+// The static scale of P's blocks ("nvfp4_qad.py" FP4_RANGE over P's largest value, 1).
+constexpr float kPScaleStatic = 448.0f * 6.0f;
 
 // Eight values rounded to E2M1 codes in one register (byte i holds pair i; ties to the even
 // code, saturating at +-6, sign kept), by the gfx950 packed FP4 conversion with a unit scale.

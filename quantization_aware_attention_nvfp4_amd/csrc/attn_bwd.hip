@@ -310,7 +310,7 @@ __device__ __forceinline__ void dkdv_stage_tile(const BwdParams &p, const DkdvLa
 }
 
 // One 64-query tile for one wave (BUF: which tile buffer holds it).
-template <int BUF>
+template <int BUF, bool GP>
 __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, DkdvLane ln, int64_t qb, bool tail,
                                           f32x16 *dk, f32x16 *dv) {
   // LDS byte addresses; lds0 is 256-byte aligned, so the swizzle XORs act on the offsets alone.
@@ -347,7 +347,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
   const float w = __builtin_amdgcn_exp2f(mc - lse2);
   float ah[16], ds[16];
   if (p.quant_p) {
-    const ProbBlock pb = prob_block(bm, p.c, mc);
+    const ProbBlock pb = GP ? prob_block_static(bm, p.c, mc, kPScaleStatic) : prob_block(bm, p.c, mc);
     const float sw = pb.Sd * w, swD = sw * Di;  // A = r * Sd * w
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -355,8 +355,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
       ds[rr] = ah[rr] * __builtin_fmaf(sw, dp[rr], -swD);
     }
     const uint32_t c0 = e2m1_codes8(ah), c1 = e2m1_codes8(ah + 8);
-    e2m1_decode8(c0, pb.S * w, ah);
-    e2m1_decode8(c1, pb.S * w, ah + 8);
+    if (GP) {
+      // P-hat as the forward used it (rounded to bf16), then the normalisation
+      e2m1_decode8(c0, pb.S, ah);
+      e2m1_decode8(c1, pb.S, ah + 8);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) ah[rr] = bf16lo(f32_to_bf16_rne(ah[rr])) * w;
+    } else {
+      e2m1_decode8(c0, pb.S * w, ah);
+      e2m1_decode8(c1, pb.S * w, ah + 8);
+    }
   } else {
     const float wD = w * Di;
 #pragma unroll
@@ -397,7 +405,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
   }
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool GP>
 __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) uint8_t lds[kDkdvLds];
   const uint32_t lds0 = lds_addr(lds);
@@ -498,16 +506,16 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
     AQ_WAIT_VMCNT(0);  // this wave's copies of tile t
     __syncthreads();   // everyone's copies landed; buffer 1 is free
     dkdv_stage_tile(p, ln, bh, bb, hh, tile_cm(t + 1), tile_qb(t + 1), lds, 1, wave, lane);
-    dkdv_tile<0>(p, lds0, ln, tile_qb(t), tail, dk, dv);
+    dkdv_tile<0, GP>(p, lds0, ln, tile_qb(t), tail, dk, dv);
     AQ_WAIT_VMCNT(0);
     __syncthreads();  // buffer 0 is free
     if (t + 2 < ntiles) dkdv_stage_tile(p, ln, bh, bb, hh, tile_cm(t + 2), tile_qb(t + 2), lds, 0, wave, lane);
-    dkdv_tile<1>(p, lds0, ln, tile_qb(t + 1), tail, dk, dv);
+    dkdv_tile<1, GP>(p, lds0, ln, tile_qb(t + 1), tail, dk, dv);
   }
   if (t < ntiles) {
     AQ_WAIT_VMCNT(0);
     __syncthreads();
-    dkdv_tile<0>(p, lds0, ln, tile_qb(t), tail, dk, dv);
+    dkdv_tile<0, GP>(p, lds0, ln, tile_qb(t), tail, dk, dv);
   }
 
   // The two waves of a key group add their partial sums: wave qh = 0 finishes dK, qh = 1 dV.
@@ -566,13 +574,19 @@ __global__ __launch_bounds__(256) void vsa_slot_kernel(const int32_t *__restrict
 hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspace &w, const int32_t *sel,
                              const int16_t *slot_t, int64_t nsel, hipStream_t stream) {
   uint8_t *ws = (uint8_t *)a.workspace;
-  const TileQuant qd_q = (a.flags & 1u) ? kQuantD : kQuantNone;
-  const TileQuant qd_k = (a.flags & 2u) ? kQuantD : kQuantNone;
-  const TileQuant qr_v = (a.flags & 4u) ? kQuantRows : kQuantNone;
+  const TileQuant qd_q = (a.flags & kFlagQ) ? kQuantD : kQuantNone;
+  const TileQuant qd_k = (a.flags & kFlagK) ? kQuantD : kQuantNone;
+  const TileQuant qr_v = (a.flags & kFlagV) ? kQuantRows : kQuantNone;
   hipError_t e;
-  if ((e = launch_tile_prepass(a.q, a.sq, a.batch, a.heads, a.lq, qd_q, ws + w.qq, nullptr, stream))) return e;
-  if ((e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, qd_k, ws + w.kq, nullptr, stream))) return e;
-  if ((e = launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qr_v, ws + w.vq, nullptr, stream))) return e;
+  // The forward's operands again (same scales and smoothing, recomputed from the same tensors).
+  if ((e = launch_variant_prep(a, w, stream))) return e;
+  const VariantPtrs vp = variant_ptrs(a, w);
+  if ((e = launch_tile_prepass(a.q, a.sq, a.batch, a.heads, a.lq, qd_q, ws + w.qq, nullptr, vp.gq, nullptr, stream)))
+    return e;
+  if ((e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, qd_k, ws + w.kq, nullptr, vp.gk, vp.kmean, stream)))
+    return e;
+  if ((e = launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qr_v, ws + w.vq, nullptr, vp.gv, nullptr, stream)))
+    return e;
 
   const int64_t bh = (int64_t)a.batch * a.heads;
   const int64_t rows = bh * a.lq;
@@ -619,8 +633,11 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   p.nwork = bh * p.Ck;
   p.per_xcd = (p.nwork + 7) / 8;
   const dim3 dkdv_grid((unsigned)(p.per_xcd * 8));
-  if (sel) AQ_LAUNCH("vsa_bwd_dkdv", bwd_dkdv_kernel<true>, dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
-  else AQ_LAUNCH("bwd_dkdv", bwd_dkdv_kernel<false>, dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
+  const bool gp = p.quant_p && (a.flags & kFlagGsfP);
+  if (sel && gp) AQ_LAUNCH("vsa_bwd_dkdv", (bwd_dkdv_kernel<true, true>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
+  else if (sel) AQ_LAUNCH("vsa_bwd_dkdv", (bwd_dkdv_kernel<true, false>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
+  else if (gp) AQ_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<false, true>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
+  else AQ_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<false, false>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
   return hipGetLastError();
 }
 

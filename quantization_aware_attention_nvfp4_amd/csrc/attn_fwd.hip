@@ -58,6 +58,9 @@ struct FwdParams {
   int64_t per_xcd;   // ceil(nblocks / 8)
   float c;           // softmax_scale * log2(e)
   bool causal, quant_q;
+  const float *gq;      // static global scale of Q (device scalar), or null for the unit scale
+  const float *m_init;  // [BH, lq] final row maxima (base 2) seeding the running max, or null
+  float *m_out;         // row-max pass: where it writes them
 };
 
 // Copy offsets of this lane's 16-byte pieces of a staged [128][256 B] tile by a workgroup of
@@ -107,11 +110,30 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void load_q_frags(const FwdParams &p, int64_t bb, int64_t hh, int64_t qrow, bool qvalid,
                                              int hf, bf16x8 (&qf)[8]) {
   const uint16_t *qp = p.q + bb * p.sq.b + hh * p.sq.h + (qvalid ? qrow : 0) * p.sq.l;
+  const float g = p.gq ? *p.gq : 1.0f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (qvalid) v = *(const u32x4 *)(qp + 16 * t + 8 * hf);
-    if (p.quant_q) {
+    if (p.quant_q && p.gq) {
+      // static global scale: the IEEE quotient and the value rounded to bf16
+      float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                    bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
+      am = pair_max(am);
+      const float S = round_e4m3((am / 6.0f) * g) / g;
+      const bool zero = !(S > 0.0f);
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = zero ? 0.0f * f[2 * i] : fq_general(f[2 * i], S);
+        const float b = zero ? 0.0f * f[2 * i + 1] : fq_general(f[2 * i + 1], S);
+        w[i] = f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+      }
+      v = u32x4{w[0], w[1], w[2], w[3]};
+    } else if (p.quant_q) {
       float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
                     bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
       float am = 0.0f;
@@ -131,12 +153,14 @@ __device__ __forceinline__ void load_q_frags(const FwdParams &p, int64_t bb, int
 
 // P of one 32-key sub-tile, whose 16 logits in the lane's registers are one P block, as the two
 // P-hat V-hat B operands (keys 0-7 and 8-15 of the block); psum gains the block's unquantized sum.
-// HP: also the unquantized P as operands (ph), for O^hp.
-template <bool QP, bool F16, bool HP>
+// HP: also the unquantized P as operands (ph), for O^hp.  GP: P's blocks under the static global
+// scale (then F16 is off: P-hat is rounded to bf16).
+template <bool QP, bool F16, bool HP, bool GP>
 __device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, float m_new, float &psum, u32x4 (&pq)[2],
                                        u32x4 (&ph)[2]) {
+  static_assert(!(GP && F16), "P-hat under the static scale is not exact in fp16");
   if (QP) {
-    const ProbBlock pb = prob_block(bmax, c, m_new);
+    const ProbBlock pb = GP ? prob_block_static(bmax, c, m_new, kPScaleStatic) : prob_block(bmax, c, m_new);
     float r[16], rsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -196,7 +220,7 @@ __device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, flo
 //
 // QL selects the 8-wave layout.  The cube-sparse training forward keeps 4 waves (its chunk lists
 // are per 128 queries) and then runs one wave per SIMD.
-template <bool TRAIN, bool QP, bool F16, bool QL>
+template <bool TRAIN, bool QP, bool F16, bool QL, bool GP>
 __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   static_assert(!F16 || QP, "the fp16 product needs a quantized P");
   constexpr bool HP = TRAIN && QP;  // O^hp needs its own product only when P is quantized
@@ -264,7 +288,8 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 #pragma unroll
   for (int dt = 0; dt < (HP ? 4 : 1); ++dt) acc_hp[dt] = f32x16{};
-  float m_run = -__builtin_inff();
+  // Final-max variant: the running max starts at the row's final maximum, so it never moves.
+  float m_run = (p.m_init && qvalid) ? p.m_init[bh * p.lq + qrow] : -__builtin_inff();
   float l_run = 0.0f;
 
   // LDS byte addresses of this lane's A-operand reads.  The arrays are 256-byte aligned and a
@@ -367,7 +392,7 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       u32x4 pq[2], ph[2];
-      form_p<QP, F16, HP>(s[kt], bmax[kt], p.c, m_new, psum, pq, ph);
+      form_p<QP, F16, HP, GP>(s[kt], bmax[kt], p.c, m_new, psum, pq, ph);
       u32x4 a[2][4];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -446,7 +471,7 @@ constexpr uint32_t kPipeK = 0, kPipeV = 32768;  // LDS byte offsets
 __device__ __forceinline__ int sw_v64(int d) { return (d >> 2) & 3; }
 constexpr int kPipeAhead = 3, kPipeValu = 5;  // LDS reads issued ahead; VALU per MFMA in a step
 
-template <bool QP, bool F16>
+template <bool QP, bool F16, bool GP>
 __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) {
   constexpr int WAVES = kPipeWaves;
   constexpr int BM = 32 * WAVES;
@@ -527,7 +552,8 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-  float m_run = -__builtin_inff();
+  // Final-max variant: the running max starts at the row's final maximum, so it never moves.
+  float m_run = (p.m_init && qvalid) ? p.m_init[bh * p.lq + qrow] : -__builtin_inff();
   float l_run = 0.0f;
 
   // Prologue: S(0), then K-hat(1) into the K buffer.
@@ -579,7 +605,7 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
     const bool near_end = it + 2 >= n_iter;  // some copies are not issued: wait for all
     float psum = 0.0f;
     u32x4 pq[2][2], ph[2][2];
-    form_p<QP, F16, false>(s[0], bmax[0], p.c, m_new, psum, pq[0], ph[0]);
+    form_p<QP, F16, false, GP>(s[0], bmax[0], p.c, m_new, psum, pq[0], ph[0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -596,7 +622,7 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pq[kt & 1][j]), acc[dt], 0, 0, 0);
         }
       if (kt < 3) {
-        form_p<QP, F16, false>(s[kt + 1], bmax[kt + 1], p.c, m_new, psum, pq[(kt + 1) & 1], ph[(kt + 1) & 1]);
+        form_p<QP, F16, false, GP>(s[kt + 1], bmax[kt + 1], p.c, m_new, psum, pq[(kt + 1) & 1], ph[(kt + 1) & 1]);
         // Pinned here: otherwise the compiler sinks this work into the next step, beside its use.
         AQ_OPAQUE(pq[(kt + 1) & 1][0]);
         AQ_OPAQUE(pq[(kt + 1) & 1][1]);
@@ -641,15 +667,146 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// Row-max pass of the final-max variant
+// ------------------------------------------------------------------------------------------
+//
+// m_out[bh, q] = c * (the largest logit of row q over its keys: all of them, the causal prefix, or
+// the selected cubes), the statistics the reference-order reading relates every P to.  The logits
+// are formed with the forward kernels' MFMA arrangement (same operands, same accumulation order),
+// so the forward's chunk maxima are bitwise at most this value and its running max, seeded with
+// it, never moves.  4 waves of 32 queries per workgroup; K-hat chunks staged through LDS.
+__global__ __launch_bounds__(256, 2) void rowmax_kernel(FwdParams p) {
+  constexpr int WAVES = 4;
+  constexpr int BM = 32 * WAVES;
+  __shared__ __attribute__((aligned(256))) uint8_t lds_k[kChunk * 256];
+  __shared__ int32_t lds_sel[kMaxSel];
+
+  const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
+  if (vid < 0) return;
+  const int64_t bh = vid / p.qtiles;
+  const int qt = (int)(vid % p.qtiles);
+  const int64_t bb = bh / p.heads, hh = bh % p.heads;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, n = lane & 31, hf = lane >> 5;
+  const int64_t qrow = (int64_t)qt * BM + wave * 32 + n;
+  const bool qvalid = qrow < p.lq;
+
+  int64_t n_iter = p.nchunks;
+  if (p.causal) {
+    const int64_t q_last = (int64_t)qt * BM + BM - 1;
+    n_iter = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
+  }
+  if (p.sel) {
+    const int32_t *src = p.sel + (bh * (p.lq / kChunk) + (int64_t)qt * BM / kChunk) * p.nchunks;
+    for (int i = tid; i < p.nchunks; i += WAVES * 64) lds_sel[i] = src[i];
+    __syncthreads();
+  }
+  auto chunk_of = [&](int64_t it) -> int64_t {
+    return p.sel ? (int64_t)__builtin_amdgcn_readfirstlane(lds_sel[it]) : it;
+  };
+  auto ktile = [&](int64_t c) { return (const uint8_t *)(p.kq + (bh * p.kchunks + c) * (kChunk * kD / 8)); };
+  const StageOffsets so = stage_offsets<WAVES>(wave, lane);
+  int64_t chunk = chunk_of(0);
+  stage_k<WAVES>(ktile(chunk), lds_k, so, wave);
+
+  bf16x8 qf[8];
+  load_q_frags(p, bb, hh, qrow, qvalid, hf, qf);
+  uint32_t ka;
+  {
+    const int krow = perm_row(n), swk = sw_kq(krow);
+    ka = lds_addr(lds_k) + krow * 256 + 16 * (hf ^ swk);
+  }
+  float mx = -__builtin_inff();
+  for (int64_t it = 0; it < n_iter; ++it) {
+    AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    AQ_OPAQUE(ka);
+    f32x16 s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt] = f32x16{};
+#pragma unroll
+      for (int t0 = 0; t0 < 8; t0 += 4) {
+        bf16x8 a[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a[t] = as_bf16x8(lds_read16((ka ^ (32 * (t0 + t))) + 8192 * kt));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qf[t0 + t], s[kt], 0, 0, 0);
+      }
+    }
+    const int64_t next = it + 1 < n_iter ? chunk_of(it + 1) : -1;
+    __builtin_amdgcn_s_barrier();  // every wave is done reading K-hat(chunk)
+    if (next >= 0) stage_k<WAVES>(ktile(next), lds_k, so, wave);
+    const int64_t key0 = chunk * kChunk + 16 * hf;
+    const bool tail = (chunk + 1) * kChunk > p.lk;
+    const bool diag = p.causal && (chunk + 1) * kChunk - 1 > (int64_t)qt * BM + wave * 32;
+    if (tail || diag) {
+      const int64_t last = p.causal ? (qrow < p.lk - 1 ? qrow : p.lk - 1) : p.lk - 1;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) mask_tail(s[kt], valid_prefix(key0 + 32 * kt, last));
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    chunk = next;
+  }
+  mx = pair_max(mx);
+  if (qvalid && hf == 0) p.m_out[bh * p.lq + qrow] = mx * p.c;
+}
+
 }  // namespace
 
-// fp16 P-hat V-hat product: both operands fake-quantized.
-static bool use_f16(unsigned flags) { return (flags & 4u) && (flags & 8u); }
+// fp16 P-hat V-hat product: both operands fake-quantized under unit global scales (a static scale
+// makes the values inexact in fp16; they are rounded to bf16 instead).
+static bool use_f16(unsigned flags) {
+  return (flags & kFlagV) && (flags & kFlagP) && !(flags & (kFlagGsfQkv | kFlagGsfP));
+}
+
+// The forward kernel of a call, by its mode: training (QL layout for dense calls), pipelined dense
+// inference, or the unpipelined kernel (cube-sparse inference); qp / f16 / gp as in form_p.
+template <bool GP>
+static void launch_fwd_kernel(const FwdParams &p, dim3 grid, dim3 block, bool train, bool ql, bool pipe, bool qp,
+                              bool f16, const char *nm, const char *nm_train, hipStream_t stream) {
+  if (GP) {  // P quantized under the static scale: bf16 product
+    if (ql) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true, GP>), grid, block, 0, stream, p);
+    else if (train) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false, GP>), grid, block, 0, stream, p);
+    else if (pipe) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, false, GP>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false, GP>), grid, block, 0, stream, p);
+    return;
+  }
+  if (ql) {
+    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, true, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true, false>), grid, block, 0, stream, p);
+  } else if (train) {
+    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, false, false>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, false, false, false, false>), grid, block, 0, stream, p);
+  } else if (pipe) {
+    if (f16) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, true, false>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, false, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<false, false, false>), grid, block, 0, stream, p);
+  } else {
+    if (f16) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, true, false, false>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm, (attn_fwd_kernel<false, false, false, false, false>), grid, block, 0, stream, p);
+  }
+}
+
+// Workgroup tiling of a forward-type kernel with `waves` 32-query waves per workgroup.
+static void set_tiling(FwdParams &p, const AttnArgs &a, int waves) {
+  p.qtiles = (int)((a.lq + 32 * waves - 1) / (32 * waves));
+  p.nblocks = (int64_t)a.batch * a.heads * p.qtiles;
+  p.per_xcd = (p.nblocks + 7) / 8;
+}
 
 hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t nsel, hipStream_t stream) {
   constexpr int WAVES = 4;
   if (sel && (nsel > kMaxSel || nsel < 1)) return hipErrorInvalidValue;
-  const Workspace w = workspace_layout(0, a.batch, a.heads, a.lq, a.lk);
+  const Workspace w = workspace_layout(sel ? 2 : 0, a.batch, a.heads, a.lq, a.lk);
+  const VariantPtrs vp = variant_ptrs(a, w);
   uint8_t *ws = (uint8_t *)a.workspace;
   FwdParams p{};
   p.q = (const uint16_t *)a.q;
@@ -667,53 +824,54 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   p.lk = a.lk;
   p.kchunks = (a.lk + kChunk - 1) / kChunk;
   p.nchunks = sel ? nsel : p.kchunks;
-  const bool qp = (a.flags & 8u) != 0, f16 = use_f16(a.flags);
+  p.c = (float)((double)a.scale * 1.4426950408889634);
+  p.causal = a.causal;
+  p.quant_q = (a.flags & kFlagQ) != 0;
+  p.gq = vp.gq;
+  const bool qp = (a.flags & kFlagP) != 0, f16 = use_f16(a.flags), gp = qp && (a.flags & kFlagGsfP);
   // Training outputs come as a set (lse, chunk maxima, O^hp).
   const bool train = a.o_hp && a.lse && a.cmax;
   if (!train && (a.o_hp || a.lse || a.cmax)) return hipErrorInvalidValue;
+
+  if (a.flags & kFlagFinalMax) {
+    // Row maxima first; the forward's running max starts there.
+    FwdParams r = p;
+    r.m_out = (float *)(ws + w.mfin);
+    set_tiling(r, a, WAVES);
+    AQ_LAUNCH("rowmax", rowmax_kernel, dim3((unsigned)(r.per_xcd * 8)), dim3(WAVES * 64), 0, stream, r);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.m_init = r.m_out;
+  }
+
   const bool ql = train && qp && !sel;  // see attn_fwd_kernel
   const bool pipe = !train && !sel;     // attn_fwd_pipe_kernel
   const int waves = ql ? 8 : pipe ? kPipeWaves : WAVES;
-  p.qtiles = (int)((a.lq + 32 * waves - 1) / (32 * waves));
-  p.nblocks = (int64_t)a.batch * a.heads * p.qtiles;
-  p.per_xcd = (p.nblocks + 7) / 8;
-  p.c = (float)((double)a.scale * 1.4426950408889634);
-  p.causal = a.causal;
-  p.quant_q = (a.flags & 1u) != 0;
+  set_tiling(p, a, waves);
   const dim3 grid((unsigned)(p.per_xcd * 8)), block(waves * 64);
   const char *nm_train = sel ? "vsa_fwd_train" : "attn_fwd_train", *nm = sel ? "vsa_fwd" : "attn_fwd";
-  if (ql) {
-    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, true>), grid, block, 0, stream, p);
-    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true>), grid, block, 0, stream, p);
-  } else if (train) {
-    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, false>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, false, false, false>), grid, block, 0, stream, p);
-  } else if (pipe) {
-    if (f16) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, true>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<false, false>), grid, block, 0, stream, p);
-  } else {
-    if (f16) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, true, false>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH(nm, (attn_fwd_kernel<false, false, false, false>), grid, block, 0, stream, p);
-  }
+  if (gp) launch_fwd_kernel<true>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
+  else launch_fwd_kernel<false>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
   return hipGetLastError();
 }
 
-// K-hat rows and V-hat tiles for keys [0, lk) of every head into the forward workspace.
-hipError_t launch_kv_prepass(const AttnArgs &a, hipStream_t stream) {
-  const Workspace w = workspace_layout(0, a.batch, a.heads, a.lq, a.lk);
+// The variants' per-call quantities, then K-hat rows and V-hat tiles for keys [0, lk) of every
+// head, into the workspace of `op` (0: dense forward, 2: cube-sparse forward).
+hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream) {
+  const Workspace w = workspace_layout(op, a.batch, a.heads, a.lq, a.lk);
   uint8_t *ws = (uint8_t *)a.workspace;
-  hipError_t e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, (a.flags & 2u) ? kQuantD : kQuantNone,
-                                     ws + w.kq, nullptr, stream);
+  hipError_t e = launch_variant_prep(a, w, stream);
   if (e != hipSuccess) return e;
-  const TileQuant qv = use_f16(a.flags) ? kQuantRowsF16 : ((a.flags & 4u) ? kQuantRows : kQuantNone);
-  return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qv, nullptr, ws + w.vt, stream);
+  const VariantPtrs vp = variant_ptrs(a, w);
+  e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, (a.flags & kFlagK) ? kQuantD : kQuantNone, ws + w.kq,
+                          nullptr, vp.gk, vp.kmean, stream);
+  if (e != hipSuccess) return e;
+  const TileQuant qv = use_f16(a.flags) ? kQuantRowsF16 : ((a.flags & kFlagV) ? kQuantRows : kQuantNone);
+  return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qv, nullptr, ws + w.vt, vp.gv, nullptr, stream);
 }
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {
-  hipError_t e = launch_kv_prepass(a, stream);
+  hipError_t e = launch_kv_prepass(a, 0, stream);
   if (e != hipSuccess) return e;
   return launch_attn_fwd_sel(a, nullptr, 0, stream);
 }

@@ -12,6 +12,12 @@ constexpr int kHeadDimHost = 128;
 constexpr int kChunkHost = 128;
 constexpr int kMaxCubesHost = 4096;  // cube-sparse backward: longest per-key-cube list
 
+// Flag bits of a call (the ABI's AQ_* values): the four quantizers and the variants.
+constexpr unsigned kFlagQ = 1u, kFlagK = 2u, kFlagV = 4u, kFlagP = 8u;
+constexpr unsigned kFlagFinalMax = 16u, kFlagGsfQkv = 32u, kFlagGsfP = 64u, kFlagSmoothK = 128u;
+// Rows of the smooth-K partial sums: one per slab of this many keys.
+constexpr int kMeanSlab = 2048;
+
 struct Strides {
   int64_t b, h, l;
 };
@@ -53,8 +59,12 @@ struct VsaArgs {
 //                    selw [B*H, n, n] int32 (selection when the caller passes none)
 //   op 3 (cube-sparse backward): the op 1 regions, plus slot [B*H, n, n] int16 (position of every
 //                    key cube in every query cube's selection, or -1)
+//   every op: scal (global scales g_q, g_k, g_v, g_p as fp32, then three uint32 abs-max
+//                    accumulators), kmean [B*H, 128] fp32 (smooth-K key means), kpart
+//                    [B*H, ceil(lk / kMeanSlab), 128] fp64 (their partial sums)
+//   ops 0 and 2: mfin [B*H, lq] fp32 (final row maxima, base-2 units, for the final-max variant)
 struct Workspace {
-  size_t kq, vt, vq, qq, dvec, pool, selw, slot, total;
+  size_t kq, vt, vq, qq, dvec, pool, selw, slot, scal, kmean, kpart, mfin, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -88,6 +98,10 @@ inline Workspace workspace_layout(int op, int batch, int heads, int64_t lq, int6
     w.pool = take(3 * bh * n * kHeadDimHost * 2);
     w.selw = take(bh * n * n * 4);
   }
+  w.scal = take(256);
+  w.kmean = take(bh * kHeadDimHost * 4);
+  w.kpart = take(bh * (size_t)((lk + kMeanSlab - 1) / kMeanSlab) * kHeadDimHost * 8);
+  if (op == 0 || op == 2) w.mfin = take(bh * (size_t)lq * 4);
   w.total = off;
   return w;
 }
@@ -105,14 +119,27 @@ hipError_t launch_static_scale(const void *x, int64_t n, float *g_out, hipStream
 // One 128-row chunk of a strided [B, L, H, 128] bf16 tensor per workgroup: optional fake
 // quantization (kQuantNone, kQuantD along d per row, kQuantRows along rows per column; kQuantRowsF16
 // the same with fp16 output values), then a
-// row-major copy and/or a d-major tile copy into the workspace.
+// row-major copy and/or a d-major tile copy into the workspace.  g: device fp32 global scale, or
+// null for the unit scale; mean: [B*H, 128] fp32 subtracted per channel before quantization (the
+// smooth-K variant), or null.
 enum TileQuant { kQuantNone = 0, kQuantD = 1, kQuantRows = 2, kQuantRowsF16 = 3 };
 hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
-                               TileQuant quant, void *rows_out, void *tiles_out,
-                               hipStream_t stream);
+                               TileQuant quant, void *rows_out, void *tiles_out, const float *g,
+                               const float *mean, hipStream_t stream);
 
-// K-hat rows and V-hat tiles of every head into the forward workspace layout.
-hipError_t launch_kv_prepass(const AttnArgs &a, hipStream_t stream);
+// The per-call quantities of the variants, into the workspace regions scal / kmean / kpart: the
+// smooth-K key means (a.flags & kFlagSmoothK), then the static global scales of Q, K (of the
+// smoothed keys) and V (kFlagGsfQkv) and of P (kFlagGsfP).  A no-op without those flags.
+hipError_t launch_variant_prep(const AttnArgs &a, const Workspace &w, hipStream_t stream);
+// Pointers into those regions for a call's flags (null when the variant is off).
+struct VariantPtrs {
+  const float *gq, *gk, *gv, *gp, *kmean;
+};
+VariantPtrs variant_ptrs(const AttnArgs &a, const Workspace &w);
+
+// The variants' per-call quantities, then K-hat rows and V-hat tiles of every head into the
+// workspace of op 0 (dense forward) or 2 (cube-sparse forward).
+hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream);
 // Forward kernel only (operands already in the workspace); sel: cube-sparse chunk lists
 // [B*H, lq/128, nsel] or null for dense attention.
 hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t nsel, hipStream_t stream);

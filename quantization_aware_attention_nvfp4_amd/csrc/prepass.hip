@@ -9,6 +9,11 @@
 // kQuantRowsF16 writes the V-hat values as fp16 instead of bf16 (exact, see below) for the
 // forward's fp16 P-hat V-hat product.
 //
+// Variants (readings stated in variants.hip): a static global scale g (block scale
+// s = E4M3(fp32(fp32(amax / 6) * g)), S = fp32(s / g), value E2M1(fp32(|x| / S)) * S rounded to
+// bf16, as "nvfp4_qad.py" quantizes under input_global_sf), and the smooth-K mean subtracted in
+// fp32 before quantization (rows past L stay zero).
+//
 // One workgroup handles one 128-row chunk of one head: the chunk is staged in LDS as
 // [row][d] (rows past L read as zero), quantized in place, then written as
 //   rows_out  [B*H, C*128, 128]       row-major (the MFMA operand rows of the attention kernels)
@@ -22,10 +27,25 @@ namespace {
 
 constexpr int kD = kHeadDim;
 
+// Fake quantization of one 16-value block in place under the static global scale g; the values
+// come back rounded to bf16 (as fp32).
+__device__ __forceinline__ void fq_block_static(float (&f)[16], float g) {
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
+  const float sc = round_e4m3((am / 6.0f) * g);
+  const float S = sc / g;
+  const bool zero = !(S > 0.0f);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) f[i] = bf16lo(f32_to_bf16_rne(zero ? 0.0f * f[i] : fq_general(f[i], S)));
+}
+
 __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__ src, Strides s,
                                                     int heads, int64_t L, int64_t C, int quant,
                                                     u32x4 *__restrict__ rows_out,
-                                                    uint16_t *__restrict__ tiles_out) {
+                                                    uint16_t *__restrict__ tiles_out,
+                                                    const float *__restrict__ gptr,
+                                                    const float *__restrict__ mean) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kChunk][kD];
   const int64_t bh = blockIdx.x / C;
   const int64_t c = blockIdx.x % C;
@@ -42,13 +62,15 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
   }
   __syncthreads();
 
-  if (quant == kQuantD) {
+  const float g = gptr ? *gptr : 1.0f;
+  if (quant == kQuantD || (quant == kQuantNone && mean)) {
     // lane: row tid/2, d in [64*(tid&1), +64): four 16-element blocks
     const int row = tid >> 1, d0 = (tid & 1) * 64;
+    const bool live = c * kChunk + row < L;
+    const float *mrow = (mean && live) ? mean + bh * kD + d0 : nullptr;
     for (int blk = 0; blk < 4; ++blk) {
       u32x4 *p = (u32x4 *)&tile[row][d0 + 16 * blk];
       float f[16];
-      float am = 0.0f;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const u32x4 v = p[i];
@@ -57,16 +79,40 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
         f[8 * i + 4] = bf16lo(v.z); f[8 * i + 5] = bf16hi(v.z);
         f[8 * i + 6] = bf16lo(v.w); f[8 * i + 7] = bf16hi(v.w);
       }
+      if (mrow) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
-      const float S = block_scale_unit(am);
-      const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+        for (int i = 0; i < 16; ++i) f[i] = f[i] - mrow[16 * blk + i];
+      }
+      if (quant == kQuantD && !gptr) {
+        float am = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);
+        for (int i = 0; i < 16; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
+        const float S = block_scale_unit(am);
+        const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);  // exact in bf16
+      } else if (quant == kQuantD) {
+        fq_block_static(f, g);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f[i] = bf16lo(f32_to_bf16_rne(f[i]));  // smoothed, unquantized
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         p[i] = u32x4{pack_exact_bf16(f[8 * i], f[8 * i + 1]), pack_exact_bf16(f[8 * i + 2], f[8 * i + 3]),
                      pack_exact_bf16(f[8 * i + 4], f[8 * i + 5]), pack_exact_bf16(f[8 * i + 6], f[8 * i + 7])};
+    }
+    __syncthreads();
+  } else if ((quant == kQuantRows || quant == kQuantRowsF16) && gptr) {
+    // static global scale (bf16 values): lane column d = tid%128, rows [64*(tid/128), +64)
+    const int d = tid & (kD - 1), r0 = (tid >> 7) * 64;
+    for (int blk = 0; blk < 4; ++blk) {
+      float f[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) f[i] = bf16lo(tile[r0 + 16 * blk + i][d]);
+      fq_block_static(f, g);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tile[r0 + 16 * blk + i][d] = (uint16_t)(f2u(f[i]) >> 16);
     }
     __syncthreads();
   } else if (quant == kQuantRows || quant == kQuantRowsF16) {
@@ -119,13 +165,13 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
 }  // namespace
 
 hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
-                               TileQuant quant, void *rows_out, void *tiles_out,
-                               hipStream_t stream) {
+                               TileQuant quant, void *rows_out, void *tiles_out, const float *g,
+                               const float *mean, hipStream_t stream) {
   const int64_t C = (L + kChunk - 1) / kChunk;
   const int64_t blocks = (int64_t)batch * heads * C;
   AQ_LAUNCH("tile_prepass", tile_prepass, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t *)src, s, heads, L, C, (int)quant, (u32x4 *)rows_out,
-                     (uint16_t *)tiles_out);
+                     (uint16_t *)tiles_out, g, mean);
   return hipGetLastError();
 }
 

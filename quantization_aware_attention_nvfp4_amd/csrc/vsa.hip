@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void select_kernel(const uint16_t *__restrict_
 hipError_t launch_vsa_fwd(const AttnArgs &a, const VsaArgs &s, hipStream_t stream) {
   const Workspace w = workspace_layout(2, a.batch, a.heads, a.lq, a.lk);
   uint8_t *ws = (uint8_t *)a.workspace;
-  hipError_t e = launch_kv_prepass(a, stream);
+  hipError_t e = launch_kv_prepass(a, 2, stream);
   if (e != hipSuccess) return e;
   const int64_t n = s.n_cubes;
   const int64_t bhn = (int64_t)a.batch * a.heads * n;

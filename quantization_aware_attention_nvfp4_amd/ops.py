@@ -22,7 +22,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (AQ_QUANT_ALL, AQ_QUANT_K, AQ_QUANT_P, AQ_QUANT_Q, AQ_QUANT_V, aq_strides, check,
+from ._lib import (AQ_FINAL_MAX, AQ_FLAGS_ALL, AQ_GSF_P, AQ_GSF_QKV, AQ_QUANT_ALL, AQ_QUANT_K, AQ_QUANT_P,
+                   AQ_QUANT_Q, AQ_QUANT_V, AQ_SMOOTH_K, aq_strides, check,
                    load)
 
 HEAD_SIZE = 128
@@ -186,10 +187,10 @@ class _AttnQatTrain(torch.autograd.Function):
     estimator of the library (fake-quant Jacobians are the identity)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, is_causal, sm_scale):
-        o, aux = attn_qat_fwd(q, k, v, causal=is_causal, sm_scale=sm_scale, training=True)
+    def forward(ctx, q, k, v, is_causal, sm_scale, quant_flags):
+        o, aux = attn_qat_fwd(q, k, v, causal=is_causal, sm_scale=sm_scale, quant_flags=quant_flags, training=True)
         ctx.save_for_backward(q, k, v, aux["lse_log2"], aux["chunk_max_log2"], aux["o_hp"])
-        ctx.is_causal, ctx.sm_scale = is_causal, sm_scale
+        ctx.is_causal, ctx.sm_scale, ctx.quant_flags = is_causal, sm_scale, quant_flags
         return o
 
     @staticmethod
@@ -197,16 +198,18 @@ class _AttnQatTrain(torch.autograd.Function):
         q, k, v, lse, cmax, ohp = ctx.saved_tensors
         aux = {"lse_log2": lse, "chunk_max_log2": cmax, "o_hp": ohp}
         dq, dk, dv = attn_qat_bwd(q, k, v, aux, d_o.contiguous(), causal=ctx.is_causal,
-                                  sm_scale=ctx.sm_scale)
-        return dq, dk, dv, None, None
+                                  sm_scale=ctx.sm_scale, quant_flags=ctx.quant_flags)
+        return dq, dk, dv, None, None, None
 
 
 def attn_qat_train(q_BLHD: torch.Tensor, k_BLHD: torch.Tensor, v_BLHD: torch.Tensor,
-                   is_causal: bool = False, sm_scale: Optional[float] = None) -> torch.Tensor:
+                   is_causal: bool = False, sm_scale: Optional[float] = None,
+                   quant_flags: int = AQ_QUANT_ALL) -> torch.Tensor:
     """Fake-quant attention with the straight-through backward, [B, L, H, D] in and out
     ("attn_qat_train" page: attn_qat_train; the kernel reads the strided BLHD tensors
-    directly, so no permuted copies are made)."""
-    return _AttnQatTrain.apply(q_BLHD, k_BLHD, v_BLHD, bool(is_causal), sm_scale)
+    directly, so no permuted copies are made).  quant_flags: quantizers and variants
+    (AQ_* constants); the page's call is AQ_QUANT_ALL."""
+    return _AttnQatTrain.apply(q_BLHD, k_BLHD, v_BLHD, bool(is_causal), sm_scale, int(quant_flags))
 
 
 class AttnQatTrainImpl:
@@ -319,28 +322,32 @@ class _VsaQatTrain(torch.autograd.Function):
     estimator (vsa_qat_bwd)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, grid, cube, sparsity, sm_scale):
-        o, aux = vsa_qat_fwd(q, k, v, grid=grid, cube=cube, sparsity=sparsity, sm_scale=sm_scale, training=True)
+    def forward(ctx, q, k, v, grid, cube, sparsity, sm_scale, quant_flags):
+        o, aux = vsa_qat_fwd(q, k, v, grid=grid, cube=cube, sparsity=sparsity, sm_scale=sm_scale,
+                             quant_flags=quant_flags, training=True)
         ctx.save_for_backward(q, k, v, aux["sel"], aux["lse_log2"], aux["chunk_max_log2"], aux["o_hp"])
-        ctx.args = (grid, cube, sparsity, sm_scale)
+        ctx.args = (grid, cube, sparsity, sm_scale, quant_flags)
         return o
 
     @staticmethod
     def backward(ctx, d_o):
         q, k, v, sel, lse, cmax, ohp = ctx.saved_tensors
-        grid, cube, sparsity, sm_scale = ctx.args
+        grid, cube, sparsity, sm_scale, quant_flags = ctx.args
         aux = {"sel": sel, "lse_log2": lse, "chunk_max_log2": cmax, "o_hp": ohp}
         dq, dk, dv = vsa_qat_bwd(q, k, v, aux, d_o.contiguous(), grid=grid, cube=cube, sparsity=sparsity,
-                                 sm_scale=sm_scale)
-        return dq, dk, dv, None, None, None, None
+                                 sm_scale=sm_scale, quant_flags=quant_flags)
+        return dq, dk, dv, None, None, None, None, None
 
 
 def vsa_qat_train(q_BLHD: torch.Tensor, k_BLHD: torch.Tensor, v_BLHD: torch.Tensor, grid=(16, 28, 56),
-                  cube=(4, 4, 8), sparsity: float = 0.9, sm_scale: Optional[float] = None) -> torch.Tensor:
+                  cube=(4, 4, 8), sparsity: float = 0.9, sm_scale: Optional[float] = None,
+                  quant_flags: int = AQ_QUANT_ALL) -> torch.Tensor:
     """Cube-sparse fine stage with the straight-through backward, cube-major [B, L, H, D] in and out."""
-    return _VsaQatTrain.apply(q_BLHD, k_BLHD, v_BLHD, tuple(grid), tuple(cube), float(sparsity), sm_scale)
+    return _VsaQatTrain.apply(q_BLHD, k_BLHD, v_BLHD, tuple(grid), tuple(cube), float(sparsity), sm_scale,
+                              int(quant_flags))
 
 
-__all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "fq_nvfp4",
+__all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "AQ_FINAL_MAX", "AQ_GSF_QKV",
+           "AQ_GSF_P", "AQ_SMOOTH_K", "AQ_FLAGS_ALL", "fq_nvfp4",
            "static_global_scale", "attn_qat_fwd", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
            "vsa_qat_fwd", "vsa_qat_bwd", "vsa_qat_train", "vsa_topk"]
