@@ -20,7 +20,8 @@ cube-sparse forward 4*B*H*n*k*128^2*D for its fine stage plus 4*B*H*n^2*D for
 its coarse stage, and its backward 2.5x the fine stage; fq contributes time but
 no FLOP.  After the step loop, the dense and cube-sparse inference forwards and
 fq on its own (back-to-back launches) are timed for the "attention" and "fq"
-objects.  Per-kernel durations come
+objects, and the attention variants (final-max statistics, static scales,
+smooth-K) for the "variants" object.  Per-kernel durations come
 from HIP events the library records around each of its launches on the launch
 stream while kernel timing is on (aq_kernel_timing).
 
@@ -259,6 +260,34 @@ def main():
     torch.cuda.synchronize()
     fwd_inf_ms = iev[0].elapsed_time(iev[1]) / 5
 
+    # The attention variants (include/attnqat.h flag bits) on the same workload: the inference
+    # forward under each, and the training forward + backward under all of them together.
+    def timed(fn, reps=3):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    fl_fwd = fl["fwd"]  # conventional 4*B*H*L^2*D (the final-max row-maximum pass is not counted)
+    variants = {}
+    for name, flg in (("final_max", 15 | 16), ("gsf_qkv", 15 | 32), ("gsf_p", 15 | 64), ("smooth_k", 15 | 128),
+                      ("all", 255)):
+        ms = timed(lambda: m.attn_qat_fwd(qd, kd, vd, quant_flags=flg))
+        variants[name] = {"flags": flg, "inference_fwd_ms": round(ms, 4),
+                          "inference_fwd_TFLOP/s": round(fl_fwd / (ms * 1e-3) / 1e12, 1)}
+
+    def train_all():
+        o, aux = m.attn_qat_fwd(qd, kd, vd, training=True, quant_flags=255)
+        m.attn_qat_bwd(qd, kd, vd, aux, dod, quant_flags=255)
+
+    ms = timed(train_all, 2)
+    variants["all"]["fwd_bwd_ms"] = round(ms, 4)
+    variants["all"]["fwd_bwd_TFLOP/s"] = round((fl["fwd"] + fl["bwd"]) / (ms * 1e-3) / 1e12, 1)
+
     # fq on its own: 40 back-to-back launches over the 4 rotating pairs between one pair of events
     # (a per-launch event pair adds about a microsecond to a 26 us kernel).
     fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -342,7 +371,7 @@ def main():
                    "B": B, "H": H, "L": L, "D": D, "causal": False, "quant": "Q,K,V,P NVFP4 unit scale",
                    "vsa_cubes": fl["cubes"], "vsa_topk": fl["topk"], "fq_shape": list(xs[0].shape)},
         "roofline": roofline, "cpu_baseline": cpu, "attention": attn, "fq": fq,
-        "phases_ms": {p: round(t, 4) for p, t in phase_ms.items()}, "kernels": kernels,
+        "phases_ms": {p: round(t, 4) for p, t in phase_ms.items()}, "kernels": kernels, "variants": variants,
     }
     print(json.dumps(out), flush=True)
 

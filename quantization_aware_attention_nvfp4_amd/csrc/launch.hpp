@@ -16,7 +16,7 @@ constexpr int kMaxCubesHost = 4096;  // cube-sparse backward: longest per-key-cu
 constexpr unsigned kFlagQ = 1u, kFlagK = 2u, kFlagV = 4u, kFlagP = 8u;
 constexpr unsigned kFlagFinalMax = 16u, kFlagGsfQkv = 32u, kFlagGsfP = 64u, kFlagSmoothK = 128u;
 // Rows of the smooth-K partial sums: one per slab of this many keys.
-constexpr int kMeanSlab = 2048;
+constexpr int kMeanSlab = 256;
 
 struct Strides {
   int64_t b, h, l;

@@ -29,22 +29,34 @@ __global__ __launch_bounds__(64) void fill_u32_kernel(uint32_t *__restrict__ p, 
 }
 
 // Partial sums of one slab of kMeanSlab keys of one head: part[(bh, slab), d] = sum over the
-// slab's keys of k[b, l, h, d] in fp64.  Lanes t and t + 128 share channel d and take alternate
-// keys; their two sums are added in that order.
+// slab's keys of k[b, l, h, d] in fp64.  Lane t reads 8 channels (one 16-byte load) of every 16th
+// key of the slab, starting at key t/16; the 16 lanes that share a channel group are then added
+// in key-group order through LDS.
 __global__ __launch_bounds__(256) void kmean_partial_kernel(const uint16_t *__restrict__ k, Strides s, int heads,
                                                             int64_t L, int nslab, double *__restrict__ part) {
-  __shared__ double half1[kD];
+  __shared__ double acc_lds[16][kD];
   const int64_t bh = blockIdx.x / nslab;
   const int slab = (int)(blockIdx.x % nslab);
   const int64_t b = bh / heads, h = bh % heads;
-  const int d = threadIdx.x & (kD - 1), sub = threadIdx.x >> 7;
+  const int grp = threadIdx.x & 15, sub = threadIdx.x >> 4;
   const int64_t l0 = (int64_t)slab * kMeanSlab, l1 = l0 + kMeanSlab < L ? l0 + kMeanSlab : L;
-  const uint16_t *base = k + b * s.b + h * s.h + d;
-  double acc = 0.0;
-  for (int64_t l = l0 + sub; l < l1; l += 2) acc += (double)bf16lo(base[l * s.l]);
-  if (sub) half1[d] = acc;
+  const uint16_t *base = k + b * s.b + h * s.h + 8 * grp;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t l = l0 + sub; l < l1; l += 16) {
+    const u32x4 v = *(const u32x4 *)(base + l * s.l);
+    acc[0] += (double)bf16lo(v.x); acc[1] += (double)bf16hi(v.x);
+    acc[2] += (double)bf16lo(v.y); acc[3] += (double)bf16hi(v.y);
+    acc[4] += (double)bf16lo(v.z); acc[5] += (double)bf16hi(v.z);
+    acc[6] += (double)bf16lo(v.w); acc[7] += (double)bf16hi(v.w);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc_lds[sub][8 * grp + j] = acc[j];
   __syncthreads();
-  if (!sub) part[(bh * nslab + slab) * kD + d] = acc + half1[d];
+  if (threadIdx.x < kD) {
+    double t = 0.0;
+    for (int i = 0; i < 16; ++i) t += acc_lds[i][threadIdx.x];
+    part[(bh * nslab + slab) * kD + threadIdx.x] = t;
+  }
 }
 
 // mean[bh, d] = fp32(sum of the slabs' partial sums, in slab order, / L).
