@@ -90,6 +90,12 @@ def _load():
             lib.oracle_vsa_bwd.argtypes = [P, P, P, P, i32, i32, i64, i32, i32, f64, f64, u32, P, i64, P, i64,
                                            P, P, P, P]
             lib.oracle_vsa_bwd.restype = i32
+            lib.oracle_linear_fwd.argtypes = [P, P, P, i64, i64, i64, f32, P]
+            lib.oracle_linear_fwd.restype = None
+            lib.oracle_linear_bwd.argtypes = [P, P, P, i64, i64, i64, P, P, P]
+            lib.oracle_linear_bwd.restype = None
+            lib.oracle_observe_amax.argtypes = [P, i64, f32]
+            lib.oracle_observe_amax.restype = f32
             _lib = lib
     return _lib
 
@@ -283,3 +289,35 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     u = u + 0x7FFF + ((u >> 16) & 1)
     return (u >> 16).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# NVFP4 QAD linear ("nvfp4_qad.py": nvfp4_gemm, _NVFP4STE, calibration)
+# ----------------------------------------------------------------------------
+
+def linear_fwd(x, w, bias=None, gx: float = 1.0) -> np.ndarray:
+    """y = fq(x, gx) @ fq(w, 448*6/amax|w|)^T + bias, fp64 [M, N].  x: [M, K], w: [N, K],
+    bias: [N] (bf16 bits); gx = 1.0 is the unit activation scale."""
+    x, w = _u16(x), _u16(w)
+    M, K = x.shape
+    N = w.shape[0]
+    b = None if bias is None else _u16(bias)
+    y = np.empty((M, N))
+    _load().oracle_linear_fwd(_ptr(x), _ptr(w), _ptr(b), M, N, K, float(gx), _ptr(y))
+    return y
+
+
+def linear_bwd(g, x, w):
+    """Full-precision straight-through gradients: gx = g @ w, gw = g^T @ x, gb = sum_m g (fp64)."""
+    g, x, w = _u16(g), _u16(x), _u16(w)
+    M, N = g.shape
+    K = x.shape[1]
+    gx, gw, gb = np.empty((M, K)), np.empty((N, K)), np.empty(N)
+    _load().oracle_linear_bwd(_ptr(g), _ptr(x), _ptr(w), M, N, K, _ptr(gx), _ptr(gw), _ptr(gb))
+    return {"gx": gx, "gw": gw, "gb": gb}
+
+
+def observe_amax(x, prev: float = 0.0) -> float:
+    """max(prev, amax|x|): one calibrating forward's update of the observed maximum."""
+    x = _u16(x)
+    return _load().oracle_observe_amax(_ptr(x), x.size, float(prev))

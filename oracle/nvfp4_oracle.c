@@ -911,3 +911,86 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
     free(sl);
     return topk;
 }
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4 QAD linear.  ["nvfp4_qad.py"] module docstring and nvfp4_gemm: the    */
+/* weight is RTN NVFP4 under g_w = 448*6 / amax(|W|) (weight_global_sf), the   */
+/* activation per-16 E4M3 blocks under a unit or static global scale          */
+/* (input_global_sf), blocks along the input features (the contraction axis); */
+/* the product of the dequantized operands plus the bias.  _NVFP4STE backward: */
+/* full-precision grad_x = grad @ W, grad_w = grad^T @ x, grad_b = sum grad.  */
+/* Reading: the operands of the (BF16) matmul are the dequantized values      */
+/* rounded to bf16 (as fq_nvfp4 outputs them); sums are fp64.                 */
+/* ------------------------------------------------------------------------ */
+
+/* y [M, N] fp64 = fq(x, gx) [M, K] . fq(w, g_w) [N, K]^T + bias, with
+   g_w = oracle_static_scale_bf16(w).  bias may be NULL.  gx = 1: unit scale. */
+void oracle_linear_fwd(const uint16_t *x, const uint16_t *w, const uint16_t *bias, int64_t M, int64_t N,
+                       int64_t K, float gx, double *y)
+{
+    init_tables();
+    uint16_t *xq = (uint16_t *)malloc(2 * M * K), *wq = (uint16_t *)malloc(2 * N * K);
+    oracle_fq_bf16(x, xq, M, K, 1, gx);
+    oracle_fq_bf16(w, wq, N, K, 1, oracle_static_scale_bf16(w, N * K));
+    float *xf = (float *)malloc(sizeof(float) * M * K), *wf = (float *)malloc(sizeof(float) * N * K);
+    for (int64_t i = 0; i < M * K; ++i) xf[i] = bf16_to_f32(xq[i]);
+    for (int64_t i = 0; i < N * K; ++i) wf[i] = bf16_to_f32(wq[i]);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = bias ? (double)bf16_to_f32(bias[n]) : 0.0;
+            for (int64_t k = 0; k < K; ++k) s += (double)xf[m * K + k] * (double)wf[n * K + k];
+            y[m * N + n] = s;
+        }
+    free(xq);
+    free(wq);
+    free(xf);
+    free(wf);
+}
+
+/* Straight-through backward of the linear: gx [M, K] = g [M, N] . w [N, K],
+   gw [N, K] = g^T . x, gb [N] = column sums of g (any output may be NULL).
+   Inputs bf16, outputs fp64. */
+void oracle_linear_bwd(const uint16_t *g, const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, int64_t K,
+                       double *gx, double *gw, double *gb)
+{
+    if (gx) {
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t k = 0; k < K; ++k) {
+                double s = 0.0;
+                for (int64_t n = 0; n < N; ++n) s += (double)bf16_to_f32(g[m * N + n]) * (double)bf16_to_f32(w[n * K + k]);
+                gx[m * K + k] = s;
+            }
+    }
+    if (gw) {
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t k = 0; k < K; ++k) {
+                double s = 0.0;
+                for (int64_t m = 0; m < M; ++m) s += (double)bf16_to_f32(g[m * N + n]) * (double)bf16_to_f32(x[m * K + k]);
+                gw[n * K + k] = s;
+            }
+    }
+    if (gb) {
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; ++m) s += (double)bf16_to_f32(g[m * N + n]);
+            gb[n] = s;
+        }
+    }
+}
+
+/* Max calibration ["nvfp4_qad.py"] NVFP4QADLinearMethod.apply while calibrating:
+   the running maximum folds in amax(|x|) of every input.  Returns
+   max(prev, amax|x|) (NaN inputs count as 0, as the static-scale formula's nan_to_num). */
+float oracle_observe_amax(const uint16_t *x, int64_t n, float prev)
+{
+    float amax = prev;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = fabsf(bf16_to_f32(x[i]));
+        if (isnan(v)) v = 0.0f;
+        if (v > amax) amax = v;
+    }
+    return amax;
+}
