@@ -236,6 +236,34 @@ int vsa_topk(double sparsity, int n_cubes);
 size_t attn_qat_workspace_size(int op, int batch, int num_heads, int64_t lq, int64_t lk);
 
 /* ---------------------------------------------------------------------------------------------
+ * NVFP4 QAD linear (["nvfp4_qad.py"] nvfp4_gemm, _NVFP4STE, NVFP4QADLinearMethod.apply).
+ *
+ * qad_linear_fwd: y [m, n] = fq(x, g_x) [m, k] . fq(w, g_w) [n, k]^T + bias [n], bf16 row-major
+ *   contiguous.  g_w = 448*6 / max(amax|w|, 1e-12) (weight_global_sf), computed on the device on
+ *   every call; g_x = *input_sf (a DEVICE fp32 scalar, the static input_global_sf
+ *   448*6 / calibrated amax) or 1 when input_sf is NULL (the unit scale of the attention
+ *   projections).  Blocks of 16 along k, E4M3 block scales, E2M1 values, dequantized and rounded
+ *   to bf16 (as fq_nvfp4 outputs them); the product runs on BF16 MFMA with fp32 accumulation and
+ *   the bias is added before the bf16 rounding.  bias may be NULL.
+ * qad_linear_bwd: the straight-through estimator's full-precision gradients: grad_x [m, k] =
+ *   grad_y [m, n] . w, grad_w [n, k] = grad_y^T . x, grad_b [n] = column sums of grad_y, bf16
+ *   (fp32 accumulation).  Any output may be NULL to skip it.
+ * qad_observe_amax: *amax = max(*amax, max|x|) over numel bf16 values (max calibration; *amax is a
+ *   DEVICE fp32 scalar the caller zeroes before the first calibrating call).
+ * Workspace: qad_linear_workspace_size(0 = forward, 1 = backward, m, n, k) bytes of DEVICE memory
+ *   (any alignment).
+ * Errors: AQ_EINVAL (null pointers, non-positive sizes, tensors not 16-byte aligned, workspace too
+ *   small); AQ_ENOTSUP (k or n not a multiple of 64, rows too long for the kernels' 32-bit tile
+ *   offsets).
+ * ------------------------------------------------------------------------------------------- */
+size_t qad_linear_workspace_size(int op, int64_t m, int64_t n, int64_t k);
+int qad_linear_fwd(const void *x, const void *w, const void *bias, void *y, int64_t m, int64_t n, int64_t k,
+                   const float *input_sf, void *workspace, size_t workspace_bytes, void *stream);
+int qad_linear_bwd(const void *grad_y, const void *x, const void *w, void *grad_x, void *grad_w, void *grad_b,
+                   int64_t m, int64_t n, int64_t k, void *workspace, size_t workspace_bytes, void *stream);
+int qad_observe_amax(const void *x, int64_t numel, float *amax, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Kernel timing (profiling aid, not part of the method).
  * aq_kernel_timing(1) makes every later kernel launch of the library, on any stream, record a
  * HIP event before and after the kernel on that stream; aq_kernel_timing(0) stops it.

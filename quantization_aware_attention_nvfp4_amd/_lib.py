@@ -22,7 +22,7 @@ AQ_FLAGS_ALL = 255
 
 EXPORTED = ("aq_last_error", "fq_nvfp4", "fq_nvfp4_static_scale", "attn_qat_fwd", "attn_qat_bwd",
             "vsa_qat_fwd", "vsa_qat_bwd", "vsa_topk", "attn_qat_workspace_size", "aq_kernel_timing",
-            "aq_kernel_times")
+            "aq_kernel_times", "qad_linear_workspace_size", "qad_linear_fwd", "qad_linear_bwd", "qad_observe_amax")
 
 
 class aq_strides(ctypes.Structure):
@@ -63,6 +63,14 @@ def _declare(lib):
     lib.aq_kernel_timing.restype = i32
     lib.aq_kernel_times.argtypes = [ctypes.c_char_p, sz, i32]
     lib.aq_kernel_times.restype = i32
+    lib.qad_linear_workspace_size.argtypes = [i32, i64, i64, i64]
+    lib.qad_linear_workspace_size.restype = sz
+    lib.qad_linear_fwd.argtypes = [P, P, P, P, i64, i64, i64, P, P, sz, P]
+    lib.qad_linear_fwd.restype = i32
+    lib.qad_linear_bwd.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, sz, P]
+    lib.qad_linear_bwd.restype = i32
+    lib.qad_observe_amax.argtypes = [P, i64, P, P]
+    lib.qad_observe_amax.restype = i32
 
 
 def load():

@@ -277,4 +277,87 @@ int vsa_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp, 
                     "vsa_qat_bwd launch");
 }
 
+// ---- NVFP4 QAD linear ---------------------------------------------------------------------------
+
+// Shapes the GEMM kernel takes: contractions over k (forward) and n (grad_x) in steps of 64,
+// 16-byte aligned contiguous rows, 32-bit row offsets inside one 256-row tile.
+static int check_linear(const char *what, int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0)
+    return fail(AQ_EINVAL, "%s: sizes must be positive (m %lld, n %lld, k %lld)", what, (long long)m,
+                (long long)n, (long long)k);
+  if (k % 64 || n % 64)
+    return fail(AQ_ENOTSUP, "%s: in_features (%lld) and out_features (%lld) must be multiples of 64", what,
+                (long long)k, (long long)n);
+  const int64_t mp = (m + 63) / 64 * 64;
+  if (256 * (k > n ? k : n) * 2 >= ((int64_t)1 << 32) || 256 * mp * 2 >= ((int64_t)1 << 32))
+    return fail(AQ_ENOTSUP, "%s: rows too long for 32-bit tile offsets", what);
+  return AQ_OK;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+size_t qad_linear_workspace_size(int op, int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || op < 0 || op > 1) return 0;
+  return aq::linear_workspace(op, m, n, k).total + 256;
+}
+
+int qad_linear_fwd(const void *x, const void *w, const void *bias, void *y, int64_t m, int64_t n, int64_t k,
+                   const float *input_sf, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!x || !w || !y || !workspace) return fail(AQ_EINVAL, "qad_linear_fwd: null pointer");
+  int rc = check_linear("qad_linear_fwd", m, n, k);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias)))
+    return fail(AQ_EINVAL, "qad_linear_fwd: tensors must be 16-byte aligned");
+  const aq::LinearWorkspace lw = aq::linear_workspace(0, m, n, k);
+  uint8_t *ws = (uint8_t *)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  if ((size_t)(ws - (uint8_t *)workspace) + lw.total > workspace_bytes)
+    return fail(AQ_EINVAL, "qad_linear_fwd: workspace of %zu bytes is too small (need %zu)", workspace_bytes,
+                qad_linear_workspace_size(0, m, n, k));
+  hipStream_t st = (hipStream_t)stream;
+  float *gw = (float *)(ws + lw.gw);
+  hipError_t e;
+  if ((e = aq::launch_static_scale(w, n * k, gw, st))) return hip_status(e, "qad_linear_fwd weight scale");
+  if ((e = aq::launch_fq(w, ws + lw.wq, n, k, 1, gw, st))) return hip_status(e, "qad_linear_fwd weight");
+  if ((e = aq::launch_fq(x, ws + lw.xq, m, k, 1, input_sf, st))) return hip_status(e, "qad_linear_fwd input");
+  return hip_status(aq::launch_gemm_tn(ws + lw.xq, k, ws + lw.wq, k, y, n, bias, m, n, k, st), "qad_linear_fwd gemm");
+}
+
+int qad_linear_bwd(const void *grad_y, const void *x, const void *w, void *grad_x, void *grad_w, void *grad_b,
+                   int64_t m, int64_t n, int64_t k, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!grad_y || !x || !w || !workspace) return fail(AQ_EINVAL, "qad_linear_bwd: null pointer");
+  int rc = check_linear("qad_linear_bwd", m, n, k);
+  if (rc) return rc;
+  if (!aligned16(grad_y) || !aligned16(x) || !aligned16(w) || (grad_x && !aligned16(grad_x)) ||
+      (grad_w && !aligned16(grad_w)) || (grad_b && !aligned16(grad_b)))
+    return fail(AQ_EINVAL, "qad_linear_bwd: tensors must be 16-byte aligned");
+  const aq::LinearWorkspace lw = aq::linear_workspace(1, m, n, k);
+  uint8_t *ws = (uint8_t *)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  if ((size_t)(ws - (uint8_t *)workspace) + lw.total > workspace_bytes)
+    return fail(AQ_EINVAL, "qad_linear_bwd: workspace of %zu bytes is too small (need %zu)", workspace_bytes,
+                qad_linear_workspace_size(1, m, n, k));
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t mp = (m + 63) / 64 * 64;
+  hipError_t e;
+  if (grad_x) {
+    if ((e = aq::launch_transpose(w, k, n, k, ws + lw.wt, n, st))) return hip_status(e, "qad_linear_bwd W^T");
+    if ((e = aq::launch_gemm_tn(grad_y, n, ws + lw.wt, n, grad_x, k, nullptr, m, k, n, st)))
+      return hip_status(e, "qad_linear_bwd grad_x");
+  }
+  if (grad_w) {
+    if ((e = aq::launch_transpose(grad_y, n, m, n, ws + lw.gt, mp, st))) return hip_status(e, "qad_linear_bwd g^T");
+    if ((e = aq::launch_transpose(x, k, m, k, ws + lw.xt, mp, st))) return hip_status(e, "qad_linear_bwd x^T");
+    if ((e = aq::launch_gemm_tn(ws + lw.gt, mp, ws + lw.xt, mp, grad_w, k, nullptr, n, k, mp, st)))
+      return hip_status(e, "qad_linear_bwd grad_w");
+  }
+  if (grad_b)
+    return hip_status(aq::launch_colsum(grad_y, m, n, grad_b, (float *)(ws + lw.part), st), "qad_linear_bwd grad_b");
+  return ok();
+}
+
+int qad_observe_amax(const void *x, int64_t numel, float *amax, void *stream) {
+  if (!x || !amax) return fail(AQ_EINVAL, "qad_observe_amax: null pointer");
+  if (numel <= 0) return fail(AQ_EINVAL, "qad_observe_amax: numel must be positive");
+  return hip_status(aq::launch_observe_amax(x, numel, amax, (hipStream_t)stream), "qad_observe_amax launch");
+}
+
 }  // extern "C"

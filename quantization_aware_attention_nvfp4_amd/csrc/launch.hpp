@@ -151,4 +151,47 @@ hipError_t launch_vsa_fwd(const AttnArgs &a, const VsaArgs &s, hipStream_t strea
 hipError_t launch_vsa_bwd(const AttnArgs &a, const BwdArgs &b, const int32_t *sel, int n_cubes, int topk,
                           hipStream_t stream);
 
+// ---- NVFP4 QAD linear (linear.hip) ----
+// C[P][Q] = sum_k L[p][k] R[q][k] (+ bias[q]); bf16, k contiguous, K a multiple of 64, row strides
+// in elements.
+hipError_t launch_gemm_tn(const void *L, int64_t ldl, const void *R, int64_t ldr, void *C, int64_t ldc,
+                          const void *bias, int64_t P, int64_t Q, int64_t K, hipStream_t stream);
+// out [C][Rp] = in [R][C]^T with rows r >= R of the result's columns zero.
+hipError_t launch_transpose(const void *in, int64_t ldi, int64_t R, int64_t C, void *out, int64_t Rp,
+                            hipStream_t stream);
+// gb [N] = bf16 column sums of g [M][N]; part: colsum_chunks(M) * N fp32 of scratch.
+hipError_t launch_colsum(const void *g, int64_t M, int64_t N, void *gb, float *part, hipStream_t stream);
+int64_t colsum_chunks(int64_t M);
+// *amax = max(*amax, max|x|) over n bf16 values.
+hipError_t launch_observe_amax(const void *x, int64_t n, float *amax, hipStream_t stream);
+
+// Workspace of the linear: op 0 (forward) x-hat [M, K] and W-hat [N, K] bf16, the weight's global
+// scale; op 1 (backward) W^T [K, N], grad^T [N, Mp], x^T [K, Mp] bf16 (Mp = M rounded up to 64)
+// and the column-sum partials.
+struct LinearWorkspace {
+  size_t xq, wq, gw, wt, gt, xt, part, total;
+};
+inline LinearWorkspace linear_workspace(int op, int64_t m, int64_t n, int64_t k) {
+  LinearWorkspace w{};
+  size_t off = 0;
+  auto take = [&off](size_t b) {
+    const size_t at = off;
+    off = align256(off + b);
+    return at;
+  };
+  const size_t mp = (size_t)((m + 63) / 64 * 64);
+  if (op == 0) {
+    w.xq = take((size_t)m * k * 2);
+    w.wq = take((size_t)n * k * 2);
+    w.gw = take(256);
+  } else {
+    w.wt = take((size_t)k * n * 2);
+    w.gt = take((size_t)n * mp * 2);
+    w.xt = take((size_t)k * mp * 2);
+    w.part = take((size_t)colsum_chunks(m) * n * 4);
+  }
+  w.total = off;
+  return w;
+}
+
 }  // namespace aq

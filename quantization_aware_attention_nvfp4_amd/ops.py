@@ -347,7 +347,145 @@ def vsa_qat_train(q_BLHD: torch.Tensor, k_BLHD: torch.Tensor, v_BLHD: torch.Tens
                               int(quant_flags))
 
 
+# ----------------------------------------------------------------------------------------------
+# NVFP4 QAD linear ("nvfp4_qad.py": nvfp4_gemm, _NVFP4STE, NVFP4QADLinearMethod)
+# ----------------------------------------------------------------------------------------------
+
+FP4_RANGE = 448.0 * 6.0
+
+
+def _linear_ws(op: int, m: int, n: int, k: int, device) -> torch.Tensor:
+    return torch.empty(load().qad_linear_workspace_size(op, m, n, k), dtype=torch.uint8, device=device)
+
+
+def _rows(x: torch.Tensor, k: int) -> torch.Tensor:
+    if x.shape[-1] != k:
+        raise ValueError(f"last dimension {x.shape[-1]} != in_features {k}")
+    return x.reshape(-1, k).contiguous()
+
+
+def input_global_sf(amax: float, device) -> torch.Tensor:
+    """The static activation scale 448*6 / max(amax, 1e-12) as a device fp32 scalar (input_global_sf)."""
+    if not amax > 0:
+        raise ValueError(f"calibrated amax must be positive, got {amax}")
+    return torch.tensor(FP4_RANGE / max(float(amax), 1e-12), dtype=torch.float32, device=device)
+
+
+def qad_linear_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                   input_sf: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = fq(x, input_sf) fq(weight, 448*6/amax|weight|)^T + bias (nvfp4_gemm on the fake-quant +
+    BF16 MFMA path).  x [..., k], weight [n, k], bias [n]: bf16 on the device; input_sf: device fp32
+    scalar (static scale) or None (unit scale)."""
+    for name, t in (("x", x), ("weight", weight)):
+        _require_bf16_cuda(name, t)
+    n, k = weight.shape
+    x2 = _rows(x, k)
+    w = weight.contiguous()
+    b = None
+    if bias is not None:
+        _require_bf16_cuda("bias", bias)
+        b = bias.contiguous()
+    if input_sf is not None and (input_sf.dtype != torch.float32 or not input_sf.is_cuda or input_sf.numel() != 1):
+        raise ValueError("input_sf must be a one-element fp32 device tensor")
+    m = x2.shape[0]
+    y = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
+    ws = _linear_ws(0, m, n, k, x.device)
+    check(load().qad_linear_fwd(x2.data_ptr(), w.data_ptr(), None if b is None else b.data_ptr(), y.data_ptr(), m,
+                                n, k, None if input_sf is None else input_sf.data_ptr(), ws.data_ptr(), ws.numel(),
+                                _stream_ptr(x)), "qad_linear_fwd")
+    return y.view(*x.shape[:-1], n)
+
+
+def qad_linear_bwd(grad_y: torch.Tensor, x: torch.Tensor, weight: torch.Tensor, need_bias: bool = True):
+    """Full-precision straight-through gradients (_NVFP4STE.backward): grad_x = grad_y W,
+    grad_w = grad_y^T x, grad_b = column sums of grad_y."""
+    n, k = weight.shape
+    g2 = grad_y.reshape(-1, n).contiguous()
+    x2 = _rows(x, k)
+    m = x2.shape[0]
+    gx = torch.empty(m, k, dtype=torch.bfloat16, device=x.device)
+    gw = torch.empty(n, k, dtype=torch.bfloat16, device=x.device)
+    gb = torch.empty(n, dtype=torch.bfloat16, device=x.device) if need_bias else None
+    ws = _linear_ws(1, m, n, k, x.device)
+    check(load().qad_linear_bwd(g2.data_ptr(), x2.data_ptr(), weight.contiguous().data_ptr(), gx.data_ptr(),
+                                gw.data_ptr(), None if gb is None else gb.data_ptr(), m, n, k, ws.data_ptr(),
+                                ws.numel(), _stream_ptr(x)), "qad_linear_bwd")
+    return gx.view(x.shape), gw, gb
+
+
+class _QadLinearSTE(torch.autograd.Function):
+    """Forward = the NVFP4 linear; backward = full-precision linear gradients (straight-through)."""
+
+    @staticmethod
+    def forward(ctx, x, weight, bias, input_sf):
+        ctx.save_for_backward(x, weight)
+        ctx.has_bias = bias is not None
+        return qad_linear_fwd(x, weight, bias, input_sf)
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        x, weight = ctx.saved_tensors
+        gx, gw, gb = qad_linear_bwd(grad_y, x, weight, need_bias=ctx.has_bias)
+        return gx, gw, gb, None
+
+
+def qad_linear(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+               input_sf: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """NVFP4 QAD linear with the straight-through backward when gradients are needed."""
+    if torch.is_grad_enabled() and (x.requires_grad or weight.requires_grad):
+        return _QadLinearSTE.apply(x, weight, bias, input_sf)
+    return qad_linear_fwd(x, weight, bias, input_sf)
+
+
+def qad_observe_amax(x: torch.Tensor, amax: torch.Tensor) -> torch.Tensor:
+    """Max calibration: amax (one-element fp32 device tensor) = max(amax, max|x|), in place."""
+    _require_bf16_cuda("x", x)
+    if amax.dtype != torch.float32 or not amax.is_cuda or amax.numel() != 1:
+        raise ValueError("amax must be a one-element fp32 device tensor")
+    xc = x.contiguous()
+    check(load().qad_observe_amax(xc.data_ptr(), xc.numel(), amax.data_ptr(), _stream_ptr(x)), "qad_observe_amax")
+    return amax
+
+
+class QADLinear:
+    """An NVFP4 QAD linear layer (NVFP4QADLinearMethod): act_scale "unit" (attention projections,
+    gates) or "static" (FFN linears, 448*6 / calibrated amax).  Inside calibrating() the dense
+    linear runs and every input's abs-max is folded into the observed maximum; enabled = False
+    runs the dense linear."""
+
+    def __init__(self, weight: torch.Tensor, bias: Optional[torch.Tensor] = None, act_scale: str = "unit"):
+        if act_scale not in ("unit", "static"):
+            raise ValueError(f"act_scale must be 'unit' or 'static', got {act_scale!r}")
+        self.weight, self.bias, self.act_scale = weight, bias, act_scale
+        self.enabled, self.calibrating = True, False
+        self.observed_amax = torch.zeros(1, dtype=torch.float32, device=weight.device)
+        self.input_amax: Optional[float] = None
+
+    def set_input_amax(self, amax: float) -> None:
+        if not amax > 0:
+            raise ValueError(f"calibrated amax must be positive, got {amax}")
+        self.input_amax = float(amax)
+
+    def finish_calibration(self) -> None:
+        self.calibrating = False
+        self.set_input_amax(float(self.observed_amax.item()))
+
+    def __call__(self, x: torch.Tensor) -> torch.Tensor:
+        if self.calibrating:
+            qad_observe_amax(x, self.observed_amax)
+            return torch.nn.functional.linear(x, self.weight, self.bias)
+        if not self.enabled:
+            return torch.nn.functional.linear(x, self.weight, self.bias)
+        sf = None
+        if self.act_scale == "static":
+            if self.input_amax is None:
+                raise RuntimeError("static activation scale used before calibration")
+            sf = input_global_sf(self.input_amax, x.device)
+        return qad_linear(x, self.weight, self.bias, sf)
+
+
 __all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "AQ_FINAL_MAX", "AQ_GSF_QKV",
            "AQ_GSF_P", "AQ_SMOOTH_K", "AQ_FLAGS_ALL", "fq_nvfp4",
            "static_global_scale", "attn_qat_fwd", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
-           "vsa_qat_fwd", "vsa_qat_bwd", "vsa_qat_train", "vsa_topk"]
+           "vsa_qat_fwd", "vsa_qat_bwd", "vsa_qat_train", "vsa_topk", "qad_linear_fwd", "qad_linear_bwd",
+           "qad_linear", "qad_observe_amax", "input_global_sf", "QADLinear"]

@@ -159,3 +159,17 @@ def test_missing_library_raises_import_error(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libattnqat.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_linear_rejects_bad_arguments(lib):
+    ws = 1 << 20
+    fwd = lambda m, n, k, x=16, ws_bytes=1 << 40: lib.qad_linear_fwd(x, 16, None, 16, m, n, k, None, ws, ws_bytes, None)
+    assert fwd(0, 64, 64) == -1 and "positive" in lib.aq_last_error().decode()
+    assert fwd(10, 64, 48) == -2 and "multiples of 64" in lib.aq_last_error().decode()
+    assert fwd(10, 96, 64) == -2
+    assert fwd(10, 64, 64, x=8) == -1 and "aligned" in lib.aq_last_error().decode()
+    assert fwd(10, 64, 64, ws_bytes=100) == -1 and "workspace" in lib.aq_last_error().decode()
+    assert lib.qad_linear_bwd(16, 16, 16, 16, 16, None, 10, 64, 40, ws, 1 << 40, None) == -2
+    assert lib.qad_observe_amax(None, 10, 16, None) == -1
+    assert lib.qad_linear_workspace_size(0, 10, 64, 64) > 10 * 64 * 2 + 64 * 64 * 2
+    assert lib.qad_linear_workspace_size(2, 10, 64, 64) == 0
