@@ -344,12 +344,17 @@ int qad_linear_bwd(const void *grad_y, const void *x, const void *w, void *grad_
       return hip_status(e, "qad_linear_bwd grad_x");
   }
   if (grad_w) {
-    if ((e = aq::launch_transpose(grad_y, n, m, n, ws + lw.gt, mp, st))) return hip_status(e, "qad_linear_bwd g^T");
+    // g^T, with grad_b's column sums taken in the same pass
+    if (grad_b)
+      e = aq::launch_transpose_colsum(grad_y, m, n, ws + lw.gt, mp, grad_b, (float *)(ws + lw.part), st);
+    else
+      e = aq::launch_transpose(grad_y, n, m, n, ws + lw.gt, mp, st);
+    if (e) return hip_status(e, "qad_linear_bwd g^T");
     if ((e = aq::launch_transpose(x, k, m, k, ws + lw.xt, mp, st))) return hip_status(e, "qad_linear_bwd x^T");
     if ((e = aq::launch_gemm_tn(ws + lw.gt, mp, ws + lw.xt, mp, grad_w, k, nullptr, n, k, mp, st)))
       return hip_status(e, "qad_linear_bwd grad_w");
   }
-  if (grad_b)
+  if (grad_b && !grad_w)
     return hip_status(aq::launch_colsum(grad_y, m, n, grad_b, (float *)(ws + lw.part), st), "qad_linear_bwd grad_b");
   return ok();
 }

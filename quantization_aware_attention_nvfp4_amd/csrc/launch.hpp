@@ -156,11 +156,17 @@ hipError_t launch_vsa_bwd(const AttnArgs &a, const BwdArgs &b, const int32_t *se
 // in elements.
 hipError_t launch_gemm_tn(const void *L, int64_t ldl, const void *R, int64_t ldr, void *C, int64_t ldc,
                           const void *bias, int64_t P, int64_t Q, int64_t K, hipStream_t stream);
-// out [C][Rp] = in [R][C]^T with rows r >= R of the result's columns zero.
+// out [C][Rp] = in [R][C]^T with rows r >= R of the result's columns zero (C and ldi multiples
+// of 8, Rp a multiple of 64).
 hipError_t launch_transpose(const void *in, int64_t ldi, int64_t R, int64_t C, void *out, int64_t Rp,
                             hipStream_t stream);
-// gb [N] = bf16 column sums of g [M][N]; part: colsum_chunks(M) * N fp32 of scratch.
+// gb [N] = bf16 column sums of g [M][N] (N a multiple of 8); part: colsum_chunks(M) * N fp32 of
+// scratch.
 hipError_t launch_colsum(const void *g, int64_t M, int64_t N, void *gb, float *part, hipStream_t stream);
+// Both of the above for g in one pass: gt [N][Mp] = g^T and gb = its column sums, bit-identical to
+// launch_colsum's.
+hipError_t launch_transpose_colsum(const void *g, int64_t M, int64_t N, void *gt, int64_t Mp, void *gb, float *part,
+                                   hipStream_t stream);
 int64_t colsum_chunks(int64_t M);
 // *amax = max(*amax, max|x|) over n bf16 values.
 hipError_t launch_observe_amax(const void *x, int64_t n, float *amax, hipStream_t stream);
