@@ -20,8 +20,10 @@ cube-sparse forward 4*B*H*n*k*128^2*D for its fine stage plus 4*B*H*n^2*D for
 its coarse stage, and its backward 2.5x the fine stage; fq contributes time but
 no FLOP.  After the step loop, the dense and cube-sparse inference forwards and
 fq on its own (back-to-back launches) are timed for the "attention" and "fq"
-objects, and the attention variants (final-max statistics, static scales,
-smooth-K) for the "variants" object.  Per-kernel durations come
+objects, the attention variants (final-max statistics, static scales,
+smooth-K) for the "variants" object, and the NVFP4 QAD linear on the model's
+feed-forward projections (25088 tokens, 1536 -> 8960 -> 1536) for the "linear"
+object.  Per-kernel durations come
 from HIP events the library records around each of its launches on the launch
 stream while kernel timing is on (aq_kernel_timing).
 
@@ -107,6 +109,11 @@ KERNEL_SOURCES = {
     "vsa_fwd_train": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "vsa_bwd_dkdv": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "vsa_bwd_dq": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
+    # the QAD linear's three GEMMs of the 1536 -> 8960 projection, in launch order
+    "gemm_tn_y": ("linear.hip", "attn_common.hpp", "aq_device.hpp"),
+    "gemm_tn_grad_x": ("linear.hip", "attn_common.hpp", "aq_device.hpp"),
+    "gemm_tn_grad_w": ("linear.hip", "attn_common.hpp", "aq_device.hpp"),
+    "transpose_colsum": ("linear.hip", "aq_device.hpp"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_qat_step_wan448x896x61_hbm_traffic.md")
 
@@ -138,7 +145,8 @@ def recorded_traffic(name):
 
 
 def pmc_probe():
-    """One pass of every stage (no timing) plus a plain 1 GiB device copy, for counter runs: the
+    """One pass of every stage (no timing), the QAD linear's forward and backward on the
+    1536 -> 8960 feed-forward projection, and a plain 1 GiB device copy, for counter runs: the
     copy's FETCH_SIZE / WRITE_SIZE readings calibrate the counters' unit."""
     import torch
 
@@ -161,6 +169,9 @@ def pmc_probe():
     m.attn_qat_bwd(q, k, v, aux, do)
     ov, auxv = m.vsa_qat_fwd(qv, kv, vv, grid=GRID, cube=CUBE, sparsity=SPARSITY, training=True)
     m.vsa_qat_bwd(qv, kv, vv, auxv, dov, grid=GRID, cube=CUBE, sparsity=SPARSITY)
+    xl, wl, bl, gl = (t.to(dev) for t in synth.wan_ffn(1536, 8960))
+    m.qad_linear_fwd(xl, wl, bl)
+    m.qad_linear_bwd(gl, xl, wl)
     torch.cuda.synchronize()
     print("pmc probe done: copy bytes", 2 * src.numel(), flush=True)
 
@@ -288,6 +299,40 @@ def main():
     variants["all"]["fwd_bwd_ms"] = round(ms, 4)
     variants["all"]["fwd_bwd_TFLOP/s"] = round((fl["fwd"] + fl["bwd"]) / (ms * 1e-3) / 1e12, 1)
 
+    # The NVFP4 QAD linear on the Wan2.1 1.3B feed-forward projections at this token count (25088
+    # tokens, 1536 -> 8960 and 8960 -> 1536): the forward (activation and weight fake-quant, BF16
+    # MFMA GEMM, bias) and the straight-through backward, each timed over back-to-back calls; the
+    # kernels' own per-launch times from the library's events over three forward + backward pairs;
+    # torch's bf16 linear (a library GEMM) on the same operands for context.
+    linear = {}
+    for lname, (kin, kout) in (("ffn_up", (1536, 8960)), ("ffn_down", (8960, 1536))):
+        xl, wl, bl, gl = (t.to(dev) for t in synth.wan_ffn(kin, kout))
+        fl_lin = 2.0 * xl.shape[0] * kin * kout
+        f_ms = timed(lambda: m.qad_linear_fwd(xl, wl, bl), 5)
+        b_ms = timed(lambda: m.qad_linear_bwd(gl, xl, wl), 3)
+        t_ms = timed(lambda: torch.nn.functional.linear(xl, wl, bl), 5)
+        _lib.kernel_times(reset=True)
+        _lib.kernel_timing(True)
+        for _ in range(3):
+            m.qad_linear_fwd(xl, wl, bl)
+            m.qad_linear_bwd(gl, xl, wl)
+        torch.cuda.synchronize()
+        _lib.kernel_timing(False)
+        kl = _lib.kernel_times(reset=True)
+        g_cnt, g_ms = kl["gemm_tn"]
+        g_avg = g_ms / g_cnt  # the three GEMMs (y, grad_x, grad_w) have the same FLOP count
+        linear[lname] = {
+            "M": xl.shape[0], "K": kin, "N": kout, "fwd_ms": round(f_ms, 4),
+            "fwd_TFLOP/s": round(fl_lin / (f_ms * 1e-3) / 1e12, 1), "bwd_ms": round(b_ms, 4),
+            "bwd_TFLOP/s": round(2 * fl_lin / (b_ms * 1e-3) / 1e12, 1), "gemm_tn_avg_ms": round(g_avg, 4),
+            "gemm_tn_TFLOP/s": round(fl_lin / (g_avg * 1e-3) / 1e12, 1),
+            "gemm_tn_frac_bf16_peak": round(fl_lin / (g_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "torch_bf16_linear_ms": round(t_ms, 4),
+            "gemm_tn_traffic": ({g: recorded_traffic("gemm_tn_" + g) for g in ("y", "grad_x", "grad_w")}
+                                if lname == "ffn_up" else None),
+            "kernels_avg_ms": {kn: round(v[1] / v[0], 4) for kn, v in sorted(kl.items())}}
+        del xl, wl, bl, gl
+
     # fq on its own: 40 back-to-back launches over the 4 rotating pairs between one pair of events
     # (a per-launch event pair adds about a microsecond to a 26 us kernel).
     fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -372,6 +417,7 @@ def main():
                    "vsa_cubes": fl["cubes"], "vsa_topk": fl["topk"], "fq_shape": list(xs[0].shape)},
         "roofline": roofline, "cpu_baseline": cpu, "attention": attn, "fq": fq,
         "phases_ms": {p: round(t, 4) for p, t in phase_ms.items()}, "kernels": kernels, "variants": variants,
+        "linear": linear,
     }
     print(json.dumps(out), flush=True)
 

@@ -80,6 +80,18 @@ def vsa_inputs(seed: int = 1005, grid=(16, 28, 56), heads: int = WAN_HEADS):
     return qkv_headscaled(1, L, heads, HEAD_DIM, seed, scaled=False)
 
 
+def wan_ffn(k_in: int = 1536, k_out: int = 8960, tokens: int = 16 * 28 * 56, seed: int = 1006):
+    """One feed-forward projection of the Wan2.1 1.3B block at 448x896, 61 frames (25088 tokens,
+    model width 1536, FFN width 8960): activations x [tokens, k_in] ~ N(0, 1), weight
+    [k_out, k_in] ~ N(0, 0.02^2) (the usual initialiser scale), bias [k_out] ~ N(0, 1) and the
+    output gradient [tokens, k_out] ~ N(0, 1), all bf16."""
+    x = normal_bf16((tokens, k_in), seed)
+    w = (torch.randn(k_out, k_in, generator=_gen(seed + 1)) * 0.02).to(torch.bfloat16)
+    b = normal_bf16((k_out,), seed + 2)
+    g = normal_bf16((tokens, k_out), seed + 3)
+    return x, w, b, g
+
+
 def sample_rows(L: int, n: int = 64, seed: int = 7, head: int = 8, tail: int = 8):
     """Sorted query/key rows: the first ``head``, the last ``tail`` and the
     rest drawn at random without repetition."""

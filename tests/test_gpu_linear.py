@@ -114,3 +114,24 @@ def test_wan_ffn_sampled_rows(m):
     rows[-1] = M - 1
     ref = oracle.linear_fwd(bits(x[torch.as_tensor(rows)]), bits(w), bits(b))
     assert_close(vals(y[torch.as_tensor(rows)]), ref, "ffn rows")
+
+
+def test_wan_ffn_backward_sampled(m):
+    # The straight-through backward at the full FFN shape, in the launch configuration the benchmark
+    # times: sampled rows of grad_x, sampled rows of grad_w and the matching grad_b entries, each
+    # from an oracle call on the sub-problem that defines exactly those outputs.
+    import synth
+    x, w, b, g = synth.wan_ffn()
+    M, N = g.shape
+    gx, gw, gb = m.qad_linear_bwd(g.cuda(), x.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(25).choice(M, 24, replace=False))
+    rows[-1] = M - 1
+    r = oracle.linear_bwd(bits(g[torch.as_tensor(rows)]), bits(x[torch.as_tensor(rows)]), bits(w))
+    assert_close(vals(gx[torch.as_tensor(rows)]), r["gx"], "ffn grad_x rows")
+    cols = np.sort(np.random.default_rng(26).choice(N, 16, replace=False))
+    cols[-1] = N - 1
+    ci = torch.as_tensor(cols)
+    r = oracle.linear_bwd(bits(g[:, ci].contiguous()), bits(x), bits(w[ci].contiguous()))
+    assert_close(vals(gw[ci]), r["gw"], "ffn grad_w rows")
+    assert_close(vals(gb[ci]), r["gb"], "ffn grad_b entries")
