@@ -37,8 +37,8 @@ QUANT_Q, QUANT_K, QUANT_V, QUANT_P = 1, 2, 4, 8
 QUANT_ALL = 15
 # Variants (readings in nvfp4_oracle.c): statistics relative to the final row
 # maximum, static per-tensor global scales for Q/K/V, the static global scale
-# of P, and smooth-K.
-FINAL_MAX, GSF_QKV, GSF_P, SMOOTH_K = 16, 32, 64, 128
+# of P, smooth-K, and the two-level (per-row, per-chunk) scale of P.
+FINAL_MAX, GSF_QKV, GSF_P, SMOOTH_K, TWO_LEVEL_P = 16, 32, 64, 128, 256
 
 
 def build(force: bool = False) -> str:
@@ -77,7 +77,7 @@ def _load():
             lib.oracle_fq_f32_rows.argtypes = [P, P, i64, i64, f32]
             lib.oracle_fq_f32_rows.restype = None
             lib.oracle_attn_fwd.argtypes = [P, P, P, i32, i32, i64, i64, i32, f64, i32, u32, i32, P, i64,
-                                            P, P, P, P]
+                                            P, P, P, P, P]
             lib.oracle_attn_fwd.restype = i32
             lib.oracle_attn_bwd.argtypes = [P, P, P, P, i32, i32, i64, i64, i32, f64, i32, u32, i32, P, i64,
                                             P, i64, P, P, P]
@@ -179,7 +179,8 @@ def attn_fwd(q, k, v, scale, causal=False, flags=QUANT_ALL, chunk=128, rows=None
 
     q: [B, H, Lq, D], k/v: [B, H, Lk, D] as bf16 bits (uint16).
     Returns dict of fp64 arrays: o, o_hp [B, H, R, D]; lse [B, H, R];
-    cmax [B, H, R, ceil(Lk/chunk)] (natural-log units)."""
+    cmax [B, H, R, ceil(Lk/chunk)] (natural-log units); pscale [B, H, R, ceil(Lk/chunk)], the
+    global scale of P's blocks in each chunk."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     B, H, Lq, D = q.shape
     Lk = k.shape[2]
@@ -192,12 +193,13 @@ def attn_fwd(q, k, v, scale, causal=False, flags=QUANT_ALL, chunk=128, rows=None
     ohp = np.empty((B, H, R, D))
     lse = np.empty((B, H, R))
     cmax = np.empty((B, H, R, C))
+    pscale = np.empty((B, H, R, C))
     rc = _load().oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, Lq, Lk, D, float(scale), int(causal),
                                  int(flags), int(chunk), _ptr(rows), R, _ptr(o), _ptr(ohp), _ptr(lse),
-                                 _ptr(cmax))
+                                 _ptr(cmax), _ptr(pscale))
     if rc != 0:
         raise ValueError("oracle_attn_fwd rejected the arguments")
-    return {"o": o, "o_hp": ohp, "lse": lse, "cmax": cmax, "rows": rows}
+    return {"o": o, "o_hp": ohp, "lse": lse, "cmax": cmax, "pscale": pscale, "rows": rows}
 
 
 def attn_bwd(q, k, v, do, scale, causal=False, flags=QUANT_ALL, chunk=128, qrows=None, krows=None):

@@ -225,7 +225,24 @@ enum { QF_Q = 1, QF_K = 2, QF_V = 4, QF_P = 8 };
    (use_global_sf_qkv, use_global_sf_p, smooth_k; "sm100_exact_m" and the
    reference-order statistics of the "Attn-QAT Training" guide); their
    arithmetic is the reading given with each use below. */
-enum { QF_FINAL_MAX = 16, QF_GSF_QKV = 32, QF_GSF_P = 64, QF_SMOOTH_K = 128 };
+enum { QF_FINAL_MAX = 16, QF_GSF_QKV = 32, QF_GSF_P = 64, QF_SMOOTH_K = 128, QF_TWO_LEVEL_P = 256 };
+
+/* Two-level quantization of P ([API] two_level_quant_p_sage3; the
+   SageAttention3 recipe the flag is named after): a first, per-row level maps
+   the largest P of the row within the chunk to 448*6, and the NVFP4 blocks are
+   quantized under that scale as under a static global scale (E4M3 block
+   scales of fp32(amax/6)*g, S = fp32(s/g)).  Per chunk and row:
+   g = fp32(448*6 / max_t P[t]) over the chunk's live keys (448*6 when that
+   maximum is 0).  Not combined with QF_FINAL_MAX or QF_GSF_P. */
+static float two_level_scale(const float *P, const int64_t *kc, int chunk)
+{
+    float rm = 0.0f;
+    for (int t = 0; t < chunk; ++t)
+        if (kc[t] >= 0 && P[t] > rm) rm = P[t];
+    if (!(rm > 0.0f)) return 448.0f * 6.0f;
+    volatile float g = (448.0f * 6.0f) / rm;
+    return g;
+}
 
 /* Per-head operands after fake quantization: Q and K along D, V along the
    key axis ([META] quant_v, qk_format/pv_format).  They are the operands of a
@@ -374,7 +391,7 @@ static float logit(const head_ops *h, int64_t i, int64_t j, int D, double scale)
    max after every chunk (cmax[c], -inf for a chunk that had no live key). */
 static void row_forward(const head_ops *h, int64_t i, const int64_t *keys, int64_t nchunks, int chunk,
                         int D, double scale, unsigned flags, double *o, double *o_hp, double *lse,
-                        double *cmax)
+                        double *cmax, double *pscale)
 {
     float *S = (float *)malloc(sizeof(float) * chunk);
     float *P = (float *)malloc(sizeof(float) * chunk);
@@ -395,14 +412,17 @@ static void row_forward(const head_ops *h, int64_t i, const int64_t *keys, int64
         }
         if (!live) {
             if (cmax) cmax[c] = -INFINITY;
+            if (pscale) pscale[c] = h->gp;
             continue;
         }
         float m_new = m > cm ? m : cm;
         for (int t = 0; t < chunk; ++t)
             P[t] = (kc[t] < 0) ? 0.0f : (float)exp((double)S[t] - (double)m_new);
         memcpy(Pq, P, sizeof(float) * chunk);
+        const float gp = (flags & QF_TWO_LEVEL_P) ? two_level_scale(P, kc, chunk) : h->gp;
+        if (pscale) pscale[c] = gp;
         if (flags & QF_P) {
-            for (int t0 = 0; t0 < chunk; t0 += 16) fq_block_f32(Pq + t0, chunk - t0 < 16 ? chunk - t0 : 16, h->gp);
+            for (int t0 = 0; t0 < chunk; t0 += 16) fq_block_f32(Pq + t0, chunk - t0 < 16 ? chunk - t0 : 16, gp);
             round_bf16(Pq, chunk); /* the P-hat V-hat matmul operand */
         }
         double alpha = (m == -INFINITY) ? 0.0 : exp((double)m - (double)m_new);
@@ -454,14 +474,17 @@ static int64_t *dense_keys(int64_t Lk, int chunk, int64_t i, int causal, int64_t
    Outputs (any may be NULL), indexed [bh][r] for row rows[r]:
      o, o_hp : [B*H, nrows, D] fp64
      lse     : [B*H, nrows]
-     cmax    : [B*H, nrows, ceil(Lk/chunk)]                               */
+     cmax    : [B*H, nrows, ceil(Lk/chunk)]
+     pscale  : [B*H, nrows, ceil(Lk/chunk)], the global scale P's blocks
+               had in each chunk (two_level_scale under QF_TWO_LEVEL_P).  */
 int oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int H, int64_t Lq,
                     int64_t Lk, int D, double scale, int causal, unsigned flags, int chunk,
                     const int64_t *rows, int64_t nrows, double *o, double *o_hp, double *lse,
-                    double *cmax)
+                    double *cmax, double *pscale)
 {
     init_tables();
     if (causal && Lq != Lk) return -1;
+    if ((flags & QF_TWO_LEVEL_P) && (flags & (QF_FINAL_MAX | QF_GSF_P))) return -2;
     if (flags & QF_FINAL_MAX) chunk = (int)((Lk + 15) / 16 * 16);
     int64_t C = (Lk + chunk - 1) / chunk;
     const call_scales cs = make_scales(q, k, v, (int64_t)B * H, Lq, Lk, D, flags);
@@ -475,7 +498,7 @@ int oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int
             int64_t idx = bh * nrows + r;
             row_forward(&hd, rows[r], keys, nc, chunk, D, scale, flags, o ? o + idx * D : NULL,
                         o_hp ? o_hp + idx * D : NULL, lse ? lse + idx : NULL,
-                        cmax ? cmax + idx * C : NULL);
+                        cmax ? cmax + idx * C : NULL, pscale ? pscale + idx * C : NULL);
             free(keys);
         }
         free_head_ops(&hd);
@@ -517,11 +540,12 @@ static void key_block(const bwd_head *x, int64_t j, int64_t *b0, int *nb)
     *nb = (int)(e - s);
 }
 
-/* For row i with forward statistics (lse, and m_c the running max after the
-   chunk that holds the block) and key block [b0, b0+nb):
-   A[t] = exp(S - lse), Ahat[t] = fq(exp(S - m_c))[t] * exp(m_c - lse),
+/* For row i with forward statistics (lse, m_c the running max after the
+   chunk that holds the block, and g the global scale its P blocks had) and
+   key block [b0, b0+nb):
+   A[t] = exp(S - lse), Ahat[t] = fq(exp(S - m_c), g)[t] * exp(m_c - lse),
    for the block's keys (masked keys give 0). */
-static void block_weights_mc(const bwd_head *x, int64_t i, int64_t b0, int nb, double lse, double mc,
+static void block_weights_mc(const bwd_head *x, int64_t i, int64_t b0, int nb, double lse, double mc, float g,
                              double *A, double *Ahat)
 {
     float P[16];
@@ -532,7 +556,7 @@ static void block_weights_mc(const bwd_head *x, int64_t i, int64_t b0, int nb, d
         P[t] = live ? (float)exp((double)S[t] - mc) : 0.0f;
     }
     if (x->flags & QF_P) {
-        fq_block_f32(P, nb, x->hd->gp);
+        fq_block_f32(P, nb, g);
         round_bf16(P, nb);
     }
     for (int t = 0; t < nb; ++t) {
@@ -544,9 +568,9 @@ static void block_weights_mc(const bwd_head *x, int64_t i, int64_t b0, int nb, d
 
 /* Dense schedule: the block's chunk is the one its keys fall in. */
 static void block_weights(const bwd_head *x, int64_t i, int64_t b0, int nb, double lse, const double *cmax,
-                          double *A, double *Ahat)
+                          const double *pscale, double *A, double *Ahat)
 {
-    block_weights_mc(x, i, b0, nb, lse, cmax[b0 / x->chunk], A, Ahat);
+    block_weights_mc(x, i, b0, nb, lse, cmax[b0 / x->chunk], (float)pscale[b0 / x->chunk], A, Ahat);
 }
 
 static double dot_do_v(const bwd_head *x, int64_t i, int64_t j)
@@ -557,14 +581,14 @@ static double dot_do_v(const bwd_head *x, int64_t i, int64_t j)
     return s;
 }
 
-/* Forward statistics of row i: lse, running max per chunk, and
-   D_i = <dO_i, Ohp_i>. */
-static void row_stats(const bwd_head *x, int64_t i, double *lse, double *cmax, double *Di)
+/* Forward statistics of row i: lse, running max and P's global scale per
+   chunk, and D_i = <dO_i, Ohp_i>. */
+static void row_stats(const bwd_head *x, int64_t i, double *lse, double *cmax, double *pscale, double *Di)
 {
     int64_t nc;
     int64_t *keys = dense_keys(x->Lk, x->chunk, i, x->causal, &nc);
     double *ohp = (double *)malloc(sizeof(double) * x->D);
-    row_forward(x->hd, i, keys, nc, x->chunk, x->D, x->scale, x->flags, NULL, ohp, lse, cmax);
+    row_forward(x->hd, i, keys, nc, x->chunk, x->D, x->scale, x->flags, NULL, ohp, lse, cmax, pscale);
     double s = 0.0;
     for (int d = 0; d < x->D; ++d) s += (double)bf16_to_f32(x->dO[i * x->D + d]) * ohp[d];
     *Di = s;
@@ -581,6 +605,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
 {
     init_tables();
     if (causal && Lq != Lk) return -1;
+    if ((flags & QF_TWO_LEVEL_P) && (flags & (QF_FINAL_MAX | QF_GSF_P))) return -2;
     if (flags & QF_FINAL_MAX) chunk = (int)((Lk + 15) / 16 * 16);
     int64_t C = (Lk + chunk - 1) / chunk;
     const call_scales cs = make_scales(q, k, v, (int64_t)B * H, Lq, Lk, D, flags);
@@ -595,14 +620,15 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                 int64_t i = qrows[a];
                 double lse, Di, A[16], Ah[16];
                 double *cmax = (double *)malloc(sizeof(double) * C);
-                row_stats(&x, i, &lse, cmax, &Di);
+                double *pg = (double *)malloc(sizeof(double) * C);
+                row_stats(&x, i, &lse, cmax, pg, &Di);
                 double *out = dq + (bh * nq + a) * D;
                 for (int d = 0; d < D; ++d) out[d] = 0.0;
                 for (int64_t b0 = 0; b0 < Lk;) {
                     int64_t s;
                     int nb;
                     key_block(&x, b0, &s, &nb);
-                    block_weights(&x, i, s, nb, lse, cmax, A, Ah);
+                    block_weights(&x, i, s, nb, lse, cmax, pg, A, Ah);
                     for (int t = 0; t < nb; ++t) {
                         int64_t j = s + t;
                         if (causal && j > i) continue;
@@ -612,6 +638,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                     b0 = s + nb;
                 }
                 free(cmax);
+                free(pg);
             }
         }
 
@@ -619,9 +646,10 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
             /* Key gradients need every row's statistics. */
             double *lse = (double *)malloc(sizeof(double) * Lq);
             double *cmax = (double *)malloc(sizeof(double) * Lq * C);
+            double *pg = (double *)malloc(sizeof(double) * Lq * C);
             double *Dv = (double *)malloc(sizeof(double) * Lq);
 #pragma omp parallel for schedule(dynamic, 16)
-            for (int64_t i = 0; i < Lq; ++i) row_stats(&x, i, lse + i, cmax + i * C, Dv + i);
+            for (int64_t i = 0; i < Lq; ++i) row_stats(&x, i, lse + i, cmax + i * C, pg + i * C, Dv + i);
 #pragma omp parallel for schedule(dynamic, 1)
             for (int64_t a = 0; a < nk; ++a) {
                 int64_t j = krows[a];
@@ -637,7 +665,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                 double A[16], Ah[16];
                 for (int64_t i = 0; i < Lq; ++i) {
                     if (causal && j > i) continue;
-                    block_weights(&x, i, s, nb, lse[i], cmax + i * C, A, Ah);
+                    block_weights(&x, i, s, nb, lse[i], cmax + i * C, pg + i * C, A, Ah);
                     double dS = A[j - s] * (dot_do_v(&x, i, j) - Dv[i]);
                     for (int d = 0; d < D; ++d) {
                         if (ok) ok[d] += scale * dS * (double)hd.qh[i * D + d];
@@ -647,6 +675,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
             }
             free(lse);
             free(cmax);
+            free(pg);
             free(Dv);
         }
         free_head_ops(&hd);
@@ -735,6 +764,7 @@ int oracle_vsa_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int 
 {
     init_tables();
     if (L % cube_tokens) return -1;
+    if ((flags & QF_TWO_LEVEL_P) && (flags & (QF_FINAL_MAX | QF_GSF_P))) return -2;
     int64_t n = L / cube_tokens;
     int topk = oracle_vsa_topk(sparsity, (int)n);
     uint16_t *qp = (uint16_t *)malloc(2 * n * D), *kp = (uint16_t *)malloc(2 * n * D),
@@ -764,7 +794,7 @@ int oracle_vsa_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int 
             int64_t *keys = vsa_keys(sl + a * topk, topk, cube_tokens);
             if (o_fine)
                 row_forward(&hd, i, keys, nchunk, chunk, D, scale, flags, o_fine + (bh * nrows + r) * D,
-                            NULL, NULL, NULL);
+                            NULL, NULL, NULL, NULL);
             if (o_coarse) {
                 double mx = -INFINITY, l = 0.0;
                 for (int64_t b = 0; b < n; ++b)
@@ -804,6 +834,7 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
 {
     init_tables();
     if (L % cube_tokens) return -1;
+    if ((flags & QF_TWO_LEVEL_P) && (flags & (QF_FINAL_MAX | QF_GSF_P))) return -2;
     const int64_t n = L / cube_tokens;
     const int ct = cube_tokens;
     const int topk = oracle_vsa_topk(sparsity, (int)n);
@@ -826,6 +857,7 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
         /* Row statistics (lse, running max after each selected cube, D_i). */
         double *lse = (double *)malloc(sizeof(double) * L);
         double *cmax = (double *)malloc(sizeof(double) * L * topk);
+        double *pg = (double *)malloc(sizeof(double) * L * topk);
         double *Dv = (double *)malloc(sizeof(double) * L);
         char *need = (char *)calloc(L, 1);
         for (int64_t a = 0; a < nq; ++a) need[qrows[a]] = 1;
@@ -837,7 +869,7 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
             int64_t *keys = vsa_keys(sl + (i / ct) * topk, topk, ct);
             double *ohp = (double *)malloc(sizeof(double) * D);
             row_forward(&hd, i, keys, nchunk, fm ? topk * ct : ct, D, scale, flags, NULL, ohp, lse + i,
-                        cmax + i * topk);
+                        cmax + i * topk, pg + i * topk);
             double s = 0.0;
             for (int d = 0; d < D; ++d) s += (double)bf16_to_f32(x.dO[i * D + d]) * ohp[d];
             Dv[i] = s;
@@ -858,7 +890,8 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
                         int64_t s;
                         int nb;
                         key_block(&x, b0, &s, &nb);
-                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + (fm ? 0 : t)], A, Ah);
+                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + (fm ? 0 : t)],
+                                         (float)pg[i * topk + (fm ? 0 : t)], A, Ah);
                         for (int u = 0; u < nb; ++u) {
                             int64_t j = s + u;
                             double dS = A[u] * (dot_do_v(&x, i, j) - Dv[i]);
@@ -889,7 +922,8 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
                         if (sl[qc * topk + u] == b) t = u;
                     if (t < 0) continue;  /* this query cube did not select j's cube */
                     for (int64_t i = qc * ct; i < (qc + 1) * ct; ++i) {
-                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + (fm ? 0 : t)], A, Ah);
+                        block_weights_mc(&x, i, s, nb, lse[i], cmax[i * topk + (fm ? 0 : t)],
+                                         (float)pg[i * topk + (fm ? 0 : t)], A, Ah);
                         double dS = A[j - s] * (dot_do_v(&x, i, j) - Dv[i]);
                         for (int d = 0; d < D; ++d) {
                             if (ok) ok[d] += scale * dS * (double)hd.qh[i * D + d];
@@ -901,6 +935,7 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
         }
         free(lse);
         free(cmax);
+        free(pg);
         free(Dv);
         free(need);
         free_head_ops(&hd);

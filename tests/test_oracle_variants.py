@@ -226,3 +226,113 @@ def test_smooth_k_with_quantization_composes_the_fp32_codec():
     bref = oracle.attn_bwd(q, kq, v, do, SCALE, flags=ALL & ~oracle.QUANT_K)
     for name in ("dq", "dk", "dv"):
         assert np.array_equal(b[name], bref[name]), name
+
+
+# -------------------------------------------------------------- two-level P
+
+TWO = oracle.TWO_LEVEL_P
+
+
+@pytest.mark.parametrize("Lk", [128, 100])
+def test_two_level_p_single_chunk_is_the_static_p_scale(Lk):
+    # One chunk: the row's largest P in it is exp(0) = 1, so the first level is 448*6 / 1, the
+    # static P scale, and every output (forward and backward) is the static-scale one.
+    Lq = 24
+    q, k, v = rand_bits((1, 2, Lq, D), 131), rand_bits((1, 2, Lk, D), 132, 2.0), rand_bits((1, 2, Lk, D), 133)
+    a = oracle.attn_fwd(q, k, v, SCALE, flags=ALL | TWO)
+    b = oracle.attn_fwd(q, k, v, SCALE, flags=ALL | oracle.GSF_P)
+    for name in ("o", "o_hp", "lse", "cmax"):
+        assert np.array_equal(a[name], b[name]), name
+    assert np.all(a["pscale"] == 2688.0)
+    do = rand_bits((1, 2, Lq, D), 134)
+    ab = oracle.attn_bwd(q, k, v, do, SCALE, flags=ALL | TWO)
+    bb = oracle.attn_bwd(q, k, v, do, SCALE, flags=ALL | oracle.GSF_P)
+    for name in ("dq", "dk", "dv"):
+        assert np.array_equal(ab[name], bb[name]), name
+
+
+def chunk_constant(seed, Lq=16, C=4):
+    """Q ~ N(0,1); keys constant within each 128-key chunk (chunk bases N(0, 2^2)); V ~ N(0,1)."""
+    q = rand_bits((1, 1, Lq, D), seed)
+    base = rand_bits((C, D), seed + 1, 2.0)
+    k = np.repeat(base, 128, axis=0).reshape(1, 1, C * 128, D)
+    v = rand_bits((1, 1, C * 128, D), seed + 2)
+    return q, k, v
+
+
+def test_two_level_p_recovers_constant_chunks():
+    # Keys constant within each chunk make every P of a (row, chunk) equal to that chunk's largest
+    # P, so the first level maps it to 448*6: the block scale is E4M3(448) = 448, the value codes to
+    # 6, and P-hat is P up to fp32 and bf16 rounding.  With Q, K, V unquantized the output is then
+    # softmax attention to within the bf16 rounding of the chunk weights; the static P scale rounds
+    # E4M3(448 P) instead and lands further away.
+    q, k, v = chunk_constant(135)
+    exact = sdpa64(f64(q), f64(k), f64(v), SCALE).numpy()
+    two = oracle.attn_fwd(q, k, v, SCALE, flags=oracle.QUANT_P | TWO)
+    stat = oracle.attn_fwd(q, k, v, SCALE, flags=oracle.QUANT_P | oracle.GSF_P)
+    scale = np.abs(exact).max()
+    e_two = np.abs(two["o"] - exact).max() / scale
+    e_stat = np.abs(stat["o"] - exact).max() / scale
+    assert e_two < 2.0 ** -8
+    assert e_stat > 4 * e_two
+    # the first level is 448*6 exactly where the chunk holds the running maximum, larger elsewhere
+    cm = two["cmax"][0, 0]
+    first = np.concatenate([np.ones((cm.shape[0], 1), bool), cm[:, 1:] > cm[:, :-1]], axis=1)
+    ps = two["pscale"][0, 0]
+    assert np.all(ps[first] == 2688.0)
+    assert np.all(ps[~first] > 2688.0)
+    assert (~first).any()
+
+
+def test_two_level_p_backward_identities():
+    # dQ and dK take the unquantized probabilities, so with Q, K, V unquantized they equal float64
+    # autograd whatever P's quantizer; dV pairs with the output (<dO, O> = sum_j <dV_j, V_j>),
+    # which ties the backward's P-hat to the forward's; on chunk-constant keys dV is autograd's
+    # to the bf16 rounding of the chunk weights.
+    q, k, v = chunk_constant(137)
+    do = rand_bits((1, 1, 16, D), 140)
+    fl = oracle.QUANT_P | TWO
+    b = oracle.attn_bwd(q, k, v, do, SCALE, flags=fl)
+    Q, K, V = (f64(t).requires_grad_() for t in (q, k, v))
+    sdpa64(Q, K, V, SCALE).backward(f64(do))
+    # (to the fp32 rounding of the logits the oracle forms)
+    assert np.abs(b["dq"] - Q.grad.numpy()).max() < 1e-6 * np.abs(Q.grad.numpy()).max()
+    assert np.abs(b["dk"] - K.grad.numpy()).max() < 1e-6 * np.abs(K.grad.numpy()).max()
+    assert np.abs(b["dv"] - V.grad.numpy()).max() < 2.0 ** -8 * np.abs(V.grad.numpy()).max()
+    f = oracle.attn_fwd(q, k, v, SCALE, flags=fl)
+    lhs = np.einsum("bhid,bhid->bh", f32(do).astype(np.float64), f["o"])
+    rhs = np.einsum("bhjd,bhjd->bh", b["dv"], f32(v).astype(np.float64))
+    assert np.allclose(lhs, rhs, rtol=1e-10)
+    # random keys: the same pairing, and the cube-sparse backward agrees with the dense one at
+    # sparsity 0
+    q, k, v = rand_bits((1, 1, 40, D), 141), rand_bits((1, 1, 384, D), 142, 2.0), rand_bits((1, 1, 384, D), 143)
+    do = rand_bits((1, 1, 40, D), 144)
+    b = oracle.attn_bwd(q, k, v, do, SCALE, flags=ALL | TWO)
+    f = oracle.attn_fwd(q, k, v, SCALE, flags=ALL | TWO)
+    vh = f32(oracle.fq_bf16(v, 2)).astype(np.float64)
+    lhs = np.einsum("bhid,bhid->bh", f32(do).astype(np.float64), f["o"])
+    rhs = np.einsum("bhjd,bhjd->bh", b["dv"], vh)
+    assert np.allclose(lhs, rhs, rtol=1e-10)
+
+
+def test_two_level_p_vsa_sparsity_zero_is_dense():
+    L = 512
+    q, k, v = (rand_bits((1, 1, L, D), s) for s in (145, 146, 147))
+    fl = ALL | TWO
+    s = oracle.vsa_fwd(q, k, v, SCALE, sparsity=0.0, flags=fl)
+    d = oracle.attn_fwd(q, k, v, SCALE, flags=fl)
+    assert np.array_equal(s["o_fine"], d["o"])
+    do = rand_bits((1, 1, L, D), 148)
+    sb = oracle.vsa_bwd(q, k, v, do, SCALE, sparsity=0.0, flags=fl, krows=np.arange(0, L, 37))
+    db = oracle.attn_bwd(q, k, v, do, SCALE, flags=fl, krows=np.arange(0, L, 37))
+    for name in ("dq", "dk", "dv"):
+        assert np.allclose(sb[name], db[name], rtol=0, atol=1e-12), name
+
+
+def test_two_level_p_rejects_final_max_and_static_p():
+    q, k, v = (rand_bits((1, 1, 64, D), s) for s in (149, 150, 151))
+    for extra in (oracle.FINAL_MAX, oracle.GSF_P):
+        with pytest.raises(ValueError):
+            oracle.attn_fwd(q, k, v, SCALE, flags=ALL | TWO | extra)
+        with pytest.raises(ValueError):
+            oracle.vsa_fwd(q, k, v, SCALE, cube_tokens=64, sparsity=0.0, flags=ALL | TWO | extra)
