@@ -61,8 +61,8 @@ enum {
 };
 
 /* Variants, OR-ed into the same flags word.  [API] lists the kernel flags use_global_sf_qkv,
-   use_global_sf_p and smooth_k (all off in attn_qat_train) and [META]'s precision records carry the
-   same names; [DOC]'s environment table names reference-order softmax statistics
+   use_global_sf_p, smooth_k and two_level_quant_p_sage3 (all off in attn_qat_train) and [META]'s
+   precision records carry the first three; [DOC]'s environment table names reference-order softmax statistics
    (FASTVIDEO_ATTN_QAT_FWD_EXACT_M).  None is defined on the pages; the readings implemented:
      AQ_FINAL_MAX  every P relative to its row's final maximum over all keys (the selected keys for
                    vsa_qat_fwd) instead of the running maximum of 128-key chunks; the forward
@@ -75,14 +75,22 @@ enum {
      AQ_SMOOTH_K   the keys' per-channel mean over the sequence (fp64 sum / L, rounded to fp32)
                    subtracted before quantization; the softmax of a row ignores the shift and the
                    gradient passes to K unchanged.
-   Under AQ_GSF_QKV or AQ_GSF_P the P-hat V-hat product runs in bf16 (the values are no longer
-   exact in fp16). */
+     AQ_TWO_LEVEL_P  two-level P, SageAttention3's recipe: per row and 128-key chunk (selected cube
+                   for vsa_qat_fwd) a first level g = 448*6 / (the row's largest P in the chunk;
+                   448*6 when it is 0) serves as the global scale of P's 16-key blocks, quantized as
+                   under a static scale.  Training calls then pass a chunk_max_log2 array of TWICE
+                   the size: its second half, laid out like the first, receives g of every
+                   (row, chunk), which the backward reads.  Not combinable with AQ_FINAL_MAX or
+                   AQ_GSF_P (AQ_ENOTSUP).
+   Under AQ_GSF_QKV, AQ_GSF_P or AQ_TWO_LEVEL_P the P-hat V-hat product runs in bf16 (the values are
+   no longer exact in fp16). */
 enum {
     AQ_FINAL_MAX = 16,
     AQ_GSF_QKV = 32,
     AQ_GSF_P = 64,
     AQ_SMOOTH_K = 128,
-    AQ_FLAGS_ALL = 255
+    AQ_TWO_LEVEL_P = 256,
+    AQ_FLAGS_ALL = 511
 };
 
 /* Element strides of a 4-D attention tensor, indexed (batch, head, token, d) with d contiguous. */
@@ -124,7 +132,7 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  * Every bf16 tensor of the attention entry points starts 16-byte aligned and has strides that
  * are multiples of 8 elements and below 2^24 (rows move in 16-byte pieces); lq, lk <= 2^30.
  * Q-hat, K-hat along D and V-hat along keys are fake-quantized per quant_flags (quantizers and
- * the AQ_FINAL_MAX / AQ_GSF_QKV / AQ_GSF_P / AQ_SMOOTH_K variants above).  The keys are
+ * the AQ_FINAL_MAX / AQ_GSF_QKV / AQ_GSF_P / AQ_SMOOTH_K / AQ_TWO_LEVEL_P variants above).  The keys are
  * visited in chunks of 128 ([0,128), [128,256), ...); in chunk c the running row maximum m_c of
  * the logits softmax_scale * <q-hat, k-hat> is refreshed first, then P = exp(logit - m_c) is
  * formed, fake-quantized in 16-key blocks (AQ_QUANT_P) and multiplied with V-hat on BF16 MFMA;
@@ -135,6 +143,8 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  *   lse_log2       [B, H, lq] fp32 contiguous: log2 of the softmax denominator in base-2 logit
  *                  units, i.e. log2(e) * (m + ln l) with m the final row maximum.
  *   chunk_max_log2 [B, H, ceil(lk/128), lq] fp32 contiguous: log2(e) * m_c after each chunk
+ *                  (under AQ_TWO_LEVEL_P twice that: then [2, B, H, ceil(lk/128), lq], the second
+ *                  half P's first-level scale of each chunk)
  *                  (entries of chunks a causal row never reaches are left unwritten).
  *   o_hp           [B, H, lq, 128] fp32 contiguous: the auxiliary high-precision output with
  *                  unquantized P ([API] use_high_prec_o).
@@ -189,7 +199,8 @@ int attn_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp,
  * softmax(coarse logits) @ Vc broadcast to every token of the query cube, bf16, strides so;
  * sel (NULL allowed) receives the [B, H, n, topk] int32 selection.
  * Optional training outputs of the fine stage (all three or none; vsa_qat_bwd needs them and
- * sel): lse_log2 [B, H, L], chunk_max_log2 [B, H, topk, L] (the running maximum after each
+ * sel): lse_log2 [B, H, L], chunk_max_log2 [B, H, topk, L] (x2 under AQ_TWO_LEVEL_P, as for
+ * attn_qat_fwd) (the running maximum after each
  * selected cube, in list order) and o_hp [B, H, L, 128], fp32 contiguous, defined as for
  * attn_qat_fwd.
  * workspace: at least attn_qat_workspace_size(2, ...) bytes with lk = L.

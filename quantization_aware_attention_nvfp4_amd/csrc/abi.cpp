@@ -59,6 +59,9 @@ int check_attention(int batch, int num_heads, int num_kv_heads, int head_size, i
     return fail(AQ_EINVAL, "softmax_scale must be finite and > 0 (got %g)", (double)softmax_scale);
   if (quant_flags & ~(unsigned)AQ_FLAGS_ALL)
     return fail(AQ_EINVAL, "quant_flags 0x%x has bits outside AQ_FLAGS_ALL", quant_flags);
+  if ((quant_flags & AQ_TWO_LEVEL_P) && (quant_flags & (AQ_FINAL_MAX | AQ_GSF_P)))
+    return fail(AQ_ENOTSUP, "AQ_TWO_LEVEL_P does not combine with AQ_FINAL_MAX or AQ_GSF_P (flags 0x%x)",
+                quant_flags);
   if (num_kv_heads != num_heads)
     return fail(AQ_ENOTSUP, "num_kv_heads (%d) must equal num_heads (%d)", num_kv_heads, num_heads);
   if (causal && lq != lk)

@@ -173,6 +173,14 @@ __device__ __forceinline__ ProbBlock prob_block_static(float logit_max, float c,
 }
 // The static scale of P's blocks ("nvfp4_qad.py" FP4_RANGE over P's largest value, 1).
 constexpr float kPScaleStatic = 448.0f * 6.0f;
+// Two-level P (SageAttention3's recipe, the two_level_quant_p_sage3 flag of the "attn_qat_train"
+// API page): the first level of a (row, chunk) maps the chunk's largest P of the row,
+// exp2(fma(cm, c, -m)) for the row's largest logit cm in the chunk, to 448*6; 448*6 when that P
+// is 0 (no live key).  P's blocks then take it as their global scale.
+__device__ __forceinline__ float two_level_scale(float cm, float c, float m) {
+  const float rm = __builtin_amdgcn_exp2f(__builtin_fmaf(cm, c, -m));
+  return rm > 0.0f ? kPScaleStatic / rm : kPScaleStatic;
+}
 
 // Eight values rounded to E2M1 codes in one register (byte i holds pair i; ties to the even
 // code, saturating at +-6, sign kept), by the gfx950 packed FP4 conversion with a unit scale.

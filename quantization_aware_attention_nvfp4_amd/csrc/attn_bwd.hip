@@ -70,6 +70,9 @@ struct BwdParams {
   const int32_t *sel;
   const int16_t *slot_t;
   int64_t nsel;
+  // Two-level P: [BH, Ck or nsel, lq] P's global scale per (query, chunk) as the forward used it,
+  // laid out like the chunk maxima; null otherwise.
+  const float *pg;
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
 constexpr int kQT = 64;  // queries per tile
 constexpr int kDkdvThreads = 512;
 constexpr int kLdsR = 65536, kLdsStat = 131072;
-constexpr int kLdsOneHot = kLdsStat + 2 * 768;  // two one-hot B operands, 16 bytes per lane
+constexpr int kLdsOneHot = kLdsStat + 2 * 1024;  // two one-hot B operands, 16 bytes per lane
 constexpr int kMaxCubes = 4096;                   // cube-sparse: longest query-cube list
 constexpr int kLdsList = kLdsOneHot + 2048;       // that list (+ its length), int32
 constexpr int kDkdvLds = kLdsList + 4 * (kMaxCubes + 1);
@@ -284,9 +287,9 @@ struct DkdvLane {
 
 // Copies of tile qb into buffer `buf`: Q-hat rows from the workspace, dO rows from the caller's
 // tensor (rows past lq repeat row lq-1; every product they feed is masked), and the three
-// per-query statistics (entries past lq repeat entry lq-1); cm_row is the chunk-max row of the
-// key chunk for these queries.  Per lane: 4 copies of 16 bytes, plus
-// one 4-byte copy in waves 0..2.
+// per-query statistics (entries past lq repeat entry lq-1), plus P's two-level scales when there
+// are any; cm_row is the chunk-max row of the key chunk for these queries.  Per lane: 4 copies of
+// 16 bytes, plus one 4-byte copy in waves 0..2 (and in wave 3 under two-level P).
 __device__ __forceinline__ void dkdv_stage_tile(const BwdParams &p, const DkdvLane &ln, int64_t bh, int64_t bb,
                                                 int64_t hh, int64_t cm_row, int64_t qb, uint8_t *lds, int buf,
                                                 int wave, int lane) {
@@ -302,10 +305,13 @@ __device__ __forceinline__ void dkdv_stage_tile(const BwdParams &p, const DkdvLa
       ov = (uint32_t)(rem * p.sdo.l * 2) + (ln.o_voff[i] - (uint32_t)(ln.o_row[i] * p.sdo.l * 2));
     load_lds16_s(osrc, ov, ro + (i * 8 + wave) * 1024);
   }
-  if (wave < 3) {
-    const float *src = (wave == 0 ? p.cmax + cm_row * p.lq : (wave == 1 ? p.lse : p.dvec) + bh * p.lq) + qb * kQT;
+  if (wave < 3 || (wave == 3 && p.pg)) {
+    const float *src = (wave == 0   ? p.cmax + cm_row * p.lq
+                        : wave == 3 ? p.pg + cm_row * p.lq
+                                    : (wave == 1 ? p.lse : p.dvec) + bh * p.lq) +
+                       qb * kQT;
     const int q = lane < rem ? lane : (int)(rem < 0 ? 0 : rem);
-    load_lds4_s(src, (uint32_t)q * 4u, lds + kLdsStat + buf * 768 + wave * 256);
+    load_lds4_s(src, (uint32_t)q * 4u, lds + kLdsStat + buf * 1024 + wave * 256);
   }
 }
 
@@ -331,7 +337,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, s, 0, 0, 0);
     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bo, dp, 0, 0, 0);
   }
-  const uint32_t sta = lds0 + kLdsStat + BUF * 768 + 4 * ln.qloc;
+  const uint32_t sta = lds0 + kLdsStat + BUF * 1024 + 4 * ln.qloc;
   const float mc = lds_read_f32(sta), lse2 = lds_read_f32(sta + 256), Di = lds_read_f32(sta + 512);
   const int qrow = (int)(qb * kQT) + ln.qloc;
   const int lq = (int)p.lq;
@@ -347,7 +353,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
   const float w = __builtin_amdgcn_exp2f(mc - lse2);
   float ah[16], ds[16];
   if (p.quant_p) {
-    const ProbBlock pb = GP ? prob_block_static(bm, p.c, mc, kPScaleStatic) : prob_block(bm, p.c, mc);
+    const float g = (GP && p.pg) ? lds_read_f32(sta + 768) : kPScaleStatic;
+    const ProbBlock pb = GP ? prob_block_static(bm, p.c, mc, g) : prob_block(bm, p.c, mc);
     const float sw = pb.Sd * w, swD = sw * Di;  // A = r * Sd * w
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -622,6 +629,7 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   p.sel = sel;
   p.slot_t = slot_t;
   p.nsel = nsel;
+  if ((a.flags & kFlagTwoLevelP) && p.quant_p) p.pg = a.cmax + bh * (sel ? nsel : p.Ck) * a.lq;
 
   p.nwork = bh * p.Cq;
   p.per_xcd = (p.nwork + 7) / 8;
@@ -633,7 +641,7 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   p.nwork = bh * p.Ck;
   p.per_xcd = (p.nwork + 7) / 8;
   const dim3 dkdv_grid((unsigned)(p.per_xcd * 8));
-  const bool gp = p.quant_p && (a.flags & kFlagGsfP);
+  const bool gp = p.quant_p && (a.flags & (kFlagGsfP | kFlagTwoLevelP));
   if (sel && gp) AQ_LAUNCH("vsa_bwd_dkdv", (bwd_dkdv_kernel<true, true>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
   else if (sel) AQ_LAUNCH("vsa_bwd_dkdv", (bwd_dkdv_kernel<true, false>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
   else if (gp) AQ_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<false, true>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);

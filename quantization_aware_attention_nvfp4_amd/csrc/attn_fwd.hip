@@ -61,6 +61,8 @@ struct FwdParams {
   const float *gq;      // static global scale of Q (device scalar), or null for the unit scale
   const float *m_init;  // [BH, lq] final row maxima (base 2) seeding the running max, or null
   float *m_out;         // row-max pass: where it writes them
+  bool two_level;       // P's global scale per (row, chunk): two_level_scale (GP kernels)
+  float *pg;            // training, two-level: [BH, C, lq] those scales, or null
 };
 
 // Copy offsets of this lane's 16-byte pieces of a staged [128][256 B] tile by a workgroup of
@@ -153,14 +155,15 @@ __device__ __forceinline__ void load_q_frags(const FwdParams &p, int64_t bb, int
 
 // P of one 32-key sub-tile, whose 16 logits in the lane's registers are one P block, as the two
 // P-hat V-hat B operands (keys 0-7 and 8-15 of the block); psum gains the block's unquantized sum.
-// HP: also the unquantized P as operands (ph), for O^hp.  GP: P's blocks under the static global
-// scale (then F16 is off: P-hat is rounded to bf16).
+// HP: also the unquantized P as operands (ph), for O^hp.  GP: P's blocks under the global scale g
+// (the static 448*6, or the two-level scale of the row and chunk; then F16 is off: P-hat is
+// rounded to bf16).
 template <bool QP, bool F16, bool HP, bool GP>
-__device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, float m_new, float &psum, u32x4 (&pq)[2],
-                                       u32x4 (&ph)[2]) {
+__device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, float m_new, float g, float &psum,
+                                       u32x4 (&pq)[2], u32x4 (&ph)[2]) {
   static_assert(!(GP && F16), "P-hat under the static scale is not exact in fp16");
   if (QP) {
-    const ProbBlock pb = GP ? prob_block_static(bmax, c, m_new, kPScaleStatic) : prob_block(bmax, c, m_new);
+    const ProbBlock pb = GP ? prob_block_static(bmax, c, m_new, g) : prob_block(bmax, c, m_new);
     float r[16], rsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -370,6 +373,8 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
     const float m_new = fmaxf(m_run, cm * p.c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
     if (TRAIN && hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
+    const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : kPScaleStatic;
+    if (TRAIN && GP && p.pg && hf == 0 && qvalid) p.pg[(bh * p.nchunks + it) * p.lq + qrow] = g;
     m_run = m_new;
     // The rescale is skipped when no row of the wave moved its maximum (alpha == 1 exactly).
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       u32x4 pq[2], ph[2];
-      form_p<QP, F16, HP, GP>(s[kt], bmax[kt], p.c, m_new, psum, pq, ph);
+      form_p<QP, F16, HP, GP>(s[kt], bmax[kt], p.c, m_new, g, psum, pq, ph);
       u32x4 a[2][4];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -598,6 +603,7 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
     }
+    const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : kPScaleStatic;
 
     // ---- steps: P-hat(it, kt+1) beside S(it+1, kt) and O^T += V-hat^T P-hat^T(it, kt) -------
     // The last iteration also computes logits, from a stale K buffer, and drops them: a branch
@@ -605,7 +611,7 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
     const bool near_end = it + 2 >= n_iter;  // some copies are not issued: wait for all
     float psum = 0.0f;
     u32x4 pq[2][2], ph[2][2];
-    form_p<QP, F16, false, GP>(s[0], bmax[0], p.c, m_new, psum, pq[0], ph[0]);
+    form_p<QP, F16, false, GP>(s[0], bmax[0], p.c, m_new, g, psum, pq[0], ph[0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -622,7 +628,8 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pq[kt & 1][j]), acc[dt], 0, 0, 0);
         }
       if (kt < 3) {
-        form_p<QP, F16, false, GP>(s[kt + 1], bmax[kt + 1], p.c, m_new, psum, pq[(kt + 1) & 1], ph[(kt + 1) & 1]);
+        form_p<QP, F16, false, GP>(s[kt + 1], bmax[kt + 1], p.c, m_new, g, psum, pq[(kt + 1) & 1],
+                                   ph[(kt + 1) & 1]);
         // Pinned here: otherwise the compiler sinks this work into the next step, beside its use.
         AQ_OPAQUE(pq[(kt + 1) & 1][0]);
         AQ_OPAQUE(pq[(kt + 1) & 1][1]);
@@ -762,7 +769,7 @@ __global__ __launch_bounds__(256, 2) void rowmax_kernel(FwdParams p) {
 // fp16 P-hat V-hat product: both operands fake-quantized under unit global scales (a static scale
 // makes the values inexact in fp16; they are rounded to bf16 instead).
 static bool use_f16(unsigned flags) {
-  return (flags & kFlagV) && (flags & kFlagP) && !(flags & (kFlagGsfQkv | kFlagGsfP));
+  return (flags & kFlagV) && (flags & kFlagP) && !(flags & (kFlagGsfQkv | kFlagGsfP | kFlagTwoLevelP));
 }
 
 // The forward kernel of a call, by its mode: training (QL layout for dense calls), pipelined dense
@@ -828,10 +835,15 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   p.causal = a.causal;
   p.quant_q = (a.flags & kFlagQ) != 0;
   p.gq = vp.gq;
-  const bool qp = (a.flags & kFlagP) != 0, f16 = use_f16(a.flags), gp = qp && (a.flags & kFlagGsfP);
+  const bool qp = (a.flags & kFlagP) != 0, f16 = use_f16(a.flags);
+  const bool gp = qp && (a.flags & (kFlagGsfP | kFlagTwoLevelP));
   // Training outputs come as a set (lse, chunk maxima, O^hp).
   const bool train = a.o_hp && a.lse && a.cmax;
   if (!train && (a.o_hp || a.lse || a.cmax)) return hipErrorInvalidValue;
+  // Two-level P: the chunk-maximum array holds a second block of the same shape, P's global
+  // scale of every (row, chunk), for the backward.
+  p.two_level = (a.flags & kFlagTwoLevelP) != 0;
+  if (train && p.two_level) p.pg = a.cmax + (int64_t)a.batch * a.heads * p.nchunks * a.lq;
 
   if (a.flags & kFlagFinalMax) {
     // Row maxima first; the forward's running max starts there.

@@ -15,6 +15,7 @@ constexpr int kMaxCubesHost = 4096;  // cube-sparse backward: longest per-key-cu
 // Flag bits of a call (the ABI's AQ_* values): the four quantizers and the variants.
 constexpr unsigned kFlagQ = 1u, kFlagK = 2u, kFlagV = 4u, kFlagP = 8u;
 constexpr unsigned kFlagFinalMax = 16u, kFlagGsfQkv = 32u, kFlagGsfP = 64u, kFlagSmoothK = 128u;
+constexpr unsigned kFlagTwoLevelP = 256u;
 // Rows of the smooth-K partial sums: one per slab of this many keys.
 constexpr int kMeanSlab = 256;
 

@@ -23,7 +23,7 @@ import torch
 
 from . import _lib
 from ._lib import (AQ_FINAL_MAX, AQ_FLAGS_ALL, AQ_GSF_P, AQ_GSF_QKV, AQ_QUANT_ALL, AQ_QUANT_K, AQ_QUANT_P,
-                   AQ_QUANT_Q, AQ_QUANT_V, AQ_SMOOTH_K, aq_strides, check,
+                   AQ_QUANT_Q, AQ_QUANT_V, AQ_SMOOTH_K, AQ_TWO_LEVEL_P, aq_strides, check,
                    load)
 
 HEAD_SIZE = 128
@@ -121,6 +121,30 @@ def _check_qkv(q, k, v):
     return B, Lq, k.shape[1], H, k.shape[2], D
 
 
+def _chunk_stats(quant_flags: int, shape, device) -> torch.Tensor:
+    """The chunk-maximum array; under AQ_TWO_LEVEL_P with room after it for P's first-level
+    scales (include/attnqat.h), returned as the view of its first half."""
+    if quant_flags & AQ_TWO_LEVEL_P:
+        return torch.empty(2, *shape, dtype=torch.float32, device=device)[0]
+    return torch.empty(*shape, dtype=torch.float32, device=device)
+
+
+def _aux_dict(quant_flags: int, lse, cmax, ohp) -> dict:
+    aux = {"lse_log2": lse, "chunk_max_log2": cmax, "o_hp": ohp}
+    if quant_flags & AQ_TWO_LEVEL_P:
+        n = cmax.numel()
+        aux["p_scale"] = torch.as_strided(cmax, cmax.shape, cmax.stride(), cmax.storage_offset() + n)
+    return aux
+
+
+def _check_chunk_stats(quant_flags: int, cmax: torch.Tensor) -> None:
+    if quant_flags & AQ_TWO_LEVEL_P:
+        need = (cmax.storage_offset() + 2 * cmax.numel()) * 4
+        if cmax.untyped_storage().nbytes() < need:
+            raise ValueError("under AQ_TWO_LEVEL_P aux['chunk_max_log2'] must be followed in its storage "
+                             "by the first-level P scales the forward wrote (pass the forward's aux)")
+
+
 def attn_qat_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                  sm_scale: Optional[float] = None, quant_flags: int = AQ_QUANT_ALL,
                  training: bool = False):
@@ -128,7 +152,8 @@ def attn_qat_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
 
     Returns o [B, Lq, H, D] bf16; with ``training`` also a dict holding the
     auxiliary outputs the backward needs: lse_log2 [B, H, Lq], chunk_max_log2
-    [B, H, ceil(Lk/128), Lq] and o_hp [B, H, Lq, D] (fp32)."""
+    [B, H, ceil(Lk/128), Lq] and o_hp [B, H, Lq, D] (fp32); under AQ_TWO_LEVEL_P also p_scale,
+    P's first-level scale per (row, chunk), which lives right after chunk_max_log2 in one buffer."""
     B, Lq, Lk, H, Hkv, D = _check_qkv(q, k, v)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)  # the pages' default (attn_qat_train)
@@ -137,7 +162,7 @@ def attn_qat_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
     if training:
         C = (Lk + CHUNK - 1) // CHUNK
         lse = torch.empty(B, H, Lq, dtype=torch.float32, device=q.device)
-        cmax = torch.empty(B, H, C, Lq, dtype=torch.float32, device=q.device)
+        cmax = _chunk_stats(quant_flags, (B, H, C, Lq), q.device)
         ohp = torch.empty(B, H, Lq, D, dtype=torch.float32, device=q.device)
     ws = _workspace(0, B, H, Lq, Lk, q.device) if D == HEAD_SIZE and Hkv == H else torch.empty(
         256, dtype=torch.uint8, device=q.device)
@@ -148,7 +173,7 @@ def attn_qat_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
                               p(ohp), _aligned_ptr(ws), ws.numel() - 256, _stream_ptr(q)),
           "attn_qat_fwd")
     if training:
-        return o, {"lse_log2": lse, "chunk_max_log2": cmax, "o_hp": ohp}
+        return o, _aux_dict(quant_flags, lse, cmax, ohp)
     return o
 
 
@@ -171,6 +196,7 @@ def attn_qat_bwd(q, k, v, aux, d_o, causal: bool = False, sm_scale: Optional[flo
         t = aux[n]
         if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"aux[{n}] must be a contiguous fp32 device tensor")
+    _check_chunk_stats(quant_flags, aux["chunk_max_log2"])
     check(load().attn_qat_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), aux["o_hp"].data_ptr(),
                               d_o.data_ptr(), aux["lse_log2"].data_ptr(), aux["chunk_max_log2"].data_ptr(),
                               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, D, Lq, Lk,
@@ -259,7 +285,7 @@ def vsa_qat_fwd(q, k, v, grid=(16, 28, 56), cube=(4, 4, 8), sparsity: float = 0.
     lse = cmax = ohp = None
     if training:
         lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device)
-        cmax = torch.empty(B, H, max(topk, 1), L, dtype=torch.float32, device=q.device)
+        cmax = _chunk_stats(quant_flags, (B, H, max(topk, 1), L), q.device)
         ohp = torch.empty(B, H, L, D, dtype=torch.float32, device=q.device)
     ws = _workspace(2, B, H, L, L, q.device) if D == HEAD_SIZE and L > 0 else torch.empty(
         256, dtype=torch.uint8, device=q.device)
@@ -271,7 +297,7 @@ def vsa_qat_fwd(q, k, v, grid=(16, 28, 56), cube=(4, 4, 8), sparsity: float = 0.
                              ws.numel() - 256, _stream_ptr(q)),
           "vsa_qat_fwd")
     if training:
-        aux = {"sel": sel, "lse_log2": lse, "chunk_max_log2": cmax, "o_hp": ohp}
+        aux = {"sel": sel, **_aux_dict(quant_flags, lse, cmax, ohp)}
         if coarse:
             aux["o_coarse"] = oc
         return o, aux
@@ -298,6 +324,7 @@ def vsa_qat_bwd(q, k, v, aux, d_o, grid=(16, 28, 56), cube=(4, 4, 8), sparsity: 
         t = aux[name]
         if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"aux[{name}] must be a contiguous fp32 device tensor")
+    _check_chunk_stats(quant_flags, aux["chunk_max_log2"])
     sel = aux["sel"]
     if sel.dtype != torch.int32 or not sel.is_contiguous() or not sel.is_cuda:
         raise ValueError("aux['sel'] must be a contiguous int32 device tensor")
@@ -485,7 +512,7 @@ class QADLinear:
 
 
 __all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "AQ_FINAL_MAX", "AQ_GSF_QKV",
-           "AQ_GSF_P", "AQ_SMOOTH_K", "AQ_FLAGS_ALL", "fq_nvfp4",
+           "AQ_GSF_P", "AQ_SMOOTH_K", "AQ_TWO_LEVEL_P", "AQ_FLAGS_ALL", "fq_nvfp4",
            "static_global_scale", "attn_qat_fwd", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
            "vsa_qat_fwd", "vsa_qat_bwd", "vsa_qat_train", "vsa_topk", "qad_linear_fwd", "qad_linear_bwd",
            "qad_linear", "qad_observe_amax", "input_global_sf", "QADLinear"]

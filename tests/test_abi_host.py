@@ -62,7 +62,9 @@ def fwd(lib, **kw):
     (dict(lq=0), -1, "positive"),
     (dict(scale=float("nan")), -1, "softmax_scale"),
     (dict(scale=-1.0), -1, "softmax_scale"),
-    (dict(flags=256), -1, "quant_flags"),
+    (dict(flags=512), -1, "quant_flags"),
+    (dict(flags=15 | 256 | 16), -2, "AQ_TWO_LEVEL_P"),
+    (dict(flags=15 | 256 | 64), -2, "AQ_TWO_LEVEL_P"),
     (dict(Hkv=1), -2, "num_kv_heads"),
     (dict(causal=1, lk=32), -2, "causal"),
     (dict(ws_bytes=100), -1, "workspace"),

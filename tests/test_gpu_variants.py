@@ -1,11 +1,12 @@
-"""GPU parity of the attention variants (AQ_FINAL_MAX, AQ_GSF_QKV, AQ_GSF_P, AQ_SMOOTH_K) against
-the oracle, within the stated attention tolerance (tests/parity.py).
+"""GPU parity of the attention variants (AQ_FINAL_MAX, AQ_GSF_QKV, AQ_GSF_P, AQ_SMOOTH_K,
+AQ_TWO_LEVEL_P) against the oracle, within the stated attention tolerance (tests/parity.py).
 
 Dense forward (inference and training outputs) and straight-through backward on ragged, cross
 and causal shapes; the cube-sparse forward and backward on a small grid (compared where the two
 selections agree, as in the other cube-sparse tests); sampled rows of the 448x896x61 workload
-under the final-max statistics.  Properties that hold for any input: under AQ_FINAL_MAX every
-chunk-maximum row equals the row's final maximum, and lse is unchanged up to rounding."""
+under the final-max statistics and under two-level P.  Properties that hold for any input: under AQ_FINAL_MAX every
+chunk-maximum row equals the row's final maximum, and lse is unchanged up to rounding; under
+AQ_TWO_LEVEL_P the first-level scales the forward stores match the oracle's to fp32 rounding."""
 import math
 
 import numpy as np
@@ -20,8 +21,8 @@ pytestmark = pytest.mark.gpu
 LOG2E = 1.0 / math.log(2.0)
 SCALE = 1.0 / math.sqrt(128)
 ALL = 15
-FM, GQKV, GP, SK = 16, 32, 64, 128
-VARIANTS = [ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, SK, ALL | FM | GQKV | GP | SK]
+FM, GQKV, GP, SK, TWO = 16, 32, 64, 128, 256
+VARIANTS = [ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, SK, ALL | FM | GQKV | GP | SK, ALL | TWO, ALL | TWO | GQKV | SK]
 
 
 @pytest.fixture(scope="module")
@@ -58,6 +59,12 @@ def test_dense_forward_and_backward(m, flags, Lq, Lk, causal):
     assert_close(aux["o_hp"].cpu().numpy(), r["o_hp"], f"o_hp flags={flags}")
     lse = aux["lse_log2"].cpu().numpy() / LOG2E
     assert np.abs(lse - r["lse"]).max() < 1e-4
+    if flags & TWO:
+        # the first-level scales of the live (row, chunk) pairs
+        ps = aux["p_scale"].cpu().numpy()
+        for c in range(ps.shape[2]):
+            reach = np.ones(Lq, bool) if not causal else (np.arange(Lq) >= 128 * c)
+            assert np.allclose(ps[:, :, c][..., reach], r["pscale"][..., c][..., reach], rtol=1e-5, atol=0)
     if flags & FM:
         # every chunk-maximum row holds the final row maximum
         cm = aux["chunk_max_log2"].cpu().numpy()
@@ -75,7 +82,7 @@ def test_static_scales_differ_from_unit(m):
     q, k, v = rand(1, 256, 2, 205), rand(1, 256, 2, 206), rand(1, 256, 2, 207)
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
     base = m.attn_qat_fwd(qg, kg, vg)
-    for fl in (ALL | FM, ALL | GQKV, ALL | GP, ALL | SK):
+    for fl in (ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, ALL | TWO):
         assert not torch.equal(m.attn_qat_fwd(qg, kg, vg, quant_flags=fl), base), fl
 
 
@@ -92,7 +99,7 @@ def agreement(sel_gpu, sel_ref):
     return qa, ka
 
 
-@pytest.mark.parametrize("flags", [ALL | FM, ALL | FM | GQKV | GP | SK])
+@pytest.mark.parametrize("flags", [ALL | FM, ALL | FM | GQKV | GP | SK, ALL | TWO | GQKV])
 def test_cube_sparse_forward_and_backward(m, flags):
     grid, L = (4, 8, 32), 1024
     q, k, v = synth.qkv_headscaled(1, L, 2, 128, seed=208, scaled=False)
@@ -112,13 +119,21 @@ def test_cube_sparse_forward_and_backward(m, flags):
         assert_close(bhrd(t)[mask], rb[name][mask], f"vsa {name} flags={flags}")
 
 
-def test_final_max_wan_448x896x61_sampled_rows(m):
+@pytest.mark.parametrize("flags", [ALL | FM, ALL | TWO])
+def test_wan_448x896x61_sampled_rows(m, flags):
     q, k, v = synth.wan_448x896x61()
     L = q.shape[1]
-    o = m.attn_qat_fwd(q.cuda(), k.cuda(), v.cuda(), quant_flags=ALL | FM)
+    o = m.attn_qat_fwd(q.cuda(), k.cuda(), v.cuda(), quant_flags=flags)
     torch.cuda.synchronize()
     rows = synth.sample_rows(L, 32, seed=12).numpy()
     h = [0, 7]
     r = oracle.attn_fwd(bhld_bits(q[:, :, h]), bhld_bits(k[:, :, h]), bhld_bits(v[:, :, h]), SCALE,
-                        flags=ALL | FM, rows=rows)
-    assert_close(bhrd(o[:, :, h], rows), r["o"], "final-max o at 448x896x61")
+                        flags=flags, rows=rows)
+    assert_close(bhrd(o[:, :, h], rows), r["o"], f"o at 448x896x61 flags={flags}")
+
+
+def test_two_level_rejections(m):
+    q = rand(1, 128, 1, 221).cuda()
+    for extra in (FM, GP):
+        with pytest.raises(NotImplementedError):
+            m.attn_qat_fwd(q, q, q, quant_flags=ALL | TWO | extra)
