@@ -225,7 +225,8 @@ enum { QF_Q = 1, QF_K = 2, QF_V = 4, QF_P = 8 };
    (use_global_sf_qkv, use_global_sf_p, smooth_k; "sm100_exact_m" and the
    reference-order statistics of the "Attn-QAT Training" guide); their
    arithmetic is the reading given with each use below. */
-enum { QF_FINAL_MAX = 16, QF_GSF_QKV = 32, QF_GSF_P = 64, QF_SMOOTH_K = 128, QF_TWO_LEVEL_P = 256 };
+enum { QF_FINAL_MAX = 16, QF_GSF_QKV = 32, QF_GSF_P = 64, QF_SMOOTH_K = 128, QF_TWO_LEVEL_P = 256,
+       QF_SMOOTH_Q = 512 };
 
 /* Two-level quantization of P ([API] two_level_quant_p_sage3; the
    SageAttention3 recipe the flag is named after): a first, per-row level maps
@@ -250,10 +251,12 @@ static float two_level_scale(const float *P, const int64_t *kc, int chunk)
    rounded to bf16 after dequantization; under the unit global scale this
    changes nothing (an E2M1 value times an E4M3 scale is exact in bf16). */
 typedef struct {
-    float *qh; /* [Lq, D] */
-    float *kh; /* [Lk, D] */
-    float *vh; /* [Lk, D] */
-    float gp;  /* global scale of P's blocks */
+    float *qh;     /* [Lq, D] */
+    float *kh;     /* [Lk, D] */
+    float *vh;     /* [Lk, D] */
+    float gp;      /* global scale of P's blocks */
+    float *qbar;   /* smooth-Q: [D] the queries' mean, else NULL */
+    double *delta; /* smooth-Q: [Lk] <qbar, k-hat_j>, else NULL */
 } head_ops;
 
 /* Global scales of one call: unit, or static per tensor (QF_GSF_QKV: the
@@ -310,6 +313,24 @@ static void smooth_rows(float *x, int64_t L, int D)
     }
 }
 
+/* Smooth-Q (flag smooth_q; SageAttention2's smoothing of Q): the queries'
+   mean over the sequence, per channel (the smooth-K reading: fp64 sum / L,
+   rounded to fp32), is subtracted before quantization, and its part of every
+   logit is added back in full precision: S_ij = scale * (<q-hat'_i, k-hat_j>
+   + delta_j) with q-hat' = fq(fp32(q - mean)) and delta_j = <mean, k-hat_j>
+   (fp64).  Unlike smooth-K the shift is per key, so it must be restored.
+   Under the straight-through estimator the effective query is q-hat' + mean:
+   dQ is unchanged (dS k-hat) and dK_j = scale * sum_i dS_ij (q-hat'_i + mean). */
+static void smooth_rows_mean(float *x, int64_t L, int D, float *mean)
+{
+    for (int d = 0; d < D; ++d) {
+        double s = 0.0;
+        for (int64_t j = 0; j < L; ++j) s += (double)x[j * D + d];
+        mean[d] = (float)(s / (double)L);
+    }
+    smooth_rows(x, L, D);
+}
+
 /* 448*6 / max(amax, 1e-12) over all B*H heads of a [B*H, L, D] tensor, on
    the values that are quantized (smoothed first when `smooth`). */
 static float tensor_scale(const uint16_t *x, int64_t BH, int64_t L, int D, int smooth)
@@ -336,7 +357,7 @@ static call_scales make_scales(const uint16_t *q, const uint16_t *k, const uint1
 {
     call_scales c = {1.0f, 1.0f, 1.0f, 1.0f};
     if (flags & QF_GSF_QKV) {
-        c.gq = tensor_scale(q, BH, Lq, D, 0);
+        c.gq = tensor_scale(q, BH, Lq, D, (flags & QF_SMOOTH_Q) != 0);
         c.gk = tensor_scale(k, BH, Lk, D, (flags & QF_SMOOTH_K) != 0);
         c.gv = tensor_scale(v, BH, Lk, D, 0);
     }
@@ -351,16 +372,30 @@ static void make_head_ops(head_ops *h, const uint16_t *q, const uint16_t *k, con
     h->kh = (float *)malloc(sizeof(float) * Lk * D);
     h->vh = (float *)malloc(sizeof(float) * Lk * D);
     h->gp = cs->gp;
+    h->qbar = NULL;
+    h->delta = NULL;
     load_head(q, h->qh, Lq, D);
     load_head(k, h->kh, Lk, D);
     load_head(v, h->vh, Lk, D);
     if (flags & QF_SMOOTH_K) smooth_rows(h->kh, Lk, D);
+    if (flags & QF_SMOOTH_Q) {
+        h->qbar = (float *)malloc(sizeof(float) * D);
+        smooth_rows_mean(h->qh, Lq, D, h->qbar);
+    }
     if (flags & QF_Q) quant_rows_D(h->qh, Lq, D, cs->gq);
     if (flags & QF_K) quant_rows_D(h->kh, Lk, D, cs->gk);
     if (flags & QF_V) quant_cols_L(h->vh, Lk, D, cs->gv);
     round_bf16(h->qh, Lq * D);
     round_bf16(h->kh, Lk * D);
     round_bf16(h->vh, Lk * D);
+    if (h->qbar) {
+        h->delta = (double *)malloc(sizeof(double) * Lk);
+        for (int64_t j = 0; j < Lk; ++j) {
+            double t = 0.0;
+            for (int d = 0; d < D; ++d) t += (double)h->qbar[d] * (double)h->kh[j * D + d];
+            h->delta[j] = t;
+        }
+    }
 }
 
 static void free_head_ops(head_ops *h)
@@ -368,15 +403,24 @@ static void free_head_ops(head_ops *h)
     free(h->qh);
     free(h->kh);
     free(h->vh);
+    free(h->qbar);
+    free(h->delta);
 }
 
-/* S_ij = fp32(scale * <q_i, k_j>), dot product in fp64. */
+/* S_ij = fp32(scale * (<q_i, k_j> + delta_j)), in fp64 (delta: smooth-Q). */
 static float logit(const head_ops *h, int64_t i, int64_t j, int D, double scale)
 {
     const float *a = h->qh + i * D, *b = h->kh + j * D;
     double s = 0.0;
     for (int d = 0; d < D; ++d) s += (double)a[d] * (double)b[d];
+    if (h->delta) s += h->delta[j];
     return (float)(scale * s);
+}
+
+/* The query the key gradients see: q-hat (+ the smoothed-away mean). */
+static double q_eff(const head_ops *h, int64_t i, int d, int D)
+{
+    return (double)h->qh[i * D + d] + (h->qbar ? (double)h->qbar[d] : 0.0);
 }
 
 /* Online-softmax forward for one query row (the fine stage of both the dense
@@ -668,7 +712,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                     block_weights(&x, i, s, nb, lse[i], cmax + i * C, pg + i * C, A, Ah);
                     double dS = A[j - s] * (dot_do_v(&x, i, j) - Dv[i]);
                     for (int d = 0; d < D; ++d) {
-                        if (ok) ok[d] += scale * dS * (double)hd.qh[i * D + d];
+                        if (ok) ok[d] += scale * dS * q_eff(&hd, i, d, D);
                         if (ov) ov[d] += Ah[j - s] * (double)bf16_to_f32(x.dO[i * D + d]);
                     }
                 }
@@ -926,7 +970,7 @@ int oracle_vsa_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
                                          (float)pg[i * topk + (fm ? 0 : t)], A, Ah);
                         double dS = A[j - s] * (dot_do_v(&x, i, j) - Dv[i]);
                         for (int d = 0; d < D; ++d) {
-                            if (ok) ok[d] += scale * dS * (double)hd.qh[i * D + d];
+                            if (ok) ok[d] += scale * dS * q_eff(&hd, i, d, D);
                             if (ov) ov[d] += Ah[j - s] * (double)bf16_to_f32(x.dO[i * D + d]);
                         }
                     }

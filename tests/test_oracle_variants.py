@@ -336,3 +336,93 @@ def test_two_level_p_rejects_final_max_and_static_p():
             oracle.attn_fwd(q, k, v, SCALE, flags=ALL | TWO | extra)
         with pytest.raises(ValueError):
             oracle.vsa_fwd(q, k, v, SCALE, cube_tokens=64, sparsity=0.0, flags=ALL | TWO | extra)
+
+
+# ----------------------------------------------------------------- smooth Q
+
+SQ = oracle.SMOOTH_Q
+
+
+def q_smoothed_eff(q_bits, g=1.0, quant=True):
+    """The query the method multiplies with under smooth-Q: fq(fp32(q - mean)) (without `quant`,
+    fp32(q - mean)) rounded to bf16 as the matmul operand, plus the mean (per (b, h, channel): fp64
+    sum / L rounded to fp32), in fp64; built from the pinned fp32 codec."""
+    qf = f32(q_bits)
+    mean = (qf.astype(np.float64).sum(axis=2, keepdims=True) / qf.shape[2]).astype(np.float32)
+    qs = (qf - mean).astype(np.float32)
+    if quant:
+        qs = oracle.fq_f32_rows(qs.reshape(-1, D), g=g).reshape(qs.shape)
+    qq = f32(bits_of(qs))
+    return torch.from_numpy(qq.astype(np.float64) + mean.astype(np.float64))
+
+
+def test_smooth_q_without_quantization_is_softmax_attention():
+    # the subtracted mean's share of every logit is added back: attention on the restored query
+    # (the smoothed query rounded to bf16 as the matmul operand, plus the mean), which is plain
+    # attention on the original Q up to that bf16 rounding
+    Lq, Lk = 40, 200
+    q, k, v = rand_bits((1, 2, Lq, D), 161, 1.0, 2.0), rand_bits((1, 2, Lk, D), 162), rand_bits((1, 2, Lk, D), 163)
+    r = oracle.attn_fwd(q, k, v, SCALE, flags=SQ)
+    ref = sdpa64(q_smoothed_eff(q, quant=False), f64(k), f64(v), SCALE).numpy()
+    assert np.abs(r["o"] - ref).max() < 1e-6 * np.abs(ref).max()
+    plain = sdpa64(f64(q), f64(k), f64(v), SCALE).numpy()
+    assert np.abs(r["o"] - plain).max() < 2.0 ** -7 * np.abs(plain).max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_smooth_q_is_attention_on_the_restored_query(causal):
+    # With Q and K quantized (P unquantized) the output is softmax attention with the query
+    # fq(q - mean) + mean and the quantized keys; the backward is float64 autograd of it (dQ passes
+    # straight through to q, dK sees the restored query).
+    L = 150
+    q, k, v = rand_bits((1, 2, L, D), 164, 1.0, 1.5), rand_bits((1, 2, L, D), 165), rand_bits((1, 2, L, D), 166)
+    do = rand_bits((1, 2, L, D), 167)
+    fl = oracle.QUANT_Q | oracle.QUANT_K | oracle.QUANT_V | SQ
+    r = oracle.attn_fwd(q, k, v, SCALE, causal=causal, flags=fl)
+    Qe = q_smoothed_eff(q).requires_grad_()
+    K = f64(oracle.fq_bf16(k, -1)).requires_grad_()
+    V = f64(oracle.fq_bf16(v, 2)).requires_grad_()
+    ref = sdpa64(Qe, K, V, SCALE, causal)
+    assert np.abs(r["o"] - ref.detach().numpy()).max() < 1e-6 * np.abs(ref.detach().numpy()).max()
+    ref.backward(f64(do))
+    b = oracle.attn_bwd(q, k, v, do, SCALE, causal=causal, flags=fl)
+    for name, want in (("dq", Qe.grad), ("dk", K.grad), ("dv", V.grad)):
+        w = want.numpy()
+        assert np.abs(b[name] - w).max() < 1e-6 * np.abs(w).max(), name
+
+
+def test_smooth_q_reduces_the_quantization_error_of_an_offset_query():
+    # the point of the smoothing: a query with a large common offset loses less to its quantization
+    Lq, Lk = 32, 256
+    q, k, v = rand_bits((1, 1, Lq, D), 168, 1.0, 4.0), rand_bits((1, 1, Lk, D), 169), rand_bits((1, 1, Lk, D), 170)
+    exact = sdpa64(f64(q), f64(k), f64(v), SCALE).numpy()
+    plain = oracle.attn_fwd(q, k, v, SCALE, flags=oracle.QUANT_Q)["o"]
+    smooth = oracle.attn_fwd(q, k, v, SCALE, flags=oracle.QUANT_Q | SQ)["o"]
+    assert np.abs(smooth - exact).mean() < 0.5 * np.abs(plain - exact).mean()
+
+
+def test_smooth_q_with_static_scale_and_smooth_k_and_sparse():
+    # the static Q scale is taken on the smoothed queries; with smooth-K as well the keys are
+    # smoothed first (the logits' per-row shift cancels in the softmax); at sparsity 0 the
+    # cube-sparse variant equals the dense one, forward and backward
+    L = 256
+    q, k, v = rand_bits((1, 1, L, D), 171, 1.0, 2.0), rand_bits((1, 1, L, D), 172, 1.0, 1.0), rand_bits((1, 1, L, D), 173)
+    fl = oracle.QUANT_Q | oracle.QUANT_K | oracle.QUANT_V | SQ | oracle.GSF_QKV
+    r = oracle.attn_fwd(q, k, v, SCALE, flags=fl)
+    qf = f32(q)
+    mean = (qf.astype(np.float64).sum(axis=2, keepdims=True) / L).astype(np.float32)
+    gq = np.float32(np.float32(2688.0) / np.float32(np.abs((qf - mean).astype(np.float32)).max()))
+    Qe = q_smoothed_eff(q, g=float(gq))
+    K = f64(oracle.fq_bf16(k, -1, g=oracle.static_scale_bf16(k)))
+    V = f64(oracle.fq_bf16(v, 2, g=oracle.static_scale_bf16(v)))
+    ref = sdpa64(Qe, K, V, SCALE).numpy()
+    assert np.abs(r["o"] - ref).max() < 1e-6 * np.abs(ref).max()
+    fl2 = ALL | SQ | oracle.SMOOTH_K
+    s = oracle.vsa_fwd(q, k, v, SCALE, sparsity=0.0, flags=fl2)
+    d = oracle.attn_fwd(q, k, v, SCALE, flags=fl2)
+    assert np.array_equal(s["o_fine"], d["o"])
+    do = rand_bits((1, 1, L, D), 174)
+    sb = oracle.vsa_bwd(q, k, v, do, SCALE, sparsity=0.0, flags=fl2, krows=np.arange(0, L, 29))
+    db = oracle.attn_bwd(q, k, v, do, SCALE, flags=fl2, krows=np.arange(0, L, 29))
+    for name in ("dq", "dk", "dv"):
+        assert np.allclose(sb[name], db[name], rtol=0, atol=1e-12), name
