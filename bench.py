@@ -21,7 +21,7 @@ its coarse stage, and its backward 2.5x the fine stage; fq contributes time but
 no FLOP.  After the step loop, the dense and cube-sparse inference forwards and
 fq on its own (back-to-back launches) are timed for the "attention" and "fq"
 objects, the attention variants (final-max statistics, static scales,
-smooth-K, two-level P) for the "variants" object, and the NVFP4 QAD linear on the model's
+smooth-K, two-level P, smooth-Q) for the "variants" object, and the NVFP4 QAD linear on the model's
 feed-forward projections (25088 tokens, 1536 -> 8960 -> 1536) for the "linear"
 object.  Per-kernel durations come
 from HIP events the library records around each of its launches on the launch
@@ -286,7 +286,7 @@ def main():
     fl_fwd = fl["fwd"]  # conventional 4*B*H*L^2*D (the final-max row-maximum pass is not counted)
     variants = {}
     for name, flg in (("final_max", 15 | 16), ("gsf_qkv", 15 | 32), ("gsf_p", 15 | 64), ("smooth_k", 15 | 128),
-                      ("two_level_p", 15 | 256), ("all", 255)):
+                      ("two_level_p", 15 | 256), ("smooth_q", 15 | 512), ("all", 255)):
         ms = timed(lambda: m.attn_qat_fwd(qd, kd, vd, quant_flags=flg))
         variants[name] = {"flags": flg, "inference_fwd_ms": round(ms, 4),
                           "inference_fwd_TFLOP/s": round(fl_fwd / (ms * 1e-3) / 1e12, 1)}

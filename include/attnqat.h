@@ -61,8 +61,8 @@ enum {
 };
 
 /* Variants, OR-ed into the same flags word.  [API] lists the kernel flags use_global_sf_qkv,
-   use_global_sf_p, smooth_k and two_level_quant_p_sage3 (all off in attn_qat_train) and [META]'s
-   precision records carry the first three; [DOC]'s environment table names reference-order softmax statistics
+   use_global_sf_p, smooth_k, smooth_q and two_level_quant_p_sage3 (all off in attn_qat_train) and
+   [META]'s precision records carry the first three; [DOC]'s environment table names reference-order softmax statistics
    (FASTVIDEO_ATTN_QAT_FWD_EXACT_M).  None is defined on the pages; the readings implemented:
      AQ_FINAL_MAX  every P relative to its row's final maximum over all keys (the selected keys for
                    vsa_qat_fwd) instead of the running maximum of 128-key chunks; the forward
@@ -82,6 +82,11 @@ enum {
                    the size: its second half, laid out like the first, receives g of every
                    (row, chunk), which the backward reads.  Not combinable with AQ_FINAL_MAX or
                    AQ_GSF_P (AQ_ENOTSUP).
+     AQ_SMOOTH_Q   SageAttention2's smoothing of Q: the queries' per-channel mean over the sequence
+                   (the AQ_SMOOTH_K reading) is subtracted before quantization and its share of the
+                   logits, delta_j = <mean, k-hat_j> (fp32), is added back to every logit of key j.
+                   The backward's key gradients see the restored query q-hat + mean; dQ is
+                   unchanged.  Under AQ_GSF_QKV the static Q scale is taken on the smoothed Q.
    Under AQ_GSF_QKV, AQ_GSF_P or AQ_TWO_LEVEL_P the P-hat V-hat product runs in bf16 (the values are
    no longer exact in fp16). */
 enum {
@@ -90,7 +95,8 @@ enum {
     AQ_GSF_P = 64,
     AQ_SMOOTH_K = 128,
     AQ_TWO_LEVEL_P = 256,
-    AQ_FLAGS_ALL = 511
+    AQ_SMOOTH_Q = 512,
+    AQ_FLAGS_ALL = 1023
 };
 
 /* Element strides of a 4-D attention tensor, indexed (batch, head, token, d) with d contiguous. */
@@ -132,7 +138,7 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  * Every bf16 tensor of the attention entry points starts 16-byte aligned and has strides that
  * are multiples of 8 elements and below 2^24 (rows move in 16-byte pieces); lq, lk <= 2^30.
  * Q-hat, K-hat along D and V-hat along keys are fake-quantized per quant_flags (quantizers and
- * the AQ_FINAL_MAX / AQ_GSF_QKV / AQ_GSF_P / AQ_SMOOTH_K / AQ_TWO_LEVEL_P variants above).  The keys are
+ * the AQ_FINAL_MAX / AQ_GSF_QKV / AQ_GSF_P / AQ_SMOOTH_K / AQ_TWO_LEVEL_P / AQ_SMOOTH_Q variants above).  The keys are
  * visited in chunks of 128 ([0,128), [128,256), ...); in chunk c the running row maximum m_c of
  * the logits softmax_scale * <q-hat, k-hat> is refreshed first, then P = exp(logit - m_c) is
  * formed, fake-quantized in 16-key blocks (AQ_QUANT_P) and multiplied with V-hat on BF16 MFMA;

@@ -73,6 +73,9 @@ struct BwdParams {
   // Two-level P: [BH, Ck or nsel, lq] P's global scale per (query, chunk) as the forward used it,
   // laid out like the chunk maxima; null otherwise.
   const float *pg;
+  // Smooth-Q: delta [BH, Ck*128] added to every logit, and the queries' mean [BH, 128], which the
+  // key gradients see added back to Q-hat; null otherwise.
+  const float *delta, *qmean;
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -95,7 +98,7 @@ constexpr int kDqLds = 2 * 65536;
 // 0 and 1 must pick the 64-byte quarter (the two high bits of the 16-byte column).
 __device__ __forceinline__ int sw_kd(int r) { return ((r >> 2) & 1) | ((r >> 3) & 2) | ((r & 3) << 2); }
 
-template <bool SPARSE>
+template <bool SPARSE, bool SQ>
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) uint8_t lds[kDqLds];
   const uint32_t lds0 = lds_addr(lds);
@@ -187,11 +190,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
     const bool diag = p.causal && (ch + 1) * kChunk - 1 > qc * kChunk + qg * 32;
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // smooth-Q: the logit chain starts from delta of the lane's 16 keys, as the forward's does
+      f32x16 s, dp = f32x16{};
+      if constexpr (SQ) s = delta16(p.delta + (bh * p.Ck + ch) * kChunk + 64 * kh + 32 * k2 + 16 * hf);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const uint32_t at = (ka ^ (32 * t)) + k2 * 8192;
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at)), qf[t], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at)), qf[t], (SQ || t > 0) ? s : f32x16{}, 0,
+                                                    0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at + 32768)), of[t], dp, 0, 0, 0);
       }
       if (tail || diag || !qvalid) {
@@ -266,7 +272,8 @@ constexpr int kLdsR = 65536, kLdsStat = 131072;
 constexpr int kLdsOneHot = kLdsStat + 2 * 1024;  // two one-hot B operands, 16 bytes per lane
 constexpr int kMaxCubes = 4096;                   // cube-sparse: longest query-cube list
 constexpr int kLdsList = kLdsOneHot + 2048;       // that list (+ its length), int32
-constexpr int kDkdvLds = kLdsList + 4 * (kMaxCubes + 1);
+constexpr int kLdsDelta = kLdsList + 4 * (kMaxCubes + 1);  // smooth-Q: delta of the chunk's 128 keys
+constexpr int kDkdvLds = kLdsDelta + 4 * kChunk;
 
 // Lane layout of the S^T B operand: lane n takes query pi(n) of its wave's 32 (bits 2 and 3 of n
 // exchanged).  After the one-hot transposition the 8 k-slots of each lane half are then 8
@@ -316,9 +323,9 @@ __device__ __forceinline__ void dkdv_stage_tile(const BwdParams &p, const DkdvLa
 }
 
 // One 64-query tile for one wave (BUF: which tile buffer holds it).
-template <int BUF, bool GP>
+template <int BUF, bool GP, bool SQ>
 __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, DkdvLane ln, int64_t qb, bool tail,
-                                          f32x16 *dk, f32x16 *dv) {
+                                          f32x16 *dk, f32x16 *dv, float &csum) {
   // LDS byte addresses; lds0 is 256-byte aligned, so the swizzle XORs act on the offsets alone.
   uint32_t ka = lds0 + ln.k_off, ra = lds0 + kLdsR + ln.r_off, ta0 = lds0 + kLdsR + ln.tr_off;
   AQ_OPAQUE(ka);
@@ -326,7 +333,19 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
   AQ_OPAQUE(ta0);
   constexpr uint32_t kQ = BUF * 32768, kO = BUF * 32768 + 16384;  // buffer offsets from kLdsR
 
+  // Smooth-Q: the logit chain starts from delta of the lane's 16 keys, as the forward's does.
   f32x16 s = f32x16{}, dp = f32x16{};
+  if (SQ) {
+    const uint32_t da = lds0 + kLdsDelta + 4 * (ln.key_base % kChunk);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const u32x4 v = lds_read16(da + 16 * r4);
+      s[4 * r4 + 0] = u2f(v.x);
+      s[4 * r4 + 1] = u2f(v.y);
+      s[4 * r4 + 2] = u2f(v.z);
+      s[4 * r4 + 3] = u2f(v.w);
+    }
+  }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const uint32_t kt_ = ka ^ (32 * t), rt = ra ^ (32 * t);
@@ -397,6 +416,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
     for (int kk = 0; kk < 8; ++kk) {
       fa[kk] = ta[8 * s2 + kk];
       fs[kk] = ts[8 * s2 + kk];
+      if (SQ) csum += fs[kk];  // smooth-Q: this key's dS summed over the queries (the dK MFMA's values)
     }
     const bf16x8 ba = pack8_exact(fa), bs = pack8_exact(fs);
 #pragma unroll
@@ -412,7 +432,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
   }
 }
 
-template <bool SPARSE, bool GP>
+template <bool SPARSE, bool GP, bool SQ>
 __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) uint8_t lds[kDkdvLds];
   const uint32_t lds0 = lds_addr(lds);
@@ -496,6 +516,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
       *(bf16x8 *)(lds + kLdsOneHot + lane * 16) = onehot_b(lane, 0);
       *(bf16x8 *)(lds + kLdsOneHot + 1024 + lane * 16) = onehot_b(lane, 1);
     }
+    if (SQ && wave == 1 && lane < 32)
+      *(f32x4 *)(lds + kLdsDelta + lane * 16) = *(const f32x4 *)(p.delta + (bh * p.Ck + kc) * kChunk + 4 * lane);
   }
   if (ntiles > 0) dkdv_stage_tile(p, ln, bh, bb, hh, tile_cm(0), tile_qb(0), lds, 0, wave, lane);
 
@@ -506,6 +528,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
+  float csum = 0.0f;
 
   // Tiles in pairs (buffer 0, then buffer 1), then an odd last tile in buffer 0.
   int64_t t = 0;
@@ -513,16 +536,16 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
     AQ_WAIT_VMCNT(0);  // this wave's copies of tile t
     __syncthreads();   // everyone's copies landed; buffer 1 is free
     dkdv_stage_tile(p, ln, bh, bb, hh, tile_cm(t + 1), tile_qb(t + 1), lds, 1, wave, lane);
-    dkdv_tile<0, GP>(p, lds0, ln, tile_qb(t), tail, dk, dv);
+    dkdv_tile<0, GP, SQ>(p, lds0, ln, tile_qb(t), tail, dk, dv, csum);
     AQ_WAIT_VMCNT(0);
     __syncthreads();  // buffer 0 is free
     if (t + 2 < ntiles) dkdv_stage_tile(p, ln, bh, bb, hh, tile_cm(t + 2), tile_qb(t + 2), lds, 0, wave, lane);
-    dkdv_tile<1, GP>(p, lds0, ln, tile_qb(t + 1), tail, dk, dv);
+    dkdv_tile<1, GP, SQ>(p, lds0, ln, tile_qb(t + 1), tail, dk, dv, csum);
   }
   if (t < ntiles) {
     AQ_WAIT_VMCNT(0);
     __syncthreads();
-    dkdv_tile<0, GP>(p, lds0, ln, tile_qb(t), tail, dk, dv);
+    dkdv_tile<0, GP, SQ>(p, lds0, ln, tile_qb(t), tail, dk, dv, csum);
   }
 
   // The two waves of a key group add their partial sums: wave qh = 0 finishes dK, qh = 1 dV.
@@ -539,9 +562,27 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
         *(f32x4 *)(dst + ((dt * 4 + a) * 64 + lane) * 4) =
             f32x4{give[dt][4 * a], give[dt][4 * a + 1], give[dt][4 * a + 2], give[dt][4 * a + 3]};
   }
+  if (SQ) {
+    // smooth-Q: this key's dS summed over all queries (both lane halves, then both query waves)
+    csum += __shfl_xor(csum, 32, 64);
+    if (qh == 1 && hf == 0) ((float *)(lds + kLdsStat))[kg * 32 + n] = csum;
+  }
   __syncthreads();
   const int64_t key = kc * kChunk + kg * 32 + n;
   f32x16 *mine = qh == 0 ? dk : dv;
+  if (SQ && qh == 0) {
+    // dK_j += (sum_i dS_ij) * mean: the key gradients see the restored query q-hat + mean
+    const float cs = csum + ((const float *)(lds + kLdsStat))[kg * 32 + n];
+    const float *qm = p.qmean + bh * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 m = *(const f32x4 *)(qm + 32 * dt + 8 * a + 4 * hf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dk[dt][4 * a + i] = __builtin_fmaf(cs, m[i], dk[dt][4 * a + i]);
+      }
+  }
   const float *src = (const float *)(lds + (kg * 2 + (qh == 0 ? 0 : 1)) * 16384);
   const float mul = qh == 0 ? p.scale : 1.0f;
   if (key >= p.lk) return;
@@ -577,6 +618,15 @@ __global__ __launch_bounds__(256) void vsa_slot_kernel(const int32_t *__restrict
   slot_t[gid] = (int16_t)s;
 }
 
+template <bool SQ>
+static void launch_dkdv(const BwdParams &p, bool sparse, bool gp, dim3 grid, hipStream_t stream) {
+  const char *nm = sparse ? "vsa_bwd_dkdv" : "bwd_dkdv";
+  if (sparse && gp) AQ_LAUNCH(nm, (bwd_dkdv_kernel<true, true, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
+  else if (sparse) AQ_LAUNCH(nm, (bwd_dkdv_kernel<true, false, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
+  else if (gp) AQ_LAUNCH(nm, (bwd_dkdv_kernel<false, true, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
+  else AQ_LAUNCH(nm, (bwd_dkdv_kernel<false, false, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
+}
+
 // Shared by the dense and the cube-sparse backward: operand prepasses, D, dQ, dK/dV.
 hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspace &w, const int32_t *sel,
                              const int16_t *slot_t, int64_t nsel, hipStream_t stream) {
@@ -588,10 +638,11 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   // The forward's operands again (same scales and smoothing, recomputed from the same tensors).
   if ((e = launch_variant_prep(a, w, stream))) return e;
   const VariantPtrs vp = variant_ptrs(a, w);
-  if ((e = launch_tile_prepass(a.q, a.sq, a.batch, a.heads, a.lq, qd_q, ws + w.qq, nullptr, vp.gq, nullptr, stream)))
+  if ((e = launch_tile_prepass(a.q, a.sq, a.batch, a.heads, a.lq, qd_q, ws + w.qq, nullptr, vp.gq, vp.qmean, stream)))
     return e;
   if ((e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, qd_k, ws + w.kq, nullptr, vp.gk, vp.kmean, stream)))
     return e;
+  if ((e = launch_qk_delta(a, w, stream))) return e;
   if ((e = launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qr_v, ws + w.vq, nullptr, vp.gv, nullptr, stream)))
     return e;
 
@@ -630,22 +681,24 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   p.slot_t = slot_t;
   p.nsel = nsel;
   if ((a.flags & kFlagTwoLevelP) && p.quant_p) p.pg = a.cmax + bh * (sel ? nsel : p.Ck) * a.lq;
+  p.delta = vp.delta;
+  p.qmean = vp.qmean;
 
   p.nwork = bh * p.Cq;
   p.per_xcd = (p.nwork + 7) / 8;
   const dim3 dq_grid((unsigned)(p.per_xcd * 8));
-  if (sel) AQ_LAUNCH("vsa_bwd_dq", bwd_dq_kernel<true>, dq_grid, dim3(kDqThreads), 0, stream, p);
-  else AQ_LAUNCH("bwd_dq", bwd_dq_kernel<false>, dq_grid, dim3(kDqThreads), 0, stream, p);
+  if (sel && p.delta) AQ_LAUNCH("vsa_bwd_dq", (bwd_dq_kernel<true, true>), dq_grid, dim3(kDqThreads), 0, stream, p);
+  else if (sel) AQ_LAUNCH("vsa_bwd_dq", (bwd_dq_kernel<true, false>), dq_grid, dim3(kDqThreads), 0, stream, p);
+  else if (p.delta) AQ_LAUNCH("bwd_dq", (bwd_dq_kernel<false, true>), dq_grid, dim3(kDqThreads), 0, stream, p);
+  else AQ_LAUNCH("bwd_dq", (bwd_dq_kernel<false, false>), dq_grid, dim3(kDqThreads), 0, stream, p);
   if ((e = hipGetLastError())) return e;
 
   p.nwork = bh * p.Ck;
   p.per_xcd = (p.nwork + 7) / 8;
   const dim3 dkdv_grid((unsigned)(p.per_xcd * 8));
   const bool gp = p.quant_p && (a.flags & (kFlagGsfP | kFlagTwoLevelP));
-  if (sel && gp) AQ_LAUNCH("vsa_bwd_dkdv", (bwd_dkdv_kernel<true, true>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
-  else if (sel) AQ_LAUNCH("vsa_bwd_dkdv", (bwd_dkdv_kernel<true, false>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
-  else if (gp) AQ_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<false, true>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
-  else AQ_LAUNCH("bwd_dkdv", (bwd_dkdv_kernel<false, false>), dkdv_grid, dim3(kDkdvThreads), 0, stream, p);
+  if (p.delta) launch_dkdv<true>(p, sel != nullptr, gp, dkdv_grid, stream);
+  else launch_dkdv<false>(p, sel != nullptr, gp, dkdv_grid, stream);
   return hipGetLastError();
 }
 

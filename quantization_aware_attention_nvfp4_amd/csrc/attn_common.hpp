@@ -168,6 +168,19 @@ __device__ __forceinline__ void mask_tail(f32x16 &s, int nvalid) {
   for (int r = 0; r < 16; ++r) s[r] = r < nvalid ? s[r] : -__builtin_inff();
 }
 
+// Smooth-Q: 16 consecutive fp32 values (delta of a lane's 16 keys), the initial accumulator of a
+// logit chain.
+__device__ __forceinline__ f32x16 delta16(const float *d) {
+  f32x16 r;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const f32x4 v = *(const f32x4 *)(d + 4 * r4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[4 * r4 + i] = v[i];
+  }
+  return r;
+}
+
 // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a contiguous range of work ids so
 // workgroups that share a head's operands share that XCD's L2.  Returns -1 for the padding
 // workgroups of the last partial range.

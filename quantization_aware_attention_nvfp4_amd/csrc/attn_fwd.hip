@@ -63,6 +63,8 @@ struct FwdParams {
   float *m_out;         // row-max pass: where it writes them
   bool two_level;       // P's global scale per (row, chunk): two_level_scale (GP kernels)
   float *pg;            // training, two-level: [BH, C, lq] those scales, or null
+  const float *qmean;   // smooth-Q: [BH, 128] the queries' mean, subtracted before quantization
+  const float *delta;   // smooth-Q: [BH, kchunks*128] <mean, k-hat_j>, added to every logit
 };
 
 // Copy offsets of this lane's 16-byte pieces of a staged [128][256 B] tile by a workgroup of
@@ -113,11 +115,45 @@ __device__ __forceinline__ void load_q_frags(const FwdParams &p, int64_t bb, int
                                              int hf, bf16x8 (&qf)[8]) {
   const uint16_t *qp = p.q + bb * p.sq.b + hh * p.sq.h + (qvalid ? qrow : 0) * p.sq.l;
   const float g = p.gq ? *p.gq : 1.0f;
+  const float *qm = p.qmean ? p.qmean + (bb * p.heads + hh) * kD : nullptr;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (qvalid) v = *(const u32x4 *)(qp + 16 * t + 8 * hf);
-    if (p.quant_q && p.gq) {
+    if (qm) {
+      // smooth-Q: fp32(q - mean) (rows past lq stay zero), then the quantizer of the K prepass
+      // (unit: the exact-quotient pair path; static: the IEEE quotient), rounded to bf16
+      float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                    bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+      if (qvalid) {
+        const f32x4 m0 = *(const f32x4 *)(qm + 16 * t + 8 * hf), m1 = *(const f32x4 *)(qm + 16 * t + 8 * hf + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[i] = f[i] - m0[i];
+          f[4 + i] = f[4 + i] - m1[i];
+        }
+      }
+      if (p.quant_q) {
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
+        am = pair_max(am);
+        if (p.gq) {
+          // the prepass's static-scale block arithmetic (fq_block_static), on this lane's half
+          const float S = round_e4m3((am / 6.0f) * g) / g;
+          const bool zero = !(S > 0.0f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f[i] = zero ? 0.0f * f[i] : fq_general(f[i], S);
+        } else {
+          const float S = block_scale_unit(am);
+          const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) fq_unit_pair(f[i], f[i + 1], S, inv);
+        }
+      }
+      v = u32x4{f32_to_bf16_rne(f[0]) | (f32_to_bf16_rne(f[1]) << 16), f32_to_bf16_rne(f[2]) | (f32_to_bf16_rne(f[3]) << 16),
+                f32_to_bf16_rne(f[4]) | (f32_to_bf16_rne(f[5]) << 16), f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16)};
+    } else if (p.quant_q && p.gq) {
       // static global scale: the IEEE quotient and the value rounded to bf16
       float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
                     bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
@@ -223,7 +259,7 @@ __device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, flo
 //
 // QL selects the 8-wave layout.  The cube-sparse training forward keeps 4 waves (its chunk lists
 // are per 128 queries) and then runs one wave per SIMD.
-template <bool TRAIN, bool QP, bool F16, bool QL, bool GP>
+template <bool TRAIN, bool QP, bool F16, bool QL, bool GP, bool SQ>
 __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void attn_fwd_kernel(FwdParams p) {
   static_assert(!F16 || QP, "the fp16 product needs a quantized P");
   constexpr bool HP = TRAIN && QP;  // O^hp needs its own product only when P is quantized
@@ -310,37 +346,46 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
 
   for (int64_t it = 0; it < n_iter; ++it) {
     // K-hat(chunk) has landed once this wave's V copies (issued after it) are the only ones
-    // outstanding; the barrier makes every wave's copies visible.
-    if constexpr (WAVES == 4) AQ_WAIT_VMCNT(8); else AQ_WAIT_VMCNT(4);
+    // outstanding; the barrier makes every wave's copies visible.  Smooth-Q: the logit chains
+    // start from delta of the lane's keys, loaded first (16 more loads the wait lets through).
+    f32x16 s[4];
+    if constexpr (SQ) {
+      const float *dl = p.delta + (bh * p.kchunks + chunk) * kChunk + 16 * hf;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[kt] = delta16(dl + 32 * kt);
+      if constexpr (WAVES == 4) AQ_WAIT_VMCNT(24); else AQ_WAIT_VMCNT(20);
+    } else {
+      if constexpr (WAVES == 4) AQ_WAIT_VMCNT(8); else AQ_WAIT_VMCNT(4);
+    }
     __builtin_amdgcn_s_barrier();
     AQ_OPAQUE(ka);
     AQ_OPAQUE(va);
 
     // ---- S^T = K-hat Q-hat^T for the 128 keys of the chunk ------------------------------
-    f32x16 s[4];
+    // (smooth-Q: the chains start from delta; otherwise from the MFMA's constant zero)
     if constexpr (QL) {
       // Q-hat column pair t is read once and feeds the four sub-tiles' chains.
       AQ_OPAQUE(qa);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) s[kt] = f32x16{};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const bf16x8 b = as_bf16x8(lds_read16(qa ^ (32 * t)));
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16((ka ^ (32 * t)) + 8192 * kt)), b, s[kt], 0, 0, 0);
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16((ka ^ (32 * t)) + 8192 * kt)), b,
+                                                          (SQ || t > 0) ? s[kt] : f32x16{}, 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        s[kt] = f32x16{};
 #pragma unroll
         for (int t0 = 0; t0 < 8; t0 += 4) {
           bf16x8 a[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) a[t] = as_bf16x8(lds_read16((ka ^ (32 * (t0 + t))) + 8192 * kt));
 #pragma unroll
-          for (int t = 0; t < 4; ++t) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qf[t0 + t], s[kt], 0, 0, 0);
+          for (int t = 0; t < 4; ++t)
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qf[t0 + t], (SQ || t0 + t > 0) ? s[kt] : f32x16{},
+                                                            0, 0, 0);
         }
       }
     }
@@ -727,13 +772,22 @@ __global__ __launch_bounds__(256, 2) void rowmax_kernel(FwdParams p) {
   }
   float mx = -__builtin_inff();
   for (int64_t it = 0; it < n_iter; ++it) {
-    AQ_WAIT_VMCNT(0);
+    // (smooth-Q: the chains start from delta, loaded after the K copies the wait is for)
+    f32x16 s[4];
+    if (p.delta) {
+      const float *dl = p.delta + (bh * p.kchunks + chunk) * kChunk + 16 * hf;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[kt] = delta16(dl + 32 * kt);
+      AQ_WAIT_VMCNT(16);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[kt] = f32x16{};
+      AQ_WAIT_VMCNT(0);
+    }
     __builtin_amdgcn_s_barrier();
     AQ_OPAQUE(ka);
-    f32x16 s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = f32x16{};
 #pragma unroll
       for (int t0 = 0; t0 < 8; t0 += 4) {
         bf16x8 a[4];
@@ -774,31 +828,31 @@ static bool use_f16(unsigned flags) {
 
 // The forward kernel of a call, by its mode: training (QL layout for dense calls), pipelined dense
 // inference, or the unpipelined kernel (cube-sparse inference); qp / f16 / gp as in form_p.
-template <bool GP>
+template <bool GP, bool SQ>
 static void launch_fwd_kernel(const FwdParams &p, dim3 grid, dim3 block, bool train, bool ql, bool pipe, bool qp,
                               bool f16, const char *nm, const char *nm_train, hipStream_t stream) {
   if (GP) {  // P quantized under the static scale: bf16 product
-    if (ql) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true, GP>), grid, block, 0, stream, p);
-    else if (train) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false, GP>), grid, block, 0, stream, p);
-    else if (pipe) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, false, GP>), grid, block, 0, stream, p);
-    else AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false, GP>), grid, block, 0, stream, p);
+    if (ql) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true, GP, SQ>), grid, block, 0, stream, p);
+    else if (train) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false, GP, SQ>), grid, block, 0, stream, p);
+    else if (pipe && !SQ) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, false, GP>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false, GP, SQ>), grid, block, 0, stream, p);
     return;
   }
   if (ql) {
-    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, true, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true, false>), grid, block, 0, stream, p);
+    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, true, false, SQ>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true, false, SQ>), grid, block, 0, stream, p);
   } else if (train) {
-    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, false, false>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, false, false, false, false>), grid, block, 0, stream, p);
-  } else if (pipe) {
+    if (f16) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, false, false, SQ>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false, false, SQ>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, false, false, false, false, SQ>), grid, block, 0, stream, p);
+  } else if (pipe && !SQ) {
     if (f16) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, true, false>), grid, block, 0, stream, p);
     else if (qp) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, false, false>), grid, block, 0, stream, p);
     else AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<false, false, false>), grid, block, 0, stream, p);
   } else {
-    if (f16) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, true, false, false>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH(nm, (attn_fwd_kernel<false, false, false, false, false>), grid, block, 0, stream, p);
+    if (f16) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, true, false, false, SQ>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false, false, SQ>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm, (attn_fwd_kernel<false, false, false, false, false, SQ>), grid, block, 0, stream, p);
   }
 }
 
@@ -835,6 +889,8 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   p.causal = a.causal;
   p.quant_q = (a.flags & kFlagQ) != 0;
   p.gq = vp.gq;
+  p.qmean = vp.qmean;
+  p.delta = vp.delta;
   const bool qp = (a.flags & kFlagP) != 0, f16 = use_f16(a.flags);
   const bool gp = qp && (a.flags & (kFlagGsfP | kFlagTwoLevelP));
   // Training outputs come as a set (lse, chunk maxima, O^hp).
@@ -857,13 +913,16 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   }
 
   const bool ql = train && qp && !sel;  // see attn_fwd_kernel
-  const bool pipe = !train && !sel;     // attn_fwd_pipe_kernel
+  const bool pipe = !train && !sel && !p.delta;  // attn_fwd_pipe_kernel (not under smooth-Q)
   const int waves = ql ? 8 : pipe ? kPipeWaves : WAVES;
   set_tiling(p, a, waves);
   const dim3 grid((unsigned)(p.per_xcd * 8)), block(waves * 64);
   const char *nm_train = sel ? "vsa_fwd_train" : "attn_fwd_train", *nm = sel ? "vsa_fwd" : "attn_fwd";
-  if (gp) launch_fwd_kernel<true>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
-  else launch_fwd_kernel<false>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
+  const bool sq = p.delta != nullptr;
+  if (gp && sq) launch_fwd_kernel<true, true>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
+  else if (gp) launch_fwd_kernel<true, false>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
+  else if (sq) launch_fwd_kernel<false, true>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
+  else launch_fwd_kernel<false, false>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
   return hipGetLastError();
 }
 
@@ -878,6 +937,7 @@ hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream) {
   e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, (a.flags & kFlagK) ? kQuantD : kQuantNone, ws + w.kq,
                           nullptr, vp.gk, vp.kmean, stream);
   if (e != hipSuccess) return e;
+  if ((e = launch_qk_delta(a, w, stream))) return e;
   const TileQuant qv = use_f16(a.flags) ? kQuantRowsF16 : ((a.flags & kFlagV) ? kQuantRows : kQuantNone);
   return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qv, nullptr, ws + w.vt, vp.gv, nullptr, stream);
 }

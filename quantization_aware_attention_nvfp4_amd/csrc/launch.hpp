@@ -15,7 +15,7 @@ constexpr int kMaxCubesHost = 4096;  // cube-sparse backward: longest per-key-cu
 // Flag bits of a call (the ABI's AQ_* values): the four quantizers and the variants.
 constexpr unsigned kFlagQ = 1u, kFlagK = 2u, kFlagV = 4u, kFlagP = 8u;
 constexpr unsigned kFlagFinalMax = 16u, kFlagGsfQkv = 32u, kFlagGsfP = 64u, kFlagSmoothK = 128u;
-constexpr unsigned kFlagTwoLevelP = 256u;
+constexpr unsigned kFlagTwoLevelP = 256u, kFlagSmoothQ = 512u;
 // Rows of the smooth-K partial sums: one per slab of this many keys.
 constexpr int kMeanSlab = 256;
 
@@ -65,7 +65,7 @@ struct VsaArgs {
 //                    [B*H, ceil(lk / kMeanSlab), 128] fp64 (their partial sums)
 //   ops 0 and 2: mfin [B*H, lq] fp32 (final row maxima, base-2 units, for the final-max variant)
 struct Workspace {
-  size_t kq, vt, vq, qq, dvec, pool, selw, slot, scal, kmean, kpart, mfin, total;
+  size_t kq, vt, vq, qq, dvec, pool, selw, slot, scal, kmean, kpart, mfin, qmean, qpart, delta, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -103,6 +103,10 @@ inline Workspace workspace_layout(int op, int batch, int heads, int64_t lq, int6
   w.kmean = take(bh * kHeadDimHost * 4);
   w.kpart = take(bh * (size_t)((lk + kMeanSlab - 1) / kMeanSlab) * kHeadDimHost * 8);
   if (op == 0 || op == 2) w.mfin = take(bh * (size_t)lq * 4);
+  // smooth-Q: the queries' means, their fp64 partial sums, and delta = <mean, k-hat> per key row
+  w.qmean = take(bh * kHeadDimHost * 4);
+  w.qpart = take(bh * (size_t)((lq + kMeanSlab - 1) / kMeanSlab) * kHeadDimHost * 8);
+  w.delta = take(bh * Ck * kChunkHost * 4);
   w.total = off;
   return w;
 }
@@ -134,9 +138,12 @@ hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads,
 hipError_t launch_variant_prep(const AttnArgs &a, const Workspace &w, hipStream_t stream);
 // Pointers into those regions for a call's flags (null when the variant is off).
 struct VariantPtrs {
-  const float *gq, *gk, *gv, *gp, *kmean;
+  const float *gq, *gk, *gv, *gp, *kmean, *qmean, *delta;
 };
 VariantPtrs variant_ptrs(const AttnArgs &a, const Workspace &w);
+// Smooth-Q: delta [B*H, Ck*128] = <query mean, K-hat row> for the K-hat rows in the workspace
+// (run after the K prepass).  No-op without the flag.
+hipError_t launch_qk_delta(const AttnArgs &a, const Workspace &w, hipStream_t stream);
 
 // The variants' per-call quantities, then K-hat rows and V-hat tiles of every head into the
 // workspace of op 0 (dense forward) or 2 (cube-sparse forward).

@@ -10,7 +10,10 @@
 //   * static Q/K/V scales: one global scale per tensor, g = 448*6 / max(amax, 1e-12) over the
 //     whole tensor ("nvfp4_qad.py": input_global_sf), on the values that are quantized (the
 //     smoothed keys under smooth-K);
-//   * static P scale: g = 448*6 / 1, P's largest value being exp(0) = 1 (a constant; no kernel).
+//   * static P scale: g = 448*6 / 1, P's largest value being exp(0) = 1 (a constant; no kernel);
+//   * smooth-Q (SageAttention2's smoothing): the queries' per-channel mean (the smooth-K reading)
+//     is subtracted before quantization and delta_j = <mean, k-hat_j> per key is added back to the
+//     logits; the mean comes from the same slab kernels, delta from qk_delta_kernel.
 //
 // Both reductions are deterministic: the mean's fp64 partial sums are combined in a fixed order,
 // and the abs-max is order-independent (one atomic maximum per workgroup on the float's bits,
@@ -117,6 +120,28 @@ __global__ void gsf_final_kernel(float *__restrict__ scal, int qkv, int pscale) 
   scal[3] = pscale ? 448.0f * 6.0f : 1.0f;
 }
 
+// delta[row] = <qmean[bh], kq[row]> for the K-hat rows (256 bytes each, plain layout) of every
+// head: 16 lanes per row, lane i taking channels 8i .. 8i+7 in order (fp32 fma), then a fixed
+// butterfly over the 16 lanes.
+__global__ __launch_bounds__(256) void qk_delta_kernel(const u32x4 *__restrict__ kq, const float *__restrict__ qmean,
+                                                       int64_t rows_per_head, int64_t total_rows,
+                                                       float *__restrict__ delta) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  float acc = 0.0f;
+  if (row < total_rows) {
+    const u32x4 v = kq[row * 16 + part];
+    const float *m = qmean + (row / rows_per_head) * kD + 8 * part;
+    const float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                        bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(f[i], m[i], acc);
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (part == 0 && row < total_rows) delta[row] = acc;
+}
+
 hipError_t launch_amax(const void *x, Strides s, int batch, int heads, int64_t L, const float *mean, uint32_t *out,
                        hipStream_t stream) {
   const int64_t nblk = (L + 63) / 64;
@@ -132,15 +157,17 @@ VariantPtrs variant_ptrs(const AttnArgs &a, const Workspace &w) {
   uint8_t *ws = (uint8_t *)a.workspace;
   const float *scal = (const float *)(ws + w.scal);
   const bool qkv = (a.flags & kFlagGsfQkv) != 0;
+  const bool sq = (a.flags & kFlagSmoothQ) != 0;
   return VariantPtrs{qkv ? scal : nullptr, qkv ? scal + 1 : nullptr, qkv ? scal + 2 : nullptr,
                      (a.flags & kFlagGsfP) ? scal + 3 : nullptr,
-                     (a.flags & kFlagSmoothK) ? (const float *)(ws + w.kmean) : nullptr};
+                     (a.flags & kFlagSmoothK) ? (const float *)(ws + w.kmean) : nullptr,
+                     sq ? (const float *)(ws + w.qmean) : nullptr, sq ? (const float *)(ws + w.delta) : nullptr};
 }
 
 hipError_t launch_variant_prep(const AttnArgs &a, const Workspace &w, hipStream_t stream) {
   const bool smooth = (a.flags & kFlagSmoothK) != 0, qkv = (a.flags & kFlagGsfQkv) != 0,
-             pscale = (a.flags & kFlagGsfP) != 0;
-  if (!smooth && !qkv && !pscale) return hipSuccess;
+             pscale = (a.flags & kFlagGsfP) != 0, smooth_q = (a.flags & kFlagSmoothQ) != 0;
+  if (!smooth && !qkv && !pscale && !smooth_q) return hipSuccess;
   uint8_t *ws = (uint8_t *)a.workspace;
   float *scal = (float *)(ws + w.scal);
   float *kmean = (float *)(ws + w.kmean);
@@ -157,15 +184,37 @@ hipError_t launch_variant_prep(const AttnArgs &a, const Workspace &w, hipStream_
               nslab, a.lk, total, kmean);
     if ((e = hipGetLastError())) return e;
   }
+  float *qmean = (float *)(ws + w.qmean);
+  if (smooth_q) {
+    const int nslab = (int)((a.lq + kMeanSlab - 1) / kMeanSlab);
+    double *part = (double *)(ws + w.qpart);
+    AQ_LAUNCH("qmean_partial", kmean_partial_kernel, dim3((unsigned)(bh * nslab)), dim3(256), 0, stream,
+              (const uint16_t *)a.q, a.sq, a.heads, a.lq, nslab, part);
+    if ((e = hipGetLastError())) return e;
+    const int64_t total = bh * kD;
+    AQ_LAUNCH("qmean_final", kmean_final_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, part,
+              nslab, a.lq, total, qmean);
+    if ((e = hipGetLastError())) return e;
+  }
   if (qkv) {
     uint32_t *bits = (uint32_t *)(scal + 4);
     AQ_LAUNCH("fill_u32", fill_u32_kernel, dim3(1), dim3(64), 0, stream, bits, 3, 0u);
     if ((e = hipGetLastError())) return e;
-    if ((e = launch_amax(a.q, a.sq, a.batch, a.heads, a.lq, nullptr, bits, stream))) return e;
+    if ((e = launch_amax(a.q, a.sq, a.batch, a.heads, a.lq, smooth_q ? qmean : nullptr, bits, stream))) return e;
     if ((e = launch_amax(a.k, a.sk, a.batch, a.heads, a.lk, smooth ? kmean : nullptr, bits + 1, stream))) return e;
     if ((e = launch_amax(a.v, a.sv, a.batch, a.heads, a.lk, nullptr, bits + 2, stream))) return e;
   }
   AQ_LAUNCH("gsf_final", gsf_final_kernel, dim3(1), dim3(64), 0, stream, scal, (int)qkv, (int)pscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_delta(const AttnArgs &a, const Workspace &w, hipStream_t stream) {
+  if (!(a.flags & kFlagSmoothQ)) return hipSuccess;
+  uint8_t *ws = (uint8_t *)a.workspace;
+  const int64_t per_head = (a.lk + kChunk - 1) / kChunk * kChunk;
+  const int64_t total = (int64_t)a.batch * a.heads * per_head;
+  AQ_LAUNCH("qk_delta", qk_delta_kernel, dim3((unsigned)((total + 15) / 16)), dim3(256), 0, stream,
+            (const u32x4 *)(ws + w.kq), (const float *)(ws + w.qmean), per_head, total, (float *)(ws + w.delta));
   return hipGetLastError();
 }
 

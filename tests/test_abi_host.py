@@ -62,7 +62,7 @@ def fwd(lib, **kw):
     (dict(lq=0), -1, "positive"),
     (dict(scale=float("nan")), -1, "softmax_scale"),
     (dict(scale=-1.0), -1, "softmax_scale"),
-    (dict(flags=512), -1, "quant_flags"),
+    (dict(flags=1024), -1, "quant_flags"),
     (dict(flags=15 | 256 | 16), -2, "AQ_TWO_LEVEL_P"),
     (dict(flags=15 | 256 | 64), -2, "AQ_TWO_LEVEL_P"),
     (dict(Hkv=1), -2, "num_kv_heads"),
@@ -135,10 +135,12 @@ def test_topk_and_workspace(lib):
     assert lib.vsa_topk(1.0, 196) == 1
     assert lib.vsa_topk(2.0, 196) == 0
     # K-hat and V-hat for 12 heads x 25088 keys (2 x 77.07 MB), then the variants' regions: the
-    # scales (256 B), key means [12, 128] fp32, their fp64 partial sums [12, 98 slabs, 128] and the
-    # final row maxima [12, 25088] fp32, each 256-byte aligned.
+    # scales (256 B), key means [12, 128] fp32, their fp64 partial sums [12, 98 slabs, 128], the
+    # final row maxima [12, 25088] fp32, then smooth-Q's query means, their partial sums and the
+    # per-key delta [12, 25088] fp32, each 256-byte aligned.
     al = lambda n: (n + 255) // 256 * 256
-    want = 2 * 12 * 25088 * 128 * 2 + 256 + al(12 * 128 * 4) + al(12 * 98 * 128 * 8) + al(12 * 25088 * 4)
+    means = al(12 * 128 * 4) + al(12 * 98 * 128 * 8)
+    want = 2 * 12 * 25088 * 128 * 2 + 256 + means + al(12 * 25088 * 4) + means + al(12 * 25088 * 4)
     assert lib.attn_qat_workspace_size(0, 1, 12, 25088, 25088) == want
     assert lib.attn_qat_workspace_size(0, 0, 12, 25088, 25088) == 0
 

@@ -1,10 +1,10 @@
 """GPU parity of the attention variants (AQ_FINAL_MAX, AQ_GSF_QKV, AQ_GSF_P, AQ_SMOOTH_K,
-AQ_TWO_LEVEL_P) against the oracle, within the stated attention tolerance (tests/parity.py).
+AQ_TWO_LEVEL_P, AQ_SMOOTH_Q) against the oracle, within the stated attention tolerance (tests/parity.py).
 
 Dense forward (inference and training outputs) and straight-through backward on ragged, cross
 and causal shapes; the cube-sparse forward and backward on a small grid (compared where the two
 selections agree, as in the other cube-sparse tests); sampled rows of the 448x896x61 workload
-under the final-max statistics and under two-level P.  Properties that hold for any input: under AQ_FINAL_MAX every
+under the final-max statistics, two-level P and smooth-Q.  Properties that hold for any input: under AQ_FINAL_MAX every
 chunk-maximum row equals the row's final maximum, and lse is unchanged up to rounding; under
 AQ_TWO_LEVEL_P the first-level scales the forward stores match the oracle's to fp32 rounding."""
 import math
@@ -21,8 +21,9 @@ pytestmark = pytest.mark.gpu
 LOG2E = 1.0 / math.log(2.0)
 SCALE = 1.0 / math.sqrt(128)
 ALL = 15
-FM, GQKV, GP, SK, TWO = 16, 32, 64, 128, 256
-VARIANTS = [ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, SK, ALL | FM | GQKV | GP | SK, ALL | TWO, ALL | TWO | GQKV | SK]
+FM, GQKV, GP, SK, TWO, SQ = 16, 32, 64, 128, 256, 512
+VARIANTS = [ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, SK, ALL | FM | GQKV | GP | SK, ALL | TWO, ALL | TWO | GQKV | SK,
+            ALL | SQ, SQ, ALL | SQ | SK | GQKV | FM | GP, ALL | SQ | TWO]
 
 
 @pytest.fixture(scope="module")
@@ -82,7 +83,7 @@ def test_static_scales_differ_from_unit(m):
     q, k, v = rand(1, 256, 2, 205), rand(1, 256, 2, 206), rand(1, 256, 2, 207)
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
     base = m.attn_qat_fwd(qg, kg, vg)
-    for fl in (ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, ALL | TWO):
+    for fl in (ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, ALL | TWO, ALL | SQ):
         assert not torch.equal(m.attn_qat_fwd(qg, kg, vg, quant_flags=fl), base), fl
 
 
@@ -99,7 +100,7 @@ def agreement(sel_gpu, sel_ref):
     return qa, ka
 
 
-@pytest.mark.parametrize("flags", [ALL | FM, ALL | FM | GQKV | GP | SK, ALL | TWO | GQKV])
+@pytest.mark.parametrize("flags", [ALL | FM, ALL | FM | GQKV | GP | SK, ALL | TWO | GQKV, ALL | SQ | SK])
 def test_cube_sparse_forward_and_backward(m, flags):
     grid, L = (4, 8, 32), 1024
     q, k, v = synth.qkv_headscaled(1, L, 2, 128, seed=208, scaled=False)
@@ -119,7 +120,7 @@ def test_cube_sparse_forward_and_backward(m, flags):
         assert_close(bhrd(t)[mask], rb[name][mask], f"vsa {name} flags={flags}")
 
 
-@pytest.mark.parametrize("flags", [ALL | FM, ALL | TWO])
+@pytest.mark.parametrize("flags", [ALL | FM, ALL | TWO, ALL | SQ])
 def test_wan_448x896x61_sampled_rows(m, flags):
     q, k, v = synth.wan_448x896x61()
     L = q.shape[1]
@@ -137,3 +138,22 @@ def test_two_level_rejections(m):
     for extra in (FM, GP):
         with pytest.raises(NotImplementedError):
             m.attn_qat_fwd(q, q, q, quant_flags=ALL | TWO | extra)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_smooth_q_offset_query(m, causal):
+    # a query with a large common offset (the case the smoothing is for): forward, training outputs
+    # and backward against the oracle
+    L = 300 if not causal else 260
+    q, k, v, do = rand(1, L, 2, 231, 1.0, 3.0), rand(1, L, 2, 232), rand(1, L, 2, 233), rand(1, L, 2, 234)
+    flags = ALL | SQ
+    qg, kg, vg, dog = (t.cuda() for t in (q, k, v, do))
+    o, aux = m.attn_qat_fwd(qg, kg, vg, causal=causal, quant_flags=flags, training=True)
+    dq, dk, dv = m.attn_qat_bwd(qg, kg, vg, aux, dog, causal=causal, quant_flags=flags)
+    torch.cuda.synchronize()
+    args = (bhld_bits(q), bhld_bits(k), bhld_bits(v))
+    r = oracle.attn_fwd(*args, SCALE, causal=causal, flags=flags)
+    assert_close(bhrd(o), r["o"], "smooth-Q o")
+    b = oracle.attn_bwd(*args, bhld_bits(do), SCALE, causal=causal, flags=flags)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(bhrd(t), b[name], f"smooth-Q {name}")
