@@ -250,8 +250,8 @@ __device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, flo
 // (both fake-quantized, hence exact in fp16) multiply on the fp16 MFMA, whose products are the
 // same as the bf16 ones for these values.
 //
-// This kernel serves training and the cube-sparse calls; dense inference runs the pipelined
-// kernel below.  Inference: 4 waves (128 queries) per workgroup, two workgroups per CU.  With the
+// This kernel serves training, smooth-Q and the cube-sparse calls; other dense inference runs the
+// ping-pong kernel below.  Inference: 4 waves (128 queries) per workgroup, two workgroups per CU.  With the
 // O^hp product
 // the two accumulators leave no room for the Q-hat operand in registers at two waves per SIMD,
 // so that variant runs 8 waves (256 queries) per workgroup, one per CU, with each wave's Q-hat
@@ -495,38 +495,42 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
 }
 
 // ------------------------------------------------------------------------------------------
-// Pipelined inference forward (dense)
+// Ping-pong inference forward (dense)
 // ------------------------------------------------------------------------------------------
 //
-// 4 waves (128 queries) per workgroup, two workgroups per CU (one wave of each per SIMD).  The
-// logits of chunk it+1 are computed during chunk it: step kt of iteration it forms P-hat(it, kt+1)
-// on the vector ALUs while the matrix cores run S(it+1, kt) = K-hat(it+1, kt) Q-hat^T into the
-// registers that sub-tile kt of chunk it has just released, and O^T += V-hat(it, kt)^T
-// P-hat(it, kt)^T.  The two workgroups of a CU drift out of phase, so one's softmax at the top of
-// a chunk runs beside the other's matrix work.
+// 8 waves (256 queries) per workgroup, one workgroup per CU: waves w and w+4 share SIMD w%4 and
+// belong to the two groups g = w/4 of 128 queries.  Each group alternates a vector phase V(it)
+// (running max, P-hat of chunk it on the VALUs) and a matrix phase M(it) (S of chunk it+1 and
+// O^T += V-hat(it)^T P-hat(it)^T on the matrix cores); group 1 runs one phase behind group 0, so
+// on every SIMD one wave's exponentials and fake quantization run beside the other wave's MFMAs.
+// One workgroup barrier separates the phases.
 //
-// LDS (64 KiB per workgroup): one K-hat chunk as four 8 KiB sub-tiles of 32 rows (256 B rows,
-// sw_kq swizzle) and one V-hat^T chunk as four 8 KiB sub-tiles [128 d][32 keys] (64 B rows,
-// 16-byte columns swizzled by sw_v64, so each sub-tile is contiguous).  After step kt every wave
-// has finished with sub-tile kt of both chunks, and one barrier later K-hat(it+2, kt) and
-// V-hat(it+1, kt) start copying into them: a full iteration ahead of their use, with one barrier
-// per step.  Measured on the 448x896x61 workload it runs ~9% fewer cycles than the
-// unpipelined kernel; the clock under this load (about 1.8-2.0 GHz) keeps the time gain small.
-constexpr int kPipeWaves = 4;
-constexpr uint32_t kPipeK = 0, kPipeV = 32768;  // LDS byte offsets
+// LDS: two buffers of 64 KiB, buffer it%2 holding K-hat(it+1) as four 8 KiB sub-tiles of 32 rows
+// (256 B rows, sw_kq swizzle) and V-hat^T(it) as four [128 d][32 keys] sub-tiles (64 B rows,
+// 16-byte columns swizzled by sw_v64, so each sub-tile is contiguous).  Group 0 reads buffer it%2
+// in phase 2it+1, group 1 in phase 2it+2; it is refilled for iteration it+2 at the start of phase
+// 2it+3 and waited for at the end of phase 2it+4.  K-hat(0) for the prologue's S(0) goes to
+// buffer 1's K half.
+//
+// Why two groups on one CU rather than one wave per SIMD doing both halves: a wave hides only
+// about 4-5 independent VALU operations behind each 32-cycle 32x32x16 MFMA of its own, while a
+// VALU stream from a second wave on the same SIMD runs beside the first wave's MFMA chain (at
+// about three quarters of its own rate when the MFMA wave has the higher priority, which
+// s_setprio gives the matrix phase).  Per 128-key chunk a wave issues 64 MFMAs and some 450 VALU
+// instructions (69 of them exponentials), so the VALU half only hides under a second wave.
+constexpr uint32_t kLdsK = 0, kLdsV = 32768;  // byte offsets of the K-hat and V-hat^T halves
 
 // A ds_read_b128 serves 16 lanes per cycle from 64 banks (256 bytes): the 16 rows d..d+15 of a
 // read must then cover the 16 distinct 16-byte slots of 256 bytes, 4 * (d & 3) + column, so rows
 // that share d & 3 get different columns.
 __device__ __forceinline__ int sw_v64(int d) { return (d >> 2) & 3; }
-constexpr int kPipeAhead = 3, kPipeValu = 5;  // LDS reads issued ahead; VALU per MFMA in a step
+constexpr int kPPWaves = 8;
+constexpr int kPPAhead = 8;  // LDS operand reads issued ahead of their MFMA in the matrix phase
 
 template <bool QP, bool F16, bool GP>
-__global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdParams p) {
-  constexpr int WAVES = kPipeWaves;
-  constexpr int BM = 32 * WAVES;
-  constexpr int kCopies = 8 / WAVES;  // 1 KiB copies per wave and sub-tile
-  __shared__ __attribute__((aligned(256))) uint8_t lds[65536];
+__global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams p) {
+  constexpr int BM = 32 * kPPWaves;
+  __shared__ __attribute__((aligned(256))) uint8_t lds[2 * 65536];
 
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
   if (vid < 0) return;
@@ -536,14 +540,13 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hf = lane >> 5;
   const int64_t qrow = (int64_t)qt * BM + wave * 32 + n;
   const bool qvalid = qrow < p.lq;
 
-  // Chunk counts and key indices in 32 bits (lengths are below 2^30): 64-bit compares of two
-  // uniform values would take a vector register.
   const int lk = (int)p.lk;
   int n_iter = (int)p.nchunks;
   if (p.causal) {
@@ -553,74 +556,69 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
   const uint32_t lds0 = lds_addr(lds);
   const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.kchunks * (kChunk * kD / 8));
   const uint8_t *vbase = (const uint8_t *)(p.vt + bh * p.kchunks * (kChunk * kD / 8));
-  // Copy of sub-tile kt of chunk c: this wave's 1 KiB of each.  K: rows 32kt + 4w + lane/16,
-  // physical column lane%16 (sw_kq does not depend on row bits 5-6).  V: rows d = 16w + lane/4,
-  // physical column lane%4, logical keys 32kt + 8*(column ^ sw_v64(d)).
-  uint32_t k_off[kCopies], v_off[kCopies];
-#pragma unroll
-  for (int i = 0; i < kCopies; ++i) {
-    const int ci = kCopies * wave + i, r = 4 * ci + (lane >> 4), d = 16 * ci + (lane >> 2);
-    k_off[i] = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
-    v_off[i] = (uint32_t)(d * 256 + (((lane & 3) ^ sw_v64(d)) << 4));
+  // Copies (one 1 KiB piece of every sub-tile per wave): K rows 32kt + 4w + lane/16, physical
+  // column lane%16; V rows d = 16w + lane/4, physical column lane%4 (logical keys 32kt +
+  // 8*(column ^ sw_v64(d))).
+  uint32_t k_off, v_off;
+  {
+    const int r = 4 * wave + (lane >> 4), d = 16 * wave + (lane >> 2);
+    k_off = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
+    v_off = (uint32_t)(d * 256 + (((lane & 3) ^ sw_v64(d)) << 4));
   }
-  auto copy_k = [&](int c, int kt) {
+  auto copy_k = [&](int c, uint32_t buf) {
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i)
-      load_lds16_sa(kbase + (int64_t)c * 32768 + kt * 8192, k_off[i],
-                    lds0 + kPipeK + kt * 8192 + 1024 * (kCopies * wave + i));
+    for (int kt = 0; kt < 4; ++kt)
+      load_lds16_sa(kbase + (int64_t)c * 32768 + kt * 8192, k_off, buf + kLdsK + kt * 8192 + 1024 * wave);
   };
-  auto copy_v = [&](int c, int kt) {
+  auto copy_v = [&](int c, uint32_t buf) {
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i)
-      load_lds16_sa(vbase + (int64_t)c * 32768 + kt * 64, v_off[i], lds0 + kPipeV + kt * 8192 + 1024 * (kCopies * wave + i));
+    for (int kt = 0; kt < 4; ++kt)
+      load_lds16_sa(vbase + (int64_t)c * 32768 + kt * 64, v_off, buf + kLdsV + kt * 8192 + 1024 * wave);
+  };
+  // Iteration j's buffer: K-hat(j+1) and V-hat(j).
+  auto fill = [&](int j) {
+    const uint32_t buf = lds0 + (uint32_t)(j & 1) * 65536;
+    if (j + 1 < n_iter) copy_k(j + 1, buf);
+    if (j < n_iter) copy_v(j, buf);
   };
 
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    copy_k(0, kt);
-    copy_v(0, kt);
-  }
+  // Prologue: K-hat(0) into buffer 1's K half, iteration 0's buffer, Q-hat.
+  copy_k(0, lds0 + 65536);
+  fill(0);
   bf16x8 qf[8];
   load_q_frags(p, bb, hh, qrow, qvalid, hf, qf);
 
   uint32_t ka, va;
   {
     const int krow = perm_row(n), swk = sw_kq(krow);
-    ka = lds0 + kPipeK + krow * 256 + 16 * (hf ^ swk);
-    va = lds0 + kPipeV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
+    ka = lds0 + kLdsK + krow * 256 + 16 * (hf ^ swk);
+    va = lds0 + kLdsV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
   }
-  // S^T of one 32-key sub-tile from the K-hat chunk in LDS, into st (old contents dropped).
-  auto logits = [&](int kt, f32x16 &st) {
-    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(ka + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
+  auto logits = [&](uint32_t kbuf, int kt, f32x16 &st) {
+    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + ka + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
     for (int t = 1; t < 8; ++t)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16((ka ^ (32 * t)) + 8192 * kt)), qf[t], st, 0,
-                                                   0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + (ka ^ (32 * t)) + 8192 * kt)), qf[t], st,
+                                                   0, 0, 0);
   };
 
   f32x16 s[4];
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-  // Final-max variant: the running max starts at the row's final maximum, so it never moves.
   float m_run = (p.m_init && qvalid) ? p.m_init[bh * p.lq + qrow] : -__builtin_inff();
-  float l_run = 0.0f;
+  float l_run = 0.0f, alpha = 1.0f;
+  u32x4 pq[4][2];
 
-  // Prologue: S(0), then K-hat(1) into the K buffer.
   AQ_WAIT_VMCNT(0);
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) logits(kt, s[kt]);
-  __builtin_amdgcn_s_barrier();
-  if (n_iter > 1) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) copy_k(1, kt);
-  }
-  AQ_WAIT_VMCNT(0);
+  for (int kt = 0; kt < 4; ++kt) logits(65536, kt, s[kt]);
+  // Buffer 1's K half is read by every wave before iteration 1's copies go there.
   __builtin_amdgcn_s_barrier();
 
-  for (int it = 0; it < n_iter; ++it) {
-    // ---- masks: keys past lk (last chunk) and causal -------------------------------------
+  // V(it): mask, running max, P-hat of chunk it (all four sub-tiles) into pq.
+  auto vphase = [&](int it) {
     const bool tail = (it + 1) * kChunk > lk;
     const bool diag = p.causal && (it + 1) * kChunk - 1 > qt * BM + wave * 32;
     if (tail || diag) {
@@ -629,8 +627,6 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) mask_tail(s[kt], valid_prefix(key0 + 32 * kt, last));
     }
-
-    // ---- running max (refreshed once per chunk) -----------------------------------------
     float bmax[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -642,65 +638,97 @@ __global__ __launch_bounds__(kPipeWaves * 64, 2) void attn_fwd_pipe_kernel(FwdPa
     float cm = fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3]));
     cm = pair_max(cm);
     const float m_new = fmaxf(m_run, cm * p.c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // applied to acc by the next matrix phase
     m_run = m_new;
+    const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : kPScaleStatic;
+    float psum = 0.0f;
+    u32x4 ph[2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) form_p<QP, F16, false, GP>(s[kt], bmax[kt], p.c, m_new, g, psum, pq[kt], ph);
+    l_run = l_run * alpha + psum;
+    // Pinned here: otherwise the compiler sinks this phase's work past the barrier into the next.
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      AQ_OPAQUE(pq[kt][0]);
+      AQ_OPAQUE(pq[kt][1]);
+    }
+    AQ_OPAQUE(l_run);
+    AQ_OPAQUE(m_run);
+    AQ_OPAQUE(alpha);
+  };
+  // M(it): S of chunk it+1 and O^T += V-hat(it)^T P-hat(it)^T, from buffer it%2.  The last
+  // iteration also computes logits, from a stale K half, and drops them: a branch would split the
+  // block whose operand reads are scheduled ahead of the MFMAs.
+  auto mphase = [&](int it) {
+    // the rescale of the running output for this chunk's maximum (skipped when no row moved)
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
     }
-    const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : kPScaleStatic;
-
-    // ---- steps: P-hat(it, kt+1) beside S(it+1, kt) and O^T += V-hat^T P-hat^T(it, kt) -------
-    // The last iteration also computes logits, from a stale K buffer, and drops them: a branch
-    // would split the block the scheduler interleaves.
-    const bool near_end = it + 2 >= n_iter;  // some copies are not issued: wait for all
-    float psum = 0.0f;
-    u32x4 pq[2][2], ph[2][2];
-    form_p<QP, F16, false, GP>(s[0], bmax[0], p.c, m_new, g, psum, pq[0], ph[0]);
-    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t buf = (uint32_t)(it & 1) * 65536;
+    // One address register per K-hat column pair and per V-hat half; the sub-tile and d-tile
+    // offsets then ride in the reads' immediate offset field.
+    uint32_t kad[8], vad[2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kad[t] = buf + (ka ^ (32 * t));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) vad[j] = buf + (va ^ (16 * j));
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      logits(kt, s[kt]);
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kad[0] + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int t = 1; t < 8; ++t)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kad[t] + 8192 * kt)), qf[t], s[kt], 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const u32x4 a = lds_read16((va ^ (16 * j)) + 8192 * kt + 2048 * dt);
+          const u32x4 a = lds_read16(vad[j] + 8192 * kt + 2048 * dt);
           if (F16)
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                             __builtin_bit_cast(f16x8, pq[kt & 1][j]), acc[dt], 0, 0, 0);
+                                                             __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
           else
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pq[kt & 1][j]), acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pq[kt][j]), acc[dt], 0, 0, 0);
         }
-      if (kt < 3) {
-        form_p<QP, F16, false, GP>(s[kt + 1], bmax[kt + 1], p.c, m_new, g, psum, pq[(kt + 1) & 1],
-                                   ph[(kt + 1) & 1]);
-        // Pinned here: otherwise the compiler sinks this work into the next step, beside its use.
-        AQ_OPAQUE(pq[(kt + 1) & 1][0]);
-        AQ_OPAQUE(pq[(kt + 1) & 1][1]);
-        AQ_OPAQUE(psum);
-      }
-      // Issue order: the A/B operands of three MFMAs ahead, then per MFMA the reads that keep
-      // that distance and a share of the P work.
-      __builtin_amdgcn_sched_group_barrier(0x100, kPipeAhead, 0);
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (g < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (kt < 3) __builtin_amdgcn_sched_group_barrier(0x002, kPipeValu, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // Sub-tile kt + 1 of both buffers has landed (this wave's copies: all but the last two
-      // steps' pairs), every wave is done with sub-tile kt, and its next contents start copying.
-      if (near_end) AQ_WAIT_VMCNT(0);
-      else if constexpr (kCopies == 1) AQ_WAIT_VMCNT(4);
-      else AQ_WAIT_VMCNT(8);
-      __builtin_amdgcn_s_barrier();
-      if (it + 2 < n_iter) copy_k(it + 2, kt);
-      if (it + 1 < n_iter) copy_v(it + 1, kt);
     }
-    l_run = l_run * alpha + psum;
+    // Operand reads kPPAhead MFMAs ahead of their use across the whole phase, not all up front.
+    __builtin_amdgcn_sched_group_barrier(0x100, kPPAhead, 0);
+#pragma unroll
+    for (int g = 0; g < 64; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (g < 64 - kPPAhead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) AQ_OPAQUE(s[kt]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) AQ_OPAQUE(acc[dt]);
+  };
+
+  // Phases ph = 0 .. 2n: group 0 runs V(0) M(0) V(1) M(1) ... and idles in the last phase, group
+  // 1 idles in phase 0 and then runs the same sequence, so phase 2it+g is V(it) and 2it+1+g is
+  // M(it) for group g.  Every wave issues its share of iteration j's copies at the start of phase
+  // 2j-1 (buffer j%2 is free: its last reader, group 1's M(j-2), ran in phase 2j-2) and waits for
+  // them at the end of phase 2j, before group 0's M(j) in phase 2j+1.
+  if (grp == 1) __builtin_amdgcn_s_barrier();
+  for (int it = 0; it < n_iter; ++it) {
+    // Iteration it+1's copies (buffer (it+1)%2, free from phase 2it+1): group 1 at the start of
+    // its V(it) (phase 2it+1), group 0 at the start of its V(it+1) (phase 2it+2); both are
+    // waited for at the end of phase 2it+2.
+    if (grp == 1 && it + 1 < n_iter) fill(it + 1);
+    if (grp == 0 && it >= 1) fill(it);
+    __builtin_amdgcn_s_setprio(0);
+    vphase(it);
+    if (grp == 0) AQ_WAIT_VMCNT(0);  // end of phase 2it
+    __builtin_amdgcn_s_barrier();
+    // the matrix phase issues first: its MFMAs keep the matrix unit busy and the vector phase
+    // beside it fills the remaining issue slots
+    __builtin_amdgcn_s_setprio(2);
+    mphase(it);
+    if (grp == 1) AQ_WAIT_VMCNT(0);  // end of phase 2it+2
+    __builtin_amdgcn_s_barrier();
   }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
 
   // ---- epilogue --------------------------------------------------------------------------
   const float l = pair_sum(l_run);
@@ -826,15 +854,16 @@ static bool use_f16(unsigned flags) {
   return (flags & kFlagV) && (flags & kFlagP) && !(flags & (kFlagGsfQkv | kFlagGsfP | kFlagTwoLevelP));
 }
 
-// The forward kernel of a call, by its mode: training (QL layout for dense calls), pipelined dense
-// inference, or the unpipelined kernel (cube-sparse inference); qp / f16 / gp as in form_p.
+// The forward kernel of a call, by its mode: training (QL layout for dense calls), ping-pong dense
+// inference, or the single-group kernel (cube-sparse or smooth-Q inference); qp / f16 / gp as in
+// form_p.
 template <bool GP, bool SQ>
 static void launch_fwd_kernel(const FwdParams &p, dim3 grid, dim3 block, bool train, bool ql, bool pipe, bool qp,
                               bool f16, const char *nm, const char *nm_train, hipStream_t stream) {
   if (GP) {  // P quantized under the static scale: bf16 product
     if (ql) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true, GP, SQ>), grid, block, 0, stream, p);
     else if (train) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false, GP, SQ>), grid, block, 0, stream, p);
-    else if (pipe && !SQ) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, false, GP>), grid, block, 0, stream, p);
+    else if (pipe && !SQ) AQ_LAUNCH(nm, (attn_fwd_pp_kernel<true, false, GP>), grid, block, 0, stream, p);
     else AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false, GP, SQ>), grid, block, 0, stream, p);
     return;
   }
@@ -846,9 +875,9 @@ static void launch_fwd_kernel(const FwdParams &p, dim3 grid, dim3 block, bool tr
     else if (qp) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false, false, SQ>), grid, block, 0, stream, p);
     else AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, false, false, false, false, SQ>), grid, block, 0, stream, p);
   } else if (pipe && !SQ) {
-    if (f16) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, true, false>), grid, block, 0, stream, p);
-    else if (qp) AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<true, false, false>), grid, block, 0, stream, p);
-    else AQ_LAUNCH(nm, (attn_fwd_pipe_kernel<false, false, false>), grid, block, 0, stream, p);
+    if (f16) AQ_LAUNCH(nm, (attn_fwd_pp_kernel<true, true, false>), grid, block, 0, stream, p);
+    else if (qp) AQ_LAUNCH(nm, (attn_fwd_pp_kernel<true, false, false>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm, (attn_fwd_pp_kernel<false, false, false>), grid, block, 0, stream, p);
   } else {
     if (f16) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, true, false, false, SQ>), grid, block, 0, stream, p);
     else if (qp) AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, false, false, false, SQ>), grid, block, 0, stream, p);
@@ -913,8 +942,8 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   }
 
   const bool ql = train && qp && !sel;  // see attn_fwd_kernel
-  const bool pipe = !train && !sel && !p.delta;  // attn_fwd_pipe_kernel (not under smooth-Q)
-  const int waves = ql ? 8 : pipe ? kPipeWaves : WAVES;
+  const bool pipe = !train && !sel && !p.delta;  // attn_fwd_pp_kernel (not under smooth-Q)
+  const int waves = ql ? 8 : pipe ? kPPWaves : WAVES;
   set_tiling(p, a, waves);
   const dim3 grid((unsigned)(p.per_xcd * 8)), block(waves * 64);
   const char *nm_train = sel ? "vsa_fwd_train" : "attn_fwd_train", *nm = sel ? "vsa_fwd" : "attn_fwd";
