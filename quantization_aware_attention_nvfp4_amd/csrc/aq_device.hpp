@@ -185,7 +185,9 @@ __device__ __forceinline__ float two_level_scale(float cm, float c, float m) {
 // Eight values rounded to E2M1 codes in one register (byte i holds pair i; ties to the even
 // code, saturating at +-6, sign kept), by the gfx950 packed FP4 conversion with a unit scale.
 __device__ __forceinline__ uint32_t e2m1_codes8(const float *r) {
-  uint32_t code = 0u;
+  // Each conversion writes one byte and keeps the rest; all four bytes are written, so the
+  // starting value only has to be some defined register (r[0]'s bits: no extra move).
+  uint32_t code = __builtin_bit_cast(uint32_t, r[0]);
   code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[0], r[1], 1.0f, 0);
   code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[2], r[3], 1.0f, 1);
   code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, r[4], r[5], 1.0f, 2);

@@ -200,9 +200,11 @@ __device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, flo
   static_assert(!(GP && F16), "P-hat under the static scale is not exact in fp16");
   if (QP) {
     const ProbBlock pb = GP ? prob_block_static(bmax, c, m_new, g) : prob_block(bmax, c, m_new);
-    float r[16], rsum = 0.0f;
+    float r[16];
+    r[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0], c, -pb.mb));
+    float rsum = r[0];  // the same sum as from 0: r >= 0
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 1; i < 16; ++i) {
       r[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -pb.mb));
       rsum += r[i];
     }
@@ -524,6 +526,26 @@ constexpr uint32_t kLdsK = 0, kLdsV = 32768;  // byte offsets of the K-hat and V
 // read must then cover the 16 distinct 16-byte slots of 256 bytes, 4 * (d & 3) + column, so rows
 // that share d & 3 get different columns.
 __device__ __forceinline__ int sw_v64(int d) { return (d >> 2) & 3; }
+// The largest of three values in one v_max3_f32.  The logits are never NaN; written out, the
+// compiler would first copy each MFMA result through a quieting v_max (it cannot know they are
+// canonical), a third more instructions in the vector phase.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// The largest of each of four blocks of 16 logits: eight v_max3_f32 per block, the four chains
+// interleaved so that consecutive instructions are independent.
+__device__ __forceinline__ void max16x4(const f32x16 (&x)[4], float (&m)[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) m[b] = max3f(x[b][0], x[b][1], x[b][2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) m[b] = max3f(m[b], x[b][i], x[b][i + 1]);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) m[b] = max3f(m[b], x[b][15], x[b][15]);
+}
 constexpr int kPPWaves = 8;
 constexpr int kPPAhead = 8;  // LDS operand reads issued ahead of their MFMA in the matrix phase
 
@@ -628,14 +650,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
       for (int kt = 0; kt < 4; ++kt) mask_tail(s[kt], valid_prefix(key0 + 32 * kt, last));
     }
     float bmax[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      float mx = s[kt][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      bmax[kt] = mx;
-    }
-    float cm = fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3]));
+    max16x4(s, bmax);
+    float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
     cm = pair_max(cm);
     const float m_new = fmaxf(m_run, cm * p.c);
     alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // applied to acc by the next matrix phase
