@@ -168,6 +168,37 @@ __device__ __forceinline__ void mask_tail(f32x16 &s, int nvalid) {
   for (int r = 0; r < 16; ++r) s[r] = r < nvalid ? s[r] : -__builtin_inff();
 }
 
+// The largest of three values in one v_max3_f32.  Logits are never NaN; written with fmaxf, the
+// compiler would first copy each MFMA result through a quieting v_max (it cannot know they are
+// canonical), a third more instructions for a block maximum.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// The largest of each of four blocks of 16 logits: eight v_max3_f32 per block, the four chains
+// interleaved so that consecutive instructions are independent.
+__device__ __forceinline__ void max16x4(const f32x16 (&x)[4], float (&m)[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) m[b] = max3f(x[b][0], x[b][1], x[b][2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) m[b] = max3f(m[b], x[b][i], x[b][i + 1]);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) m[b] = max3f(m[b], x[b][15], x[b][15]);
+}
+// The largest of one block of 16 logits, as two interleaved chains.
+__device__ __forceinline__ float max16(const f32x16 &x) {
+  float a = max3f(x[0], x[1], x[2]), b = max3f(x[3], x[4], x[5]);
+#pragma unroll
+  for (int i = 6; i < 14; i += 4) {
+    a = max3f(a, x[i], x[i + 1]);
+    b = max3f(b, x[i + 2], x[i + 3]);
+  }
+  return max3f(a, b, max3f(x[14], x[15], x[15]));
+}
+
 // Smooth-Q: 16 consecutive fp32 values (delta of a lane's 16 keys), the initial accumulator of a
 // logit chain.
 __device__ __forceinline__ f32x16 delta16(const float *d) {

@@ -408,14 +408,8 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
     // ---- running max (refreshed once per chunk) -----------------------------------------
     // Block maxima of the logits first: each lane's 16 registers of a sub-tile are one P block.
     float bmax[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      float mx = s[kt][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      bmax[kt] = mx;
-    }
-    float cm = fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3]));
+    max16x4(s, bmax);
+    float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
     cm = pair_max(cm);
     const float m_new = fmaxf(m_run, cm * p.c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
@@ -526,26 +520,6 @@ constexpr uint32_t kLdsK = 0, kLdsV = 32768;  // byte offsets of the K-hat and V
 // read must then cover the 16 distinct 16-byte slots of 256 bytes, 4 * (d & 3) + column, so rows
 // that share d & 3 get different columns.
 __device__ __forceinline__ int sw_v64(int d) { return (d >> 2) & 3; }
-// The largest of three values in one v_max3_f32.  The logits are never NaN; written out, the
-// compiler would first copy each MFMA result through a quieting v_max (it cannot know they are
-// canonical), a third more instructions in the vector phase.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-// The largest of each of four blocks of 16 logits: eight v_max3_f32 per block, the four chains
-// interleaved so that consecutive instructions are independent.
-__device__ __forceinline__ void max16x4(const f32x16 (&x)[4], float (&m)[4]) {
-#pragma unroll
-  for (int b = 0; b < 4; ++b) m[b] = max3f(x[b][0], x[b][1], x[b][2]);
-#pragma unroll
-  for (int i = 3; i < 15; i += 2)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) m[b] = max3f(m[b], x[b][i], x[b][i + 1]);
-#pragma unroll
-  for (int b = 0; b < 4; ++b) m[b] = max3f(m[b], x[b][15], x[b][15]);
-}
 constexpr int kPPWaves = 8;
 constexpr int kPPAhead = 8;  // LDS operand reads issued ahead of their MFMA in the matrix phase
 
