@@ -299,6 +299,27 @@ def main():
     variants["all"]["fwd_bwd_ms"] = round(ms, 4)
     variants["all"]["fwd_bwd_TFLOP/s"] = round((fl["fwd"] + fl["bwd"]) / (ms * 1e-3) / 1e12, 1)
 
+    # The Wan2.1 480x832, 81-frame workload (L = 21*30*52 = 32760, a ragged multiple of the 128-key
+    # chunk): the training forward (with the auxiliary high-precision output) alone and followed by
+    # the backward, over back-to-back calls.  TFLOP/s on the conventional 4*B*H*L^2*D forward and
+    # 2.5x that backward; the auxiliary P.V adds half a forward of executed MFMA work.
+    q4, k4, v4, do4 = (t.to(dev) for t in synth.wan_480x832x81())
+    L4 = q4.shape[1]
+    fl4 = 4.0 * B * H * L4 * L4 * D
+
+    def train4():
+        o, aux = m.attn_qat_fwd(q4, k4, v4, training=True)
+        m.attn_qat_bwd(q4, k4, v4, aux, do4)
+
+    fwd4_ms = timed(lambda: m.attn_qat_fwd(q4, k4, v4, training=True), 3)
+    fb4_ms = timed(train4, 3)
+    wan480 = {"L": L4, "fwd_flop": fl4, "bwd_flop": 2.5 * fl4, "aux_pv_flop": 0.5 * fl4,
+              "train_fwd_ms": round(fwd4_ms, 4), "train_fwd_TFLOP/s": round(fl4 / (fwd4_ms * 1e-3) / 1e12, 1),
+              "train_fwd_executed_TFLOP/s": round(1.5 * fl4 / (fwd4_ms * 1e-3) / 1e12, 1),
+              "fwd_bwd_ms": round(fb4_ms, 4), "fwd_bwd_TFLOP/s": round(3.5 * fl4 / (fb4_ms * 1e-3) / 1e12, 1),
+              "frac_bf16_peak": round(3.5 * fl4 / (fb4_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q4, k4, v4, do4
+
     # The NVFP4 QAD linear on the Wan2.1 1.3B feed-forward projections at this token count (25088
     # tokens, 1536 -> 8960 and 8960 -> 1536): the forward (activation and weight fake-quant, BF16
     # MFMA GEMM, bias) and the straight-through backward, each timed over back-to-back calls; the
@@ -417,7 +438,7 @@ def main():
                    "vsa_cubes": fl["cubes"], "vsa_topk": fl["topk"], "fq_shape": list(xs[0].shape)},
         "roofline": roofline, "cpu_baseline": cpu, "attention": attn, "fq": fq,
         "phases_ms": {p: round(t, 4) for p, t in phase_ms.items()}, "kernels": kernels, "variants": variants,
-        "linear": linear,
+        "linear": linear, "wan_480x832x81": wan480,
     }
     print(json.dumps(out), flush=True)
 
