@@ -186,7 +186,7 @@ def main():
     ap.add_argument("--pmc-probe", action="store_true", help="one untimed pass of each stage plus a 1 GiB copy")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); sharding the "
+        print(f"bench.py: the library and this benchmark run on one GPU only (asked for --gpus {args.gpus}); sharding the "
               "heads of a call over several GPUs is not built.", file=sys.stderr)
         sys.exit(2)
 
