@@ -188,39 +188,49 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
     AQ_OPAQUE(ta);
     const bool tail = (ch + 1) * kChunk > p.lk;
     const bool diag = p.causal && (ch + 1) * kChunk - 1 > qc * kChunk + qg * 32;
+    // Both 32-key halves' logits and dP first, then both halves' dS, then both halves' dQ
+    // products: the second half's MFMAs are independent of the first half's vector work.
+    f32x16 s[2], dp[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       // smooth-Q: the logit chain starts from delta of the lane's 16 keys, as the forward's does
-      f32x16 s, dp = f32x16{};
-      if constexpr (SQ) s = delta16(p.delta + (bh * p.Ck + ch) * kChunk + 64 * kh + 32 * k2 + 16 * hf);
+      dp[k2] = f32x16{};
+      if constexpr (SQ) s[k2] = delta16(p.delta + (bh * p.Ck + ch) * kChunk + 64 * kh + 32 * k2 + 16 * hf);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const uint32_t at = (ka ^ (32 * t)) + k2 * 8192;
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at)), qf[t], (SQ || t > 0) ? s : f32x16{}, 0,
-                                                    0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at + 32768)), of[t], dp, 0, 0, 0);
+        s[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at)), qf[t],
+                                                        (SQ || t > 0) ? s[k2] : f32x16{}, 0, 0, 0);
+        dp[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at + 32768)), of[t], dp[k2], 0, 0, 0);
       }
+    }
+    bf16x8 d0[2], d1[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
       if (tail || diag || !qvalid) {
         const int key0 = (int)(ch * kChunk) + 64 * kh + 32 * k2 + 16 * hf;
-        mask_tail(s, valid_prefix(key0, last));
+        mask_tail(s[k2], valid_prefix(key0, last));
       }
       float ds[16];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const float A = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -lse2));
-        ds[rr] = A * (dp[rr] - Di);
+        const float A = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k2][rr], p.c, -lse2));
+        ds[rr] = A * (dp[k2][rr] - Di);
       }
-      const bf16x8 d0 = pack8_cvt(ds), d1 = pack8_cvt(ds + 8);
+      d0[k2] = pack8_cvt(ds);
+      d1[k2] = pack8_cvt(ds + 8);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         // k-slot group jj = 0 (keys 16h + 0..7, register pack d0) and jj = 1 (keys 16h + 8..15)
         const uint32_t b0 = (ta ^ (dt << 6)) + k2 * 8192, b1 = (ta ^ ((dt << 6) | 16)) + k2 * 8192;
         const uint2 x0 = ds_read_tr16_at(b0), x1 = ds_read_tr16_at(b1 + 1024);
         const uint2 y0 = ds_read_tr16_at(b0 + 2048), y1 = ds_read_tr16_at(b1 + 3072);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{x0.x, x0.y, x1.x, x1.y}), d0, acc[dt], 0, 0, 0);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{y0.x, y0.y, y1.x, y1.y}), d1, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{x0.x, x0.y, x1.x, x1.y}), d0[k2], acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{y0.x, y0.y, y1.x, y1.y}), d1[k2], acc[dt], 0, 0, 0);
       }
-    }
   }
 
   // The two waves of a query group add their partial sums; wave kh = 0 stores.
