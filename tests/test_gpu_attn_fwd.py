@@ -65,7 +65,8 @@ def test_quantizer_subsets(m, flags):
 
 
 @pytest.mark.parametrize("Lq,Lk,causal", [(300, 300, False), (200, 333, False), (77, 1000, False),
-                                          (300, 300, True), (129, 129, True), (1, 17, False)])
+                                          (300, 300, True), (129, 129, True), (1, 17, False),
+                                          (520, 128, False), (513, 513, True)])
 def test_ragged_cross_and_causal(m, Lq, Lk, causal):
     q, k, v = rand_qkv(2, Lq, Lk, 3, seed=Lq * 7 + Lk, mult=2.0)
     o = run(m, q, k, v, causal=causal)
