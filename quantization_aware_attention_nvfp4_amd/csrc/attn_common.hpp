@@ -188,16 +188,6 @@ __device__ __forceinline__ void max16x4(const f32x16 (&x)[4], float (&m)[4]) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) m[b] = max3f(m[b], x[b][15], x[b][15]);
 }
-// The largest of one block of 16 logits, as two interleaved chains.
-__device__ __forceinline__ float max16(const f32x16 &x) {
-  float a = max3f(x[0], x[1], x[2]), b = max3f(x[3], x[4], x[5]);
-#pragma unroll
-  for (int i = 6; i < 14; i += 4) {
-    a = max3f(a, x[i], x[i + 1]);
-    b = max3f(b, x[i + 2], x[i + 3]);
-  }
-  return max3f(a, b, max3f(x[14], x[15], x[15]));
-}
 
 // Smooth-Q: 16 consecutive fp32 values (delta of a lane's 16 keys), the initial accumulator of a
 // logit chain.
