@@ -14,11 +14,13 @@ B=1, H=12, L=16*28*56=25088, D=128):
      top-20; its fine stage's lse, chunk maxima and auxiliary output written);
   5. vsa_qat_bwd, the straight-through backward of the cube-sparse fine stage.
 
-value = algorithmic attention FLOP per step / ms_per_step, where the dense
-forward counts 4*B*H*L^2*D, the backward 2.5x that (10*B*H*L^2*D), the
-cube-sparse forward 4*B*H*n*k*128^2*D for its fine stage plus 4*B*H*n^2*D for
-its coarse stage, and its backward 2.5x the fine stage; fq contributes time but
-no FLOP.  After the step loop, the dense and cube-sparse inference forwards and
+value = the metric's own quantity: dense fake-quant attention forward + backward
+TFLOP/s at H=12, L=25088, D=128, i.e. (4 + 10)*B*H*L^2*D FLOP over the time of
+stages 2 and 3 inside the step (HIP events on the launch stream).  ms_per_step
+is the wall time of the whole step; the "step" object reports the step's
+composite rate, where the cube-sparse forward counts 4*B*H*n*k*128^2*D for its
+fine stage plus 4*B*H*n^2*D for its coarse stage, its backward 2.5x the fine
+stage, and fq contributes time but no FLOP.  After the step loop, the dense and cube-sparse inference forwards and
 fq on its own (back-to-back launches) are timed for the "attention" and "fq"
 objects, the attention variants (final-max statistics, static scales,
 smooth-K, two-level P, smooth-Q) for the "variants" object, and the NVFP4 QAD linear on the model's
@@ -369,7 +371,8 @@ def main():
     ms_step = wall * 1e3 / args.steps
     phase_ms = {p: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, p in enumerate(phases)}
     total_flop = fl["fwd"] + fl["bwd"] + fl["vsa"] + fl["vsa_bwd"]
-    value = total_flop / (ms_step * 1e-3) / 1e12
+    value_ms = phase_ms["fwd"] + phase_ms["bwd"]
+    value = (fl["fwd"] + fl["bwd"]) / (value_ms * 1e-3) / 1e12
 
     # Per-kernel averages and their algorithmic work per launch.
     fq_bytes = 2.0 * 2 * xs[0].numel()
@@ -433,9 +436,15 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "Wan2.1-T2V-1.3B attention at 448x896, 61 frames: fq + fwd + bwd + VSA fwd + VSA bwd",
+        "config": {"workload": "Wan2.1-T2V-1.3B attention at 448x896, 61 frames: NVFP4 fake-quant training forward "
+                               "+ straight-through backward (value); the step also runs fq, the cube-sparse "
+                               "forward and its backward",
                    "B": B, "H": H, "L": L, "D": D, "causal": False, "quant": "Q,K,V,P NVFP4 unit scale",
                    "vsa_cubes": fl["cubes"], "vsa_topk": fl["topk"], "fq_shape": list(xs[0].shape)},
+        "value_basis": {"flop": fl["fwd"] + fl["bwd"], "ms": round(value_ms, 4),
+                        "timing": "HIP events around the training forward and the backward inside each timed step"},
+        "step": {"stages": list(phases), "ms": round(ms_step, 4), "flop": total_flop,
+                 "TFLOP/s": round(total_flop / (ms_step * 1e-3) / 1e12, 2)},
         "roofline": roofline, "cpu_baseline": cpu, "attention": attn, "fq": fq,
         "phases_ms": {p: round(t, 4) for p, t in phase_ms.items()}, "kernels": kernels, "variants": variants,
         "linear": linear, "wan_480x832x81": wan480,

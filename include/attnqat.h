@@ -177,8 +177,11 @@ int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch
  * dS = A * (dP - D), dQ = scale dS K-hat, dK = scale dS^T Q-hat.
  * Inputs q, k, v, d_o (bf16, strided as in the forward) and o_hp, lse_log2, chunk_max_log2
  * exactly as written by attn_qat_fwd with the same arguments, quant_flags included (the
- * variants' scales and key means are recomputed from the same tensors); outputs dq, dk, dv bf16 with
- * their own strides.  workspace: at least attn_qat_workspace_size(1, ...) bytes.
+ * variants' scales and key means are recomputed from the same tensors): o_hp [B, H, lq, 128],
+ * lse_log2 [B, H, lq] and chunk_max_log2 [B, H, ceil(lk/128), lq] (x2 under AQ_TWO_LEVEL_P), fp32
+ * contiguous.  The pointers carry no sizes, so the library cannot check these shapes: smaller
+ * buffers are read past their end.  Outputs dq, dk, dv bf16 with their own strides.
+ * workspace: at least attn_qat_workspace_size(1, ...) bytes.
  * Errors: as attn_qat_fwd, plus AQ_EINVAL for any null gradient or statistics pointer.
  * ------------------------------------------------------------------------------------------- */
 int attn_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp, const void *d_o,
@@ -210,9 +213,12 @@ int attn_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp,
  * selected cube, in list order) and o_hp [B, H, L, 128], fp32 contiguous, defined as for
  * attn_qat_fwd.
  * workspace: at least attn_qat_workspace_size(2, ...) bytes with lk = L.
+ * A query cube whose coarse logits are NaN (a NaN among its tokens) ranks them below every
+ * number, so its list still holds topk distinct cubes (the lowest indices among equals).
  * Errors: AQ_EINVAL (as the forward, plus grid sizes not divisible by the cube, L !=
  * grid_t*grid_h*grid_w, sparsity outside [0,1], only some of the training outputs);
- * AQ_ENOTSUP (cube of other than 128 tokens).
+ * AQ_ENOTSUP (cube of other than 128 tokens, more than 4096 cubes, more than 1024 selected cubes
+ * per query cube).
  * ------------------------------------------------------------------------------------------- */
 int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void *o_coarse,
                 int32_t *sel, int batch, int num_heads, int head_size, int64_t seq_len,
@@ -230,9 +236,13 @@ int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void 
  * selected cubes: dQ of a query sums over its cube's selected keys; dK and dV of a key sum over
  * the queries of every cube that selected the key's cube, with the chunk maximum of the
  * selection slot that cube used.  The coarse stage (o_coarse) is not differentiated here.
- * Inputs q, k, v, d_o (bf16 [B, L, H, 128] by strides), sel, lse_log2, chunk_max_log2 and o_hp
- * exactly as written by vsa_qat_fwd with the same arguments (sel: ascending, distinct);
- * outputs dq, dk, dv bf16 with their own strides.
+ * Inputs q, k, v, d_o (bf16 [B, L, H, 128] by strides), sel [B, H, n, topk] int32,
+ * lse_log2 [B, H, L], chunk_max_log2 [B, H, topk, L] (x2 under AQ_TWO_LEVEL_P) and o_hp
+ * [B, H, L, 128] fp32, exactly as written by vsa_qat_fwd with the same arguments, sparsity
+ * included (topk follows from it; the shapes cannot be checked here, and smaller buffers are read
+ * past their end).  sel must hold distinct cube indices in ascending order; an entry outside
+ * [0, n) is clamped into it, so a malformed list gives meaningless gradients but no access
+ * outside the operands.  Outputs dq, dk, dv bf16 with their own strides.
  * workspace: at least attn_qat_workspace_size(3, ...) bytes with lq = lk = L.
  * Errors: as vsa_qat_fwd, plus AQ_EINVAL for a null gradient, statistics or sel pointer and
  * AQ_ENOTSUP for more than 4096 cubes.
@@ -267,6 +277,8 @@ size_t attn_qat_workspace_size(int op, int batch, int num_heads, int64_t lq, int
  *   (fp32 accumulation).  Any output may be NULL to skip it.
  * qad_observe_amax: *amax = max(*amax, max|x|) over numel bf16 values (max calibration; *amax is a
  *   DEVICE fp32 scalar the caller zeroes before the first calibrating call).
+ * qad_input_global_sf: *g_out = fp32(448*6 / max(*amax, 1e-12)) ([QAD] input_global_sf after
+ *   calibration; NaN read as 0), both DEVICE fp32 scalars; *g_out serves as input_sf.
  * Workspace: qad_linear_workspace_size(0 = forward, 1 = backward, m, n, k) bytes of DEVICE memory
  *   (any alignment).
  * Errors: AQ_EINVAL (null pointers, non-positive sizes, tensors not 16-byte aligned, workspace too
@@ -279,6 +291,7 @@ int qad_linear_fwd(const void *x, const void *w, const void *bias, void *y, int6
 int qad_linear_bwd(const void *grad_y, const void *x, const void *w, void *grad_x, void *grad_w, void *grad_b,
                    int64_t m, int64_t n, int64_t k, void *workspace, size_t workspace_bytes, void *stream);
 int qad_observe_amax(const void *x, int64_t numel, float *amax, void *stream);
+int qad_input_global_sf(const float *amax, float *g_out, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Kernel timing (profiling aid, not part of the method).

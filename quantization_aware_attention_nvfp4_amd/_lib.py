@@ -23,7 +23,8 @@ AQ_FLAGS_ALL = 1023
 
 EXPORTED = ("aq_last_error", "fq_nvfp4", "fq_nvfp4_static_scale", "attn_qat_fwd", "attn_qat_bwd",
             "vsa_qat_fwd", "vsa_qat_bwd", "vsa_topk", "attn_qat_workspace_size", "aq_kernel_timing",
-            "aq_kernel_times", "qad_linear_workspace_size", "qad_linear_fwd", "qad_linear_bwd", "qad_observe_amax")
+            "aq_kernel_times", "qad_linear_workspace_size", "qad_linear_fwd", "qad_linear_bwd", "qad_observe_amax",
+            "qad_input_global_sf")
 
 
 class aq_strides(ctypes.Structure):
@@ -72,6 +73,8 @@ def _declare(lib):
     lib.qad_linear_bwd.restype = i32
     lib.qad_observe_amax.argtypes = [P, i64, P, P]
     lib.qad_observe_amax.restype = i32
+    lib.qad_input_global_sf.argtypes = [P, P, P]
+    lib.qad_input_global_sf.restype = i32
 
 
 def load():

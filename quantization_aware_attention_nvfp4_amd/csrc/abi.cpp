@@ -234,6 +234,10 @@ int vsa_qat_fwd(const void *q, const void *k, const void *v, void *o_fine, void 
   s.o_coarse = o_coarse; s.sel = sel;
   s.n_cubes = (int)(seq_len / aq::kChunkHost);
   s.topk = vsa_topk(sparsity, s.n_cubes);
+  // The backward walks lists of at most kMaxCubesHost query cubes per key cube, and the top-k
+  // kernel keeps every cube's score in LDS (8 bytes per cube): the same cap for both directions.
+  if (s.n_cubes > aq::kMaxCubesHost)
+    return fail(AQ_ENOTSUP, "vsa_qat_fwd: at most %d cubes (got %d)", aq::kMaxCubesHost, s.n_cubes);
   if (s.topk > 1024)
     return fail(AQ_ENOTSUP, "vsa_qat_fwd: at most 1024 selected cubes per query cube (got %d)", s.topk);
   return hip_status(aq::launch_vsa_fwd(a, s, (hipStream_t)stream), "vsa_qat_fwd launch");
@@ -360,6 +364,11 @@ int qad_linear_bwd(const void *grad_y, const void *x, const void *w, void *grad_
   if (grad_b && !grad_w)
     return hip_status(aq::launch_colsum(grad_y, m, n, grad_b, (float *)(ws + lw.part), st), "qad_linear_bwd grad_b");
   return ok();
+}
+
+int qad_input_global_sf(const float *amax, float *g_out, void *stream) {
+  if (!amax || !g_out) return fail(AQ_EINVAL, "qad_input_global_sf: null pointer");
+  return hip_status(aq::launch_scale_from_amax(amax, g_out, (hipStream_t)stream), "qad_input_global_sf launch");
 }
 
 int qad_observe_amax(const void *x, int64_t numel, float *amax, void *stream) {

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
   }
   // Key chunk of iteration `it`: the it-th selected cube, or chunk `it` (a uniform scalar).
   const int32_t *sel_row = SPARSE ? p.sel + (bh * p.Cq + qc) * p.nsel : nullptr;
-  auto chunk_at = [&](int64_t it) -> int64_t { return SPARSE ? (int64_t)sel_row[it] : it; };
+  auto chunk_at = [&](int64_t it) -> int64_t { return SPARSE ? clamp_chunk(sel_row[it], p.Ck) : it; };
   // Chunk copies: per lane 4 K-hat and 4 V-hat pieces of 16 bytes.
   uint32_t c_voff[4];
 #pragma unroll

@@ -202,6 +202,11 @@ __device__ __forceinline__ f32x16 delta16(const float *d) {
   return r;
 }
 
+// A cube-sparse chunk index, read from a selection list, clamped into [0, n): a list that is not
+// the forward's (out-of-range entries) then gives meaningless numbers, never an access outside the
+// K-hat/V-hat workspace.
+__device__ __forceinline__ int64_t clamp_chunk(int64_t c, int64_t n) { return c < 0 ? 0 : (c >= n ? n - 1 : c); }
+
 // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a contiguous range of work ids so
 // workgroups that share a head's operands share that XCD's L2.  Returns -1 for the padding
 // workgroups of the last partial range.

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
     __syncthreads();
   }
   auto chunk_of = [&](int64_t it) -> int64_t {
-    return p.sel ? (int64_t)__builtin_amdgcn_readfirstlane(lds_sel[it]) : it;  // uniform: a scalar
+    return p.sel ? clamp_chunk(__builtin_amdgcn_readfirstlane(lds_sel[it]), p.kchunks) : it;  // uniform: a scalar
   };
   auto ktile = [&](int64_t c) { return (const uint8_t *)(p.kq + (bh * p.kchunks + c) * (kChunk * kD / 8)); };
   auto vtile = [&](int64_t c) { return (const uint8_t *)(p.vt + (bh * p.kchunks + c) * (kChunk * kD / 8)); };
@@ -774,7 +774,7 @@ __global__ __launch_bounds__(256, 2) void rowmax_kernel(FwdParams p) {
     __syncthreads();
   }
   auto chunk_of = [&](int64_t it) -> int64_t {
-    return p.sel ? (int64_t)__builtin_amdgcn_readfirstlane(lds_sel[it]) : it;
+    return p.sel ? clamp_chunk(__builtin_amdgcn_readfirstlane(lds_sel[it]), p.kchunks) : it;
   };
   auto ktile = [&](int64_t c) { return (const uint8_t *)(p.kq + (bh * p.kchunks + c) * (kChunk * kD / 8)); };
   const StageOffsets so = stage_offsets<WAVES>(wave, lane);

@@ -144,6 +144,12 @@ __global__ void static_scale_final(float *g) {
   *g = 2688.0f / a;  // FP4_RANGE = 448 * 6
 }
 
+// The same scale from an observed maximum (a calibrated activation's amax; fmaxf reads NaN as 0).
+__global__ void scale_from_amax_kernel(const float *amax, float *g) {
+  const float a = fmaxf(fmaxf(*amax, 0.0f), 1e-12f);
+  *g = 2688.0f / a;
+}
+
 int grid_for(int64_t work_items, int per_thread) {
   int64_t blocks = (work_items + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
   if (blocks < 1) blocks = 1;
@@ -177,6 +183,11 @@ hipError_t launch_fq(const void *x, void *y, int64_t outer, int64_t axis, int64_
       AQ_LAUNCH("fq_general_static", fq_general_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
                          (const uint16_t *)x, (uint16_t *)y, outer, axis, inner, g);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_from_amax(const float *amax, float *g_out, hipStream_t stream) {
+  AQ_LAUNCH("scale_from_amax", scale_from_amax_kernel, dim3(1), dim3(1), 0, stream, amax, g_out);
   return hipGetLastError();
 }
 

@@ -10,7 +10,8 @@ namespace aq {
 
 constexpr int kHeadDimHost = 128;
 constexpr int kChunkHost = 128;
-constexpr int kMaxCubesHost = 4096;  // cube-sparse backward: longest per-key-cube list
+constexpr int kMaxCubesHost = 4096;  // cube-sparse: most cubes per head (longest per-key-cube list)
+constexpr int kMaxSelHost = 1024;    // cube-sparse: most selected cubes per query cube
 
 // Flag bits of a call (the ABI's AQ_* values): the four quantizers and the variants.
 constexpr unsigned kFlagQ = 1u, kFlagK = 2u, kFlagV = 4u, kFlagP = 8u;
@@ -57,7 +58,8 @@ struct VsaArgs {
 //   op 0 (forward):  kq (K-hat rows), vt (V-hat tiles)
 //   op 1 (backward): kq, vq (V-hat rows), qq (Q-hat rows), dvec [B*H, lq] fp32 (D_i = <dO_i, o_hp_i>)
 //   op 2 (cube-sparse forward): kq, vt, pool [3, B*H, n, 128] bf16 (cube means of Q, K, V),
-//                    selw [B*H, n, n] int32 (selection when the caller passes none)
+//                    selw [B*H, n, min(n, kMaxSelHost)] int32 (selection when the caller passes
+//                    none; a call's topk entries per query cube)
 //   op 3 (cube-sparse backward): the op 1 regions, plus slot [B*H, n, n] int16 (position of every
 //                    key cube in every query cube's selection, or -1)
 //   every op: scal (global scales g_q, g_k, g_v, g_p as fp32, then three uint32 abs-max
@@ -97,7 +99,8 @@ inline Workspace workspace_layout(int op, int batch, int heads, int64_t lq, int6
   if (op == 2) {
     const size_t n = (size_t)(lk / kChunkHost);
     w.pool = take(3 * bh * n * kHeadDimHost * 2);
-    w.selw = take(bh * n * n * 4);
+    // a selection list has topk <= min(n, kMaxSel) entries per query cube
+    w.selw = take(bh * n * (n < (size_t)kMaxSelHost ? n : (size_t)kMaxSelHost) * 4);
   }
   w.scal = take(256);
   w.kmean = take(bh * kHeadDimHost * 4);
@@ -120,6 +123,8 @@ hipError_t launch_fq(const void *x, void *y, int64_t outer, int64_t axis, int64_
                      const float *g, hipStream_t stream);
 // *g_out = 2688 / max(max|x|, 1e-12).
 hipError_t launch_static_scale(const void *x, int64_t n, float *g_out, hipStream_t stream);
+// *g_out = 2688 / max(*amax, 1e-12) (NaN read as 0), both device scalars.
+hipError_t launch_scale_from_amax(const float *amax, float *g_out, hipStream_t stream);
 
 // One 128-row chunk of a strided [B, L, H, 128] bf16 tensor per workgroup: optional fake
 // quantization (kQuantNone, kQuantD along d per row, kQuantRows along rows per column; kQuantRowsF16

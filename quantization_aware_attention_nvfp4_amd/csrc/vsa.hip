@@ -76,7 +76,10 @@ __global__ __launch_bounds__(256) void select_kernel(const uint16_t *__restrict_
     const uint16_t *kr = kc + b * kD;
     float acc = 0.0f;
     for (int d = 0; d < kD; ++d) acc = __builtin_fmaf(qa[d], bf16lo(kr[d]), acc);
-    score[b] = scale * acc;
+    // A NaN score (a NaN anywhere in the cube's tokens) ranks below every number, so the top-k
+    // always finds topk distinct cubes.
+    const float sc = scale * acc;
+    score[b] = sc == sc ? sc : -__builtin_inff();
     taken[b] = 0;
   }
   __syncthreads();
@@ -95,6 +98,12 @@ __global__ __launch_bounds__(256) void select_kernel(const uint16_t *__restrict_
       float s0 = red_s[0];
       int i0 = red_i[0];
       for (int w = 1; w < 4; ++w) argmax_step(s0, i0, red_s[w], red_i[w]);
+      // Every score is a number (at worst -inf, which the tie rule still picks), so i0 is an
+      // untaken cube; the lowest untaken one stands in should that ever fail.
+      if (i0 < 0 || i0 >= n || taken[i0]) {
+        i0 = 0;
+        while (i0 < n - 1 && taken[i0]) ++i0;
+      }
       taken[i0] = 1;
     }
     __syncthreads();

@@ -137,6 +137,21 @@ def _aux_dict(quant_flags: int, lse, cmax, ohp) -> dict:
     return aux
 
 
+def _check_aux(aux: dict, B: int, H: int, Lq: int, C: int, D: int, quant_flags: int) -> None:
+    """The forward's auxiliary outputs, as the backward reads them: contiguous fp32 device tensors
+    lse_log2 [B, H, Lq], chunk_max_log2 [B, H, C, Lq] (C = key chunks, or selected cubes) and
+    o_hp [B, H, Lq, D].  Any other shape would make the kernels read past the buffers."""
+    want = {"lse_log2": (B, H, Lq), "chunk_max_log2": (B, H, C, Lq), "o_hp": (B, H, Lq, D)}
+    for name, shape in want.items():
+        t = aux.get(name)
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"aux[{name!r}] must be a contiguous fp32 device tensor")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"aux[{name!r}] has shape {tuple(t.shape)}, expected {shape} "
+                             "(pass the aux of the forward call with the same arguments)")
+    _check_chunk_stats(quant_flags, aux["chunk_max_log2"])
+
+
 def _check_chunk_stats(quant_flags: int, cmax: torch.Tensor) -> None:
     if quant_flags & AQ_TWO_LEVEL_P:
         need = (cmax.storage_offset() + 2 * cmax.numel()) * 4
@@ -192,11 +207,7 @@ def attn_qat_bwd(q, k, v, aux, d_o, causal: bool = False, sm_scale: Optional[flo
     dv = torch.empty_like(v, memory_format=torch.contiguous_format)
     ws = _workspace(1, B, H, Lq, Lk, q.device) if D == HEAD_SIZE and Hkv == H else torch.empty(
         256, dtype=torch.uint8, device=q.device)
-    for n in ("lse_log2", "chunk_max_log2", "o_hp"):
-        t = aux[n]
-        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"aux[{n}] must be a contiguous fp32 device tensor")
-    _check_chunk_stats(quant_flags, aux["chunk_max_log2"])
+    _check_aux(aux, B, H, Lq, (Lk + CHUNK - 1) // CHUNK, D, quant_flags)
     check(load().attn_qat_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), aux["o_hp"].data_ptr(),
                               d_o.data_ptr(), aux["lse_log2"].data_ptr(), aux["chunk_max_log2"].data_ptr(),
                               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, D, Lq, Lk,
@@ -320,14 +331,15 @@ def vsa_qat_bwd(q, k, v, aux, d_o, grid=(16, 28, 56), cube=(4, 4, 8), sparsity: 
         raise ValueError("d_o must have q's shape")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
-    for name in ("lse_log2", "chunk_max_log2", "o_hp"):
-        t = aux[name]
-        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"aux[{name}] must be a contiguous fp32 device tensor")
-    _check_chunk_stats(quant_flags, aux["chunk_max_log2"])
-    sel = aux["sel"]
-    if sel.dtype != torch.int32 or not sel.is_contiguous() or not sel.is_cuda:
+    n = L // max(1, cube[0] * cube[1] * cube[2])
+    topk = vsa_topk(sparsity, n) if n > 0 else 0
+    sel = aux.get("sel")
+    if not isinstance(sel, torch.Tensor) or sel.dtype != torch.int32 or not sel.is_contiguous() or not sel.is_cuda:
         raise ValueError("aux['sel'] must be a contiguous int32 device tensor")
+    if tuple(sel.shape) != (B, H, n, topk):
+        raise ValueError(f"aux['sel'] has shape {tuple(sel.shape)}, expected {(B, H, n, topk)} for "
+                         f"{n} cubes at sparsity {sparsity} (pass the forward's aux and sparsity)")
+    _check_aux(aux, B, H, L, topk, D, quant_flags)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format)
     dk = torch.empty_like(k, memory_format=torch.contiguous_format)
     dv = torch.empty_like(v, memory_format=torch.contiguous_format)
@@ -391,11 +403,14 @@ def _rows(x: torch.Tensor, k: int) -> torch.Tensor:
     return x.reshape(-1, k).contiguous()
 
 
-def input_global_sf(amax: float, device) -> torch.Tensor:
-    """The static activation scale 448*6 / max(amax, 1e-12) as a device fp32 scalar (input_global_sf)."""
-    if not amax > 0:
-        raise ValueError(f"calibrated amax must be positive, got {amax}")
-    return torch.tensor(FP4_RANGE / max(float(amax), 1e-12), dtype=torch.float32, device=device)
+def input_global_sf(amax: torch.Tensor) -> torch.Tensor:
+    """The static activation scale (input_global_sf) of a calibrated maximum, formed by the library
+    (qad_input_global_sf): ``amax`` and the result are one-element fp32 device tensors."""
+    if not isinstance(amax, torch.Tensor) or amax.dtype != torch.float32 or not amax.is_cuda or amax.numel() != 1:
+        raise ValueError("amax must be a one-element fp32 device tensor")
+    g = torch.empty(1, dtype=torch.float32, device=amax.device)
+    check(load().qad_input_global_sf(amax.data_ptr(), g.data_ptr(), _stream_ptr(amax)), "qad_input_global_sf")
+    return g
 
 
 def qad_linear_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
@@ -487,15 +502,23 @@ class QADLinear:
         self.enabled, self.calibrating = True, False
         self.observed_amax = torch.zeros(1, dtype=torch.float32, device=weight.device)
         self.input_amax: Optional[float] = None
+        self.input_sf: Optional[torch.Tensor] = None
 
     def set_input_amax(self, amax: float) -> None:
+        """Fix the activation's calibrated maximum; the static scale is formed on the device."""
         if not amax > 0:
             raise ValueError(f"calibrated amax must be positive, got {amax}")
         self.input_amax = float(amax)
+        dev_amax = torch.tensor([self.input_amax], dtype=torch.float32).to(self.weight.device)
+        self.input_sf = input_global_sf(dev_amax)
 
     def finish_calibration(self) -> None:
         self.calibrating = False
-        self.set_input_amax(float(self.observed_amax.item()))
+        amax = float(self.observed_amax.item())
+        if not amax > 0:
+            raise ValueError(f"calibrated amax must be positive, got {amax}")
+        self.input_amax = amax
+        self.input_sf = input_global_sf(self.observed_amax)
 
     def __call__(self, x: torch.Tensor) -> torch.Tensor:
         if self.calibrating:
@@ -505,9 +528,9 @@ class QADLinear:
             return torch.nn.functional.linear(x, self.weight, self.bias)
         sf = None
         if self.act_scale == "static":
-            if self.input_amax is None:
+            if self.input_sf is None:
                 raise RuntimeError("static activation scale used before calibration")
-            sf = input_global_sf(self.input_amax, x.device)
+            sf = self.input_sf
         return qad_linear(x, self.weight, self.bias, sf)
 
 

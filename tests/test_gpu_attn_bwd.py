@@ -1,9 +1,12 @@
 """GPU parity of the straight-through backward (attn_qat_bwd) against the oracle,
 within the stated tolerance (tests/parity.py): full gradients on shapes that span
-several 128-key chunks with ragged tails, cross attention and causal masking;
-sampled dQ rows on the Wan2.1 480x832x81 workload (B=1, H=12, L=32760, D=128,
-L = 8 mod 16, so the last V/P block is partial) in the benchmark's launch
-configuration, plus properties that hold at any size for dK and dV there."""
+several 128-key chunks with ragged tails, cross attention and causal masking; on
+the Wan2.1 480x832x81 workload (B=1, H=12, L=32760, D=128, L = 8 mod 16, so the
+last V/P block is partial) sampled dQ rows of every head and sampled dK/dV key rows
+of one head (chunk edges and the whole last partial block included), plus
+properties that hold at any size for dK and dV there; on the 448x896x61 workload
+(L=25088) the training forward's outputs (o, lse, chunk maxima, o_hp) at sampled
+rows and sampled dQ/dK/dV rows, all in the benchmark's launch configuration."""
 import math
 
 import numpy as np
@@ -102,6 +105,22 @@ def test_autograd_function(m):
     assert torch.equal(vg.grad.view(torch.int16).cpu(), dv.view(torch.int16).cpu())
 
 
+def key_rows(L, n=64, seed=13):
+    """Sampled key rows: the first keys, both sides of the first chunk edge, the last full chunk's
+    edge, every key of the last 16-key block (partial when L is not a multiple of 16), then
+    seeded random keys up to n."""
+    last_chunk = (L - 1) // 128 * 128
+    fixed = {0, 1, 127, 128, last_chunk - 1, last_chunk, *range((L - 1) // 16 * 16, L)}
+    rng = np.random.default_rng(seed)
+    rest = [int(x) for x in rng.permutation(L) if int(x) not in fixed][: n - len(fixed)]
+    return np.array(sorted(fixed | set(rest)), np.int64)
+
+
+def one_head_bwd(q, k, v, do, h, qrows, krows):
+    sl = slice(h, h + 1)
+    return ref_bwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl], qrows=qrows, krows=krows)
+
+
 def test_wan_480x832x81_fwd_bwd(m):
     q, k, v, do = synth.wan_480x832x81()
     L = q.shape[1]
@@ -109,6 +128,15 @@ def test_wan_480x832x81_fwd_bwd(m):
     qrows = synth.sample_rows(L, 32, seed=5).numpy()
     r = ref_bwd(q, k, v, do, qrows=qrows, krows=np.zeros(0, np.int64))
     assert_close(bhrd(dq, qrows), r["dq"], "Wan 480x832x81 dq")
+    # dK and dV element by element at 64 key rows of one head (the oracle needs every row's
+    # statistics for a key gradient, so one head): keys 0, 1, 127, 128, 32639, 32640 and the
+    # partial last block 32752..32759 among them.
+    h = 4
+    krows = key_rows(L)
+    assert {0, 1, 127, 128, 32639, 32640, *range(32752, 32760)} <= set(krows.tolist()) and krows.size == 64
+    rk = one_head_bwd(q, k, v, do, h, np.zeros(0, np.int64), krows)
+    assert_close(bhrd(dk[:, :, h:h + 1], krows), rk["dk"], "Wan 480x832x81 dk rows")
+    assert_close(bhrd(dv[:, :, h:h + 1], krows), rk["dv"], "Wan 480x832x81 dv rows")
     # dK and dV at full size, through identities that hold at any size (non-causal):
     #   sum_j dK_j = scale * sum_i (sum_j dS_ij) Q-hat_i = 0, since every row of dS sums to 0;
     #   sum_j <dV_j, V-hat_j> = sum_i <dO_i, O_i>, since O = A-hat V-hat and dV = A-hat^T dO.
@@ -121,3 +149,41 @@ def test_wan_480x832x81_fwd_bwd(m):
     assert np.all(np.abs(lhs - rhs) <= 2e-3 * np.abs(terms).sum(-1)), (lhs, rhs)
     colsum = np.abs(dkv.sum(axis=2)).max()
     assert colsum <= 2e-3 * np.abs(dkv).sum(axis=2).max(), colsum
+
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+def test_wan_448x896x61_training(m):
+    # The benchmark's timed path at its own size: training forward (o, lse, chunk maxima, o_hp)
+    # and the backward, compared with the oracle at sampled rows.
+    q, k, v = synth.wan_448x896x61()
+    L = q.shape[1]
+    do = synth.normal_bf16(q.shape, 2003)
+    qg, kg, vg, dog = (t.cuda() for t in (q, k, v, do))
+    o, aux = m.attn_qat_fwd(qg, kg, vg, training=True)
+    dq, dk, dv = m.attn_qat_bwd(qg, kg, vg, aux, dog)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(L, 64, seed=21).numpy()
+    heads = [2, 9]
+    hs = torch.as_tensor(heads)
+    rf = oracle.attn_fwd(bhld_bits(q[:, :, hs]), bhld_bits(k[:, :, hs]), bhld_bits(v[:, :, hs]),
+                         1.0 / math.sqrt(128), rows=rows)
+    ri = torch.as_tensor(rows)
+    assert_close(bhrd(o[:, :, hs], rows), rf["o"], "448x896x61 training o")
+    assert_close(aux["o_hp"][:, hs][:, :, ri].cpu().numpy(), rf["o_hp"], "448x896x61 o_hp")
+    lse = aux["lse_log2"][:, hs][:, :, ri].cpu().numpy().astype(np.float64) / LOG2E
+    assert np.abs(lse - rf["lse"]).max() <= 1e-5 * max(1.0, np.abs(rf["lse"]).max())
+    cm = aux["chunk_max_log2"][:, hs][:, :, :, ri].cpu().numpy().astype(np.float64) / LOG2E  # [1, 2, C, R]
+    ref_cm = np.moveaxis(rf["cmax"], -1, 2)
+    assert cm.shape == ref_cm.shape == (1, 2, 196, rows.size)
+    assert np.abs(cm - ref_cm).max() <= 1e-5 * max(1.0, np.abs(ref_cm).max())
+    # gradients: dQ rows of both heads, dK/dV key rows of one
+    rb = oracle.attn_bwd(bhld_bits(q[:, :, hs]), bhld_bits(k[:, :, hs]), bhld_bits(v[:, :, hs]),
+                         bhld_bits(do[:, :, hs]), 1.0 / math.sqrt(128), qrows=rows, krows=np.zeros(0, np.int64))
+    assert_close(bhrd(dq[:, :, hs], rows), rb["dq"], "448x896x61 dq rows")
+    h = 9
+    krows = key_rows(L, seed=22)
+    rk = one_head_bwd(q, k, v, do, h, np.zeros(0, np.int64), krows)
+    assert_close(bhrd(dk[:, :, h:h + 1], krows), rk["dk"], "448x896x61 dk rows")
+    assert_close(bhrd(dv[:, :, h:h + 1], krows), rk["dv"], "448x896x61 dv rows")

@@ -99,10 +99,24 @@ def test_calibration_and_layer(m):
     layer.finish_calibration()
     want = oracle.observe_amax(bits(x2), oracle.observe_amax(bits(x1)))
     assert layer.input_amax == want
+    # the library's input_global_sf of the observed maximum is the oracle's static scale of the
+    # calibration data (whose abs-max is that maximum), bit for bit
+    gx = oracle.static_scale_bf16(np.concatenate([bits(x1).ravel(), bits(x2).ravel()]))
+    got = layer.input_sf.cpu().numpy()
+    assert got.view(np.uint32)[0] == np.float32(gx).view(np.uint32), (got[0], gx)
     y = layer(x1.cuda())
     torch.cuda.synchronize()
-    gx = float(np.float32(448.0 * 6.0 / want))
     assert_close(vals(y), oracle.linear_fwd(bits(x1), bits(w), None, gx=gx), "static layer")
+
+
+def test_input_global_sf_matches_oracle(m):
+    # every observed maximum the calibration can hold (bf16 magnitudes from 2^-133 to 2^127, and 0)
+    # against the oracle's static-scale arithmetic on a tensor with that abs-max
+    mags = np.arange(0, 0x7F80, 97, dtype=np.uint16)
+    amax = torch.from_numpy(oracle.bf16_bits_to_f32(mags).copy()).cuda()
+    got = torch.stack([m.input_global_sf(amax[i:i + 1]) for i in range(amax.numel())]).cpu().numpy().ravel()
+    want = np.array([oracle.static_scale_bf16(np.array([mg, 0x8000 | mg], np.uint16)) for mg in mags], np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
 def test_wan_ffn_sampled_rows(m):

@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import synth
+from tests import parity
 from tests.parity import assert_close, bf16_values, bhld_bits
 
 pytestmark = pytest.mark.gpu
@@ -87,17 +88,6 @@ def test_static_scales_differ_from_unit(m):
         assert not torch.equal(m.attn_qat_fwd(qg, kg, vg, quant_flags=fl), base), fl
 
 
-def agreement(sel_gpu, sel_ref):
-    sel_gpu = np.sort(sel_gpu, -1)
-    qa = np.all(sel_gpu == sel_ref, axis=-1)
-    B, H, n, _ = sel_ref.shape
-    ka = np.ones((B, H, n), bool)
-    for b in range(B):
-        for h in range(H):
-            for a in np.nonzero(~qa[b, h])[0]:
-                for c in set(sel_gpu[b, h, a]) ^ set(sel_ref[b, h, a]):
-                    ka[b, h, c] = False
-    return qa, ka
 
 
 @pytest.mark.parametrize("flags", [ALL | FM, ALL | FM | GQKV | GP | SK, ALL | TWO | GQKV, ALL | SQ | SK])
@@ -112,8 +102,8 @@ def test_cube_sparse_forward_and_backward(m, flags):
     args = (bhld_bits(q), bhld_bits(k), bhld_bits(v))
     rf = oracle.vsa_fwd(*args, SCALE, sparsity=0.6, flags=flags)
     rb = oracle.vsa_bwd(*args, bhld_bits(do), SCALE, sparsity=0.6, flags=flags)
-    qa, ka = agreement(aux["sel"].cpu().numpy(), rf["sel"])
-    assert qa.mean() >= 0.75
+    # selection is not affected by the variants (coarse stage unquantized): near ties only
+    qa, ka = parity.check_selection(aux["sel"].cpu().numpy(), rf["sel"], rf["score"], min_agree=0.75)
     qmask, kmask = np.repeat(qa, 128, -1), np.repeat(ka, 128, -1)
     assert_close(bhrd(o)[qmask], rf["o_fine"][qmask], f"o_fine flags={flags}")
     for name, t, mask in (("dq", dq, qmask), ("dk", dk, kmask), ("dv", dv, kmask)):
