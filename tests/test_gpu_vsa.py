@@ -97,9 +97,11 @@ def test_nan_token_keeps_selection_valid(m, where):
     if where == "q":
         # the NaN query cube's logits are all -inf after the mapping: ties to the lowest cubes
         assert np.array_equal(sel[0, 1, 3], np.arange(topk))
+        # every other row is finite (the NaN token's own row is whatever the fake quantizer makes
+        # of a NaN element: E2M1 has no NaN code)
         bad = np.zeros((L, H), bool)
         bad[tok, 1] = True
-        assert np.all(np.isfinite(on[0][~bad])) and np.all(np.isnan(on[0, tok, 1]))
+        assert np.all(np.isfinite(on[0][~bad]))
     else:
         # the NaN key cube ranks last for every query cube of that head and is never selected
         assert not np.any(sel[0, 1] == 3)
