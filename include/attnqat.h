@@ -168,6 +168,30 @@ int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * attn_qat_fwd_noalloc - attn_qat_fwd for callers that cannot allocate device memory: code under
+ * HIP stream capture, serving loops and harnesses that forbid hipMalloc.
+ *
+ * Same arguments, checks, kernels and results as attn_qat_fwd, without the workspace: the library
+ * uses a fixed scratch of AQ_NOALLOC_SCRATCH_BYTES in a file-scope device array, one copy per
+ * device, present from the library's first use of that device until the process ends.  The
+ * scratch of the CURRENT device (hipGetDevice) is used; `stream` must belong to it.  Nothing is
+ * allocated or freed (leave aq_kernel_timing off: its events are created per launch).
+ * Every call on a device shares that device's scratch and finds it as the last call left it;
+ * nothing in it needs to start at zero.  Calls that can overlap on one device (different streams,
+ * or different host threads) race on the scratch: the caller orders them.
+ * Errors: as attn_qat_fwd (the workspace ones aside), plus AQ_ENOTSUP when the call's workspace,
+ * attn_qat_workspace_size(0, batch, num_heads, lq, lk), exceeds AQ_NOALLOC_SCRATCH_BYTES (for
+ * example 12 heads of 32768 tokens fit: about 208 MB), and AQ_EHIP when the scratch's device
+ * address cannot be obtained.  Size checks come before any HIP call.
+ * ------------------------------------------------------------------------------------------- */
+#define AQ_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int attn_qat_fwd_noalloc(const void *q, const void *k, const void *v, void *o, int batch, int num_heads,
+                         int num_kv_heads, int head_size, int64_t lq, int64_t lk, aq_strides sq,
+                         aq_strides sk, aq_strides sv, aq_strides so, float softmax_scale, int causal,
+                         unsigned quant_flags, float *lse_log2, float *chunk_max_log2, float *o_hp,
+                         void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * attn_qat_bwd - straight-through backward ([META] backward "consistent STE with auxiliary
  * output"; [API] use_qat_qkv_backward, fake_quant_p_bwd, use_high_prec_o).
  *

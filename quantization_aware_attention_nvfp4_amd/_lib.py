@@ -24,7 +24,7 @@ AQ_FLAGS_ALL = 1023
 EXPORTED = ("aq_last_error", "fq_nvfp4", "fq_nvfp4_static_scale", "attn_qat_fwd", "attn_qat_bwd",
             "vsa_qat_fwd", "vsa_qat_bwd", "vsa_topk", "attn_qat_workspace_size", "aq_kernel_timing",
             "aq_kernel_times", "qad_linear_workspace_size", "qad_linear_fwd", "qad_linear_bwd", "qad_observe_amax",
-            "qad_input_global_sf")
+            "qad_input_global_sf", "attn_qat_fwd_noalloc")
 
 
 class aq_strides(ctypes.Structure):
@@ -48,6 +48,9 @@ def _declare(lib):
     lib.attn_qat_fwd.argtypes = [P, P, P, P, i32, i32, i32, i32, i64, i64, S, S, S, S, f32, i32, u32,
                                  P, P, P, P, sz, P]
     lib.attn_qat_fwd.restype = i32
+    lib.attn_qat_fwd_noalloc.argtypes = [P, P, P, P, i32, i32, i32, i32, i64, i64, S, S, S, S, f32, i32, u32,
+                                         P, P, P, P]
+    lib.attn_qat_fwd_noalloc.restype = i32
     lib.attn_qat_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i64, i64, S, S, S,
                                  S, S, S, S, f32, i32, u32, P, sz, P]
     lib.attn_qat_bwd.restype = i32

@@ -110,27 +110,30 @@ size_t attn_qat_workspace_size(int op, int batch, int num_heads, int64_t lq, int
   return aq::workspace_bytes(op, batch, num_heads, lq, lk);
 }
 
-int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch, int num_heads,
-                 int num_kv_heads, int head_size, int64_t lq, int64_t lk, aq_strides sq,
-                 aq_strides sk, aq_strides sv, aq_strides so, float softmax_scale, int causal,
-                 unsigned quant_flags, float *lse_log2, float *chunk_max_log2, float *o_hp,
-                 void *workspace, size_t workspace_bytes, void *stream) {
-  if (!q || !k || !v || !o) return fail(AQ_EINVAL, "attn_qat_fwd: null tensor pointer");
+// Argument checks of attn_qat_fwd and attn_qat_fwd_noalloc (everything but the workspace).
+static int check_fwd(const char *fn, const void *q, const void *k, const void *v, void *o, int batch,
+                     int num_heads, int num_kv_heads, int head_size, int64_t lq, int64_t lk, aq_strides sq,
+                     aq_strides sk, aq_strides sv, aq_strides so, float softmax_scale, int causal,
+                     unsigned quant_flags, float *lse_log2, float *chunk_max_log2, float *o_hp) {
+  if (!q || !k || !v || !o) return fail(AQ_EINVAL, "%s: null tensor pointer", fn);
   int rc = check_attention(batch, num_heads, num_kv_heads, head_size, lq, lk, softmax_scale, causal,
                            quant_flags);
   if (rc) return rc;
   if (!strides_ok(sq) || !strides_ok(sk) || !strides_ok(sv) || !strides_ok(so))
-    return fail(AQ_EINVAL, "attn_qat_fwd: strides must be positive with d contiguous");
+    return fail(AQ_EINVAL, "%s: strides must be positive with d contiguous", fn);
   if (!tensor_ok(q, sq) || !tensor_ok(k, sk) || !tensor_ok(v, sv) || !tensor_ok(o, so))
-    return fail(AQ_EINVAL, "attn_qat_fwd: tensors must be 16-byte aligned with strides that are multiples of 8 "
-                           "elements and below 2^24");
+    return fail(AQ_EINVAL, "%s: tensors must be 16-byte aligned with strides that are multiples of 8 "
+                           "elements and below 2^24", fn);
   if ((lse_log2 || chunk_max_log2 || o_hp) && !(lse_log2 && chunk_max_log2 && o_hp))
-    return fail(AQ_EINVAL, "attn_qat_fwd: the training outputs lse_log2, chunk_max_log2 and o_hp come together "
-                           "(all three or none)");
-  const size_t need = aq::workspace_bytes(0, batch, num_heads, lq, lk);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
-    return fail(AQ_EINVAL, "attn_qat_fwd: workspace must be 256-byte aligned and hold %zu bytes",
-                need);
+    return fail(AQ_EINVAL, "%s: the training outputs lse_log2, chunk_max_log2 and o_hp come together "
+                           "(all three or none)", fn);
+  return AQ_OK;
+}
+
+static int run_fwd(const char *fn, const void *q, const void *k, const void *v, void *o, int batch, int num_heads,
+                   int64_t lq, int64_t lk, aq_strides sq, aq_strides sk, aq_strides sv, aq_strides so,
+                   float softmax_scale, int causal, unsigned quant_flags, float *lse_log2, float *chunk_max_log2,
+                   float *o_hp, void *workspace, void *stream) {
   aq::AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o;
   a.batch = batch; a.heads = num_heads; a.lq = lq; a.lk = lk;
@@ -138,7 +141,43 @@ int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch
   a.scale = softmax_scale; a.causal = causal != 0; a.flags = quant_flags;
   a.lse = lse_log2; a.cmax = chunk_max_log2; a.o_hp = o_hp;
   a.workspace = workspace;
-  return hip_status(aq::launch_attn_fwd(a, (hipStream_t)stream), "attn_qat_fwd launch");
+  return hip_status(aq::launch_attn_fwd(a, (hipStream_t)stream), fn);
+}
+
+int attn_qat_fwd(const void *q, const void *k, const void *v, void *o, int batch, int num_heads,
+                 int num_kv_heads, int head_size, int64_t lq, int64_t lk, aq_strides sq,
+                 aq_strides sk, aq_strides sv, aq_strides so, float softmax_scale, int causal,
+                 unsigned quant_flags, float *lse_log2, float *chunk_max_log2, float *o_hp,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_fwd("attn_qat_fwd", q, k, v, o, batch, num_heads, num_kv_heads, head_size, lq, lk, sq, sk, sv,
+                     so, softmax_scale, causal, quant_flags, lse_log2, chunk_max_log2, o_hp);
+  if (rc) return rc;
+  const size_t need = aq::workspace_bytes(0, batch, num_heads, lq, lk);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
+    return fail(AQ_EINVAL, "attn_qat_fwd: workspace must be 256-byte aligned and hold %zu bytes",
+                need);
+  return run_fwd("attn_qat_fwd launch", q, k, v, o, batch, num_heads, lq, lk, sq, sk, sv, so, softmax_scale,
+                 causal, quant_flags, lse_log2, chunk_max_log2, o_hp, workspace, stream);
+}
+
+int attn_qat_fwd_noalloc(const void *q, const void *k, const void *v, void *o, int batch, int num_heads,
+                         int num_kv_heads, int head_size, int64_t lq, int64_t lk, aq_strides sq,
+                         aq_strides sk, aq_strides sv, aq_strides so, float softmax_scale, int causal,
+                         unsigned quant_flags, float *lse_log2, float *chunk_max_log2, float *o_hp,
+                         void *stream) {
+  int rc = check_fwd("attn_qat_fwd_noalloc", q, k, v, o, batch, num_heads, num_kv_heads, head_size, lq, lk, sq,
+                     sk, sv, so, softmax_scale, causal, quant_flags, lse_log2, chunk_max_log2, o_hp);
+  if (rc) return rc;
+  const size_t need = aq::workspace_bytes(0, batch, num_heads, lq, lk);
+  if (need > (size_t)AQ_NOALLOC_SCRATCH_BYTES)
+    return fail(AQ_ENOTSUP,
+                "attn_qat_fwd_noalloc: this call needs %zu bytes of scratch, above the library's fixed %zu "
+                "(use attn_qat_fwd with a workspace)", need, (size_t)AQ_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  hipError_t e = aq::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "attn_qat_fwd_noalloc scratch address");
+  return run_fwd("attn_qat_fwd_noalloc launch", q, k, v, o, batch, num_heads, lq, lk, sq, sk, sv, so,
+                 softmax_scale, causal, quant_flags, lse_log2, chunk_max_log2, o_hp, ws, stream);
 }
 
 int attn_qat_bwd(const void *q, const void *k, const void *v, const float *o_hp, const void *d_o,

@@ -157,6 +157,9 @@ hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream);
 // [B*H, lq/128, nsel] or null for dense attention.
 hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t nsel, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
+// The current device's address of the library's fixed forward scratch (AQ_NOALLOC_SCRATCH_BYTES,
+// looked up once per device; noalloc.hip).
+hipError_t noalloc_scratch(void **out);
 hipError_t launch_attn_bwd(const AttnArgs &a, const BwdArgs &b, hipStream_t stream);
 hipError_t launch_vsa_fwd(const AttnArgs &a, const VsaArgs &s, hipStream_t stream);
 // Straight-through backward of the cube-sparse fine stage; sel [B*H, n, topk] is the forward's

@@ -192,6 +192,40 @@ def attn_qat_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
     return o
 
 
+def attn_qat_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                         sm_scale: Optional[float] = None, quant_flags: int = AQ_QUANT_ALL,
+                         training: bool = False, out: Optional[torch.Tensor] = None, aux: Optional[dict] = None):
+    """attn_qat_fwd through attn_qat_fwd_noalloc: the library uses its fixed device scratch instead
+    of a workspace, so a call with ``out`` (and, with ``training``, ``aux``) given allocates
+    nothing.  Returns what attn_qat_fwd returns."""
+    B, Lq, Lk, H, Hkv, D = _check_qkv(q, k, v)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty(B, Lq, H, D, dtype=torch.bfloat16, device=q.device)
+    _require_bf16_cuda("out", o)
+    if tuple(o.shape) != (B, Lq, H, D):
+        raise ValueError(f"out must be [B, Lq, H, D] = {(B, Lq, H, D)}")
+    lse = cmax = ohp = None
+    if training:
+        C = (Lk + CHUNK - 1) // CHUNK
+        if aux is None:
+            lse = torch.empty(B, H, Lq, dtype=torch.float32, device=q.device)
+            cmax = _chunk_stats(quant_flags, (B, H, C, Lq), q.device)
+            ohp = torch.empty(B, H, Lq, D, dtype=torch.float32, device=q.device)
+            aux = _aux_dict(quant_flags, lse, cmax, ohp)
+        _check_aux(aux, B, H, Lq, C, D, quant_flags)
+        lse, cmax, ohp = aux["lse_log2"], aux["chunk_max_log2"], aux["o_hp"]
+    p = lambda t: None if t is None else t.data_ptr()
+    check(load().attn_qat_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, Hkv, D, Lq,
+                                      Lk, _strides_blhd(q), _strides_blhd(k), _strides_blhd(v), _strides_blhd(o),
+                                      float(sm_scale), int(bool(causal)), int(quant_flags), p(lse), p(cmax),
+                                      p(ohp), _stream_ptr(q)),
+          "attn_qat_fwd_noalloc")
+    if training:
+        return o, aux
+    return o
+
+
 def attn_qat_bwd(q, k, v, aux, d_o, causal: bool = False, sm_scale: Optional[float] = None,
                  quant_flags: int = AQ_QUANT_ALL):
     """Straight-through backward.  ``aux`` is the dict returned by
@@ -536,6 +570,6 @@ class QADLinear:
 
 __all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "AQ_FINAL_MAX", "AQ_GSF_QKV",
            "AQ_GSF_P", "AQ_SMOOTH_K", "AQ_SMOOTH_Q", "AQ_TWO_LEVEL_P", "AQ_FLAGS_ALL", "fq_nvfp4",
-           "static_global_scale", "attn_qat_fwd", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
+           "static_global_scale", "attn_qat_fwd", "attn_qat_fwd_noalloc", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
            "vsa_qat_fwd", "vsa_qat_bwd", "vsa_qat_train", "vsa_topk", "qad_linear_fwd", "qad_linear_bwd",
            "qad_linear", "qad_observe_amax", "input_global_sf", "QADLinear"]
