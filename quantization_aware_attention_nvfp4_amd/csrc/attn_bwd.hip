@@ -261,6 +261,217 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// dQ, software-pipelined form (every call but smooth-Q): workgroup = (head, 128 queries), 4 waves,
+// two workgroups per CU.  Wave w holds Q-hat and dO of queries 32w .. +31 in registers and walks
+// every 32-key sub-tile of the head's key sequence (chunk list) itself.  Iteration s does the
+// vector work of sub-tile s (A = exp2(y - lse2), dS = A (dP - D), packed to bf16) interleaved with
+// the MFMAs of dQ^T += K-hat^T dS^T for sub-tile s-1 and of S^T, dP^T for sub-tile s+1, none of
+// which depends on it: per sub-tile a wave issues 24 MFMAs and about 72 vector instructions, few
+// enough for its own MFMAs to hide them.  The workgroup barrier of each iteration only publishes
+// the copies.
+//
+// LDS: five slots of 16 KiB, each one sub-tile's K-hat rows [32][256 B] then V-hat rows [32][256 B]
+// (sw_kd swizzle).  Sub-tile s is read in iterations s-1 (S^T, dP^T) and s+1 (K-hat^T for dQ^T);
+// sub-tile s+3 is copied into the slot of s-2 at the start of iteration s and waited for at the
+// start of iteration s+2.
+// ---------------------------------------------------------------------------------------------
+constexpr int kDqsWaves = 4;
+constexpr int kDqsSlots = 5;
+constexpr int kDqsSlot = 16384;
+
+template <bool SPARSE>
+__global__ __launch_bounds__(kDqsWaves * 64, 2) void bwd_dq_sp_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kDqsSlots * kDqsSlot];
+  const uint32_t lds0 = lds_addr(lds);
+  const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nwork);
+  if (vid < 0) return;
+  const int64_t bh = vid / p.Cq;
+  const int64_t qc = vid % p.Cq;
+  const int64_t bb = bh / p.heads, hh = bh % p.heads;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, n = lane & 31, hf = lane >> 5;
+  const int qrow = (int)(qc * kChunk) + wave * 32 + n;
+  const bool qvalid = qrow < p.lq;
+
+  int64_t n_chunks = SPARSE ? p.nsel : p.Ck;
+  if (p.causal) {
+    const int64_t q_last = qc * kChunk + kChunk - 1;
+    n_chunks = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
+  }
+  const int nsteps = (int)(4 * n_chunks);
+  const int32_t *sel_row = SPARSE ? p.sel + (bh * p.Cq + qc) * p.nsel : nullptr;
+  // Head-local key of row 0 of sub-tile s (a uniform scalar).
+  auto step_key = [&](int s) -> int64_t {
+    const int64_t ch = SPARSE ? clamp_chunk(sel_row[s >> 2], p.Ck) : (int64_t)(s >> 2);
+    return ch * kChunk + 32 * (s & 3);
+  };
+  const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.Ck * kChunk * (kD / 8));
+  const uint8_t *vbase = (const uint8_t *)(p.vq + bh * p.Ck * kChunk * (kD / 8));
+  // Copies of one sub-tile by the four waves: wave w copies rows 16i + 4w + lane/16 (i = 0, 1) of
+  // K-hat and of V-hat, physical column lane%16.
+  uint32_t c_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (i * 4 + wave) * 4 + (lane >> 4);
+    c_off[i] = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kd(r)) << 4));
+  }
+  auto slot_of = [&](int s) -> uint32_t { return lds0 + (uint32_t)(s % kDqsSlots) * kDqsSlot; };
+  auto copy_step = [&](int s) {
+    const int64_t row0 = step_key(s);
+    const uint32_t dst = slot_of(s) + (uint32_t)wave * 1024;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      load_lds16_sa(kbase + row0 * 256, c_off[i], dst + i * 4096);
+      load_lds16_sa(vbase + row0 * 256, c_off[i], dst + 8192 + i * 4096);
+    }
+  };
+
+  for (int s = 0; s < 3 && s < nsteps; ++s) copy_step(s);
+  bf16x8 qf[8], of[8];
+  {
+    const u32x4 *qsrc = p.qq + (bh * p.Cq * kChunk + qc * kChunk + wave * 32 + n) * (kD / 8);
+    const uint16_t *osrc = p.d_o + bb * p.sdo.b + hh * p.sdo.h + (int64_t)(qvalid ? qrow : 0) * p.sdo.l;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      qf[t] = as_bf16x8(qsrc[2 * t + hf]);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qvalid) v = *(const u32x4 *)(osrc + 16 * t + 8 * hf);
+      of[t] = as_bf16x8(v);
+    }
+  }
+  const float lse2 = qvalid ? p.lse[bh * p.lq + qrow] : 0.0f;
+  const float Di = qvalid ? p.dvec[bh * p.lq + qrow] : 0.0f;
+  const int last = !qvalid ? -1 : (p.causal && qrow < p.lk - 1 ? qrow : (int)p.lk - 1);
+
+  // Lane offsets inside a slot (slots are 16 KiB aligned, so the XOR terms, bits 4..7, act on the
+  // offsets alone): the S^T / dP^T A operand at column pair t is `a_off ^ 32t`; the transposed
+  // reads of K-hat^T for dQ^T d tile dt are `t_off ^ 64dt` and `(t_off ^ (64dt | 16)) + 1024`.
+  uint32_t a_off, t_off;
+  {
+    const int r = perm_row(n), sw = sw_kd(r);
+    a_off = (uint32_t)(r * 256 + 16 * ((hf ^ sw) & 1) + 32 * (sw >> 1));
+    const int e = (lane >> 2) & 3, j = lane & 3, g2 = (lane >> 4) & 1;
+    const int lo = (2 * g2 + (j >> 1)) ^ (2 * hf);
+    t_off = (uint32_t)((16 * hf + e) * 256 + 64 * e + 16 * lo + 8 * (j & 1));
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+  // S^T and dP^T of sub-tile s.
+  auto logits = [&](int s, f32x16 &sv, f32x16 &dpv) {
+    const uint32_t a = slot_of(s) + a_off;
+    sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(a)), qf[0], f32x16{}, 0, 0, 0);
+    dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(a + 8192)), of[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int t = 1; t < 8; ++t) {
+      const uint32_t at = a ^ (32u * t);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at)), qf[t], sv, 0, 0, 0);
+      dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(at + 8192)), of[t], dpv, 0, 0, 0);
+    }
+  };
+  // dQ^T += K-hat^T dS^T of sub-tile s (dS in d0 / d1).
+  auto dq_products = [&](int s, const bf16x8 &d0, const bf16x8 &d1) {
+    const uint32_t b = slot_of(s) + t_off;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint32_t b0 = b ^ (uint32_t)(dt << 6), b1 = (b ^ (uint32_t)((dt << 6) | 16)) + 1024;
+      const uint2 x0 = ds_read_tr16_at(b0), x1 = ds_read_tr16_at(b1);
+      const uint2 y0 = ds_read_tr16_at(b0 + 2048), y1 = ds_read_tr16_at(b1 + 2048);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{x0.x, x0.y, x1.x, x1.y}), d0, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{y0.x, y0.y, y1.x, y1.y}), d1, acc[dt], 0, 0, 0);
+    }
+  };
+  // Keys past lk, causal keys past the query, and query rows past lq (every key) are masked.
+  auto mask_step = [&](int s, f32x16 &sv) {
+    const int64_t k0 = step_key(s);
+    const bool tail = k0 + 32 > p.lk;
+    const bool diag = p.causal && k0 + 31 > qc * kChunk + wave * 32;
+    if (tail || diag || !qvalid) mask_tail(sv, valid_prefix(k0 + 16 * hf, (int64_t)last));
+  };
+  // dS of one sub-tile, packed to bf16.
+  auto dscores = [&](const f32x16 &sv, const f32x16 &dpv, bf16x8 &d0, bf16x8 &d1) {
+    float ds[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const float A = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rr], p.c, -lse2));
+      ds[rr] = A * (dpv[rr] - Di);
+    }
+    d0 = pack8_cvt(ds);
+    d1 = pack8_cvt(ds + 8);
+  };
+
+  // Iteration 0 runs the dQ products of "sub-tile -1" with dS = 0 from the slot sub-tile 4 will use:
+  // zero it, or bits left in LDS by an earlier kernel (a NaN or Inf pattern) would turn 0 * x into
+  // NaN.  Sub-tile 4's copy is issued in iteration 1, after that read.
+  {
+    u32x4 *z = (u32x4 *)(lds + (kDqsSlots - 1) * kDqsSlot) + tid;
+#pragma unroll
+    for (int i = 0; i < kDqsSlot / (16 * kDqsWaves * 64); ++i) z[i * kDqsWaves * 64] = u32x4{0u, 0u, 0u, 0u};
+  }
+  AQ_WAIT_VMCNT(0);
+  __syncthreads();
+  f32x16 sA, dpA, sB, dpB;
+  bf16x8 dA0 = {}, dA1 = {}, dB0, dB1;  // dS of sub-tile -1 is zero: its products add nothing
+  logits(0, sA, dpA);
+  // One iteration: wait for sub-tile s+1, refill, then the interleaved work of sub-tile s.
+  // (cur: S/dP of sub-tile s in, S/dP of s+1 out; dprev: dS of s-1 in, dnext: dS of s out.)
+  auto iteration = [&](int s, f32x16 &s_cur, f32x16 &dp_cur, f32x16 &s_nxt, f32x16 &dp_nxt, const bf16x8 &dp0,
+                       const bf16x8 &dp1, bf16x8 &dn0, bf16x8 &dn1) {
+    if (s >= 1 && s + 2 < nsteps) AQ_WAIT_VMCNT(4);
+    else AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    if (s + 3 < nsteps) copy_step(s + 3);
+    mask_step(s, s_cur);
+    AQ_OPAQUE(s_cur);
+    // MFMAs: dQ of s-1 (8, two transposed reads each), S/dP of s+1 (16, one read each); between
+    // them the vector work of s, about three instructions per MFMA.
+    dq_products(s - 1 + kDqsSlots, dp0, dp1);
+    logits(s + 1, s_nxt, dp_nxt);
+    dscores(s_cur, dp_cur, dn0, dn1);
+    // per MFMA: its operand reads a few MFMAs ahead, then one exponential (the first 16) and two
+    // other vector instructions
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int g = 0; g < 24; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (g < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (g < 19) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (g < 16) __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    AQ_OPAQUE(dn0);
+    AQ_OPAQUE(dn1);
+  };
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    iteration(s, sA, dpA, sB, dpB, dA0, dA1, dB0, dB1);
+    iteration(s + 1, sB, dpB, sA, dpA, dB0, dB1, dA0, dA1);
+  }
+  if (s < nsteps) {
+    iteration(s, sA, dpA, sB, dpB, dA0, dA1, dB0, dB1);
+    dq_products(s, dB0, dB1);
+  } else if (nsteps > 0) {
+    dq_products(s - 1, dA0, dA1);
+  }
+
+  if (!qvalid) return;
+  uint16_t *op = p.dq + bb * p.sdq.b + hh * p.sdq.h + (int64_t)qrow * p.sdq.l;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0i = 32 * dt + 8 * a + 4 * hf;
+      *(bf16x4 *)(op + d0i) = bf16x4{(__bf16)(acc[dt][4 * a] * p.scale), (__bf16)(acc[dt][4 * a + 1] * p.scale),
+                                     (__bf16)(acc[dt][4 * a + 2] * p.scale), (__bf16)(acc[dt][4 * a + 3] * p.scale)};
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // dK, dV: workgroup = (head, 128-key chunk), 8 waves, loop over 64-query tiles.  Wave w owns keys
 // 32*(w%4) .. +31 of the chunk and queries 32*(w/4) .. +31 of every tile; the two waves that share
 // keys add their partial dK/dV through LDS at the end.  Two waves per SIMD, so one wave's
@@ -698,9 +909,9 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   p.per_xcd = (p.nwork + 7) / 8;
   const dim3 dq_grid((unsigned)(p.per_xcd * 8));
   if (sel && p.delta) AQ_LAUNCH("vsa_bwd_dq", (bwd_dq_kernel<true, true>), dq_grid, dim3(kDqThreads), 0, stream, p);
-  else if (sel) AQ_LAUNCH("vsa_bwd_dq", (bwd_dq_kernel<true, false>), dq_grid, dim3(kDqThreads), 0, stream, p);
+  else if (sel) AQ_LAUNCH("vsa_bwd_dq", (bwd_dq_sp_kernel<true>), dq_grid, dim3(kDqsWaves * 64), 0, stream, p);
   else if (p.delta) AQ_LAUNCH("bwd_dq", (bwd_dq_kernel<false, true>), dq_grid, dim3(kDqThreads), 0, stream, p);
-  else AQ_LAUNCH("bwd_dq", (bwd_dq_kernel<false, false>), dq_grid, dim3(kDqThreads), 0, stream, p);
+  else AQ_LAUNCH("bwd_dq", (bwd_dq_sp_kernel<false>), dq_grid, dim3(kDqsWaves * 64), 0, stream, p);
   if ((e = hipGetLastError())) return e;
 
   p.nwork = bh * p.Ck;
