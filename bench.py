@@ -178,6 +178,51 @@ def pmc_probe():
     print("pmc probe done: copy bytes", 2 * src.numel(), flush=True)
 
 
+def profile_step(steps: int):
+    """The benchmark step's launches only (448x896x61: fq, training forward, backward, cube-sparse
+    training forward and backward), `steps` times after one warm-up, then the dense inference
+    forward three times and one QAD linear forward + backward (1536 -> 8960, 25088 tokens),
+    preceded by a plain 1 GiB device copy whose FETCH_SIZE / WRITE_SIZE readings calibrate the
+    traffic counters.  For rocprofv3 kernel-trace and counter runs: every
+    attention launch it makes is one of the timed workload's."""
+    import torch
+
+    import quantization_aware_attention_nvfp4_amd as m
+    import synth
+    dev = torch.device("cuda", 0)
+    x = synth.fq_tensor().to(dev)
+    y = torch.empty_like(x)
+    q, k, v = (t.to(dev) for t in synth.wan_448x896x61())
+    do = synth.normal_bf16((B, L, H, D), 2003).to(dev)
+    qv, kv, vv = (t.to(dev) for t in synth.vsa_inputs())
+    dov = synth.normal_bf16((B, L, H, D), 2005).to(dev)
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    vsa_args = dict(grid=GRID, cube=CUBE, sparsity=SPARSITY)
+    for i in range(steps + 1):
+        m.fq_nvfp4(x, out=y)
+        o, aux = m.attn_qat_fwd(q, k, v, training=True)
+        m.attn_qat_bwd(q, k, v, aux, do)
+        ov, auxv = m.vsa_qat_fwd(qv, kv, vv, training=True, **vsa_args)
+        m.vsa_qat_bwd(qv, kv, vv, auxv, dov, **vsa_args)
+        torch.cuda.synchronize()
+        print(f"profile step {i} done", flush=True)
+    for _ in range(3):
+        m.attn_qat_fwd(q, k, v)
+    torch.cuda.synchronize()
+    print("profile step: inference forward done", flush=True)
+    # one QAD linear forward + backward on the 1536 -> 8960 feed-forward projection (25088 tokens)
+    xl, wl, bl, gl = (t.to(dev) for t in synth.wan_ffn(1536, 8960))
+    m.qad_linear_fwd(xl, wl, bl)
+    m.qad_linear_bwd(gl, xl, wl)
+    torch.cuda.synchronize()
+    print("profile step: done", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +231,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true", help="one untimed pass of each stage plus a 1 GiB copy")
+    ap.add_argument("--profile-step", action="store_true",
+                    help="only the step's launches (--steps of them after one warm-up) and the inference forward, "
+                         "for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the library and this benchmark run on one GPU only (asked for --gpus {args.gpus}); sharding the "
@@ -194,6 +242,9 @@ def main():
 
     if args.pmc_probe:
         pmc_probe()
+        return
+    if args.profile_step:
+        profile_step(args.steps)
         return
 
     import torch
