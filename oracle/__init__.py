@@ -37,8 +37,10 @@ QUANT_Q, QUANT_K, QUANT_V, QUANT_P = 1, 2, 4, 8
 QUANT_ALL = 15
 # Variants (readings in nvfp4_oracle.c): statistics relative to the final row
 # maximum, static per-tensor global scales for Q/K/V, the static global scale
-# of P, smooth-K, the two-level (per-row, per-chunk) scale of P, and smooth-Q.
+# of P, smooth-K, the two-level (per-row, per-chunk) scale of P, smooth-Q.
 FINAL_MAX, GSF_QKV, GSF_P, SMOOTH_K, TWO_LEVEL_P, SMOOTH_Q = 16, 32, 64, 128, 256, 512
+# FP8 P.V product: both operands of P.V rounded to FP8 E4M3FN (reading in nvfp4_oracle.c).
+PV_FP8 = 1024
 
 
 def build(force: bool = False) -> str:

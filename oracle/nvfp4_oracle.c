@@ -226,7 +226,21 @@ enum { QF_Q = 1, QF_K = 2, QF_V = 4, QF_P = 8 };
    reference-order statistics of the "Attn-QAT Training" guide); their
    arithmetic is the reading given with each use below. */
 enum { QF_FINAL_MAX = 16, QF_GSF_QKV = 32, QF_GSF_P = 64, QF_SMOOTH_K = 128, QF_TWO_LEVEL_P = 256,
-       QF_SMOOTH_Q = 512 };
+       QF_SMOOTH_Q = 512, QF_PV_FP8 = 1024 };
+
+/* FP8 P.V product ([META] precision records, flag pv_fp8; named there, not
+   defined).  Reading: both operands of the P.V product, as the BF16 path forms
+   them (P-hat, or P rounded to bf16 when P is not quantized; V-hat rounded to
+   bf16), are rounded to FP8 E4M3FN - nearest value with ties to the even
+   code, subnormals kept, saturating at 448, sign kept - and multiplied with
+   fp32 accumulation (a product of two E4M3 values is exact).  The
+   straight-through backward uses the same operands: dP against the rounded
+   V, dV from the rounded P-hat times exp(m_c - lse), and o_hp (unquantized P
+   times the rounded V) for D. */
+static void round_e4m3_vals(float *x, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) x[i] = copysignf(oracle_e4m3(fabsf(x[i])), x[i]);
+}
 
 /* Two-level quantization of P ([API] two_level_quant_p_sage3; the
    SageAttention3 recipe the flag is named after): a first, per-row level maps
@@ -388,6 +402,7 @@ static void make_head_ops(head_ops *h, const uint16_t *q, const uint16_t *k, con
     round_bf16(h->qh, Lq * D);
     round_bf16(h->kh, Lk * D);
     round_bf16(h->vh, Lk * D);
+    if (flags & QF_PV_FP8) round_e4m3_vals(h->vh, Lk * D);
     if (h->qbar) {
         h->delta = (double *)malloc(sizeof(double) * Lk);
         for (int64_t j = 0; j < Lk; ++j) {
@@ -468,6 +483,10 @@ static void row_forward(const head_ops *h, int64_t i, const int64_t *keys, int64
         if (flags & QF_P) {
             for (int t0 = 0; t0 < chunk; t0 += 16) fq_block_f32(Pq + t0, chunk - t0 < 16 ? chunk - t0 : 16, gp);
             round_bf16(Pq, chunk); /* the P-hat V-hat matmul operand */
+        }
+        if (flags & QF_PV_FP8) {
+            round_bf16(Pq, chunk); /* the BF16 path's operand (no change when P is quantized) */
+            round_e4m3_vals(Pq, chunk);
         }
         double alpha = (m == -INFINITY) ? 0.0 : exp((double)m - (double)m_new);
         double psum = 0.0;
@@ -602,6 +621,10 @@ static void block_weights_mc(const bwd_head *x, int64_t i, int64_t b0, int nb, d
     if (x->flags & QF_P) {
         fq_block_f32(P, nb, g);
         round_bf16(P, nb);
+    }
+    if (x->flags & QF_PV_FP8) {
+        round_bf16(P, nb);
+        round_e4m3_vals(P, nb);
     }
     for (int t = 0; t < nb; ++t) {
         int live = !(x->causal && b0 + t > i);

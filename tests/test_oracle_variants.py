@@ -19,7 +19,13 @@ variant to something other than the oracle's own variant code:
     smoothed keys, which matches attention on the original keys up to the
     keys' bf16 rounding (the softmax ignores a per-row shift); with
     quantization it equals attention on keys smoothed and quantized by the
-    pinned fp32 codec.
+    pinned fp32 codec;
+  * FP8 P.V product: with every logit of a row equal, P-hat = 1.03125 rounds
+    to 1.0 and the output is the key mean of the E4M3-rounded V-hat (torch's
+    float8_e4m3fn cast); operands already exact in E4M3 leave the BF16
+    path's output unchanged bit for bit; random inputs match the unrolled
+    closed form with both operands rounded by that cast; dQ/dK equal float64
+    autograd on (Q-hat, K-hat, E4M3(V-hat)) and dV pairs with the output.
 """
 import math
 
@@ -56,11 +62,12 @@ def sdpa64(q, k, v, scale, causal=False):
     return torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale, is_causal=causal)
 
 
-def closed_form(S, vh, gp=1.0, chunk=None):
+def closed_form(S, vh, gp=1.0, chunk=None, pq_map=None):
     """Per row: the unrolled online recurrence over `chunk`-key chunks (one
     chunk = the whole row when None), fp32 probabilities relative to each
     chunk's running max (libm exp), P-hat from the pinned codec under global
-    scale gp rounded to bf16, the denominator summing unquantized P."""
+    scale gp rounded to bf16 (then passed through pq_map when given), the
+    denominator summing unquantized P."""
     Lq, Lk = S.shape
     chunk = chunk or (Lk + 15) // 16 * 16
     C = (Lk + chunk - 1) // chunk
@@ -74,6 +81,8 @@ def closed_form(S, vh, gp=1.0, chunk=None):
             Pp = np.zeros((len(P) + 15) // 16 * 16, np.float32)
             Pp[: len(P)] = P
             Pq = f32(bits_of(oracle.fq_f32_rows(Pp[None], g=gp)[0][: len(P)]))
+            if pq_map is not None:
+                Pq = pq_map(Pq)
             w = math.exp(float(mc[c]) - float(mc[-1]))
             lsum += w * P.astype(np.float64).sum()
             acc += w * (Pq.astype(np.float64) @ vh[chunk * c: chunk * c + len(P)])
@@ -426,3 +435,83 @@ def test_smooth_q_with_static_scale_and_smooth_k_and_sparse():
     db = oracle.attn_bwd(q, k, v, do, SCALE, flags=fl2, krows=np.arange(0, L, 29))
     for name in ("dq", "dk", "dv"):
         assert np.allclose(sb[name], db[name], rtol=0, atol=1e-12), name
+
+
+# ---------------------------------------------------------------- FP8 P.V product
+
+PVF8 = oracle.PV_FP8
+
+
+def fp8(x):
+    """Nearest FP8 E4M3FN value (torch's float8_e4m3fn cast: ties to even, subnormals kept; the
+    values here stay far below its 448 limit), as float64."""
+    return torch.as_tensor(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_pv_fp8_constant_logits_closed_form():
+    # every key equal: every logit of a row is equal, so P = 1 everywhere, P-hat = 6 * E4M3(1/6) =
+    # 1.03125 (l = Lk), and E4M3 rounds it to 1.0: O_i = mean_j E4M3(V-hat_j).  The last chunk is
+    # partial (200 keys) and its last block has 8 keys.
+    Lq, Lk = 8, 200
+    q = rand_bits((1, 1, Lq, D), 401)
+    k = np.repeat(rand_bits((1, 1, 1, D), 402), Lk, axis=2)
+    v = rand_bits((1, 1, Lk, D), 403, 3.0)
+    assert fp8(1.03125) == 1.0
+    vh = f32(oracle.fq_bf16(v, 2))[0, 0]
+    r = oracle.attn_fwd(q, k, v, SCALE, flags=ALL | PVF8)
+    assert np.allclose(r["o"][0, 0], np.broadcast_to(fp8(vh).mean(0), (Lq, D)), rtol=1e-12, atol=1e-14)
+    d = oracle.attn_fwd(q, k, v, SCALE, flags=ALL)
+    assert np.allclose(d["o"][0, 0], np.broadcast_to(1.03125 * vh.astype(np.float64).mean(0), (Lq, D)),
+                       rtol=1e-12, atol=1e-14)
+
+
+def test_pv_fp8_exact_operands_leave_the_bf16_path_unchanged():
+    # P unquantized and every logit equal: P = 1 (exact in E4M3); V in 16-key blocks whose abs-max is 6
+    # has the unit E4M3 block scale, so V-hat is an E2M1 value (exact in E4M3).  Both readings then
+    # multiply the same operands: identical outputs, bit for bit.
+    Lq, Lk = 6, 160
+    q = rand_bits((1, 1, Lq, D), 404)
+    k = np.repeat(rand_bits((1, 1, 1, D), 405), Lk, axis=2)
+    g = torch.Generator().manual_seed(406)
+    vv = torch.rand(1, 1, Lk, D, generator=g) * 12 - 6
+    vv[:, :, ::16, :] = 6.0  # one entry of 6 in every block along the keys
+    v = vv.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    vh = f32(oracle.fq_bf16(v, 2))[0, 0]
+    assert np.array_equal(fp8(vh), vh.astype(np.float64))
+    fl = oracle.QUANT_Q | oracle.QUANT_K | oracle.QUANT_V
+    a = oracle.attn_fwd(q, k, v, SCALE, flags=fl | PVF8)
+    b = oracle.attn_fwd(q, k, v, SCALE, flags=fl)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["o_hp"], b["o_hp"])
+
+
+def test_pv_fp8_random_inputs_match_the_unrolled_closed_form():
+    Lq, Lk = 12, 300
+    q, k, v = rand_bits((1, 1, Lq, D), 407), rand_bits((1, 1, Lk, D), 408, 2.0), rand_bits((1, 1, Lk, D), 409)
+    r = oracle.attn_fwd(q, k, v, SCALE, flags=ALL | PVF8)
+    qh, kh, vh = quantized_ops(q, k, v)
+    S = (SCALE * (qh @ kh.T)).astype(np.float32)
+    want = closed_form(S, fp8(vh), chunk=128, pq_map=fp8)
+    assert np.allclose(r["o"][0, 0], want, rtol=1e-9, atol=1e-12)
+    # and the rounding changes the result (the flag reaches the arithmetic)
+    assert not np.allclose(r["o"], oracle.attn_fwd(q, k, v, SCALE, flags=ALL)["o"], rtol=0, atol=1e-6)
+
+
+def test_pv_fp8_backward():
+    Lq, Lk = 50, 200
+    q, do = rand_bits((1, 2, Lq, D), 410), rand_bits((1, 2, Lq, D), 413)
+    k, v = rand_bits((1, 2, Lk, D), 411, 1.5), rand_bits((1, 2, Lk, D), 412)
+    fl = ALL | PVF8
+    b = oracle.attn_bwd(q, k, v, do, SCALE, flags=fl)
+    # dS uses the unquantized probabilities and dP the rounded V-hat: dQ, dK are plain attention's
+    # gradients on (Q-hat, K-hat, E4M3(V-hat))
+    Q = f64(oracle.fq_bf16(q, -1)).requires_grad_()
+    K = f64(oracle.fq_bf16(k, -1)).requires_grad_()
+    V8 = torch.from_numpy(fp8(f32(oracle.fq_bf16(v, 2))))
+    sdpa64(Q, K, V8, SCALE).backward(f64(do))
+    assert np.allclose(b["dq"], Q.grad.numpy(), rtol=0, atol=5e-6)
+    assert np.allclose(b["dk"], K.grad.numpy(), rtol=0, atol=5e-6)
+    # dV = A-hat^T dO with the forward's rounded P-hat: <dO, O> = sum_j <dV_j, E4M3(V-hat)_j>
+    o = oracle.attn_fwd(q, k, v, SCALE, flags=fl)["o"]
+    lhs = np.einsum("bhid,bhid->bh", f64(do).numpy(), o)
+    rhs = np.einsum("bhjd,bhjd->bh", b["dv"], V8.numpy())
+    assert np.allclose(lhs, rhs, rtol=1e-10, atol=1e-10)
