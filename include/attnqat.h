@@ -87,8 +87,18 @@ enum {
                    logits, delta_j = <mean, k-hat_j> (fp32), is added back to every logit of key j.
                    The backward's key gradients see the restored query q-hat + mean; dQ is
                    unchanged.  Under AQ_GSF_QKV the static Q scale is taken on the smoothed Q.
-   Under AQ_GSF_QKV, AQ_GSF_P or AQ_TWO_LEVEL_P the P-hat V-hat product runs in bf16 (the values are
-   no longer exact in fp16). */
+     AQ_PV_FP8     the FP8 P.V product ([META]'s precision records carry pv_fp8, undefined there):
+                   both operands of the P-hat V-hat product, as the bf16 path forms them, rounded
+                   to the nearest FP8 E4M3FN value (ties to even, subnormals kept, saturating at
+                   448, sign kept), then multiplied with fp32 accumulation; P's blocks are
+                   quantized under a global scale of 1 (448*6 with AQ_GSF_P, the two-level scale
+                   with AQ_TWO_LEVEL_P), which is the plain block scale.  The backward uses the
+                   same operands: dP against the rounded V-hat, dV from the rounded P-hat, O^hp
+                   from the rounded V-hat.  Requires AQ_QUANT_P (else AQ_ENOTSUP).  The forward
+                   multiplies these operands on the fp16 MFMA (every E4M3FN value is exact in fp16,
+                   so the products are the FP8 ones), which also carries O^hp's unquantized P.
+   Otherwise, under AQ_GSF_QKV, AQ_GSF_P or AQ_TWO_LEVEL_P the P-hat V-hat product runs in bf16 (the
+   values are no longer exact in fp16). */
 enum {
     AQ_FINAL_MAX = 16,
     AQ_GSF_QKV = 32,
@@ -96,7 +106,8 @@ enum {
     AQ_SMOOTH_K = 128,
     AQ_TWO_LEVEL_P = 256,
     AQ_SMOOTH_Q = 512,
-    AQ_FLAGS_ALL = 1023
+    AQ_PV_FP8 = 1024,
+    AQ_FLAGS_ALL = 2047
 };
 
 /* Element strides of a 4-D attention tensor, indexed (batch, head, token, d) with d contiguous. */
@@ -138,7 +149,7 @@ int fq_nvfp4_static_scale(const void *x, int64_t n, float *g_out, void *stream);
  * Every bf16 tensor of the attention entry points starts 16-byte aligned and has strides that
  * are multiples of 8 elements and below 2^24 (rows move in 16-byte pieces); lq, lk <= 2^30.
  * Q-hat, K-hat along D and V-hat along keys are fake-quantized per quant_flags (quantizers and
- * the AQ_FINAL_MAX / AQ_GSF_QKV / AQ_GSF_P / AQ_SMOOTH_K / AQ_TWO_LEVEL_P / AQ_SMOOTH_Q variants above).  The keys are
+ * the AQ_FINAL_MAX / AQ_GSF_QKV / AQ_GSF_P / AQ_SMOOTH_K / AQ_TWO_LEVEL_P / AQ_SMOOTH_Q / AQ_PV_FP8 variants above).  The keys are
  * visited in chunks of 128 ([0,128), [128,256), ...); in chunk c the running row maximum m_c of
  * the logits softmax_scale * <q-hat, k-hat> is refreshed first, then P = exp(logit - m_c) is
  * formed, fake-quantized in 16-key blocks (AQ_QUANT_P) and multiplied with V-hat on BF16 MFMA;

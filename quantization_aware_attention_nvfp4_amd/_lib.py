@@ -17,9 +17,9 @@ AQ_OK, AQ_EINVAL, AQ_ENOTSUP, AQ_EHIP = 0, -1, -2, -3
 AQ_QUANT_Q, AQ_QUANT_K, AQ_QUANT_V, AQ_QUANT_P = 1, 2, 4, 8
 AQ_QUANT_ALL = 15
 # Variants (include/attnqat.h): final-max statistics, static Q/K/V and P global scales, smooth-K,
-# two-level P, smooth-Q.
-AQ_FINAL_MAX, AQ_GSF_QKV, AQ_GSF_P, AQ_SMOOTH_K, AQ_TWO_LEVEL_P, AQ_SMOOTH_Q = 16, 32, 64, 128, 256, 512
-AQ_FLAGS_ALL = 1023
+# two-level P, smooth-Q, the FP8 P.V product.
+AQ_FINAL_MAX, AQ_GSF_QKV, AQ_GSF_P, AQ_SMOOTH_K, AQ_TWO_LEVEL_P, AQ_SMOOTH_Q, AQ_PV_FP8 = 16, 32, 64, 128, 256, 512, 1024
+AQ_FLAGS_ALL = 2047
 
 EXPORTED = ("aq_last_error", "fq_nvfp4", "fq_nvfp4_static_scale", "attn_qat_fwd", "attn_qat_bwd",
             "vsa_qat_fwd", "vsa_qat_bwd", "vsa_topk", "attn_qat_workspace_size", "aq_kernel_timing",

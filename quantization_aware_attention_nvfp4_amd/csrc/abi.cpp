@@ -62,6 +62,8 @@ int check_attention(int batch, int num_heads, int num_kv_heads, int head_size, i
   if ((quant_flags & AQ_TWO_LEVEL_P) && (quant_flags & (AQ_FINAL_MAX | AQ_GSF_P)))
     return fail(AQ_ENOTSUP, "AQ_TWO_LEVEL_P does not combine with AQ_FINAL_MAX or AQ_GSF_P (flags 0x%x)",
                 quant_flags);
+  if ((quant_flags & AQ_PV_FP8) && !(quant_flags & AQ_QUANT_P))
+    return fail(AQ_ENOTSUP, "AQ_PV_FP8 needs AQ_QUANT_P (flags 0x%x)", quant_flags);
   if (num_kv_heads != num_heads)
     return fail(AQ_ENOTSUP, "num_kv_heads (%d) must equal num_heads (%d)", num_kv_heads, num_heads);
   if (causal && lq != lk)

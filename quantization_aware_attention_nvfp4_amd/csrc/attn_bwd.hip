@@ -76,6 +76,10 @@ struct BwdParams {
   // Smooth-Q: delta [BH, Ck*128] added to every logit, and the queries' mean [BH, 128], which the
   // key gradients see added back to Q-hat; null otherwise.
   const float *delta, *qmean;
+  // GP kernels: P's global scale when it is not the two-level one (448*6, or 1), and whether P-hat is
+  // rounded to FP8 E4M3FN (the FP8 P.V product), as the forward did.
+  float gp_static;
+  bool pv_fp8;
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -593,7 +597,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
   const float w = __builtin_amdgcn_exp2f(mc - lse2);
   float ah[16], ds[16];
   if (p.quant_p) {
-    const float g = (GP && p.pg) ? lds_read_f32(sta + 768) : kPScaleStatic;
+    const float g = (GP && p.pg) ? lds_read_f32(sta + 768) : p.gp_static;
     const ProbBlock pb = GP ? prob_block_static(bm, p.c, mc, g) : prob_block(bm, p.c, mc);
     const float sw = pb.Sd * w, swD = sw * Di;  // A = r * Sd * w
 #pragma unroll
@@ -607,7 +611,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams &p, uint32_t lds0, Dkd
       e2m1_decode8(c0, pb.S, ah);
       e2m1_decode8(c1, pb.S, ah + 8);
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) ah[rr] = bf16lo(f32_to_bf16_rne(ah[rr])) * w;
+      for (int rr = 0; rr < 16; ++rr) {
+        const float b = bf16lo(f32_to_bf16_rne(ah[rr]));
+        ah[rr] = (p.pv_fp8 ? round_e4m3(b) : b) * w;
+      }
     } else {
       e2m1_decode8(c0, pb.S * w, ah);
       e2m1_decode8(c1, pb.S * w, ah + 8);
@@ -864,7 +871,8 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   if ((e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, qd_k, ws + w.kq, nullptr, vp.gk, vp.kmean, stream)))
     return e;
   if ((e = launch_qk_delta(a, w, stream))) return e;
-  if ((e = launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qr_v, ws + w.vq, nullptr, vp.gv, nullptr, stream)))
+  if ((e = launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qr_v, ws + w.vq, nullptr, vp.gv, nullptr, stream,
+                               (a.flags & kFlagPvFp8) ? kFp8Bf16 : kFp8None)))
     return e;
 
   const int64_t bh = (int64_t)a.batch * a.heads;
@@ -917,7 +925,9 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   p.nwork = bh * p.Ck;
   p.per_xcd = (p.nwork + 7) / 8;
   const dim3 dkdv_grid((unsigned)(p.per_xcd * 8));
-  const bool gp = p.quant_p && (a.flags & (kFlagGsfP | kFlagTwoLevelP));
+  const bool gp = p.quant_p && (a.flags & kFlagsPGlobal);
+  p.gp_static = (a.flags & kFlagGsfP) ? kPScaleStatic : 1.0f;
+  p.pv_fp8 = (a.flags & kFlagPvFp8) != 0;
   if (p.delta) launch_dkdv<true>(p, sel != nullptr, gp, dkdv_grid, stream);
   else launch_dkdv<false>(p, sel != nullptr, gp, dkdv_grid, stream);
   return hipGetLastError();

@@ -65,6 +65,7 @@ struct FwdParams {
   float *pg;            // training, two-level: [BH, C, lq] those scales, or null
   const float *qmean;   // smooth-Q: [BH, 128] the queries' mean, subtracted before quantization
   const float *delta;   // smooth-Q: [BH, kchunks*128] <mean, k-hat_j>, added to every logit
+  float gp_static;      // GP kernels: P's global scale when it is not the two-level one (448*6, or 1)
 };
 
 // Copy offsets of this lane's 16-byte pieces of a staged [128][256 B] tile by a workgroup of
@@ -192,12 +193,12 @@ __device__ __forceinline__ void load_q_frags(const FwdParams &p, int64_t bb, int
 // P of one 32-key sub-tile, whose 16 logits in the lane's registers are one P block, as the two
 // P-hat V-hat B operands (keys 0-7 and 8-15 of the block); psum gains the block's unquantized sum.
 // HP: also the unquantized P as operands (ph), for O^hp.  GP: P's blocks under the global scale g
-// (the static 448*6, or the two-level scale of the row and chunk; then F16 is off: P-hat is
-// rounded to bf16).
+// (the static 448*6, the two-level scale of the row and chunk, or 1), P-hat rounded to bf16.  GP
+// with F16 is the FP8 P.V product: that bf16 P-hat is further rounded to the nearest E4M3FN value,
+// which fp16 holds exactly.
 template <bool QP, bool F16, bool HP, bool GP>
 __device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, float m_new, float g, float &psum,
                                        u32x4 (&pq)[2], u32x4 (&ph)[2]) {
-  static_assert(!(GP && F16), "P-hat under the static scale is not exact in fp16");
   if (QP) {
     const ProbBlock pb = GP ? prob_block_static(bmax, c, m_new, g) : prob_block(bmax, c, m_new);
     float r[16];
@@ -210,15 +211,23 @@ __device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, flo
     }
     psum = __builtin_fmaf(pb.Sd, rsum, psum);
     const uint32_t c0 = e2m1_codes8(r), c1 = e2m1_codes8(r + 8);
-    if (F16) {
+    if (F16 && !GP) {
       pq[0] = e2m1_decode8_f16(c0, pb.S);
       pq[1] = e2m1_decode8_f16(c1, pb.S);
     } else {
       float x[8];
-      e2m1_decode8(c0, pb.S, x);
-      pq[0] = __builtin_bit_cast(u32x4, pack8_cvt(x));
-      e2m1_decode8(c1, pb.S, x);
-      pq[1] = __builtin_bit_cast(u32x4, pack8_cvt(x));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        e2m1_decode8(j ? c1 : c0, pb.S, x);
+        if (F16) {  // FP8 P.V product (P-hat >= 0)
+          f16x8 h;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) h[i] = (_Float16)round_e4m3(bf16lo(f32_to_bf16_rne(x[i])));
+          pq[j] = __builtin_bit_cast(u32x4, h);
+        } else {
+          pq[j] = __builtin_bit_cast(u32x4, pack8_cvt(x));
+        }
+      }
     }
     if (HP) {
 #pragma unroll
@@ -414,7 +423,7 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
     const float m_new = fmaxf(m_run, cm * p.c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
     if (TRAIN && hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
-    const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : kPScaleStatic;
+    const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : p.gp_static;
     if (TRAIN && GP && p.pg && hf == 0 && qvalid) p.pg[(bh * p.nchunks + it) * p.lq + qrow] = g;
     m_run = m_new;
     // The rescale is skipped when no row of the wave moved its maximum (alpha == 1 exactly).
@@ -630,7 +639,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
     const float m_new = fmaxf(m_run, cm * p.c);
     alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // applied to acc by the next matrix phase
     m_run = m_new;
-    const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : kPScaleStatic;
+    const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : p.gp_static;
     float psum = 0.0f;
     u32x4 ph[2];
 #pragma unroll
@@ -839,10 +848,12 @@ __global__ __launch_bounds__(256, 2) void rowmax_kernel(FwdParams p) {
 }  // namespace
 
 // fp16 P-hat V-hat product: both operands fake-quantized under unit global scales (a static scale
-// makes the values inexact in fp16; they are rounded to bf16 instead).
-static bool use_f16(unsigned flags) {
-  return (flags & kFlagV) && (flags & kFlagP) && !(flags & (kFlagGsfQkv | kFlagGsfP | kFlagTwoLevelP));
+// makes the values inexact in fp16; they are rounded to bf16 instead), or both rounded to E4M3FN
+// (the FP8 P.V product, which requires a quantized P).
+static bool use_f16_unit(unsigned flags) {
+  return (flags & kFlagV) && (flags & kFlagP) && !(flags & (kFlagGsfQkv | kFlagsPGlobal));
 }
+static bool use_f16(unsigned flags) { return use_f16_unit(flags) || (flags & kFlagPvFp8); }
 
 // The forward kernel of a call, by its mode: training (QL layout for dense calls), ping-pong dense
 // inference, or the single-group kernel (cube-sparse or smooth-Q inference); qp / f16 / gp as in
@@ -850,7 +861,14 @@ static bool use_f16(unsigned flags) {
 template <bool GP, bool SQ>
 static void launch_fwd_kernel(const FwdParams &p, dim3 grid, dim3 block, bool train, bool ql, bool pipe, bool qp,
                               bool f16, const char *nm, const char *nm_train, hipStream_t stream) {
-  if (GP) {  // P quantized under the static scale: bf16 product
+  if (GP && f16) {  // the FP8 P.V product: E4M3FN operands, exact in fp16
+    if (ql) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, true, GP, SQ>), grid, block, 0, stream, p);
+    else if (train) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, true, false, GP, SQ>), grid, block, 0, stream, p);
+    else if (pipe && !SQ) AQ_LAUNCH(nm, (attn_fwd_pp_kernel<true, true, GP>), grid, block, 0, stream, p);
+    else AQ_LAUNCH(nm, (attn_fwd_kernel<false, true, true, false, GP, SQ>), grid, block, 0, stream, p);
+    return;
+  }
+  if (GP) {  // P quantized under a global scale: bf16 product
     if (ql) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, true, GP, SQ>), grid, block, 0, stream, p);
     else if (train) AQ_LAUNCH(nm_train, (attn_fwd_kernel<true, true, false, false, GP, SQ>), grid, block, 0, stream, p);
     else if (pipe && !SQ) AQ_LAUNCH(nm, (attn_fwd_pp_kernel<true, false, GP>), grid, block, 0, stream, p);
@@ -911,7 +929,8 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   p.qmean = vp.qmean;
   p.delta = vp.delta;
   const bool qp = (a.flags & kFlagP) != 0, f16 = use_f16(a.flags);
-  const bool gp = qp && (a.flags & (kFlagGsfP | kFlagTwoLevelP));
+  const bool gp = qp && (a.flags & kFlagsPGlobal);
+  p.gp_static = (a.flags & kFlagGsfP) ? kPScaleStatic : 1.0f;
   // Training outputs come as a set (lse, chunk maxima, O^hp).
   const bool train = a.o_hp && a.lse && a.cmax;
   if (!train && (a.o_hp || a.lse || a.cmax)) return hipErrorInvalidValue;
@@ -957,8 +976,9 @@ hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream) {
                           nullptr, vp.gk, vp.kmean, stream);
   if (e != hipSuccess) return e;
   if ((e = launch_qk_delta(a, w, stream))) return e;
-  const TileQuant qv = use_f16(a.flags) ? kQuantRowsF16 : ((a.flags & kFlagV) ? kQuantRows : kQuantNone);
-  return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qv, nullptr, ws + w.vt, vp.gv, nullptr, stream);
+  const TileQuant qv = use_f16_unit(a.flags) ? kQuantRowsF16 : ((a.flags & kFlagV) ? kQuantRows : kQuantNone);
+  return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qv, nullptr, ws + w.vt, vp.gv, nullptr, stream,
+                             (a.flags & kFlagPvFp8) ? kFp8F16 : kFp8None);
 }
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {

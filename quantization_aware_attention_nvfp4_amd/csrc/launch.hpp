@@ -16,7 +16,10 @@ constexpr int kMaxSelHost = 1024;    // cube-sparse: most selected cubes per que
 // Flag bits of a call (the ABI's AQ_* values): the four quantizers and the variants.
 constexpr unsigned kFlagQ = 1u, kFlagK = 2u, kFlagV = 4u, kFlagP = 8u;
 constexpr unsigned kFlagFinalMax = 16u, kFlagGsfQkv = 32u, kFlagGsfP = 64u, kFlagSmoothK = 128u;
-constexpr unsigned kFlagTwoLevelP = 256u, kFlagSmoothQ = 512u;
+constexpr unsigned kFlagTwoLevelP = 256u, kFlagSmoothQ = 512u, kFlagPvFp8 = 1024u;
+// P's blocks take a global scale (the static-scale kernels) under these flags: 448*6, the two-level
+// scale, or 1 under the FP8 P.V product alone.
+constexpr unsigned kFlagsPGlobal = kFlagGsfP | kFlagTwoLevelP | kFlagPvFp8;
 // Rows of the smooth-K partial sums: one per slab of this many keys.
 constexpr int kMeanSlab = 256;
 
@@ -131,11 +134,13 @@ hipError_t launch_scale_from_amax(const float *amax, float *g_out, hipStream_t s
 // the same with fp16 output values), then a
 // row-major copy and/or a d-major tile copy into the workspace.  g: device fp32 global scale, or
 // null for the unit scale; mean: [B*H, 128] fp32 subtracted per channel before quantization (the
-// smooth-K variant), or null.
+// smooth-K variant), or null; fp8: every value then rounded to FP8 E4M3FN (the FP8 P.V product),
+// stored as bf16 or as fp16 (after kQuantNone / kQuantD / kQuantRows only).
 enum TileQuant { kQuantNone = 0, kQuantD = 1, kQuantRows = 2, kQuantRowsF16 = 3 };
+enum Fp8Round { kFp8None = 0, kFp8Bf16 = 1, kFp8F16 = 2 };
 hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
                                TileQuant quant, void *rows_out, void *tiles_out, const float *g,
-                               const float *mean, hipStream_t stream);
+                               const float *mean, hipStream_t stream, Fp8Round fp8 = kFp8None);
 
 // The per-call quantities of the variants, into the workspace regions scal / kmean / kpart: the
 // smooth-K key means (a.flags & kFlagSmoothK), then the static global scales of Q, K (of the

@@ -23,7 +23,7 @@ import torch
 
 from . import _lib
 from ._lib import (AQ_FINAL_MAX, AQ_FLAGS_ALL, AQ_GSF_P, AQ_GSF_QKV, AQ_QUANT_ALL, AQ_QUANT_K, AQ_QUANT_P,
-                   AQ_QUANT_Q, AQ_QUANT_V, AQ_SMOOTH_K, AQ_SMOOTH_Q, AQ_TWO_LEVEL_P, aq_strides, check,
+                   AQ_QUANT_Q, AQ_QUANT_V, AQ_PV_FP8, AQ_SMOOTH_K, AQ_SMOOTH_Q, AQ_TWO_LEVEL_P, aq_strides, check,
                    load)
 
 HEAD_SIZE = 128
@@ -569,7 +569,7 @@ class QADLinear:
 
 
 __all__ = ["AQ_QUANT_ALL", "AQ_QUANT_Q", "AQ_QUANT_K", "AQ_QUANT_V", "AQ_QUANT_P", "AQ_FINAL_MAX", "AQ_GSF_QKV",
-           "AQ_GSF_P", "AQ_SMOOTH_K", "AQ_SMOOTH_Q", "AQ_TWO_LEVEL_P", "AQ_FLAGS_ALL", "fq_nvfp4",
+           "AQ_GSF_P", "AQ_SMOOTH_K", "AQ_SMOOTH_Q", "AQ_TWO_LEVEL_P", "AQ_PV_FP8", "AQ_FLAGS_ALL", "fq_nvfp4",
            "static_global_scale", "attn_qat_fwd", "attn_qat_fwd_noalloc", "attn_qat_bwd", "attn_qat_train", "AttnQatTrainImpl",
            "vsa_qat_fwd", "vsa_qat_bwd", "vsa_qat_train", "vsa_topk", "qad_linear_fwd", "qad_linear_bwd",
            "qad_linear", "qad_observe_amax", "input_global_sf", "QADLinear"]

@@ -62,9 +62,10 @@ def fwd(lib, **kw):
     (dict(lq=0), -1, "positive"),
     (dict(scale=float("nan")), -1, "softmax_scale"),
     (dict(scale=-1.0), -1, "softmax_scale"),
-    (dict(flags=1024), -1, "quant_flags"),
+    (dict(flags=2048), -1, "quant_flags"),
     (dict(flags=15 | 256 | 16), -2, "AQ_TWO_LEVEL_P"),
     (dict(flags=15 | 256 | 64), -2, "AQ_TWO_LEVEL_P"),
+    (dict(flags=7 | 1024), -2, "AQ_PV_FP8"),
     (dict(Hkv=1), -2, "num_kv_heads"),
     (dict(causal=1, lk=32), -2, "causal"),
     (dict(ws_bytes=100), -1, "workspace"),

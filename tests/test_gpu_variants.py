@@ -1,5 +1,5 @@
 """GPU parity of the attention variants (AQ_FINAL_MAX, AQ_GSF_QKV, AQ_GSF_P, AQ_SMOOTH_K,
-AQ_TWO_LEVEL_P, AQ_SMOOTH_Q) against the oracle, within the stated attention tolerance (tests/parity.py).
+AQ_TWO_LEVEL_P, AQ_SMOOTH_Q, AQ_PV_FP8) against the oracle, within the stated attention tolerance (tests/parity.py).
 
 Dense forward (inference and training outputs) and straight-through backward on ragged, cross
 and causal shapes; the cube-sparse forward and backward on a small grid (compared where the two
@@ -22,9 +22,10 @@ pytestmark = pytest.mark.gpu
 LOG2E = 1.0 / math.log(2.0)
 SCALE = 1.0 / math.sqrt(128)
 ALL = 15
-FM, GQKV, GP, SK, TWO, SQ = 16, 32, 64, 128, 256, 512
+FM, GQKV, GP, SK, TWO, SQ, PV8 = 16, 32, 64, 128, 256, 512, 1024
 VARIANTS = [ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, SK, ALL | FM | GQKV | GP | SK, ALL | TWO, ALL | TWO | GQKV | SK,
-            ALL | SQ, SQ, ALL | SQ | SK | GQKV | FM | GP, ALL | SQ | TWO]
+            ALL | SQ, SQ, ALL | SQ | SK | GQKV | FM | GP, ALL | SQ | TWO, ALL | PV8, 8 | PV8, ALL | PV8 | GP | FM,
+            ALL | PV8 | TWO | GQKV]
 
 
 @pytest.fixture(scope="module")
@@ -84,13 +85,13 @@ def test_static_scales_differ_from_unit(m):
     q, k, v = rand(1, 256, 2, 205), rand(1, 256, 2, 206), rand(1, 256, 2, 207)
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
     base = m.attn_qat_fwd(qg, kg, vg)
-    for fl in (ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, ALL | TWO, ALL | SQ):
+    for fl in (ALL | FM, ALL | GQKV, ALL | GP, ALL | SK, ALL | TWO, ALL | SQ, ALL | PV8):
         assert not torch.equal(m.attn_qat_fwd(qg, kg, vg, quant_flags=fl), base), fl
 
 
 
 
-@pytest.mark.parametrize("flags", [ALL | FM, ALL | FM | GQKV | GP | SK, ALL | TWO | GQKV, ALL | SQ | SK])
+@pytest.mark.parametrize("flags", [ALL | FM, ALL | FM | GQKV | GP | SK, ALL | TWO | GQKV, ALL | SQ | SK, ALL | PV8 | SK])
 def test_cube_sparse_forward_and_backward(m, flags):
     grid, L = (4, 8, 32), 1024
     q, k, v = synth.qkv_headscaled(1, L, 2, 128, seed=208, scaled=False)
@@ -110,7 +111,7 @@ def test_cube_sparse_forward_and_backward(m, flags):
         assert_close(bhrd(t)[mask], rb[name][mask], f"vsa {name} flags={flags}")
 
 
-@pytest.mark.parametrize("flags", [ALL | FM, ALL | TWO, ALL | SQ])
+@pytest.mark.parametrize("flags", [ALL | FM, ALL | TWO, ALL | SQ, ALL | PV8])
 def test_wan_448x896x61_sampled_rows(m, flags):
     q, k, v = synth.wan_448x896x61()
     L = q.shape[1]
@@ -128,6 +129,13 @@ def test_two_level_rejections(m):
     for extra in (FM, GP):
         with pytest.raises(NotImplementedError):
             m.attn_qat_fwd(q, q, q, quant_flags=ALL | TWO | extra)
+
+
+def test_pv_fp8_needs_quantized_p(m):
+    q = rand(1, 128, 1, 222).cuda()
+    for fl in (PV8, 7 | PV8):
+        with pytest.raises(NotImplementedError):
+            m.attn_qat_fwd(q, q, q, quant_flags=fl)
 
 
 @pytest.mark.parametrize("causal", [False, True])
