@@ -192,59 +192,71 @@ __device__ __forceinline__ void load_q_frags(const FwdParams &p, int64_t bb, int
 
 // P of one 32-key sub-tile, whose 16 logits in the lane's registers are one P block, as the two
 // P-hat V-hat B operands (keys 0-7 and 8-15 of the block); psum gains the block's unquantized sum.
-// HP: also the unquantized P as operands (ph), for O^hp.  GP: P's blocks under the global scale g
-// (the static 448*6, the two-level scale of the row and chunk, or 1), P-hat rounded to bf16.  GP
-// with F16 is the FP8 P.V product: that bf16 P-hat is further rounded to the nearest E4M3FN value,
-// which fp16 holds exactly.
+// pb: the block's scale (prob_block, or prob_block_static under P's global scale).  HP: also the
+// unquantized P as operands (ph), for O^hp.  GP: P's blocks under a global scale, P-hat rounded to
+// bf16.  GP with F16 is the FP8 P.V product: that bf16 P-hat is further rounded to the nearest
+// E4M3FN value, which fp16 holds exactly.
+template <bool F16, bool HP, bool GP>
+__device__ __forceinline__ void form_pq(const f32x16 &s, const ProbBlock &pb, float c, float &psum, u32x4 (&pq)[2],
+                                        u32x4 (&ph)[2]) {
+  float r[16];
+  r[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0], c, -pb.mb));
+  float rsum = r[0];  // the same sum as from 0: r >= 0
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    r[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -pb.mb));
+    rsum += r[i];
+  }
+  psum = __builtin_fmaf(pb.Sd, rsum, psum);
+  const uint32_t c0 = e2m1_codes8(r), c1 = e2m1_codes8(r + 8);
+  if (F16 && !GP) {
+    pq[0] = e2m1_decode8_f16(c0, pb.S);
+    pq[1] = e2m1_decode8_f16(c1, pb.S);
+  } else {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      e2m1_decode8(j ? c1 : c0, pb.S, x);
+      if (F16) {  // FP8 P.V product (P-hat >= 0)
+        f16x8 h;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = (_Float16)round_e4m3(bf16lo(f32_to_bf16_rne(x[i])));
+        pq[j] = __builtin_bit_cast(u32x4, h);
+      } else {
+        pq[j] = __builtin_bit_cast(u32x4, pack8_cvt(x));
+      }
+    }
+  }
+  if (HP) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] *= pb.Sd;  // the unquantized P
+    if (F16) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f16x8 h;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = (_Float16)r[8 * j + i];
+        ph[j] = __builtin_bit_cast(u32x4, h);
+      }
+    } else {
+      ph[0] = __builtin_bit_cast(u32x4, pack8_cvt(r));
+      ph[1] = __builtin_bit_cast(u32x4, pack8_cvt(r + 8));
+    }
+  }
+}
+
+// The scale of a P block from its largest logit: unit or global scale g.
+template <bool GP>
+__device__ __forceinline__ ProbBlock p_block(float bmax, float c, float m_new, float g) {
+  return GP ? prob_block_static(bmax, c, m_new, g) : prob_block(bmax, c, m_new);
+}
+
+// form_pq with the block's scale computed here; without QP, P itself (bf16) as the operands.
 template <bool QP, bool F16, bool HP, bool GP>
 __device__ __forceinline__ void form_p(const f32x16 &s, float bmax, float c, float m_new, float g, float &psum,
                                        u32x4 (&pq)[2], u32x4 (&ph)[2]) {
   if (QP) {
-    const ProbBlock pb = GP ? prob_block_static(bmax, c, m_new, g) : prob_block(bmax, c, m_new);
-    float r[16];
-    r[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0], c, -pb.mb));
-    float rsum = r[0];  // the same sum as from 0: r >= 0
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      r[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -pb.mb));
-      rsum += r[i];
-    }
-    psum = __builtin_fmaf(pb.Sd, rsum, psum);
-    const uint32_t c0 = e2m1_codes8(r), c1 = e2m1_codes8(r + 8);
-    if (F16 && !GP) {
-      pq[0] = e2m1_decode8_f16(c0, pb.S);
-      pq[1] = e2m1_decode8_f16(c1, pb.S);
-    } else {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        e2m1_decode8(j ? c1 : c0, pb.S, x);
-        if (F16) {  // FP8 P.V product (P-hat >= 0)
-          f16x8 h;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) h[i] = (_Float16)round_e4m3(bf16lo(f32_to_bf16_rne(x[i])));
-          pq[j] = __builtin_bit_cast(u32x4, h);
-        } else {
-          pq[j] = __builtin_bit_cast(u32x4, pack8_cvt(x));
-        }
-      }
-    }
-    if (HP) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r[i] *= pb.Sd;  // the unquantized P
-      if (F16) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          f16x8 h;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) h[i] = (_Float16)r[8 * j + i];
-          ph[j] = __builtin_bit_cast(u32x4, h);
-        }
-      } else {
-        ph[0] = __builtin_bit_cast(u32x4, pack8_cvt(r));
-        ph[1] = __builtin_bit_cast(u32x4, pack8_cvt(r + 8));
-      }
-    }
+    form_pq<F16, HP, GP>(s, p_block<GP>(bmax, c, m_new, g), c, psum, pq, ph);
   } else {
     float P[16];
 #pragma unroll
@@ -642,8 +654,17 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
     const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : p.gp_static;
     float psum = 0.0f;
     u32x4 ph[2];
+    if constexpr (QP) {
+      // the four blocks' scales first: their dependent chains (two transcendentals each) overlap
+      ProbBlock pb[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) form_p<QP, F16, false, GP>(s[kt], bmax[kt], p.c, m_new, g, psum, pq[kt], ph);
+      for (int kt = 0; kt < 4; ++kt) pb[kt] = p_block<GP>(bmax[kt], p.c, m_new, g);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) form_pq<F16, false, GP>(s[kt], pb[kt], p.c, psum, pq[kt], ph);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) form_p<QP, F16, false, GP>(s[kt], bmax[kt], p.c, m_new, g, psum, pq[kt], ph);
+    }
     l_run = l_run * alpha + psum;
     // Pinned here: otherwise the compiler sinks this phase's work past the barrier into the next.
 #pragma unroll
