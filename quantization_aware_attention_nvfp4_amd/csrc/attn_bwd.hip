@@ -80,6 +80,13 @@ struct BwdParams {
   // rounded to FP8 E4M3FN (the FP8 P.V product), as the forward did.
   float gp_static;
   bool pv_fp8;
+  // Dense dK/dV: work ids below nfull are whole (head, key chunk) units on blocks [0, full_blocks)
+  // (XCD-ordered, per_xcd per XCD); each of the remaining units is split along its query tiles
+  // into `split` pieces, one block each after full_blocks, whose fp32 sums go to part
+  // [piece][dK, dV][128 keys][128 d] for dkdv_reduce_kernel.  split = 0: no pieces.
+  int64_t nfull, full_blocks;
+  int split;
+  float *part;
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -664,20 +671,33 @@ template <bool SPARSE, bool GP, bool SQ>
 __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) uint8_t lds[kDkdvLds];
   const uint32_t lds0 = lds_addr(lds);
-  const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nwork);
-  if (vid < 0) return;
+  // A whole unit, or piece `piece` (>= 0) of a split one.
+  int64_t vid, piece = -1;
+  if ((int64_t)blockIdx.x < p.full_blocks) {
+    vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nfull);
+    if (vid < 0) return;
+  } else {
+    piece = (int64_t)blockIdx.x - p.full_blocks;
+    vid = p.nfull + piece / p.split;
+  }
   const int64_t bh = vid / p.Ck;
   const int64_t kc = vid % p.Ck;
   const int64_t bb = bh / p.heads, hh = bh % p.heads;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, hf = lane >> 5;
   const int kg = wave & 3, qh = wave >> 2;
   const int64_t nqt = (p.lq + kQT - 1) / kQT;
-  const int64_t qt0 = p.causal ? (kc * kChunk) / kQT : 0;
+  int64_t qt0 = p.causal ? (kc * kChunk) / kQT : 0;
 
   // Cube-sparse: the query cubes that selected this key cube, ascending, with the key cube's
   // position in each one's list (packed qc | slot << 16), compacted by wave 0.
   int32_t *lds_list = (int32_t *)(lds + kLdsList);
   int64_t ntiles = nqt - qt0;
+  if (!SPARSE && piece >= 0) {
+    // piece j of `split`: query tiles [ntiles * j / split, ntiles * (j + 1) / split)
+    const int64_t j = piece % p.split, lo = ntiles * j / p.split, hi = ntiles * (j + 1) / p.split;
+    qt0 += lo;
+    ntiles = hi - lo;
+  }
   if constexpr (SPARSE) {
     if (wave == 0) {
       const int16_t *col = p.slot_t + (bh * p.Ck + kc) * p.Cq;
@@ -812,6 +832,19 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
       }
   }
   const float *src = (const float *)(lds + (kg * 2 + (qh == 0 ? 0 : 1)) * 16384);
+  if (!SPARSE && piece >= 0) {
+    // a piece: its fp32 sums (before the dK scale) for dkdv_reduce_kernel
+    float *dst = p.part + (piece * 2 + qh) * (kChunk * kD) + (kg * 32 + n) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 o = *(const f32x4 *)(src + ((dt * 4 + a) * 64 + lane) * 4);
+        *(f32x4 *)(dst + 32 * dt + 8 * a + 4 * hf) =
+            f32x4{mine[dt][4 * a] + o[0], mine[dt][4 * a + 1] + o[1], mine[dt][4 * a + 2] + o[2], mine[dt][4 * a + 3] + o[3]};
+      }
+    return;
+  }
   const float mul = qh == 0 ? p.scale : 1.0f;
   if (key >= p.lk) return;
   uint16_t *out = qh == 0 ? p.dk + bb * p.sdk.b + hh * p.sdk.h + key * p.sdk.l
@@ -828,9 +861,48 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
     }
 }
 
+// dK and dV of the split units: the pieces' fp32 sums added in piece order (deterministic), dK
+// scaled, rounded to bf16.  One lane per 4 consecutive d of one key of one tensor.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, int64_t total) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int d4 = (int)(gid & 31), key_local = (int)((gid >> 5) & 127), tensor = (int)((gid >> 12) & 1);
+  const int64_t u = gid >> 13;
+  const int64_t vid = p.nfull + u;
+  const int64_t bh = vid / p.Ck, kc = vid % p.Ck;
+  const int64_t key = kc * kChunk + key_local;
+  if (key >= p.lk) return;
+  const float *src = p.part + (u * p.split * 2 + tensor) * (kChunk * kD) + key_local * kD + 4 * d4;
+  f32x4 acc = *(const f32x4 *)src;
+  for (int j = 1; j < p.split; ++j) {
+    const f32x4 x = *(const f32x4 *)(src + (int64_t)j * 2 * kChunk * kD);
+    acc = f32x4{acc[0] + x[0], acc[1] + x[1], acc[2] + x[2], acc[3] + x[3]};
+  }
+  const float mul = tensor == 0 ? p.scale : 1.0f;
+  const int64_t bb = bh / p.heads, hh = bh % p.heads;
+  uint16_t *out = tensor == 0 ? p.dk + bb * p.sdk.b + hh * p.sdk.h + key * p.sdk.l
+                              : p.dv + bb * p.sdv.b + hh * p.sdv.h + key * p.sdv.l;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  *(bf16x4 *)(out + 4 * d4) =
+      bf16x4{(__bf16)(acc[0] * mul), (__bf16)(acc[1] * mul), (__bf16)(acc[2] * mul), (__bf16)(acc[3] * mul)};
+}
+
 }  // namespace
 
 namespace {
+
+// Compute units of the current device (one dK/dV workgroup each at a time), cached per device.
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 // slot_t[bh][kc][qc] = position of key cube kc in query cube qc's selection, or -1: one lane per
 // entry, a linear search of the (short) selection row.
@@ -922,14 +994,42 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   else AQ_LAUNCH("bwd_dq", (bwd_dq_sp_kernel<false>), dq_grid, dim3(kDqsWaves * 64), 0, stream, p);
   if ((e = hipGetLastError())) return e;
 
+  // dK/dV units (head, key chunk), one workgroup per CU at a time.  Dense non-causal calls whose
+  // last round would leave CUs idle split each of its units into pieces along the query tiles
+  // (all units are equally long there), so that round ends sooner.
   p.nwork = bh * p.Ck;
-  p.per_xcd = (p.nwork + 7) / 8;
-  const dim3 dkdv_grid((unsigned)(p.per_xcd * 8));
+  p.nfull = p.nwork;
+  p.split = 0;
+  int64_t pieces = 0;
+  if (!sel && !a.causal) {
+    const int64_t cus = cu_count(), tail = p.nwork % cus, nqt = (a.lq + kQT - 1) / kQT;
+    if (tail > 0 && 2 * tail <= cus) {
+      int64_t parts = cus / tail;
+      if (parts > 8) parts = 8;
+      if (parts > nqt) parts = nqt;
+      if (parts * tail > kSplitPieces) parts = kSplitPieces / tail;
+      if (parts >= 2) {
+        p.split = (int)parts;
+        p.nfull = p.nwork - tail;
+        pieces = parts * tail;
+        p.part = (float *)(ws + w.part);
+      }
+    }
+  }
+  p.per_xcd = (p.nfull + 7) / 8;
+  p.full_blocks = p.per_xcd * 8;
+  const dim3 dkdv_grid((unsigned)(p.full_blocks + pieces));
   const bool gp = p.quant_p && (a.flags & kFlagsPGlobal);
   p.gp_static = (a.flags & kFlagGsfP) ? kPScaleStatic : 1.0f;
   p.pv_fp8 = (a.flags & kFlagPvFp8) != 0;
   if (p.delta) launch_dkdv<true>(p, sel != nullptr, gp, dkdv_grid, stream);
   else launch_dkdv<false>(p, sel != nullptr, gp, dkdv_grid, stream);
+  if ((e = hipGetLastError())) return e;
+  if (pieces > 0) {
+    const int64_t total = (p.nwork - p.nfull) * 2 * kChunk * (kD / 4);
+    AQ_LAUNCH("dkdv_reduce", dkdv_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p,
+              total);
+  }
   return hipGetLastError();
 }
 

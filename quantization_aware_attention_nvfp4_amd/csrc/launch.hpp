@@ -70,8 +70,13 @@ struct VsaArgs {
 //                    [B*H, ceil(lk / kMeanSlab), 128] fp64 (their partial sums)
 //   ops 0 and 2: mfin [B*H, lq] fp32 (final row maxima, base-2 units, for the final-max variant)
 struct Workspace {
-  size_t kq, vt, vq, qq, dvec, pool, selw, slot, scal, kmean, kpart, mfin, qmean, qpart, delta, total;
+  size_t kq, vt, vq, qq, dvec, part, pool, selw, slot, scal, kmean, kpart, mfin, qmean, qpart, delta, total;
 };
+
+// Dense backward: fp32 partial sums of the work units split to fill the last round of
+// workgroups (dK/dV: 128 KiB per piece, at most kSplitPieces pieces).
+constexpr int64_t kSplitPieces = 256;
+constexpr size_t kSplitPieceBytes = (size_t)2 * 128 * 128 * 4;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -94,6 +99,12 @@ inline Workspace workspace_layout(int op, int batch, int heads, int64_t lq, int6
     w.vq = take(kbytes);
     w.qq = take(qbytes);
     w.dvec = take(bh * (size_t)lq * 4);
+  }
+  if (op == 1) {
+    // at most 8 pieces per work unit
+    const size_t units = bh * (Ck > Cq ? Ck : Cq);
+    const size_t pieces = 8 * units < (size_t)kSplitPieces ? 8 * units : (size_t)kSplitPieces;
+    w.part = take(pieces * kSplitPieceBytes);
   }
   if (op == 3) {
     const size_t n = (size_t)(lk / kChunkHost);
