@@ -80,10 +80,12 @@ struct BwdParams {
   // rounded to FP8 E4M3FN (the FP8 P.V product), as the forward did.
   float gp_static;
   bool pv_fp8;
-  // Dense dK/dV: work ids below nfull are whole (head, key chunk) units on blocks [0, full_blocks)
-  // (XCD-ordered, per_xcd per XCD); each of the remaining units is split along its query tiles
-  // into `split` pieces, one block each after full_blocks, whose fp32 sums go to part
-  // [piece][dK, dV][128 keys][128 d] for dkdv_reduce_kernel.  split = 0: no pieces.
+  // Dense dQ and dK/dV (set per launch): work ids below nfull are whole units on blocks
+  // [0, full_blocks) (XCD-ordered, per_xcd per XCD); each of the remaining units is split into
+  // `split` pieces, one block each after full_blocks, whose fp32 sums go to part for the reduction
+  // kernel: dQ units (head, 128 queries) along their key chunks, part [piece][128 queries][128 d];
+  // dK/dV units (head, key chunk) along their query tiles, part [piece][dK, dV][128 keys][128 d].
+  // split = 0: no pieces.
   int64_t nfull, full_blocks;
   int split;
   float *part;
@@ -294,8 +296,15 @@ template <bool SPARSE>
 __global__ __launch_bounds__(kDqsWaves * 64, 2) void bwd_dq_sp_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) uint8_t lds[kDqsSlots * kDqsSlot];
   const uint32_t lds0 = lds_addr(lds);
-  const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nwork);
-  if (vid < 0) return;
+  // A whole unit, or piece `piece` (>= 0) of a split one (dense only).
+  int64_t vid, piece = -1;
+  if ((int64_t)blockIdx.x < p.full_blocks) {
+    vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nfull);
+    if (vid < 0) return;
+  } else {
+    piece = (int64_t)blockIdx.x - p.full_blocks;
+    vid = p.nfull + piece / p.split;
+  }
   const int64_t bh = vid / p.Cq;
   const int64_t qc = vid % p.Cq;
   const int64_t bb = bh / p.heads, hh = bh % p.heads;
@@ -310,11 +319,18 @@ __global__ __launch_bounds__(kDqsWaves * 64, 2) void bwd_dq_sp_kernel(BwdParams 
     const int64_t q_last = qc * kChunk + kChunk - 1;
     n_chunks = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
   }
+  // piece j of `split`: key chunks [n_chunks * j / split, n_chunks * (j + 1) / split)
+  int64_t c_lo = 0;
+  if (!SPARSE && piece >= 0) {
+    const int64_t j = piece % p.split, hi = n_chunks * (j + 1) / p.split;
+    c_lo = n_chunks * j / p.split;
+    n_chunks = hi - c_lo;
+  }
   const int nsteps = (int)(4 * n_chunks);
   const int32_t *sel_row = SPARSE ? p.sel + (bh * p.Cq + qc) * p.nsel : nullptr;
   // Head-local key of row 0 of sub-tile s (a uniform scalar).
   auto step_key = [&](int s) -> int64_t {
-    const int64_t ch = SPARSE ? clamp_chunk(sel_row[s >> 2], p.Ck) : (int64_t)(s >> 2);
+    const int64_t ch = SPARSE ? clamp_chunk(sel_row[s >> 2], p.Ck) : c_lo + (int64_t)(s >> 2);
     return ch * kChunk + 32 * (s & 3);
   };
   const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.Ck * kChunk * (kD / 8));
@@ -469,6 +485,17 @@ __global__ __launch_bounds__(kDqsWaves * 64, 2) void bwd_dq_sp_kernel(BwdParams 
     dq_products(s - 1, dA0, dA1);
   }
 
+  if (!SPARSE && piece >= 0) {
+    // a piece: its fp32 sums (before the scale) for dq_reduce_kernel
+    float *dst = p.part + piece * (kChunk * kD) + (wave * 32 + n) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *(f32x4 *)(dst + 32 * dt + 8 * a + 4 * hf) =
+            f32x4{acc[dt][4 * a], acc[dt][4 * a + 1], acc[dt][4 * a + 2], acc[dt][4 * a + 3]};
+    return;
+  }
   if (!qvalid) return;
   uint16_t *op = p.dq + bb * p.sdq.b + hh * p.sdq.h + (int64_t)qrow * p.sdq.l;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -480,6 +507,30 @@ __global__ __launch_bounds__(kDqsWaves * 64, 2) void bwd_dq_sp_kernel(BwdParams 
       *(bf16x4 *)(op + d0i) = bf16x4{(__bf16)(acc[dt][4 * a] * p.scale), (__bf16)(acc[dt][4 * a + 1] * p.scale),
                                      (__bf16)(acc[dt][4 * a + 2] * p.scale), (__bf16)(acc[dt][4 * a + 3] * p.scale)};
     }
+}
+
+// dQ of the split units: the pieces' fp32 sums added in piece order (deterministic), scaled,
+// rounded to bf16.  One lane per 4 consecutive d of one query.
+__global__ __launch_bounds__(256) void dq_reduce_kernel(BwdParams p, int64_t total) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int d4 = (int)(gid & 31), row = (int)((gid >> 5) & 127);
+  const int64_t u = gid >> 12;
+  const int64_t vid = p.nfull + u;
+  const int64_t bh = vid / p.Cq, qc = vid % p.Cq;
+  const int64_t q = qc * kChunk + row;
+  if (q >= p.lq) return;
+  const float *src = p.part + u * p.split * (kChunk * kD) + row * kD + 4 * d4;
+  f32x4 acc = *(const f32x4 *)src;
+  for (int j = 1; j < p.split; ++j) {
+    const f32x4 x = *(const f32x4 *)(src + (int64_t)j * kChunk * kD);
+    acc = f32x4{acc[0] + x[0], acc[1] + x[1], acc[2] + x[2], acc[3] + x[3]};
+  }
+  const int64_t bb = bh / p.heads, hh = bh % p.heads;
+  uint16_t *out = p.dq + bb * p.sdq.b + hh * p.sdq.h + q * p.sdq.l;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  *(bf16x4 *)(out + 4 * d4) = bf16x4{(__bf16)(acc[0] * p.scale), (__bf16)(acc[1] * p.scale),
+                                      (__bf16)(acc[2] * p.scale), (__bf16)(acc[3] * p.scale)};
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -891,6 +942,35 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, int64_t t
 
 namespace {
 
+// How many of `units` equally long work units to split, and into how many pieces, so that the
+// last round of `slots` concurrent workgroups ends sooner: the last `units % slots` units become
+// `split` pieces each (2..8, at most max_parts, at most max_pieces pieces in all), taking the
+// split with the fewest rounds of pieces per piece length (the smallest on ties).
+struct SplitPlan {
+  int64_t nfull = 0, pieces = 0;
+  int split = 0;
+};
+SplitPlan plan_split(int64_t units, int64_t slots, int64_t max_parts, int64_t max_pieces) {
+  SplitPlan r;
+  r.nfull = units;
+  const int64_t tail = slots > 0 ? units % slots : 0;
+  if (tail == 0) return r;
+  int64_t best_num = 1, best_den = 1;  // the tail's length in rounds now: one
+  for (int64_t parts = 2; parts <= 8 && parts <= max_parts && tail * parts <= max_pieces; ++parts) {
+    const int64_t rounds = (tail * parts + slots - 1) / slots;  // rounds of pieces, each 1/parts long
+    if (rounds * best_den < best_num * parts) {
+      best_num = rounds;
+      best_den = parts;
+      r.split = (int)parts;
+    }
+  }
+  if (r.split) {
+    r.nfull = units - tail;
+    r.pieces = tail * r.split;
+  }
+  return r;
+}
+
 // Compute units of the current device (one dK/dV workgroup each at a time), cached per device.
 int cu_count() {
   static int cached[64];
@@ -985,37 +1065,44 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   p.delta = vp.delta;
   p.qmean = vp.qmean;
 
+  // dQ units (head, 128 queries), two workgroups per CU.  The software-pipelined kernel (dense
+  // non-causal calls, where all units are equally long) splits the units of a partly filled last
+  // round along their key chunks.
   p.nwork = bh * p.Cq;
-  p.per_xcd = (p.nwork + 7) / 8;
-  const dim3 dq_grid((unsigned)(p.per_xcd * 8));
+  p.nfull = p.nwork;
+  p.split = 0;
+  p.part = (float *)(ws + w.part);
+  SplitPlan dq_plan;
+  dq_plan.nfull = p.nwork;
+  if (!sel && !a.causal && !p.delta)
+    dq_plan = plan_split(p.nwork, 2 * (int64_t)cu_count(), p.Ck, (int64_t)(w.part_bytes / kDqPieceBytes));
+  p.nfull = dq_plan.nfull;
+  p.split = dq_plan.split;
+  p.per_xcd = (p.nfull + 7) / 8;
+  p.full_blocks = p.per_xcd * 8;
+  const dim3 dq_grid((unsigned)(p.full_blocks + dq_plan.pieces));
   if (sel && p.delta) AQ_LAUNCH("vsa_bwd_dq", (bwd_dq_kernel<true, true>), dq_grid, dim3(kDqThreads), 0, stream, p);
   else if (sel) AQ_LAUNCH("vsa_bwd_dq", (bwd_dq_sp_kernel<true>), dq_grid, dim3(kDqsWaves * 64), 0, stream, p);
   else if (p.delta) AQ_LAUNCH("bwd_dq", (bwd_dq_kernel<false, true>), dq_grid, dim3(kDqThreads), 0, stream, p);
   else AQ_LAUNCH("bwd_dq", (bwd_dq_sp_kernel<false>), dq_grid, dim3(kDqsWaves * 64), 0, stream, p);
   if ((e = hipGetLastError())) return e;
+  if (dq_plan.pieces > 0) {
+    const int64_t total = (p.nwork - p.nfull) * kChunk * (kD / 4);
+    AQ_LAUNCH("dq_reduce", dq_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p, total);
+    if ((e = hipGetLastError())) return e;
+  }
 
   // dK/dV units (head, key chunk), one workgroup per CU at a time.  Dense non-causal calls whose
   // last round would leave CUs idle split each of its units into pieces along the query tiles
   // (all units are equally long there), so that round ends sooner.
   p.nwork = bh * p.Ck;
-  p.nfull = p.nwork;
-  p.split = 0;
-  int64_t pieces = 0;
-  if (!sel && !a.causal) {
-    const int64_t cus = cu_count(), tail = p.nwork % cus, nqt = (a.lq + kQT - 1) / kQT;
-    if (tail > 0 && 2 * tail <= cus) {
-      int64_t parts = cus / tail;
-      if (parts > 8) parts = 8;
-      if (parts > nqt) parts = nqt;
-      if (parts * tail > kSplitPieces) parts = kSplitPieces / tail;
-      if (parts >= 2) {
-        p.split = (int)parts;
-        p.nfull = p.nwork - tail;
-        pieces = parts * tail;
-        p.part = (float *)(ws + w.part);
-      }
-    }
-  }
+  SplitPlan kv_plan;
+  kv_plan.nfull = p.nwork;
+  if (!sel && !a.causal)
+    kv_plan = plan_split(p.nwork, cu_count(), (a.lq + kQT - 1) / kQT, (int64_t)(w.part_bytes / kDkdvPieceBytes));
+  p.nfull = kv_plan.nfull;
+  p.split = kv_plan.split;
+  const int64_t pieces = kv_plan.pieces;
   p.per_xcd = (p.nfull + 7) / 8;
   p.full_blocks = p.per_xcd * 8;
   const dim3 dkdv_grid((unsigned)(p.full_blocks + pieces));

@@ -70,13 +70,14 @@ struct VsaArgs {
 //                    [B*H, ceil(lk / kMeanSlab), 128] fp64 (their partial sums)
 //   ops 0 and 2: mfin [B*H, lq] fp32 (final row maxima, base-2 units, for the final-max variant)
 struct Workspace {
-  size_t kq, vt, vq, qq, dvec, part, pool, selw, slot, scal, kmean, kpart, mfin, qmean, qpart, delta, total;
+  size_t kq, vt, vq, qq, dvec, part, part_bytes, pool, selw, slot, scal, kmean, kpart, mfin, qmean, qpart, delta, total;
 };
 
 // Dense backward: fp32 partial sums of the work units split to fill the last round of
-// workgroups (dK/dV: 128 KiB per piece, at most kSplitPieces pieces).
-constexpr int64_t kSplitPieces = 256;
-constexpr size_t kSplitPieceBytes = (size_t)2 * 128 * 128 * 4;
+// workgroups (a dQ piece 64 KiB, a dK/dV piece 128 KiB), at most kSplitBytes.
+constexpr size_t kSplitBytes = (size_t)64 << 20;
+constexpr size_t kDkdvPieceBytes = (size_t)2 * 128 * 128 * 4;
+constexpr size_t kDqPieceBytes = (size_t)128 * 128 * 4;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -103,8 +104,9 @@ inline Workspace workspace_layout(int op, int batch, int heads, int64_t lq, int6
   if (op == 1) {
     // at most 8 pieces per work unit
     const size_t units = bh * (Ck > Cq ? Ck : Cq);
-    const size_t pieces = 8 * units < (size_t)kSplitPieces ? 8 * units : (size_t)kSplitPieces;
-    w.part = take(pieces * kSplitPieceBytes);
+    const size_t most = 8 * units * kDkdvPieceBytes;
+    w.part_bytes = most < kSplitBytes ? most : kSplitBytes;
+    w.part = take(w.part_bytes);
   }
   if (op == 3) {
     const size_t n = (size_t)(lk / kChunkHost);
