@@ -6,7 +6,10 @@ last V/P block is partial) sampled dQ rows of every head and sampled dK/dV key r
 of one head (chunk edges and the whole last partial block included), plus
 properties that hold at any size for dK and dV there; on the 448x896x61 workload
 (L=25088) the training forward's outputs (o, lse, chunk maxima, o_hp) at sampled
-rows and sampled dQ/dK/dV rows, all in the benchmark's launch configuration."""
+rows and sampled dQ/dK/dV rows, all in the benchmark's launch configuration, on a head
+whose work units run whole and on one whose units are split into pieces (the last
+round of workgroups).  The small non-causal shapes run every unit as pieces (fewer
+units than CUs), the 480x832x81 workload none (its unit counts fill whole rounds)."""
 import math
 
 import numpy as np
@@ -165,7 +168,9 @@ def test_wan_448x896x61_training(m):
     dq, dk, dv = m.attn_qat_bwd(qg, kg, vg, aux, dog)
     torch.cuda.synchronize()
     rows = synth.sample_rows(L, 64, seed=21).numpy()
-    heads = [2, 9]
+    # On 256 CUs the last, partly filled round of work units is split into pieces: head 2's dQ and
+    # dK/dV units run whole; head 11's dQ units and its dK/dV units of key chunks 148-195 are pieces.
+    heads = [2, 11]
     hs = torch.as_tensor(heads)
     rf = oracle.attn_fwd(bhld_bits(q[:, :, hs]), bhld_bits(k[:, :, hs]), bhld_bits(v[:, :, hs]),
                          1.0 / math.sqrt(128), rows=rows)
@@ -182,8 +187,8 @@ def test_wan_448x896x61_training(m):
     rb = oracle.attn_bwd(bhld_bits(q[:, :, hs]), bhld_bits(k[:, :, hs]), bhld_bits(v[:, :, hs]),
                          bhld_bits(do[:, :, hs]), 1.0 / math.sqrt(128), qrows=rows, krows=np.zeros(0, np.int64))
     assert_close(bhrd(dq[:, :, hs], rows), rb["dq"], "448x896x61 dq rows")
-    h = 9
-    krows = key_rows(L, seed=22)
+    h = 11
+    krows = np.union1d(key_rows(L, seed=22), [148 * 128 - 1, 148 * 128])  # the last whole / first split unit
     rk = one_head_bwd(q, k, v, do, h, np.zeros(0, np.int64), krows)
     assert_close(bhrd(dk[:, :, h:h + 1], krows), rk["dk"], "448x896x61 dk rows")
     assert_close(bhrd(dv[:, :, h:h + 1], krows), rk["dv"], "448x896x61 dv rows")
