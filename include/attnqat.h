@@ -216,6 +216,10 @@ int attn_qat_fwd_noalloc(const void *q, const void *k, const void *v, void *o, i
  * lse_log2 [B, H, lq] and chunk_max_log2 [B, H, ceil(lk/128), lq] (x2 under AQ_TWO_LEVEL_P), fp32
  * contiguous.  The pointers carry no sizes, so the library cannot check these shapes: smaller
  * buffers are read past their end.  Outputs dq, dk, dv bf16 with their own strides.
+ * Deterministic: no atomics.  Non-causal calls may compute some (head, 128-row) blocks of the
+ * gradients in pieces whose fp32 sums are added in a fixed order, to fill the last round of
+ * workgroups; which blocks depends on the device's compute-unit count, so results can differ in
+ * the last bits between GPU models, never between runs on one.
  * workspace: at least attn_qat_workspace_size(1, ...) bytes.
  * Errors: as attn_qat_fwd, plus AQ_EINVAL for any null gradient or statistics pointer.
  * ------------------------------------------------------------------------------------------- */
