@@ -1024,7 +1024,7 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
     return e;
   if ((e = launch_qk_delta(a, w, stream))) return e;
   if ((e = launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qr_v, ws + w.vq, nullptr, vp.gv, nullptr, stream,
-                               (a.flags & kFlagPvFp8) ? kFp8Bf16 : kFp8None)))
+                               (a.flags & kFlagPvFp8) ? kOutFp8Bf16 : kOutBf16)))
     return e;
 
   const int64_t bh = (int64_t)a.batch * a.heads;

@@ -768,6 +768,284 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
 }
 
 // ------------------------------------------------------------------------------------------
+// Ping-pong training forward (dense; unit scales with every quantizer on, smooth-K allowed)
+// ------------------------------------------------------------------------------------------
+//
+// The inference ping-pong schedule with the training outputs: the second accumulator for O^hp
+// and its unquantized P operands (fp16), the chunk maxima and lse.  The two accumulators leave
+// no room for the Q-hat operand in registers, and the two chunk buffers no room for Q-hat as
+// bf16 in LDS, so each wave keeps its Q-hat in LDS as E2M1 codes and fp16 block scales (3 KiB)
+// and decodes each column pair to fp16 before the logit MFMAs that use it; the K-hat rows are
+// staged as fp16.  Under the unit scale every Q-hat and K-hat value is exact in fp16 and so is
+// every product, so the logits are those of the bf16 kernels bit for bit.  The matrix phase runs
+// chunk it's P-hat V-hat and P V-hat products first and chunk it+1's logits after them, so the P
+// operands are dead before the logits are born.  With 96 MFMAs per chunk the matrix phase is the
+// longer one, so the rescale of the running outputs moves to the vector phase.
+
+// The lane's Q-hat (zero past lq) as codes: for column pair t (d = 16t + 8hf .. +7), code[t]
+// holds the 8 E2M1 codes (byte i: elements 2i, 2i+1), scale[t] the block's E4M3 scale.  The codes
+// are the codec's decisions: E2M1 of the exact quotient x / S, ties to even, sign kept.
+__device__ __forceinline__ void load_q_codes(const FwdParams &p, int64_t bb, int64_t hh, int64_t qrow, bool qvalid,
+                                             int hf, uint32_t (&code)[8], float (&scale)[8]) {
+  const uint16_t *qp = p.q + bb * p.sq.b + hh * p.sq.h + (qvalid ? qrow : 0) * p.sq.l;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (qvalid) v = *(const u32x4 *)(qp + 16 * t + 8 * hf);
+    float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y), bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
+    am = pair_max(am);
+    const float S = block_scale_unit(am);
+    const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = div_e4m3(f[i], S, inv);
+    code[t] = e2m1_codes8(f);
+    scale[t] = S;
+  }
+}
+
+// LDS of the training kernel past the two chunk buffers: per wave, its lanes' Q-hat codes
+// [t][lane] (4 bytes) and block scales [t][lane] (fp16), read back once per column pair and chunk.
+constexpr uint32_t kLdsQc = 2 * 65536, kQcWave = 8 * 64 * 4 + 8 * 64 * 2;
+
+__global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(FwdParams p) {
+  constexpr int BM = 32 * kPPWaves;
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kLdsQc + kPPWaves * kQcWave];
+
+  const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
+  if (vid < 0) return;
+  const int64_t bh = vid / p.qtiles;
+  const int qt = (int)(vid % p.qtiles);
+  const int64_t bb = bh / p.heads, hh = bh % p.heads;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const int64_t qrow = (int64_t)qt * BM + wave * 32 + n;
+  const bool qvalid = qrow < p.lq;
+
+  const int lk = (int)p.lk;
+  int n_iter = (int)p.nchunks;
+  if (p.causal) {
+    const int q_last = qt * BM + BM - 1;
+    n_iter = (q_last < lk - 1 ? q_last : lk - 1) / kChunk + 1;
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.kchunks * (kChunk * kD / 8));
+  const uint8_t *vbase = (const uint8_t *)(p.vt + bh * p.kchunks * (kChunk * kD / 8));
+  // Copies, buffers and phases exactly as in attn_fwd_pp_kernel.
+  uint32_t k_off, v_off;
+  {
+    const int r = 4 * wave + (lane >> 4), d = 16 * wave + (lane >> 2);
+    k_off = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
+    v_off = (uint32_t)(d * 256 + (((lane & 3) ^ sw_v64(d)) << 4));
+  }
+  auto copy_k = [&](int c, uint32_t buf) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      load_lds16_sa(kbase + (int64_t)c * 32768 + kt * 8192, k_off, buf + kLdsK + kt * 8192 + 1024 * wave);
+  };
+  auto copy_v = [&](int c, uint32_t buf) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      load_lds16_sa(vbase + (int64_t)c * 32768 + kt * 64, v_off, buf + kLdsV + kt * 8192 + 1024 * wave);
+  };
+  auto fill = [&](int j) {
+    const uint32_t buf = lds0 + (uint32_t)(j & 1) * 65536;
+    if (j + 1 < n_iter) copy_k(j + 1, buf);
+    if (j < n_iter) copy_v(j, buf);
+  };
+
+  copy_k(0, lds0 + 65536);
+  fill(0);
+  // The lane's Q-hat codes and scales into the wave's LDS region (registers are short here).
+  const uint32_t qca = lds0 + kLdsQc + (uint32_t)wave * kQcWave + 4 * lane;
+  const uint32_t qsa = lds0 + kLdsQc + (uint32_t)wave * kQcWave + 8 * 64 * 4 + 2 * lane;
+  {
+    uint32_t qc[8];
+    float qs[8];
+    load_q_codes(p, bb, hh, qrow, qvalid, hf, qc, qs);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(qca + 256 * t) = qc[t];
+      *(__attribute__((address_space(3))) _Float16 *)(uintptr_t)(qsa + 128 * t) = (_Float16)qs[t];
+    }
+  }
+
+  uint32_t ka, va;
+  {
+    const int krow = perm_row(n), swk = sw_kq(krow);
+    ka = lds0 + kLdsK + krow * 256 + 16 * (hf ^ swk);
+    va = lds0 + kLdsV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
+  }
+  // S^T of a chunk from buffer offset kbuf: column pair t outermost, so each Q-hat pair is decoded
+  // once and feeds the four sub-tiles' chains.
+  auto logits = [&](uint32_t kbuf, f32x16 (&st)[4]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t code = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(qca + 256 * t);
+      const _Float16 h = *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)(qsa + 128 * t);
+      const f16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0) * h;
+      const f16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 1) * h;
+      const f16x2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 2) * h;
+      const f16x2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 3) * h;
+      const f16x8 b = {x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, lds_read16(kbuf + (ka ^ (32 * t)) + 8192 * kt)),
+                                                        b, t ? st[kt] : f32x16{}, 0, 0, 0);
+    }
+  };
+
+  f32x16 s[4], acc[4], acc_hp[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    acc[dt] = f32x16{};
+    acc_hp[dt] = f32x16{};
+  }
+  float m_run = (p.m_init && qvalid) ? p.m_init[bh * p.lq + qrow] : -__builtin_inff();
+  float l_run = 0.0f, alpha = 1.0f;
+  u32x4 pq[4][2], ph[4][2];
+
+  AQ_WAIT_VMCNT(0);
+  __builtin_amdgcn_s_barrier();
+  logits(65536u, s);
+  __builtin_amdgcn_s_barrier();
+
+  // V(it): mask, running max (stored as chunk it's maximum), P-hat and P of chunk it.
+  auto vphase = [&](int it) {
+    const bool tail = (it + 1) * kChunk > lk;
+    const bool diag = p.causal && (it + 1) * kChunk - 1 > qt * BM + wave * 32;
+    if (tail || diag) {
+      const int key0 = it * kChunk + 16 * hf, lk1 = lk - 1, q = (int)qrow;
+      const int last = p.causal ? (q < lk1 ? q : lk1) : lk1;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) mask_tail(s[kt], valid_prefix(key0 + 32 * kt, last));
+    }
+    float bmax[4];
+    max16x4(s, bmax);
+    float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
+    cm = pair_max(cm);
+    const float m_new = fmaxf(m_run, cm * p.c);
+    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    if (hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
+    float psum = 0.0f;
+    ProbBlock pb[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) pb[kt] = prob_block(bmax[kt], p.c, m_new);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) form_pq<true, true, false>(s[kt], pb[kt], p.c, psum, pq[kt], ph[kt]);
+    l_run = l_run * alpha + psum;
+    // the running outputs' rescale (skipped when no row moved) here rather than in the matrix
+    // phase, which is the longer one in this kernel
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        acc[dt] *= alpha;
+        acc_hp[dt] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      AQ_OPAQUE(pq[kt][0]);
+      AQ_OPAQUE(pq[kt][1]);
+      AQ_OPAQUE(ph[kt][0]);
+      AQ_OPAQUE(ph[kt][1]);
+    }
+    AQ_OPAQUE(l_run);
+    AQ_OPAQUE(m_run);
+    AQ_OPAQUE(alpha);
+  };
+  // M(it): O^T += V-hat(it)^T P-hat(it)^T and O^hp^T += V-hat(it)^T P(it)^T, then S of chunk it+1,
+  // from buffer it%2 (the last iteration's logits come from a stale K half and are dropped).
+  auto mphase = [&](int it) {
+    const uint32_t buf = (uint32_t)(it & 1) * 65536;
+    uint32_t vad[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) vad[j] = buf + (va ^ (16 * j));
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const f16x8 a = __builtin_bit_cast(f16x8, lds_read16(vad[j] + 8192 * kt + 2048 * dt));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
+          acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, ph[kt][j]), acc_hp[dt], 0, 0, 0);
+        }
+    // each V-hat read 4 reads ahead of its two MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (g < 28) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    // the P operands die here, before the logits' accumulators are born
+    __builtin_amdgcn_sched_barrier(0);
+    logits(buf, s);
+    // each K-hat read 6 reads ahead of its MFMA; the next column pair's Q-hat decode spread over
+    // the MFMAs of the current one
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (g < 26) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (g < 28) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) AQ_OPAQUE(s[kt]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      AQ_OPAQUE(acc[dt]);
+      AQ_OPAQUE(acc_hp[dt]);
+    }
+  };
+
+  if (grp == 1) __builtin_amdgcn_s_barrier();
+  for (int it = 0; it < n_iter; ++it) {
+    if (grp == 1 && it + 1 < n_iter) fill(it + 1);
+    if (grp == 0 && it >= 1) fill(it);
+    __builtin_amdgcn_s_setprio(0);
+    vphase(it);
+    if (grp == 0) AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_setprio(2);
+    mphase(it);
+    if (grp == 1) AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
+
+  // ---- epilogue: O, O^hp, lse --------------------------------------------------------------
+  const float l = pair_sum(l_run);
+  const float inv_l = 1.0f / l;
+  if (!qvalid) return;
+  uint16_t *op = p.o + bb * p.so.b + hh * p.so.h + qrow * p.so.l;
+  float *hp = p.o_hp + (bh * p.lq + qrow) * kD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * dt + 8 * a + 4 * hf;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 w = {(__bf16)(acc[dt][4 * a + 0] * inv_l), (__bf16)(acc[dt][4 * a + 1] * inv_l),
+                        (__bf16)(acc[dt][4 * a + 2] * inv_l), (__bf16)(acc[dt][4 * a + 3] * inv_l)};
+      *(bf16x4 *)(op + d0) = w;
+      *(f32x4 *)(hp + d0) = f32x4{acc_hp[dt][4 * a] * inv_l, acc_hp[dt][4 * a + 1] * inv_l,
+                                  acc_hp[dt][4 * a + 2] * inv_l, acc_hp[dt][4 * a + 3] * inv_l};
+    }
+  if (hf == 0) p.lse[bh * p.lq + qrow] = m_run + __builtin_amdgcn_logf(l);
+}
+
+// ------------------------------------------------------------------------------------------
 // Row-max pass of the final-max variant
 // ------------------------------------------------------------------------------------------
 //
@@ -875,6 +1153,14 @@ static bool use_f16_unit(unsigned flags) {
   return (flags & kFlagV) && (flags & kFlagP) && !(flags & (kFlagGsfQkv | kFlagsPGlobal));
 }
 static bool use_f16(unsigned flags) { return use_f16_unit(flags) || (flags & kFlagPvFp8); }
+// Dense training calls that attn_fwd_pp_train_kernel serves: every quantizer on under unit scales
+// (Q-hat, K-hat exact in fp16), smooth-K allowed; not the final-max pass (it reads bf16 K-hat rows)
+// nor smooth-Q.
+static bool pp_train_ok(const AttnArgs &a, bool sparse) {
+  const bool train = a.o_hp && a.lse && a.cmax;
+  return train && !sparse && (a.flags & kFlagQ) && (a.flags & kFlagK) && use_f16_unit(a.flags) &&
+         !(a.flags & (kFlagFinalMax | kFlagSmoothQ));
+}
 
 // The forward kernel of a call, by its mode: training (QL layout for dense calls), ping-pong dense
 // inference, or the single-group kernel (cube-sparse or smooth-Q inference); qp / f16 / gp as in
@@ -971,12 +1257,17 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
     p.m_init = r.m_out;
   }
 
-  const bool ql = train && qp && !sel;  // see attn_fwd_kernel
+  const bool pp_train = pp_train_ok(a, sel != nullptr);  // attn_fwd_pp_train_kernel
+  const bool ql = train && qp && !sel && !pp_train;  // see attn_fwd_kernel
   const bool pipe = !train && !sel && !p.delta;  // attn_fwd_pp_kernel (not under smooth-Q)
-  const int waves = ql ? 8 : pipe ? kPPWaves : WAVES;
+  const int waves = ql ? 8 : (pipe || pp_train) ? kPPWaves : WAVES;
   set_tiling(p, a, waves);
   const dim3 grid((unsigned)(p.per_xcd * 8)), block(waves * 64);
   const char *nm_train = sel ? "vsa_fwd_train" : "attn_fwd_train", *nm = sel ? "vsa_fwd" : "attn_fwd";
+  if (pp_train) {
+    AQ_LAUNCH(nm_train, attn_fwd_pp_train_kernel, grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
   const bool sq = p.delta != nullptr;
   if (gp && sq) launch_fwd_kernel<true, true>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
   else if (gp) launch_fwd_kernel<true, false>(p, grid, block, train, ql, pipe, qp, f16, nm, nm_train, stream);
@@ -993,13 +1284,14 @@ hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream) {
   hipError_t e = launch_variant_prep(a, w, stream);
   if (e != hipSuccess) return e;
   const VariantPtrs vp = variant_ptrs(a, w);
+  // (fp16 K-hat rows for the ping-pong training kernel, bf16 for every other forward kernel)
   e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, (a.flags & kFlagK) ? kQuantD : kQuantNone, ws + w.kq,
-                          nullptr, vp.gk, vp.kmean, stream);
+                          nullptr, vp.gk, vp.kmean, stream, pp_train_ok(a, op == 2) ? kOutF16 : kOutBf16);
   if (e != hipSuccess) return e;
   if ((e = launch_qk_delta(a, w, stream))) return e;
   const TileQuant qv = use_f16_unit(a.flags) ? kQuantRowsF16 : ((a.flags & kFlagV) ? kQuantRows : kQuantNone);
   return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qv, nullptr, ws + w.vt, vp.gv, nullptr, stream,
-                             (a.flags & kFlagPvFp8) ? kFp8F16 : kFp8None);
+                             (a.flags & kFlagPvFp8) ? kOutFp8F16 : kOutBf16);
 }
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {

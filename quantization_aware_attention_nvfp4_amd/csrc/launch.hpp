@@ -147,13 +147,14 @@ hipError_t launch_scale_from_amax(const float *amax, float *g_out, hipStream_t s
 // the same with fp16 output values), then a
 // row-major copy and/or a d-major tile copy into the workspace.  g: device fp32 global scale, or
 // null for the unit scale; mean: [B*H, 128] fp32 subtracted per channel before quantization (the
-// smooth-K variant), or null; fp8: every value then rounded to FP8 E4M3FN (the FP8 P.V product),
-// stored as bf16 or as fp16 (after kQuantNone / kQuantD / kQuantRows only).
+// smooth-K variant), or null; out: the values as they are (bf16), rounded to FP8 E4M3FN (the
+// FP8 P.V product) and kept as bf16 or as fp16, or as fp16 unchanged (for unit-scale NVFP4 values,
+// which fp16 holds exactly); all after kQuantNone / kQuantD / kQuantRows only.
 enum TileQuant { kQuantNone = 0, kQuantD = 1, kQuantRows = 2, kQuantRowsF16 = 3 };
-enum Fp8Round { kFp8None = 0, kFp8Bf16 = 1, kFp8F16 = 2 };
+enum TileOut { kOutBf16 = 0, kOutFp8Bf16 = 1, kOutFp8F16 = 2, kOutF16 = 3 };
 hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
                                TileQuant quant, void *rows_out, void *tiles_out, const float *g,
-                               const float *mean, hipStream_t stream, Fp8Round fp8 = kFp8None);
+                               const float *mean, hipStream_t stream, TileOut out = kOutBf16);
 
 // The per-call quantities of the variants, into the workspace regions scal / kmean / kpart: the
 // smooth-K key means (a.flags & kFlagSmoothK), then the static global scales of Q, K (of the

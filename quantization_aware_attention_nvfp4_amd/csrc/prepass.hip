@@ -7,9 +7,11 @@
 // where it would be repeated by every query tile of a head.
 //
 // kQuantRowsF16 writes the V-hat values as fp16 instead of bf16 (exact, see below) for the
-// forward's fp16 P-hat V-hat product.  `fp8` (the FP8 P.V product variant) rounds every value,
-// after its quantization, to the nearest FP8 E4M3FN value, kept as bf16 (kFp8Bf16) or as fp16
-// (kFp8F16: every E4M3FN value is exact in fp16, for the forward's fp16 product).
+// forward's fp16 P-hat V-hat product.  `out` (TileOut) then rounds every value, after its
+// quantization, to the nearest FP8 E4M3FN value (the FP8 P.V product variant), kept as bf16
+// (kOutFp8Bf16) or as fp16 (kOutFp8F16: every E4M3FN value is exact in fp16, for the forward's
+// fp16 product), or stores the value as fp16 unchanged (kOutF16: K-hat rows under the unit scale,
+// exact NVFP4 values, for the training forward's fp16 logits).
 //
 // Variants (readings stated in variants.hip): a static global scale g (block scale
 // s = E4M3(fp32(fp32(amax / 6) * g)), S = fp32(s / g), value E2M1(fp32(|x| / S)) * S rounded to
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
                                                     u32x4 *__restrict__ rows_out,
                                                     uint16_t *__restrict__ tiles_out,
                                                     const float *__restrict__ gptr,
-                                                    const float *__restrict__ mean, int fp8) {
+                                                    const float *__restrict__ mean, int out) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kChunk][kD];
   const int64_t bh = blockIdx.x / C;
   const int64_t c = blockIdx.x % C;
@@ -145,19 +147,20 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
     __syncthreads();
   }
 
-  if (fp8 != kFp8None) {
+  if (out != kOutBf16) {
     // FP8 P.V product: every (bf16) value rounded to the nearest E4M3FN value, sign kept (exact in
-    // bf16 and in fp16); rows past L stay zero
+    // bf16 and in fp16); kOutF16: the value itself; rows past L stay zero
     for (int i = tid; i < kChunk * kD / 2; i += 256) {
       uint32_t *w = (uint32_t *)&tile[0][0] + i;
       const float a = bf16lo(*w), b = bf16hi(*w);
-      const float ra = u2f(f2u(round_e4m3(__builtin_fabsf(a))) | (f2u(a) & 0x80000000u));
-      const float rb = u2f(f2u(round_e4m3(__builtin_fabsf(b))) | (f2u(b) & 0x80000000u));
-      if (fp8 == kFp8F16)
+      const bool e4m3 = out == kOutFp8Bf16 || out == kOutFp8F16;
+      const float ra = e4m3 ? u2f(f2u(round_e4m3(__builtin_fabsf(a))) | (f2u(a) & 0x80000000u)) : a;
+      const float rb = e4m3 ? u2f(f2u(round_e4m3(__builtin_fabsf(b))) | (f2u(b) & 0x80000000u)) : b;
+      if (out == kOutFp8Bf16)
+        *w = pack_exact_bf16(ra, rb);
+      else
         *w = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)ra) |
              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)rb) << 16);
-      else
-        *w = pack_exact_bf16(ra, rb);
     }
     __syncthreads();
   }
@@ -185,12 +188,12 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
 
 hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
                                TileQuant quant, void *rows_out, void *tiles_out, const float *g,
-                               const float *mean, hipStream_t stream, Fp8Round fp8) {
+                               const float *mean, hipStream_t stream, TileOut out) {
   const int64_t C = (L + kChunk - 1) / kChunk;
   const int64_t blocks = (int64_t)batch * heads * C;
   AQ_LAUNCH("tile_prepass", tile_prepass, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t *)src, s, heads, L, C, (int)quant, (u32x4 *)rows_out,
-                     (uint16_t *)tiles_out, g, mean, (int)fp8);
+                     (uint16_t *)tiles_out, g, mean, (int)out);
   return hipGetLastError();
 }
 
