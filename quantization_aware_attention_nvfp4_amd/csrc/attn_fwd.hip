@@ -768,6 +768,249 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
 }
 
 // ------------------------------------------------------------------------------------------
+// Ping-pong cube-sparse inference forward
+// ------------------------------------------------------------------------------------------
+//
+// One workgroup per query cube (128 queries), 8 waves: waves w and w+4 hold the same 32 queries.
+// Group 0 walks the cube's list positions 0, 2, 4, ..., group 1 positions 1, 3, 5, ..., in the
+// two-group vector / matrix schedule of attn_fwd_pp_kernel.  A vector phase takes the running
+// maximum of the previous list position from LDS, where the other group left it one phase
+// earlier, so every P is quantized against the same maximum as in the sequential order; each
+// group keeps its own output and sum relative to its own last maximum, and the two are merged at
+// the end.  Global phase ph: the vector phase of position ph and the matrix phase of position
+// ph-1 (P-hat V-hat of it and the logits of position ph+1, its group's next), which reads buffer
+// ph%2 = {K-hat(ph+1), V-hat(ph-1)}; every wave issues its share of that buffer's copies at the
+// start of phase ph-1 and waits for them at its end.
+constexpr uint32_t kLdsMx = 2 * 65536;  // [128] running maximum handed between the groups
+
+template <bool QP, bool F16>
+__global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdParams p) {
+  constexpr int BM = kChunk;
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kLdsMx + BM * 4];
+
+  const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
+  if (vid < 0) return;
+  const int64_t bh = vid / p.qtiles;
+  const int qt = (int)(vid % p.qtiles);
+  const int64_t bb = bh / p.heads, hh = bh % p.heads;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, qs = wave & 3;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const int64_t qrow = (int64_t)qt * BM + qs * 32 + n;
+  const bool qvalid = qrow < p.lq;
+
+  const int nsel = (int)p.nchunks;
+  const int n_it = (nsel + 1) / 2;
+  const int32_t *sel_row = p.sel + (bh * p.qtiles + qt) * p.nchunks;
+  auto chunk_of = [&](int pos) -> int64_t {
+    return clamp_chunk(__builtin_amdgcn_readfirstlane(sel_row[pos]), p.kchunks);
+  };
+  const uint32_t lds0 = lds_addr(lds);
+  const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.kchunks * (kChunk * kD / 8));
+  const uint8_t *vbase = (const uint8_t *)(p.vt + bh * p.kchunks * (kChunk * kD / 8));
+  uint32_t k_off, v_off;
+  {
+    const int r = 4 * wave + (lane >> 4), d = 16 * wave + (lane >> 2);
+    k_off = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
+    v_off = (uint32_t)(d * 256 + (((lane & 3) ^ sw_v64(d)) << 4));
+  }
+  auto copy_k = [&](int64_t c, uint32_t buf) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      load_lds16_sa(kbase + c * 32768 + kt * 8192, k_off, buf + kLdsK + kt * 8192 + 1024 * wave);
+  };
+  auto copy_v = [&](int64_t c, uint32_t buf) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      load_lds16_sa(vbase + c * 32768 + kt * 64, v_off, buf + kLdsV + kt * 8192 + 1024 * wave);
+  };
+  // The buffer of phase ph: K-hat(ph+1) and V-hat(ph-1), when those positions exist.
+  auto fill_for = [&](int ph) {
+    const uint32_t buf = lds0 + (uint32_t)(ph & 1) * 65536;
+    if (ph + 1 < nsel) copy_k(chunk_of(ph + 1), buf);
+    if (ph >= 1 && ph - 1 < nsel) copy_v(chunk_of(ph - 1), buf);
+  };
+
+  // Prologue: K-hat of positions 0 and 1 into buffer 0 (its K half, then its V half, which phase
+  // 2's copies overwrite only after phase 1 starts), the running maximum, Q-hat.
+  copy_k(chunk_of(0), lds0);
+  if (nsel > 1) copy_k(chunk_of(1), lds0 + 32768);
+  if (grp == 0 && hf == 0) {
+    const float m0 = (p.m_init && qvalid) ? p.m_init[bh * p.lq + qrow] : -__builtin_inff();
+    *(__attribute__((address_space(3))) float *)(uintptr_t)(lds0 + kLdsMx + 4 * (qs * 32 + n)) = m0;
+  }
+  bf16x8 qf[8];
+  load_q_frags(p, bb, hh, qrow, qvalid, hf, qf);
+
+  uint32_t ka, va;
+  {
+    const int krow = perm_row(n), swk = sw_kq(krow);
+    ka = lds0 + kLdsK + krow * 256 + 16 * (hf ^ swk);
+    va = lds0 + kLdsV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
+  }
+  const uint32_t mxa = lds0 + kLdsMx + 4 * (qs * 32 + n);
+  auto logits = [&](uint32_t kbuf, int kt, f32x16 &st) {
+    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + ka + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int t = 1; t < 8; ++t)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + (ka ^ (32 * t)) + 8192 * kt)), qf[t], st,
+                                                   0, 0, 0);
+  };
+
+  f32x16 s[4];
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+  float m_g = -__builtin_inff();  // the maximum this group's output and sum are relative to
+  float l_run = 0.0f, alpha = 1.0f;
+  u32x4 pq[4][2];
+
+  AQ_WAIT_VMCNT(0);
+  __syncthreads();
+  if (grp == 0 || nsel > 1) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) logits(grp ? 32768u : 0u, kt, s[kt]);
+  }
+  __builtin_amdgcn_s_barrier();  // buffer 0 is read; phase 0 fills buffer 1
+
+  // V(pos): running maximum from the other group, P-hat of position pos (none past the list).
+  auto vphase = [&](int pos) {
+    alpha = 1.0f;
+    if (pos >= nsel) return;
+    float bmax[4];
+    max16x4(s, bmax);
+    float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
+    cm = pair_max(cm);
+    const float m_prev = *(const __attribute__((address_space(3))) float *)(uintptr_t)mxa;
+    const float m_new = fmaxf(m_prev, cm * p.c);
+    if (hf == 0) *(__attribute__((address_space(3))) float *)(uintptr_t)mxa = m_new;
+    alpha = __builtin_amdgcn_exp2f(m_g - m_new);  // applied to acc by the next matrix phase
+    m_g = m_new;
+    float psum = 0.0f;
+    u32x4 ph[2];
+    ProbBlock pb[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) pb[kt] = prob_block(bmax[kt], p.c, m_new);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      if (QP) form_pq<F16, false, false>(s[kt], pb[kt], p.c, psum, pq[kt], ph);
+      else form_p<false, false, false, false>(s[kt], bmax[kt], p.c, m_new, 1.0f, psum, pq[kt], ph);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      AQ_OPAQUE(pq[kt][0]);
+      AQ_OPAQUE(pq[kt][1]);
+    }
+    AQ_OPAQUE(l_run);
+    AQ_OPAQUE(alpha);
+  };
+  // M(pos) at phase pos+1: O^T += V-hat(pos)^T P-hat(pos)^T and S of position pos+2, from buffer
+  // (pos+1)%2 (logits of a position past the list come from a stale K half and are dropped).
+  auto mphase = [&](int pos) {
+    if (pos >= nsel) return;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+    }
+    const uint32_t buf = (uint32_t)((pos + 1) & 1) * 65536;
+    uint32_t kad[8], vad[2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kad[t] = buf + (ka ^ (32 * t));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) vad[j] = buf + (va ^ (16 * j));
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kad[0] + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int t = 1; t < 8; ++t)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kad[t] + 8192 * kt)), qf[t], s[kt], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const u32x4 a = lds_read16(vad[j] + 8192 * kt + 2048 * dt);
+          if (F16)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                             __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
+          else
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pq[kt][j]), acc[dt], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kPPAhead, 0);
+#pragma unroll
+    for (int g = 0; g < 64; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (g < 64 - kPPAhead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) AQ_OPAQUE(s[kt]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) AQ_OPAQUE(acc[dt]);
+  };
+
+  // Group g's iteration it: V(2it+g) in phase 2it+g, M(2it+g) in phase 2it+g+1.  Each wave issues
+  // its share of phase ph+1's copies at the start of phase ph and waits for them at its end.
+  if (grp == 1) {
+    fill_for(1);
+    AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+  }
+  for (int it = 0; it < n_it; ++it) {
+    const int pos = 2 * it + grp;
+    fill_for(pos + 1);
+    __builtin_amdgcn_s_setprio(0);
+    vphase(pos);
+    AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    fill_for(pos + 2);
+    __builtin_amdgcn_s_setprio(2);
+    mphase(pos);
+    AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_s_setprio(0);
+
+  // ---- merge the groups' outputs, epilogue ---------------------------------------------------
+  // Group 1 leaves its output, sum and maximum in LDS (the chunk buffers are free now).
+  float *xo = (float *)lds + ((qs * 64 + lane) * 66);
+  if (grp == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[16 * dt + r] = acc[dt][r];
+    xo[64] = l_run;
+    xo[65] = m_g;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float l1 = xo[64], m1 = xo[65];
+  const float mx = fmaxf(m_g, m1);
+  const float e0 = __builtin_amdgcn_exp2f(m_g - mx), e1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
+  const float l = pair_sum(l_run * e0 + l1 * e1);
+  const float inv_l = 1.0f / l;
+  if (!qvalid) return;
+  uint16_t *op = p.o + bb * p.so.b + hh * p.so.h + qrow * p.so.l;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * dt + 8 * a + 4 * hf;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (acc[dt][4 * a + i] * e0 + xo[16 * dt + 4 * a + i] * e1) * inv_l;
+      *(bf16x4 *)(op + d0) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Ping-pong training forward (dense; unit scales with every quantizer on, smooth-K allowed)
 // ------------------------------------------------------------------------------------------
 //
@@ -1266,6 +1509,17 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   const char *nm_train = sel ? "vsa_fwd_train" : "attn_fwd_train", *nm = sel ? "vsa_fwd" : "attn_fwd";
   if (pp_train) {
     AQ_LAUNCH(nm_train, attn_fwd_pp_train_kernel, grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
+  // Cube-sparse inference under unit scales with P and V quantized: the ping-pong kernel over the
+  // list, one query cube per workgroup.
+  if (sel && !train && !p.delta && qp && use_f16_unit(a.flags)) {
+    FwdParams v = p;
+    v.qtiles = (int)(a.lq / kChunk);
+    v.nblocks = (int64_t)a.batch * a.heads * v.qtiles;
+    v.per_xcd = (v.nblocks + 7) / 8;
+    AQ_LAUNCH(nm, (attn_fwd_vsa_pp_kernel<true, true>), dim3((unsigned)(v.per_xcd * 8)), dim3(kPPWaves * 64), 0,
+              stream, v);
     return hipGetLastError();
   }
   const bool sq = p.delta != nullptr;

@@ -56,13 +56,37 @@ def test_small_grid(m):
 
 
 def test_sparsity_zero_equals_dense(m):
+    # Every cube selected: the same chunk maxima and P-hat as the dense forward, so the outputs
+    # agree to the rounding of the two wave groups' partial sums, merged at the end (the
+    # training kernel walks the list in one accumulator and matches the dense one bit for bit).
     grid = (4, 8, 16)  # 4 cubes
     q, k, v = synth.qkv_headscaled(1, 512, 3, 128, seed=92, scaled=False)
     o, oc, sel = run(m, q, k, v, grid, 0.0)
     assert np.array_equal(sel, np.broadcast_to(np.arange(4), sel.shape))
     dense = m.attn_qat_fwd(q.cuda(), k.cuda(), v.cuda())
+    o_tr, _ = m.vsa_qat_fwd(q.cuda(), k.cuda(), v.cuda(), grid=grid, cube=(4, 4, 8), sparsity=0.0, training=True)
+    dense_tr, _ = m.attn_qat_fwd(q.cuda(), k.cuda(), v.cuda(), training=True)
     torch.cuda.synchronize()
-    assert torch.equal(o.cpu().view(torch.int16), dense.cpu().view(torch.int16))
+    assert torch.equal(o_tr.cpu().view(torch.int16), dense_tr.cpu().view(torch.int16))
+    a, b = o.float().cpu(), dense.float().cpu()
+    assert ((a - b).abs() <= 2.0 ** -7 * b.abs() + 1e-6).all()  # one bf16 rounding step
+    r = oracle.attn_fwd(bhld_bits(q), bhld_bits(k), bhld_bits(v), SCALE)
+    assert_close(bf16_values(o.permute(0, 2, 1, 3)), r["o"], "vsa at sparsity 0")
+
+
+@pytest.mark.parametrize("sparsity,topk", [(0.7, 3), (0.9, 1), (0.5, 4)])
+def test_list_lengths(m, sparsity, topk):
+    # odd lists (the second wave group's last position is empty), a single cube, an even list
+    grid = (4, 8, 32)  # 8 cubes
+    q, k, v = synth.qkv_headscaled(1, 1024, 2, 128, seed=95 + topk, scaled=False)
+    o, oc, sel = run(m, q, k, v, grid, sparsity)
+    rows = np.arange(1, 1024, 5)
+    r = oracle.vsa_fwd(bhld_bits(q), bhld_bits(k), bhld_bits(v), SCALE, sparsity=sparsity, rows=rows)
+    assert r["topk"] == topk and sel.shape[-1] == topk
+    agree = check_selection(sel, r)
+    ok = agree[:, :, rows // 128]
+    got = bf16_values(o.permute(0, 2, 1, 3)[:, :, torch.as_tensor(rows)])
+    assert_close(got[ok], r["o_fine"][ok], f"vsa fine topk={topk}")
 
 
 def test_wan_vsa_workload(m):
