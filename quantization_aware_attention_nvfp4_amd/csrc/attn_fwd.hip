@@ -781,12 +781,13 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
 // ph-1 (P-hat V-hat of it and the logits of position ph+1, its group's next), which reads buffer
 // ph%2 = {K-hat(ph+1), V-hat(ph-1)}; every wave issues its share of that buffer's copies at the
 // start of phase ph-1 and waits for them at its end.
-constexpr uint32_t kLdsMx = 2 * 65536;  // [128] running maximum handed between the groups
+constexpr uint32_t kLdsMx = 2 * 65536;           // [128] running maximum handed between the groups
+constexpr uint32_t kLdsList = kLdsMx + kChunk * 4;  // the cube's list, int32
 
 template <bool QP, bool F16>
 __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdParams p) {
   constexpr int BM = kChunk;
-  __shared__ __attribute__((aligned(256))) uint8_t lds[kLdsMx + BM * 4];
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kLdsList + kMaxSel * 4];
 
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
   if (vid < 0) return;
@@ -805,9 +806,14 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
 
   const int nsel = (int)p.nchunks;
   const int n_it = (nsel + 1) / 2;
-  const int32_t *sel_row = p.sel + (bh * p.qtiles + qt) * p.nchunks;
+  // The cube's list, read once into LDS.
+  {
+    const int32_t *sel_row = p.sel + (bh * p.qtiles + qt) * p.nchunks;
+    for (int i = tid; i < nsel; i += kPPWaves * 64) ((int32_t *)(lds + kLdsList))[i] = sel_row[i];
+    __syncthreads();
+  }
   auto chunk_of = [&](int pos) -> int64_t {
-    return clamp_chunk(__builtin_amdgcn_readfirstlane(sel_row[pos]), p.kchunks);
+    return clamp_chunk(__builtin_amdgcn_readfirstlane(((const int32_t *)(lds + kLdsList))[pos]), p.kchunks);
   };
   const uint32_t lds0 = lds_addr(lds);
   const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.kchunks * (kChunk * kD / 8));
