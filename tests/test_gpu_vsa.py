@@ -74,6 +74,17 @@ def test_sparsity_zero_equals_dense(m):
     assert_close(bf16_values(o.permute(0, 2, 1, 3)), r["o"], "vsa at sparsity 0")
 
 
+def test_batch_of_two(m):
+    grid = (4, 8, 16)  # 4 cubes, top-3
+    q, k, v = synth.qkv_headscaled(2, 512, 3, 128, seed=96, scaled=False)
+    o, oc, sel = run(m, q, k, v, grid, 0.4)
+    r = oracle.vsa_fwd(bhld_bits(q), bhld_bits(k), bhld_bits(v), SCALE, sparsity=0.4, rows=np.arange(512))
+    assert r["topk"] == 3 and sel.shape == (2, 3, 4, 3)
+    agree = check_selection(sel, r)
+    ok = np.repeat(agree, 128, axis=-1)
+    assert_close(bf16_values(o.permute(0, 2, 1, 3))[ok], r["o_fine"][ok], "vsa fine B=2")
+
+
 @pytest.mark.parametrize("sparsity,topk", [(0.7, 3), (0.9, 1), (0.5, 4)])
 def test_list_lengths(m, sparsity, topk):
     # odd lists (the second wave group's last position is empty), a single cube, an even list
