@@ -75,7 +75,7 @@ struct Workspace {
 
 // Dense backward: fp32 partial sums of the work units split to fill the last round of
 // workgroups (a dQ piece 64 KiB, a dK/dV piece 128 KiB), at most kSplitBytes.
-constexpr size_t kSplitBytes = (size_t)64 << 20;
+constexpr size_t kSplitBytes = (size_t)96 << 20;
 constexpr size_t kDkdvPieceBytes = (size_t)2 * 128 * 128 * 4;
 constexpr size_t kDqPieceBytes = (size_t)128 * 128 * 4;
 
