@@ -319,9 +319,9 @@ __global__ __launch_bounds__(kDqsWaves * 64, 2) void bwd_dq_sp_kernel(BwdParams 
     const int64_t q_last = qc * kChunk + kChunk - 1;
     n_chunks = (q_last < p.lk - 1 ? q_last : p.lk - 1) / kChunk + 1;
   }
-  // piece j of `split`: key chunks [n_chunks * j / split, n_chunks * (j + 1) / split)
+  // piece j of `split`: key chunks (list positions) [n_chunks * j / split, n_chunks * (j + 1) / split)
   int64_t c_lo = 0;
-  if (!SPARSE && piece >= 0) {
+  if (piece >= 0) {
     const int64_t j = piece % p.split, hi = n_chunks * (j + 1) / p.split;
     c_lo = n_chunks * j / p.split;
     n_chunks = hi - c_lo;
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kDqsWaves * 64, 2) void bwd_dq_sp_kernel(BwdParams 
   const int32_t *sel_row = SPARSE ? p.sel + (bh * p.Cq + qc) * p.nsel : nullptr;
   // Head-local key of row 0 of sub-tile s (a uniform scalar).
   auto step_key = [&](int s) -> int64_t {
-    const int64_t ch = SPARSE ? clamp_chunk(sel_row[s >> 2], p.Ck) : c_lo + (int64_t)(s >> 2);
+    const int64_t ch = SPARSE ? clamp_chunk(sel_row[c_lo + (s >> 2)], p.Ck) : c_lo + (int64_t)(s >> 2);
     return ch * kChunk + 32 * (s & 3);
   };
   const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.Ck * kChunk * (kD / 8));
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kDqsWaves * 64, 2) void bwd_dq_sp_kernel(BwdParams 
     dq_products(s - 1, dA0, dA1);
   }
 
-  if (!SPARSE && piece >= 0) {
+  if (piece >= 0) {
     // a piece: its fp32 sums (before the scale) for dq_reduce_kernel
     float *dst = p.part + piece * (kChunk * kD) + (wave * 32 + n) * kD;
 #pragma unroll
@@ -1065,17 +1065,17 @@ hipError_t launch_bwd_common(const AttnArgs &a, const BwdArgs &b, const Workspac
   p.delta = vp.delta;
   p.qmean = vp.qmean;
 
-  // dQ units (head, 128 queries), two workgroups per CU.  The software-pipelined kernel (dense
-  // non-causal calls, where all units are equally long) splits the units of a partly filled last
-  // round along their key chunks.
+  // dQ units (head, 128 queries), two workgroups per CU.  The software-pipelined kernel splits
+  // the units of a partly filled last round along their key chunks (list positions) when all
+  // units are equally long: non-causal dense calls, and cube-sparse calls (topk cubes each).
   p.nwork = bh * p.Cq;
   p.nfull = p.nwork;
   p.split = 0;
   p.part = (float *)(ws + w.part);
   SplitPlan dq_plan;
   dq_plan.nfull = p.nwork;
-  if (!sel && !a.causal && !p.delta)
-    dq_plan = plan_split(p.nwork, 2 * (int64_t)cu_count(), p.Ck, (int64_t)(w.part_bytes / kDqPieceBytes));
+  if (!a.causal && !p.delta)  // (the cube-sparse units all walk topk cubes)
+    dq_plan = plan_split(p.nwork, 2 * (int64_t)cu_count(), sel ? nsel : p.Ck, (int64_t)(w.part_bytes / kDqPieceBytes));
   p.nfull = dq_plan.nfull;
   p.split = dq_plan.split;
   p.per_xcd = (p.nfull + 7) / 8;

@@ -101,7 +101,7 @@ inline Workspace workspace_layout(int op, int batch, int heads, int64_t lq, int6
     w.qq = take(qbytes);
     w.dvec = take(bh * (size_t)lq * 4);
   }
-  if (op == 1) {
+  if (op == 1 || op == 3) {
     // at most 8 pieces per work unit
     const size_t units = bh * (Ck > Cq ? Ck : Cq);
     const size_t most = 8 * units * kDkdvPieceBytes;
