@@ -7,9 +7,9 @@
 // chunk of the dense kernels and V-hat's 16-key blocks never straddle cubes.
 //
 //   pool_kernel    cube means of Q, K (and V for the coarse output) in fp32, rounded to bf16.
-//   select_kernel  per (head, query cube): coarse logits against every key cube in fp32, top-k
-//                  by repeated block-wide argmax (ties to the lower index), the selected cubes
-//                  listed in ascending order; optionally the coarse output softmax(logits) @ Vc.
+//   select_kernel  per (head, query cube), one wave: coarse logits against every key cube in
+//                  fp32, top-k by repeated wave argmax (ties to the lower index), the selected
+//                  cubes listed in ascending order; optionally the coarse output softmax(logits) @ Vc.
 //   fine stage     the dense forward kernel with each query cube's chunk list (attn_fwd.hip).
 #include "attn_common.hpp"
 #include "launch.hpp"
@@ -20,127 +20,155 @@ namespace {
 
 constexpr int kD = kHeadDim;
 
-// One workgroup per (head, cube, tensor): 256 lanes = 128 d x 2 halves of the cube's tokens.
+// One half-wave (32 lanes) per (tensor, head, cube), eight per workgroup, heads fastest (a
+// workgroup reads neighbouring heads' columns of the same token rows): lane (half h, 16-byte
+// column c) adds the 8 values of column c over the 64 tokens of half h in token order; the two
+// halves' sums are added, scaled by 1/128 and rounded to bf16.
 __global__ __launch_bounds__(256) void pool_kernel(const uint16_t *__restrict__ q, Strides sq,
                                                    const uint16_t *__restrict__ k, Strides sk,
                                                    const uint16_t *__restrict__ v, Strides sv,
                                                    uint16_t *__restrict__ pool, int heads, int64_t n,
-                                                   int64_t bhn) {
-  __shared__ float part[kD];
-  const int64_t id = blockIdx.x % bhn;
-  const int which = (int)(blockIdx.x / bhn);
-  const int64_t bh = id / n, cube = id % n;
-  const int64_t b = bh / heads, h = bh % heads;
+                                                   int64_t bhn, int64_t items) {
+  const int64_t item = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (item >= items) return;  // both lanes of every pair below belong to the same item
+  const int64_t h = item % heads, r = item / heads, cube = r % n, r2 = r / n;
+  const int64_t nb = bhn / ((int64_t)heads * n), b = r2 % nb;
+  const int which = (int)(r2 / nb);
+  const int64_t id = (b * heads + h) * n + cube;
   const uint16_t *src = which == 0 ? q : (which == 1 ? k : v);
   const Strides s = which == 0 ? sq : (which == 1 ? sk : sv);
-  const int d = threadIdx.x & (kD - 1), half = threadIdx.x >> 7;
-  const uint16_t *base = src + b * s.b + h * s.h + (cube * kChunk + half * 64) * s.l + d;
-  float acc = 0.0f;
-  for (int t = 0; t < 64; ++t) acc += bf16lo(base[t * s.l]);
-  if (half == 1) part[d] = acc;
-  __syncthreads();
+  const int l = threadIdx.x & 31, c = l & 15, half = l >> 4;
+  const uint16_t *base = src + b * s.b + h * s.h + (cube * kChunk + half * 64) * s.l + 8 * c;
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+  for (int t = 0; t < 64; ++t) {
+    const u32x4 x = *(const u32x4 *)(base + t * s.l);
+    acc[0] += bf16lo(x.x);
+    acc[1] += bf16hi(x.x);
+    acc[2] += bf16lo(x.y);
+    acc[3] += bf16hi(x.y);
+    acc[4] += bf16lo(x.z);
+    acc[5] += bf16hi(x.z);
+    acc[6] += bf16lo(x.w);
+    acc[7] += bf16hi(x.w);
+  }
+  float other[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) other[i] = __shfl_xor(acc[i], 16, 64);  // the other half's sums
   if (half == 0) {
-    const float mean = (acc + part[d]) * (1.0f / kChunk);
-    pool[((int64_t)which * bhn + id) * kD + d] = (uint16_t)f32_to_bf16_rne(mean);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = f32_to_bf16_rne((acc[2 * i] + other[2 * i]) * (1.0f / kChunk)) |
+             (f32_to_bf16_rne((acc[2 * i + 1] + other[2 * i + 1]) * (1.0f / kChunk)) << 16);
+    *(u32x4 *)(pool + ((int64_t)which * bhn + id) * kD + 8 * c) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
-// Block-wide argmax of (score, -index) over 256 lanes.
-__device__ __forceinline__ void argmax_step(float &s, int &i, float s2, int i2) {
-  if (s2 > s || (s2 == s && i2 < i)) {
-    s = s2;
-    i = i2;
-  }
-}
-
-// One workgroup per (head, query cube a).  Handles up to 256 key cubes per lane pass.
+// One wave per (head, query cube a), four per workgroup, no workgroup barrier.  LDS per wave: the
+// n coarse logits, their exponentials (coarse output) and the query cube's pooled row.  The
+// logits: lanes over key cubes, each a dot product in d order in fp32.  Top-k: the largest topk,
+// ties to the lower index, listed in ascending order.  Optionally the coarse output
+// softmax(logits) @ Vc, broadcast to the cube's 128 tokens.
 __global__ __launch_bounds__(256) void select_kernel(const uint16_t *__restrict__ pool, int64_t bhn, int64_t n,
                                                      int topk, float scale, int32_t *__restrict__ sel,
                                                      uint16_t *__restrict__ o_coarse, Strides so,
                                                      int heads) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float *score = (float *)smem;                  // [n]
-  int *taken = (int *)(score + n);               // [n]
-  float *qa = (float *)(taken + n);              // [128]
-  float *red_s = qa + kD;                        // [4]
-  int *red_i = (int *)(red_s + 4);               // [4]
-  const int64_t id = blockIdx.x;                 // bh * n + a
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t id = (int64_t)blockIdx.x * 4 + wave;  // bh * n + a
+  if (id >= bhn) return;
+  const int64_t n4 = (n + 3) & ~(int64_t)3;    // 16-byte aligned regions
+  float *score = smem + wave * (2 * n4 + kD);  // [n]
+  float *ex = score + n4;                      // [n]
+  float *qa = ex + n4;                         // [128]
   const int64_t bh = id / n, a = id % n;
   const uint16_t *qc = pool + id * kD;
   const uint16_t *kc = pool + (bhn + bh * n) * kD;
   const uint16_t *vc = pool + (2 * bhn + bh * n) * kD;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < kD) qa[tid] = bf16lo(qc[tid]);
-  __syncthreads();
-  for (int64_t b = tid; b < n; b += 256) {
-    const uint16_t *kr = kc + b * kD;
+  {
+    const uint32_t x = *(const uint32_t *)(qc + 2 * lane);
+    qa[2 * lane] = bf16lo(x);
+    qa[2 * lane + 1] = bf16hi(x);
+  }
+  for (int64_t b = lane; b < n; b += 64) {
+    const u32x4 *kr = (const u32x4 *)(kc + b * kD);
     float acc = 0.0f;
-    for (int d = 0; d < kD; ++d) acc = __builtin_fmaf(qa[d], bf16lo(kr[d]), acc);
+    u32x4 xs[kD / 8];
+#pragma unroll
+    for (int j = 0; j < kD / 8; ++j) xs[j] = kr[j];
+#pragma unroll
+    for (int j = 0; j < kD / 8; ++j) {
+      const u32x4 x = xs[j];
+      const f32x4 q0 = *(const f32x4 *)(qa + 8 * j), q1 = *(const f32x4 *)(qa + 8 * j + 4);
+      acc = __builtin_fmaf(q0[0], bf16lo(x.x), acc);
+      acc = __builtin_fmaf(q0[1], bf16hi(x.x), acc);
+      acc = __builtin_fmaf(q0[2], bf16lo(x.y), acc);
+      acc = __builtin_fmaf(q0[3], bf16hi(x.y), acc);
+      acc = __builtin_fmaf(q1[0], bf16lo(x.z), acc);
+      acc = __builtin_fmaf(q1[1], bf16hi(x.z), acc);
+      acc = __builtin_fmaf(q1[2], bf16lo(x.w), acc);
+      acc = __builtin_fmaf(q1[3], bf16hi(x.w), acc);
+    }
     // A NaN score (a NaN anywhere in the cube's tokens) ranks below every number, so the top-k
     // always finds topk distinct cubes.
     const float sc = scale * acc;
     score[b] = sc == sc ? sc : -__builtin_inff();
-    taken[b] = 0;
-  }
-  __syncthreads();
-  for (int r = 0; r < topk; ++r) {
-    float bs = -__builtin_inff();
-    int bi = 0x7fffffff;
-    for (int64_t b = tid; b < n; b += 256)
-      if (!taken[b]) argmax_step(bs, bi, score[b], (int)b);
-    for (int off = 32; off > 0; off >>= 1) argmax_step(bs, bi, __shfl_xor(bs, off), __shfl_xor(bi, off));
-    if (lane == 0) {
-      red_s[wave] = bs;
-      red_i[wave] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float s0 = red_s[0];
-      int i0 = red_i[0];
-      for (int w = 1; w < 4; ++w) argmax_step(s0, i0, red_s[w], red_i[w]);
-      // Every score is a number (at worst -inf, which the tie rule still picks), so i0 is an
-      // untaken cube; the lowest untaken one stands in should that ever fail.
-      if (i0 < 0 || i0 >= n || taken[i0]) {
-        i0 = 0;
-        while (i0 < n - 1 && taken[i0]) ++i0;
-      }
-      taken[i0] = 1;
-    }
-    __syncthreads();
-  }
-  // ascending list of the selected cubes
-  if (tid == 0) {
-    int t = 0;
-    int32_t *out = sel + id * topk;
-    for (int64_t b = 0; b < n; ++b)
-      if (taken[b]) out[t++] = (int32_t)b;
   }
   if (o_coarse) {
     // softmax over all key cubes (not quantized), then the mean values Vc
-    __syncthreads();
     float mx = -__builtin_inff();
-    for (int64_t b = tid; b < n; b += 256) mx = fmaxf(mx, score[b]);
+    for (int64_t b = lane; b < n; b += 64) mx = fmaxf(mx, score[b]);
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) red_s[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-    __syncthreads();
-    for (int64_t b = tid; b < n; b += 256) score[b] = __expf(score[b] - mx);
-    __syncthreads();
-    if (tid < kD) {
-      float num = 0.0f, den = 0.0f;
-      for (int64_t b = 0; b < n; ++b) {
-        num = __builtin_fmaf(score[b], bf16lo(vc[b * kD + tid]), num);
-        den += score[b];
-      }
-      qa[tid] = num / den;
+    for (int64_t b = lane; b < n; b += 64) ex[b] = __expf(score[b] - mx);
+    float num0 = 0.0f, num1 = 0.0f, den = 0.0f;
+    for (int64_t b = 0; b < n; ++b) {
+      const float e = ex[b];
+      const uint32_t x = *(const uint32_t *)(vc + b * kD + 2 * lane);
+      num0 = __builtin_fmaf(e, bf16lo(x), num0);
+      num1 = __builtin_fmaf(e, bf16hi(x), num1);
+      den += e;
     }
-    __syncthreads();
+    const uint32_t val = f32_to_bf16_rne(num0 / den) | (f32_to_bf16_rne(num1 / den) << 16);
     const int64_t bb = bh / heads, hh = bh % heads;
-    const int d = tid & (kD - 1);
-    const uint16_t val = (uint16_t)f32_to_bf16_rne(qa[d]);
-    for (int t = tid >> 7; t < kChunk; t += 2)
-      o_coarse[bb * so.b + hh * so.h + (a * kChunk + t) * so.l + d] = val;
+    uint16_t *dst = o_coarse + bb * so.b + hh * so.h + a * kChunk * so.l + 2 * lane;
+    for (int t = 0; t < kChunk; ++t) *(uint32_t *)(dst + t * so.l) = val;
+  }
+  // The topk-th largest logit T by bisection over order-preserving keys (no NaN is left: those
+  // became -inf), then every logit above T and, of those equal to T, the lowest cubes: the same
+  // set as topk rounds of argmax with ties to the lower index, listed in ascending order.
+  auto okey = [](float x) -> uint32_t {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x + 0.0f);  // -0 as +0: they tie
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  };
+  auto count_ge = [&](uint32_t t) -> int {
+    int c = 0;
+    for (int64_t base = 0; base < n; base += 64) {
+      const int64_t b = base + lane;
+      c += (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(b < n && okey(score[b]) >= t));
+    }
+    return c;
+  };
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu;  // count_ge(lo) >= topk holds throughout
+  while (lo < hi) {
+    const uint32_t mid = lo + (uint32_t)(((uint64_t)(hi - lo) + 1u) >> 1);
+    if (count_ge(mid) >= topk) lo = mid;
+    else hi = mid - 1u;
+  }
+  int need_eq = topk - (lo == 0xFFFFFFFFu ? 0 : count_ge(lo + 1u));  // cubes equal to T to take
+  int32_t *out = sel + id * topk;
+  int cnt = 0;
+  for (int64_t base = 0; base < n; base += 64) {
+    const int64_t b = base + lane;
+    const uint32_t kb = b < n ? okey(score[b]) : 0u;
+    const uint64_t meq = __builtin_amdgcn_ballot_w64(b < n && kb == lo);
+    const int eq_before = (int)__builtin_popcountll(meq & ((1ull << lane) - 1ull));
+    const bool take = b < n && (kb > lo || (kb == lo && eq_before < need_eq));
+    const uint64_t m = __builtin_amdgcn_ballot_w64(take);
+    if (take) out[cnt + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = (int32_t)b;
+    cnt += (int)__builtin_popcountll(m);
+    const int eq_all = (int)__builtin_popcountll(meq);
+    need_eq -= eq_all < need_eq ? eq_all : need_eq;
   }
 }
 
@@ -155,17 +183,18 @@ hipError_t launch_vsa_fwd(const AttnArgs &a, const VsaArgs &s, hipStream_t strea
   const int64_t bhn = (int64_t)a.batch * a.heads * n;
   uint16_t *pool = (uint16_t *)(ws + w.pool);
   const int ntensors = s.o_coarse ? 3 : 2;
-  AQ_LAUNCH("vsa_pool", pool_kernel, dim3((unsigned)(bhn * ntensors)), dim3(256), 0, stream,
+  const int64_t items = bhn * ntensors;
+  AQ_LAUNCH("vsa_pool", pool_kernel, dim3((unsigned)((items + 7) / 8)), dim3(256), 0, stream,
                      (const uint16_t *)a.q, a.sq, (const uint16_t *)a.k, a.sk, (const uint16_t *)a.v, a.sv,
-                     pool, a.heads, n, bhn);
+                     pool, a.heads, n, bhn, items);
   if ((e = hipGetLastError())) return e;
   int32_t *sel = s.sel ? s.sel : (int32_t *)(ws + w.selw);
-  const size_t smem = (size_t)n * 8 + kD * 4 + 32;
+  const size_t smem = (size_t)4 * (2 * ((n + 3) & ~(int64_t)3) + kD) * 4;
   if ((e = hipFuncSetAttribute((const void *)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)(smem < 65536 ? 65536 : smem))))
     return e;
-  AQ_LAUNCH("vsa_select", select_kernel, dim3((unsigned)bhn), dim3(256), smem, stream, pool, bhn, n, s.topk,
-                     a.scale, sel, (uint16_t *)s.o_coarse, a.so, a.heads);
+  AQ_LAUNCH("vsa_select", select_kernel, dim3((unsigned)((bhn + 3) / 4)), dim3(256), smem, stream, pool, bhn, n,
+                     s.topk, a.scale, sel, (uint16_t *)s.o_coarse, a.so, a.heads);
   if ((e = hipGetLastError())) return e;
   return launch_attn_fwd_sel(a, sel, s.topk, stream);
 }
