@@ -1295,6 +1295,255 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
 }
 
 // ------------------------------------------------------------------------------------------
+// Ping-pong cube-sparse training forward
+// ------------------------------------------------------------------------------------------
+//
+// attn_fwd_pp_train_kernel over chunk lists: one workgroup per two query cubes, wave group g
+// holding cube 2*qt + g (128 queries, 32 per wave) and walking that cube's list in order, so each
+// group's running maximum, outputs and statistics are its own and final.  The groups' matrix
+// phases read different chunks, so (as in attn_fwd_vsa_pp_kernel) the buffer of phase ph holds
+// K-hat(it+1) and V-hat(it) of the group whose matrix phase ph is (group (ph-1)%2, iteration it),
+// copied by every wave during phase ph-1.  A missing second cube (odd n) walks the first cube's
+// list and stores nothing.
+constexpr uint32_t kLdsVtList = kLdsQc + kPPWaves * kQcWave;  // the two cubes' lists, int16
+
+__global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kLdsVtList + 2 * kMaxSel * 2];
+
+  const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
+  if (vid < 0) return;
+  const int64_t bh = vid / p.qtiles;
+  const int qt = (int)(vid % p.qtiles);
+  const int64_t bb = bh / p.heads, hh = bh % p.heads;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, qs = wave & 3;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const int64_t ncubes = p.kchunks;
+  const int64_t qrow = (int64_t)(2 * qt + grp) * kChunk + qs * 32 + n;
+  const bool qvalid = qrow < p.lq;
+
+  const int nsel = (int)p.nchunks;
+  int16_t *lists = (int16_t *)(lds + kLdsVtList);
+  for (int i = tid; i < 2 * nsel; i += kPPWaves * 64) {
+    const int g = i / nsel, pos = i - g * nsel;
+    const int64_t c = 2 * qt + g < ncubes ? 2 * qt + g : ncubes - 1;
+    lists[i] = (int16_t)clamp_chunk(p.sel[(bh * ncubes + c) * nsel + pos], p.kchunks);
+  }
+  __syncthreads();
+  auto chunk_of = [&](int g, int pos) -> int64_t { return __builtin_amdgcn_readfirstlane((int)lists[g * nsel + pos]); };
+
+  const uint32_t lds0 = lds_addr(lds);
+  const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.kchunks * (kChunk * kD / 8));
+  const uint8_t *vbase = (const uint8_t *)(p.vt + bh * p.kchunks * (kChunk * kD / 8));
+  // Copies as in attn_fwd_pp_kernel.
+  uint32_t k_off, v_off;
+  {
+    const int r = 4 * wave + (lane >> 4), d = 16 * wave + (lane >> 2);
+    k_off = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
+    v_off = (uint32_t)(d * 256 + (((lane & 3) ^ sw_v64(d)) << 4));
+  }
+  auto copy_k = [&](int64_t c, uint32_t buf) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      load_lds16_sa(kbase + c * 32768 + kt * 8192, k_off, buf + kLdsK + kt * 8192 + 1024 * wave);
+  };
+  auto copy_v = [&](int64_t c, uint32_t buf) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      load_lds16_sa(vbase + c * 32768 + kt * 64, v_off, buf + kLdsV + kt * 8192 + 1024 * wave);
+  };
+  // The buffer of phase ph >= 1: K-hat(it+1) and V-hat(it) of group g = (ph-1)%2's iteration
+  // it = (ph-1-g)/2, when those positions exist.
+  auto fill_for = [&](int ph) {
+    if (ph < 1) return;
+    const int g = (ph - 1) & 1, it = (ph - 1 - g) >> 1;
+    const uint32_t buf = lds0 + (uint32_t)(ph & 1) * 65536;
+    if (it + 1 < nsel) copy_k(chunk_of(g, it + 1), buf);
+    if (it < nsel) copy_v(chunk_of(g, it), buf);
+  };
+
+  // Prologue: the groups' first K-hat chunks into buffer 0's halves, Q-hat codes, first logits.
+  copy_k(chunk_of(0, 0), lds0);
+  copy_k(chunk_of(1, 0), lds0 + 32768);
+  const uint32_t qca = lds0 + kLdsQc + (uint32_t)wave * kQcWave + 4 * lane;
+  const uint32_t qsa = lds0 + kLdsQc + (uint32_t)wave * kQcWave + 8 * 64 * 4 + 2 * lane;
+  {
+    uint32_t qc[8];
+    float qsc[8];
+    load_q_codes(p, bb, hh, qrow, qvalid, hf, qc, qsc);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(qca + 256 * t) = qc[t];
+      *(__attribute__((address_space(3))) _Float16 *)(uintptr_t)(qsa + 128 * t) = (_Float16)qsc[t];
+    }
+  }
+  uint32_t ka, va;
+  {
+    const int krow = perm_row(n), swk = sw_kq(krow);
+    ka = lds0 + kLdsK + krow * 256 + 16 * (hf ^ swk);
+    va = lds0 + kLdsV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
+  }
+  // S^T of a chunk from buffer offset kbuf (attn_fwd_pp_train_kernel's arrangement).
+  auto logits = [&](uint32_t kbuf, f32x16 (&st)[4]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t code = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(qca + 256 * t);
+      const _Float16 h = *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)(qsa + 128 * t);
+      const f16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0) * h;
+      const f16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 1) * h;
+      const f16x2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 2) * h;
+      const f16x2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 3) * h;
+      const f16x8 b = {x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, lds_read16(kbuf + (ka ^ (32 * t)) + 8192 * kt)),
+                                                        b, t ? st[kt] : f32x16{}, 0, 0, 0);
+    }
+  };
+
+  f32x16 s[4], acc[4], acc_hp[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    acc[dt] = f32x16{};
+    acc_hp[dt] = f32x16{};
+  }
+  float m_run = -__builtin_inff();
+  float l_run = 0.0f, alpha = 1.0f;
+  u32x4 pq[4][2], ph[4][2];
+
+  AQ_WAIT_VMCNT(0);
+  __syncthreads();
+  logits(grp ? 32768u : 0u, s);
+  __builtin_amdgcn_s_barrier();  // buffer 0 is read; phase 0 fills buffer 1
+
+  // V(it): running max (stored as position it's maximum), P-hat and P of position it.
+  auto vphase = [&](int it) {
+    float bmax[4];
+    max16x4(s, bmax);
+    float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
+    cm = pair_max(cm);
+    const float m_new = fmaxf(m_run, cm * p.c);
+    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    if (hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
+    float psum = 0.0f;
+    ProbBlock pb[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) pb[kt] = prob_block(bmax[kt], p.c, m_new);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) form_pq<true, true, false>(s[kt], pb[kt], p.c, psum, pq[kt], ph[kt]);
+    l_run = l_run * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        acc[dt] *= alpha;
+        acc_hp[dt] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      AQ_OPAQUE(pq[kt][0]);
+      AQ_OPAQUE(pq[kt][1]);
+      AQ_OPAQUE(ph[kt][0]);
+      AQ_OPAQUE(ph[kt][1]);
+    }
+    AQ_OPAQUE(l_run);
+    AQ_OPAQUE(m_run);
+    AQ_OPAQUE(alpha);
+  };
+  // M(it) in phase phm: O^T += V-hat(it)^T P-hat(it)^T and O^hp^T += V-hat(it)^T P(it)^T, then S
+  // of position it+1, from buffer phm%2 (the last position's next logits come from a stale K half
+  // and are dropped).
+  auto mphase = [&](int phm) {
+    const uint32_t buf = (uint32_t)(phm & 1) * 65536;
+    uint32_t vad[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) vad[j] = buf + (va ^ (16 * j));
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const f16x8 a = __builtin_bit_cast(f16x8, lds_read16(vad[j] + 8192 * kt + 2048 * dt));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
+          acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, ph[kt][j]), acc_hp[dt], 0, 0, 0);
+        }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (g < 28) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    logits(buf, s);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (g < 26) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (g < 28) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) AQ_OPAQUE(s[kt]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      AQ_OPAQUE(acc[dt]);
+      AQ_OPAQUE(acc_hp[dt]);
+    }
+  };
+
+  // Group g's iteration it: V(it) in phase 2it+g, M(it) in phase 2it+g+1.  Each wave issues its
+  // share of phase ph+1's copies at the start of phase ph and waits for them at its end.
+  if (grp == 1) {
+    fill_for(1);
+    AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+  }
+  for (int it = 0; it < nsel; ++it) {
+    const int phv = 2 * it + grp;
+    fill_for(phv + 1);
+    __builtin_amdgcn_s_setprio(0);
+    vphase(it);
+    AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    fill_for(phv + 2);
+    __builtin_amdgcn_s_setprio(2);
+    mphase(phv + 1);
+    AQ_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_s_setprio(0);
+
+  // ---- epilogue: O, O^hp, lse --------------------------------------------------------------
+  const float l = pair_sum(l_run);
+  const float inv_l = 1.0f / l;
+  if (!qvalid) return;
+  uint16_t *op = p.o + bb * p.so.b + hh * p.so.h + qrow * p.so.l;
+  float *hp = p.o_hp + (bh * p.lq + qrow) * kD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * dt + 8 * a + 4 * hf;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 w = {(__bf16)(acc[dt][4 * a + 0] * inv_l), (__bf16)(acc[dt][4 * a + 1] * inv_l),
+                        (__bf16)(acc[dt][4 * a + 2] * inv_l), (__bf16)(acc[dt][4 * a + 3] * inv_l)};
+      *(bf16x4 *)(op + d0) = w;
+      *(f32x4 *)(hp + d0) = f32x4{acc_hp[dt][4 * a] * inv_l, acc_hp[dt][4 * a + 1] * inv_l,
+                                  acc_hp[dt][4 * a + 2] * inv_l, acc_hp[dt][4 * a + 3] * inv_l};
+    }
+  if (hf == 0) p.lse[bh * p.lq + qrow] = m_run + __builtin_amdgcn_logf(l);
+}
+
+// ------------------------------------------------------------------------------------------
 // Row-max pass of the final-max variant
 // ------------------------------------------------------------------------------------------
 //
@@ -1402,12 +1651,12 @@ static bool use_f16_unit(unsigned flags) {
   return (flags & kFlagV) && (flags & kFlagP) && !(flags & (kFlagGsfQkv | kFlagsPGlobal));
 }
 static bool use_f16(unsigned flags) { return use_f16_unit(flags) || (flags & kFlagPvFp8); }
-// Dense training calls that attn_fwd_pp_train_kernel serves: every quantizer on under unit scales
-// (Q-hat, K-hat exact in fp16), smooth-K allowed; not the final-max pass (it reads bf16 K-hat rows)
-// nor smooth-Q.
-static bool pp_train_ok(const AttnArgs &a, bool sparse) {
+// Training calls that attn_fwd_pp_train_kernel (dense) and attn_fwd_vsa_pp_train_kernel
+// (cube-sparse) serve: every quantizer on under unit scales (Q-hat, K-hat exact in fp16), smooth-K
+// allowed; not the final-max pass (it reads bf16 K-hat rows) nor smooth-Q.
+static bool pp_train_ok(const AttnArgs &a) {
   const bool train = a.o_hp && a.lse && a.cmax;
-  return train && !sparse && (a.flags & kFlagQ) && (a.flags & kFlagK) && use_f16_unit(a.flags) &&
+  return train && (a.flags & kFlagQ) && (a.flags & kFlagK) && use_f16_unit(a.flags) &&
          !(a.flags & (kFlagFinalMax | kFlagSmoothQ));
 }
 
@@ -1506,7 +1755,7 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
     p.m_init = r.m_out;
   }
 
-  const bool pp_train = pp_train_ok(a, sel != nullptr);  // attn_fwd_pp_train_kernel
+  const bool pp_train = pp_train_ok(a) && !sel;  // attn_fwd_pp_train_kernel
   const bool ql = train && qp && !sel && !pp_train;  // see attn_fwd_kernel
   const bool pipe = !train && !sel && !p.delta;  // attn_fwd_pp_kernel (not under smooth-Q)
   const int waves = ql ? 8 : (pipe || pp_train) ? kPPWaves : WAVES;
@@ -1515,6 +1764,17 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
   const char *nm_train = sel ? "vsa_fwd_train" : "attn_fwd_train", *nm = sel ? "vsa_fwd" : "attn_fwd";
   if (pp_train) {
     AQ_LAUNCH(nm_train, attn_fwd_pp_train_kernel, grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
+  // Cube-sparse training under unit scales: the ping-pong training kernel over the lists, two
+  // query cubes per workgroup.
+  if (sel && pp_train_ok(a)) {
+    FwdParams v = p;
+    v.qtiles = (int)((a.lq / kChunk + 1) / 2);
+    v.nblocks = (int64_t)a.batch * a.heads * v.qtiles;
+    v.per_xcd = (v.nblocks + 7) / 8;
+    AQ_LAUNCH(nm_train, attn_fwd_vsa_pp_train_kernel, dim3((unsigned)(v.per_xcd * 8)), dim3(kPPWaves * 64), 0,
+              stream, v);
     return hipGetLastError();
   }
   // Cube-sparse inference under unit scales with P and V quantized: the ping-pong kernel over the
@@ -1546,7 +1806,7 @@ hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream) {
   const VariantPtrs vp = variant_ptrs(a, w);
   // (fp16 K-hat rows for the ping-pong training kernel, bf16 for every other forward kernel)
   e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, (a.flags & kFlagK) ? kQuantD : kQuantNone, ws + w.kq,
-                          nullptr, vp.gk, vp.kmean, stream, pp_train_ok(a, op == 2) ? kOutF16 : kOutBf16);
+                          nullptr, vp.gk, vp.kmean, stream, pp_train_ok(a) ? kOutF16 : kOutBf16);
   if (e != hipSuccess) return e;
   if ((e = launch_qk_delta(a, w, stream))) return e;
   const TileQuant qv = use_f16_unit(a.flags) ? kQuantRowsF16 : ((a.flags & kFlagV) ? kQuantRows : kQuantNone);

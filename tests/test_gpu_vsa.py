@@ -74,6 +74,22 @@ def test_sparsity_zero_equals_dense(m):
     assert_close(bf16_values(o.permute(0, 2, 1, 3)), r["o"], "vsa at sparsity 0")
 
 
+@pytest.mark.parametrize("grid", [(4, 8, 16), (4, 12, 8)])
+def test_training_outputs_at_sparsity_zero_equal_dense(m, grid):
+    # Every cube selected, every list in ascending order: each query walks the dense chunk order
+    # with the dense training kernel's arithmetic, so O, lse, the chunk maxima and O^hp are the
+    # dense ones bit for bit.  (4, 12, 8) has 3 cubes: the last workgroup's second cube is missing.
+    L = grid[0] * grid[1] * grid[2]
+    q, k, v = synth.qkv_headscaled(1, L, 3, 128, seed=97 + L, scaled=False)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    o_tr, aux = m.vsa_qat_fwd(qg, kg, vg, grid=grid, cube=(4, 4, 8), sparsity=0.0, training=True)
+    d_tr, daux = m.attn_qat_fwd(qg, kg, vg, training=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_tr.cpu().view(torch.int16), d_tr.cpu().view(torch.int16))
+    for name in ("lse_log2", "chunk_max_log2", "o_hp"):
+        assert torch.equal(aux[name].cpu().view(torch.int32), daux[name].cpu().view(torch.int32)), name
+
+
 def test_batch_of_two(m):
     grid = (4, 8, 16)  # 4 cubes, top-3
     q, k, v = synth.qkv_headscaled(2, 512, 3, 128, seed=96, scaled=False)
