@@ -771,23 +771,17 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
 // Ping-pong cube-sparse inference forward
 // ------------------------------------------------------------------------------------------
 //
-// One workgroup per query cube (128 queries), 8 waves: waves w and w+4 hold the same 32 queries.
-// Group 0 walks the cube's list positions 0, 2, 4, ..., group 1 positions 1, 3, 5, ..., in the
-// two-group vector / matrix schedule of attn_fwd_pp_kernel.  A vector phase takes the running
-// maximum of the previous list position from LDS, where the other group left it one phase
-// earlier, so every P is quantized against the same maximum as in the sequential order; each
-// group keeps its own output and sum relative to its own last maximum, and the two are merged at
-// the end.  Global phase ph: the vector phase of position ph and the matrix phase of position
-// ph-1 (P-hat V-hat of it and the logits of position ph+1, its group's next), which reads buffer
-// ph%2 = {K-hat(ph+1), V-hat(ph-1)}; every wave issues its share of that buffer's copies at the
-// start of phase ph-1 and waits for them at its end.
-constexpr uint32_t kLdsMx = 2 * 65536;           // [128] running maximum handed between the groups
-constexpr uint32_t kLdsList = kLdsMx + kChunk * 4;  // the cube's list, int32
+// attn_fwd_pp_kernel over chunk lists: one workgroup per two query cubes, wave group g holding
+// cube 2*qt + g (128 queries, 32 per wave) and walking that cube's list in order with the dense
+// kernel's arithmetic, so each group's output is final (no state crosses groups).  The groups'
+// matrix phases read different chunks, so the buffer of phase ph holds K-hat(it+1) and V-hat(it)
+// of the group whose matrix phase ph is (group (ph-1)%2, iteration it), copied by every wave
+// during phase ph-1.  A missing second cube (odd n) walks the first cube's list and stores
+// nothing.
+constexpr uint32_t kLdsVList = 2 * 65536;  // the two cubes' lists, int16
 
-template <bool QP, bool F16>
 __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdParams p) {
-  constexpr int BM = kChunk;
-  __shared__ __attribute__((aligned(256))) uint8_t lds[kLdsList + kMaxSel * 4];
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kLdsVList + 2 * kMaxSel * 2];
 
   const int64_t vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nblocks);
   if (vid < 0) return;
@@ -801,23 +795,24 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hf = lane >> 5;
-  const int64_t qrow = (int64_t)qt * BM + qs * 32 + n;
+  const int64_t ncubes = p.kchunks;
+  const int64_t qrow = (int64_t)(2 * qt + grp) * kChunk + qs * 32 + n;
   const bool qvalid = qrow < p.lq;
 
   const int nsel = (int)p.nchunks;
-  const int n_it = (nsel + 1) / 2;
-  // The cube's list, read once into LDS.
-  {
-    const int32_t *sel_row = p.sel + (bh * p.qtiles + qt) * p.nchunks;
-    for (int i = tid; i < nsel; i += kPPWaves * 64) ((int32_t *)(lds + kLdsList))[i] = sel_row[i];
-    __syncthreads();
+  int16_t *lists = (int16_t *)(lds + kLdsVList);
+  for (int i = tid; i < 2 * nsel; i += kPPWaves * 64) {
+    const int g = i / nsel, pos = i - g * nsel;
+    const int64_t c = 2 * qt + g < ncubes ? 2 * qt + g : ncubes - 1;
+    lists[i] = (int16_t)clamp_chunk(p.sel[(bh * ncubes + c) * nsel + pos], p.kchunks);
   }
-  auto chunk_of = [&](int pos) -> int64_t {
-    return clamp_chunk(__builtin_amdgcn_readfirstlane(((const int32_t *)(lds + kLdsList))[pos]), p.kchunks);
-  };
+  __syncthreads();
+  auto chunk_of = [&](int g, int pos) -> int64_t { return __builtin_amdgcn_readfirstlane((int)lists[g * nsel + pos]); };
+
   const uint32_t lds0 = lds_addr(lds);
   const uint8_t *kbase = (const uint8_t *)(p.kq + bh * p.kchunks * (kChunk * kD / 8));
   const uint8_t *vbase = (const uint8_t *)(p.vt + bh * p.kchunks * (kChunk * kD / 8));
+  // Copies as in attn_fwd_pp_kernel.
   uint32_t k_off, v_off;
   {
     const int r = 4 * wave + (lane >> 4), d = 16 * wave + (lane >> 2);
@@ -834,21 +829,19 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     for (int kt = 0; kt < 4; ++kt)
       load_lds16_sa(vbase + c * 32768 + kt * 64, v_off, buf + kLdsV + kt * 8192 + 1024 * wave);
   };
-  // The buffer of phase ph: K-hat(ph+1) and V-hat(ph-1), when those positions exist.
+  // The buffer of phase ph >= 1: K-hat(it+1) and V-hat(it) of group g = (ph-1)%2's iteration
+  // it = (ph-1-g)/2, when those positions exist.
   auto fill_for = [&](int ph) {
+    if (ph < 1) return;
+    const int g = (ph - 1) & 1, it = (ph - 1 - g) >> 1;
     const uint32_t buf = lds0 + (uint32_t)(ph & 1) * 65536;
-    if (ph + 1 < nsel) copy_k(chunk_of(ph + 1), buf);
-    if (ph >= 1 && ph - 1 < nsel) copy_v(chunk_of(ph - 1), buf);
+    if (it + 1 < nsel) copy_k(chunk_of(g, it + 1), buf);
+    if (it < nsel) copy_v(chunk_of(g, it), buf);
   };
 
-  // Prologue: K-hat of positions 0 and 1 into buffer 0 (its K half, then its V half, which phase
-  // 2's copies overwrite only after phase 1 starts), the running maximum, Q-hat.
-  copy_k(chunk_of(0), lds0);
-  if (nsel > 1) copy_k(chunk_of(1), lds0 + 32768);
-  if (grp == 0 && hf == 0) {
-    const float m0 = (p.m_init && qvalid) ? p.m_init[bh * p.lq + qrow] : -__builtin_inff();
-    *(__attribute__((address_space(3))) float *)(uintptr_t)(lds0 + kLdsMx + 4 * (qs * 32 + n)) = m0;
-  }
+  // Prologue: the groups' first K-hat chunks into buffer 0's halves, Q-hat, first logits.
+  copy_k(chunk_of(0, 0), lds0);
+  copy_k(chunk_of(1, 0), lds0 + 32768);
   bf16x8 qf[8];
   load_q_frags(p, bb, hh, qrow, qvalid, hf, qf);
 
@@ -858,7 +851,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     ka = lds0 + kLdsK + krow * 256 + 16 * (hf ^ swk);
     va = lds0 + kLdsV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
   }
-  const uint32_t mxa = lds0 + kLdsMx + 4 * (qs * 32 + n);
   auto logits = [&](uint32_t kbuf, int kt, f32x16 &st) {
     st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + ka + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
@@ -871,41 +863,32 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-  float m_g = -__builtin_inff();  // the maximum this group's output and sum are relative to
+  float m_run = (p.m_init && qvalid) ? p.m_init[bh * p.lq + qrow] : -__builtin_inff();
   float l_run = 0.0f, alpha = 1.0f;
   u32x4 pq[4][2];
 
   AQ_WAIT_VMCNT(0);
   __syncthreads();
-  if (grp == 0 || nsel > 1) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) logits(grp ? 32768u : 0u, kt, s[kt]);
-  }
+  for (int kt = 0; kt < 4; ++kt) logits(grp ? 32768u : 0u, kt, s[kt]);
   __builtin_amdgcn_s_barrier();  // buffer 0 is read; phase 0 fills buffer 1
 
-  // V(pos): running maximum from the other group, P-hat of position pos (none past the list).
-  auto vphase = [&](int pos) {
-    alpha = 1.0f;
-    if (pos >= nsel) return;
+  // V(it): running max, P-hat of position it (attn_fwd_pp_kernel's vector phase).
+  auto vphase = [&]() {
     float bmax[4];
     max16x4(s, bmax);
     float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
     cm = pair_max(cm);
-    const float m_prev = *(const __attribute__((address_space(3))) float *)(uintptr_t)mxa;
-    const float m_new = fmaxf(m_prev, cm * p.c);
-    if (hf == 0) *(__attribute__((address_space(3))) float *)(uintptr_t)mxa = m_new;
-    alpha = __builtin_amdgcn_exp2f(m_g - m_new);  // applied to acc by the next matrix phase
-    m_g = m_new;
+    const float m_new = fmaxf(m_run, cm * p.c);
+    alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // applied to acc by the next matrix phase
+    m_run = m_new;
     float psum = 0.0f;
     u32x4 ph[2];
     ProbBlock pb[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) pb[kt] = prob_block(bmax[kt], p.c, m_new);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      if (QP) form_pq<F16, false, false>(s[kt], pb[kt], p.c, psum, pq[kt], ph);
-      else form_p<false, false, false, false>(s[kt], bmax[kt], p.c, m_new, 1.0f, psum, pq[kt], ph);
-    }
+    for (int kt = 0; kt < 4; ++kt) form_pq<true, false, false>(s[kt], pb[kt], p.c, psum, pq[kt], ph);
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -913,17 +896,17 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
       AQ_OPAQUE(pq[kt][1]);
     }
     AQ_OPAQUE(l_run);
+    AQ_OPAQUE(m_run);
     AQ_OPAQUE(alpha);
   };
-  // M(pos) at phase pos+1: O^T += V-hat(pos)^T P-hat(pos)^T and S of position pos+2, from buffer
-  // (pos+1)%2 (logits of a position past the list come from a stale K half and are dropped).
-  auto mphase = [&](int pos) {
-    if (pos >= nsel) return;
+  // M(it) in phase phm: S of position it+1 and O^T += V-hat(it)^T P-hat(it)^T, from buffer phm%2
+  // (the last position's next logits come from a stale K half and are dropped).
+  auto mphase = [&](int phm) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
     }
-    const uint32_t buf = (uint32_t)((pos + 1) & 1) * 65536;
+    const uint32_t buf = (uint32_t)(phm & 1) * 65536;
     uint32_t kad[8], vad[2];
 #pragma unroll
     for (int t = 0; t < 8; ++t) kad[t] = buf + (ka ^ (32 * t));
@@ -940,11 +923,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const u32x4 a = lds_read16(vad[j] + 8192 * kt + 2048 * dt);
-          if (F16)
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                             __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
-          else
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pq[kt][j]), acc[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                           __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
         }
     }
     __builtin_amdgcn_sched_group_barrier(0x100, kPPAhead, 0);
@@ -960,46 +940,31 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     for (int dt = 0; dt < 4; ++dt) AQ_OPAQUE(acc[dt]);
   };
 
-  // Group g's iteration it: V(2it+g) in phase 2it+g, M(2it+g) in phase 2it+g+1.  Each wave issues
-  // its share of phase ph+1's copies at the start of phase ph and waits for them at its end.
+  // Group g's iteration it: V(it) in phase 2it+g, M(it) in phase 2it+g+1.  Each wave issues its
+  // share of phase ph+1's copies at the start of phase ph and waits for them at its end.
   if (grp == 1) {
     fill_for(1);
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
-  for (int it = 0; it < n_it; ++it) {
-    const int pos = 2 * it + grp;
-    fill_for(pos + 1);
+  for (int it = 0; it < nsel; ++it) {
+    const int phv = 2 * it + grp;
+    fill_for(phv + 1);
     __builtin_amdgcn_s_setprio(0);
-    vphase(pos);
+    vphase();
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
-    fill_for(pos + 2);
+    fill_for(phv + 2);
     __builtin_amdgcn_s_setprio(2);
-    mphase(pos);
+    mphase(phv + 1);
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
   if (grp == 0) __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_s_setprio(0);
 
-  // ---- merge the groups' outputs, epilogue ---------------------------------------------------
-  // Group 1 leaves its output, sum and maximum in LDS (the chunk buffers are free now).
-  float *xo = (float *)lds + ((qs * 64 + lane) * 66);
-  if (grp == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xo[16 * dt + r] = acc[dt][r];
-    xo[64] = l_run;
-    xo[65] = m_g;
-  }
-  __syncthreads();
-  if (grp == 1) return;
-  const float l1 = xo[64], m1 = xo[65];
-  const float mx = fmaxf(m_g, m1);
-  const float e0 = __builtin_amdgcn_exp2f(m_g - mx), e1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
-  const float l = pair_sum(l_run * e0 + l1 * e1);
+  // ---- epilogue ----------------------------------------------------------------------------
+  const float l = pair_sum(l_run);
   const float inv_l = 1.0f / l;
   if (!qvalid) return;
   uint16_t *op = p.o + bb * p.so.b + hh * p.so.h + qrow * p.so.l;
@@ -1009,10 +974,9 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     for (int a = 0; a < 4; ++a) {
       const int d0 = 32 * dt + 8 * a + 4 * hf;
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = (acc[dt][4 * a + i] * e0 + xo[16 * dt + 4 * a + i] * e1) * inv_l;
-      *(bf16x4 *)(op + d0) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      const bf16x4 w = {(__bf16)(acc[dt][4 * a + 0] * inv_l), (__bf16)(acc[dt][4 * a + 1] * inv_l),
+                        (__bf16)(acc[dt][4 * a + 2] * inv_l), (__bf16)(acc[dt][4 * a + 3] * inv_l)};
+      *(bf16x4 *)(op + d0) = w;
     }
 }
 
@@ -1778,14 +1742,13 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
     return hipGetLastError();
   }
   // Cube-sparse inference under unit scales with P and V quantized: the ping-pong kernel over the
-  // list, one query cube per workgroup.
+  // lists, two query cubes per workgroup.
   if (sel && !train && !p.delta && qp && use_f16_unit(a.flags)) {
     FwdParams v = p;
-    v.qtiles = (int)(a.lq / kChunk);
+    v.qtiles = (int)((a.lq / kChunk + 1) / 2);
     v.nblocks = (int64_t)a.batch * a.heads * v.qtiles;
     v.per_xcd = (v.nblocks + 7) / 8;
-    AQ_LAUNCH(nm, (attn_fwd_vsa_pp_kernel<true, true>), dim3((unsigned)(v.per_xcd * 8)), dim3(kPPWaves * 64), 0,
-              stream, v);
+    AQ_LAUNCH(nm, attn_fwd_vsa_pp_kernel, dim3((unsigned)(v.per_xcd * 8)), dim3(kPPWaves * 64), 0, stream, v);
     return hipGetLastError();
   }
   const bool sq = p.delta != nullptr;

@@ -56,9 +56,8 @@ def test_small_grid(m):
 
 
 def test_sparsity_zero_equals_dense(m):
-    # Every cube selected: the same chunk maxima and P-hat as the dense forward, so the outputs
-    # agree to the rounding of the two wave groups' partial sums, merged at the end (the
-    # training kernel walks the list in one accumulator and matches the dense one bit for bit).
+    # Every cube selected: each query walks the dense chunk order with the dense kernels'
+    # arithmetic (inference and training), so the outputs are the dense ones bit for bit.
     grid = (4, 8, 16)  # 4 cubes
     q, k, v = synth.qkv_headscaled(1, 512, 3, 128, seed=92, scaled=False)
     o, oc, sel = run(m, q, k, v, grid, 0.0)
@@ -68,17 +67,17 @@ def test_sparsity_zero_equals_dense(m):
     dense_tr, _ = m.attn_qat_fwd(q.cuda(), k.cuda(), v.cuda(), training=True)
     torch.cuda.synchronize()
     assert torch.equal(o_tr.cpu().view(torch.int16), dense_tr.cpu().view(torch.int16))
-    a, b = o.float().cpu(), dense.float().cpu()
-    assert ((a - b).abs() <= 2.0 ** -7 * b.abs() + 1e-6).all()  # one bf16 rounding step
+    assert torch.equal(o.cpu().view(torch.int16), dense.cpu().view(torch.int16))
     r = oracle.attn_fwd(bhld_bits(q), bhld_bits(k), bhld_bits(v), SCALE)
     assert_close(bf16_values(o.permute(0, 2, 1, 3)), r["o"], "vsa at sparsity 0")
 
 
 @pytest.mark.parametrize("grid", [(4, 8, 16), (4, 12, 8)])
-def test_training_outputs_at_sparsity_zero_equal_dense(m, grid):
+def test_outputs_at_sparsity_zero_equal_dense(m, grid):
     # Every cube selected, every list in ascending order: each query walks the dense chunk order
-    # with the dense training kernel's arithmetic, so O, lse, the chunk maxima and O^hp are the
-    # dense ones bit for bit.  (4, 12, 8) has 3 cubes: the last workgroup's second cube is missing.
+    # with the dense kernels' arithmetic, so O (inference and training), lse, the chunk maxima and
+    # O^hp are the dense ones bit for bit.  (4, 12, 8) has 3 cubes: the last workgroup's second
+    # cube is missing.
     L = grid[0] * grid[1] * grid[2]
     q, k, v = synth.qkv_headscaled(1, L, 3, 128, seed=97 + L, scaled=False)
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
@@ -86,6 +85,9 @@ def test_training_outputs_at_sparsity_zero_equal_dense(m, grid):
     d_tr, daux = m.attn_qat_fwd(qg, kg, vg, training=True)
     torch.cuda.synchronize()
     assert torch.equal(o_tr.cpu().view(torch.int16), d_tr.cpu().view(torch.int16))
+    o_inf = m.vsa_qat_fwd(qg, kg, vg, grid=grid, cube=(4, 4, 8), sparsity=0.0)
+    d_inf = m.attn_qat_fwd(qg, kg, vg)
+    assert torch.equal(o_inf.cpu().view(torch.int16), d_inf.cpu().view(torch.int16))
     for name in ("lse_log2", "chunk_max_log2", "o_hp"):
         assert torch.equal(aux[name].cpu().view(torch.int32), daux[name].cpu().view(torch.int32)), name
 
