@@ -184,6 +184,45 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
   }
 }
 
+// The common row case (D-axis blocks under the unit scale, no smoothing, bf16 or fp16 values) as
+// a stream: one lane per 16-byte piece (8 values) of an output row, two neighbouring lanes per
+// 16-value block exchanging their partial abs-max through one DPP move, one-wave workgroups (the
+// standalone fake quantizer's arrangement); rows past L come out zero.  The values are those of
+// tile_prepass: the same scale, quotient and E2M1 rounding, the input's sign kept on zeros.
+__global__ __launch_bounds__(64) void rows_prepass(const uint16_t *__restrict__ src, Strides s, int heads, int64_t L,
+                                                   int64_t C, int64_t n8, u32x4 *__restrict__ rows_out, int f16) {
+  const int64_t j = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (j >= n8) return;  // n8 is a multiple of 64: whole waves only, so every lane's partner is live
+  const int64_t row = j >> 4, part = j & 15;
+  const int64_t bh = row / (C * kChunk), r = row % (C * kChunk);
+  const int64_t b = bh / heads, h = bh % heads;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (r < L) v = __builtin_nontemporal_load((const u32x4 *)(src + b * s.b + h * s.h + r * s.l + part * 8));
+  float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y), bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(f[i]));
+  am = fmaxf(am, xor1(am));
+  const float S = block_scale_unit(am);
+  const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = div_e4m3(f[i], S, inv);
+  e2m1_decode8(e2m1_codes8(q), S, q);
+  const uint32_t vin[4] = {v.x, v.y, v.z, v.w};
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (f16)  // exact: at most 6 significant bits in [2^-10, 6 * 448]
+      w[i] = ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)q[2 * i]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)q[2 * i + 1]) << 16)) |
+             (vin[i] & 0x80008000u);
+    else
+      w[i] = __builtin_amdgcn_perm(f2u(q[2 * i + 1]), f2u(q[2 * i]), 0x07060302u) | (vin[i] & 0x80008000u);
+  }
+  __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, rows_out + j);
+}
+
 }  // namespace
 
 hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
@@ -191,6 +230,12 @@ hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads,
                                const float *mean, hipStream_t stream, TileOut out) {
   const int64_t C = (L + kChunk - 1) / kChunk;
   const int64_t blocks = (int64_t)batch * heads * C;
+  if (quant == kQuantD && !g && !mean && rows_out && !tiles_out && (out == kOutBf16 || out == kOutF16)) {
+    const int64_t n8 = blocks * kChunk * (kD / 8);
+    AQ_LAUNCH("tile_prepass", rows_prepass, dim3((unsigned)(n8 / 64)), dim3(64), 0, stream, (const uint16_t *)src, s,
+              heads, L, C, n8, (u32x4 *)rows_out, (int)(out == kOutF16));
+    return hipGetLastError();
+  }
   AQ_LAUNCH("tile_prepass", tile_prepass, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t *)src, s, heads, L, C, (int)quant, (u32x4 *)rows_out,
                      (uint16_t *)tiles_out, g, mean, (int)out);
