@@ -109,6 +109,7 @@ KERNEL_SOURCES = {
     "attn_fwd": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "fq_contig_unit": ("fq.hip", "aq_device.hpp"),
     "vsa_fwd_train": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
+    "vsa_fwd": ("attn_fwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "vsa_bwd_dkdv": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "vsa_bwd_dq": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
     "dkdv_reduce": ("attn_bwd.hip", "attn_common.hpp", "aq_device.hpp"),
@@ -182,8 +183,8 @@ def pmc_probe():
 
 def profile_step(steps: int):
     """The benchmark step's launches only (448x896x61: fq, training forward, backward, cube-sparse
-    training forward and backward), `steps` times after one warm-up, then the dense inference
-    forward three times and one QAD linear forward + backward (1536 -> 8960, 25088 tokens),
+    training forward and backward), `steps` times after one warm-up, then the dense and the
+    cube-sparse inference forward three times each and one QAD linear forward + backward (1536 -> 8960, 25088 tokens),
     preceded by a plain 1 GiB device copy whose FETCH_SIZE / WRITE_SIZE readings calibrate the
     traffic counters.  For rocprofv3 kernel-trace and counter runs: every
     attention launch it makes is one of the timed workload's."""
@@ -215,6 +216,7 @@ def profile_step(steps: int):
         print(f"profile step {i} done", flush=True)
     for _ in range(3):
         m.attn_qat_fwd(q, k, v)
+        m.vsa_qat_fwd(qv, kv, vv, **vsa_args)
     torch.cuda.synchronize()
     print("profile step: inference forward done", flush=True)
     # one QAD linear forward + backward on the 1536 -> 8960 feed-forward projection (25088 tokens)

@@ -92,6 +92,24 @@ def test_outputs_at_sparsity_zero_equal_dense(m, grid):
         assert torch.equal(aux[name].cpu().view(torch.int32), daux[name].cpu().view(torch.int32)), name
 
 
+def test_odd_cube_count(m):
+    # 3 cubes, top-2: the last workgroup's second wave group has no cube; inference and training
+    # outputs against the oracle on every row of the agreeing query cubes.
+    grid = (4, 12, 8)
+    L = 384
+    q, k, v = synth.qkv_headscaled(1, L, 2, 128, seed=98, scaled=False)
+    o, oc, sel = run(m, q, k, v, grid, 0.4)
+    o_tr, aux = m.vsa_qat_fwd(q.cuda(), k.cuda(), v.cuda(), grid=grid, cube=(4, 4, 8), sparsity=0.4, training=True)
+    torch.cuda.synchronize()
+    r = oracle.vsa_fwd(bhld_bits(q), bhld_bits(k), bhld_bits(v), SCALE, sparsity=0.4, rows=np.arange(L))
+    assert r["topk"] == 2 and sel.shape == (1, 2, 3, 2)
+    assert np.array_equal(aux["sel"].cpu().numpy(), sel)
+    agree = check_selection(sel, r)
+    ok = np.repeat(agree, 128, axis=-1)
+    assert_close(bf16_values(o.permute(0, 2, 1, 3))[ok], r["o_fine"][ok], "vsa fine, 3 cubes")
+    assert_close(bf16_values(o_tr.permute(0, 2, 1, 3))[ok], r["o_fine"][ok], "vsa fine training, 3 cubes")
+
+
 def test_batch_of_two(m):
     grid = (4, 8, 16)  # 4 cubes, top-3
     q, k, v = synth.qkv_headscaled(2, 512, 3, 128, seed=96, scaled=False)
