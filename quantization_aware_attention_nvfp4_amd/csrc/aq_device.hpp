@@ -148,19 +148,56 @@ __device__ __forceinline__ void e2m1_pair(float &a, float &b) {
 // S = E4M3(amax / 6) with amax = exp2(c * logit_max - m), logit_max the block's largest logit
 // (exp2 is monotone).
 // The E2M1 argument P / S is taken in one exponential, r = exp2(y - mb) with mb = m + log2(Sd),
-// Sd = S, or 1 for a block whose scale is 0 (then every P <= 6 * 2^-10 < 0.25 and every code is
-// 0).  The unquantized P of the block is Sd * r.  Forward and backward both use this exact
-// sequence, so they agree on every code.
+// Sd = max(S, 2^-9).  A block whose scale is 0 has amax / 6 <= 2^-10, so its r = 512 P stays at
+// most 3 and its dequantized values, code * S, are 0 whatever the codes; Sd = 2^-9 (the smallest
+// E4M3 step, an exact power of two) keeps the unquantized P = Sd * r of every block.  Forward and
+// backward both use this exact sequence, so they agree on every code.
+//
+// The E4M3 rounding of amax / 6 runs on the gfx950 FP8 conversions (fp32 -> E4M3FN -> fp32 and
+// -> fp16, unit scale): round to nearest even with subnormals kept, equal to round_e4m3 for every
+// fp32 in [0, 464] (an in-bounds sweep of every fp32 bit pattern in [0, 0.25] matched bit for bit;
+// above 464 the conversion gives NaN instead of saturating, and amax / 6 is at most about 1/6
+// here).  amax / 6 is one multiply by RN(1/6), within one ulp of the quotient.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+constexpr float kRcp6 = 0.16666667163372039794921875f;  // RN(1/6)
+constexpr float kScaleFloor = 0.001953125f;             // 2^-9
+
 struct ProbBlock {
-  float S;   // the block scale (0 for a zero block)
-  float Sd;  // S, or 1 when S == 0
-  float mb;  // m + log2(Sd)
+  float S;      // the block scale (0 for a zero block)
+  float Sd;     // max(S, 2^-9)
+  float mb;     // m + log2(Sd)
+  _Float16 Sh;  // S as fp16 (exact)
 };
 __device__ __forceinline__ ProbBlock prob_block(float logit_max, float c, float m) {
-  const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(logit_max, c, -m));
-  const float S = block_scale_unit(am);
-  const float Sd = S == 0.0f ? 1.0f : S;
-  return ProbBlock{S, Sd, m + __builtin_amdgcn_logf(Sd)};
+  const float a6 = __builtin_amdgcn_exp2f(__builtin_fmaf(logit_max, c, -m)) * kRcp6;
+  const s16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, a6, a6, 1.0f, false);
+  const uint32_t wb = __builtin_bit_cast(uint32_t, w);
+  const float S = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wb, 1.0f, false)[0];
+  const f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb, 1.0f, false);
+  const float Sd = fmaxf(S, kScaleFloor);
+  return ProbBlock{S, Sd, m + __builtin_amdgcn_logf(Sd), h[0]};
+}
+// The four blocks of a lane's 64 logits (four 32-key sub-tiles) at once: the conversions take
+// two values each.
+__device__ __forceinline__ void prob_blocks4(const float *logit_max, float c, float m, ProbBlock *pb) {
+  float a6[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a6[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(logit_max[i], c, -m)) * kRcp6;
+  s16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, a6[0], a6[1], 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a6[2], a6[3], 1.0f, true);
+  const uint32_t wb = __builtin_bit_cast(uint32_t, w);
+  const auto S01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wb, 1.0f, false);
+  const auto S23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wb, 1.0f, true);
+  const f16x2 h01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb, 1.0f, false);
+  const f16x2 h23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb, 1.0f, true);
+  const float S[4] = {S01[0], S01[1], S23[0], S23[1]};
+  const _Float16 h[4] = {h01[0], h01[1], h23[0], h23[1]};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float Sd = fmaxf(S[i], kScaleFloor);
+    pb[i] = ProbBlock{S[i], Sd, m + __builtin_amdgcn_logf(Sd), h[i]};
+  }
 }
 // The same under the static global scale g of P's blocks: s = E4M3(fp32(fp32(amax / 6) * g)),
 // S = fp32(s / g).  S is then not an E4M3 value, so the dequantized P-hat is rounded to bf16 as
@@ -169,7 +206,7 @@ __device__ __forceinline__ ProbBlock prob_block_static(float logit_max, float c,
   const float am = __builtin_amdgcn_exp2f(__builtin_fmaf(logit_max, c, -m));
   const float S = round_e4m3((am / 6.0f) * g) / g;
   const float Sd = S == 0.0f ? 1.0f : S;
-  return ProbBlock{S, Sd, m + __builtin_amdgcn_logf(Sd)};
+  return ProbBlock{S, Sd, m + __builtin_amdgcn_logf(Sd), (_Float16)S};
 }
 // The static scale of P's blocks ("nvfp4_qad.py" FP4_RANGE over P's largest value, 1).
 constexpr float kPScaleStatic = 448.0f * 6.0f;
@@ -205,9 +242,7 @@ __device__ __forceinline__ void e2m1_decode8(uint32_t code, float f, float *x) {
 }
 // The eight coded values times S as fp16 (exact: an E2M1 value times an E4M3 scale has at most 6
 // significant bits and lies in [2^-10, 6 * 448]), packed two per register.
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u32x4 e2m1_decode8_f16(uint32_t code, float S) {
-  const _Float16 h = (_Float16)S;
+__device__ __forceinline__ u32x4 e2m1_decode8_f16(uint32_t code, _Float16 h) {
   const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0) * h;
   const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 1) * h;
   const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 2) * h;

@@ -210,8 +210,8 @@ __device__ __forceinline__ void form_pq(const f32x16 &s, const ProbBlock &pb, fl
   psum = __builtin_fmaf(pb.Sd, rsum, psum);
   const uint32_t c0 = e2m1_codes8(r), c1 = e2m1_codes8(r + 8);
   if (F16 && !GP) {
-    pq[0] = e2m1_decode8_f16(c0, pb.S);
-    pq[1] = e2m1_decode8_f16(c1, pb.S);
+    pq[0] = e2m1_decode8_f16(c0, pb.Sh);
+    pq[1] = e2m1_decode8_f16(c1, pb.Sh);
   } else {
     float x[8];
 #pragma unroll
@@ -657,8 +657,12 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
     if constexpr (QP) {
       // the four blocks' scales first: their dependent chains (two transcendentals each) overlap
       ProbBlock pb[4];
+      if constexpr (GP) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) pb[kt] = p_block<GP>(bmax[kt], p.c, m_new, g);
+        for (int kt = 0; kt < 4; ++kt) pb[kt] = prob_block_static(bmax[kt], p.c, m_new, g);
+      } else {
+        prob_blocks4(bmax, p.c, m_new, pb);
+      }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) form_pq<F16, false, GP>(s[kt], pb[kt], p.c, psum, pq[kt], ph);
     } else {
@@ -885,8 +889,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     float psum = 0.0f;
     u32x4 ph[2];
     ProbBlock pb[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) pb[kt] = prob_block(bmax[kt], p.c, m_new);
+    prob_blocks4(bmax, p.c, m_new, pb);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) form_pq<true, false, false>(s[kt], pb[kt], p.c, psum, pq[kt], ph);
     l_run = l_run * alpha + psum;
@@ -1150,8 +1153,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
     if (hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
     float psum = 0.0f;
     ProbBlock pb[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) pb[kt] = prob_block(bmax[kt], p.c, m_new);
+    prob_blocks4(bmax, p.c, m_new, pb);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) form_pq<true, true, false>(s[kt], pb[kt], p.c, psum, pq[kt], ph[kt]);
     l_run = l_run * alpha + psum;
@@ -1396,8 +1398,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel
     if (hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
     float psum = 0.0f;
     ProbBlock pb[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) pb[kt] = prob_block(bmax[kt], p.c, m_new);
+    prob_blocks4(bmax, p.c, m_new, pb);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) form_pq<true, true, false>(s[kt], pb[kt], p.c, psum, pq[kt], ph[kt]);
     l_run = l_run * alpha + psum;
