@@ -119,13 +119,21 @@ __host__ __device__ __forceinline__ float fq_general(float x, float S) {
 __device__ __forceinline__ float xor1(float v) {
   return u2f(__builtin_amdgcn_mov_dpp((int)f2u(v), 0xB1, 0xF, 0xF, true));
 }
+// The larger of two values in one v_max_f32.  fmaxf would first copy each operand through a
+// quieting v_max (the compiler cannot know they are not signalling NaNs); the values here are
+// logits and running maxima, which come from MFMAs and maxima, never from memory.
+__device__ __forceinline__ float max_nq(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 // Combine a value with the one in lane (l ^ 32).  v_permlane32_swap exchanges the upper half
 // of its first operand with the lower half of its second; with both operands equal to v its two
 // results hold (v_l, v_{l^32}) in some order in every lane, so a symmetric combination of the two
 // gives both lanes of a pair the same bits.
 __device__ __forceinline__ float pair_max(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
-  return fmaxf(u2f(p[0]), u2f(p[1]));
+  return max_nq(u2f(p[0]), u2f(p[1]));
 }
 __device__ __forceinline__ float pair_sum(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
@@ -175,7 +183,7 @@ __device__ __forceinline__ ProbBlock prob_block(float logit_max, float c, float 
   const uint32_t wb = __builtin_bit_cast(uint32_t, w);
   const float S = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wb, 1.0f, false)[0];
   const f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb, 1.0f, false);
-  const float Sd = fmaxf(S, kScaleFloor);
+  const float Sd = u2f(max(f2u(S), f2u(kScaleFloor)));  // S >= 0: the integer maximum
   return ProbBlock{S, Sd, m + __builtin_amdgcn_logf(Sd), h[0]};
 }
 // The four blocks of a lane's 64 logits (four 32-key sub-tiles) at once: the conversions take
@@ -195,7 +203,7 @@ __device__ __forceinline__ void prob_blocks4(const float *logit_max, float c, fl
   const _Float16 h[4] = {h01[0], h01[1], h23[0], h23[1]};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float Sd = fmaxf(S[i], kScaleFloor);
+    const float Sd = u2f(max(f2u(S[i]), f2u(kScaleFloor)));
     pb[i] = ProbBlock{S[i], Sd, m + __builtin_amdgcn_logf(Sd), h[i]};
   }
 }

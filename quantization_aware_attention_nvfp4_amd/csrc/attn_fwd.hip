@@ -432,7 +432,7 @@ __global__ __launch_bounds__(QL ? 512 : 256, (QL || (TRAIN && QP)) ? 1 : 2) void
     max16x4(s, bmax);
     float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
     cm = pair_max(cm);
-    const float m_new = fmaxf(m_run, cm * p.c);
+    const float m_new = max_nq(m_run, cm * p.c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
     if (TRAIN && hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
     const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : p.gp_static;
@@ -648,7 +648,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
     max16x4(s, bmax);
     float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
     cm = pair_max(cm);
-    const float m_new = fmaxf(m_run, cm * p.c);
+    const float m_new = max_nq(m_run, cm * p.c);
     alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // applied to acc by the next matrix phase
     m_run = m_new;
     const float g = (GP && p.two_level) ? two_level_scale(cm, p.c, m_new) : p.gp_static;
@@ -731,16 +731,18 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
 
   // Phases ph = 0 .. 2n: group 0 runs V(0) M(0) V(1) M(1) ... and idles in the last phase, group
   // 1 idles in phase 0 and then runs the same sequence, so phase 2it+g is V(it) and 2it+1+g is
-  // M(it) for group g.  Every wave issues its share of iteration j's copies at the start of phase
-  // 2j-1 (buffer j%2 is free: its last reader, group 1's M(j-2), ran in phase 2j-2) and waits for
-  // them at the end of phase 2j, before group 0's M(j) in phase 2j+1.
+  // M(it) for group g.  Every wave issues its share of iteration j's copies in phase 2j-1 (buffer
+  // j%2 is free: its last reader, group 1's M(j-2), ran in phase 2j-2) and waits for them at the
+  // end of phase 2j, before group 0's M(j) in phase 2j+1.
   if (grp == 1) __builtin_amdgcn_s_barrier();
   for (int it = 0; it < n_iter; ++it) {
-    // Iteration it+1's copies (buffer (it+1)%2, free from phase 2it+1): group 1 at the start of
-    // its V(it) (phase 2it+1), group 0 at the start of its V(it+1) (phase 2it+2); both are
-    // waited for at the end of phase 2it+2.
+    // Iteration it+1's copies (buffer (it+1)%2, free from phase 2it+1), both in phase 2it+1: group
+    // 1 at the start of its V(it), group 0 after the MFMAs of its M(it), where it would otherwise
+    // wait for group 1 at the barrier.  A wave stays at a copy instruction until the CU's address
+    // unit takes it (1 KiB each, about 64 bytes per clock for the CU), so the four waves of a
+    // group spend about 500 cycles issuing their 32; group 0's share then costs no vector-phase
+    // time.  Both are waited for at the end of phase 2it+2.
     if (grp == 1 && it + 1 < n_iter) fill(it + 1);
-    if (grp == 0 && it >= 1) fill(it);
     __builtin_amdgcn_s_setprio(0);
     vphase(it);
     if (grp == 0) AQ_WAIT_VMCNT(0);  // end of phase 2it
@@ -749,6 +751,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
     // beside it fills the remaining issue slots
     __builtin_amdgcn_s_setprio(2);
     mphase(it);
+    if (grp == 0 && it + 1 < n_iter) fill(it + 1);
     if (grp == 1) AQ_WAIT_VMCNT(0);  // end of phase 2it+2
     __builtin_amdgcn_s_barrier();
   }
@@ -883,7 +886,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     max16x4(s, bmax);
     float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
     cm = pair_max(cm);
-    const float m_new = fmaxf(m_run, cm * p.c);
+    const float m_new = max_nq(m_run, cm * p.c);
     alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // applied to acc by the next matrix phase
     m_run = m_new;
     float psum = 0.0f;
@@ -957,9 +960,9 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     vphase();
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
-    fill_for(phv + 2);
     __builtin_amdgcn_s_setprio(2);
     mphase(phv + 1);
+    fill_for(phv + 2);
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
@@ -1147,7 +1150,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
     max16x4(s, bmax);
     float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
     cm = pair_max(cm);
-    const float m_new = fmaxf(m_run, cm * p.c);
+    const float m_new = max_nq(m_run, cm * p.c);
     alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     if (hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
@@ -1224,16 +1227,18 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
     }
   };
 
+  // The same phases and copies as the inference kernel: iteration it+1's copies by group 1 at
+  // the start of its V(it), by group 0 after the MFMAs of its M(it).
   if (grp == 1) __builtin_amdgcn_s_barrier();
   for (int it = 0; it < n_iter; ++it) {
     if (grp == 1 && it + 1 < n_iter) fill(it + 1);
-    if (grp == 0 && it >= 1) fill(it);
     __builtin_amdgcn_s_setprio(0);
     vphase(it);
     if (grp == 0) AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_setprio(2);
     mphase(it);
+    if (grp == 0 && it + 1 < n_iter) fill(it + 1);
     if (grp == 1) AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
@@ -1392,7 +1397,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel
     max16x4(s, bmax);
     float cm = max3f(max3f(bmax[0], bmax[1], bmax[2]), bmax[3], bmax[3]);
     cm = pair_max(cm);
-    const float m_new = fmaxf(m_run, cm * p.c);
+    const float m_new = max_nq(m_run, cm * p.c);
     alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     if (hf == 0 && qvalid) p.cmax[(bh * p.nchunks + it) * p.lq + qrow] = m_new;
@@ -1478,9 +1483,9 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel
     vphase(it);
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
-    fill_for(phv + 2);
     __builtin_amdgcn_s_setprio(2);
     mphase(phv + 1);
+    fill_for(phv + 2);
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
