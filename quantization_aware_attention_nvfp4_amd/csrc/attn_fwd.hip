@@ -1767,24 +1767,28 @@ hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t ns
 
 // The variants' per-call quantities, then K-hat rows and V-hat tiles for keys [0, lk) of every
 // head, into the workspace of `op` (0: dense forward, 2: cube-sparse forward).
-hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream) {
+hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream, bool overlap) {
   const Workspace w = workspace_layout(op, a.batch, a.heads, a.lq, a.lk);
   uint8_t *ws = (uint8_t *)a.workspace;
   hipError_t e = launch_variant_prep(a, w, stream);
   if (e != hipSuccess) return e;
+  SideFork f{stream, -1};
+  if (overlap && (e = side_fork(stream, f)) != hipSuccess) return e;
   const VariantPtrs vp = variant_ptrs(a, w);
   // (fp16 K-hat rows for the ping-pong training kernel, bf16 for every other forward kernel)
   e = launch_tile_prepass(a.k, a.sk, a.batch, a.heads, a.lk, (a.flags & kFlagK) ? kQuantD : kQuantNone, ws + w.kq,
                           nullptr, vp.gk, vp.kmean, stream, pp_train_ok(a) ? kOutF16 : kOutBf16);
-  if (e != hipSuccess) return e;
-  if ((e = launch_qk_delta(a, w, stream))) return e;
+  if (e == hipSuccess) e = launch_qk_delta(a, w, stream);
   const TileQuant qv = use_f16_unit(a.flags) ? kQuantRowsF16 : ((a.flags & kFlagV) ? kQuantRows : kQuantNone);
-  return launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qv, nullptr, ws + w.vt, vp.gv, nullptr, stream,
-                             (a.flags & kFlagPvFp8) ? kOutFp8F16 : kOutBf16);
+  if (e == hipSuccess)
+    e = launch_tile_prepass(a.v, a.sv, a.batch, a.heads, a.lk, qv, nullptr, ws + w.vt, vp.gv, nullptr, f.stream,
+                            (a.flags & kFlagPvFp8) ? kOutFp8F16 : kOutBf16);
+  const hipError_t j = side_join(stream, f);
+  return e != hipSuccess ? e : j;
 }
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {
-  hipError_t e = launch_kv_prepass(a, 0, stream);
+  hipError_t e = launch_kv_prepass(a, 0, stream, true);
   if (e != hipSuccess) return e;
   return launch_attn_fwd_sel(a, nullptr, 0, stream);
 }

@@ -171,7 +171,19 @@ hipError_t launch_qk_delta(const AttnArgs &a, const Workspace &w, hipStream_t st
 
 // The variants' per-call quantities, then K-hat rows and V-hat tiles of every head into the
 // workspace of op 0 (dense forward) or 2 (cube-sparse forward).
-hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream);
+// The side stream of the current device (side_stream.hip).  side_fork: work enqueued on f.stream
+// from here on starts after everything already queued on `main`; f.stream is `main` itself when no
+// side stream is available.  side_join: `main` waits for that work.  Between the two, calls on the
+// same device from other host threads wait.
+struct SideFork {
+  hipStream_t stream;
+  int dev;
+};
+hipError_t side_fork(hipStream_t main, SideFork &f);
+hipError_t side_join(hipStream_t main, SideFork &f);
+// The K and V prepasses (after the variants' statistics, which both use); with `overlap`, the V
+// prepass runs on the side stream beside the K prepass, joined before this returns.
+hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream, bool overlap = false);
 // Forward kernel only (operands already in the workspace); sel: cube-sparse chunk lists
 // [B*H, lq/128, nsel] or null for dense attention.
 hipError_t launch_attn_fwd_sel(const AttnArgs &a, const int32_t *sel, int64_t nsel, hipStream_t stream);

@@ -174,11 +174,29 @@ __global__ __launch_bounds__(256) void select_kernel(const uint16_t *__restrict_
 
 }  // namespace
 
+hipError_t launch_vsa_select(const AttnArgs &a, const VsaArgs &s, const Workspace &w, hipStream_t stream);
+
 hipError_t launch_vsa_fwd(const AttnArgs &a, const VsaArgs &s, hipStream_t stream) {
   const Workspace w = workspace_layout(2, a.batch, a.heads, a.lq, a.lk);
   uint8_t *ws = (uint8_t *)a.workspace;
-  hipError_t e = launch_kv_prepass(a, 2, stream);
+  // The K/V prepass (workspace regions kq, vt) on the side stream, beside the cube means and the
+  // selection (regions pool, selw), which read only the caller's Q, K and V.
+  SideFork f;
+  hipError_t e = side_fork(stream, f);
   if (e != hipSuccess) return e;
+  e = launch_kv_prepass(a, 2, f.stream);
+  if (e == hipSuccess) e = launch_vsa_select(a, s, w, stream);
+  const hipError_t j = side_join(stream, f);
+  if (e != hipSuccess) return e;
+  if (j != hipSuccess) return j;
+  int32_t *sel = s.sel ? s.sel : (int32_t *)(ws + w.selw);
+  return launch_attn_fwd_sel(a, sel, s.topk, stream);
+}
+
+// The cube means and the coarse selection (and the coarse output when asked for).
+hipError_t launch_vsa_select(const AttnArgs &a, const VsaArgs &s, const Workspace &w, hipStream_t stream) {
+  uint8_t *ws = (uint8_t *)a.workspace;
+  hipError_t e;
   const int64_t n = s.n_cubes;
   const int64_t bhn = (int64_t)a.batch * a.heads * n;
   uint16_t *pool = (uint16_t *)(ws + w.pool);
@@ -195,8 +213,7 @@ hipError_t launch_vsa_fwd(const AttnArgs &a, const VsaArgs &s, hipStream_t strea
     return e;
   AQ_LAUNCH("vsa_select", select_kernel, dim3((unsigned)((bhn + 3) / 4)), dim3(256), smem, stream, pool, bhn, n,
                      s.topk, a.scale, sel, (uint16_t *)s.o_coarse, a.so, a.heads);
-  if ((e = hipGetLastError())) return e;
-  return launch_attn_fwd_sel(a, sel, s.topk, stream);
+  return hipGetLastError();
 }
 
 }  // namespace aq
