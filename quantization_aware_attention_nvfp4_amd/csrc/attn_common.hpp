@@ -92,6 +92,13 @@ __device__ __forceinline__ void load_lds16_sa(const void *sbase, uint32_t voff, 
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(voff), "s"(uniform_ptr(sbase))
                : "memory", "m0");
 }
+// load_lds16_sa without the "memory" clobber, for copies issued among a phase's LDS operand reads:
+// the compiler may then move those reads across the copy.  Only for a destination that no read
+// between the copy and its s_waitcnt + barrier touches (the other buffer of a double buffer).
+__device__ __forceinline__ void load_lds16_sa_free(const void *sbase, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(voff), "s"(uniform_ptr(sbase))
+               : "m0");
+}
 __device__ __forceinline__ void load_lds4_s(const void *sbase, uint32_t voff, uint8_t *lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0v), "v"(voff), "s"(uniform_ptr(sbase))

@@ -24,6 +24,8 @@
 //   permlane32 swap, the denominator is combined once at the end.
 // LDS: one K-hat chunk (32 KiB) and one V-hat^T chunk (32 KiB), 16-byte columns XOR-swizzled by
 // row so the A-operand reads of 8 lanes hit 8 different bank groups.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -598,6 +600,20 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
     if (j + 1 < n_iter) copy_k(j + 1, buf);
     if (j < n_iter) copy_v(j, buf);
   };
+  // Piece q of fill(j) as a copy the operand reads of the matrix phase may pass: q < 4 the K-hat
+  // sub-tile q of chunk j+1, else the V-hat sub-tile q-4 of chunk j, with both chunks clamped to
+  // the last one (fill(n_iter) then rewrites buffer n_iter%2, which nothing reads any more).
+  auto fill_piece = [&](int j, int q) {
+    const uint32_t buf = lds0 + (uint32_t)(j & 1) * 65536;
+    const int last = n_iter - 1;
+    if (q < 4) {
+      const int jk = j + 1 < last ? j + 1 : last;
+      load_lds16_sa_free(kbase + (int64_t)jk * 32768 + q * 8192, k_off, buf + kLdsK + q * 8192 + 1024 * wave);
+    } else {
+      const int jv = j < last ? j : last;
+      load_lds16_sa_free(vbase + (int64_t)jv * 32768 + (q - 4) * 64, v_off, buf + kLdsV + (q - 4) * 8192 + 1024 * wave);
+    }
+  };
 
   // Prologue: K-hat(0) into buffer 1's K half, iteration 0's buffer, Q-hat.
   copy_k(0, lds0 + 65536);
@@ -701,8 +717,13 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
     for (int kt = 0; kt < 4; ++kt) {
       s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kad[0] + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-      for (int t = 1; t < 8; ++t)
+      for (int t = 1; t < 8; ++t) {
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kad[t] + 8192 * kt)), qf[t], s[kt], 0, 0, 0);
+        // this wave's share of fill(it+1), spread over the first half of the phase: one copy per
+        // few MFMAs keeps the address unit from backing up, so a copy holds the wave about as
+        // long as the MFMA in flight
+        if (kt >= 1 && kt <= 2 && (t & 1)) fill_piece(it + 1, 4 * (kt - 1) + (t >> 1));
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -736,13 +757,11 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
   // end of phase 2j, before group 0's M(j) in phase 2j+1.
   if (grp == 1) __builtin_amdgcn_s_barrier();
   for (int it = 0; it < n_iter; ++it) {
-    // Iteration it+1's copies (buffer (it+1)%2, free from phase 2it+1), both in phase 2it+1: group
-    // 1 at the start of its V(it), group 0 after the MFMAs of its M(it), where it would otherwise
-    // wait for group 1 at the barrier.  A wave stays at a copy instruction until the CU's address
-    // unit takes it (1 KiB each, about 64 bytes per clock for the CU), so the four waves of a
-    // group spend about 500 cycles issuing their 32; group 0's share then costs no vector-phase
-    // time.  Both are waited for at the end of phase 2it+2.
-    if (grp == 1 && it + 1 < n_iter) fill(it + 1);
+    // Iteration it+1's copies (buffer (it+1)%2, free from phase 2it+1): each group's share among
+    // the MFMAs of its M(it) (phases 2it+1 and 2it+2).  A wave stays at a copy instruction until
+    // the CU's address unit takes it (1 KiB each, about 64 bytes per clock for the CU): issued all
+    // at once at the start of a vector phase, the four waves of a group spent about 500 cycles on
+    // their 32.  Both shares are waited for at the end of phase 2it+2.
     __builtin_amdgcn_s_setprio(0);
     vphase(it);
     if (grp == 0) AQ_WAIT_VMCNT(0);  // end of phase 2it
@@ -751,7 +770,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
     // beside it fills the remaining issue slots
     __builtin_amdgcn_s_setprio(2);
     mphase(it);
-    if (grp == 0 && it + 1 < n_iter) fill(it + 1);
     if (grp == 1) AQ_WAIT_VMCNT(0);  // end of phase 2it+2
     __builtin_amdgcn_s_barrier();
   }
@@ -1079,6 +1097,19 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
     if (j + 1 < n_iter) copy_k(j + 1, buf);
     if (j < n_iter) copy_v(j, buf);
   };
+  // Piece q of fill(j) among the matrix phase's MFMAs, chunks clamped to the last one (as in the
+  // inference kernel).
+  auto fill_piece = [&](int j, int q) {
+    const uint32_t buf = lds0 + (uint32_t)(j & 1) * 65536;
+    const int last = n_iter - 1;
+    if (q < 4) {
+      const int jk = j + 1 < last ? j + 1 : last;
+      load_lds16_sa_free(kbase + (int64_t)jk * 32768 + q * 8192, k_off, buf + kLdsK + q * 8192 + 1024 * wave);
+    } else {
+      const int jv = j < last ? j : last;
+      load_lds16_sa_free(vbase + (int64_t)jv * 32768 + (q - 4) * 64, v_off, buf + kLdsV + (q - 4) * 8192 + 1024 * wave);
+    }
+  };
 
   copy_k(0, lds0 + 65536);
   fill(0);
@@ -1196,6 +1227,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
           const f16x8 a = __builtin_bit_cast(f16x8, lds_read16(vad[j] + 8192 * kt + 2048 * dt));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
           acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, ph[kt][j]), acc_hp[dt], 0, 0, 0);
+          // this wave's share of fill(it+1), one copy per 8 MFMAs of the P.V products
+          if (dt == 1) fill_piece(it + 1, 2 * kt + j);
         }
     // each V-hat read 4 reads ahead of its two MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -1227,18 +1260,16 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
     }
   };
 
-  // The same phases and copies as the inference kernel: iteration it+1's copies by group 1 at
-  // the start of its V(it), by group 0 after the MFMAs of its M(it).
+  // The same phases and copies as the inference kernel: iteration it+1's copies among the P.V
+  // MFMAs of each group's M(it).
   if (grp == 1) __builtin_amdgcn_s_barrier();
   for (int it = 0; it < n_iter; ++it) {
-    if (grp == 1 && it + 1 < n_iter) fill(it + 1);
     __builtin_amdgcn_s_setprio(0);
     vphase(it);
     if (grp == 0) AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_setprio(2);
     mphase(it);
-    if (grp == 0 && it + 1 < n_iter) fill(it + 1);
     if (grp == 1) AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
