@@ -855,13 +855,31 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
       load_lds16_sa(vbase + c * 32768 + kt * 64, v_off, buf + kLdsV + kt * 8192 + 1024 * wave);
   };
   // The buffer of phase ph >= 1: K-hat(it+1) and V-hat(it) of group g = (ph-1)%2's iteration
-  // it = (ph-1-g)/2, when those positions exist.
-  auto fill_for = [&](int ph) {
-    if (ph < 1) return;
-    const int g = (ph - 1) & 1, it = (ph - 1 - g) >> 1;
+  // it = (ph-1-g)/2, positions clamped to the list (a buffer no later phase reads may then get
+  // a copy of a listed chunk).  It is copied during phase ph-1 by the wave group whose matrix
+  // phase that is: each of its waves copies its own 1 KiB slice of every sub-tile and that of its
+  // partner wave in the other group (row and d offsets 16 rows / 64 d apart: the partner's K
+  // column swizzle differs, its V swizzle does not), so the vector phase issues no copies.
+  uint32_t k_off2;
+  {
+    const int r = (4 * wave + (lane >> 4)) ^ 16;
+    k_off2 = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
+  }
+  const uint32_t v_off2 = v_off ^ 16384u;
+  auto buffer_chunks = [&](int ph, int64_t &ck, int64_t &cv) {
+    const int g = (ph - 1) & 1, it = (ph - 1 - g) >> 1, last = nsel - 1;
+    ck = chunk_of(g, it + 1 < last ? it + 1 : last);
+    cv = chunk_of(g, it < last ? it : last);
+  };
+  // Piece pc (0..15) of buffer ph's copies: slice (wave, then partner) pc / 8, sub-tile pc % 8
+  // (K-hat 0..3, V-hat 4..7).
+  auto fill_piece = [&](int ph, int64_t ck, int64_t cv, int pc) {
     const uint32_t buf = lds0 + (uint32_t)(ph & 1) * 65536;
-    if (it + 1 < nsel) copy_k(chunk_of(g, it + 1), buf);
-    if (it < nsel) copy_v(chunk_of(g, it), buf);
+    const int q = pc & 7, w = pc < 8 ? wave : wave ^ 4;
+    if (q < 4)
+      load_lds16_sa_free(kbase + ck * 32768 + q * 8192, pc < 8 ? k_off : k_off2, buf + kLdsK + q * 8192 + 1024 * w);
+    else
+      load_lds16_sa_free(vbase + cv * 32768 + (q - 4) * 64, pc < 8 ? v_off : v_off2, buf + kLdsV + (q - 4) * 8192 + 1024 * w);
   };
 
   // Prologue: the groups' first K-hat chunks into buffer 0's halves, Q-hat, first logits.
@@ -925,7 +943,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
   };
   // M(it) in phase phm: S of position it+1 and O^T += V-hat(it)^T P-hat(it)^T, from buffer phm%2
   // (the last position's next logits come from a stale K half and are dropped).
-  auto mphase = [&](int phm) {
+  auto mphase = [&](int phm, int64_t ck, int64_t cv) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
@@ -940,8 +958,12 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     for (int kt = 0; kt < 4; ++kt) {
       s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kad[0] + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-      for (int t = 1; t < 8; ++t)
+      for (int t = 1; t < 8; ++t) {
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kad[t] + 8192 * kt)), qf[t], s[kt], 0, 0, 0);
+        // the next buffer's copies, about one per two MFMAs over the first three quarters of
+        // the phase
+        if (t & 1) fill_piece(phm + 1, ck, cv, 4 * kt + (t >> 1));
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -964,23 +986,26 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     for (int dt = 0; dt < 4; ++dt) AQ_OPAQUE(acc[dt]);
   };
 
-  // Group g's iteration it: V(it) in phase 2it+g, M(it) in phase 2it+g+1.  Each wave issues its
-  // share of phase ph+1's copies at the start of phase ph and waits for them at its end.
+  // Group g's iteration it: V(it) in phase 2it+g, M(it) in phase 2it+g+1.  Phase ph+1's buffer
+  // is copied during phase ph by the group whose matrix phase ph is (in phase 0, by group 1, idle
+  // then) and waited for at the end of phase ph.
   if (grp == 1) {
-    fill_for(1);
+    int64_t ck, cv;
+    buffer_chunks(1, ck, cv);
+#pragma unroll
+    for (int pc = 0; pc < 16; ++pc) fill_piece(1, ck, cv, pc);
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
   for (int it = 0; it < nsel; ++it) {
     const int phv = 2 * it + grp;
-    fill_for(phv + 1);
+    int64_t ck, cv;
+    buffer_chunks(phv + 2, ck, cv);
     __builtin_amdgcn_s_setprio(0);
     vphase();
-    AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_setprio(2);
-    mphase(phv + 1);
-    fill_for(phv + 2);
+    mphase(phv + 1, ck, cv);
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
@@ -1358,14 +1383,27 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel
     for (int kt = 0; kt < 4; ++kt)
       load_lds16_sa(vbase + c * 32768 + kt * 64, v_off, buf + kLdsV + kt * 8192 + 1024 * wave);
   };
-  // The buffer of phase ph >= 1: K-hat(it+1) and V-hat(it) of group g = (ph-1)%2's iteration
-  // it = (ph-1-g)/2, when those positions exist.
-  auto fill_for = [&](int ph) {
-    if (ph < 1) return;
-    const int g = (ph - 1) & 1, it = (ph - 1 - g) >> 1;
+  // The buffer of phase ph >= 1 (K-hat(it+1) and V-hat(it) of group (ph-1)%2's iteration it,
+  // positions clamped), copied during phase ph-1 by the group whose matrix phase that is, each
+  // wave its own slice and its partner's, as in the inference kernel.
+  uint32_t k_off2;
+  {
+    const int r = (4 * wave + (lane >> 4)) ^ 16;
+    k_off2 = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
+  }
+  const uint32_t v_off2 = v_off ^ 16384u;
+  auto buffer_chunks = [&](int ph, int64_t &ck, int64_t &cv) {
+    const int g = (ph - 1) & 1, it = (ph - 1 - g) >> 1, last = nsel - 1;
+    ck = chunk_of(g, it + 1 < last ? it + 1 : last);
+    cv = chunk_of(g, it < last ? it : last);
+  };
+  auto fill_piece = [&](int ph, int64_t ck, int64_t cv, int pc) {
     const uint32_t buf = lds0 + (uint32_t)(ph & 1) * 65536;
-    if (it + 1 < nsel) copy_k(chunk_of(g, it + 1), buf);
-    if (it < nsel) copy_v(chunk_of(g, it), buf);
+    const int q = pc & 7, w = pc < 8 ? wave : wave ^ 4;
+    if (q < 4)
+      load_lds16_sa_free(kbase + ck * 32768 + q * 8192, pc < 8 ? k_off : k_off2, buf + kLdsK + q * 8192 + 1024 * w);
+    else
+      load_lds16_sa_free(vbase + cv * 32768 + (q - 4) * 64, pc < 8 ? v_off : v_off2, buf + kLdsV + (q - 4) * 8192 + 1024 * w);
   };
 
   // Prologue: the groups' first K-hat chunks into buffer 0's halves, Q-hat codes, first logits.
@@ -1459,7 +1497,7 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel
   // M(it) in phase phm: O^T += V-hat(it)^T P-hat(it)^T and O^hp^T += V-hat(it)^T P(it)^T, then S
   // of position it+1, from buffer phm%2 (the last position's next logits come from a stale K half
   // and are dropped).
-  auto mphase = [&](int phm) {
+  auto mphase = [&](int phm, int64_t ck, int64_t cv) {
     const uint32_t buf = (uint32_t)(phm & 1) * 65536;
     uint32_t vad[2];
 #pragma unroll
@@ -1473,6 +1511,8 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel
           const f16x8 a = __builtin_bit_cast(f16x8, lds_read16(vad[j] + 8192 * kt + 2048 * dt));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
           acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, ph[kt][j]), acc_hp[dt], 0, 0, 0);
+          // the next buffer's copies, one per four MFMAs of the P.V products
+          if (dt & 1) fill_piece(phm + 1, ck, cv, 4 * kt + 2 * j + (dt >> 1));
         }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -1500,23 +1540,26 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel
     }
   };
 
-  // Group g's iteration it: V(it) in phase 2it+g, M(it) in phase 2it+g+1.  Each wave issues its
-  // share of phase ph+1's copies at the start of phase ph and waits for them at its end.
+  // Group g's iteration it: V(it) in phase 2it+g, M(it) in phase 2it+g+1.  Phase ph+1's buffer
+  // is copied during phase ph by the group whose matrix phase ph is (in phase 0, by group 1) and
+  // waited for at the end of phase ph.
   if (grp == 1) {
-    fill_for(1);
+    int64_t ck, cv;
+    buffer_chunks(1, ck, cv);
+#pragma unroll
+    for (int pc = 0; pc < 16; ++pc) fill_piece(1, ck, cv, pc);
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
   for (int it = 0; it < nsel; ++it) {
     const int phv = 2 * it + grp;
-    fill_for(phv + 1);
+    int64_t ck, cv;
+    buffer_chunks(phv + 2, ck, cv);
     __builtin_amdgcn_s_setprio(0);
     vphase(it);
-    AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_setprio(2);
-    mphase(phv + 1);
-    fill_for(phv + 2);
+    mphase(phv + 1, ck, cv);
     AQ_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
   }
