@@ -570,53 +570,38 @@ struct DkdvLane {
   int r_off;     // Q-hat/dO B-operand row qloc, column hf
   int tr_off;    // transposed reads, query group a = 0; bits 6..7 hold e (d tile dt enters as ^ 64*dt)
   int qloc;      // tile-local query of this lane's S^T column
-  uint32_t q_voff, o_voff;  // copy offsets of this lane's first Q-hat and dO row of a tile
-  int o_row;                // that row, tile-local (the lane's others are 16, 32 and 48 below)
+  uint32_t q_voff[2], o_voff[2];  // copy offsets of this lane's two Q-hat and dO rows of a tile
+  int o_row[2];  // those rows, tile-local
   int key_base;  // head-local key of register 0
 };
 
 // Copies of tile qb into buffer `buf`: Q-hat rows from the workspace, dO rows from the caller's
-// tensor (rows past lq read bytes of row lq-1; every product they feed is masked), and the three
+// tensor (rows past lq repeat row lq-1; every product they feed is masked), and the three
 // per-query statistics (entries past lq repeat entry lq-1), plus P's two-level scales when there
-// are any; cm_row is the chunk-max row of the key chunk for these queries.
-// Only one wave per SIMD copies a tile: buffer 1 is filled by waves 0..3, buffer 0 by waves 4..7.
-// A wave stays at a copy instruction until the CU's address unit takes it (1 KiB per instruction,
-// about 64 bytes per clock for the CU), so a tile's 32 KiB hold the copying waves for about 500
-// cycles; meanwhile their partners on the same SIMDs compute, and the halves alternate tiles.
-// Per lane of a copying wave w (mod 4): the Q-hat and dO pieces w, w+4, w+8, w+12 (rows 16 apart,
-// so one swizzled column), plus one 4-byte copy in waves 0..2 (and in wave 3 under two-level P).
+// are any; cm_row is the chunk-max row of the key chunk for these queries.  Per lane: 4 copies of
+// 16 bytes, plus one 4-byte copy in waves 0..2 (and in wave 3 under two-level P).
 __device__ __forceinline__ void dkdv_stage_tile(const BwdParams &p, const DkdvLane &ln, int64_t bh, int64_t bb,
                                                 int64_t hh, int64_t cm_row, int64_t qb, uint8_t *lds, int buf,
                                                 int wave, int lane) {
-  if ((__builtin_amdgcn_readfirstlane(wave) >> 2) != (buf ^ 1)) return;  // a branch, not a lane mask
-  const int w4 = wave & 3;
   uint8_t *rq = lds + kLdsR + buf * 32768, *ro = rq + 16384;
   const u32x4 *qsrc = p.qq + (bh * p.Cq * kChunk + qb * kQT) * (kD / 8);
   const uint16_t *osrc = p.d_o + bb * p.sdo.b + hh * p.sdo.h + qb * kQT * p.sdo.l;
   const int64_t rem = p.lq - 1 - qb * kQT;  // last valid tile-local row
-  // Piece i's rows are 16*i below the first: the step rides in the (scalar) base address.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_lds16_s(qsrc + 256 * i, ln.q_voff, rq + (i * 4 + w4) * 1024);
-  if (rem >= kQT - 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) load_lds16_s(osrc + 16 * i * p.sdo.l, ln.o_voff, ro + (i * 4 + w4) * 1024);
-  } else {  // tail tile: rows past the last valid one read bytes of that row instead
-    // (finite values; every product they feed is masked).  A lane's offset is at most
-    // rem * row_bytes + 240 exactly when its row is at most rem, so one minimum clamps it.
-    const uint32_t orow_bytes = (uint32_t)(p.sdo.l * 2), lim = (uint32_t)rem * orow_bytes + 240u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t ov = ln.o_voff + 16u * orow_bytes * i;
-      load_lds16_s(osrc, ov < lim ? ov : lim, ro + (i * 4 + w4) * 1024);
-    }
+  for (int i = 0; i < 2; ++i) {
+    load_lds16_s(qsrc, ln.q_voff[i], rq + (i * 8 + wave) * 1024);
+    uint32_t ov = ln.o_voff[i];
+    if (rem < kQT - 1 && ln.o_row[i] > rem)  // tail tile: repeat the last valid row
+      ov = (uint32_t)(rem * p.sdo.l * 2) + (ln.o_voff[i] - (uint32_t)(ln.o_row[i] * p.sdo.l * 2));
+    load_lds16_s(osrc, ov, ro + (i * 8 + wave) * 1024);
   }
-  if (w4 < 3 || (w4 == 3 && p.pg)) {
-    const float *src = (w4 == 0   ? p.cmax + cm_row * p.lq
-                        : w4 == 3 ? p.pg + cm_row * p.lq
-                                  : (w4 == 1 ? p.lse : p.dvec) + bh * p.lq) +
+  if (wave < 3 || (wave == 3 && p.pg)) {
+    const float *src = (wave == 0   ? p.cmax + cm_row * p.lq
+                        : wave == 3 ? p.pg + cm_row * p.lq
+                                    : (wave == 1 ? p.lse : p.dvec) + bh * p.lq) +
                        qb * kQT;
     const int q = lane < rem ? lane : (int)(rem < 0 ? 0 : rem);
-    load_lds4_s(src, (uint32_t)q * 4u, lds + kLdsStat + buf * 1024 + w4 * 256);
+    load_lds4_s(src, (uint32_t)q * 4u, lds + kLdsStat + buf * 1024 + wave * 256);
   }
 }
 
@@ -804,12 +789,13 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
     const int e = (lane >> 2) & 3, j = lane & 3, g = (lane >> 4) & 1;
     const int lo = (2 * g + (j >> 1)) ^ (2 * hf);
     ln.tr_off = (32 * qh + 8 * hf + e) * 256 + 64 * e + 16 * lo + 8 * (j & 1);
-    {
-      const int r = (wave & 3) * 4 + (lane >> 4);
-      const int jc = (lane & 15) ^ sw_qr(r);  // sw_qr depends on r mod 16 only
-      ln.o_row = r;
-      ln.q_voff = (uint32_t)(r * 256 + jc * 16);
-      ln.o_voff = (uint32_t)(r * p.sdo.l * 2 + jc * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = (i * 8 + wave) * 4 + (lane >> 4);
+      const int jc = (lane & 15) ^ sw_qr(r);
+      ln.o_row[i] = r;
+      ln.q_voff[i] = (uint32_t)(r * 256 + jc * 16);
+      ln.o_voff[i] = (uint32_t)(r * p.sdo.l * 2 + jc * 16);
     }
   }
   ln.key_base = (int)(kc * kChunk) + kg * 32 + 16 * hf;
