@@ -1122,19 +1122,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
     if (j + 1 < n_iter) copy_k(j + 1, buf);
     if (j < n_iter) copy_v(j, buf);
   };
-  // Piece q of fill(j) among the matrix phase's MFMAs, chunks clamped to the last one (as in the
-  // inference kernel).
-  auto fill_piece = [&](int j, int q) {
-    const uint32_t buf = lds0 + (uint32_t)(j & 1) * 65536;
-    const int last = n_iter - 1;
-    if (q < 4) {
-      const int jk = j + 1 < last ? j + 1 : last;
-      load_lds16_sa_free(kbase + (int64_t)jk * 32768 + q * 8192, k_off, buf + kLdsK + q * 8192 + 1024 * wave);
-    } else {
-      const int jv = j < last ? j : last;
-      load_lds16_sa_free(vbase + (int64_t)jv * 32768 + (q - 4) * 64, v_off, buf + kLdsV + (q - 4) * 8192 + 1024 * wave);
-    }
-  };
 
   copy_k(0, lds0 + 65536);
   fill(0);
@@ -1252,8 +1239,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
           const f16x8 a = __builtin_bit_cast(f16x8, lds_read16(vad[j] + 8192 * kt + 2048 * dt));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
           acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, ph[kt][j]), acc_hp[dt], 0, 0, 0);
-          // this wave's share of fill(it+1), one copy per 8 MFMAs of the P.V products
-          if (dt == 1) fill_piece(it + 1, 2 * kt + j);
         }
     // each V-hat read 4 reads ahead of its two MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -1285,10 +1270,15 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
     }
   };
 
-  // The same phases and copies as the inference kernel: iteration it+1's copies among the P.V
-  // MFMAs of each group's M(it).
+  // The phases of the inference kernel.  Here the matrix phase is the longer one (96 MFMAs and
+  // the Q-hat decode against about 3900 cycles of vector work), so the copies go where the vector
+  // phase leaves time: iteration it+1's by group 1 at the start of its V(it) (phase 2it+1), by
+  // group 0 at the start of its V(it+1) (phase 2it+2); both are waited for at the end of phase
+  // 2it+2.
   if (grp == 1) __builtin_amdgcn_s_barrier();
   for (int it = 0; it < n_iter; ++it) {
+    if (grp == 1 && it + 1 < n_iter) fill(it + 1);
+    if (grp == 0 && it >= 1) fill(it);
     __builtin_amdgcn_s_setprio(0);
     vphase(it);
     if (grp == 0) AQ_WAIT_VMCNT(0);
