@@ -1836,6 +1836,15 @@ hipError_t launch_kv_prepass(const AttnArgs &a, int op, hipStream_t stream, bool
   uint8_t *ws = (uint8_t *)a.workspace;
   hipError_t e = launch_variant_prep(a, w, stream);
   if (e != hipSuccess) return e;
+  const VariantPtrs vp0 = variant_ptrs(a, w);
+  const bool kq = (a.flags & kFlagK) != 0 && !vp0.gk && !vp0.kmean;
+  const bool vq = (a.flags & kFlagV) != 0 && !vp0.gv && !(a.flags & kFlagPvFp8);
+  if (kq && vq) {
+    // the common case: both operands under unit scales, one streamed launch
+    e = launch_kv_stream(a.k, a.sk, a.v, a.sv, a.batch, a.heads, a.lk, 0, (int64_t)a.batch * a.heads, ws + w.kq,
+                         pp_train_ok(a), ws + w.vt, use_f16_unit(a.flags), stream);
+    return e != hipSuccess ? e : launch_qk_delta(a, w, stream);
+  }
   SideFork f{stream, -1};
   if (overlap && (e = side_fork(stream, f)) != hipSuccess) return e;
   const VariantPtrs vp = variant_ptrs(a, w);

@@ -156,6 +156,14 @@ hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads,
                                TileQuant quant, void *rows_out, void *tiles_out, const float *g,
                                const float *mean, hipStream_t stream, TileOut out = kOutBf16);
 
+// Under unit scales without smoothing: K-hat rows (quantized along d; fp16 or bf16 values) and
+// V-hat d-major tiles (quantized along rows; fp16 or bf16 values) of the heads [bh0, bh0 + nbh)
+// of the flattened batch*heads, in one streamed launch (the layouts and values of
+// launch_tile_prepass with kQuantD / kOutF16|kOutBf16 for K and kQuantRows(F16) / kOutBf16 for V).
+hipError_t launch_kv_stream(const void *k, Strides sk, const void *v, Strides sv, int batch, int heads, int64_t L,
+                            int64_t bh0, int64_t nbh, void *krows, bool kf16, void *vtiles, bool vf16,
+                            hipStream_t stream);
+
 // The per-call quantities of the variants, into the workspace regions scal / kmean / kpart: the
 // smooth-K key means (a.flags & kFlagSmoothK), then the static global scales of Q, K (of the
 // smoothed keys) and V (kFlagGsfQkv) and of P (kFlagGsfP).  A no-op without those flags.

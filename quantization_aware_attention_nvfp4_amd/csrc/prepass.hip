@@ -186,18 +186,20 @@ __global__ __launch_bounds__(256) void tile_prepass(const uint16_t *__restrict__
 
 // The common row case (D-axis blocks under the unit scale, no smoothing, bf16 or fp16 values) as
 // a stream: one lane per 16-byte piece (8 values) of an output row, two neighbouring lanes per
-// 16-value block exchanging their partial abs-max through one DPP move, one-wave workgroups (the
-// standalone fake quantizer's arrangement); rows past L come out zero.  The values are those of
-// tile_prepass: the same scale, quotient and E2M1 rounding, the input's sign kept on zeros.
-__global__ __launch_bounds__(64) void rows_prepass(const uint16_t *__restrict__ src, Strides s, int heads, int64_t L,
-                                                   int64_t C, int64_t n8, u32x4 *__restrict__ rows_out, int f16) {
-  const int64_t j = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (j >= n8) return;  // n8 is a multiple of 64: whole waves only, so every lane's partner is live
+// 16-value block exchanging their partial abs-max through one DPP move (the standalone fake
+// quantizer's arrangement); rows past L come out zero.  The values are those of tile_prepass: the
+// same scale, quotient and E2M1 rounding, the input's sign kept on zeros.  j: the piece's index
+// over all rows of all heads; whole waves only, so every lane's partner is live.
+__device__ __forceinline__ u32x4 rows_load(const uint16_t *__restrict__ src, Strides s, int heads, int64_t L,
+                                           int64_t C, int64_t j) {
   const int64_t row = j >> 4, part = j & 15;
   const int64_t bh = row / (C * kChunk), r = row % (C * kChunk);
   const int64_t b = bh / heads, h = bh % heads;
   u32x4 v = {0u, 0u, 0u, 0u};
   if (r < L) v = __builtin_nontemporal_load((const u32x4 *)(src + b * s.b + h * s.h + r * s.l + part * 8));
+  return v;
+}
+__device__ __forceinline__ void rows_store(u32x4 v, int64_t j, u32x4 *__restrict__ rows_out, int f16) {
   float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y), bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
   float am = 0.0f;
 #pragma unroll
@@ -223,6 +225,96 @@ __global__ __launch_bounds__(64) void rows_prepass(const uint16_t *__restrict__ 
   __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, rows_out + j);
 }
 
+__global__ __launch_bounds__(64) void rows_prepass(const uint16_t *__restrict__ src, Strides s, int heads, int64_t L,
+                                                   int64_t C, int64_t n8, u32x4 *__restrict__ rows_out, int f16) {
+  const int64_t j = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (j >= n8) return;  // n8 is a multiple of 64
+  rows_store(rows_load(src, s, heads, L, C, j), j, rows_out, f16);
+}
+
+// V-hat of one 128-row chunk (blocks of 16 rows per column under the unit scale), d-major: wave w
+// loads rows [32w, 32w+32) of columns 2*lane and 2*lane+1 (one 32-bit load per row: 256
+// contiguous bytes per row and wave), quantizes its two 16-row blocks of each column in registers
+// and writes the column's 32 values into the LDS tile [128 d][128 rows]; after one barrier every
+// wave stores four whole 256-byte tile rows per instruction.  The tile's 16-byte pieces are
+// swizzled by d (physical piece = piece ^ ((d >> 1) & 15)), so the 16 lanes of one LDS access
+// touch 16 different piece positions: all 64 banks, no conflicts.  Rows past L read as zero.  The
+// values are tile_prepass's for kQuantRows (bf16) and kQuantRowsF16 (fp16) under the unit scale:
+// the same blocks, scale, quotient and rounding.
+__device__ __forceinline__ uint32_t vt_piece(int d, int piece) {
+  return (uint32_t)(d * 256 + ((piece ^ ((d >> 1) & 15)) << 4));
+}
+__device__ __forceinline__ void vtile_chunk(const uint16_t *__restrict__ src, Strides s, int heads, int64_t L,
+                                            int64_t C, int64_t chunk, uint16_t *__restrict__ tiles_out, int f16,
+                                            uint8_t *lds) {
+  const int64_t bh = chunk / C, c = chunk % C;
+  const int64_t b = bh / heads, h = bh % heads;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r0 = c * kChunk + 32 * wave;
+  const uint16_t *base = src + b * s.b + h * s.h + 2 * lane;
+  uint32_t x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    x[i] = r0 + i < L ? __builtin_nontemporal_load((const uint32_t *)(base + (r0 + i) * s.l)) : 0u;
+#pragma unroll
+  for (int col = 0; col < 2; ++col) {
+    uint32_t w[16];  // the column's 32 values, two per word, in row order
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      float f[16];
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        f[i] = col ? bf16hi(x[16 * blk + i]) : bf16lo(x[16 * blk + i]);
+        am = fmaxf(am, __builtin_fabsf(f[i]));
+      }
+      const float S = block_scale_unit(am);
+      const float inv = S == 0.0f ? 0.0f : recip_e4m3(S);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        fq_unit_pair(f[i], f[i + 1], S, inv);
+        w[8 * blk + i / 2] =
+            f16 ? ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[i]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[i + 1]) << 16))
+                : ((f2u(f[i]) >> 16) | (f2u(f[i + 1]) & 0xFFFF0000u));
+      }
+    }
+    const int d = 2 * lane + col;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(u32x4 *)(lds + vt_piece(d, 4 * wave + q)) = u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+  }
+  __syncthreads();
+  // instruction i of wave w: tile rows d = 16i + 4w + lane/16, piece lane%16
+  u32x4 *dst = (u32x4 *)(tiles_out + (bh * C + c) * kD * kChunk);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int d = 16 * i + 4 * wave + (lane >> 4), piece = lane & 15;
+    __builtin_nontemporal_store(*(const u32x4 *)(lds + vt_piece(d, piece)), dst + d * 16 + piece);
+  }
+}
+
+// K-hat rows and V-hat tiles of heads [bh0, bh0 + nbh) in one launch: the first kblocks
+// workgroups stream K rows (64 rows each: four 16-byte pieces per lane, loaded together), the rest
+// one V chunk each.
+__global__ __launch_bounds__(256) void kv_prepass(const uint16_t *__restrict__ k, Strides sk,
+                                                  const uint16_t *__restrict__ v, Strides sv, int heads, int64_t L,
+                                                  int64_t C, int64_t bh0, int64_t kblocks,
+                                                  u32x4 *__restrict__ krows, int kf16,
+                                                  uint16_t *__restrict__ vtiles, int vf16) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kD * kChunk * 2];
+  if ((int64_t)blockIdx.x < kblocks) {
+    const int64_t j0 = (bh0 * C * kChunk + (int64_t)blockIdx.x * 64) * 16 + threadIdx.x;
+    u32x4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = rows_load(k, sk, heads, L, C, j0 + 256 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rows_store(x[i], j0 + 256 * i, krows, kf16);
+    return;
+  }
+  vtile_chunk(v, sv, heads, L, C, bh0 * C + ((int64_t)blockIdx.x - kblocks), vtiles, vf16, lds);
+}
+
 }  // namespace
 
 hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads, int64_t L,
@@ -239,6 +331,20 @@ hipError_t launch_tile_prepass(const void *src, Strides s, int batch, int heads,
   AQ_LAUNCH("tile_prepass", tile_prepass, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t *)src, s, heads, L, C, (int)quant, (u32x4 *)rows_out,
                      (uint16_t *)tiles_out, g, mean, (int)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_stream(const void *k, Strides sk, const void *v, Strides sv, int batch, int heads, int64_t L,
+                            int64_t bh0, int64_t nbh, void *krows, bool kf16, void *vtiles, bool vf16,
+                            hipStream_t stream) {
+  const int64_t C = (L + kChunk - 1) / kChunk;
+  if (bh0 < 0 || nbh < 0 || bh0 + nbh > (int64_t)batch * heads) return hipErrorInvalidValue;
+  if (nbh == 0 || C == 0) return hipSuccess;
+  const int64_t kblocks = nbh * C * (kChunk / 64);  // 64 K rows per workgroup
+  const int64_t blocks = kblocks + nbh * C;
+  AQ_LAUNCH("kv_prepass", kv_prepass, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint16_t *)k, sk,
+            (const uint16_t *)v, sv, heads, L, C, bh0, kblocks, (u32x4 *)krows, (int)kf16, (uint16_t *)vtiles,
+            (int)vf16);
   return hipGetLastError();
 }
 
