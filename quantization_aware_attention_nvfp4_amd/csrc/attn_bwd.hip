@@ -912,6 +912,336 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Ping-pong dK/dV (dense calls without a global P scale or smooth-Q)
+// ---------------------------------------------------------------------------------------------
+// bwd_dkdv_kernel's work and arithmetic (same units, pieces, operands and per-element operations),
+// scheduled as the forward's ping-pong kernels are.  Wave group g (waves 4g .. 4g+3, one per SIMD,
+// key group kg = wave % 4) owns query half g of every 64-query tile, and the two groups run one
+// phase apart, each alternating
+//   matrix phase M(t): dK/dV += the products of tile t-1 (transposed Q-hat and dO reads against
+//                      the key-major A-hat and dS operands of V(t-1)), then S^T and dP^T of tile t;
+//   vector phase V(t): masks, P-hat and dS of tile t and their one-hot transpositions;
+// so on every SIMD one group's MFMAs run beside the other group's vector work, with one workgroup
+// barrier per phase (group 0 runs M(0) V(0) M(1) ... V(T-1) M(T) and idles last, group 1 idles
+// first; M(0) adds zero operands, M(T)'s S^T and dP^T are dropped).  A group reads only its own 32
+// rows of a tile buffer, so the halves are independent: the group in its matrix phase copies the
+// other group's next tile half (16 KiB of Q-hat and dO rows and its three statistics) among its
+// MFMAs, into the half that group finished reading in its last matrix phase, and waits for the
+// copies before the phase's closing barrier.
+// LDS (bytes):
+//   [0, 64K)         K-hat and V-hat rows of the chunk (as in bwd_dkdv_kernel)
+//   [64K, 128K)      two tile buffers, Q-hat rows [64][256 B] then dO rows [64][256 B], sw_qr
+//   [128K, +3K)      statistics [buffer][group][chunk max, lse, D][64 floats] (entries 32..63 of
+//                    a group repeat 0..31)
+//   [128K+3K, +2K)   the two one-hot B operands
+constexpr int kPPStat = 131072;
+constexpr int kPPOneHot = kPPStat + 2 * 1536;
+constexpr int kDkdvPPLds = kPPOneHot + 2048;
+
+__global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kDkdvPPLds];
+  const uint32_t lds0 = lds_addr(lds);
+  int64_t vid, piece = -1;
+  if ((int64_t)blockIdx.x < p.full_blocks) {
+    vid = xcd_work_id(blockIdx.x, p.per_xcd, p.nfull);
+    if (vid < 0) return;
+  } else {
+    piece = (int64_t)blockIdx.x - p.full_blocks;
+    vid = p.nfull + piece / p.split;
+  }
+  const int64_t bh = vid / p.Ck;
+  const int64_t kc = vid % p.Ck;
+  const int64_t bb = bh / p.heads, hh = bh % p.heads;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3, grp = wave >> 2, other = grp ^ 1;
+  const int64_t nqt = (p.lq + kQT - 1) / kQT;
+  int64_t qt0 = p.causal ? (kc * kChunk) / kQT : 0;
+  int64_t ntiles = nqt - qt0;
+  if (piece >= 0) {
+    const int64_t j = piece % p.split, lo = ntiles * j / p.split, hi = ntiles * (j + 1) / p.split;
+    qt0 += lo;
+    ntiles = hi - lo;
+  }
+  const int T = (int)ntiles;
+
+  DkdvLane ln;
+  {
+    const int krow = kg * 32 + perm_row(n), swk = sw_kq(krow);
+    ln.k_off = krow * 256 + 16 * ((hf ^ swk) & 1) + 32 * (swk >> 1);
+    ln.qloc = 32 * grp + pi_q(n);
+    const int swq = sw_qr(ln.qloc);
+    ln.r_off = ln.qloc * 256 + 16 * ((hf ^ swq) & 1) + 32 * (swq >> 1);
+    const int e = (lane >> 2) & 3, j = lane & 3, g = (lane >> 4) & 1;
+    const int lo = (2 * g + (j >> 1)) ^ (2 * hf);
+    ln.tr_off = (32 * grp + 8 * hf + e) * 256 + 64 * e + 16 * lo + 8 * (j & 1);
+  }
+  ln.key_base = (int)(kc * kChunk) + kg * 32 + 16 * hf;
+  // Copy `what` (0..3: Q-hat / dO rows of step i = what/2; 4: a statistic) of the other group's
+  // half of tile t into buffer t%2: this wave's rows 32*other + 4*(kg + 4i) + lane/16, and
+  // statistic min(kg, 2) (wave 3 rewrites D with the same values).  dO rows and statistics past
+  // lq repeat the last valid one.  Offsets are formed here, not held across the loop.
+  const int stat_k = kg < 2 ? kg : 2;
+  const float *stat_src = stat_k == 0 ? p.cmax + (bh * p.Ck + kc) * p.lq : (stat_k == 1 ? p.lse : p.dvec) + bh * p.lq;
+  auto copy_piece = [&](int t, int what) {
+    const int64_t qb = qt0 + t;
+    const int rem = (int)(p.lq - 1 - qb * kQT);
+    const uint32_t rq = lds0 + kLdsR + (uint32_t)(t & 1) * 32768;
+    if (what < 4) {
+      const int i = what >> 1;
+      const int r = 32 * other + 4 * (kg + 4 * i) + (lane >> 4);
+      const uint32_t jc16 = (uint32_t)(((lane & 15) ^ sw_qr(r)) << 4);
+      const uint32_t dst = rq + (uint32_t)(8 * other + kg + 4 * i) * 1024;
+      if ((what & 1) == 0) {
+        load_lds16_sa_free(p.qq + (bh * p.Cq * kChunk + qb * kQT) * (kD / 8), (uint32_t)r * 256u + jc16, dst);
+      } else {
+        const int rr = r < rem ? r : rem;
+        load_lds16_sa_free(p.d_o + bb * p.sdo.b + hh * p.sdo.h + qb * kQT * p.sdo.l,
+                           (uint32_t)(rr * p.sdo.l * 2) + jc16, dst + 16384);
+      }
+    } else {
+      const int q = 32 * other + (lane & 31);
+      const int qe = q < rem ? q : rem;
+      load_lds4_sa_free(stat_src + qb * kQT, (uint32_t)qe * 4u,
+                        lds0 + kPPStat + (uint32_t)(t & 1) * 1536 + other * 768 + stat_k * 256);
+    }
+  };
+
+  // This chunk's K-hat and V-hat rows, the one-hot operands, and group 0's half of tile 0.
+  {
+    const u32x4 *ks = p.kq + (bh * p.Ck + kc) * (kChunk * kD / 8);
+    const u32x4 *vs = p.vq + (bh * p.Ck + kc) * (kChunk * kD / 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (i * 8 + wave) * 4 + (lane >> 4);
+      const uint32_t off = (uint32_t)(r * 256 + (((lane & 15) ^ sw_kq(r)) << 4));
+      load_lds16_s(ks, off, lds + (i * 8 + wave) * 1024);
+      load_lds16_s(vs, off, lds + 32768 + (i * 8 + wave) * 1024);
+    }
+    if (wave == 0) {
+      *(bf16x8 *)(lds + kPPOneHot + lane * 16) = onehot_b(lane, 0);
+      *(bf16x8 *)(lds + kPPOneHot + 1024 + lane * 16) = onehot_b(lane, 1);
+    }
+    if (T > 0 && grp == 1) {
+#pragma unroll
+      for (int w = 0; w < 5; ++w) copy_piece(0, w);
+    }
+  }
+  AQ_WAIT_VMCNT(0);
+  __syncthreads();
+  // The wave's K-hat A operands stay in registers for the whole loop.
+  bf16x8 kfr[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) kfr[u] = as_bf16x8(lds_read16((lds0 + ln.k_off) ^ (32 * u)));
+
+  const bool tail = (kc + 1) * kChunk > p.lk;
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+  f32x16 s = f32x16{}, dp = f32x16{};
+  bf16x8 ba[2], bs[2];  // key-major A-hat and dS of the last vector phase (zero before the first)
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    ba[s2] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    bs[s2] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+
+  // M(t): dK/dV of tile t-1 (t = 0: zero operands against tile 0), then S^T and dP^T of tile t
+  // (t = T: tile T-1 again, dropped); copies of the other group's tile t+grp among the MFMAs.
+  // Operands are read one step ahead of their MFMAs (a step: the two MFMAs of one (s2, dt) of
+  // dK/dV, or of one k-slot of S^T and dP^T).
+  auto mphase = [&](int t) {
+    const int t2 = t >= 1 ? t - 1 : 0, t1 = t < T ? t : T - 1;
+    uint32_t ta0 = lds0 + kLdsR + (uint32_t)(t2 & 1) * 32768 + ln.tr_off;
+    uint32_t va = lds0 + 32768 + ln.k_off, ra = lds0 + kLdsR + (uint32_t)(t1 & 1) * 32768 + ln.r_off;
+    AQ_OPAQUE(va);  // per-step addresses formed in the phase, not held across the loop
+    const int tc = t + grp < T ? t + grp : T - 1;  // past the last tile: tile T-1 again (same bytes)
+    u32x4 opo[2], opq[2];      // dK/dV A operands (transposed dO and Q-hat reads), by step parity
+    u32x4 bq[2], av[2], bo[2];  // S^T / dP^T operands, by step parity
+    auto load_m2 = [&](int g, int b) {
+      const int s2 = g >> 2, dt = g & 3;
+      const uint32_t a0 = ta0 ^ (dt << 6), a1 = ta0 ^ ((dt << 6) | 16);
+      const uint32_t s2o = s2 * 4096;
+      const uint2 o0 = ds_read_tr16_at(a0 + 16384 + s2o), o1 = ds_read_tr16_at(a1 + 16384 + s2o + 1024);
+      const uint2 q0 = ds_read_tr16_at(a0 + s2o), q1 = ds_read_tr16_at(a1 + s2o + 1024);
+      opo[b] = u32x4{o0.x, o0.y, o1.x, o1.y};
+      opq[b] = u32x4{q0.x, q0.y, q1.x, q1.y};
+    };
+    auto load_m1 = [&](int u, int b) {
+      const uint32_t rt = ra ^ (32 * u);
+      bq[b] = lds_read16(rt);
+      av[b] = lds_read16(va ^ (32 * u));
+      bo[b] = lds_read16(rt + 16384);
+    };
+    load_m2(0, 0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (g < 7) load_m2(g + 1, (g + 1) & 1);
+      else load_m1(0, 0);
+      const int s2 = g >> 2, dt = g & 3;
+      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opo[g & 1]), ba[s2], dv[dt], 0, 0, 0);
+      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opq[g & 1]), bs[s2], dk[dt], 0, 0, 0);
+      if (g < 5) copy_piece(tc, g);
+    }
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < 7) load_m1(u + 1, (u + 1) & 1);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[u], as_bf16x8(bq[u & 1]), s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[u & 1]), as_bf16x8(bo[u & 1]), dp, 0, 0, 0);
+    }
+    // DS reads one step ahead: 4 before the first MFMA, then 2 after each dK/dV MFMA (the last
+    // step's slots take S^T / dP^T step 0's three), then 2 and 1 after the two MFMAs of each S^T /
+    // dP^T step.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 15) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j < 14 && (j & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (j < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    AQ_OPAQUE(s);
+    AQ_OPAQUE(dp);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      AQ_OPAQUE(dk[dt]);
+      AQ_OPAQUE(dv[dt]);
+    }
+  };
+
+  // V(t): P-hat and dS of tile t exactly as bwd_dkdv_kernel forms them, moved to one key per lane.
+  auto vphase = [&](int t) {
+    const int64_t qb = qt0 + t;
+    const uint32_t sta = lds0 + kPPStat + (uint32_t)(t & 1) * 1536 + grp * 768 + 4 * pi_q(n);
+    const float mc = lds_read_f32(sta), lse2 = lds_read_f32(sta + 256), Di = lds_read_f32(sta + 512);
+    const int qrow = (int)(qb * kQT) + ln.qloc;
+    const int lq = (int)p.lq;
+    if (tail || qrow >= lq || (p.causal && ln.key_base + 15 > qrow)) {
+      const int last = qrow >= lq ? -1 : (p.causal && qrow < (int)p.lk - 1 ? qrow : (int)p.lk - 1);
+      mask_tail(s, valid_prefix(ln.key_base, last));
+    }
+    float bm = s[0];
+#pragma unroll
+    for (int rr = 1; rr < 16; ++rr) bm = fmaxf(bm, s[rr]);
+    const float w = __builtin_amdgcn_exp2f(mc - lse2);
+    float ah[16], ds[16];
+    if (p.quant_p) {
+      const ProbBlock pb = prob_block(bm, p.c, mc);
+      const float sw = pb.Sd * w, swD = sw * Di;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        ah[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -pb.mb));
+        ds[rr] = ah[rr] * __builtin_fmaf(sw, dp[rr], -swD);
+      }
+      const uint32_t c0 = e2m1_codes8(ah), c1 = e2m1_codes8(ah + 8);
+      e2m1_decode8(c0, pb.S * w, ah);
+      e2m1_decode8(c1, pb.S * w, ah + 8);
+    } else {
+      const float wD = w * Di;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        ah[rr] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], p.c, -mc));
+        ds[rr] = ah[rr] * __builtin_fmaf(w, dp[rr], -wD);
+        ah[rr] *= w;
+      }
+    }
+    const uint32_t oh = lds0 + kPPOneHot + 16 * lane;
+    const bf16x8 one0 = as_bf16x8(lds_read16(oh)), one1 = as_bf16x8(lds_read16(oh + 1024));
+    f32x16 ta = f32x16{}, ts = f32x16{};
+    ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ah), one0, ta, 0, 0, 0);
+    ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ah + 8), one1, ta, 0, 0, 0);
+    ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds), one0, ts, 0, 0, 0);
+    ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds + 8), one1, ts, 0, 0, 0);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float fa[8], fs[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        fa[kk] = ta[8 * s2 + kk];
+        fs[kk] = ts[8 * s2 + kk];
+      }
+      ba[s2] = pack8_exact(fa);
+      bs[s2] = pack8_exact(fs);
+      AQ_OPAQUE(ba[s2]);
+      AQ_OPAQUE(bs[s2]);
+    }
+  };
+
+  if (T > 0) {
+    if (grp == 1) __syncthreads();  // group 1 idles in the first phase
+    for (int t = 0; t <= T; ++t) {
+      __builtin_amdgcn_s_setprio(2);
+      mphase(t);
+      AQ_WAIT_VMCNT(0);  // this wave's copies for the other group
+      __syncthreads();
+      if (t < T) {
+        __builtin_amdgcn_s_setprio(0);
+        vphase(t);
+        __syncthreads();
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (grp == 0) __syncthreads();  // group 0 idles in the last phase
+  }
+
+  // The two waves of a key group add their partial sums (as bwd_dkdv_kernel): group 0 finishes
+  // dK, group 1 dV.
+  AQ_WAIT_VMCNT(0);
+  __syncthreads();
+  {
+    f32x16 *give = grp == 0 ? dv : dk;
+    float *dst = (float *)(lds + (kg * 2 + (grp == 0 ? 1 : 0)) * 16384);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *(f32x4 *)(dst + ((dt * 4 + a) * 64 + lane) * 4) =
+            f32x4{give[dt][4 * a], give[dt][4 * a + 1], give[dt][4 * a + 2], give[dt][4 * a + 3]};
+  }
+  __syncthreads();
+  const int64_t key = kc * kChunk + kg * 32 + n;
+  f32x16 *mine = grp == 0 ? dk : dv;
+  const float *src = (const float *)(lds + (kg * 2 + (grp == 0 ? 0 : 1)) * 16384);
+  if (piece >= 0) {
+    float *dst = p.part + (piece * 2 + grp) * (kChunk * kD) + (kg * 32 + n) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 o = *(const f32x4 *)(src + ((dt * 4 + a) * 64 + lane) * 4);
+        *(f32x4 *)(dst + 32 * dt + 8 * a + 4 * hf) =
+            f32x4{mine[dt][4 * a] + o[0], mine[dt][4 * a + 1] + o[1], mine[dt][4 * a + 2] + o[2], mine[dt][4 * a + 3] + o[3]};
+      }
+    return;
+  }
+  const float mul = grp == 0 ? p.scale : 1.0f;
+  if (key >= p.lk) return;
+  uint16_t *out = grp == 0 ? p.dk + bb * p.sdk.b + hh * p.sdk.h + key * p.sdk.l
+                           : p.dv + bb * p.sdv.b + hh * p.sdv.h + key * p.sdv.l;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 o = *(const f32x4 *)(src + ((dt * 4 + a) * 64 + lane) * 4);
+      const int d0 = 32 * dt + 8 * a + 4 * hf;
+      *(bf16x4 *)(out + d0) = bf16x4{(__bf16)((mine[dt][4 * a] + o[0]) * mul), (__bf16)((mine[dt][4 * a + 1] + o[1]) * mul),
+                                     (__bf16)((mine[dt][4 * a + 2] + o[2]) * mul), (__bf16)((mine[dt][4 * a + 3] + o[3]) * mul)};
+    }
+}
+
 // dK and dV of the split units: the pieces' fp32 sums added in piece order (deterministic), dK
 // scaled, rounded to bf16.  One lane per 4 consecutive d of one key of one tensor.
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, int64_t total) {
@@ -1001,7 +1331,8 @@ __global__ __launch_bounds__(256) void vsa_slot_kernel(const int32_t *__restrict
 template <bool SQ>
 static void launch_dkdv(const BwdParams &p, bool sparse, bool gp, dim3 grid, hipStream_t stream) {
   const char *nm = sparse ? "vsa_bwd_dkdv" : "bwd_dkdv";
-  if (sparse && gp) AQ_LAUNCH(nm, (bwd_dkdv_kernel<true, true, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
+  if (!sparse && !gp && !SQ) AQ_LAUNCH(nm, bwd_dkdv_pp_kernel, grid, dim3(kDkdvThreads), 0, stream, p);
+  else if (sparse && gp) AQ_LAUNCH(nm, (bwd_dkdv_kernel<true, true, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
   else if (sparse) AQ_LAUNCH(nm, (bwd_dkdv_kernel<true, false, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
   else if (gp) AQ_LAUNCH(nm, (bwd_dkdv_kernel<false, true, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
   else AQ_LAUNCH(nm, (bwd_dkdv_kernel<false, false, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);

@@ -99,6 +99,11 @@ __device__ __forceinline__ void load_lds16_sa_free(const void *sbase, uint32_t v
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(voff), "s"(uniform_ptr(sbase))
                : "m0");
 }
+// The 4-byte copy in the same form (LDS destination in a scalar register, no "memory" clobber).
+__device__ __forceinline__ void load_lds4_sa_free(const void *sbase, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_off), "v"(voff), "s"(uniform_ptr(sbase))
+               : "m0");
+}
 __device__ __forceinline__ void load_lds4_s(const void *sbase, uint32_t voff, uint8_t *lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0v), "v"(voff), "s"(uniform_ptr(sbase))
