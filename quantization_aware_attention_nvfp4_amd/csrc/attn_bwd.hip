@@ -919,9 +919,11 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
 // scheduled as the forward's ping-pong kernels are.  Wave group g (waves 4g .. 4g+3, one per SIMD,
 // key group kg = wave % 4) owns query half g of every 64-query tile, and the two groups run one
 // phase apart, each alternating
-//   matrix phase M(t): dK/dV += the products of tile t-1 (transposed Q-hat and dO reads against
-//                      the key-major A-hat and dS operands of V(t-1)), then S^T and dP^T of tile t;
-//   vector phase V(t): masks, P-hat and dS of tile t and their one-hot transpositions;
+//   matrix phase M(t): the one-hot transposition of tile t-1's dS, dK/dV += the products of tile
+//                      t-1 (transposed Q-hat and dO reads against the key-major A-hat and dS; the
+//                      dV MFMAs first, while dS's transposition completes), then S^T and dP^T of
+//                      tile t;
+//   vector phase V(t): masks, P-hat and dS of tile t, A-hat's one-hot transposition;
 // so on every SIMD one group's MFMAs run beside the other group's vector work, with one workgroup
 // barrier per phase (group 0 runs M(0) V(0) M(1) ... V(T-1) M(T) and idles last, group 1 idles
 // first; M(0) adds zero operands, M(T)'s S^T and dP^T are dropped).  A group reads only its own 32
@@ -1043,33 +1045,33 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     dv[dt] = f32x16{};
   }
   f32x16 s = f32x16{}, dp = f32x16{};
-  bf16x8 ba[2], bs[2];  // key-major A-hat and dS of the last vector phase (zero before the first)
+  // The last vector phase's A-hat, key-major, and dS, still query-major (packed to bf16; the
+  // matrix phase moves it to one key per lane); zero before the first.
+  bf16x8 ba[2], pd[2];
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    ba[s2] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-    bs[s2] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  for (int h = 0; h < 2; ++h) {
+    ba[h] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    pd[h] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
 
-  // M(t): dK/dV of tile t-1 (t = 0: zero operands against tile 0), then S^T and dP^T of tile t
-  // (t = T: tile T-1 again, dropped); copies of the other group's tile t+grp among the MFMAs.
-  // Operands are read one step ahead of their MFMAs (a step: the two MFMAs of one (s2, dt) of
-  // dK/dV, or of one k-slot of S^T and dP^T).
+  // M(t) as above (t = 0: zero operands against tile 0; t = T: S^T and dP^T of tile T-1 again,
+  // dropped); copies of the other group's tile t+grp among the first MFMAs.  Operands are read
+  // two dK/dV steps or one S^T / dP^T step (two MFMAs) ahead of their use.
   auto mphase = [&](int t) {
     const int t2 = t >= 1 ? t - 1 : 0, t1 = t < T ? t : T - 1;
     uint32_t ta0 = lds0 + kLdsR + (uint32_t)(t2 & 1) * 32768 + ln.tr_off;
     uint32_t va = lds0 + 32768 + ln.k_off, ra = lds0 + kLdsR + (uint32_t)(t1 & 1) * 32768 + ln.r_off;
     AQ_OPAQUE(va);  // per-step addresses formed in the phase, not held across the loop
     const int tc = t + grp < T ? t + grp : T - 1;  // past the last tile: tile T-1 again (same bytes)
-    u32x4 opo[2], opq[2];      // dK/dV A operands (transposed dO and Q-hat reads), by step parity
+    u32x4 op[3];                // one dK/dV A operand (two transposed reads), by step % 3
     u32x4 bq[2], av[2], bo[2];  // S^T / dP^T operands, by step parity
+    // dK/dV steps 0..7: dV of (s2, dt) = (g/4, g%4); 8..15: dK of the same
     auto load_m2 = [&](int g, int b) {
-      const int s2 = g >> 2, dt = g & 3;
+      const int s2 = (g >> 2) & 1, dt = g & 3;
       const uint32_t a0 = ta0 ^ (dt << 6), a1 = ta0 ^ ((dt << 6) | 16);
-      const uint32_t s2o = s2 * 4096;
-      const uint2 o0 = ds_read_tr16_at(a0 + 16384 + s2o), o1 = ds_read_tr16_at(a1 + 16384 + s2o + 1024);
-      const uint2 q0 = ds_read_tr16_at(a0 + s2o), q1 = ds_read_tr16_at(a1 + s2o + 1024);
-      opo[b] = u32x4{o0.x, o0.y, o1.x, o1.y};
-      opq[b] = u32x4{q0.x, q0.y, q1.x, q1.y};
+      const uint32_t off = (g < 8 ? 16384u : 0u) + s2 * 4096;
+      const uint2 x0 = ds_read_tr16_at(a0 + off), x1 = ds_read_tr16_at(a1 + off + 1024);
+      op[b] = u32x4{x0.x, x0.y, x1.x, x1.y};
     };
     auto load_m1 = [&](int u, int b) {
       const uint32_t rt = ra ^ (32 * u);
@@ -1077,15 +1079,36 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
       av[b] = lds_read16(va ^ (32 * u));
       bo[b] = lds_read16(rt + 16384);
     };
+    // dS of tile t-1 to one key per lane (exact in bf16): its MFMAs finish during the dV MFMAs
+    f32x16 ts = f32x16{};
+    {
+      const uint32_t oh = lds0 + kPPOneHot + 16 * lane;
+      ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pd[0], as_bf16x8(lds_read16(oh)), ts, 0, 0, 0);
+      ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pd[1], as_bf16x8(lds_read16(oh + 1024)), ts, 0, 0, 0);
+    }
+    bf16x8 bs[2];
     load_m2(0, 0);
+    load_m2(1, 1);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      if (g < 7) load_m2(g + 1, (g + 1) & 1);
-      else load_m1(0, 0);
-      const int s2 = g >> 2, dt = g & 3;
-      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opo[g & 1]), ba[s2], dv[dt], 0, 0, 0);
-      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(opq[g & 1]), bs[s2], dk[dt], 0, 0, 0);
+    for (int g = 0; g < 16; ++g) {
+      if (g < 14) load_m2(g + 2, (g + 2) % 3);
+      else if (g == 14) load_m1(0, 0);
+      const int s2 = (g >> 2) & 1, dt = g & 3;
+      if (g < 8) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(op[g % 3]), ba[s2], dv[dt], 0, 0, 0);
+      } else {
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(op[g % 3]), bs[s2], dk[dt], 0, 0, 0);
+      }
       if (g < 5) copy_piece(tc, g);
+      if (g == 5) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float fs[8];
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) fs[kk] = ts[8 * h + kk];
+          bs[h] = pack8_exact(fs);
+        }
+      }
     }
     s = f32x16{};
     dp = f32x16{};
@@ -1095,15 +1118,17 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[u], as_bf16x8(bq[u & 1]), s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[u & 1]), as_bf16x8(bo[u & 1]), dp, 0, 0, 0);
     }
-    // DS reads one step ahead: 4 before the first MFMA, then 2 after each dK/dV MFMA (the last
-    // step's slots take S^T / dP^T step 0's three), then 2 and 1 after the two MFMAs of each S^T /
-    // dP^T step.
+    // the one-hot reads and dS's two MFMAs, dK/dV steps 0 and 1's reads; per dK/dV MFMA the
+    // reads two steps ahead (the second last: S^T / dP^T step 0's three); per S^T / dP^T step its
+    // next step's three reads after its MFMAs (2 + 1)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < 15) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (i == 14) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -1121,7 +1146,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     }
   };
 
-  // V(t): P-hat and dS of tile t exactly as bwd_dkdv_kernel forms them, moved to one key per lane.
+  // V(t): P-hat and dS of tile t exactly as bwd_dkdv_kernel forms them; A-hat moved to one key per
+  // lane.
   auto vphase = [&](int t) {
     const int64_t qb = qt0 + t;
     const uint32_t sta = lds0 + kPPStat + (uint32_t)(t & 1) * 1536 + grp * 768 + 4 * pi_q(n);
@@ -1159,23 +1185,19 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     }
     const uint32_t oh = lds0 + kPPOneHot + 16 * lane;
     const bf16x8 one0 = as_bf16x8(lds_read16(oh)), one1 = as_bf16x8(lds_read16(oh + 1024));
-    f32x16 ta = f32x16{}, ts = f32x16{};
+    pd[0] = pack8_cvt(ds);
+    pd[1] = pack8_cvt(ds + 8);
+    f32x16 ta = f32x16{};
     ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ah), one0, ta, 0, 0, 0);
     ta = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ah + 8), one1, ta, 0, 0, 0);
-    ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds), one0, ts, 0, 0, 0);
-    ts = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pack8_cvt(ds + 8), one1, ts, 0, 0, 0);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      float fa[8], fs[8];
+      float fa[8];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        fa[kk] = ta[8 * s2 + kk];
-        fs[kk] = ts[8 * s2 + kk];
-      }
+      for (int kk = 0; kk < 8; ++kk) fa[kk] = ta[8 * s2 + kk];
       ba[s2] = pack8_exact(fa);
-      bs[s2] = pack8_exact(fs);
       AQ_OPAQUE(ba[s2]);
-      AQ_OPAQUE(bs[s2]);
+      AQ_OPAQUE(pd[s2]);
     }
   };
 
