@@ -940,9 +940,13 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_kernel(BwdParams p) 
 constexpr int kPPStat = 131072;
 constexpr int kPPOneHot = kPPStat + 2 * 1536;
 constexpr int kDkdvPPLds = kPPOneHot + 2048;
+constexpr int kPPList = kDkdvPPLds;  // cube-sparse: the list of (query cube, position), int32
 
+// SPARSE: the cube-sparse mode of bwd_dkdv_kernel (the query cubes that selected this key cube,
+// two tiles each, listed by wave 0 in LDS).
+template <bool SPARSE>
 __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(256))) uint8_t lds[kDkdvPPLds];
+  __shared__ __attribute__((aligned(256))) uint8_t lds[kDkdvPPLds + (SPARSE ? 4 * (kMaxCubes + 1) : 0)];
   const uint32_t lds0 = lds_addr(lds);
   int64_t vid, piece = -1;
   if ((int64_t)blockIdx.x < p.full_blocks) {
@@ -961,12 +965,39 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   const int64_t nqt = (p.lq + kQT - 1) / kQT;
   int64_t qt0 = p.causal ? (kc * kChunk) / kQT : 0;
   int64_t ntiles = nqt - qt0;
-  if (piece >= 0) {
+  if (!SPARSE && piece >= 0) {
     const int64_t j = piece % p.split, lo = ntiles * j / p.split, hi = ntiles * (j + 1) / p.split;
     qt0 += lo;
     ntiles = hi - lo;
   }
+  int32_t *lds_list = (int32_t *)(lds + kPPList);
+  if constexpr (SPARSE) {
+    if (wave == 0) {
+      const int16_t *col = p.slot_t + (bh * p.Ck + kc) * p.Cq;
+      int cnt = 0;
+      for (int64_t base = 0; base < p.Cq; base += 64) {
+        const int64_t qcube = base + lane;
+        const int sl = qcube < p.Cq ? (int)col[qcube] : -1;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(sl >= 0);
+        const int pos = cnt + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+        if (sl >= 0) lds_list[pos] = (int32_t)qcube | (sl << 16);
+        cnt += (int)__builtin_popcountll(m);
+      }
+      if (lane == 0) lds_list[kMaxCubes] = cnt;
+    }
+    __syncthreads();
+    ntiles = 2 * (int64_t)lds_list[kMaxCubes];
+  }
   const int T = (int)ntiles;
+  // Tile t: its query tile, and the row of the chunk maxima its queries use.
+  auto tile_qb = [&](int t) -> int64_t {
+    if constexpr (SPARSE) return 2 * (int64_t)(__builtin_amdgcn_readfirstlane(lds_list[t >> 1]) & 0xffff) + (t & 1);
+    return qt0 + t;
+  };
+  auto tile_cm = [&](int t) -> int64_t {
+    if constexpr (SPARSE) return bh * p.nsel + (__builtin_amdgcn_readfirstlane(lds_list[t >> 1]) >> 16);
+    return bh * p.Ck + kc;
+  };
 
   DkdvLane ln;
   {
@@ -985,9 +1016,9 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   // statistic min(kg, 2) (wave 3 rewrites D with the same values).  dO rows and statistics past
   // lq repeat the last valid one.  Offsets are formed here, not held across the loop.
   const int stat_k = kg < 2 ? kg : 2;
-  const float *stat_src = stat_k == 0 ? p.cmax + (bh * p.Ck + kc) * p.lq : (stat_k == 1 ? p.lse : p.dvec) + bh * p.lq;
+  const float *stat_src0 = stat_k == 0 ? p.cmax + (bh * p.Ck + kc) * p.lq : (stat_k == 1 ? p.lse : p.dvec) + bh * p.lq;
   auto copy_piece = [&](int t, int what) {
-    const int64_t qb = qt0 + t;
+    const int64_t qb = tile_qb(t);
     const int rem = (int)(p.lq - 1 - qb * kQT);
     const uint32_t rq = lds0 + kLdsR + (uint32_t)(t & 1) * 32768;
     if (what < 4) {
@@ -1005,6 +1036,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
     } else {
       const int q = 32 * other + (lane & 31);
       const int qe = q < rem ? q : rem;
+      const float *stat_src = SPARSE && stat_k == 0 ? p.cmax + tile_cm(t) * p.lq : stat_src0;
       load_lds4_sa_free(stat_src + qb * kQT, (uint32_t)qe * 4u,
                         lds0 + kPPStat + (uint32_t)(t & 1) * 1536 + other * 768 + stat_k * 256);
     }
@@ -1149,7 +1181,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void bwd_dkdv_pp_kernel(BwdParams 
   // V(t): P-hat and dS of tile t exactly as bwd_dkdv_kernel forms them; A-hat moved to one key per
   // lane.
   auto vphase = [&](int t) {
-    const int64_t qb = qt0 + t;
+    const int64_t qb = tile_qb(t);
     const uint32_t sta = lds0 + kPPStat + (uint32_t)(t & 1) * 1536 + grp * 768 + 4 * pi_q(n);
     const float mc = lds_read_f32(sta), lse2 = lds_read_f32(sta + 256), Di = lds_read_f32(sta + 512);
     const int qrow = (int)(qb * kQT) + ln.qloc;
@@ -1353,7 +1385,8 @@ __global__ __launch_bounds__(256) void vsa_slot_kernel(const int32_t *__restrict
 template <bool SQ>
 static void launch_dkdv(const BwdParams &p, bool sparse, bool gp, dim3 grid, hipStream_t stream) {
   const char *nm = sparse ? "vsa_bwd_dkdv" : "bwd_dkdv";
-  if (!sparse && !gp && !SQ) AQ_LAUNCH(nm, bwd_dkdv_pp_kernel, grid, dim3(kDkdvThreads), 0, stream, p);
+  if (!sparse && !gp && !SQ) AQ_LAUNCH(nm, bwd_dkdv_pp_kernel<false>, grid, dim3(kDkdvThreads), 0, stream, p);
+  else if (sparse && !gp && !SQ) AQ_LAUNCH(nm, bwd_dkdv_pp_kernel<true>, grid, dim3(kDkdvThreads), 0, stream, p);
   else if (sparse && gp) AQ_LAUNCH(nm, (bwd_dkdv_kernel<true, true, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
   else if (sparse) AQ_LAUNCH(nm, (bwd_dkdv_kernel<true, false, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
   else if (gp) AQ_LAUNCH(nm, (bwd_dkdv_kernel<false, true, SQ>), grid, dim3(kDkdvThreads), 0, stream, p);
