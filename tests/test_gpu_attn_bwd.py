@@ -55,7 +55,9 @@ def ref_bwd(q, k, v, do, causal=False, flags=15, qrows=None, krows=None):
 
 
 @pytest.mark.parametrize("Lq,Lk,causal,flags", [(256, 256, False, 15), (300, 300, False, 15), (200, 333, False, 15),
-                                                (300, 300, True, 15), (190, 260, False, 0), (130, 130, True, 0)])
+                                                (300, 300, True, 15), (190, 260, False, 0), (130, 130, True, 0),
+                                                # one 64-query tile per key chunk; a last tile of one row
+                                                (40, 300, False, 15), (65, 200, False, 15), (65, 65, True, 15)])
 def test_full_gradients(m, Lq, Lk, causal, flags):
     B, H = 1, 2
     q, do = rand(B, Lq, H, 100 + Lq, 1.5), rand(B, Lq, H, 300 + Lq)
