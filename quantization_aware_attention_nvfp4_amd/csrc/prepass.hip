@@ -18,10 +18,12 @@
 // bf16, as "nvfp4_qad.py" quantizes under input_global_sf), and the smooth-K mean subtracted in
 // fp32 before quantization (rows past L stay zero).
 //
-// One workgroup handles one 128-row chunk of one head: the chunk is staged in LDS as
+// tile_prepass (every mode): one workgroup per 128-row chunk of one head, staged in LDS as
 // [row][d] (rows past L read as zero), quantized in place, then written as
 //   rows_out  [B*H, C*128, 128]       row-major (the MFMA operand rows of the attention kernels)
 //   tiles_out [B*H, C, 128 d, 128 rows] d-major (operands whose contraction runs over rows).
+// rows_prepass streams the common row case (unit scale, no smoothing); kv_prepass writes the
+// forward's K-hat rows and V-hat tiles of the common case in one launch.
 #include "aq_device.hpp"
 #include "launch.hpp"
 #include "timing.hpp"

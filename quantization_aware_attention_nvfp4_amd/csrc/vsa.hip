@@ -6,10 +6,12 @@
 // Tokens arrive cube-major (each cube's 128 tokens contiguous), so a cube is exactly one 128-key
 // chunk of the dense kernels and V-hat's 16-key blocks never straddle cubes.
 //
-//   pool_kernel    cube means of Q, K (and V for the coarse output) in fp32, rounded to bf16.
-//   select_kernel  per (head, query cube), one wave: coarse logits against every key cube in
-//                  fp32, top-k by repeated wave argmax (ties to the lower index), the selected
-//                  cubes listed in ascending order; optionally the coarse output softmax(logits) @ Vc.
+//   pool_kernel        cube means of Q, K (and V for the coarse output) in fp32, rounded to bf16.
+//   select_lds_kernel  per (head, query cube), one wave, the head's key-cube means staged in LDS
+//                      (up to 256 key cubes; select_kernel, the same selection without the
+//                      staging, past that): coarse logits against every key cube in fp32, the
+//                      top-k (ties to the lower index) listed in ascending order; optionally the
+//                      coarse output softmax(logits) @ Vc.
 //   fine stage     the dense forward kernel with each query cube's chunk list (attn_fwd.hip).
 #include "attn_common.hpp"
 #include "launch.hpp"
