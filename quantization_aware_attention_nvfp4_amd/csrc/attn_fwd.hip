@@ -1439,20 +1439,54 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel
     va = lds0 + kLdsV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
   }
   // S^T of a chunk from buffer offset kbuf (attn_fwd_pp_train_kernel's arrangement).
+  // S^T of a chunk from buffer offset kbuf: column pair t outermost, so each Q-hat pair is decoded
+  // once and feeds the four sub-tiles' chains.  Software-pipelined by hand, a scheduling barrier
+  // closing each pair's step: step t issues pair t+1's K-hat and code/scale reads, then pair t's
+  // four MFMAs (their operands read in step t-1), then pair t+1's decode; so each read has a
+  // step of MFMAs to land in, and only two Q-hat pairs are live at a time.
   auto logits = [&](uint32_t kbuf, f32x16 (&st)[4]) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t code = *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(qca + 256 * t);
-      const _Float16 h = *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)(qsa + 128 * t);
+    uint32_t kb = kbuf + ka;
+    AQ_OPAQUE(kb);  // per-pair addresses formed here, not held across the loop
+    auto kread = [&](int t, int kt) -> u32x4 { return lds_read16((kb ^ (32 * t)) + 8192 * kt); };
+    auto qdec = [&](uint32_t code, _Float16 h) -> f16x8 {
       const f16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0) * h;
       const f16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 1) * h;
       const f16x2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 2) * h;
       const f16x2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 3) * h;
-      const f16x8 b = {x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+      return f16x8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+    };
+    auto code_of = [&](int t) -> uint32_t {
+      return *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)(qca + 256 * t);
+    };
+    auto scale_of = [&](int t) -> _Float16 {
+      return *(const __attribute__((address_space(3))) _Float16 *)(uintptr_t)(qsa + 128 * t);
+    };
+    u32x4 kc[4], kn[4];
+    f16x8 b = qdec(code_of(0), scale_of(0)), bn = b;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) kc[kt] = kread(0, kt);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t cn = 0u;
+      _Float16 hn = (_Float16)0.0f;
+      if (t < 7) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) kn[kt] = kread(t + 1, kt);
+        cn = code_of(t + 1);
+        hn = scale_of(t + 1);
+      }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, lds_read16(kbuf + (ka ^ (32 * t)) + 8192 * kt)),
-                                                        b, t ? st[kt] : f32x16{}, 0, 0, 0);
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kc[kt]), b, t ? st[kt] : f32x16{}, 0, 0,
+                                                        0);
+      if (t < 7) bn = qdec(cn, hn);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t < 7) {
+        b = bn;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) kc[kt] = kn[kt];
+      }
     }
   };
 
@@ -1533,15 +1567,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_train_kernel
     }
     __builtin_amdgcn_sched_barrier(0);
     logits(buf, s);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-#pragma unroll
-    for (int g = 0; g < 32; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (g < 26) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (g < 28) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) AQ_OPAQUE(s[kt]);
 #pragma unroll
