@@ -1122,6 +1122,20 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
     if (j + 1 < n_iter) copy_k(j + 1, buf);
     if (j < n_iter) copy_v(j, buf);
   };
+  // Piece q of fill(j) as a copy the operand reads of the matrix phase may pass (as in
+  // attn_fwd_pp_kernel): q < 4 the K-hat sub-tile q of chunk j+1, else the V-hat sub-tile q-4 of
+  // chunk j, both chunks clamped to the last one.
+  auto fill_piece = [&](int j, int q) {
+    const uint32_t buf = lds0 + (uint32_t)(j & 1) * 65536;
+    const int last = n_iter - 1;
+    if (q < 4) {
+      const int jk = j + 1 < last ? j + 1 : last;
+      load_lds16_sa_free(kbase + (int64_t)jk * 32768 + q * 8192, k_off, buf + kLdsK + q * 8192 + 1024 * wave);
+    } else {
+      const int jv = j < last ? j : last;
+      load_lds16_sa_free(vbase + (int64_t)jv * 32768 + (q - 4) * 64, v_off, buf + kLdsV + (q - 4) * 8192 + 1024 * wave);
+    }
+  };
 
   copy_k(0, lds0 + 65536);
   fill(0);
@@ -1271,6 +1285,9 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
           const f16x8 a = __builtin_bit_cast(f16x8, lds_read16(vad[j] + 8192 * kt + 2048 * dt));
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, pq[kt][j]), acc[dt], 0, 0, 0);
           acc_hp[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, ph[kt][j]), acc_hp[dt], 0, 0, 0);
+          // this wave's share of fill(it+1) (buffer (it+1)%2, which no read of this phase
+          // touches), one copy per eight MFMAs
+          if (dt == 1) fill_piece(it + 1, 2 * kt + j);
         }
     // each V-hat read 4 reads ahead of its two MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -1291,15 +1308,11 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_train_kernel(Fwd
     }
   };
 
-  // The phases of the inference kernel.  Here the matrix phase is the longer one (96 MFMAs and
-  // the Q-hat decode against about 3900 cycles of vector work), so the copies go where the vector
-  // phase leaves time: iteration it+1's by group 1 at the start of its V(it) (phase 2it+1), by
-  // group 0 at the start of its V(it+1) (phase 2it+2); both are waited for at the end of phase
-  // 2it+2.
+  // The phases and copies of the inference kernel: iteration it+1's copies issued by each group
+  // among the MFMAs of its M(it) (phases 2it+1 and 2it+2), both shares waited for at the end of
+  // phase 2it+2.
   if (grp == 1) __builtin_amdgcn_s_barrier();
   for (int it = 0; it < n_iter; ++it) {
-    if (grp == 1 && it + 1 < n_iter) fill(it + 1);
-    if (grp == 0 && it >= 1) fill(it);
     __builtin_amdgcn_s_setprio(0);
     vphase(it);
     if (grp == 0) AQ_WAIT_VMCNT(0);
