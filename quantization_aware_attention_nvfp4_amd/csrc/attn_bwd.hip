@@ -454,22 +454,48 @@ __global__ __launch_bounds__(kDqsWaves * 64, 2) void bwd_dq_sp_kernel(BwdParams 
     mask_step(s, s_cur);
     AQ_OPAQUE(s_cur);
     // MFMAs: dQ of s-1 (8, two transposed reads each), S/dP of s+1 (16, one read each); between
-    // them the vector work of s, about three instructions per MFMA.
-    dq_products(s - 1 + kDqsSlots, dp0, dp1);
-    logits(s + 1, s_nxt, dp_nxt);
-    dscores(s_cur, dp_cur, dn0, dn1);
-    // per MFMA: its operand reads a few MFMAs ahead, then one exponential (the first 16) and two
-    // other vector instructions
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    // them the vector work of s.  Software-pipelined by hand in 8 steps, a scheduling barrier
+    // closing each: step t issues the operand reads of step t+1, then the S^T and dP^T MFMAs of
+    // column pair t and dQ^T MFMA t (d tile t/2, dS half t%2), whose operands step t-1 read, and
+    // dS of rows 2t and 2t+1; so every read has a step of MFMAs to land in (left to the compiler,
+    // each read sat just before its MFMA).  Same products in the same order as logits,
+    // dq_products and dscores.
+    const uint32_t a = slot_of(s + 1) + a_off;
+    const uint32_t b = slot_of(s - 1 + kDqsSlots) + t_off;
+    u32x4 ks[2], kp[2];
+    uint2 t0[2], t1[2];
+    auto reads = [&](int t) {
+      const uint32_t at = a ^ (32u * t);
+      ks[t & 1] = lds_read16(at);
+      kp[t & 1] = lds_read16(at + 8192);
+      const int dt = t >> 1;
+      const uint32_t h = (uint32_t)(t & 1) * 2048;
+      t0[t & 1] = ds_read_tr16_at((b ^ (uint32_t)(dt << 6)) + h);
+      t1[t & 1] = ds_read_tr16_at((b ^ (uint32_t)((dt << 6) | 16)) + 1024 + h);
+    };
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    uint32_t dsw[8];
+    reads(0);
 #pragma unroll
-    for (int g = 0; g < 24; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (g < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else if (g < 19) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (g < 16) __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    for (int t = 0; t < 8; ++t) {
+      if (t + 1 < 8) reads(t + 1);
+      const int c = t & 1;
+      s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ks[c]), qf[t], t == 0 ? f32x16{} : s_nxt, 0, 0, 0);
+      dp_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kp[c]), of[t], t == 0 ? f32x16{} : dp_nxt, 0, 0, 0);
+      acc[t >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u32x4{t0[c].x, t0[c].y, t1[c].x, t1[c].y}),
+                                                            c ? dp1 : dp0, acc[t >> 1], 0, 0, 0);
+      float ds[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float A = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[2 * t + r], p.c, -lse2));
+        ds[r] = A * (dp_cur[2 * t + r] - Di);
+      }
+      dsw[t] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)ds[0], (__bf16)ds[1]});
+      AQ_OPAQUE(dsw[t]);  // formed in this step, not sunk to its use after the loop
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    dn0 = __builtin_bit_cast(bf16x8, u32x4{dsw[0], dsw[1], dsw[2], dsw[3]});
+    dn1 = __builtin_bit_cast(bf16x8, u32x4{dsw[4], dsw[5], dsw[6], dsw[7]});
     AQ_OPAQUE(dn0);
     AQ_OPAQUE(dn1);
   };
