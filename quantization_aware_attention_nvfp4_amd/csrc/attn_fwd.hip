@@ -627,14 +627,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
     ka = lds0 + kLdsK + krow * 256 + 16 * (hf ^ swk);
     va = lds0 + kLdsV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
   }
-  auto logits = [&](uint32_t kbuf, int kt, f32x16 &st) {
-    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + ka + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-    for (int t = 1; t < 8; ++t)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + (ka ^ (32 * t)) + 8192 * kt)), qf[t], st,
-                                                   0, 0, 0);
-  };
-
   f32x16 s[4];
   f32x16 acc[4];
 #pragma unroll
@@ -643,10 +635,27 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_pp_kernel(FwdParams
   float l_run = 0.0f, alpha = 1.0f;
   u32x4 pq[4][2];
 
+  // The first chunk's logits: column pair t outermost (each chain's sum in the same order), the
+  // operand reads eight MFMAs ahead of their use; left to the compiler, each MFMA waited for its
+  // own read.
+  auto first_logits = [&](uint32_t kbuf) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + (ka ^ (32 * t)) + 8192 * kt)), qf[t],
+                                                        t == 0 ? f32x16{} : s[kt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (g < 24) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
   AQ_WAIT_VMCNT(0);
   __builtin_amdgcn_s_barrier();
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) logits(65536, kt, s[kt]);
+  first_logits(65536);
   // Buffer 1's K half is read by every wave before iteration 1's copies go there.
   __builtin_amdgcn_s_barrier();
 
@@ -894,14 +903,6 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
     ka = lds0 + kLdsK + krow * 256 + 16 * (hf ^ swk);
     va = lds0 + kLdsV + n * 64 + 16 * ((2 * hf) ^ sw_v64(n));
   }
-  auto logits = [&](uint32_t kbuf, int kt, f32x16 &st) {
-    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + ka + 8192 * kt)), qf[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-    for (int t = 1; t < 8; ++t)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + (ka ^ (32 * t)) + 8192 * kt)), qf[t], st,
-                                                   0, 0, 0);
-  };
-
   f32x16 s[4];
   f32x16 acc[4];
 #pragma unroll
@@ -910,10 +911,27 @@ __global__ __launch_bounds__(kPPWaves * 64, 1) void attn_fwd_vsa_pp_kernel(FwdPa
   float l_run = 0.0f, alpha = 1.0f;
   u32x4 pq[4][2];
 
+  // The first chunk's logits: column pair t outermost (each chain's sum in the same order), the
+  // operand reads eight MFMAs ahead of their use; left to the compiler, each MFMA waited for its
+  // own read.
+  auto first_logits = [&](uint32_t kbuf) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(kbuf + (ka ^ (32 * t)) + 8192 * kt)), qf[t],
+                                                        t == 0 ? f32x16{} : s[kt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (g < 24) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
   AQ_WAIT_VMCNT(0);
   __syncthreads();
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) logits(grp ? 32768u : 0u, kt, s[kt]);
+  first_logits(grp ? 32768u : 0u);
   __builtin_amdgcn_s_barrier();  // buffer 0 is read; phase 0 fills buffer 1
 
   // V(it): running max, P-hat of position it (attn_fwd_pp_kernel's vector phase).
